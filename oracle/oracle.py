@@ -1,0 +1,179 @@
+"""ctypes front end of the fp64 CPU oracle in pkv_oracle.c.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+CPU-baseline leg of bench.py, never by the product package.  It shares no
+code with the HIP path.
+
+Arrays are numpy arrays holding raw element bits:
+  'f32' -> float32, 'f16' / 'bf16' -> uint16, 'fp8' -> uint8 (OCP E4M3FN).
+Cache arrays use the layout [num_blocks][num_kv_heads][block_size][head_dim].
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pkv_oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
+BITS_NP = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+
+_lib = None
+
+
+def build_oracle():
+    """Compile pkv_oracle.c with gcc (no fast-math, no FP contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+           "-ffp-contract=off", _SRC, "-o", _SO + ".tmp", "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(_SO + ".tmp", _SO)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_SO):
+        build_oracle()
+    lib = ctypes.CDLL(_SO)
+    P, I, D, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_float
+    I64 = ctypes.c_int64
+    lib.orc_paged_decode.argtypes = [P, P, I, P, P, I, P, P, I, I, I, I, I, I, D, D, D]
+    lib.orc_paged_decode.restype = I
+    lib.orc_softmax_weights.argtypes = [P, I, I, P, I, P, I, P, P, I, I, I, I, I, I, D, D]
+    lib.orc_softmax_weights.restype = I
+    lib.orc_partition_stats.argtypes = [P, P, P, I, I, I, I, P, I, P, P, I, P, P,
+                                        I, I, I, I, I, I, D, D, D]
+    lib.orc_partition_stats.restype = I
+    lib.orc_lse_merge.argtypes = [P, P, P, P, I, I]
+    lib.orc_lse_merge.restype = None
+    lib.orc_cache_append.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, F]
+    lib.orc_cache_append.restype = I
+    lib.orc_e4m3_encode_array.argtypes = [P, I64, P]
+    lib.orc_e4m3_encode_array.restype = None
+    lib.orc_bits_to_f64.argtypes = [P, I, I64, P]
+    lib.orc_bits_to_f64.restype = None
+    lib.orc_kv_bytes_per_token.argtypes = [I, I, I, I]
+    lib.orc_kv_bytes_per_token.restype = ctypes.c_uint64
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check_bits(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != BITS_NP[dtype]:
+        raise TypeError(f"{dtype} data must be given as {BITS_NP[dtype].__name__} bits, got {a.dtype}")
+    return a
+
+
+def to_f64(bits, dtype):
+    """Exact widening of raw element bits to float64 (E4M3 via its definition)."""
+    bits = _check_bits(bits, dtype)
+    out = np.empty(bits.shape, dtype=np.float64)
+    _load().orc_bits_to_f64(_ptr(bits), DTYPES[dtype], bits.size, _ptr(out))
+    return out
+
+
+def e4m3_encode(x):
+    """Nearest E4M3FN code of each float32 value, ties to even, saturating."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _load().orc_e4m3_encode_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def kv_bytes_per_token(layers, kv_heads, head_dim, dtype):
+    return int(_load().orc_kv_bytes_per_token(layers, kv_heads, head_dim, ELEM_BYTES[dtype]))
+
+
+def cache_append(k_cache, v_cache, k_new, v_new, slot_mapping, new_dtype, kv_dtype,
+                 k_scale=1.0, v_scale=1.0):
+    """In-place append of new K/V rows [T][H_kv][d] at slot_mapping[T]."""
+    k_cache = _check_bits(k_cache, kv_dtype)
+    v_cache = _check_bits(v_cache, kv_dtype)
+    k_new = _check_bits(k_new, new_dtype)
+    v_new = _check_bits(v_new, new_dtype)
+    slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    nb, hkv, bs, d = k_cache.shape
+    T = slots.shape[0]
+    assert k_new.shape == (T, hkv, d) and v_new.shape == (T, hkv, d)
+    rc = _load().orc_cache_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                                  _ptr(slots), T, hkv, d, bs, nb, DTYPES[new_dtype],
+                                  DTYPES[kv_dtype], k_scale, v_scale)
+    if rc != 0:
+        raise ValueError(f"oracle cache_append failed ({rc})")
+    return k_cache, v_cache
+
+
+def _common(q, q_dtype, k_cache, kv_dtype, block_tables, context_lens):
+    q = _check_bits(q, q_dtype)
+    k_cache = _check_bits(k_cache, kv_dtype)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    assert d == d2 and bt.shape[0] == S and cl.shape[0] == S
+    return q, k_cache, bt, cl, S, hq, hkv, d, bs
+
+
+def paged_decode(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
+                 scale, k_scale=1.0, v_scale=1.0):
+    """fp64 out[S][H_q][d] of single-query attention through the block table."""
+    q, k_cache, bt, cl, S, hq, hkv, d, bs = _common(q, q_dtype, k_cache, kv_dtype,
+                                                    block_tables, context_lens)
+    v_cache = _check_bits(v_cache, kv_dtype)
+    out = np.empty((S, hq, d), dtype=np.float64)
+    rc = _load().orc_paged_decode(_ptr(out), _ptr(q), DTYPES[q_dtype], _ptr(k_cache),
+                                  _ptr(v_cache), DTYPES[kv_dtype], _ptr(bt), _ptr(cl),
+                                  S, hq, hkv, d, bs, bt.shape[1], scale, k_scale, v_scale)
+    if rc != 0:
+        raise ValueError(f"oracle paged_decode failed ({rc})")
+    return out
+
+
+def softmax_weights(s, h, q, q_dtype, k_cache, kv_dtype, block_tables, context_lens,
+                    scale, k_scale=1.0):
+    q, k_cache, bt, cl, S, hq, hkv, d, bs = _common(q, q_dtype, k_cache, kv_dtype,
+                                                    block_tables, context_lens)
+    w = np.zeros(max(int(cl[s]), 1), dtype=np.float64)
+    n = _load().orc_softmax_weights(_ptr(w), s, h, _ptr(q), DTYPES[q_dtype], _ptr(k_cache),
+                                    DTYPES[kv_dtype], _ptr(bt), _ptr(cl), S, hq, hkv, d, bs,
+                                    bt.shape[1], scale, k_scale)
+    return w[:n]
+
+
+def partition_stats(s, h, t0, t1, q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
+                    context_lens, scale, k_scale=1.0, v_scale=1.0):
+    """(m, l, acc[d]) of tokens [t0, t1) for one (sequence, q-head)."""
+    q, k_cache, bt, cl, S, hq, hkv, d, bs = _common(q, q_dtype, k_cache, kv_dtype,
+                                                    block_tables, context_lens)
+    v_cache = _check_bits(v_cache, kv_dtype)
+    m = np.zeros(1)
+    l = np.zeros(1)
+    acc = np.zeros(d)
+    rc = _load().orc_partition_stats(_ptr(m), _ptr(l), _ptr(acc), s, h, t0, t1, _ptr(q),
+                                     DTYPES[q_dtype], _ptr(k_cache), _ptr(v_cache),
+                                     DTYPES[kv_dtype], _ptr(bt), _ptr(cl), S, hq, hkv, d, bs,
+                                     bt.shape[1], scale, k_scale, v_scale)
+    if rc != 0:
+        raise ValueError(f"oracle partition_stats failed ({rc})")
+    return float(m[0]), float(l[0]), acc
+
+
+def lse_merge(m, l, acc):
+    """Merge per-partition (m_p, l_p, acc_p[d]) into one output row."""
+    m = np.ascontiguousarray(m, dtype=np.float64)
+    l = np.ascontiguousarray(l, dtype=np.float64)
+    acc = np.ascontiguousarray(acc, dtype=np.float64)
+    P, d = acc.shape
+    out = np.empty(d)
+    _load().orc_lse_merge(_ptr(out), _ptr(m), _ptr(l), _ptr(acc), P, d)
+    return out

@@ -1,0 +1,339 @@
+/*
+ * pkv_oracle.c -- slow, plain, fp64 CPU oracle for paged decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
+ * or calls this file; only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load it (through oracle/oracle.py).  It shares
+ * no header, table or helper with the HIP path.
+ *
+ * What it computes, and where the pages define it:
+ *  - Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V, evaluated for the single
+ *    query of a decode step over the prefix plus the new token
+ *    ("KV Cache 与 PageAttention深度实战", section 1.2, the attention formula and
+ *    Output_t = Attention(Q_t, [K_prefix, K_t], [V_prefix, V_t])).  The scale is
+ *    an explicit argument; callers pass 1/sqrt(d).
+ *  - K/V are reached through a per-sequence block table that maps logical
+ *    block j to a physical block ("Transformer 推理优化：KV Cache、PagedAttention
+ *    与 vLLM", section 3.3 Block Table; "KV Cache 与 PageAttention深度实战",
+ *    section 3.2: attention addresses K/V indirectly through the block table).
+ *    The oracle walks the table in logical order, token by token.
+ *  - Physical layout (a reading; the pages only say a block holds the KV of
+ *    16 tokens): cache[block][kv_head][offset][dim], one (block, head) tile
+ *    contiguous.  Element index = ((blk*H_kv + h)*bs + off)*d + i.
+ *  - Grouped-query attention: q-head h reads kv-head h / (H_q/H_kv) (a reading;
+ *    the pages name GQA for Qwen3-8B and Llama-3-70B without the mapping).
+ *  - FP8 E4M3 KV (range +-448, "大语言模型推理引擎深度剖析", section 4.2): OCP
+ *    E4M3FN, per-tensor scale, real value = decode(code) * scale.
+ *  - Cache append: only the new token's K and V are written ("Transformer 推理
+ *    优化", section 2.2), at slot = physical_block*bs + offset.
+ *
+ * Everything is evaluated in double precision with plain loops.  Compile
+ * without -ffast-math and with -ffp-contract=off.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <stdlib.h>
+
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_FP8_E4M3 = 3 };
+
+/* ---------------------------------------------------------------- decoders */
+
+/* IEEE-754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double orc_f16_to_f64(uint16_t h) {
+  int s = (h >> 15) & 1, e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-10 * 2^-14 */
+  else if (e == 31)
+    v = (m == 0) ? INFINITY : NAN;
+  else
+    v = ldexp(1.0 + (double)m / 1024.0, e - 15);
+  return s ? -v : v;
+}
+
+/* bfloat16 is the top half of an IEEE binary32. */
+double orc_bf16_to_f64(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+double orc_f32_bits_to_f64(uint32_t u) {
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* OCP E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits, no infinities,
+ * S.1111.111 is NaN, largest finite magnitude 1.75 * 2^8 = 448. */
+double orc_e4m3_to_f64(uint8_t c) {
+  int s = (c >> 7) & 1, e = (c >> 3) & 0xF, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6); /* subnormal */
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* Encode a binary32 value as E4M3FN: the nearest finite code, ties to the
+ * code with an even mantissa, magnitudes beyond 448 (and infinities)
+ * saturate to +-448, NaN gives 0x7F.  Written as a search over the 127
+ * non-negative finite codes so that it is the definition itself. */
+uint8_t orc_e4m3_encode(float x) {
+  if (isnan(x)) return 0x7F;
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  int neg = (u >> 31) & 1;
+  if (isinf(x)) return (uint8_t)(neg ? 0xFE : 0x7E);
+  double ax = fabs((double)x);
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c <= 126; ++c) {
+    double d = fabs(ax - orc_e4m3_to_f64((uint8_t)c));
+    if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(best | (neg ? 0x80 : 0));
+}
+
+static double load_elem(const void* base, int64_t idx, int dtype) {
+  switch (dtype) {
+    case ORC_F32: return orc_f32_bits_to_f64(((const uint32_t*)base)[idx]);
+    case ORC_F16: return orc_f16_to_f64(((const uint16_t*)base)[idx]);
+    case ORC_BF16: return orc_bf16_to_f64(((const uint16_t*)base)[idx]);
+    case ORC_FP8_E4M3: return orc_e4m3_to_f64(((const uint8_t*)base)[idx]);
+  }
+  return NAN;
+}
+
+/* The new-token value as binary32 (every f16/bf16 value is exact in f32). */
+static float load_as_f32(const void* base, int64_t idx, int dtype) {
+  return (float)load_elem(base, idx, dtype);
+}
+
+void orc_bits_to_f64(const void* src, int dtype, int64_t n, double* dst) {
+  for (int64_t i = 0; i < n; ++i) dst[i] = load_elem(src, i, dtype);
+}
+
+void orc_e4m3_encode_array(const float* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(x[i]);
+}
+
+/* --------------------------------------------------------------- KV bytes */
+
+/* Per-token KV bytes over the whole model: 2 (K and V) x layers x kv_heads x
+ * head_dim x element bytes ("Transformer 推理优化", section 2.5). */
+uint64_t orc_kv_bytes_per_token(int layers, int kv_heads, int head_dim,
+                                int elem_bytes) {
+  return 2ull * (uint64_t)layers * (uint64_t)kv_heads * (uint64_t)head_dim *
+         (uint64_t)elem_bytes;
+}
+
+/* ------------------------------------------------------------ cache append */
+
+static int elem_bytes(int dtype) {
+  return dtype == ORC_F32 ? 4 : (dtype == ORC_FP8_E4M3 ? 1 : 2);
+}
+
+/* Write the new tokens' K and V rows into the paged caches.
+ * k_new/v_new: [T][H_kv][d] in new_dtype.  slot_mapping[t] < 0 skips token t.
+ * Bit copy when kv_dtype == new_dtype; for an E4M3 cache each element is
+ * encoded from the f32 value x * (1/scale), with 1/scale and the product
+ * both rounded to binary32.  Returns -1 on an out-of-range slot, else 0. */
+int orc_cache_append(void* k_cache, void* v_cache, const void* k_new,
+                     const void* v_new, const int64_t* slot_mapping,
+                     int num_tokens, int num_kv_heads, int head_dim,
+                     int block_size, int num_blocks, int new_dtype,
+                     int kv_dtype, float k_scale, float v_scale) {
+  const int eb_new = elem_bytes(new_dtype), eb_kv = elem_bytes(kv_dtype);
+  for (int t = 0; t < num_tokens; ++t) {
+    int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    if (slot >= (int64_t)num_blocks * block_size) return -1;
+    int64_t blk = slot / block_size, off = slot % block_size;
+    for (int h = 0; h < num_kv_heads; ++h) {
+      for (int i = 0; i < head_dim; ++i) {
+        int64_t src = ((int64_t)t * num_kv_heads + h) * head_dim + i;
+        int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * head_dim + i;
+        for (int which = 0; which < 2; ++which) {
+          const void* nb = which ? v_new : k_new;
+          void* cb = which ? v_cache : k_cache;
+          if (kv_dtype == ORC_FP8_E4M3) {
+            float scale = which ? v_scale : k_scale;
+            float inv = 1.0f / scale;
+            float y = load_as_f32(nb, src, new_dtype) * inv;
+            ((uint8_t*)cb)[dst] = orc_e4m3_encode(y);
+          } else {
+            if (eb_new != eb_kv) return -2;
+            memcpy((char*)cb + dst * eb_kv, (const char*)nb + src * eb_new, eb_kv);
+          }
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+/* --------------------------------------------------------- decode attention */
+
+typedef struct {
+  const void* q;
+  int q_dtype;
+  const void* k_cache;
+  const void* v_cache;
+  int kv_dtype;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs, num_q_heads, num_kv_heads, head_dim, block_size;
+  int max_blocks_per_seq;
+  double scale, k_scale, v_scale;
+} orc_args;
+
+/* Element i of token t of sequence s, kv-head h, found through the block
+ * table: logical block t / bs, slot t % bs inside the physical block. */
+static double cache_elem(const orc_args* a, const void* cache, double cscale,
+                         int s, int h, int t, int i) {
+  int32_t phys = a->block_tables[(int64_t)s * a->max_blocks_per_seq + t / a->block_size];
+  int64_t idx = (((int64_t)phys * a->num_kv_heads + h) * a->block_size +
+                 t % a->block_size) * a->head_dim + i;
+  return load_elem(cache, idx, a->kv_dtype) * cscale;
+}
+
+static double logit(const orc_args* a, int s, int hq, int t) {
+  int g = a->num_q_heads / a->num_kv_heads;
+  int hk = hq / g;
+  double dot = 0.0;
+  for (int i = 0; i < a->head_dim; ++i) {
+    double qi = load_elem(a->q, ((int64_t)s * a->num_q_heads + hq) * a->head_dim + i, a->q_dtype);
+    dot += qi * cache_elem(a, a->k_cache, a->k_scale, s, hk, t, i);
+  }
+  return a->scale * dot;
+}
+
+/* softmax weights of one (sequence, q-head) over its context, w[ctx]. */
+static void weights(const orc_args* a, int s, int hq, int t0, int t1, double* z,
+                    double* m_out, double* l_out) {
+  double m = -INFINITY;
+  for (int t = t0; t < t1; ++t) {
+    z[t - t0] = logit(a, s, hq, t);
+    if (z[t - t0] > m) m = z[t - t0];
+  }
+  double l = 0.0;
+  for (int t = t0; t < t1; ++t) {
+    z[t - t0] = exp(z[t - t0] - m);
+    l += z[t - t0];
+  }
+  *m_out = m;
+  *l_out = l;
+}
+
+/* out[S][H_q][d] (double).  A sequence with context length 0 yields zeros. */
+int orc_paged_decode(double* out, const void* q, int q_dtype, const void* k_cache,
+                     const void* v_cache, int kv_dtype,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     int num_seqs, int num_q_heads, int num_kv_heads,
+                     int head_dim, int block_size, int max_blocks_per_seq,
+                     double scale, double k_scale, double v_scale) {
+  if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
+  orc_args a = {q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
+                context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                block_size, max_blocks_per_seq, scale,
+                kv_dtype == ORC_FP8_E4M3 ? k_scale : 1.0,
+                kv_dtype == ORC_FP8_E4M3 ? v_scale : 1.0};
+  int g = num_q_heads / num_kv_heads;
+  int max_ctx = max_blocks_per_seq * block_size;
+  double* w = (double*)malloc(sizeof(double) * (max_ctx > 0 ? max_ctx : 1));
+  if (!w) return -3;
+  for (int s = 0; s < num_seqs; ++s) {
+    int n = context_lens[s];
+    if (n > max_ctx) { free(w); return -2; }
+    for (int hq = 0; hq < num_q_heads; ++hq) {
+      double* o = out + ((int64_t)s * num_q_heads + hq) * head_dim;
+      for (int i = 0; i < head_dim; ++i) o[i] = 0.0;
+      if (n <= 0) continue;
+      double m, l;
+      weights(&a, s, hq, 0, n, w, &m, &l);
+      for (int t = 0; t < n; ++t) {
+        double wt = w[t] / l;
+        for (int i = 0; i < head_dim; ++i)
+          o[i] += wt * cache_elem(&a, v_cache, a.v_scale, s, hq / g, t, i);
+      }
+    }
+  }
+  free(w);
+  return 0;
+}
+
+/* Normalised softmax weights of one (sequence, q-head): w[ctx]. */
+int orc_softmax_weights(double* w, int s, int hq, const void* q, int q_dtype,
+                        const void* k_cache, int kv_dtype,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        int num_seqs, int num_q_heads, int num_kv_heads,
+                        int head_dim, int block_size, int max_blocks_per_seq,
+                        double scale, double k_scale) {
+  orc_args a = {q, q_dtype, k_cache, NULL, kv_dtype, block_tables,
+                context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                block_size, max_blocks_per_seq, scale,
+                kv_dtype == ORC_FP8_E4M3 ? k_scale : 1.0, 1.0};
+  int n = context_lens[s];
+  if (n <= 0) return 0;
+  double m, l;
+  weights(&a, s, hq, 0, n, w, &m, &l);
+  for (int t = 0; t < n; ++t) w[t] /= l;
+  return n;
+}
+
+/* Statistics of one partition [t0, t1) of one (sequence, q-head):
+ *   m = max_t z_t,  l = sum_t exp(z_t - m),  acc = sum_t exp(z_t - m) v_t.
+ * These are the quantities a partitioned evaluation keeps; merging them with
+ * orc_lse_merge must give the direct result. */
+int orc_partition_stats(double* m_out, double* l_out, double* acc, int s, int hq,
+                        int t0, int t1, const void* q, int q_dtype,
+                        const void* k_cache, const void* v_cache, int kv_dtype,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        int num_seqs, int num_q_heads, int num_kv_heads,
+                        int head_dim, int block_size, int max_blocks_per_seq,
+                        double scale, double k_scale, double v_scale) {
+  orc_args a = {q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
+                context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                block_size, max_blocks_per_seq, scale,
+                kv_dtype == ORC_FP8_E4M3 ? k_scale : 1.0,
+                kv_dtype == ORC_FP8_E4M3 ? v_scale : 1.0};
+  int g = num_q_heads / num_kv_heads;
+  for (int i = 0; i < head_dim; ++i) acc[i] = 0.0;
+  if (t1 <= t0) { *m_out = -INFINITY; *l_out = 0.0; return 0; }
+  double* w = (double*)malloc(sizeof(double) * (t1 - t0));
+  if (!w) return -3;
+  weights(&a, s, hq, t0, t1, w, m_out, l_out);
+  for (int t = t0; t < t1; ++t)
+    for (int i = 0; i < head_dim; ++i)
+      acc[i] += w[t - t0] * cache_elem(&a, v_cache, a.v_scale, s, hq / g, t, i);
+  free(w);
+  return 0;
+}
+
+/* Log-sum-exp merge of P partition statistics into one output row:
+ *   M = max_p m_p,  L = sum_p l_p e^(m_p - M),  out = sum_p acc_p e^(m_p - M) / L.
+ * Partitions with l_p == 0 (empty) contribute nothing; all empty gives zeros. */
+void orc_lse_merge(double* out, const double* m, const double* l,
+                   const double* acc, int num_parts, int head_dim) {
+  double M = -INFINITY;
+  for (int p = 0; p < num_parts; ++p)
+    if (l[p] > 0.0 && m[p] > M) M = m[p];
+  for (int i = 0; i < head_dim; ++i) out[i] = 0.0;
+  if (M == -INFINITY) return;
+  double L = 0.0;
+  for (int p = 0; p < num_parts; ++p)
+    if (l[p] > 0.0) L += l[p] * exp(m[p] - M);
+  for (int p = 0; p < num_parts; ++p) {
+    if (l[p] <= 0.0) continue;
+    double f = exp(m[p] - M) / L;
+    for (int i = 0; i < head_dim; ++i) out[i] += f * acc[(int64_t)p * head_dim + i];
+  }
+}

@@ -1,0 +1,154 @@
+"""Plain-Python reference of the host block bookkeeping (block pool).
+
+TEST INFRASTRUCTURE ONLY: used by tests/ to check the native pool bit for bit;
+the product never imports it.
+
+What it models, from the pages:
+  - KV memory is cut into fixed blocks of 16 tokens; a per-sequence block table
+    maps logical block j to any physical block ("Transformer 推理优化：KV Cache、
+    PagedAttention 与 vLLM", sections 3.2-3.3).
+  - Blocks are taken on demand, a new one each time 16 more tokens have been
+    produced ("vLLM推理引擎深度解析", section 2.2), so only the last block of a
+    sequence is partly filled (same page as above, section 3.4).
+  - A pool hands out and takes back blocks in O(1) ("大语言模型推理引擎深度剖析",
+    section 2.2); free blocks sit in a queue ("vLLM推理引擎深度解析", section 2.2).
+  - Sharing and copy-on-write: several tables may point at one physical block;
+    a reference count is kept and a block returns to the free pool when it
+    reaches zero; a shared block is copied before a sequence writes into it
+    ("大语言模型推理引擎深度剖析", section 2.3; "Transformer 推理优化", section 3.5).
+
+Readings where the pages leave a choice:
+  - the free queue is FIFO, initially in the order given (default 0..N-1);
+    a block whose count drops to zero goes to its tail;
+  - a sequence is freed from its last block to its first;
+  - a write into an existing block whose count is above one copies it first
+    (copy-on-write), whether or not the block is full;
+  - an append that cannot get every block it needs fails and changes nothing.
+"""
+from collections import deque
+
+
+class PoolError(Exception):
+    pass
+
+
+class OutOfBlocks(PoolError):
+    pass
+
+
+class RefcountError(PoolError):
+    pass
+
+
+class InvalidArg(PoolError):
+    pass
+
+
+class RefPool:
+    def __init__(self, num_blocks, block_size=16, free_order=None):
+        if num_blocks < 0 or block_size <= 0:
+            raise InvalidArg("bad pool size")
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise InvalidArg("free_order must be a permutation of the block ids")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free = deque(order)
+        self.ref = [0] * num_blocks
+
+    # -- single blocks -------------------------------------------------------
+    def _check(self, b):
+        if not (0 <= b < self.num_blocks):
+            raise InvalidArg(f"block id {b} out of range")
+
+    def alloc(self):
+        if not self.free:
+            raise OutOfBlocks("no free block")
+        b = self.free.popleft()
+        self.ref[b] = 1
+        return b
+
+    def incref(self, b):
+        self._check(b)
+        if self.ref[b] < 1:
+            raise RefcountError(f"incref of free block {b}")
+        self.ref[b] += 1
+
+    def decref(self, b):
+        self._check(b)
+        if self.ref[b] < 1:
+            raise RefcountError(f"decref of free block {b}")
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self.free.append(b)
+
+    def refcount(self, b):
+        self._check(b)
+        return self.ref[b]
+
+    def num_free(self):
+        return len(self.free)
+
+    def free_list(self):
+        return list(self.free)
+
+    # -- sequences -----------------------------------------------------------
+    def blocks_for(self, n_tokens):
+        """Blocks needed to hold n tokens: ceil(n / block_size)."""
+        return -(-n_tokens // self.block_size)
+
+    def seq_create(self, prompt_len, cap=None):
+        table = []
+        self.seq_append_slots(table, 0, prompt_len, cap)
+        return table
+
+    def seq_fork(self, table):
+        for b in table:
+            self._check(b)
+            if self.ref[b] < 1:
+                raise RefcountError(f"fork of free block {b}")
+        for b in table:
+            self.ref[b] += 1
+        return list(table)
+
+    def seq_append_slots(self, table, cur_len, n_new, cap=None):
+        """Slots for positions cur_len .. cur_len+n_new-1, growing `table`
+        in place.  Returns (slots, cow_pairs) where each cow pair (src, dst)
+        asks the caller to copy physical block src into dst."""
+        bs = self.block_size
+        if cur_len < 0 or n_new < 0:
+            raise InvalidArg("negative length")
+        if n_new == 0:
+            return [], []
+        first, last = cur_len // bs, (cur_len + n_new - 1) // bs
+        if first > len(table):
+            raise InvalidArg("positions leave a gap after the table")
+        if cap is not None and last + 1 > cap:
+            raise InvalidArg("table capacity exceeded")
+        needed = 0
+        for bi in range(first, last + 1):
+            if bi >= len(table) or self.ref[table[bi]] > 1:
+                needed += 1
+        if needed > len(self.free):
+            raise OutOfBlocks(f"need {needed} blocks, {len(self.free)} free")
+        cows = []
+        for bi in range(first, last + 1):
+            if bi < len(table):
+                old = table[bi]
+                if self.ref[old] > 1:
+                    new = self.alloc()
+                    cows.append((old, new))
+                    self.decref(old)
+                    table[bi] = new
+            else:
+                table.append(self.alloc())
+        slots = [table[p // bs] * bs + p % bs for p in range(cur_len, cur_len + n_new)]
+        return slots, cows
+
+    def seq_free(self, table):
+        for b in table:
+            self._check(b)
+            if self.ref[b] < 1:
+                raise RefcountError(f"free of free block {b}")
+        for b in reversed(table):
+            self.decref(b)
