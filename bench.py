@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X.
+
+A step is one pass of the whole decode hot path over one batch: the cache
+append of every sequence's new token (slot_mapping write) followed by paged
+decode attention over each sequence's context (partition kernel, plus the
+log-sum-exp reduction kernel when the context is split).  The block tables,
+context lengths and slot mapping come from the native block pool, built
+before the timed region (its host cost per step is measured separately).
+
+Prints one JSON line.  Inputs are seeded synthetic data of the workload's
+shape.  To keep every timed step reading cold HBM rather than the 256 MB
+Infinity Cache, the caches are replicated and the steps rotate over the
+replicas.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+MALL_BYTES = 256 * 2 ** 20      # Infinity Cache
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2_qwen3_8b_bf16")
+    ap.add_argument("--algo", default="auto", choices=["auto", "vector", "mfma"])
+    ap.add_argument("--partition", type=int, default=-1, help="-1: the workload's own setting")
+    ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 4x the MALL")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also time the other workloads and add them under 'other_configs'")
+    return ap.parse_args()
+
+
+def kv_elem_bytes(kv):
+    return {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[kv]
+
+
+def setup(cfg, dev):
+    import numpy as np
+    import torch
+    import paged_kv_cache_363_amd as pkv
+    from synth import gen
+    from synth.scenario import build_state, table_array
+
+    ctx = gen.context_lens(cfg)
+    nb = gen.num_blocks(cfg, ctx)
+    pool = pkv.BlockPool(nb, cfg.block_size, gen.free_order(cfg, nb))
+    t0 = time.perf_counter()
+    st = build_state(cfg, pool, ctx)
+    t_pool = time.perf_counter() - t0
+    kv_t = torch.uint8 if cfg.kv_dtype == "fp8" else gen.TORCH_DTYPE[cfg.kv_dtype]
+    shape = (nb, cfg.num_kv_heads, cfg.block_size, cfg.head_dim)
+    kc = torch.zeros(shape, dtype=kv_t, device=dev)
+    vc = torch.zeros(shape, dtype=kv_t, device=dev)
+    k_scale, v_scale = gen.kv_scales(cfg, ctx)
+    for s, p0, slots in st["prefill"]:
+        if not slots:
+            continue
+        k, v = gen.seq_kv(cfg, s, p0 + len(slots))
+        pkv.paged_cache_append(kc, vc, k[p0:].to(dev), v[p0:].to(dev),
+                               torch.tensor(slots, dtype=torch.int64, device=dev),
+                               k_scale, v_scale)
+    kn, vn = gen.step_kv(cfg)
+    torch.cuda.synchronize()
+    return dict(ctx=ctx, nb=nb, pool=pool, state=st, k_cache=kc, v_cache=vc,
+                block_tables=torch.from_numpy(table_array(cfg, st["tables"])).to(dev),
+                context_lens=torch.from_numpy(ctx).to(dev), q=gen.queries(cfg).to(dev),
+                k_new=kn.to(dev), v_new=vn.to(dev),
+                slots=torch.from_numpy(st["step_slots"]).to(dev),
+                k_scale=k_scale, v_scale=v_scale, t_pool_build=t_pool)
+
+
+def host_bookkeeping_us(cfg, st):
+    """Host time per decode step of the block bookkeeping: one append_slots
+    call per sequence on a copy of the tables (the real step's a1)."""
+    import paged_kv_cache_363_amd as pkv
+    from synth import gen
+    nb = st["nb"]
+    pool = pkv.BlockPool(nb, cfg.block_size, gen.free_order(cfg, nb))
+    from synth.scenario import build_state
+    ctx = st["ctx"]
+    # rebuild to the pre-step state but stop before the step's own append
+    cfg_pre = cfg
+    state = build_state(cfg_pre, pool, ctx)
+    tables = [list(t) for t in state["tables"]]
+    reps = 20
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        for s in range(cfg.num_seqs):
+            pool.seq_append_slots(tables[s], int(ctx[s]) - 1, 1, cfg.max_blocks_per_seq)
+    return (time.perf_counter() - t0) / reps * 1e6
+
+
+def time_config(cfg, args, dev, partition, with_cpu=True):
+    import numpy as np
+    import torch
+    import paged_kv_cache_363_amd as pkv
+
+    st = setup(cfg, dev)
+    eb = kv_elem_bytes(cfg.kv_dtype)
+    ctx = st["ctx"].astype(np.int64)
+    kv_bytes = int(ctx.sum()) * 2 * cfg.num_kv_heads * cfg.head_dim * eb
+    cache_bytes = 2 * st["k_cache"].numel() * st["k_cache"].element_size()
+    R = args.replicas or max(1, min(8, math.ceil(4 * MALL_BYTES / max(kv_bytes, 1))))
+    kcs, vcs = [st["k_cache"]], [st["v_cache"]]
+    for _ in range(R - 1):
+        kcs.append(st["k_cache"].clone())
+        vcs.append(st["v_cache"].clone())
+    ps = partition
+    ws = pkv.alloc_workspace(st["q"], st["k_cache"], st["block_tables"], ps)
+    out = torch.empty_like(st["q"])
+    stream = torch.cuda.current_stream()
+
+    def step(i, evs=None):
+        r = i % R
+        pkv.paged_cache_append(kcs[r], vcs[r], st["k_new"], st["v_new"], st["slots"],
+                               st["k_scale"], st["v_scale"])
+        pkv.paged_decode_attention(st["q"], kcs[r], vcs[r], st["block_tables"],
+                                   st["context_lens"], cfg.scale, st["k_scale"], st["v_scale"],
+                                   partition_size=ps, out=out, workspace=ws, algo=args.algo,
+                                   events=evs)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for trio in evs:       # create the underlying HIP events before handing them over
+        for e in trio:
+            e.record(stream)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    part_ms = [a.elapsed_time(b) for a, b, _ in evs]
+    red_ms = [b.elapsed_time(c) for _, b, c in evs]
+    part_avg = sum(part_ms) / K
+    red_avg = sum(red_ms) / K
+    step_ms = total_ms / K
+    achieved = kv_bytes / (part_avg * 1e-3) / 1e9
+    res = dict(
+        config=cfg.name, kv_bytes=kv_bytes, replicas=R, cache_bytes_per_replica=cache_bytes,
+        partition=pkv.decode_partition_size(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads,
+                                            cfg.head_dim, cfg.max_blocks_per_seq, 0, ps),
+        algo=args.algo if args.algo != "auto" else pkv.decode_algo_for(
+            cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+            pkv.api._DT[st["q"].dtype], pkv.api._DT[st["k_cache"].dtype]),
+        ms_per_step=step_ms, wall_ms_per_step=wall / K * 1e3,
+        decode_kernel_ms=part_avg, reduce_kernel_ms=red_avg,
+        step_gbs=kv_bytes / (step_ms * 1e-3) / 1e9,
+        decode_kernel_gbs=achieved, tokens_per_s=cfg.num_seqs / (step_ms * 1e-3),
+        t_pool_build_s=st["t_pool_build"])
+    res["host_bookkeeping_us_per_step"] = host_bookkeeping_us(cfg, st)
+    if with_cpu and args.cpu_budget > 0:
+        res["cpu_baseline"] = cpu_baseline(cfg, st, args.cpu_budget, out)
+    return res
+
+
+def cpu_baseline(cfg, st, budget_s, gpu_out):
+    """The fp64 oracle, single-threaded, on a bounded sample of the same
+    workload's sequences (longest context first, until the time budget is
+    spent): oracle KV GB/s and decode tokens/s.  The sampled rows are also
+    compared with the GPU output of the timed steps."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from harness import allclose_report, oracle_setup
+    from oracle import oracle as orc
+    from synth import gen
+    ctx = st["ctx"]
+    est = int(math.ceil(budget_s / max(1e-9, 2.5e-8 * cfg.num_q_heads * cfg.head_dim *
+                                       float(ctx.max())))) + 1
+    order = [int(s) for s in np.argsort(-ctx, kind="stable")][:max(1, est)]
+    o = oracle_setup(cfg, order)
+    qb = gen.bits(o["q"])
+    eb = kv_elem_bytes(cfg.kv_dtype)
+    done, t_used, nbytes, worst, ok_all = 0, 0.0, 0, 0.0, True
+    for s in order:
+        t0 = time.perf_counter()
+        ref = orc.paged_decode(qb[[s]], cfg.q_dtype, o["k_cache"], o["v_cache"], cfg.kv_dtype,
+                               o["block_tables"][[s]], o["ctx"][[s]], cfg.scale, o["k_scale"],
+                               o["v_scale"])
+        t_used += time.perf_counter() - t0
+        done += 1
+        nbytes += int(ctx[s]) * 2 * cfg.num_kv_heads * cfg.head_dim * eb
+        got = gpu_out[s:s + 1].float().cpu().numpy().astype(np.float64)
+        ok, _, err = allclose_report(got, ref, 2e-3, 1e-2)
+        ok_all &= ok
+        worst = max(worst, err)
+        if t_used >= budget_s:
+            break
+    return {"value": round(nbytes / t_used / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "tokens_per_s": round(done / t_used, 3),
+            "sample": f"{done} of {cfg.num_seqs} sequences of {cfg.name} (longest first), all "
+                      f"q-heads, {t_used:.1f} s of single-threaded fp64 oracle",
+            "gpu_rows_match_oracle": ok_all, "max_abs_err": worst}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the decode path has "
+                                   "no multi-GPU mode in this build", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_363_amd as pkv  # noqa: F401  (fails loudly if libpkv.so is missing)
+    from synth import CONFIGS
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = "cuda:0"
+    cfg = CONFIGS[args.config]
+    ps = cfg.partition_size if args.partition < 0 else args.partition
+    res = time_config(cfg, args, dev, ps)
+    line = {
+        "metric": "paged-decode effective KV GB/s (% of MI355X HBM peak) and decode tokens/s",
+        "value": round(res["step_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.kv_dtype if cfg.kv_dtype == cfg.q_dtype else f"{cfg.q_dtype}+{cfg.kv_dtype}-kv",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "description": cfg.description,
+                   "num_seqs": cfg.num_seqs, "num_q_heads": cfg.num_q_heads,
+                   "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
+                   "block_size": cfg.block_size, "partition": res["partition"],
+                   "algo": res["algo"], "kv_bytes_per_step": res["kv_bytes"],
+                   "replicas": res["replicas"]},
+        "decode_tokens_per_s": round(res["tokens_per_s"], 1),
+        "pct_hbm_peak_step": round(100 * res["step_gbs"] / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(res["decode_kernel_gbs"], 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(res["decode_kernel_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "kernel": f"decode_{res['algo']}_kernel",
+                     "kernel_ms": round(res["decode_kernel_ms"], 5)},
+        "reduce_kernel_ms": round(res["reduce_kernel_ms"], 5),
+        "host_bookkeeping_us_per_step": round(res["host_bookkeeping_us_per_step"], 1),
+        "cpu_baseline": res.get("cpu_baseline"),
+    }
+    if args.all_configs:
+        others = {}
+        for name, c in CONFIGS.items():
+            if name == cfg.name:
+                continue
+            r = time_config(c, args, dev, c.partition_size, with_cpu=False)
+            others[name] = {"step_gbs": round(r["step_gbs"], 2),
+                            "decode_kernel_gbs": round(r["decode_kernel_gbs"], 2),
+                            "frac": round(r["decode_kernel_gbs"] / HBM_PEAK_GBS, 4),
+                            "ms_per_step": round(r["ms_per_step"], 5),
+                            "decode_kernel_ms": round(r["decode_kernel_ms"], 5),
+                            "tokens_per_s": round(r["tokens_per_s"], 1), "algo": r["algo"],
+                            "partition": r["partition"]}
+            del r
+            torch.cuda.empty_cache()
+        line["other_configs"] = others
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

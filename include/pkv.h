@@ -1,0 +1,265 @@
+/*
+ * pkv.h -- C ABI of the paged KV-cache decode library for AMD MI355X (gfx950).
+ *
+ * The library implements the decode-side hot path of PagedAttention: the KV
+ * cache lives in a pool of fixed 16-token blocks, each sequence reaches its
+ * blocks through a block table that maps logical block j to any physical
+ * block, and one decode step appends the new token's K/V rows and then runs
+ * single-query attention over the whole context.
+ *
+ * Sources for the operations (page title, section):
+ *   - "Transformer 推理优化：KV Cache、PagedAttention 与 vLLM": 2.2 (only the
+ *     new token's K and V are computed and appended), 2.5 (KV bytes per
+ *     token), 3.2-3.3 (16-token blocks, block table, non-contiguous blocks),
+ *     3.5 (copy-on-write of shared blocks).
+ *   - "KV Cache 与 PageAttention深度实战": 1.2 (Attention(Q,K,V) =
+ *     softmax(QK^T/sqrt(d_k))V; the decode output attends over
+ *     [K_prefix, K_t], [V_prefix, V_t]), 3.2 (attention gathers K/V through
+ *     the block table).
+ *   - "大语言模型推理引擎深度剖析": 2.2 (O(1) block allocation and release),
+ *     2.3 (shared prefix blocks, reference counts, copy before write),
+ *     4.2 (FP8 E4M3 with range +-448), 4.3 (FP8 KV cache, dequantised for
+ *     compute).
+ *   - "vLLM推理引擎深度解析": 2.2 (block pool, block tables, free-block queue,
+ *     a new block every 16 generated tokens).
+ *
+ * Conventions shared by every entry point:
+ *   - Every call returns a pkv_status; nothing throws across the ABI.  On an
+ *     error, pkv_last_error() returns a message for the calling thread.
+ *   - Device pointers are caller-owned device memory (for example torch
+ *     tensors).  The library never allocates or frees device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     GPU calls are asynchronous on that stream; argument errors are reported
+ *     synchronously before anything is launched.
+ *   - Cache layout: k_cache and v_cache are separate arrays
+ *       [num_blocks][num_kv_heads][block_size][head_dim]
+ *     so that the 16 x head_dim tile of one (block, kv-head) is contiguous.
+ *     Token t of a sequence lives in physical block block_tables[s][t / 16]
+ *     at offset t % 16.  slot = physical_block * 16 + offset.
+ *   - q-head h attends with kv-head h / (num_q_heads / num_kv_heads).
+ *   - FP8 caches hold OCP E4M3FN codes with one scale per tensor (k_scale for
+ *     K, v_scale for V): real value = decode(code) * scale.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,   /* bad pointer, size, shape or id */
+  PKV_ERR_UNSUPPORTED = 2,   /* valid but not implemented (block size, head dim, dtype mix) */
+  PKV_ERR_OUT_OF_BLOCKS = 3, /* the pool cannot satisfy the request; nothing changed */
+  PKV_ERR_REFCOUNT = 4,      /* reference-count misuse (decref of a free block, ...) */
+  PKV_ERR_HIP = 5,           /* a HIP runtime call or kernel launch failed */
+  PKV_ERR_WORKSPACE = 6      /* workspace missing or smaller than pkv_decode_workspace_size */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 } pkv_dtype;
+
+/* Which decode kernel family runs.  AUTO picks per shape (see
+ * pkv_decode_algo_for).  VECTOR: per-lane fp32 arithmetic with wavefront
+ * reductions.  MFMA: QK^T and PV on the matrix cores (16-bit or FP8 caches,
+ * 16-bit q). */
+typedef enum { PKV_ALGO_AUTO = 0, PKV_ALGO_VECTOR = 1, PKV_ALGO_MFMA = 2 } pkv_algo;
+
+/* Message describing the last error on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+const char* pkv_status_string(int32_t status);
+/* Library version: major*10000 + minor*100 + patch. */
+int32_t pkv_version(void);
+
+/* --------------------------------------------------------------- sizes -- */
+
+/* KV-cache bytes per token of a whole model: 2 x layers x kv_heads x head_dim
+ * x element bytes ("Transformer 推理优化", section 2.5; e.g. 147,456 for 36
+ * layers, 8 KV heads, head_dim 128, fp16).  Returns 0 on a bad dtype. */
+uint64_t pkv_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                                int32_t dtype);
+
+/* --------------------------------------------------------- cache append -- */
+
+/* Write the K/V rows of num_tokens new tokens into the paged caches.
+ *   k_new, v_new : device, [num_tokens][num_kv_heads][head_dim] of new_dtype,
+ *                  contiguous.
+ *   slot_mapping : device int64[num_tokens]; slot = block * block_size + offset.
+ *                  A negative slot skips that token (padding).  Slots at or
+ *                  beyond num_blocks * block_size are also skipped (the kernel
+ *                  never writes out of bounds).  Slots must be distinct within
+ *                  one call; the block pool guarantees this.
+ *   dtypes       : kv_dtype == new_dtype (bit copy), or kv_dtype == FP8_E4M3
+ *                  with new_dtype in {F32, F16, BF16}: each element becomes the
+ *                  E4M3 code nearest to the binary32 product x * (1/scale),
+ *                  ties to even, saturating at +-448, NaN -> 0x7F; 1/scale is
+ *                  rounded to binary32 first.  k_scale/v_scale must be > 0 and
+ *                  finite for FP8 and are ignored otherwise.
+ *   block_size must be 16; head_dim a multiple of 8 in [8, 256]. */
+pkv_status pkv_paged_cache_append(void* k_cache, void* v_cache, const void* k_new,
+                                  const void* v_new, const int64_t* slot_mapping,
+                                  int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks, int32_t new_dtype,
+                                  int32_t kv_dtype, float k_scale, float v_scale, void* stream);
+
+/* ------------------------------------------------------ decode attention -- */
+
+/* Effective partition size (tokens) a decode call with these arguments will
+ * use: partition_size itself if > 0 (it must be a multiple of 16), else the
+ * library's choice.  A call whose max_blocks_per_seq * 16 fits in one
+ * partition runs single-pass and needs no workspace.  Returns -1 on bad
+ * arguments. */
+int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_blocks_per_seq, int32_t kv_dtype,
+                                  int32_t partition_size);
+
+/* Bytes of device workspace a decode call with these arguments needs (0 for
+ * single-pass).  Layout: float m[S][H_q][P], float l[S][H_q][P],
+ * float acc[S][H_q][P][head_dim] (each part 256-byte aligned), where
+ * P = ceil(max_blocks_per_seq * 16 / partition).  Returns SIZE_MAX on bad
+ * arguments. */
+size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t kv_dtype,
+                                 int32_t partition_size);
+
+/* Kernel family AUTO resolves to for these arguments (PKV_ALGO_VECTOR or
+ * PKV_ALGO_MFMA), or -1 if the combination is unsupported. */
+int32_t pkv_decode_algo_for(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t q_dtype, int32_t kv_dtype);
+
+/* Single-query paged attention for one decode step ("KV Cache 与
+ * PageAttention深度实战", sections 1.2 and 3.2):
+ *   out[s][h][:] = sum_t softmax_t(scale * q[s][h] . K_s[t]) * V_s[t]
+ * over t < context_lens[s], K_s[t] and V_s[t] read through block_tables.
+ *   out          : device, [num_seqs][num_q_heads][head_dim] of q_dtype,
+ *                  rounded to nearest even.  A sequence with context length
+ *                  <= 0 gets zeros.
+ *   q            : device, [num_seqs][num_q_heads][head_dim] of q_dtype.
+ *   block_tables : device int32[num_seqs][max_blocks_per_seq]; only the first
+ *                  ceil(context_lens[s] / 16) entries of a row are read.  An
+ *                  entry outside [0, num_blocks) is skipped (its tokens get no
+ *                  weight) instead of being read.
+ *   context_lens : device int32[num_seqs], tokens per sequence after this
+ *                  step's append; values above max_blocks_per_seq * 16 are
+ *                  clamped to it.
+ *   dtypes       : (q, kv) in {(F32,F32), (F16,F16), (BF16,BF16),
+ *                  (F16,FP8_E4M3), (BF16,FP8_E4M3)}; k_scale/v_scale apply to
+ *                  FP8 caches only.
+ *   shape limits : block_size 16; head_dim 64 or 128; num_q_heads a multiple
+ *                  of num_kv_heads.
+ *   partition_size: 0 = library's choice, else a multiple of 16 in [16, 2^20].
+ *   workspace    : device memory of at least pkv_decode_workspace_size(...)
+ *                  bytes (may be NULL when that is 0).  Its contents on entry
+ *                  do not matter. */
+pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, float scale, int32_t q_dtype,
+                                      int32_t kv_dtype, float k_scale, float v_scale,
+                                      int32_t partition_size, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* Same as pkv_paged_decode_attention with an explicit kernel family. */
+pkv_status pkv_paged_decode_attention_algo(void* out, const void* q, const void* k_cache,
+                                           const void* v_cache, const int32_t* block_tables,
+                                           const int32_t* context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, int32_t max_blocks_per_seq,
+                                           float scale, int32_t q_dtype, int32_t kv_dtype,
+                                           float k_scale, float v_scale, int32_t partition_size,
+                                           void* workspace, size_t workspace_bytes,
+                                           int32_t algo, void* stream);
+
+/* Same as pkv_paged_decode_attention_algo, and records caller-created HIP
+ * events (hipEvent_t passed as void*, NULL = skip) on `stream`: ev_begin
+ * before the partition kernel, ev_mid after it, ev_end after the reduction
+ * kernel (right after the partition kernel when the call is single-pass).
+ * For timing the kernels from outside the library. */
+pkv_status pkv_paged_decode_attention_profiled(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, float scale, int32_t q_dtype,
+    int32_t kv_dtype, float k_scale, float v_scale, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, int32_t algo, void* stream, void* ev_begin, void* ev_mid,
+    void* ev_end);
+
+/* ---------------------------------------------------- copy-on-write copy -- */
+
+/* Copy whole physical blocks, K and V: for i < num_pairs, block
+ * src_dst_pairs[2i] is copied into block src_dst_pairs[2i+1] ("大语言模型推理
+ * 引擎深度剖析", section 2.3: a shared block is copied before it is written).
+ *   src_dst_pairs : device int32[num_pairs][2]; pairs with an id outside
+ *                   [0, num_blocks) are skipped.  Destinations must be
+ *                   distinct and no destination may be a source.
+ *   block_bytes   : bytes of one physical block of one cache
+ *                   (num_kv_heads * block_size * head_dim * element bytes),
+ *                   a multiple of 16. */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
+                           int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------ host block pool -- */
+
+/* Host-side pool of physical block ids with reference counts ("vLLM推理引擎
+ * 深度解析", section 2.2; "大语言模型推理引擎深度剖析", sections 2.2-2.3).
+ * Free ids wait in a FIFO queue (initially free_order, or 0..num_blocks-1
+ * when free_order is NULL); a block whose count falls to 0 joins its tail.
+ * Every operation is O(1) per block touched.  A pool is not thread-safe:
+ * one owner at a time.  Block tables are caller-owned host int32 arrays. */
+typedef struct pkv_pool pkv_pool;
+
+pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                           pkv_pool** out);
+void pkv_pool_destroy(pkv_pool* pool);
+/* Take the block at the head of the free queue (count becomes 1). */
+pkv_status pkv_pool_alloc(pkv_pool* pool, int32_t* block_out);
+/* Count += 1 for a block in use; PKV_ERR_REFCOUNT for a free block. */
+pkv_status pkv_pool_incref(pkv_pool* pool, int32_t block);
+/* Count -= 1; at 0 the block joins the free queue.  PKV_ERR_REFCOUNT for a
+ * free block. */
+pkv_status pkv_pool_decref(pkv_pool* pool, int32_t block);
+/* Count of a block (0 = free), or -1 for an id out of range. */
+int32_t pkv_pool_refcount(const pkv_pool* pool, int32_t block);
+int32_t pkv_pool_num_free(const pkv_pool* pool);
+int32_t pkv_pool_num_blocks(const pkv_pool* pool);
+int32_t pkv_pool_block_size(const pkv_pool* pool);
+/* Copy the free queue, head first, into out[0..cap); *n receives its length.
+ * PKV_ERR_INVALID_ARG if cap is too small (nothing written then). */
+pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n);
+
+/* A new table holding ceil(prompt_len / block_size) freshly allocated blocks.
+ * table: host int32[cap]; *nblocks receives the count. */
+pkv_status pkv_seq_create(pkv_pool* pool, int32_t prompt_len, int32_t* table, int32_t cap,
+                          int32_t* nblocks);
+/* Share every block of a table with a new sequence: each count += 1.  The
+ * caller copies the table itself. */
+pkv_status pkv_seq_fork(pkv_pool* pool, const int32_t* table, int32_t nblocks);
+/* Slots for the n_new positions cur_len .. cur_len+n_new-1 of a sequence whose
+ * table is table[0..*nblocks).  A position past the table takes a new block
+ * (a new block every block_size tokens); a position in an existing block whose
+ * count is above 1 first gets a private copy: a new block replaces it in the
+ * table, the old count drops by one and (src, dst) is appended to
+ * cow_pairs[2*k], cow_pairs[2*k+1] for the caller to copy on the device with
+ * pkv_copy_blocks.  slots_out: host int64[n_new].  cow_pairs: host
+ * int32[2*cow_cap] (may be NULL if cow_cap is 0); *n_cow receives the count.
+ * All-or-nothing: PKV_ERR_OUT_OF_BLOCKS (pool too small),
+ * PKV_ERR_INVALID_ARG (gap after the table, table capacity or cow_cap too
+ * small) leave the pool and the table unchanged. */
+pkv_status pkv_seq_append_slots(pkv_pool* pool, int32_t* table, int32_t* nblocks, int32_t cap,
+                                int32_t cur_len, int32_t n_new, int64_t* slots_out,
+                                int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow);
+/* Release a sequence: decref its blocks from the last to the first. */
+pkv_status pkv_seq_free(pkv_pool* pool, const int32_t* table, int32_t nblocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

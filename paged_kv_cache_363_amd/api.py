@@ -1,0 +1,133 @@
+"""torch-facing binding of the C ABI: argument marshalling only.
+
+Tensors supply device memory and the current HIP stream; every step of the
+decode path runs in the library's kernels.  FP8 caches are uint8 (or
+torch.float8_e4m3fn) tensors holding OCP E4M3FN codes.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import check, lib
+
+_DT = {torch.float32: _lib.PKV_F32, torch.float16: _lib.PKV_F16,
+       torch.bfloat16: _lib.PKV_BF16, torch.uint8: _lib.PKV_FP8_E4M3,
+       torch.float8_e4m3fn: _lib.PKV_FP8_E4M3}
+_ALGO = {"auto": _lib.PKV_ALGO_AUTO, "vector": _lib.PKV_ALGO_VECTOR, "mfma": _lib.PKV_ALGO_MFMA}
+BLOCK_SIZE = 16
+
+
+def dtype_code(t):
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _stream(t, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def kv_bytes_per_token(layers, kv_heads, head_dim, dtype):
+    code = dtype if isinstance(dtype, int) else _DT[dtype]
+    return int(lib().pkv_kv_bytes_per_token(layers, kv_heads, head_dim, code))
+
+
+def paged_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping, k_scale=1.0, v_scale=1.0,
+                       stream=None):
+    """Write k_new/v_new [T][H_kv][d] into the caches [NB][H_kv][16][d] at
+    slot_mapping[T] (int64 device tensor; negative = skip)."""
+    nb, hkv, bs, d = k_cache.shape
+    T = slot_mapping.shape[0]
+    if tuple(k_new.shape) != (T, hkv, d) or tuple(v_new.shape) != (T, hkv, d):
+        raise ValueError(f"k_new/v_new must be [{T}, {hkv}, {d}]")
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    check(lib().pkv_paged_cache_append(
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_new, "k_new"),
+        _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"), T, hkv, d, bs, nb,
+        dtype_code(k_new), dtype_code(k_cache), float(k_scale), float(v_scale),
+        _stream(k_cache, stream)))
+
+
+def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                          kv_dtype=_lib.PKV_BF16, partition_size=0):
+    return int(lib().pkv_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                               max_blocks_per_seq, kv_dtype, partition_size))
+
+
+def decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                          kv_dtype=_lib.PKV_BF16, partition_size=0):
+    n = lib().pkv_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                        max_blocks_per_seq, kv_dtype, partition_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise _lib.InvalidArg(_lib.PKV_ERR_INVALID_ARG, "bad decode workspace arguments")
+    return int(n)
+
+
+def decode_algo_for(num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype):
+    a = int(lib().pkv_decode_algo_for(num_q_heads, num_kv_heads, head_dim, q_dtype, kv_dtype))
+    return {1: "vector", 2: "mfma"}.get(a)
+
+
+def alloc_workspace(q, k_cache, block_tables, partition_size=0):
+    S, hq, d = q.shape
+    n = decode_workspace_size(S, hq, k_cache.shape[1], d, block_tables.shape[1],
+                              dtype_code(k_cache), partition_size)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+
+
+def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale=1.0,
+                           v_scale=1.0, partition_size=0, out=None, workspace=None, algo="auto",
+                           stream=None, events=None):
+    """out[S][H_q][d] (q dtype) = softmax(scale * q K^T) V over each sequence's
+    context_lens[s] tokens, K/V gathered through block_tables [S][MB] (int32).
+    events: optional (begin, mid, end) torch.cuda.Event triple recorded around
+    the partition kernel and the reduction kernel."""
+    S, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables/context_lens must have one row per sequence")
+    mb = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(q, k_cache, block_tables, partition_size)
+    evs = [None, None, None]
+    if events is not None:
+        evs = [ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events]
+    check(lib().pkv_paged_decode_attention_profiled(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, hq, hkv, d,
+        bs, nb, mb, float(scale), dtype_code(q), dtype_code(k_cache), float(k_scale),
+        float(v_scale), int(partition_size), _dev(workspace, "workspace"), workspace.numel(),
+        _ALGO[algo], _stream(q, stream), *evs))
+    return out
+
+
+def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
+    """Copy physical block pairs[i][0] into pairs[i][1] in both caches
+    (src_dst_pairs: int32 device tensor [n][2])."""
+    nb = k_cache.shape[0]
+    block_bytes = k_cache[0].numel() * k_cache.element_size()
+    if src_dst_pairs.dtype != torch.int32:
+        raise TypeError("src_dst_pairs must be int32")
+    n = src_dst_pairs.shape[0]
+    check(lib().pkv_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                _dev(src_dst_pairs, "src_dst_pairs"), n, nb, block_bytes,
+                                _stream(k_cache, stream)))

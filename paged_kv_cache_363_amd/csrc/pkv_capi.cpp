@@ -1,0 +1,342 @@
+// C ABI entry points: argument checks, partition and workspace sizing,
+// kernel-family choice and launches.  Nothing here computes attention; every
+// step of the decode path runs in the HIP kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+static thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static bool valid_dtype(int32_t dt) { return dt >= PKV_F32 && dt <= PKV_FP8_E4M3; }
+
+// (q, kv) dtype pairs the decode kernels implement.
+static bool decode_pair_ok(int32_t q, int32_t kv) {
+  if (q == PKV_F32) return kv == PKV_F32;
+  if (q == PKV_F16) return kv == PKV_F16 || kv == PKV_FP8_E4M3;
+  if (q == PKV_BF16) return kv == PKV_BF16 || kv == PKV_FP8_E4M3;
+  return false;
+}
+
+static int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx) {
+  // Enough workgroups to cover 256 CUs several times over, without cutting
+  // contexts into slivers whose partials cost more than they save.
+  int32_t ps = 512;
+  while (ps > 128) {
+    const int64_t units = (int64_t)num_seqs * num_kv_heads * ((max_ctx + ps - 1) / ps);
+    if (units >= 2048) break;
+    ps /= 2;
+  }
+  return ps;
+}
+
+static int32_t resolve_algo(int32_t g, int32_t q, int32_t kv) {
+  const bool mfma_ok = (q == PKV_F16 || q == PKV_BF16) && (kv == q || kv == PKV_FP8_E4M3);
+  return (mfma_ok && g >= 4) ? PKV_ALGO_MFMA : PKV_ALGO_VECTOR;
+}
+
+struct Plan {
+  int32_t partition;
+  int32_t num_parts;
+  size_t ws_bytes;
+  size_t off_l, off_acc;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static bool make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t max_blocks_per_seq, int32_t partition_size,
+                      Plan* plan) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_blocks_per_seq < 0 || partition_size < 0)
+    return false;
+  if (partition_size > 0 && (partition_size % kBlockSize != 0 || partition_size > kMaxPartition))
+    return false;
+  const int32_t max_ctx = max_blocks_per_seq * kBlockSize;
+  const int32_t ps = partition_size > 0 ? partition_size
+                                        : choose_partition(num_seqs, num_kv_heads, max_ctx);
+  plan->partition = ps;
+  plan->num_parts = max_ctx <= ps ? 1 : (max_ctx + ps - 1) / ps;
+  if (plan->num_parts == 1) {
+    plan->ws_bytes = 0;
+    plan->off_l = plan->off_acc = 0;
+    return true;
+  }
+  const size_t rows = (size_t)num_seqs * num_q_heads * plan->num_parts;
+  const size_t bm = align256(rows * sizeof(float));
+  plan->off_l = bm;
+  plan->off_acc = 2 * bm;
+  plan->ws_bytes = 2 * bm + align256(rows * head_dim * sizeof(float));
+  return true;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+const char* pkv_status_string(int32_t st) {
+  switch (st) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported";
+    case PKV_ERR_OUT_OF_BLOCKS: return "out of blocks";
+    case PKV_ERR_REFCOUNT: return "reference count error";
+    case PKV_ERR_HIP: return "HIP error";
+    case PKV_ERR_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+int32_t pkv_version(void) { return 100; }
+
+uint64_t pkv_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                                int32_t dtype) {
+  if (!valid_dtype(dtype) || layers < 0 || kv_heads < 0 || head_dim < 0) return 0;
+  return 2ull * (uint64_t)layers * (uint64_t)kv_heads * (uint64_t)head_dim *
+         (uint64_t)elem_bytes(dtype);
+}
+
+pkv_status pkv_paged_cache_append(void* k_cache, void* v_cache, const void* k_new,
+                                  const void* v_new, const int64_t* slot_mapping,
+                                  int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks, int32_t new_dtype,
+                                  int32_t kv_dtype, float k_scale, float v_scale, void* stream) {
+  clear_error();
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
+    return fail(PKV_ERR_INVALID_ARG, "cache_append: bad sizes");
+  if (block_size != kBlockSize)
+    return fail(PKV_ERR_UNSUPPORTED, "cache_append: block_size must be 16 (got %d)", block_size);
+  if (head_dim < 8 || head_dim > 256 || head_dim % 8 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "cache_append: head_dim must be a multiple of 8 in [8,256]");
+  if (!valid_dtype(new_dtype) || !valid_dtype(kv_dtype))
+    return fail(PKV_ERR_INVALID_ARG, "cache_append: bad dtype");
+  if (new_dtype == PKV_FP8_E4M3)
+    return fail(PKV_ERR_UNSUPPORTED, "cache_append: new rows must be f32, f16 or bf16");
+  if (kv_dtype != new_dtype && kv_dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_UNSUPPORTED, "cache_append: kv dtype must equal the new rows' dtype or be FP8");
+  float k_inv = 1.0f, v_inv = 1.0f;
+  if (kv_dtype == PKV_FP8_E4M3) {
+    if (!(k_scale > 0.0f) || !std::isfinite(k_scale) || !(v_scale > 0.0f) ||
+        !std::isfinite(v_scale))
+      return fail(PKV_ERR_INVALID_ARG, "cache_append: FP8 scales must be finite and > 0");
+    k_inv = 1.0f / k_scale;
+    v_inv = 1.0f / v_scale;
+  }
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "cache_append: NULL pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_ERR_INVALID_ARG, "cache_append: caches and new rows must be 16-byte aligned");
+  int rc = launch_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens,
+                               num_kv_heads, head_dim, num_blocks, new_dtype, kv_dtype, k_inv,
+                               v_inv, stream);
+  if (rc != 0) return fail(PKV_ERR_HIP, "cache_append: launch failed: %s",
+                           hipGetErrorString((hipError_t)rc));
+  return PKV_OK;
+}
+
+int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_blocks_per_seq, int32_t kv_dtype,
+                                  int32_t partition_size) {
+  (void)kv_dtype;
+  Plan plan;
+  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                 partition_size, &plan))
+    return -1;
+  return plan.partition;
+}
+
+size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t kv_dtype,
+                                 int32_t partition_size) {
+  (void)kv_dtype;
+  Plan plan;
+  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                 partition_size, &plan))
+    return SIZE_MAX;
+  return plan.ws_bytes;
+}
+
+int32_t pkv_decode_algo_for(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t q_dtype, int32_t kv_dtype) {
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
+  if (head_dim != 64 && head_dim != 128) return -1;
+  if (!decode_pair_ok(q_dtype, kv_dtype)) return -1;
+  return resolve_algo(num_q_heads / num_kv_heads, q_dtype, kv_dtype);
+}
+
+pkv_status pkv_paged_decode_attention_profiled(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, float scale, int32_t q_dtype,
+    int32_t kv_dtype, float k_scale, float v_scale, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, int32_t algo, void* stream, void* ev_begin, void* ev_mid,
+    void* ev_end) {
+  clear_error();
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 ||
+      max_blocks_per_seq < 0)
+    return fail(PKV_ERR_INVALID_ARG, "decode: bad sizes");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "decode: num_q_heads %% num_kv_heads != 0");
+  if (block_size != kBlockSize)
+    return fail(PKV_ERR_UNSUPPORTED, "decode: block_size must be 16 (got %d)", block_size);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "decode: head_dim must be 64 or 128 (got %d)", head_dim);
+  if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype))
+    return fail(PKV_ERR_INVALID_ARG, "decode: bad dtype");
+  if (!decode_pair_ok(q_dtype, kv_dtype))
+    return fail(PKV_ERR_UNSUPPORTED, "decode: unsupported (q, kv) dtype pair (%d, %d)", q_dtype,
+                kv_dtype);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "decode: scale must be finite");
+  if (kv_dtype == PKV_FP8_E4M3 && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
+    return fail(PKV_ERR_INVALID_ARG, "decode: FP8 scales must be finite");
+  if (partition_size < 0 || (partition_size > 0 && (partition_size % kBlockSize != 0 ||
+                                                     partition_size > kMaxPartition)))
+    return fail(PKV_ERR_INVALID_ARG, "decode: partition_size must be 0 or a multiple of 16 <= %d",
+                kMaxPartition);
+  if (algo < PKV_ALGO_AUTO || algo > PKV_ALGO_MFMA)
+    return fail(PKV_ERR_INVALID_ARG, "decode: bad algo %d", algo);
+  const int32_t g = num_q_heads / num_kv_heads;
+  const bool mfma_ok =
+      (q_dtype == PKV_F16 || q_dtype == PKV_BF16) && (kv_dtype == q_dtype || kv_dtype == PKV_FP8_E4M3);
+  if (algo == PKV_ALGO_MFMA && !mfma_ok)
+    return fail(PKV_ERR_UNSUPPORTED, "decode: the MFMA path needs 16-bit q and a 16-bit/FP8 cache");
+  if (algo == PKV_ALGO_AUTO) algo = resolve_algo(g, q_dtype, kv_dtype);
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "decode: NULL pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "decode: out, q and the caches must be 16-byte aligned");
+  Plan plan;
+  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                 partition_size, &plan))
+    return fail(PKV_ERR_INVALID_ARG, "decode: bad partition arguments");
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes)
+      return fail(PKV_ERR_WORKSPACE, "decode: workspace needs %zu bytes, got %zu", plan.ws_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(PKV_ERR_INVALID_ARG, "decode: workspace must be 256-byte aligned");
+  }
+  DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = kv_dtype;
+  a.scale = scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.partition = plan.partition;
+  a.num_parts = plan.num_parts;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_m = plan.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_l = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
+  a.ws_acc = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_acc) : nullptr;
+  a.stream = stream;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), hs) != hipSuccess)
+    return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
+  int rc = (algo == PKV_ALGO_MFMA) ? launch_decode_mfma(a) : launch_decode_vector(a);
+  if (rc != 0)
+    return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString((hipError_t)rc));
+  if (ev_mid && hipEventRecord(static_cast<hipEvent_t>(ev_mid), hs) != hipSuccess)
+    return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
+  if (plan.num_parts > 1) {
+    rc = launch_decode_reduce(a);
+    if (rc != 0)
+      return fail(PKV_ERR_HIP, "decode: reduce launch failed: %s",
+                  hipGetErrorString((hipError_t)rc));
+  }
+  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), hs) != hipSuccess)
+    return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
+  return PKV_OK;
+}
+
+pkv_status pkv_paged_decode_attention_algo(void* out, const void* q, const void* k_cache,
+                                           const void* v_cache, const int32_t* block_tables,
+                                           const int32_t* context_lens, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size,
+                                           int32_t num_blocks, int32_t max_blocks_per_seq,
+                                           float scale, int32_t q_dtype, int32_t kv_dtype,
+                                           float k_scale, float v_scale, int32_t partition_size,
+                                           void* workspace, size_t workspace_bytes,
+                                           int32_t algo, void* stream) {
+  return pkv_paged_decode_attention_profiled(
+      out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+      head_dim, block_size, num_blocks, max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale,
+      v_scale, partition_size, workspace, workspace_bytes, algo, stream, nullptr, nullptr,
+      nullptr);
+}
+
+pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      int32_t max_blocks_per_seq, float scale, int32_t q_dtype,
+                                      int32_t kv_dtype, float k_scale, float v_scale,
+                                      int32_t partition_size, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return pkv_paged_decode_attention_algo(
+      out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+      head_dim, block_size, num_blocks, max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale,
+      v_scale, partition_size, workspace, workspace_bytes, PKV_ALGO_AUTO, stream);
+}
+
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
+                           int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
+                           void* stream) {
+  clear_error();
+  if (num_pairs < 0 || num_blocks < 0 || block_bytes <= 0 || block_bytes % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: bad sizes");
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !src_dst_pairs)
+    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: NULL pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: caches must be 16-byte aligned");
+  int rc = launch_copy_blocks(k_cache, v_cache, src_dst_pairs, num_pairs, num_blocks,
+                              block_bytes, stream);
+  if (rc != 0)
+    return fail(PKV_ERR_HIP, "copy_blocks: launch failed: %s", hipGetErrorString((hipError_t)rc));
+  return PKV_OK;
+}
+
+}  // extern "C"

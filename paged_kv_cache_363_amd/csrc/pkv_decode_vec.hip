@@ -1,0 +1,310 @@
+// Paged decode attention on the vector ALUs, plus the split-K reduction.
+//
+// Every lane owns 16-byte chunks of the 16-token K and V tiles (chunk j*64+l
+// of a tile goes to lane l, so each load instruction of a wave reads 1 KiB of
+// contiguous memory).  A token's row spans CPT consecutive lanes; the partial
+// dot products of those lanes are summed with butterfly shuffles, after which
+// every lane holding part of a token knows its logit for all the q-heads of
+// the group, so the PV update needs no further exchange: each lane scales its
+// own V chunk.  This path serves every dtype pair (it is the only one for f32
+// and for MHA, g = 1); see pkv_decode_mfma.hip for the matrix-core path.
+//
+// Math: softmax(q K^T * scale) V through the block table ("KV Cache 与
+// PageAttention深度实战", sections 1.2 and 3.2) with an online softmax in base
+// 2; partitions of a long context are merged by the log-sum-exp rule.
+#include <hip/hip_runtime.h>
+
+#include "pkv_decode_common.h"
+
+namespace {
+
+using namespace pkvd;
+
+template <int QT>
+__device__ __forceinline__ void load_q(const void* q, int64_t off, int n, float* f) {
+  // n consecutive q elements (n = 4, 8 or 16) starting at element `off`
+  if constexpr (QT == PKV_F32) {
+    const float* p = reinterpret_cast<const float*>(q) + off;
+    for (int i = 0; i < n; ++i) f[i] = p[i];
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(q) + off;
+    for (int i = 0; i < n; ++i)
+      f[i] = QT == PKV_F16 ? f16_lo(p[i]) : bf16_lo(p[i]);
+  }
+}
+
+template <int QT, int KVT, int D, int GMAX>
+__global__ __launch_bounds__(64 * pkv::kWaves) void decode_vec_kernel(DecodeParams p) {
+  constexpr int EB = DType<KVT>::bytes;
+  constexpr int EPC = 16 / EB;          // elements per 16-byte chunk
+  constexpr int CPT = D / EPC;          // chunks (lanes) per token row
+  constexpr int NJ = D * EB / 64;       // chunks per lane per tile
+  constexpr int64_t TILE = 16 * D * EB;
+  constexpr int LD = D + 4;
+  static_assert(CPT >= 1 && CPT <= 64 && NJ >= 1, "tile shape");
+
+  __shared__ float sm_m[pkv::kWaves * GMAX];
+  __shared__ float sm_l[pkv::kWaves * GMAX];
+  __shared__ float sm_o[pkv::kWaves * GMAX * LD];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int part = blockIdx.x, s = blockIdx.z;
+  const int hk = blockIdx.y / p.hchunks, hc = blockIdx.y % p.hchunks;
+  const int h_first = hk * p.g + hc * p.chunk_heads;
+  const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
+  const int ctx = clamped_ctx(p, s);
+  const int nblk = (ctx + 15) >> 4;
+  const int b_begin = part * p.part_blocks;
+  if (part > 0 && b_begin >= nblk) return;
+  const int b_end = min(b_begin + p.part_blocks, nblk);
+
+  const int dim0 = (lane % CPT) * EPC;  // the lane's dims, the same for every chunk j
+  float qf[GMAX][EPC];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    if (h < nh) {
+      load_q<QT>(p.q, ((int64_t)s * p.Hq + h_first + h) * D + dim0, EPC, qf[h]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) qf[h][e] = 0.f;
+    }
+  }
+
+  float acc[GMAX][EPC];
+  float m_run[GMAX], l_run[GMAX];
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+    m_run[h] = kNegInf;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
+  }
+
+  const int64_t blk_stride = (int64_t)p.Hkv * TILE;
+  const int64_t head_off = (int64_t)hk * TILE;
+  const int32_t* btrow = p.bt + (int64_t)s * p.mb;
+
+  for (int b = b_begin + w; b < b_end; b += pkv::kWaves) {
+    const int phys = btrow[b];
+    if ((unsigned)phys >= (unsigned)p.nb) continue;   // bad table entry: no weight
+    const int valid = min(16, ctx - b * 16);
+    const uint4* kt = reinterpret_cast<const uint4*>(p.kc + phys * blk_stride + head_off);
+    const uint4* vt = reinterpret_cast<const uint4*>(p.vc + phys * blk_stride + head_off);
+    uint4 kr[NJ], vr[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) kr[j] = kt[j * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) vr[j] = vt[j * 64 + lane];
+
+    float z[NJ][GMAX];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float kf[EPC];
+      chunk_to_f32<KVT>(kr[j], kf);
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) a = fmaf(qf[h][e], kf[e], a);
+        z[j][h] = a;
+      }
+    }
+    // sum the partial dots of the CPT lanes sharing a token
+#pragma unroll
+    for (int off = 1; off < CPT; off <<= 1)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) z[j][h] += __shfl_xor(z[j][h], off);
+
+    float bm[GMAX];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) bm[h] = kNegInf;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int tok = (j * 64 + lane) / CPT;
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) {
+        z[j][h] = tok < valid ? z[j][h] * p.sl2 : kNegInf;
+        bm[h] = fmaxf(bm[h], z[j][h]);
+      }
+    }
+    // block maximum over the lanes holding other tokens
+#pragma unroll
+    for (int off = CPT; off < 64; off <<= 1)
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) bm[h] = fmaxf(bm[h], __shfl_xor(bm[h], off));
+
+    float alpha[GMAX];
+    bool moved = false;
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      const float m_new = fmaxf(m_run[h], bm[h]);
+      alpha[h] = __builtin_amdgcn_exp2f(m_run[h] - m_new);
+      moved |= alpha[h] != 1.0f;
+      m_run[h] = m_new;
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        z[j][h] = __builtin_amdgcn_exp2f(z[j][h] - m_new);
+        ps += z[j][h];
+      }
+      // each token's weight is replicated over its CPT lanes: count it once
+      l_run[h] = l_run[h] * alpha[h] + ((lane % CPT) == 0 ? ps : 0.f);
+    }
+    if (__any(moved)) {
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[h][e] *= alpha[h];
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float vf[EPC];
+      chunk_to_f32<KVT>(vr[j], vf);
+      if ((j * 64 + lane) / CPT >= valid) {
+        // stale slot past the context (possibly NaN): contributes nothing
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) vf[e] = 0.f;
+      }
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[h][e] = fmaf(z[j][h], vf[e], acc[h][e]);
+    }
+  }
+
+  // l: every lane holds part of it; acc: lanes with equal dims hold parts
+#pragma unroll
+  for (int h = 0; h < GMAX; ++h) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) l_run[h] += __shfl_xor(l_run[h], off);
+#pragma unroll
+    for (int off = CPT; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
+  }
+  if (lane < CPT) {
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) {
+      if (h < nh) {
+        if (lane == 0) {
+          sm_m[w * GMAX + h] = m_run[h];
+          sm_l[w * GMAX + h] = l_run[h];
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) sm_o[(w * GMAX + h) * LD + dim0 + e] = acc[h][e];
+      }
+    }
+  }
+  __syncthreads();
+  merge_waves_and_store<QT, D, GMAX>(p, sm_m, sm_l, sm_o, nh, s, h_first, part);
+}
+
+// Split-K reduction: one wave per (sequence, q-head) merges the partitions
+// that cover the sequence's context,
+//   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  out = sum_p acc_p 2^(m_p - M) / L.
+template <int QT, int D>
+__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
+  const int row = blockIdx.x;            // s * Hq + h
+  const int s = row / p.Hq;
+  const int ctx = clamped_ctx(p, s);
+  const int part_tokens = p.part_blocks * pkv::kBlockSize;
+  int np = (ctx + part_tokens - 1) / part_tokens;
+  np = np < 1 ? 1 : (np > p.num_parts ? p.num_parts : np);
+  const float* m = p.ws_m + (int64_t)row * p.num_parts;
+  const float* l = p.ws_l + (int64_t)row * p.num_parts;
+  const float* a = p.ws_acc + (int64_t)row * p.num_parts * D;
+  const int lane = threadIdx.x;
+  float M = kNegInf;
+  for (int i = lane; i < np; i += 64) M = fmaxf(M, l[i] > 0.f ? m[i] : kNegInf);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+  constexpr int PER = (D + 63) / 64;
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+  float L = 0.f;
+  if (M != kNegInf) {
+    for (int i = 0; i < np; ++i) {
+      const float li = l[i];
+      if (!(li > 0.f)) continue;
+      const float f = __builtin_amdgcn_exp2f(m[i] - M);
+      L += f * li;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int d = lane + 64 * k;
+        if (d < D) acc[k] = fmaf(f, a[(int64_t)i * D + d], acc[k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int d = lane + 64 * k;
+    if (d < D) store_out<QT>(p.out, (int64_t)row * D + d, L > 0.f ? acc[k] / L : 0.f);
+  }
+}
+
+template <int QT, int KVT, int D, int GMAX>
+int launch_vec_t(const pkv::DecodeArgs& a) {
+  const DecodeParams kp = make_params(a, GMAX);
+  dim3 grid(kp.num_parts, a.num_kv_heads * kp.hchunks, a.num_seqs);
+  decode_vec_kernel<QT, KVT, D, GMAX>
+      <<<grid, dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(kp);
+  return (int)hipGetLastError();
+}
+
+template <int QT, int KVT, int D>
+int launch_vec_g(const pkv::DecodeArgs& a) {
+  const int g = a.num_q_heads / a.num_kv_heads;
+  if (g <= 1) return launch_vec_t<QT, KVT, D, 1>(a);
+  if (g <= 2) return launch_vec_t<QT, KVT, D, 2>(a);
+  if (g <= 4) return launch_vec_t<QT, KVT, D, 4>(a);
+  return launch_vec_t<QT, KVT, D, 8>(a);   // larger groups run in chunks of 8 heads
+}
+
+template <int QT, int D>
+int launch_reduce_t(const pkv::DecodeArgs& a) {
+  const DecodeParams kp = make_params(a, 16);
+  decode_reduce_kernel<QT, D><<<dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
+                                (hipStream_t)a.stream>>>(kp);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+namespace pkv {
+
+int launch_decode_vector(const DecodeArgs& a) {
+  const int q = a.q_dtype, kv = a.kv_dtype, D = a.head_dim;
+#define PKV_VEC_CASE(QT, KVT, DD) \
+  if (q == QT && kv == KVT && D == DD) return launch_vec_g<QT, KVT, DD>(a);
+  PKV_VEC_CASE(PKV_F32, PKV_F32, 64)
+  PKV_VEC_CASE(PKV_F32, PKV_F32, 128)
+  PKV_VEC_CASE(PKV_BF16, PKV_BF16, 64)
+  PKV_VEC_CASE(PKV_BF16, PKV_BF16, 128)
+  PKV_VEC_CASE(PKV_F16, PKV_F16, 64)
+  PKV_VEC_CASE(PKV_F16, PKV_F16, 128)
+  PKV_VEC_CASE(PKV_BF16, PKV_FP8_E4M3, 64)
+  PKV_VEC_CASE(PKV_BF16, PKV_FP8_E4M3, 128)
+  PKV_VEC_CASE(PKV_F16, PKV_FP8_E4M3, 64)
+  PKV_VEC_CASE(PKV_F16, PKV_FP8_E4M3, 128)
+#undef PKV_VEC_CASE
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_decode_reduce(const DecodeArgs& a) {
+  const int q = a.q_dtype, D = a.head_dim;
+#define PKV_RED_CASE(QT, DD) \
+  if (q == QT && D == DD) return launch_reduce_t<QT, DD>(a);
+  PKV_RED_CASE(PKV_F32, 64)
+  PKV_RED_CASE(PKV_F32, 128)
+  PKV_RED_CASE(PKV_BF16, 64)
+  PKV_RED_CASE(PKV_BF16, 128)
+  PKV_RED_CASE(PKV_F16, 64)
+  PKV_RED_CASE(PKV_F16, 128)
+#undef PKV_RED_CASE
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace pkv

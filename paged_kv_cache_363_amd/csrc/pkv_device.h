@@ -1,0 +1,128 @@
+// Device-side helpers shared by the HIP kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pkv.h"
+
+namespace pkvd {
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_inff();
+
+template <int DT>
+struct DType;
+template <>
+struct DType<PKV_F32> {
+  static constexpr int bytes = 4;
+};
+template <>
+struct DType<PKV_F16> {
+  static constexpr int bytes = 2;
+};
+template <>
+struct DType<PKV_BF16> {
+  static constexpr int bytes = 2;
+};
+template <>
+struct DType<PKV_FP8_E4M3> {
+  static constexpr int bytes = 1;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Round a binary32 to bfloat16, nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// Widen 4 elements of one 32-bit word group (a uint4 holds 16 bytes) to f32.
+// Element e of a 16-byte chunk, for each storage type.
+template <int DT>
+__device__ __forceinline__ void chunk_to_f32(const uint4& r, float* f);
+
+template <>
+__device__ __forceinline__ void chunk_to_f32<PKV_F32>(const uint4& r, float* f) {
+  f[0] = __uint_as_float(r.x);
+  f[1] = __uint_as_float(r.y);
+  f[2] = __uint_as_float(r.z);
+  f[3] = __uint_as_float(r.w);
+}
+template <>
+__device__ __forceinline__ void chunk_to_f32<PKV_BF16>(const uint4& r, float* f) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(w[i]);
+    f[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+template <>
+__device__ __forceinline__ void chunk_to_f32<PKV_F16>(const uint4& r, float* f) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = f16_lo(w[i]);
+    f[2 * i + 1] = f16_hi(w[i]);
+  }
+}
+// OCP E4M3FN codes -> f32 with the hardware converter (scale 1.0: exact).
+template <>
+__device__ __forceinline__ void chunk_to_f32<PKV_FP8_E4M3>(const uint4& r, float* f) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[i], 1.0f, false);
+    f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[i], 1.0f, true);
+    f[4 * i + 0] = a[0];
+    f[4 * i + 1] = a[1];
+    f[4 * i + 2] = b[0];
+    f[4 * i + 3] = b[1];
+  }
+}
+
+// Binary32 -> E4M3FN code: nearest, ties to even, |x| >= 448 (and +-inf)
+// saturate to +-448, NaN -> 0x7F.  Integer arithmetic only, so the result
+// does not depend on the float rounding mode.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  u &= 0x7FFFFFFFu;
+  if (u > 0x7F800000u) return 0x7Fu;              // NaN
+  if (u >= 0x43E00000u) return sign | 0x7Eu;      // >= 448: saturate (incl. inf)
+  if (u < 0x3C800000u) {                          // below 2^-6: subnormal codes
+    // m = round_half_even(|x| * 2^9) in 0..8; 8 is the smallest normal code
+    float q = __uint_as_float(u) * 512.0f;        // exact: power-of-two scale
+    uint32_t m = (uint32_t)__builtin_rintf(q);
+    return sign | m;
+  }
+  // normal: keep 3 mantissa bits with round-to-nearest-even on bit 20
+  uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  uint32_t code = (r >> 20) - (120u << 3);        // rebias exponent 127 -> 7
+  return sign | (code > 0x7Eu ? 0x7Eu : code);
+}
+
+}  // namespace pkvd

@@ -1,0 +1,57 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Record a message for pkv_last_error() on this thread and return `st`.
+pkv_status fail(pkv_status st, const char* fmt, ...);
+void clear_error();
+
+inline int elem_bytes(int32_t dt) {
+  switch (dt) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+constexpr int kBlockSize = 16;   // tokens per physical block
+constexpr int kWaves = 4;        // waves per decode workgroup
+constexpr int kMaxPartition = 1 << 20;
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq;
+  int32_t q_dtype, kv_dtype;
+  float scale, k_scale, v_scale;
+  int32_t partition;   // tokens per partition
+  int32_t num_parts;   // max partitions per sequence (1 = single pass)
+  float* ws_m;         // [S][Hq][P]
+  float* ws_l;         // [S][Hq][P]
+  float* ws_acc;       // [S][Hq][P][D]
+  void* stream;
+};
+
+// Kernel launchers (return hipError_t as int).
+int launch_decode_vector(const DecodeArgs& a);
+int launch_decode_mfma(const DecodeArgs& a);
+int launch_decode_reduce(const DecodeArgs& a);
+int launch_cache_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                        const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t num_blocks, int32_t new_dtype, int32_t kv_dtype,
+                        float k_inv_scale, float v_inv_scale, void* stream);
+int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                       int32_t num_blocks, int64_t block_bytes, void* stream);
+
+}  // namespace pkv

@@ -1,0 +1,222 @@
+// Host block pool: physical block ids, reference counts and a FIFO free queue.
+//
+// Follows "vLLM推理引擎深度解析" section 2.2 (a pool of physical blocks, a table
+// per request, a queue of free blocks, a new block every 16 generated tokens)
+// and "大语言模型推理引擎深度剖析" sections 2.2-2.3 (O(1) allocation and
+// release; tables may share blocks; counts are kept and a block goes back to
+// the free pool at zero; a shared block is copied before it is written).
+//
+// The free queue is a ring buffer over the block ids, so alloc (pop head) and
+// release (push tail) are O(1).  Every operation that can fail checks first
+// and mutates only when it is sure to succeed.
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+struct pkv_pool {
+  int32_t num_blocks;
+  int32_t block_size;
+  std::vector<int32_t> ref;   // 0 = free
+  std::vector<int32_t> ring;  // free queue storage, capacity num_blocks
+  int32_t head = 0;           // index of the queue head in ring
+  int32_t count = 0;          // queue length
+
+  int32_t pop() {
+    int32_t b = ring[head];
+    head = (head + 1 == num_blocks) ? 0 : head + 1;
+    --count;
+    ref[b] = 1;
+    return b;
+  }
+  void push(int32_t b) {
+    int32_t tail = head + count;
+    if (tail >= num_blocks) tail -= num_blocks;
+    ring[tail] = b;
+    ++count;
+  }
+  bool valid(int32_t b) const { return b >= 0 && b < num_blocks; }
+};
+
+extern "C" {
+
+pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                           pkv_pool** out) {
+  if (!out) return pkv::fail(PKV_ERR_INVALID_ARG, "pool_create: out is NULL");
+  *out = nullptr;
+  if (num_blocks < 0 || block_size <= 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "pool_create: bad num_blocks/block_size");
+  pkv_pool* p = new (std::nothrow) pkv_pool();
+  if (!p) return pkv::fail(PKV_ERR_INVALID_ARG, "pool_create: out of host memory");
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->ref.assign(num_blocks, 0);
+  p->ring.resize(num_blocks);
+  if (free_order) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete p;
+        return pkv::fail(PKV_ERR_INVALID_ARG, "pool_create: free_order is not a permutation");
+      }
+      seen[b] = 1;
+      p->ring[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) p->ring[i] = i;
+  }
+  p->count = num_blocks;
+  *out = p;
+  return PKV_OK;
+}
+
+void pkv_pool_destroy(pkv_pool* pool) { delete pool; }
+
+pkv_status pkv_pool_alloc(pkv_pool* pool, int32_t* block_out) {
+  if (!pool || !block_out) return pkv::fail(PKV_ERR_INVALID_ARG, "pool_alloc: NULL argument");
+  if (pool->count == 0) return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "pool_alloc: no free block");
+  *block_out = pool->pop();
+  return PKV_OK;
+}
+
+pkv_status pkv_pool_incref(pkv_pool* pool, int32_t block) {
+  if (!pool || !pool->valid(block))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "pool_incref: bad block id");
+  if (pool->ref[block] < 1) return pkv::fail(PKV_ERR_REFCOUNT, "pool_incref: block is free");
+  ++pool->ref[block];
+  return PKV_OK;
+}
+
+pkv_status pkv_pool_decref(pkv_pool* pool, int32_t block) {
+  if (!pool || !pool->valid(block))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "pool_decref: bad block id");
+  if (pool->ref[block] < 1) return pkv::fail(PKV_ERR_REFCOUNT, "pool_decref: block is free");
+  if (--pool->ref[block] == 0) pool->push(block);
+  return PKV_OK;
+}
+
+int32_t pkv_pool_refcount(const pkv_pool* pool, int32_t block) {
+  if (!pool || !pool->valid(block)) return -1;
+  return pool->ref[block];
+}
+
+int32_t pkv_pool_num_free(const pkv_pool* pool) { return pool ? pool->count : -1; }
+int32_t pkv_pool_num_blocks(const pkv_pool* pool) { return pool ? pool->num_blocks : -1; }
+int32_t pkv_pool_block_size(const pkv_pool* pool) { return pool ? pool->block_size : -1; }
+
+pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n) {
+  if (!pool || !n) return pkv::fail(PKV_ERR_INVALID_ARG, "pool_free_list: NULL argument");
+  *n = pool->count;
+  if (cap < pool->count || (pool->count > 0 && !out))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "pool_free_list: cap too small");
+  for (int32_t i = 0; i < pool->count; ++i) {
+    int32_t j = pool->head + i;
+    if (j >= pool->num_blocks) j -= pool->num_blocks;
+    out[i] = pool->ring[j];
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_append_slots(pkv_pool* pool, int32_t* table, int32_t* nblocks, int32_t cap,
+                                int32_t cur_len, int32_t n_new, int64_t* slots_out,
+                                int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow) {
+  if (!pool || !nblocks) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_append_slots: NULL argument");
+  if (n_cow) *n_cow = 0;
+  if (cur_len < 0 || n_new < 0 || *nblocks < 0 || cap < 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "seq_append_slots: negative length");
+  if (n_new == 0) return PKV_OK;
+  if (!table || !slots_out)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "seq_append_slots: NULL table/slots");
+  const int32_t bs = pool->block_size;
+  const int64_t last_pos = (int64_t)cur_len + n_new - 1;
+  const int64_t first = cur_len / bs, last = last_pos / bs;
+  const int32_t nb = *nblocks;
+  if (first > nb) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_append_slots: gap after the table");
+  if (last + 1 > cap) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_append_slots: table capacity");
+  int64_t need_new = 0, need_cow = 0;
+  for (int64_t bi = first; bi <= last; ++bi) {
+    if (bi >= nb) {
+      ++need_new;
+    } else {
+      int32_t b = table[bi];
+      if (!pool->valid(b) || pool->ref[b] < 1)
+        return pkv::fail(PKV_ERR_INVALID_ARG, "seq_append_slots: table holds a bad block");
+      if (pool->ref[b] > 1) ++need_cow;
+    }
+  }
+  if (need_cow > 0 && (!cow_pairs || need_cow > cow_cap))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "seq_append_slots: cow_pairs too small");
+  if (need_new + need_cow > pool->count)
+    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "seq_append_slots: not enough free blocks");
+  int32_t ncow = 0;
+  for (int64_t bi = first; bi <= last; ++bi) {
+    if (bi < nb) {
+      int32_t old = table[bi];
+      if (pool->ref[old] > 1) {
+        int32_t fresh = pool->pop();
+        cow_pairs[2 * ncow] = old;
+        cow_pairs[2 * ncow + 1] = fresh;
+        ++ncow;
+        --pool->ref[old];  // stays >= 1: it was above 1
+        table[bi] = fresh;
+      }
+    } else {
+      table[bi] = pool->pop();
+    }
+  }
+  if (last + 1 > nb) *nblocks = (int32_t)(last + 1);
+  for (int32_t i = 0; i < n_new; ++i) {
+    int64_t pos = (int64_t)cur_len + i;
+    slots_out[i] = (int64_t)table[pos / bs] * bs + pos % bs;
+  }
+  if (n_cow) *n_cow = ncow;
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_create(pkv_pool* pool, int32_t prompt_len, int32_t* table, int32_t cap,
+                          int32_t* nblocks) {
+  if (!pool || !nblocks) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_create: NULL argument");
+  if (prompt_len < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_create: negative length");
+  *nblocks = 0;
+  if (prompt_len == 0) return PKV_OK;
+  std::vector<int64_t> slots(prompt_len);
+  int32_t nb = 0;
+  pkv_status st = pkv_seq_append_slots(pool, table, &nb, cap, 0, prompt_len, slots.data(),
+                                       nullptr, 0, nullptr);
+  if (st == PKV_OK) *nblocks = nb;
+  return st;
+}
+
+pkv_status pkv_seq_fork(pkv_pool* pool, const int32_t* table, int32_t nblocks) {
+  if (!pool || nblocks < 0 || (nblocks > 0 && !table))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "seq_fork: bad argument");
+  for (int32_t i = 0; i < nblocks; ++i) {
+    if (!pool->valid(table[i])) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_fork: bad block id");
+    if (pool->ref[table[i]] < 1) return pkv::fail(PKV_ERR_REFCOUNT, "seq_fork: block is free");
+  }
+  for (int32_t i = 0; i < nblocks; ++i) ++pool->ref[table[i]];
+  return PKV_OK;
+}
+
+pkv_status pkv_seq_free(pkv_pool* pool, const int32_t* table, int32_t nblocks) {
+  if (!pool || nblocks < 0 || (nblocks > 0 && !table))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "seq_free: bad argument");
+  // check first so that a bad table changes nothing (a table never names
+  // one block twice)
+  for (int32_t i = 0; i < nblocks; ++i) {
+    int32_t b = table[i];
+    if (!pool->valid(b)) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_free: bad block id");
+    if (pool->ref[b] < 1) return pkv::fail(PKV_ERR_REFCOUNT, "seq_free: block is free");
+  }
+  for (int32_t i = nblocks - 1; i >= 0; --i) {
+    int32_t b = table[i];
+    if (--pool->ref[b] == 0) pool->push(b);
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

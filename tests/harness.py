@@ -1,53 +1,13 @@
 """Test orchestration shared by CPU and GPU tests.
 
-`build_state` replays a workload's pool operations on any pool object that
-offers seq_create / seq_fork / seq_append_slots (the plain-Python reference
-pool or the native one); it computes no slot itself.  `oracle_setup` then
-fills oracle-side caches with the oracle's own append.
+`synth.scenario.build_state` replays a workload's pool operations on either
+pool; `oracle_setup` then fills oracle-side caches with the oracle's own
+append.
 """
 import numpy as np
 
 from synth import gen
-
-
-def build_state(cfg, pool, ctx):
-    """Each sequence first holds ctx[s]-1 tokens (prefill), then one decode
-    step appends its new token.  With cfg.shared_prefix, sequence 0 takes the
-    prefix blocks and every other table is a fork of them."""
-    S, P, MB = cfg.num_seqs, cfg.shared_prefix, cfg.max_blocks_per_seq
-    tables, prefill = [], []
-    if P:
-        base = []
-        slots, cows = pool.seq_append_slots(base, 0, P, MB)
-        assert not cows
-        prefill.append((0, 0, slots))
-        forks = [base] + [pool.seq_fork(base) for _ in range(S - 1)]
-    for s in range(S):
-        n_pre = int(ctx[s]) - 1
-        if P:
-            t = forks[s]
-            slots, cows = pool.seq_append_slots(t, P, n_pre - P, MB)
-            prefill.append((s, P, slots))
-        else:
-            t = []
-            slots, cows = pool.seq_append_slots(t, 0, n_pre, MB)
-            prefill.append((s, 0, slots))
-        assert not cows
-        tables.append(t)
-    step_slots, step_cows = [], []
-    for s in range(S):
-        slots, cows = pool.seq_append_slots(tables[s], int(ctx[s]) - 1, 1, MB)
-        step_slots += slots
-        step_cows += cows
-    return dict(tables=tables, prefill=prefill, step_slots=np.array(step_slots, np.int64),
-                step_cows=step_cows)
-
-
-def table_array(cfg, tables):
-    bt = np.full((len(tables), cfg.max_blocks_per_seq), -1, dtype=np.int32)
-    for s, t in enumerate(tables):
-        bt[s, :len(t)] = t
-    return bt
+from synth.scenario import build_state, table_array  # noqa: F401
 
 
 def poison_bits(dtype):

@@ -1,0 +1,94 @@
+"""Argument checks of the C ABI that return before any GPU work: they run on
+a host without a GPU.  Null device pointers are never dereferenced because
+every call here is rejected first."""
+import ctypes
+
+import pytest
+
+from paged_kv_cache_363_amd import _lib
+
+L = None
+NULL = None
+
+
+def lib():
+    return _lib.lib()
+
+
+def decode(**kw):
+    a = dict(out=NULL, q=NULL, k=NULL, v=NULL, bt=NULL, cl=NULL, S=4, hq=8, hkv=2, d=128, bs=16,
+             nb=10, mb=4, scale=0.1, qd=_lib.PKV_BF16, kvd=_lib.PKV_BF16, ks=1.0, vs=1.0, ps=0,
+             ws=NULL, wsb=0, algo=0, stream=NULL)
+    a.update(kw)
+    return lib().pkv_paged_decode_attention_algo(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["S"], a["hq"], a["hkv"], a["d"],
+        a["bs"], a["nb"], a["mb"], a["scale"], a["qd"], a["kvd"], a["ks"], a["vs"], a["ps"],
+        a["ws"], a["wsb"], a["algo"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bs=32), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(d=96), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(hq=6, hkv=4), _lib.PKV_ERR_INVALID_ARG),
+    (dict(qd=_lib.PKV_F32, kvd=_lib.PKV_BF16), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(qd=_lib.PKV_BF16, kvd=_lib.PKV_F16), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(qd=_lib.PKV_FP8_E4M3, kvd=_lib.PKV_FP8_E4M3), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(qd=7), _lib.PKV_ERR_INVALID_ARG),
+    (dict(ps=24), _lib.PKV_ERR_INVALID_ARG),
+    (dict(algo=5), _lib.PKV_ERR_INVALID_ARG),
+    (dict(qd=_lib.PKV_F32, kvd=_lib.PKV_F32, algo=_lib.PKV_ALGO_MFMA), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(scale=float("inf")), _lib.PKV_ERR_INVALID_ARG),
+    (dict(), _lib.PKV_ERR_INVALID_ARG),                       # NULL pointers
+])
+def test_decode_rejects(kw, status):
+    assert decode(**kw) == status
+    assert lib().pkv_last_error() != b""
+
+
+def test_decode_workspace_error_before_launch():
+    # 16-byte aligned fake pointers are never touched: the workspace check fails first
+    fake = ctypes.c_void_p(1 << 20)
+    st = decode(out=fake, q=fake, k=fake, v=fake, bt=fake, cl=fake, mb=256, ps=512, ws=NULL, wsb=0)
+    assert st == _lib.PKV_ERR_WORKSPACE
+
+
+def test_zero_sequences_is_a_no_op():
+    assert decode(S=0) == _lib.PKV_OK
+
+
+def test_workspace_and_partition_helpers():
+    l = lib()
+    assert l.pkv_decode_workspace_size(4, 4, 2, 64, 3, 0, 0) == 0      # single pass
+    ps = l.pkv_decode_partition_size(64, 32, 8, 128, 256, 2, 0)
+    assert ps % 16 == 0 and ps >= 128
+    n = l.pkv_decode_workspace_size(16, 32, 8, 128, 2048, 2, 512)
+    rows = 16 * 32 * 64
+    assert n >= rows * (128 + 2) * 4
+    assert l.pkv_decode_partition_size(1, 1, 1, 128, 4, 2, 24) == -1
+    assert l.pkv_decode_algo_for(64, 8, 128, _lib.PKV_BF16, _lib.PKV_FP8_E4M3) == _lib.PKV_ALGO_MFMA
+    assert l.pkv_decode_algo_for(32, 32, 128, _lib.PKV_F16, _lib.PKV_F16) == _lib.PKV_ALGO_VECTOR
+    assert l.pkv_decode_algo_for(4, 2, 64, _lib.PKV_F32, _lib.PKV_F32) == _lib.PKV_ALGO_VECTOR
+    assert l.pkv_decode_algo_for(4, 2, 96, _lib.PKV_F32, _lib.PKV_F32) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bs=8), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(d=12), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(nd=_lib.PKV_FP8_E4M3), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(nd=_lib.PKV_BF16, kvd=_lib.PKV_F16), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(kvd=_lib.PKV_FP8_E4M3, ks=0.0), _lib.PKV_ERR_INVALID_ARG),
+    (dict(kvd=_lib.PKV_FP8_E4M3, vs=float("nan")), _lib.PKV_ERR_INVALID_ARG),
+    (dict(T=-1), _lib.PKV_ERR_INVALID_ARG),
+    (dict(), _lib.PKV_ERR_INVALID_ARG),                       # NULL pointers
+])
+def test_append_rejects(kw, status):
+    a = dict(T=3, h=2, d=64, bs=16, nb=4, nd=_lib.PKV_BF16, kvd=_lib.PKV_BF16, ks=1.0, vs=1.0)
+    a.update(kw)
+    st = lib().pkv_paged_cache_append(NULL, NULL, NULL, NULL, NULL, a["T"], a["h"], a["d"],
+                                      a["bs"], a["nb"], a["nd"], a["kvd"], a["ks"], a["vs"], NULL)
+    assert st == status
+
+
+def test_copy_blocks_rejects():
+    assert lib().pkv_copy_blocks(NULL, NULL, NULL, 1, 4, 24, NULL) == _lib.PKV_ERR_INVALID_ARG
+    assert lib().pkv_copy_blocks(NULL, NULL, NULL, 0, 4, 32, NULL) == _lib.PKV_OK
