@@ -43,6 +43,10 @@ def parse():
     return ap.parse_args()
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def kv_elem_bytes(kv):
     return {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[kv]
 
@@ -108,7 +112,9 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
     import torch
     import paged_kv_cache_363_amd as pkv
 
+    log(f"setup {cfg.name}")
     st = setup(cfg, dev)
+    log("setup done")
     eb = kv_elem_bytes(cfg.kv_dtype)
     ctx = st["ctx"].astype(np.int64)
     kv_bytes = int(ctx.sum()) * 2 * cfg.num_kv_heads * cfg.head_dim * eb
@@ -135,6 +141,7 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    log(f"warmup done ({R} replicas)")
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for trio in evs:       # create the underlying HIP events before handing them over
@@ -169,9 +176,11 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
         step_gbs=kv_bytes / (step_ms * 1e-3) / 1e9,
         decode_kernel_gbs=achieved, tokens_per_s=cfg.num_seqs / (step_ms * 1e-3),
         t_pool_build_s=st["t_pool_build"])
+    log(f"timed {K} steps: {step_ms:.4f} ms/step, decode kernel {part_avg:.4f} ms")
     res["host_bookkeeping_us_per_step"] = host_bookkeeping_us(cfg, st)
     if with_cpu and args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(cfg, st, args.cpu_budget, out)
+        log("cpu baseline done")
     return res
 
 

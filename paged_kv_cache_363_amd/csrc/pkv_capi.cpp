@@ -205,6 +205,8 @@ pkv_status pkv_paged_decode_attention_profiled(
     return fail(PKV_ERR_INVALID_ARG, "decode: bad sizes");
   if (num_q_heads % num_kv_heads != 0)
     return fail(PKV_ERR_INVALID_ARG, "decode: num_q_heads %% num_kv_heads != 0");
+  if (num_seqs > 65535 || num_q_heads > 65535)
+    return fail(PKV_ERR_UNSUPPORTED, "decode: at most 65535 sequences and q-heads per call");
   if (block_size != kBlockSize)
     return fail(PKV_ERR_UNSUPPORTED, "decode: block_size must be 16 (got %d)", block_size);
   if (head_dim != 64 && head_dim != 128)
