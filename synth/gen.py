@@ -129,6 +129,8 @@ def kv_scales(cfg, ctx):
     k, v = step_kv(cfg)
     ak, av = float(k.float().abs().max()), float(v.float().abs().max())
     for s in range(cfg.num_seqs):
+        if int(ctx[s]) <= 1:
+            continue
         k, v = seq_kv(cfg, s, int(ctx[s]) - 1)
         ak = max(ak, float(k.float().abs().max()))
         av = max(av, float(v.float().abs().max()))
