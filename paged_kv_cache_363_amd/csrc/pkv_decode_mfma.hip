@@ -127,12 +127,11 @@ __device__ __forceinline__ Row<BYTES> load_row(const uint8_t* ptr) {
   return r;
 }
 
-template <int QT, int KVT, int D>
-__global__ __launch_bounds__(64 * pkv::kWaves) void decode_mfma_kernel(DecodeParams p) {
+template <int QT, int KVT, int D, int HS>
+__global__ __launch_bounds__(64 * pkv::kWaves) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_mfma_kernel(DecodeParams p) {
   using M = Mfma<QT>;
   using V8 = typename M::v8;
   using V4 = typename M::v4;
-  constexpr int HP = 16;             // MFMA columns = q-heads per workgroup
   constexpr int LD = D + 4;
   constexpr int DPL = D / 16;        // dims per lane in a V row = PV m-tiles
   constexpr int KSTEPS = D / 32;     // QK k-steps of 32
@@ -140,10 +139,17 @@ __global__ __launch_bounds__(64 * pkv::kWaves) void decode_mfma_kernel(DecodePar
   constexpr int KVB = FP8 ? 1 : 2;
   constexpr int64_t TILE = 16 * D * KVB;   // bytes of one (block, kv-head) tile
   constexpr int ROWB = DPL * KVB;          // bytes of a lane's slice of one V row
+  constexpr int KL = FP8 ? D / 64 : KSTEPS;  // 16-byte K loads per lane
 
-  __shared__ float sm_m[pkv::kWaves * HP];
-  __shared__ float sm_l[pkv::kWaves * HP];
-  __shared__ float sm_o[pkv::kWaves * HP * LD];
+  // raw bytes of one block as loaded by one lane
+  struct Raw {
+    uint4 k[KL];
+    Row<ROWB> v[4];
+  };
+
+  __shared__ float sm_m[pkv::kWaves * HS];
+  __shared__ float sm_l[pkv::kWaves * HS];
+  __shared__ float sm_o[pkv::kWaves * HS * LD];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, G = lane >> 4;
@@ -180,43 +186,47 @@ __global__ __launch_bounds__(64 * pkv::kWaves) void decode_mfma_kernel(DecodePar
   const int64_t head_off = (int64_t)hk * TILE;
   const int32_t* btrow = p.bt + (int64_t)s * p.mb;
 
-  for (int b = b_begin + w; b < b_end; b += pkv::kWaves) {
-    const int phys = btrow[b];
-    if ((unsigned)phys >= (unsigned)p.nb) continue;   // bad table entry: no weight
-    const int valid = min(16, ctx - b * 16);
+  auto issue = [&](Raw& r, int phys) {
     const uint8_t* kt = p.kc + phys * blk_stride + head_off;
     const uint8_t* vt = p.vc + phys * blk_stride + head_off;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int mm = 0; mm < KL; ++mm)
+        r.k[mm] = *reinterpret_cast<const uint4*>(kt + c * D + 64 * mm + 16 * G);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KL; ++kk)
+        r.k[kk] = *reinterpret_cast<const uint4*>(kt + (c * D + 32 * kk + 8 * G) * 2);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      r.v[rr] = load_row<ROWB>(vt + ((4 * G + rr) * D + DPL * c) * KVB);
+  };
 
+  auto consume = [&](Raw& r, int valid) {
     // A operand of QK: lane (G, c) holds token c, the dims of k-slot G.
     V8 kop[KSTEPS];
     if constexpr (FP8) {
 #pragma unroll
-      for (int mm = 0; mm < D / 64; ++mm) {
-        const uint4 r = *reinterpret_cast<const uint4*>(kt + c * D + 64 * mm + 16 * G);
-        kop[2 * mm] = as_v8<V8>(make_uint4(M::fp8x2(r.x, false), M::fp8x2(r.x, true),
-                                           M::fp8x2(r.y, false), M::fp8x2(r.y, true)));
-        kop[2 * mm + 1] = as_v8<V8>(make_uint4(M::fp8x2(r.z, false), M::fp8x2(r.z, true),
-                                               M::fp8x2(r.w, false), M::fp8x2(r.w, true)));
+      for (int mm = 0; mm < KL; ++mm) {
+        const uint4 x = r.k[mm];
+        kop[2 * mm] = as_v8<V8>(make_uint4(M::fp8x2(x.x, false), M::fp8x2(x.x, true),
+                                           M::fp8x2(x.y, false), M::fp8x2(x.y, true)));
+        kop[2 * mm + 1] = as_v8<V8>(make_uint4(M::fp8x2(x.z, false), M::fp8x2(x.z, true),
+                                               M::fp8x2(x.w, false), M::fp8x2(x.w, true)));
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
-        kop[kk] = as_v8<V8>(
-            *reinterpret_cast<const uint4*>(kt + (c * D + 32 * kk + 8 * G) * 2));
+      for (int kk = 0; kk < KSTEPS; ++kk) kop[kk] = as_v8<V8>(r.k[kk]);
     }
-
-    // V rows: lane (G, c) reads tokens 4G..4G+3, dims DPL*c .. DPL*c+DPL-1.
-    Row<ROWB> vr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) vr[r] = load_row<ROWB>(vt + ((4 * G + r) * D + DPL * c) * KVB);
     if (valid < 16) {
-      // tokens past the context hold stale data (possibly NaN): zero them so
-      // that a zero weight cannot meet a NaN in the PV product
+      // tokens past the context hold stale data (possibly NaN): zero their V
+      // so that a zero weight cannot meet a NaN in the PV product
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * G + r >= valid)
+      for (int rr = 0; rr < 4; ++rr)
+        if (4 * G + rr >= valid)
 #pragma unroll
-          for (int i = 0; i < ROWB / 4; ++i) vr[r].w[i] = 0u;
+          for (int i = 0; i < ROWB / 4; ++i) r.v[rr].w[i] = 0u;
     }
 
     // S = K Q^T: lane (G, c) gets tokens 4G+i, head c.
@@ -249,8 +259,8 @@ __global__ __launch_bounds__(64 * pkv::kWaves) void decode_mfma_kernel(DecodePar
       for (int e = 0; e < DPL; e += 2) {
         const int wi = e / 4, k = e % 4;
         const uint32_t sel = (uint32_t)k | ((4u + k) << 8) | ((k + 1u) << 16) | ((5u + k) << 24);
-        const uint32_t x01 = __builtin_amdgcn_perm(vr[1].w[wi], vr[0].w[wi], sel);
-        const uint32_t x23 = __builtin_amdgcn_perm(vr[3].w[wi], vr[2].w[wi], sel);
+        const uint32_t x01 = __builtin_amdgcn_perm(r.v[1].w[wi], r.v[0].w[wi], sel);
+        const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
         o[e] = M::pv(as_v4<V4>(M::fp8x2(x01, false), M::fp8x2(x23, false)), pb, o[e]);
         o[e + 1] = M::pv(as_v4<V4>(M::fp8x2(x01, true), M::fp8x2(x23, true)), pb, o[e + 1]);
       }
@@ -259,10 +269,45 @@ __global__ __launch_bounds__(64 * pkv::kWaves) void decode_mfma_kernel(DecodePar
       for (int e = 0; e < DPL; ++e) {
         const int wi = e / 2;
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t x01 = __builtin_amdgcn_perm(vr[1].w[wi], vr[0].w[wi], sel);
-        const uint32_t x23 = __builtin_amdgcn_perm(vr[3].w[wi], vr[2].w[wi], sel);
+        const uint32_t x01 = __builtin_amdgcn_perm(r.v[1].w[wi], r.v[0].w[wi], sel);
+        const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
         o[e] = M::pv(as_v4<V4>(x01, x23), pb, o[e]);
       }
+    }
+  };
+
+  // This wave's blocks are b_begin + w + 4*i, i < n_it.  Their physical ids
+  // are fetched 64 at a time into one VGPR (lane i holds block i), then read
+  // back with readlane; the K/V loads of block i+1 are issued before block i
+  // is consumed so that every wave keeps a block in flight.
+  const int n_it = b_end - b_begin - w > 0 ? (b_end - b_begin - w + pkv::kWaves - 1) / pkv::kWaves
+                                           : 0;
+  for (int base = 0; base < n_it; base += 64) {
+    const int cnt = min(64, n_it - base);
+    const int ids = lane < cnt ? btrow[b_begin + w + pkv::kWaves * (base + lane)] : -1;
+    auto tokens = [&](int i) {
+      return min(16, ctx - 16 * (b_begin + w + pkv::kWaves * (base + i)));
+    };
+    Raw ra, rb;
+    int pa = __builtin_amdgcn_readlane(ids, 0);
+    bool va = (unsigned)pa < (unsigned)p.nb;   // bad table entry: no weight
+    if (va) issue(ra, pa);
+    for (int i = 0; i < cnt; i += 2) {
+      bool vb = false;
+      if (i + 1 < cnt) {
+        const int pb = __builtin_amdgcn_readlane(ids, i + 1);
+        vb = (unsigned)pb < (unsigned)p.nb;
+        if (vb) issue(rb, pb);
+      }
+      if (va) consume(ra, tokens(i));
+      if (i + 1 >= cnt) break;
+      va = false;
+      if (i + 2 < cnt) {
+        pa = __builtin_amdgcn_readlane(ids, i + 2);
+        va = (unsigned)pa < (unsigned)p.nb;
+        if (va) issue(ra, pa);
+      }
+      if (vb) consume(rb, tokens(i + 1));
     }
   }
 
@@ -270,25 +315,32 @@ __global__ __launch_bounds__(64 * pkv::kWaves) void decode_mfma_kernel(DecodePar
   l_run = wave_sum4(l_run);
   if (c < nh) {
     if (G == 0) {
-      sm_m[w * HP + c] = m_run;
-      sm_l[w * HP + c] = l_run;
+      sm_m[w * HS + c] = m_run;
+      sm_l[w * HS + c] = l_run;
     }
-    float* dst = sm_o + (w * HP + c) * LD + DPL * 4 * G;
+    float* dst = sm_o + (w * HS + c) * LD + DPL * 4 * G;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < DPL; ++e) dst[DPL * i + e] = o[e][i];
   }
   __syncthreads();
-  merge_waves_and_store<QT, D, HP>(p, sm_m, sm_l, sm_o, nh, s, h_first, part);
+  merge_waves_and_store<QT, D, HS>(p, sm_m, sm_l, sm_o, nh, s, h_first, part);
+}
+
+template <int QT, int KVT, int D, int HS>
+int launch_t(const pkv::DecodeArgs& a, const DecodeParams& kp) {
+  dim3 grid(kp.num_parts, a.num_kv_heads * kp.hchunks, a.num_seqs);
+  decode_mfma_kernel<QT, KVT, D, HS>
+      <<<grid, dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(kp);
+  return (int)hipGetLastError();
 }
 
 template <int QT, int KVT, int D>
-int launch_t(const pkv::DecodeArgs& a, const DecodeParams& kp) {
-  dim3 grid(kp.num_parts, a.num_kv_heads * kp.hchunks, a.num_seqs);
-  decode_mfma_kernel<QT, KVT, D>
-      <<<grid, dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(kp);
-  return (int)hipGetLastError();
+int launch_hs(const pkv::DecodeArgs& a, const DecodeParams& kp) {
+  if (kp.chunk_heads <= 4) return launch_t<QT, KVT, D, 4>(a, kp);
+  if (kp.chunk_heads <= 8) return launch_t<QT, KVT, D, 8>(a, kp);
+  return launch_t<QT, KVT, D, 16>(a, kp);
 }
 
 }  // namespace
@@ -299,7 +351,7 @@ int launch_decode_mfma(const DecodeArgs& a) {
   const pkvd::DecodeParams kp = pkvd::make_params(a, 16);
   const int q = a.q_dtype, kv = a.kv_dtype, D = a.head_dim;
 #define PKV_MFMA_CASE(QT, KVT, DD) \
-  if (q == QT && kv == KVT && D == DD) return launch_t<QT, KVT, DD>(a, kp);
+  if (q == QT && kv == KVT && D == DD) return launch_hs<QT, KVT, DD>(a, kp);
   PKV_MFMA_CASE(PKV_BF16, PKV_BF16, 128)
   PKV_MFMA_CASE(PKV_BF16, PKV_BF16, 64)
   PKV_MFMA_CASE(PKV_F16, PKV_F16, 128)

@@ -204,6 +204,8 @@ __global__ __launch_bounds__(64 * pkv::kWaves) void decode_vec_kernel(DecodePara
 // Split-K reduction: one wave per (sequence, q-head) merges the partitions
 // that cover the sequence's context,
 //   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  out = sum_p acc_p 2^(m_p - M) / L.
+// Lane p computes partition p's weight; the accumulation then reads every
+// partition's row with independent loads.
 template <int QT, int D>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
   const int row = blockIdx.x;            // s * Hq + h
@@ -226,18 +228,29 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
   float L = 0.f;
   if (M != kNegInf) {
-    for (int i = 0; i < np; ++i) {
-      const float li = l[i];
-      if (!(li > 0.f)) continue;
-      const float f = __builtin_amdgcn_exp2f(m[i] - M);
-      L += f * li;
+    for (int base = 0; base < np; base += 64) {
+      const int i = base + lane;
+      float wgt = 0.f;
+      if (i < np) {
+        const float li = l[i];
+        wgt = li > 0.f ? __builtin_amdgcn_exp2f(m[i] - M) : 0.f;
+        L += wgt * li;
+      }
+      const int cnt = min(64, np - base);
+      const float* ab = a + (int64_t)base * D;
+#pragma unroll 8
+      for (int j = 0; j < cnt; ++j) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), j));
 #pragma unroll
-      for (int k = 0; k < PER; ++k) {
-        const int d = lane + 64 * k;
-        if (d < D) acc[k] = fmaf(f, a[(int64_t)i * D + d], acc[k]);
+        for (int k = 0; k < PER; ++k) {
+          const int d = lane + 64 * k;
+          if (d < D) acc[k] = fmaf(wj, ab[(int64_t)j * D + d], acc[k]);
+        }
       }
     }
   }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off);
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int d = lane + 64 * k;
