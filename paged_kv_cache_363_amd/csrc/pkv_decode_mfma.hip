@@ -64,6 +64,7 @@ struct Mfma<PKV_BF16> {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
   }
+  __device__ static float rounded(float a) { return (float)(__bf16)a; }
 };
 
 template <>
@@ -85,6 +86,7 @@ struct Mfma<PKV_F16> {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
   }
+  __device__ static float rounded(float a) { return (float)(_Float16)a; }
 };
 
 template <typename V>
@@ -250,8 +252,14 @@ __global__ __launch_bounds__(64 * pkv::kWaves) __attribute__((amdgpu_waves_per_e
 #pragma unroll
       for (int e = 0; e < DPL; ++e) o[e] *= alpha;
     }
-    // B operand of PV: k-slot (G, i) = token 4G+i, column c = head c.
+    // B operand of PV: k-slot (G, i) = token 4G+i, column c = head c.  The
+    // weights go in as a 16-bit head plus a 16-bit remainder, so the product
+    // keeps about 16 bits of each weight instead of 8 (bf16) or 11 (f16).
     const V4 pb = as_v4<V4>(M::pack2(pr[0], pr[1]), M::pack2(pr[2], pr[3]));
+    float lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo[i] = pr[i] - M::rounded(pr[i]);
+    const V4 pl = as_v4<V4>(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]));
 
     // A operand of PV for m-tile e: dim DPL*c + e of tokens 4G..4G+3.
     if constexpr (FP8) {
@@ -261,8 +269,10 @@ __global__ __launch_bounds__(64 * pkv::kWaves) __attribute__((amdgpu_waves_per_e
         const uint32_t sel = (uint32_t)k | ((4u + k) << 8) | ((k + 1u) << 16) | ((5u + k) << 24);
         const uint32_t x01 = __builtin_amdgcn_perm(r.v[1].w[wi], r.v[0].w[wi], sel);
         const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
-        o[e] = M::pv(as_v4<V4>(M::fp8x2(x01, false), M::fp8x2(x23, false)), pb, o[e]);
-        o[e + 1] = M::pv(as_v4<V4>(M::fp8x2(x01, true), M::fp8x2(x23, true)), pb, o[e + 1]);
+        const V4 a0 = as_v4<V4>(M::fp8x2(x01, false), M::fp8x2(x23, false));
+        const V4 a1 = as_v4<V4>(M::fp8x2(x01, true), M::fp8x2(x23, true));
+        o[e] = M::pv(a0, pl, M::pv(a0, pb, o[e]));
+        o[e + 1] = M::pv(a1, pl, M::pv(a1, pb, o[e + 1]));
       }
     } else {
 #pragma unroll
@@ -271,7 +281,8 @@ __global__ __launch_bounds__(64 * pkv::kWaves) __attribute__((amdgpu_waves_per_e
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         const uint32_t x01 = __builtin_amdgcn_perm(r.v[1].w[wi], r.v[0].w[wi], sel);
         const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
-        o[e] = M::pv(as_v4<V4>(x01, x23), pb, o[e]);
+        const V4 a0 = as_v4<V4>(x01, x23);
+        o[e] = M::pv(a0, pl, M::pv(a0, pb, o[e]));
       }
     }
   };

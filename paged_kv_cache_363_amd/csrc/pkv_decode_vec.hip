@@ -238,13 +238,24 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
       }
       const int cnt = min(64, np - base);
       const float* ab = a + (int64_t)base * D;
-#pragma unroll 8
-      for (int j = 0; j < cnt; ++j) {
-        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), j));
+      // 8 partitions per round, loads issued together (rows past cnt are
+      // not read: their weight is zero and the load is predicated off)
+      for (int j0 = 0; j0 < cnt; j0 += 8) {
+        float x[8][PER];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          const int d = lane + 64 * k;
-          if (d < D) acc[k] = fmaf(wj, ab[(int64_t)j * D + d], acc[k]);
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int k = 0; k < PER; ++k) {
+            const int d = lane + 64 * k;
+            x[u][k] = (j0 + u < cnt && d < D) ? ab[(int64_t)(j0 + u) * D + d] : 0.f;
+          }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float wj = __int_as_float(
+              __builtin_amdgcn_readlane(__float_as_int(wgt), min(j0 + u, 63)));
+          const float wu = (j0 + u < cnt) ? wj : 0.f;
+#pragma unroll
+          for (int k = 0; k < PER; ++k) acc[k] = fmaf(wu, x[u][k], acc[k]);
         }
       }
     }
