@@ -74,6 +74,11 @@ const char* pkv_status_string(int32_t status);
 /* Library version: major*10000 + minor*100 + patch. */
 int32_t pkv_version(void);
 
+/* Workgroups (of 4 waves) the balanced decode schedule launches; 0 restores
+ * the default (512, two per CU of an MI355X).  Process-wide; it changes what
+ * pkv_decode_workspace_size returns, so set it before sizing workspaces. */
+pkv_status pkv_set_stream_workgroups(int32_t n);
+
 /* --------------------------------------------------------------- sizes -- */
 
 /* KV-cache bytes per token of a whole model: 2 x layers x kv_heads x head_dim
@@ -108,19 +113,24 @@ pkv_status pkv_paged_cache_append(void* k_cache, void* v_cache, const void* k_ne
 /* ------------------------------------------------------ decode attention -- */
 
 /* Effective partition size (tokens) a decode call with these arguments will
- * use: partition_size itself if > 0 (it must be a multiple of 16), else the
- * library's choice.  A call whose max_blocks_per_seq * 16 fits in one
- * partition runs single-pass and needs no workspace.  Returns -1 on bad
- * arguments. */
+ * use: partition_size itself if > 0 (it must be a multiple of 16); for
+ * partition_size 0, 0 when the call runs the balanced schedule (16-bit or
+ * FP8 cache, at most 2048 sequences: the work is cut into equal shares of
+ * 16-token blocks instead of fixed partitions), else the library's choice of
+ * fixed partition.  A fixed-partition call whose max_blocks_per_seq * 16 fits
+ * in one partition runs single-pass.  Returns -1 on bad arguments. */
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_blocks_per_seq, int32_t kv_dtype,
                                   int32_t partition_size);
 
-/* Bytes of device workspace a decode call with these arguments needs (0 for
- * single-pass).  Layout: float m[S][H_q][P], float l[S][H_q][P],
- * float acc[S][H_q][P][head_dim] (each part 256-byte aligned), where
- * P = ceil(max_blocks_per_seq * 16 / partition).  Returns SIZE_MAX on bad
- * arguments. */
+/* Bytes of device workspace a decode call with these arguments needs (0 for a
+ * single-pass fixed partition).  Fixed partitions: float m[S][H_q][P],
+ * float l[S][H_q][P], float acc[S][H_q][P][head_dim] (each part 256-byte
+ * aligned), P = ceil(max_blocks_per_seq * 16 / partition).  Balanced
+ * schedule: per-segment arrival counters (uint64, tagged with a per-call
+ * epoch, so their contents on entry do not matter) and two partial slots per
+ * wave.  For partition_size 0 the size covers both schedules.  Returns
+ * SIZE_MAX on bad arguments. */
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_blocks_per_seq, int32_t kv_dtype,
                                  int32_t partition_size);
@@ -150,10 +160,15 @@ int32_t pkv_decode_algo_for(int32_t num_q_heads, int32_t num_kv_heads, int32_t h
  *                  FP8 caches only.
  *   shape limits : block_size 16; head_dim 64 or 128; num_q_heads a multiple
  *                  of num_kv_heads.
- *   partition_size: 0 = library's choice, else a multiple of 16 in [16, 2^20].
+ *   partition_size: 0 = library's schedule (balanced shares on the matrix
+ *                  cores when algo is AUTO or MFMA and the cache is 16-bit or
+ *                  FP8, else fixed partitions of its choice), else a multiple
+ *                  of 16 in [16, 2^20] (fixed partitions plus the reduction
+ *                  kernel).
  *   workspace    : device memory of at least pkv_decode_workspace_size(...)
  *                  bytes (may be NULL when that is 0).  Its contents on entry
- *                  do not matter. */
+ *                  do not matter; calls sharing one workspace must not
+ *                  overlap in time. */
 pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_cache,
                                       const void* v_cache, const int32_t* block_tables,
                                       const int32_t* context_lens, int32_t num_seqs,

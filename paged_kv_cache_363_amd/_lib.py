@@ -22,6 +22,7 @@ SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_status_string": (ctypes.c_char_p, [I32]),
     "pkv_version": (I32, []),
+    "pkv_set_stream_workgroups": (I32, [I32]),
     "pkv_kv_bytes_per_token": (U64, [I32, I32, I32, I32]),
     "pkv_paged_cache_append": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F32, F32, P]),
     "pkv_decode_partition_size": (I32, [I32, I32, I32, I32, I32, I32, I32]),

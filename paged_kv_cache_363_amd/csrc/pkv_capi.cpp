@@ -3,6 +3,7 @@
 // step of the decode path runs in the HIP kernels.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -54,23 +55,36 @@ static int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t 
 
 static int32_t resolve_algo(int32_t g, int32_t q, int32_t kv) {
   const bool mfma_ok = (q == PKV_F16 || q == PKV_BF16) && (kv == q || kv == PKV_FP8_E4M3);
-  return (mfma_ok && g >= 4) ? PKV_ALGO_MFMA : PKV_ALGO_VECTOR;
+  (void)g;
+  return mfma_ok ? PKV_ALGO_MFMA : PKV_ALGO_VECTOR;
 }
 
+static std::atomic<int32_t> g_stream_workgroups{kDefaultStreamWorkgroups};
+static std::atomic<uint32_t> g_epoch{0};
+
 struct Plan {
+  // fixed partitions (the partition kernels plus the reduction kernel)
   int32_t partition;
   int32_t num_parts;
-  size_t ws_bytes;
+  size_t ws_bytes;   // max over the schedules this call may use
   size_t off_l, off_acc;
+  // balanced schedule (partition_size == 0, MFMA-capable caches)
+  bool stream_ok;
+  int32_t stream_grid;
+  size_t stream_off_ml, stream_off_part, stream_bytes;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+static bool stream_capable_kv(int32_t kv_dtype) {
+  return kv_dtype == PKV_F16 || kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3;
+}
+
 static bool make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                      int32_t head_dim, int32_t max_blocks_per_seq, int32_t partition_size,
-                      Plan* plan) {
+                      int32_t head_dim, int32_t max_blocks_per_seq, int32_t kv_dtype,
+                      int32_t partition_size, Plan* plan) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      max_blocks_per_seq < 0 || partition_size < 0)
+      max_blocks_per_seq < 0 || partition_size < 0 || num_q_heads % num_kv_heads != 0)
     return false;
   if (partition_size > 0 && (partition_size % kBlockSize != 0 || partition_size > kMaxPartition))
     return false;
@@ -79,16 +93,34 @@ static bool make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
                                         : choose_partition(num_seqs, num_kv_heads, max_ctx);
   plan->partition = ps;
   plan->num_parts = max_ctx <= ps ? 1 : (max_ctx + ps - 1) / ps;
-  if (plan->num_parts == 1) {
-    plan->ws_bytes = 0;
-    plan->off_l = plan->off_acc = 0;
-    return true;
+  plan->off_l = plan->off_acc = 0;
+  size_t fixed_bytes = 0;
+  if (plan->num_parts > 1) {
+    const size_t rows = (size_t)num_seqs * num_q_heads * plan->num_parts;
+    const size_t bm = align256(rows * sizeof(float));
+    plan->off_l = bm;
+    plan->off_acc = 2 * bm;
+    fixed_bytes = 2 * bm + align256(rows * head_dim * sizeof(float));
   }
-  const size_t rows = (size_t)num_seqs * num_q_heads * plan->num_parts;
-  const size_t bm = align256(rows * sizeof(float));
-  plan->off_l = bm;
-  plan->off_acc = 2 * bm;
-  plan->ws_bytes = 2 * bm + align256(rows * head_dim * sizeof(float));
+  // balanced schedule: every sequence's block count fits the in-LDS prefix
+  // and the unit count stays below 2^31
+  const int32_t g = num_q_heads / num_kv_heads;
+  const int32_t chunk = g < 16 ? g : 16;
+  const int64_t Y = (int64_t)num_kv_heads * ((g + chunk - 1) / chunk);
+  plan->stream_ok = partition_size == 0 && stream_capable_kv(kv_dtype) &&
+                    num_seqs <= kMaxStreamSeqs &&
+                    (int64_t)num_seqs * max_blocks_per_seq * Y < ((int64_t)1 << 31);
+  plan->stream_grid = g_stream_workgroups.load();
+  plan->stream_off_ml = plan->stream_off_part = plan->stream_bytes = 0;
+  if (plan->stream_ok) {
+    const size_t workers = (size_t)plan->stream_grid * 4;
+    const size_t cnt = align256((size_t)num_seqs * Y * 8);
+    const size_t ml = align256(2 * workers * chunk * 2 * sizeof(float));
+    plan->stream_off_ml = cnt;
+    plan->stream_off_part = cnt + ml;
+    plan->stream_bytes = cnt + ml + align256(2 * workers * chunk * head_dim * sizeof(float));
+  }
+  plan->ws_bytes = fixed_bytes > plan->stream_bytes ? fixed_bytes : plan->stream_bytes;
   return true;
 }
 
@@ -114,6 +146,13 @@ const char* pkv_status_string(int32_t st) {
 }
 
 int32_t pkv_version(void) { return 100; }
+
+pkv_status pkv_set_stream_workgroups(int32_t n) {
+  clear_error();
+  if (n < 0 || n > 65535) return fail(PKV_ERR_INVALID_ARG, "set_stream_workgroups: bad count");
+  g_stream_workgroups.store(n == 0 ? kDefaultStreamWorkgroups : n);
+  return PKV_OK;
+}
 
 uint64_t pkv_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
                                 int32_t dtype) {
@@ -164,20 +203,18 @@ pkv_status pkv_paged_cache_append(void* k_cache, void* v_cache, const void* k_ne
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_blocks_per_seq, int32_t kv_dtype,
                                   int32_t partition_size) {
-  (void)kv_dtype;
   Plan plan;
-  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, kv_dtype,
                  partition_size, &plan))
     return -1;
-  return plan.partition;
+  return plan.stream_ok ? 0 : plan.partition;
 }
 
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_blocks_per_seq, int32_t kv_dtype,
                                  int32_t partition_size) {
-  (void)kv_dtype;
   Plan plan;
-  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, kv_dtype,
                  partition_size, &plan))
     return SIZE_MAX;
   return plan.ws_bytes;
@@ -237,12 +274,14 @@ pkv_status pkv_paged_decode_attention_profiled(
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_ERR_INVALID_ARG, "decode: out, q and the caches must be 16-byte aligned");
   Plan plan;
-  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+  if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, kv_dtype,
                  partition_size, &plan))
     return fail(PKV_ERR_INVALID_ARG, "decode: bad partition arguments");
-  if (plan.ws_bytes > 0) {
-    if (!workspace || workspace_bytes < plan.ws_bytes)
-      return fail(PKV_ERR_WORKSPACE, "decode: workspace needs %zu bytes, got %zu", plan.ws_bytes,
+  const bool use_stream = plan.stream_ok && algo == PKV_ALGO_MFMA;
+  const size_t need = use_stream ? plan.stream_bytes : (plan.num_parts > 1 ? plan.ws_bytes : 0);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "decode: workspace needs %zu bytes, got %zu", need,
                   workspace ? workspace_bytes : (size_t)0);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
       return fail(PKV_ERR_INVALID_ARG, "decode: workspace must be 256-byte aligned");
@@ -275,6 +314,19 @@ pkv_status pkv_paged_decode_attention_profiled(
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), hs) != hipSuccess)
     return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
+  if (use_stream) {
+    uint32_t epoch = ++g_epoch;
+    if (epoch == 0) epoch = ++g_epoch;   // 0 is what cleared memory holds
+    int rc = launch_decode_stream(a, plan.stream_grid, epoch, workspace, plan.stream_off_ml,
+                                  plan.stream_off_part);
+    if (rc != 0)
+      return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString((hipError_t)rc));
+    if (ev_mid && hipEventRecord(static_cast<hipEvent_t>(ev_mid), hs) != hipSuccess)
+      return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
+    if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), hs) != hipSuccess)
+      return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
+    return PKV_OK;
+  }
   int rc = (algo == PKV_ALGO_MFMA) ? launch_decode_mfma(a) : launch_decode_vector(a);
   if (rc != 0)
     return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString((hipError_t)rc));

@@ -24,6 +24,8 @@ inline int elem_bytes(int32_t dt) {
 constexpr int kBlockSize = 16;   // tokens per physical block
 constexpr int kWaves = 4;        // waves per decode workgroup
 constexpr int kMaxPartition = 1 << 20;
+constexpr int kMaxStreamSeqs = 2048;        // sequences the balanced schedule handles per call
+constexpr int kDefaultStreamWorkgroups = 512;  // 2 per CU on a 256-CU MI355X
 
 struct DecodeArgs {
   void* out;
@@ -47,6 +49,8 @@ struct DecodeArgs {
 int launch_decode_vector(const DecodeArgs& a);
 int launch_decode_mfma(const DecodeArgs& a);
 int launch_decode_reduce(const DecodeArgs& a);
+int launch_decode_stream(const DecodeArgs& a, int grid, uint32_t epoch, void* ws, size_t off_ml,
+                         size_t off_part);
 int launch_cache_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                         const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
                         int32_t head_dim, int32_t num_blocks, int32_t new_dtype, int32_t kv_dtype,

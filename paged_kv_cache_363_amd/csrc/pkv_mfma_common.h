@@ -1,0 +1,264 @@
+// Matrix-core building blocks shared by the MFMA decode kernels: operand
+// types, the per-lane loads of one 16-token K/V tile and the per-tile update
+// (QK^T on v_mfma_f32_16x16x32, online softmax, PV on v_mfma_f32_16x16x16).
+//
+// With grouped-query attention the g q-heads sharing one kv-head read the
+// same K and V tiles, so per tile QK^T is a [16 tokens x d] by [d x g]
+// product and PV a [g x 16] by [16 x d] product.  The g heads are padded to
+// the 16 MFMA columns with zero queries.  The accumulator layout of the first
+// product (lane l holds rows 4(l/16)+i, column l%16) is the B-operand layout
+// of the second one (PV computed as O^T = V^T P^T), so the softmax weights
+// stay in registers, and O^T keeps one head per lane column, which makes the
+// online-softmax rescale a per-lane multiply.  The weights enter PV as a
+// 16-bit head plus a 16-bit remainder (two MFMAs), keeping about 16 bits of
+// each weight.
+//
+// E4M3 caches are widened to the q type in registers (every E4M3 value is
+// exact in bf16 and f16); k_scale is folded into the logit scale and v_scale
+// into the final normalisation.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "pkv_decode_common.h"
+
+namespace pkvd {
+
+__device__ __forceinline__ float wave_max4(float x) {
+  // max over the 4 lanes l, l^16, l^32, l^48 (same lane column)
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float wave_sum4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int QT>
+struct Mfma;
+
+template <>
+struct Mfma<PKV_BF16> {
+  using v8 = bf16x8;
+  using v4 = i16x4;
+  __device__ static f32x4 qk(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static f32x4 pv(v4 a, v4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  // two E4M3 bytes (word `hi` of w) -> two bf16 in a 32-bit word
+  __device__ static uint32_t fp8x2(uint32_t w, bool hi) {
+    return __builtin_bit_cast(uint32_t,
+                              hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                 : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  }
+  __device__ static uint32_t pack2(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+  }
+  __device__ static float rounded(float a) { return (float)(__bf16)a; }
+};
+
+template <>
+struct Mfma<PKV_F16> {
+  using v8 = f16x8;
+  using v4 = f16x4;
+  __device__ static f32x4 qk(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static f32x4 pv(v4 a, v4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static uint32_t fp8x2(uint32_t w, bool hi) {
+    return __builtin_bit_cast(uint32_t,
+                              hi ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+                                 : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  }
+  __device__ static uint32_t pack2(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+  }
+  __device__ static float rounded(float a) { return (float)(_Float16)a; }
+};
+
+template <typename V>
+__device__ __forceinline__ V as_v8(uint4 r) {
+  return __builtin_bit_cast(V, r);
+}
+template <typename V>
+__device__ __forceinline__ V as_v4(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(V, make_uint2(a, b));
+}
+
+// Row of V for one token as seen by one lane: DPL elements of the kv type.
+template <int BYTES>
+struct Row;
+template <>
+struct Row<4> {
+  uint32_t w[1];
+};
+template <>
+struct Row<8> {
+  uint32_t w[2];
+};
+template <>
+struct Row<16> {
+  uint32_t w[4];
+};
+
+template <int BYTES>
+__device__ __forceinline__ Row<BYTES> load_row(const uint8_t* ptr) {
+  Row<BYTES> r;
+  if constexpr (BYTES == 16) {
+    uint4 v = *reinterpret_cast<const uint4*>(ptr);
+    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  } else if constexpr (BYTES == 8) {
+    uint2 v = *reinterpret_cast<const uint2*>(ptr);
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else {
+    r.w[0] = *reinterpret_cast<const uint32_t*>(ptr);
+  }
+  return r;
+}
+
+
+// One 16-token tile of one kv-head, as seen by one lane of a wave.
+//   K loads: lane (G = l/16, c = l%16) reads token c, the dims of k-slot G.
+//   V loads: lane (G, c) reads tokens 4G..4G+3, dims DPL*c .. DPL*c+DPL-1.
+template <int QT, int KVT, int D>
+struct MfmaTile {
+  using M = Mfma<QT>;
+  using V8 = typename M::v8;
+  using V4 = typename M::v4;
+  static constexpr int DPL = D / 16;        // dims per lane in a V row = PV m-tiles
+  static constexpr int KSTEPS = D / 32;     // QK k-steps of 32
+  static constexpr bool FP8 = (KVT == PKV_FP8_E4M3);
+  static constexpr int KVB = FP8 ? 1 : 2;
+  static constexpr int64_t TILE = 16 * D * KVB;   // bytes of one (block, kv-head) tile
+  static constexpr int ROWB = DPL * KVB;          // bytes of a lane's slice of one V row
+  static constexpr int KL = FP8 ? D / 64 : KSTEPS;  // 16-byte K loads per lane
+
+  struct Raw {
+    uint4 k[KL];
+    Row<ROWB> v[4];
+  };
+
+  // dim of element i of k-slot G in QK step kk (the same map for q and K)
+  __device__ static int qk_dim0(int kk, int G) {
+    return FP8 ? (64 * (kk / 2) + 16 * G + 8 * (kk % 2)) : (32 * kk + 8 * G);
+  }
+
+  // raw q row slice of q-head `row` (or zeros when !live) for every QK step
+  __device__ static void load_q(uint4* qr, const void* q, int64_t row, bool live, int G) {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(q) + row * D;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      qr[kk] = make_uint4(0, 0, 0, 0);
+      if (live) qr[kk] = *reinterpret_cast<const uint4*>(qrow + qk_dim0(kk, G));
+    }
+  }
+
+  __device__ static void issue(Raw& r, const uint8_t* kt, const uint8_t* vt, int c, int G) {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int mm = 0; mm < KL; ++mm)
+        r.k[mm] = *reinterpret_cast<const uint4*>(kt + c * D + 64 * mm + 16 * G);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KL; ++kk)
+        r.k[kk] = *reinterpret_cast<const uint4*>(kt + (c * D + 32 * kk + 8 * G) * 2);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+      r.v[rr] = load_row<ROWB>(vt + ((4 * G + rr) * D + DPL * c) * KVB);
+  }
+
+  // Online-softmax update of (m_run, l_run, o) with one tile holding `valid`
+  // live tokens.  qr: raw q operand (zeros for padding heads).
+  __device__ static void consume(Raw& r, int valid, const uint4* qr, float sl2, float& m_run,
+                                 float& l_run, f32x4* o, int c, int G) {
+    V8 kop[KSTEPS];
+    if constexpr (FP8) {
+#pragma unroll
+      for (int mm = 0; mm < KL; ++mm) {
+        const uint4 x = r.k[mm];
+        kop[2 * mm] = as_v8<V8>(make_uint4(M::fp8x2(x.x, false), M::fp8x2(x.x, true),
+                                           M::fp8x2(x.y, false), M::fp8x2(x.y, true)));
+        kop[2 * mm + 1] = as_v8<V8>(make_uint4(M::fp8x2(x.z, false), M::fp8x2(x.z, true),
+                                               M::fp8x2(x.w, false), M::fp8x2(x.w, true)));
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) kop[kk] = as_v8<V8>(r.k[kk]);
+    }
+    if (valid < 16) {
+      // tokens past the context hold stale data (possibly NaN): zero their V
+      // so that a zero weight cannot meet a NaN in the PV product
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        if (4 * G + rr >= valid)
+#pragma unroll
+          for (int i = 0; i < ROWB / 4; ++i) r.v[rr].w[i] = 0u;
+    }
+
+    // S = K Q^T: lane (G, c) gets tokens 4G+i, head c.
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) sacc = M::qk(kop[kk], as_v8<V8>(qr[kk]), sacc);
+
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = (4 * G + i < valid) ? sacc[i] * sl2 : kNegInf;
+    float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    bm = wave_max4(bm);
+    const float m_new = fmaxf(m_run, bm);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
+    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m_run = m_new;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] *= alpha;
+    }
+    // B operand of PV: k-slot (G, i) = token 4G+i, column c = head c, as a
+    // 16-bit head plus a 16-bit remainder.
+    const V4 pb = as_v4<V4>(M::pack2(pr[0], pr[1]), M::pack2(pr[2], pr[3]));
+    float lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo[i] = pr[i] - M::rounded(pr[i]);
+    const V4 pl = as_v4<V4>(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]));
+
+    // A operand of PV for m-tile e: dim DPL*c + e of tokens 4G..4G+3.
+    if constexpr (FP8) {
+#pragma unroll
+      for (int e = 0; e < DPL; e += 2) {
+        const int wi = e / 4, k = e % 4;
+        const uint32_t sel = (uint32_t)k | ((4u + k) << 8) | ((k + 1u) << 16) | ((5u + k) << 24);
+        const uint32_t x01 = __builtin_amdgcn_perm(r.v[1].w[wi], r.v[0].w[wi], sel);
+        const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
+        const V4 a0 = as_v4<V4>(M::fp8x2(x01, false), M::fp8x2(x23, false));
+        const V4 a1 = as_v4<V4>(M::fp8x2(x01, true), M::fp8x2(x23, true));
+        o[e] = M::pv(a0, pl, M::pv(a0, pb, o[e]));
+        o[e + 1] = M::pv(a1, pl, M::pv(a1, pb, o[e + 1]));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const int wi = e / 2;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t x01 = __builtin_amdgcn_perm(r.v[1].w[wi], r.v[0].w[wi], sel);
+        const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
+        const V4 a0 = as_v4<V4>(x01, x23);
+        o[e] = M::pv(a0, pl, M::pv(a0, pb, o[e]));
+      }
+    }
+  }
+};
+
+}  // namespace pkvd

@@ -40,23 +40,63 @@ def check_parity(name, out, seqs, ref):
         assert ok, f"{name}: max|err| {err}, worst excess over bound {excess}"
 
 
-ALGOS = {
-    "c1_tiny_f32": ["auto", "vector"],
-    "c2_qwen3_8b_bf16": ["auto", "vector", "mfma"],
-    "c3_llama2_7b_f16": ["auto", "vector", "mfma"],
-    "c4_llama3_70b_fp8": ["auto", "vector", "mfma"],
-    "c5_long_shared_bf16": ["auto", "vector", "mfma"],
+# (algo, partition): partition None = the workload's own setting; 0 with a
+# 16-bit or FP8 cache = the balanced schedule; > 0 = fixed partitions + reduce
+SCHEDULES = {
+    "c1_tiny_f32": [("auto", None), ("vector", 16)],
+    "c2_qwen3_8b_bf16": [("auto", None), ("mfma", 0), ("mfma", 512), ("vector", 0)],
+    "c3_llama2_7b_f16": [("auto", None), ("mfma", 0), ("mfma", 256), ("vector", 2048)],
+    "c4_llama3_70b_fp8": [("auto", None), ("mfma", 0), ("mfma", 256), ("vector", 512)],
+    "c5_long_shared_bf16": [("auto", None), ("mfma", 0), ("mfma", 512), ("vector", 1024)],
 }
-CASES = [(n, a) for n in CONFIGS for a in ALGOS[n]]
+CASES = [(n, a, ps) for n in CONFIGS for a, ps in SCHEDULES[n]]
 
 
-@pytest.mark.parametrize("name,algo", CASES)
-def test_decode_matches_oracle(name, algo):
-    print(f"[case] decode {name} algo={algo}", flush=True)
+@pytest.mark.parametrize("name,algo,ps", CASES)
+def test_decode_matches_oracle(name, algo, ps):
+    print(f"[case] decode {name} algo={algo} partition={ps}", flush=True)
     st = gpu_state(name)
     seqs, ref, _ = oracle_ref(name)
-    out = run_decode(st, algo)
+    out = run_decode(st, algo, ps)
     check_parity(name, out, seqs, ref)
+
+
+@pytest.mark.parametrize("wgs", [1, 3, 37, 512, 2048])
+@pytest.mark.parametrize("name", ["c2_qwen3_8b_bf16", "c4_llama3_70b_fp8"])
+def test_balanced_schedule_any_grid(name, wgs):
+    """The balanced schedule cuts the work into as many shares as it has
+    waves; every grid size must give the same answer (shares spanning many
+    segments, segments spanning many shares, shares of one block)."""
+    import paged_kv_cache_363_amd as pkv
+    print(f"[case] balanced {name} workgroups={wgs}", flush=True)
+    st = gpu_state(name)
+    seqs, ref, _ = oracle_ref(name)
+    pkv.lib().pkv_set_stream_workgroups(wgs)
+    try:
+        out = run_decode(st, "mfma", 0)
+    finally:
+        pkv.lib().pkv_set_stream_workgroups(0)
+    check_parity(name, out, seqs, ref)
+
+
+def test_balanced_schedule_ignores_stale_workspace():
+    """Arrival counters carry a per-call epoch: a workspace full of garbage or
+    left by earlier calls gives the same result, bit for bit."""
+    import paged_kv_cache_363_amd as pkv
+    name = "c2_qwen3_8b_bf16"
+    st = gpu_state(name)
+    cfg = st["cfg"]
+    ws = pkv.alloc_workspace(st["q"], st["k_cache"], st["block_tables"], 0)
+    outs = []
+    for fill in (None, 0xFF, 0x00, 0x5A):
+        if fill is not None:
+            ws.fill_(fill)
+        outs.append(pkv.paged_decode_attention(st["q"], st["k_cache"], st["v_cache"],
+                                               st["block_tables"], st["context_lens"], cfg.scale,
+                                               workspace=ws, algo="mfma"))
+        torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
 
 
 @pytest.mark.parametrize("ps", [16, 64, 128, 512, 1024, 4096])

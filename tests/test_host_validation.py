@@ -59,14 +59,21 @@ def test_zero_sequences_is_a_no_op():
 def test_workspace_and_partition_helpers():
     l = lib()
     assert l.pkv_decode_workspace_size(4, 4, 2, 64, 3, 0, 0) == 0      # single pass
-    ps = l.pkv_decode_partition_size(64, 32, 8, 128, 256, 2, 0)
+    # 16-bit cache, partition 0: the balanced schedule (reported as 0)
+    assert l.pkv_decode_partition_size(64, 32, 8, 128, 256, _lib.PKV_BF16, 0) == 0
+    # f32 cache: fixed partitions of the library's choice
+    ps = l.pkv_decode_partition_size(64, 32, 8, 128, 256, _lib.PKV_F32, 0)
     assert ps % 16 == 0 and ps >= 128
+    assert l.pkv_decode_partition_size(64, 32, 8, 128, 256, _lib.PKV_BF16, 256) == 256
+    # more sequences than the balanced schedule takes: fixed partitions
+    assert l.pkv_decode_partition_size(5000, 32, 8, 128, 256, _lib.PKV_BF16, 0) > 0
+    assert l.pkv_decode_workspace_size(64, 32, 8, 128, 256, _lib.PKV_BF16, 0) > 0
     n = l.pkv_decode_workspace_size(16, 32, 8, 128, 2048, 2, 512)
     rows = 16 * 32 * 64
     assert n >= rows * (128 + 2) * 4
     assert l.pkv_decode_partition_size(1, 1, 1, 128, 4, 2, 24) == -1
     assert l.pkv_decode_algo_for(64, 8, 128, _lib.PKV_BF16, _lib.PKV_FP8_E4M3) == _lib.PKV_ALGO_MFMA
-    assert l.pkv_decode_algo_for(32, 32, 128, _lib.PKV_F16, _lib.PKV_F16) == _lib.PKV_ALGO_VECTOR
+    assert l.pkv_decode_algo_for(32, 32, 128, _lib.PKV_F16, _lib.PKV_F16) == _lib.PKV_ALGO_MFMA
     assert l.pkv_decode_algo_for(4, 2, 64, _lib.PKV_F32, _lib.PKV_F32) == _lib.PKV_ALGO_VECTOR
     assert l.pkv_decode_algo_for(4, 2, 96, _lib.PKV_F32, _lib.PKV_F32) == -1
 
@@ -87,6 +94,18 @@ def test_append_rejects(kw, status):
     st = lib().pkv_paged_cache_append(NULL, NULL, NULL, NULL, NULL, a["T"], a["h"], a["d"],
                                       a["bs"], a["nb"], a["nd"], a["kvd"], a["ks"], a["vs"], NULL)
     assert st == status
+
+
+def test_stream_workgroups_setting_changes_workspace():
+    l = lib()
+    base = l.pkv_decode_workspace_size(64, 32, 8, 128, 256, _lib.PKV_BF16, 0)
+    assert l.pkv_set_stream_workgroups(1024) == _lib.PKV_OK
+    try:
+        assert l.pkv_decode_workspace_size(64, 32, 8, 128, 256, _lib.PKV_BF16, 0) > base
+    finally:
+        assert l.pkv_set_stream_workgroups(0) == _lib.PKV_OK
+    assert l.pkv_decode_workspace_size(64, 32, 8, 128, 256, _lib.PKV_BF16, 0) == base
+    assert l.pkv_set_stream_workgroups(-1) == _lib.PKV_ERR_INVALID_ARG
 
 
 def test_copy_blocks_rejects():
