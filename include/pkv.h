@@ -127,9 +127,8 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t
  * single-pass fixed partition).  Fixed partitions: float m[S][H_q][P],
  * float l[S][H_q][P], float acc[S][H_q][P][head_dim] (each part 256-byte
  * aligned), P = ceil(max_blocks_per_seq * 16 / partition).  Balanced
- * schedule: per-segment arrival counters (uint64, tagged with a per-call
- * epoch, so their contents on entry do not matter) and two partial slots per
- * wave.  For partition_size 0 the size covers both schedules.  Returns
+ * schedule: two partial slots (m, l and acc of up to 16 q-heads) per wave of
+ * its grid.  For partition_size 0 the size covers both schedules.  Returns
  * SIZE_MAX on bad arguments. */
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_blocks_per_seq, int32_t kv_dtype,

@@ -60,7 +60,6 @@ static int32_t resolve_algo(int32_t g, int32_t q, int32_t kv) {
 }
 
 static std::atomic<int32_t> g_stream_workgroups{kDefaultStreamWorkgroups};
-static std::atomic<uint32_t> g_epoch{0};
 
 struct Plan {
   // fixed partitions (the partition kernels plus the reduction kernel)
@@ -114,11 +113,10 @@ static bool make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
   plan->stream_off_ml = plan->stream_off_part = plan->stream_bytes = 0;
   if (plan->stream_ok) {
     const size_t workers = (size_t)plan->stream_grid * 4;
-    const size_t cnt = align256((size_t)num_seqs * Y * 8);
     const size_t ml = align256(2 * workers * chunk * 2 * sizeof(float));
-    plan->stream_off_ml = cnt;
-    plan->stream_off_part = cnt + ml;
-    plan->stream_bytes = cnt + ml + align256(2 * workers * chunk * head_dim * sizeof(float));
+    plan->stream_off_ml = 0;
+    plan->stream_off_part = ml;
+    plan->stream_bytes = ml + align256(2 * workers * chunk * head_dim * sizeof(float));
   }
   plan->ws_bytes = fixed_bytes > plan->stream_bytes ? fixed_bytes : plan->stream_bytes;
   return true;
@@ -315,14 +313,17 @@ pkv_status pkv_paged_decode_attention_profiled(
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), hs) != hipSuccess)
     return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
   if (use_stream) {
-    uint32_t epoch = ++g_epoch;
-    if (epoch == 0) epoch = ++g_epoch;   // 0 is what cleared memory holds
-    int rc = launch_decode_stream(a, plan.stream_grid, epoch, workspace, plan.stream_off_ml,
+    int rc = launch_decode_stream(a, plan.stream_grid, workspace, plan.stream_off_ml,
                                   plan.stream_off_part);
     if (rc != 0)
       return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString((hipError_t)rc));
     if (ev_mid && hipEventRecord(static_cast<hipEvent_t>(ev_mid), hs) != hipSuccess)
       return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
+    rc = launch_decode_split_merge(a, plan.stream_grid, workspace, plan.stream_off_ml,
+                                   plan.stream_off_part);
+    if (rc != 0)
+      return fail(PKV_ERR_HIP, "decode: merge launch failed: %s",
+                  hipGetErrorString((hipError_t)rc));
     if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), hs) != hipSuccess)
       return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
     return PKV_OK;

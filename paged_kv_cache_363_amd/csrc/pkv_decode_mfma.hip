@@ -1,9 +1,9 @@
 // Paged decode attention on the CDNA4 matrix cores, fixed partitions.
 //
 // Each workgroup owns one (partition, kv-head, head chunk, sequence); its four
-// waves take the partition's 16-token blocks round-robin, each with an online
-// softmax, and merge through LDS at the end (see pkv_decode_common.h).  The
-// per-tile arithmetic is MfmaTile (pkv_mfma_common.h).
+// waves take four contiguous runs of the partition's 16-token blocks, each
+// with an online softmax (mfma_piece, pkv_mfma_common.h), and merge through
+// LDS at the end (see pkv_decode_common.h).
 //
 // Math: softmax(q K^T * scale) V over the block-table-gathered context
 // ("KV Cache 与 PageAttention深度实战", sections 1.2 and 3.2).
@@ -11,15 +11,21 @@
 
 #include "pkv_mfma_common.h"
 
+#ifndef PKV_PIPE_DEPTH
+#define PKV_PIPE_DEPTH 2   // K/V blocks in flight per wave
+#endif
+#ifndef PKV_MFMA_WPE
+#define PKV_MFMA_WPE 2     // minimum waves per SIMD the register budget must allow
+#endif
+
 namespace {
 
 using namespace pkvd;
 
 template <int QT, int KVT, int D, int HS>
-__global__ __launch_bounds__(64 * pkv::kWaves) __attribute__((amdgpu_waves_per_eu(3, 8)))
+__global__ __launch_bounds__(64 * pkv::kWaves) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WPE, 8)))
 void decode_mfma_kernel(DecodeParams p) {
   using T = MfmaTile<QT, KVT, D>;
-  using Raw = typename T::Raw;
   constexpr int LD = D + 4;
   constexpr int DPL = T::DPL;
 
@@ -47,46 +53,18 @@ void decode_mfma_kernel(DecodeParams p) {
   for (int e = 0; e < DPL; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
-  const int64_t head_off = (int64_t)hk * T::TILE;
-  const int32_t* btrow = p.bt + (int64_t)s * p.mb;
-  auto issue = [&](Raw& r, int phys) {
-    T::issue(r, p.kc + phys * blk_stride + head_off, p.vc + phys * blk_stride + head_off, c, G);
-  };
-
-  // This wave's blocks are b_begin + w + 4*i, i < n_it.  Their physical ids
-  // are fetched 64 at a time into one VGPR (lane i holds block i), then read
-  // back with readlane; the K/V loads of block i+1 are issued before block i
-  // is consumed so that every wave keeps a block in flight.
-  const int n_it = b_end - b_begin - w > 0 ? (b_end - b_begin - w + pkv::kWaves - 1) / pkv::kWaves
-                                           : 0;
-  for (int base = 0; base < n_it; base += 64) {
-    const int cnt = min(64, n_it - base);
-    const int ids = lane < cnt ? btrow[b_begin + w + pkv::kWaves * (base + lane)] : -1;
-    auto tokens = [&](int i) {
-      return min(16, ctx - 16 * (b_begin + w + pkv::kWaves * (base + i)));
-    };
-    Raw ra, rb;
-    int pa = __builtin_amdgcn_readlane(ids, 0);
-    bool va = (unsigned)pa < (unsigned)p.nb;   // bad table entry: no weight
-    if (va) issue(ra, pa);
-    for (int i = 0; i < cnt; i += 2) {
-      bool vb = false;
-      if (i + 1 < cnt) {
-        const int pb = __builtin_amdgcn_readlane(ids, i + 1);
-        vb = (unsigned)pb < (unsigned)p.nb;
-        if (vb) issue(rb, pb);
-      }
-      if (va) T::consume(ra, tokens(i), qr, p.sl2, m_run, l_run, o, c, G);
-      if (i + 1 >= cnt) break;
-      va = false;
-      if (i + 2 < cnt) {
-        pa = __builtin_amdgcn_readlane(ids, i + 2);
-        va = (unsigned)pa < (unsigned)p.nb;
-        if (va) issue(ra, pa);
-      }
-      if (vb) T::consume(rb, tokens(i + 1), qr, p.sl2, m_run, l_run, o, c, G);
-    }
+  // wave w takes the w-th of four contiguous, near-equal runs of the
+  // partition's blocks
+  const int nblk_p = b_end - b_begin;
+  const int w0 = b_begin + (nblk_p * w) / pkv::kWaves;
+  const int w1 = b_begin + (nblk_p * (w + 1)) / pkv::kWaves;
+  if (p.nb > 0 && w1 > w0) {
+    const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
+    const int64_t head_off = (int64_t)hk * T::TILE;
+    mfma_piece<QT, KVT, D, PKV_PIPE_DEPTH>(p.kc + head_off, p.vc + head_off, blk_stride,
+                                           p.bt + (int64_t)s * p.mb, w0, w1, nblk - 1,
+                                           ctx - 16 * (nblk - 1), p.nb, qr, p.sl2, m_run, l_run,
+                                           o, lane);
   }
 
   // lane (G, c) holds O[head c][dim DPL*(4G+i) + e]; l needs the 4 G lanes

@@ -6,26 +6,31 @@
 // flattened into units -- one 16-token block of one segment, a segment being
 // the q-heads of one kv-head (at most 16 of them) of one sequence, segments
 // in sequence order -- and a fixed grid of waves splits the units into equal
-// contiguous shares.  Every wave streams its share with the per-tile update
-// of MfmaTile, keeping the next block's loads (and, at a segment change, the
-// next q rows) in flight while it works on the current block.
+// contiguous shares.  Every wave walks its share one piece (the part of one
+// segment inside the share) at a time with mfma_piece, which keeps the K/V
+// loads of the next blocks in flight while it works on the current one.
 //
 // A share covers the tail of one segment, whole segments and the head of
 // another.  A whole segment is normalised and stored by its wave.  A piece of
 // a segment is stored as (m, l, acc) in the wave's partial slot (its first
-// piece in slot 0, its last in slot 1) and counted on the segment's arrival
-// counter; the wave that completes the count merges the pieces with the
+// piece in slot 0, its last in slot 1).  The waves never signal each other:
+// across the XCDs of an MI355X that would need the L2 written back and
+// invalidated at every signal.  Instead decode_split_merge_kernel runs next
+// on the stream and merges the pieces of every split segment with the
 // log-sum-exp rule
 //   M = max_k m_k,  L = sum_k l_k 2^(m_k - M),  out = sum_k acc_k 2^(m_k - M) / L.
-// Counters are tagged with a per-call epoch in their high 32 bits, so a
-// counter left by an earlier call reads as zero and the workspace needs no
-// clearing.
+// Both kernels derive the shares from the same prefix sums of the block
+// counts, so the workspace carries nothing but the partial slots.
 //
 // Math: softmax(q K^T * scale) V over the block-table-gathered context
 // ("KV Cache 与 PageAttention深度实战", sections 1.2 and 3.2).
 #include <hip/hip_runtime.h>
 
 #include "pkv_mfma_common.h"
+
+#ifndef PKV_PIPE_DEPTH
+#define PKV_PIPE_DEPTH 2   // K/V blocks in flight per wave
+#endif
 
 namespace {
 
@@ -42,25 +47,15 @@ struct StreamParams {
   const int32_t* cl;
   int S, Hq, Hkv, g, Y, hchunks, chunk_heads, nb, mb;
   float sl2, vsc;
-  uint32_t epoch;
   float* part;                 // [2 W][chunk_heads][D]
   float* ml;                   // [2 W][chunk_heads][2]
-  unsigned long long* cnt;     // [S][Y]
+  int W;                       // waves of the decode grid
 };
 
-template <int QT, int KVT, int D>
-__global__ __launch_bounds__(64 * kSkWaves) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void decode_stream_kernel(StreamParams p) {
-  using T = MfmaTile<QT, KVT, D>;
-  using Raw = typename T::Raw;
-  constexpr int DPL = T::DPL;
-  constexpr int KS = T::KSTEPS;
-
-  __shared__ int sm_pref[pkv::kMaxStreamSeqs + 1];   // blocks before sequence s
-  __shared__ int sm_ctx[pkv::kMaxStreamSeqs];        // clamped context lengths
-
+// Block prefix sums of the (clamped) context lengths in LDS, computed by one
+// workgroup of 4 waves: pref[s] = blocks of the sequences before s.
+__device__ __forceinline__ void block_prefix(const StreamParams& p, int* sm_pref, int* sm_ctx) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int c = lane & 15, G = lane >> 4;
   const int S = p.S;
   const int cap = p.mb * pkv::kBlockSize;
   for (int i = threadIdx.x; i < S; i += 64 * kSkWaves) {
@@ -84,10 +79,26 @@ void decode_stream_kernel(StreamParams p) {
     if (lane == 0) sm_pref[0] = 0;
   }
   __syncthreads();
+}
+
+template <int QT, int KVT, int D>
+__global__ __launch_bounds__(64 * kSkWaves) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void decode_stream_kernel(StreamParams p) {
+  using T = MfmaTile<QT, KVT, D>;
+  constexpr int DPL = T::DPL;
+  constexpr int KS = T::KSTEPS;
+
+  __shared__ int sm_pref[pkv::kMaxStreamSeqs + 1];   // blocks before sequence s
+  __shared__ int sm_ctx[pkv::kMaxStreamSeqs];        // clamped context lengths
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, G = lane >> 4;
+  const int S = p.S;
+  block_prefix(p, sm_pref, sm_ctx);
 
   const int64_t Y = p.Y;
   const int64_t U = Y * sm_pref[S];
-  const int W = gridDim.x * kSkWaves;
+  const int W = p.W;
   const int wk = blockIdx.x * kSkWaves + w;
 
   // sequences without context get zero rows
@@ -98,7 +109,6 @@ void decode_stream_kernel(StreamParams p) {
   const int64_t We = U < W ? U : W;   // workers with a non-empty share
   if (wk >= We) return;
   auto share = [&](int64_t k) { return (U * k) / We; };
-  auto worker_of = [&](int64_t u) { return ((u + 1) * We - 1) / U; };
   const int64_t u_lo = share(wk), u_hi = share(wk + 1);
 
   // unit u -> (sequence s, segment y, block b): s is the last sequence whose
@@ -117,51 +127,8 @@ void decode_stream_kernel(StreamParams p) {
     b = (int)(r - (int64_t)y * nbk);
   };
 
-  // per-lane descriptors of 64 consecutive units (lane i: unit base + i)
-  struct Info {
-    int s, y, b, phys, ntok;
-  };
-  auto fetch = [&](int64_t base, Info& f) {
-    const int64_t u = base + lane;
-    f.s = 0;
-    f.y = 0;
-    f.b = 0;
-    f.phys = -1;
-    f.ntok = 0;
-    if (u < u_hi) {
-      locate(u, f.s, f.y, f.b);
-      f.phys = p.bt[(int64_t)f.s * p.mb + f.b];
-      f.ntok = min(16, sm_ctx[f.s] - 16 * f.b);
-    }
-  };
-  Info cur, nxt;
-  int64_t cur_base = u_lo;
-  fetch(u_lo, cur);
-  fetch(u_lo + 64, nxt);
-  auto info = [&](int64_t u, int& s, int& y, int& b, int& phys, int& ntok) {
-    const int64_t d = u - cur_base;
-    const Info& f = d < 64 ? cur : nxt;
-    const int i = (int)(d < 64 ? d : d - 64);
-    s = __builtin_amdgcn_readlane(f.s, i);
-    y = __builtin_amdgcn_readlane(f.y, i);
-    b = __builtin_amdgcn_readlane(f.b, i);
-    phys = __builtin_amdgcn_readlane(f.phys, i);
-    ntok = __builtin_amdgcn_readlane(f.ntok, i);
-  };
-
   const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
-  auto issue = [&](Raw& r, int phys, int y) {
-    const int64_t off = phys * blk_stride + (int64_t)(y / p.hchunks) * T::TILE;
-    T::issue(r, p.kc + off, p.vc + off, c, G);
-  };
-  auto q_rows = [&](uint4* qr, int s, int y) {
-    const int hc = y % p.hchunks;
-    const int h_first = (y / p.hchunks) * p.g + hc * p.chunk_heads;
-    const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
-    T::load_q(qr, p.q, (int64_t)s * p.Hq + h_first + c, c < nh, G);
-  };
-
-  uint4 qr[KS], qn[KS];
+  uint4 qr[KS];
   f32x4 o[DPL];
   float m_run = kNegInf, l_run = 0.f;
   auto reset = [&]() {
@@ -170,7 +137,6 @@ void decode_stream_kernel(StreamParams p) {
     m_run = kNegInf;
     l_run = 0.f;
   };
-  reset();
 
   // Close the piece [b0, b_last] of segment (s, y): store or merge.
   auto finish = [&](int s, int y, int b0, int b_last, bool first_piece) {
@@ -203,112 +169,138 @@ void decode_stream_kernel(StreamParams p) {
         p.ml[(slot * HS + c) * 2 + 1] = l_tot;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const int64_t seg_start = Y * sm_pref[s] + (int64_t)y * nbk;
-    const int64_t wa = worker_of(seg_start), wb = worker_of(seg_start + nbk - 1);
-    unsigned mine = 0;
-    if (lane == 0) {
-      unsigned long long* ctr = p.cnt + (int64_t)s * p.Y + y;
-      unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      while (true) {
-        const unsigned have = (unsigned)(old >> 32) == p.epoch ? (unsigned)old : 0u;
-        const unsigned long long nw = ((unsigned long long)p.epoch << 32) | (have + 1u);
-        if (__hip_atomic_compare_exchange_strong(ctr, &old, nw, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)) {
-          mine = have + 1u;
-          break;
-        }
-      }
+  };
+
+  // Walk the share piece by piece: a piece is the part of one segment that
+  // lies in [u_lo, u_hi).  Segments follow each other in (sequence, y)
+  // order; sequences without blocks own no segment.
+  int64_t u = u_lo;
+  int s, y, b;
+  locate(u, s, y, b);
+  while (true) {
+    const int nbk = sm_pref[s + 1] - sm_pref[s];
+    const int64_t seg_end = Y * sm_pref[s] + (int64_t)(y + 1) * nbk;
+    const int64_t pe = seg_end < u_hi ? seg_end : u_hi;
+    const int b1 = b + (int)(pe - u);
+    const int hc = y % p.hchunks;
+    const int hk = y / p.hchunks;
+    const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
+    T::load_q(qr, p.q, (int64_t)s * p.Hq + hk * p.g + hc * p.chunk_heads + c, c < nh, G);
+    reset();
+    const int ctx = sm_ctx[s];
+    const int last = ((ctx + 15) >> 4) - 1;
+    if (p.nb > 0) {
+      const int64_t off = (int64_t)hk * T::TILE;
+      mfma_piece<QT, KVT, D, PKV_PIPE_DEPTH>(p.kc + off, p.vc + off, blk_stride,
+                                             p.bt + (int64_t)s * p.mb, b, b1, last,
+                                             ctx - 16 * last, p.nb, qr, p.sl2, m_run, l_run, o,
+                                             lane);
     }
-    mine = __shfl(mine, 0);
-    if ((int64_t)mine != wb - wa + 1) return;
-    // last piece in: merge every piece of the segment
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    const bool wa_first = share(wa) == seg_start;
-    for (int h = 0; h < nh; ++h) {
-      float M = kNegInf;
-      for (int64_t k = wa; k <= wb; ++k) {
-        const int64_t sl = 2 * k + ((k == wa && !wa_first) ? 1 : 0);
-        if (p.ml[(sl * HS + h) * 2 + 1] > 0.f) M = fmaxf(M, p.ml[(sl * HS + h) * 2]);
-      }
-      constexpr int PER = (D + 63) / 64;
-      float acc[PER];
+    finish(s, y, b, b1 - 1, u == u_lo);
+    u = pe;
+    if (u >= u_hi) break;
+    b = 0;
+    if (++y == p.Y) {
+      y = 0;
+      do {
+        ++s;
+      } while (sm_pref[s + 1] == sm_pref[s]);
+    }
+  }
+}
+
+// Merge the pieces of every segment that the decode grid split between
+// waves.  One wave per (segment, q-head of the segment); segments kept whole
+// by one wave were already stored by it.  The shares are recomputed exactly
+// as the decode kernel computed them: worker k owns units
+// [U k / We, U (k+1) / We).  Lane j holds piece j's (m, l) and weight; the
+// accumulator rows of all pieces are then read with independent loads.
+template <int QT, int D>
+__global__ __launch_bounds__(64 * kSkWaves) void decode_split_merge_kernel(StreamParams p) {
+  __shared__ int sm_pref[pkv::kMaxStreamSeqs + 1];
+  __shared__ int sm_ctx[pkv::kMaxStreamSeqs];
+  block_prefix(p, sm_pref, sm_ctx);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t Y = p.Y;
+  const int64_t U = Y * sm_pref[p.S];
+  const int64_t We = U < p.W ? U : p.W;
+  if (We == 0) return;
+  const int HS = p.chunk_heads;
+  constexpr int PER = (D + 63) / 64;
+  const int64_t nitems = (int64_t)p.S * Y * HS;
+  for (int64_t it = (int64_t)blockIdx.x * kSkWaves + w; it < nitems;
+       it += (int64_t)gridDim.x * kSkWaves) {
+    const int h = (int)(it % HS);
+    const int64_t seg = it / HS;
+    const int s = (int)(seg / Y), y = (int)(seg % Y);
+    const int hc = y % p.hchunks;
+    const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
+    if (h >= nh) continue;
+    const int nbk = sm_pref[s + 1] - sm_pref[s];
+    if (nbk == 0) continue;
+    const int64_t seg_start = Y * sm_pref[s] + (int64_t)y * nbk;
+    const int64_t wa = ((seg_start + 1) * We - 1) / U;
+    const int64_t wb = ((seg_start + nbk) * We - 1) / U;
+    if (wa == wb) continue;
+    // the first worker's piece is its last one unless its share starts here
+    const int64_t sl0 = 2 * wa + ((U * wa) / We == seg_start ? 0 : 1);
+    const int np = (int)(wb - wa + 1);
+    auto slot_of = [&](int k) { return k == 0 ? sl0 : 2 * (wa + k); };
+    float acc[PER];
 #pragma unroll
-      for (int k2 = 0; k2 < PER; ++k2) acc[k2] = 0.f;
-      float L = 0.f;
-      if (M != kNegInf) {
-        for (int64_t k = wa; k <= wb; ++k) {
-          const int64_t sl = 2 * k + ((k == wa && !wa_first) ? 1 : 0);
+    for (int k2 = 0; k2 < PER; ++k2) acc[k2] = 0.f;
+    float L = 0.f;
+    // pass 1: the maximum over every piece
+    float M = kNegInf;
+    for (int k = lane; k < np; k += 64) {
+      const int64_t sl = slot_of(k);
+      const float lk = p.ml[(sl * HS + h) * 2 + 1];
+      const float mk = p.ml[(sl * HS + h) * 2];
+      if (lk > 0.f) M = fmaxf(M, mk);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if (M != kNegInf) {
+      for (int base = 0; base < np; base += 64) {
+        float wgt = 0.f;
+        if (base + lane < np) {
+          const int64_t sl = slot_of(base + lane);
           const float lk = p.ml[(sl * HS + h) * 2 + 1];
-          if (!(lk > 0.f)) continue;
-          const float f = __builtin_amdgcn_exp2f(p.ml[(sl * HS + h) * 2] - M);
-          L += f * lk;
-          const float* src = p.part + (sl * HS + h) * D;
+          wgt = lk > 0.f ? __builtin_amdgcn_exp2f(p.ml[(sl * HS + h) * 2] - M) : 0.f;
+          L += wgt * lk;
+        }
+        const int cnt = min(64, np - base);
+        for (int j0 = 0; j0 < cnt; j0 += 8) {
+          float x[8][PER];
 #pragma unroll
-          for (int k2 = 0; k2 < PER; ++k2) {
-            const int d = lane + 64 * k2;
-            if (d < D) acc[k2] = fmaf(f, src[d], acc[k2]);
+          for (int u = 0; u < 8; ++u) {
+            const int64_t sl = slot_of(base + min(j0 + u, cnt - 1));
+#pragma unroll
+            for (int k2 = 0; k2 < PER; ++k2) {
+              const int d = lane + 64 * k2;
+              x[u][k2] = d < D ? p.part[(sl * HS + h) * D + d] : 0.f;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float wj = __int_as_float(
+                __builtin_amdgcn_readlane(__float_as_int(wgt), min(j0 + u, 63)));
+            const float wu = (j0 + u < cnt) ? wj : 0.f;
+#pragma unroll
+            for (int k2 = 0; k2 < PER; ++k2) acc[k2] = fmaf(wu, x[u][k2], acc[k2]);
           }
         }
       }
-      const int64_t row = (int64_t)s * p.Hq + h_first + h;
+    }
 #pragma unroll
-      for (int k2 = 0; k2 < PER; ++k2) {
-        const int d = lane + 64 * k2;
-        if (d < D) store_out<QT>(p.out, row * D + d, L > 0.f ? acc[k2] / L : 0.f);
-      }
-    }
-  };
-
-  // current unit's descriptor; its loads and q rows are requested before the loop
-  int s_, y_, b_, ph_, nt_;
-  info(u_lo, s_, y_, b_, ph_, nt_);
-  bool v_ = (unsigned)ph_ < (unsigned)p.nb;   // bad table entry: no weight
-  int64_t piece_u0 = u_lo;
-  int piece_b0 = b_;
-  q_rows(qn, s_, y_);
-
-  Raw ra, rb;
-  if (v_) issue(ra, ph_, y_);
-
-  // one unit: prefetch the next, consume the current, close the piece if the
-  // next unit belongs to another segment
-  auto step = [&](Raw& rc, Raw& rn, int64_t u) {
-    if (u == piece_u0) {
+    for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off);
+    const int h_first = (y / p.hchunks) * p.g + hc * p.chunk_heads;
+    const int64_t row = (int64_t)s * p.Hq + h_first + h;
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) qr[kk] = qn[kk];
+    for (int k2 = 0; k2 < PER; ++k2) {
+      const int d = lane + 64 * k2;
+      if (d < D) store_out<QT>(p.out, row * D + d, L > 0.f ? acc[k2] / L : 0.f);
     }
-    const bool has_next = u + 1 < u_hi;
-    int ns = 0, ny = 0, nbb = 0, nph = -1, nnt = 0;
-    if (has_next) info(u + 1, ns, ny, nbb, nph, nnt);
-    const bool nv = has_next && (unsigned)nph < (unsigned)p.nb;
-    const bool new_seg = has_next && (ns != s_ || ny != y_);
-    if (nv) issue(rn, nph, ny);
-    if (new_seg) q_rows(qn, ns, ny);
-    if (v_) T::consume(rc, nt_, qr, p.sl2, m_run, l_run, o, c, G);
-    if (!has_next || new_seg) {
-      finish(s_, y_, piece_b0, b_, piece_u0 == u_lo);
-      reset();
-      piece_u0 = u + 1;
-      piece_b0 = nbb;
-    }
-    s_ = ns;
-    y_ = ny;
-    b_ = nbb;
-    ph_ = nph;
-    nt_ = nnt;
-    v_ = nv;
-    if (u + 1 - cur_base == 64) {   // the next unit opens the next descriptor batch
-      cur = nxt;
-      cur_base += 64;
-      fetch(cur_base + 64, nxt);
-    }
-  };
-
-  for (int64_t u = u_lo; u < u_hi; u += 2) {
-    step(ra, rb, u);
-    if (u + 1 >= u_hi) break;
-    step(rb, ra, u + 1);
   }
 }
 
@@ -319,12 +311,18 @@ int launch_t(const pkv::DecodeArgs& a, const StreamParams& sp, int grid) {
   return (int)hipGetLastError();
 }
 
-}  // namespace
+template <int QT, int D>
+int launch_merge_t(const pkv::DecodeArgs& a, const StreamParams& sp) {
+  const int64_t nitems = (int64_t)sp.S * sp.Y * sp.chunk_heads;
+  int64_t grid = (nitems + kSkWaves - 1) / kSkWaves;
+  if (grid > 4096) grid = 4096;
+  decode_split_merge_kernel<QT, D>
+      <<<dim3((unsigned)grid), dim3(64 * kSkWaves), 0, (hipStream_t)a.stream>>>(sp);
+  return (int)hipGetLastError();
+}
 
-namespace pkv {
-
-int launch_decode_stream(const DecodeArgs& a, int grid, uint32_t epoch, void* ws,
-                         size_t off_ml, size_t off_part) {
+StreamParams make_stream_params(const pkv::DecodeArgs& a, int grid, void* ws, size_t off_ml,
+                                size_t off_part) {
   const pkvd::DecodeParams kp = pkvd::make_params(a, 16);
   StreamParams sp;
   sp.out = a.out;
@@ -344,11 +342,20 @@ int launch_decode_stream(const DecodeArgs& a, int grid, uint32_t epoch, void* ws
   sp.mb = a.max_blocks_per_seq;
   sp.sl2 = kp.sl2;
   sp.vsc = kp.vsc;
-  sp.epoch = epoch;
   char* w = static_cast<char*>(ws);
-  sp.cnt = reinterpret_cast<unsigned long long*>(w);
   sp.ml = reinterpret_cast<float*>(w + off_ml);
   sp.part = reinterpret_cast<float*>(w + off_part);
+  sp.W = grid * kSkWaves;
+  return sp;
+}
+
+}  // namespace
+
+namespace pkv {
+
+int launch_decode_stream(const DecodeArgs& a, int grid, void* ws, size_t off_ml,
+                         size_t off_part) {
+  const StreamParams sp = make_stream_params(a, grid, ws, off_ml, off_part);
   const int q = a.q_dtype, kv = a.kv_dtype, D = a.head_dim;
 #define PKV_STREAM_CASE(QT, KVT, DD) \
   if (q == QT && kv == KVT && D == DD) return launch_t<QT, KVT, DD>(a, sp, grid);
@@ -361,6 +368,17 @@ int launch_decode_stream(const DecodeArgs& a, int grid, uint32_t epoch, void* ws
   PKV_STREAM_CASE(PKV_F16, PKV_FP8_E4M3, 128)
   PKV_STREAM_CASE(PKV_F16, PKV_FP8_E4M3, 64)
 #undef PKV_STREAM_CASE
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_decode_split_merge(const DecodeArgs& a, int grid, void* ws, size_t off_ml,
+                              size_t off_part) {
+  const StreamParams sp = make_stream_params(a, grid, ws, off_ml, off_part);
+  const int q = a.q_dtype, D = a.head_dim;
+  if (q == PKV_BF16 && D == 128) return launch_merge_t<PKV_BF16, 128>(a, sp);
+  if (q == PKV_BF16 && D == 64) return launch_merge_t<PKV_BF16, 64>(a, sp);
+  if (q == PKV_F16 && D == 128) return launch_merge_t<PKV_F16, 128>(a, sp);
+  if (q == PKV_F16 && D == 64) return launch_merge_t<PKV_F16, 64>(a, sp);
   return (int)hipErrorInvalidValue;
 }
 

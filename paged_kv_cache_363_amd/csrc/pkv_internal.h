@@ -49,8 +49,9 @@ struct DecodeArgs {
 int launch_decode_vector(const DecodeArgs& a);
 int launch_decode_mfma(const DecodeArgs& a);
 int launch_decode_reduce(const DecodeArgs& a);
-int launch_decode_stream(const DecodeArgs& a, int grid, uint32_t epoch, void* ws, size_t off_ml,
-                         size_t off_part);
+int launch_decode_stream(const DecodeArgs& a, int grid, void* ws, size_t off_ml, size_t off_part);
+int launch_decode_split_merge(const DecodeArgs& a, int grid, void* ws, size_t off_ml,
+                              size_t off_part);
 int launch_cache_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                         const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
                         int32_t head_dim, int32_t num_blocks, int32_t new_dtype, int32_t kv_dtype,

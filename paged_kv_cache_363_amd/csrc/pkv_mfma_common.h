@@ -261,4 +261,52 @@ struct MfmaTile {
   }
 };
 
+
+// Online-softmax pass of one wave over the blocks [b0, b1) of one
+// (sequence, kv-head) segment, continuing the running (m_run, l_run, o).
+//   kc, vc   : the caches, already offset to the segment's kv-head tile
+//   row      : the sequence's block-table row
+//   last     : index of the sequence's last block, tail its token count
+// Block ids come 64 at a time, one per lane of a VGPR, and are read back with
+// readlane.  K/V loads run DEPTH blocks ahead of the block being consumed.
+// Every load is issued unconditionally (ids past the chunk repeat its last
+// block, invalid ids read block 0 and carry no weight), so the load counter
+// can be waited on per block instead of drained.  nb must be > 0.
+template <int QT, int KVT, int D, int DEPTH>
+__device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
+                                           int64_t blk_stride, const int32_t* row, int b0,
+                                           int b1, int last, int tail, int nb, const uint4* qr,
+                                           float sl2, float& m_run, float& l_run, f32x4* o,
+                                           int lane) {
+  using T = MfmaTile<QT, KVT, D>;
+  using Raw = typename T::Raw;
+  const int c = lane & 15, G = lane >> 4;
+  for (int c0 = b0; c0 < b1; c0 += 64) {
+    const int n = min(64, b1 - c0);
+    const int ids = lane < n ? row[c0 + lane] : 0;
+    auto id_at = [&](int i) { return __builtin_amdgcn_readlane(ids, i < n ? i : n - 1); };
+    auto addr = [&](int id) { return (int64_t)((unsigned)id < (unsigned)nb ? id : 0) * blk_stride; };
+    Raw buf[DEPTH];
+    int idc[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      idc[d] = id_at(d);
+      const int64_t a = addr(idc[d]);
+      T::issue(buf[d], kc + a, vc + a, c, G);
+    }
+    for (int i = 0; i < n; i += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int ii = i + d;
+        const int idn = id_at(ii + DEPTH);
+        if (ii < n && (unsigned)idc[d] < (unsigned)nb)
+          T::consume(buf[d], c0 + ii == last ? tail : 16, qr, sl2, m_run, l_run, o, c, G);
+        const int64_t a = addr(idn);
+        T::issue(buf[d], kc + a, vc + a, c, G);
+        idc[d] = idn;
+      }
+    }
+  }
+}
+
 }  // namespace pkvd

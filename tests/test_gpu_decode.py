@@ -80,8 +80,9 @@ def test_balanced_schedule_any_grid(name, wgs):
 
 
 def test_balanced_schedule_ignores_stale_workspace():
-    """Arrival counters carry a per-call epoch: a workspace full of garbage or
-    left by earlier calls gives the same result, bit for bit."""
+    """The workspace only carries partials written and read within one call:
+    a workspace full of garbage or left by earlier calls gives the same
+    result, bit for bit."""
     import paged_kv_cache_363_amd as pkv
     name = "c2_qwen3_8b_bf16"
     st = gpu_state(name)
