@@ -40,6 +40,9 @@ def parse():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--all-configs", action="store_true",
                     help="also time the other workloads and add them under 'other_configs'")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB (10 times): the reference for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     return ap.parse_args()
 
 
@@ -49,6 +52,53 @@ def log(msg):
 
 def kv_elem_bytes(kv):
     return {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[kv]
+
+
+DT_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    """sha256 over the HIP/C++ sources of the library (what a counter profile
+    was taken of)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "paged_kv_cache_363_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def decode_path(cfg, algo, partition):
+    """(kernel name, kernel family, partition tokens) of the decode call a
+    step makes; partition 0 = the balanced schedule."""
+    import paged_kv_cache_363_amd as pkv
+    kv = DT_CODE[cfg.kv_dtype]
+    a = algo if algo != "auto" else pkv.decode_algo_for(cfg.num_q_heads, cfg.num_kv_heads,
+                                                        cfg.head_dim, DT_CODE[cfg.q_dtype], kv)
+    if a == "mfma" and partition == 0 and cfg.num_seqs <= 2048:
+        return "decode_stream_kernel", a, 0
+    # the fixed partition such a call uses (an f32 cache never takes the
+    # balanced schedule, so the helper reports the fixed choice)
+    ps = pkv.decode_partition_size(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                                   cfg.max_blocks_per_seq, DT_CODE["f32"], partition)
+    return ("decode_mfma_kernel" if a == "mfma" else "decode_vec_kernel"), a, ps
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from a committed counter
+    summary (profiles/<kernel>_<workload>_traffic.json), or None when there is
+    none or the library's sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def setup(cfg, dev):
@@ -166,11 +216,9 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
     achieved = kv_bytes / (part_avg * 1e-3) / 1e9
     res = dict(
         config=cfg.name, kv_bytes=kv_bytes, replicas=R, cache_bytes_per_replica=cache_bytes,
-        partition=pkv.decode_partition_size(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads,
-                                            cfg.head_dim, cfg.max_blocks_per_seq, 0, ps),
-        algo=args.algo if args.algo != "auto" else pkv.decode_algo_for(
-            cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
-            pkv.api._DT[st["q"].dtype], pkv.api._DT[st["k_cache"].dtype]),
+        kernel=decode_path(cfg, args.algo, ps)[0],
+        algo=decode_path(cfg, args.algo, ps)[1],
+        partition=decode_path(cfg, args.algo, ps)[2],
         ms_per_step=step_ms, wall_ms_per_step=wall / K * 1e3,
         decode_kernel_ms=part_avg, reduce_kernel_ms=red_avg,
         step_gbs=kv_bytes / (step_ms * 1e-3) / 1e9,
@@ -195,9 +243,7 @@ def cpu_baseline(cfg, st, budget_s, gpu_out):
     from oracle import oracle as orc
     from synth import gen
     ctx = st["ctx"]
-    est = int(math.ceil(budget_s / max(1e-9, 2.5e-8 * cfg.num_q_heads * cfg.head_dim *
-                                       float(ctx.max())))) + 1
-    order = [int(s) for s in np.argsort(-ctx, kind="stable")][:max(1, est)]
+    order = [int(s) for s in np.argsort(-ctx, kind="stable")]
     o = oracle_setup(cfg, order)
     qb = gen.bits(o["q"])
     eb = kv_elem_bytes(cfg.kv_dtype)
@@ -223,6 +269,21 @@ def cpu_baseline(cfg, st, budget_s, gpu_out):
             "gpu_rows_match_oracle": ok_all, "max_abs_err": worst}
 
 
+def copy_calibration():
+    """A plain device-to-device copy of exactly 1 GiB, ten times: under
+    rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE give the counter's scale
+    (2^30 bytes read and written per dispatch)."""
+    import torch
+    n = 2 ** 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 10}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -230,6 +291,9 @@ def main():
                                    "no multi-GPU mode in this build", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import paged_kv_cache_363_amd as pkv  # noqa: F401  (fails loudly if libpkv.so is missing)
     from synth import CONFIGS
     if not torch.cuda.is_available():
@@ -263,10 +327,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(res["decode_kernel_gbs"], 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(res["decode_kernel_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": None,
-                     "kernel": f"decode_{res['algo']}_kernel",
-                     "kernel_ms": round(res["decode_kernel_ms"], 5)},
-        "reduce_kernel_ms": round(res["reduce_kernel_ms"], 5),
+                     "traffic": measured_traffic(cfg.name, res["kernel"]),
+                     "kernel": res["kernel"],
+                     "kernel_ms": round(res["decode_kernel_ms"], 5),
+                     "algorithmic_bytes_per_launch": res["kv_bytes"]},
+        "merge_or_reduce_ms": round(res["reduce_kernel_ms"], 5),
         "host_bookkeeping_us_per_step": round(res["host_bookkeeping_us_per_step"], 1),
         "cpu_baseline": res.get("cpu_baseline"),
     }
@@ -282,7 +347,7 @@ def main():
                             "ms_per_step": round(r["ms_per_step"], 5),
                             "decode_kernel_ms": round(r["decode_kernel_ms"], 5),
                             "tokens_per_s": round(r["tokens_per_s"], 1), "algo": r["algo"],
-                            "partition": r["partition"]}
+                            "kernel": r["kernel"], "partition": r["partition"]}
             del r
             torch.cuda.empty_cache()
         line["other_configs"] = others

@@ -63,7 +63,8 @@ typedef enum {
 typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 } pkv_dtype;
 
 /* Which decode kernel family runs.  AUTO picks per shape (see
- * pkv_decode_algo_for).  VECTOR: per-lane fp32 arithmetic with wavefront
+ * pkv_decode_algo_for): MFMA when the q-head group g > 1 and the dtypes
+ * allow it, else VECTOR.  VECTOR: per-lane fp32 arithmetic with wavefront
  * reductions.  MFMA: QK^T and PV on the matrix cores (16-bit or FP8 caches,
  * 16-bit q). */
 typedef enum { PKV_ALGO_AUTO = 0, PKV_ALGO_VECTOR = 1, PKV_ALGO_MFMA = 2 } pkv_algo;
@@ -112,13 +113,15 @@ pkv_status pkv_paged_cache_append(void* k_cache, void* v_cache, const void* k_ne
 
 /* ------------------------------------------------------ decode attention -- */
 
-/* Effective partition size (tokens) a decode call with these arguments will
- * use: partition_size itself if > 0 (it must be a multiple of 16); for
- * partition_size 0, 0 when the call runs the balanced schedule (16-bit or
- * FP8 cache, at most 2048 sequences: the work is cut into equal shares of
- * 16-token blocks instead of fixed partitions), else the library's choice of
- * fixed partition.  A fixed-partition call whose max_blocks_per_seq * 16 fits
- * in one partition runs single-pass.  Returns -1 on bad arguments. */
+/* Effective partition size (tokens) an AUTO decode call with these arguments
+ * will use: partition_size itself if > 0 (it must be a multiple of 16); for
+ * partition_size 0, 0 when the call runs the balanced schedule (q-head group
+ * g > 1 with a 16-bit or FP8 cache, at most 2048 sequences: the work is cut
+ * into equal shares of 16-token blocks instead of fixed partitions), else
+ * the library's choice of fixed partition (a single pass when the sequences
+ * times kv-heads reach 2048).  A fixed-partition call whose
+ * max_blocks_per_seq * 16 fits in one partition runs single-pass.  Returns -1
+ * on bad arguments. */
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_blocks_per_seq, int32_t kv_dtype,
                                   int32_t partition_size);
@@ -160,10 +163,11 @@ int32_t pkv_decode_algo_for(int32_t num_q_heads, int32_t num_kv_heads, int32_t h
  *   shape limits : block_size 16; head_dim 64 or 128; num_q_heads a multiple
  *                  of num_kv_heads.
  *   partition_size: 0 = library's schedule (balanced shares on the matrix
- *                  cores when algo is AUTO or MFMA and the cache is 16-bit or
- *                  FP8, else fixed partitions of its choice), else a multiple
- *                  of 16 in [16, 2^20] (fixed partitions plus the reduction
- *                  kernel).
+ *                  cores, then a merge kernel for the segments split between
+ *                  waves, when the algo resolves to MFMA and the cache is
+ *                  16-bit or FP8; else fixed partitions of its choice), else
+ *                  a multiple of 16 in [16, 2^20] (fixed partitions plus the
+ *                  reduction kernel when a context spans several).
  *   workspace    : device memory of at least pkv_decode_workspace_size(...)
  *                  bytes (may be NULL when that is 0).  Its contents on entry
  *                  do not matter; calls sharing one workspace must not

@@ -42,8 +42,11 @@ static bool decode_pair_ok(int32_t q, int32_t kv) {
 }
 
 static int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx) {
-  // Enough workgroups to cover 256 CUs several times over, without cutting
-  // contexts into slivers whose partials cost more than they save.
+  // One workgroup per (sequence, kv-head) already gives 8 workgroups per CU
+  // of a 256-CU MI355X: run single-pass, with no partials and no reduction.
+  if ((int64_t)num_seqs * num_kv_heads >= 2048) return max_ctx > kBlockSize ? max_ctx : kBlockSize;
+  // Otherwise enough partitions to cover the CUs several times over, without
+  // cutting contexts into slivers whose partials cost more than they save.
   int32_t ps = 512;
   while (ps > 128) {
     const int64_t units = (int64_t)num_seqs * num_kv_heads * ((max_ctx + ps - 1) / ps);
@@ -53,10 +56,12 @@ static int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t 
   return ps;
 }
 
+// AUTO: the matrix cores when the q-head group makes QK^T and PV real
+// contractions (g > 1) and the dtypes allow it; for g = 1 an MFMA tile would
+// use one of its 16 columns, so the vector kernel serves.
 static int32_t resolve_algo(int32_t g, int32_t q, int32_t kv) {
   const bool mfma_ok = (q == PKV_F16 || q == PKV_BF16) && (kv == q || kv == PKV_FP8_E4M3);
-  (void)g;
-  return mfma_ok ? PKV_ALGO_MFMA : PKV_ALGO_VECTOR;
+  return mfma_ok && g > 1 ? PKV_ALGO_MFMA : PKV_ALGO_VECTOR;
 }
 
 static std::atomic<int32_t> g_stream_workgroups{kDefaultStreamWorkgroups};
@@ -205,7 +210,8 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t
   if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, kv_dtype,
                  partition_size, &plan))
     return -1;
-  return plan.stream_ok ? 0 : plan.partition;
+  // AUTO runs the balanced schedule for a q-head group g > 1 (see resolve_algo)
+  return plan.stream_ok && num_q_heads / num_kv_heads > 1 ? 0 : plan.partition;
 }
 
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

@@ -73,7 +73,11 @@ def test_workspace_and_partition_helpers():
     assert n >= rows * (128 + 2) * 4
     assert l.pkv_decode_partition_size(1, 1, 1, 128, 4, 2, 24) == -1
     assert l.pkv_decode_algo_for(64, 8, 128, _lib.PKV_BF16, _lib.PKV_FP8_E4M3) == _lib.PKV_ALGO_MFMA
-    assert l.pkv_decode_algo_for(32, 32, 128, _lib.PKV_F16, _lib.PKV_F16) == _lib.PKV_ALGO_MFMA
+    # MHA (g = 1): the vector kernel; one WG per (sequence, kv-head) fills the GPU -> single pass
+    assert l.pkv_decode_algo_for(32, 32, 128, _lib.PKV_F16, _lib.PKV_F16) == _lib.PKV_ALGO_VECTOR
+    assert l.pkv_decode_algo_for(32, 16, 128, _lib.PKV_F16, _lib.PKV_F16) == _lib.PKV_ALGO_MFMA
+    assert l.pkv_decode_partition_size(256, 32, 32, 128, 128, _lib.PKV_F16, 0) == 2048
+    assert l.pkv_decode_workspace_size(256, 32, 32, 128, 128, _lib.PKV_F16, 2048) == 0
     assert l.pkv_decode_algo_for(4, 2, 64, _lib.PKV_F32, _lib.PKV_F32) == _lib.PKV_ALGO_VECTOR
     assert l.pkv_decode_algo_for(4, 2, 96, _lib.PKV_F32, _lib.PKV_F32) == -1
 
