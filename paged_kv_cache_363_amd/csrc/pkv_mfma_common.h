@@ -162,23 +162,35 @@ struct MfmaTile {
     }
   }
 
+  // Byte offsets of a lane's first K and V element inside a tile; the other
+  // loads of the lane sit at fixed distances from them.  Unsigned 32-bit, so
+  // that a load is a wave-uniform base plus one lane offset (the SGPR-base
+  // form of global_load) with no per-lane 64-bit address arithmetic.
+  __device__ static uint32_t k_lane_off(int c, int G) {
+    return FP8 ? (uint32_t)(c * D + 16 * G) : (uint32_t)((c * D + 8 * G) * 2);
+  }
+  __device__ static uint32_t v_lane_off(int c, int G) {
+    return (uint32_t)((4 * G * D + DPL * c) * KVB);
+  }
+
+  __device__ static void issue(Raw& r, const uint8_t* kt, const uint8_t* vt, uint32_t koff,
+                               uint32_t voff) {
+    const uint8_t* kp = kt + koff;
+    const uint8_t* vp = vt + voff;
+#pragma unroll
+    for (int kk = 0; kk < KL; ++kk)
+      r.k[kk] = *reinterpret_cast<const uint4*>(kp + (FP8 ? 64 * kk : 64 * kk));
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) r.v[rr] = load_row<ROWB>(vp + rr * D * KVB);
+  }
   __device__ static void issue(Raw& r, const uint8_t* kt, const uint8_t* vt, int c, int G) {
-    if constexpr (FP8) {
-#pragma unroll
-      for (int mm = 0; mm < KL; ++mm)
-        r.k[mm] = *reinterpret_cast<const uint4*>(kt + c * D + 64 * mm + 16 * G);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < KL; ++kk)
-        r.k[kk] = *reinterpret_cast<const uint4*>(kt + (c * D + 32 * kk + 8 * G) * 2);
-    }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      r.v[rr] = load_row<ROWB>(vt + ((4 * G + rr) * D + DPL * c) * KVB);
+    issue(r, kt, vt, k_lane_off(c, G), v_lane_off(c, G));
   }
 
   // Online-softmax update of (m_run, l_run, o) with one tile holding `valid`
-  // live tokens.  qr: raw q operand (zeros for padding heads).
+  // live tokens (0 = none: the state does not change, and the tile's
+  // registers are still read, so the caller need not branch around it).
+  // qr: raw q operand (zeros for padding heads).
   __device__ static void consume(Raw& r, int valid, const uint4* qr, float sl2, float& m_run,
                                  float& l_run, f32x4* o, int c, int G) {
     V8 kop[KSTEPS];
@@ -216,10 +228,13 @@ struct MfmaTile {
     float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     bm = wave_max4(bm);
     const float m_new = fmaxf(m_run, bm);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // A tile with no valid token so far (m_new still -inf) shifts by 0, so
+    // that it leaves the state at zero instead of producing NaN.
+    const float m_ref = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
     float pr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
+    for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_ref);
     l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
     m_run = m_new;
     if (__any(alpha != 1.0f)) {
@@ -299,8 +314,9 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
       for (int d = 0; d < DEPTH; ++d) {
         const int ii = i + d;
         const int idn = id_at(ii + DEPTH);
-        if (ii < n && (unsigned)idc[d] < (unsigned)nb)
-          T::consume(buf[d], c0 + ii == last ? tail : 16, qr, sl2, m_run, l_run, o, c, G);
+        const int valid = (ii < n && (unsigned)idc[d] < (unsigned)nb)
+                              ? (c0 + ii == last ? tail : 16) : 0;
+        T::consume(buf[d], valid, qr, sl2, m_run, l_run, o, c, G);
         const int64_t a = addr(idn);
         T::issue(buf[d], kc + a, vc + a, c, G);
         idc[d] = idn;
