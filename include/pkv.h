@@ -76,8 +76,9 @@ const char* pkv_status_string(int32_t status);
 int32_t pkv_version(void);
 
 /* Workgroups (of 4 waves) the balanced decode schedule launches; 0 restores
- * the default (512, two per CU of an MI355X).  Process-wide; it changes what
- * pkv_decode_workspace_size returns, so set it before sizing workspaces. */
+ * the default (256: one wave on every SIMD of a 256-CU MI355X).
+ * Process-wide; it changes what pkv_decode_workspace_size returns, so set it
+ * before sizing workspaces. */
 pkv_status pkv_set_stream_workgroups(int32_t n);
 
 /* --------------------------------------------------------------- sizes -- */

@@ -29,7 +29,10 @@
 #include "pkv_mfma_common.h"
 
 #ifndef PKV_PIPE_DEPTH
-#define PKV_PIPE_DEPTH 2   // K/V blocks in flight per wave
+#define PKV_PIPE_DEPTH 2       // K/V blocks in flight per wave, 16-bit caches
+#endif
+#ifndef PKV_PIPE_DEPTH_FP8
+#define PKV_PIPE_DEPTH_FP8 2   // same for E4M3 caches
 #endif
 
 namespace {
@@ -191,7 +194,8 @@ void decode_stream_kernel(StreamParams p) {
     const int last = ((ctx + 15) >> 4) - 1;
     if (p.nb > 0) {
       const int64_t off = (int64_t)hk * T::TILE;
-      mfma_piece<QT, KVT, D, PKV_PIPE_DEPTH>(p.kc + off, p.vc + off, blk_stride,
+      mfma_piece<QT, KVT, D, KVT == PKV_FP8_E4M3 ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
+                 KVT != PKV_FP8_E4M3>(p.kc + off, p.vc + off, blk_stride,
                                              p.bt + (int64_t)s * p.mb, b, b1, last,
                                              ctx - 16 * last, p.nb, qr, p.sl2, m_run, l_run, o,
                                              lane);

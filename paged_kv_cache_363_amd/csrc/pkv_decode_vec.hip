@@ -92,9 +92,9 @@ __global__ __launch_bounds__(64 * pkv::kWaves) void decode_vec_kernel(DecodePara
     const uint4* vt = reinterpret_cast<const uint4*>(p.vc + phys * blk_stride + head_off);
     uint4 kr[NJ], vr[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) kr[j] = kt[j * 64 + lane];
+    for (int j = 0; j < NJ; ++j) kr[j] = ld_tile16<true>(kt + j * 64 + lane);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) vr[j] = vt[j * 64 + lane];
+    for (int j = 0; j < NJ; ++j) vr[j] = ld_tile16<true>(vt + j * 64 + lane);
 
     float z[NJ][GMAX];
 #pragma unroll

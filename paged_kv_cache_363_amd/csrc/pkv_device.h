@@ -17,6 +17,44 @@ typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+// Loads of cache tiles.  Every K/V byte of a decode step is read once, so
+// the streaming form carries the non-temporal hint and does not displace
+// other lines from the L2 and the Infinity Cache.  Measured on MI355X: random
+// 4 KiB tiles stream at 6.8 TB/s with the hint against 6.1 TB/s without, and
+// the balanced kernel on 16-bit caches gains 7-14%; the fixed-partition
+// kernel and E4M3 caches measure faster with ordinary loads (with the hint
+// the fixed-partition kernel fetches 12% more bytes from HBM), so NT is a
+// choice per call site.
+template <bool NT>
+__device__ __forceinline__ uint4 ld_tile16(const void* p) {
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    return *reinterpret_cast<const uint4*>(p);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ uint2 ld_tile8(const void* p) {
+  if constexpr (NT) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(v.x, v.y);
+  } else {
+    return *reinterpret_cast<const uint2*>(p);
+  }
+}
+template <bool NT>
+__device__ __forceinline__ uint32_t ld_tile4(const void* p) {
+  if constexpr (NT) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  } else {
+    return *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 

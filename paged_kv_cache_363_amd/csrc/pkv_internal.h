@@ -25,7 +25,7 @@ constexpr int kBlockSize = 16;   // tokens per physical block
 constexpr int kWaves = 4;        // waves per decode workgroup
 constexpr int kMaxPartition = 1 << 20;
 constexpr int kMaxStreamSeqs = 2048;        // sequences the balanced schedule handles per call
-constexpr int kDefaultStreamWorkgroups = 512;  // 2 per CU on a 256-CU MI355X
+constexpr int kDefaultStreamWorkgroups = 256;  // one wave per SIMD of a 256-CU MI355X
 
 struct DecodeArgs {
   void* out;

@@ -110,17 +110,17 @@ struct Row<16> {
   uint32_t w[4];
 };
 
-template <int BYTES>
+template <int BYTES, bool NT>
 __device__ __forceinline__ Row<BYTES> load_row(const uint8_t* ptr) {
   Row<BYTES> r;
   if constexpr (BYTES == 16) {
-    uint4 v = *reinterpret_cast<const uint4*>(ptr);
+    uint4 v = ld_tile16<NT>(ptr);
     r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
   } else if constexpr (BYTES == 8) {
-    uint2 v = *reinterpret_cast<const uint2*>(ptr);
+    uint2 v = ld_tile8<NT>(ptr);
     r.w[0] = v.x; r.w[1] = v.y;
   } else {
-    r.w[0] = *reinterpret_cast<const uint32_t*>(ptr);
+    r.w[0] = ld_tile4<NT>(ptr);
   }
   return r;
 }
@@ -173,18 +173,16 @@ struct MfmaTile {
     return (uint32_t)((4 * G * D + DPL * c) * KVB);
   }
 
+  // NT: non-temporal (streaming) loads, see ld_tile16
+  template <bool NT>
   __device__ static void issue(Raw& r, const uint8_t* kt, const uint8_t* vt, uint32_t koff,
                                uint32_t voff) {
     const uint8_t* kp = kt + koff;
     const uint8_t* vp = vt + voff;
 #pragma unroll
-    for (int kk = 0; kk < KL; ++kk)
-      r.k[kk] = *reinterpret_cast<const uint4*>(kp + (FP8 ? 64 * kk : 64 * kk));
+    for (int kk = 0; kk < KL; ++kk) r.k[kk] = ld_tile16<NT>(kp + 64 * kk);
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) r.v[rr] = load_row<ROWB>(vp + rr * D * KVB);
-  }
-  __device__ static void issue(Raw& r, const uint8_t* kt, const uint8_t* vt, int c, int G) {
-    issue(r, kt, vt, k_lane_off(c, G), v_lane_off(c, G));
+    for (int rr = 0; rr < 4; ++rr) r.v[rr] = load_row<ROWB, NT>(vp + rr * D * KVB);
   }
 
   // Online-softmax update of (m_run, l_run, o) with one tile holding `valid`
@@ -287,7 +285,7 @@ struct MfmaTile {
 // Every load is issued unconditionally (ids past the chunk repeat its last
 // block, invalid ids read block 0 and carry no weight), so the load counter
 // can be waited on per block instead of drained.  nb must be > 0.
-template <int QT, int KVT, int D, int DEPTH>
+template <int QT, int KVT, int D, int DEPTH, bool NT>
 __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
                                            int64_t blk_stride, const int32_t* row, int b0,
                                            int b1, int last, int tail, int nb, const uint4* qr,
@@ -296,6 +294,7 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
   using T = MfmaTile<QT, KVT, D>;
   using Raw = typename T::Raw;
   const int c = lane & 15, G = lane >> 4;
+  const uint32_t koff = T::k_lane_off(c, G), voff = T::v_lane_off(c, G);
   for (int c0 = b0; c0 < b1; c0 += 64) {
     const int n = min(64, b1 - c0);
     const int ids = lane < n ? row[c0 + lane] : 0;
@@ -307,7 +306,7 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
     for (int d = 0; d < DEPTH; ++d) {
       idc[d] = id_at(d);
       const int64_t a = addr(idc[d]);
-      T::issue(buf[d], kc + a, vc + a, c, G);
+      T::template issue<NT>(buf[d], kc + a, vc + a, koff, voff);
     }
     for (int i = 0; i < n; i += DEPTH) {
 #pragma unroll
@@ -318,7 +317,7 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
                               ? (c0 + ii == last ? tail : 16) : 0;
         T::consume(buf[d], valid, qr, sl2, m_run, l_run, o, c, G);
         const int64_t a = addr(idn);
-        T::issue(buf[d], kc + a, vc + a, c, G);
+        T::template issue<NT>(buf[d], kc + a, vc + a, koff, voff);
         idc[d] = idn;
       }
     }
