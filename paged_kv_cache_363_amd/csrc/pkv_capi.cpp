@@ -113,7 +113,8 @@ static bool make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
   const int64_t Y = (int64_t)num_kv_heads * ((g + chunk - 1) / chunk);
   plan->stream_ok = partition_size == 0 && stream_capable_kv(kv_dtype) &&
                     num_seqs <= kMaxStreamSeqs &&
-                    (int64_t)num_seqs * max_blocks_per_seq * Y < ((int64_t)1 << 31);
+                    (int64_t)num_seqs * (max_blocks_per_seq + kv_restart_units(kv_dtype)) * Y <
+                        ((int64_t)1 << 31);
   plan->stream_grid = g_stream_workgroups.load();
   plan->stream_off_ml = plan->stream_off_part = plan->stream_bytes = 0;
   if (plan->stream_ok) {

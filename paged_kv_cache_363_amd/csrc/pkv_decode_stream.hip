@@ -53,10 +53,16 @@ struct StreamParams {
   float* part;                 // [2 W][chunk_heads][D]
   float* ml;                   // [2 W][chunk_heads][2]
   int W;                       // waves of the decode grid
+  int R;                       // restart units counted at the start of every segment
 };
 
-// Block prefix sums of the (clamped) context lengths in LDS, computed by one
-// workgroup of 4 waves: pref[s] = blocks of the sequences before s.
+// Unit prefix sums in LDS, computed by one workgroup of 4 waves.  A segment
+// of a sequence with nbk blocks spans nbk + R units: R units that stand for
+// the cost of starting a piece (the q rows and block ids must arrive before
+// the first K/V loads can go out) followed by one unit per block.  Equal
+// shares of units are then equal in time, not just in blocks.
+// pref[s] = units of one segment of each sequence before s (0 for a
+// sequence without context).
 __device__ __forceinline__ void block_prefix(const StreamParams& p, int* sm_pref, int* sm_ctx) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int S = p.S;
@@ -70,7 +76,8 @@ __device__ __forceinline__ void block_prefix(const StreamParams& p, int* sm_pref
     int carry = 0;
     for (int base = 0; base < S; base += 64) {
       const int i = base + lane;
-      int x = i < S ? (sm_ctx[i] + 15) >> 4 : 0;
+      const int nbk = i < S ? (sm_ctx[i] + 15) >> 4 : 0;
+      int x = nbk > 0 ? nbk + p.R : 0;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(x, off);
@@ -91,7 +98,7 @@ void decode_stream_kernel(StreamParams p) {
   constexpr int DPL = T::DPL;
   constexpr int KS = T::KSTEPS;
 
-  __shared__ int sm_pref[pkv::kMaxStreamSeqs + 1];   // blocks before sequence s
+  __shared__ int sm_pref[pkv::kMaxStreamSeqs + 1];   // segment units before sequence s
   __shared__ int sm_ctx[pkv::kMaxStreamSeqs];        // clamped context lengths
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -114,9 +121,10 @@ void decode_stream_kernel(StreamParams p) {
   auto share = [&](int64_t k) { return (U * k) / We; };
   const int64_t u_lo = share(wk), u_hi = share(wk + 1);
 
-  // unit u -> (sequence s, segment y, block b): s is the last sequence whose
-  // first unit is <= u (sequences without blocks own no unit)
-  auto locate = [&](int64_t u, int& s, int& y, int& b) {
+  // unit u -> (sequence s, segment y, position j in the segment's units): s
+  // is the last sequence whose first unit is <= u (sequences without blocks
+  // own no unit)
+  auto locate = [&](int64_t u, int& s, int& y, int& j) {
     int lo = 0, hi = S - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -124,10 +132,10 @@ void decode_stream_kernel(StreamParams p) {
       else hi = mid - 1;
     }
     s = lo;
-    const int nbk = sm_pref[s + 1] - sm_pref[s];
+    const int len = sm_pref[s + 1] - sm_pref[s];
     const int64_t r = u - Y * sm_pref[s];
-    y = (int)(r / nbk);
-    b = (int)(r - (int64_t)y * nbk);
+    y = (int)(r / len);
+    j = (int)(r - (int64_t)y * len);
   };
 
   const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
@@ -143,7 +151,7 @@ void decode_stream_kernel(StreamParams p) {
 
   // Close the piece [b0, b_last] of segment (s, y): store or merge.
   auto finish = [&](int s, int y, int b0, int b_last, bool first_piece) {
-    const int nbk = sm_pref[s + 1] - sm_pref[s];
+    const int nbk = sm_pref[s + 1] - sm_pref[s] - p.R;
     const int hc = y % p.hchunks;
     const int h_first = (y / p.hchunks) * p.g + hc * p.chunk_heads;
     const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
@@ -174,36 +182,41 @@ void decode_stream_kernel(StreamParams p) {
     }
   };
 
-  // Walk the share piece by piece: a piece is the part of one segment that
-  // lies in [u_lo, u_hi).  Segments follow each other in (sequence, y)
-  // order; sequences without blocks own no segment.
+  // Walk the share piece by piece: a piece is the part of one segment's
+  // blocks that lies in [u_lo, u_hi).  Segments follow each other in
+  // (sequence, y) order; sequences without blocks own no segment.  A piece
+  // made of restart units only has no block and is skipped.
   int64_t u = u_lo;
-  int s, y, b;
-  locate(u, s, y, b);
+  int s, y, j;
+  locate(u, s, y, j);
+  bool first_piece = true;
   while (true) {
-    const int nbk = sm_pref[s + 1] - sm_pref[s];
-    const int64_t seg_end = Y * sm_pref[s] + (int64_t)(y + 1) * nbk;
-    const int64_t pe = seg_end < u_hi ? seg_end : u_hi;
-    const int b1 = b + (int)(pe - u);
-    const int hc = y % p.hchunks;
-    const int hk = y / p.hchunks;
-    const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
-    T::load_q(qr, p.q, (int64_t)s * p.Hq + hk * p.g + hc * p.chunk_heads + c, c < nh, G);
-    reset();
-    const int ctx = sm_ctx[s];
-    const int last = ((ctx + 15) >> 4) - 1;
-    if (p.nb > 0) {
-      const int64_t off = (int64_t)hk * T::TILE;
-      mfma_piece<QT, KVT, D, KVT == PKV_FP8_E4M3 ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
-                 KVT != PKV_FP8_E4M3>(p.kc + off, p.vc + off, blk_stride,
-                                             p.bt + (int64_t)s * p.mb, b, b1, last,
-                                             ctx - 16 * last, p.nb, qr, p.sl2, m_run, l_run, o,
-                                             lane);
+    const int len = sm_pref[s + 1] - sm_pref[s];
+    const int64_t seg_start = Y * sm_pref[s] + (int64_t)y * len;
+    const int64_t pe = seg_start + len < u_hi ? seg_start + len : u_hi;
+    const int b = max(j - p.R, 0);
+    const int b1 = max((int)(pe - seg_start) - p.R, 0);
+    if (b1 > b) {
+      const int hc = y % p.hchunks;
+      const int hk = y / p.hchunks;
+      const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
+      T::load_q(qr, p.q, (int64_t)s * p.Hq + hk * p.g + hc * p.chunk_heads + c, c < nh, G);
+      reset();
+      const int ctx = sm_ctx[s];
+      const int last = ((ctx + 15) >> 4) - 1;
+      if (p.nb > 0) {
+        const int64_t off = (int64_t)hk * T::TILE;
+        mfma_piece<QT, KVT, D, KVT == PKV_FP8_E4M3 ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
+                   KVT != PKV_FP8_E4M3>(p.kc + off, p.vc + off, blk_stride,
+                                        p.bt + (int64_t)s * p.mb, b, b1, last, ctx - 16 * last,
+                                        p.nb, qr, p.sl2, m_run, l_run, o, lane);
+      }
+      finish(s, y, b, b1 - 1, first_piece);
+      first_piece = false;
     }
-    finish(s, y, b, b1 - 1, u == u_lo);
     u = pe;
     if (u >= u_hi) break;
-    b = 0;
+    j = 0;
     if (++y == p.Y) {
       y = 0;
       do {
@@ -240,14 +253,16 @@ __global__ __launch_bounds__(64 * kSkWaves) void decode_split_merge_kernel(Strea
     const int hc = y % p.hchunks;
     const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
     if (h >= nh) continue;
-    const int nbk = sm_pref[s + 1] - sm_pref[s];
-    if (nbk == 0) continue;
-    const int64_t seg_start = Y * sm_pref[s] + (int64_t)y * nbk;
-    const int64_t wa = ((seg_start + 1) * We - 1) / U;
-    const int64_t wb = ((seg_start + nbk) * We - 1) / U;
+    const int len = sm_pref[s + 1] - sm_pref[s];
+    if (len == 0) continue;
+    // the segment's blocks are its units [seg_start + R, seg_start + len)
+    const int64_t seg_start = Y * sm_pref[s] + (int64_t)y * len;
+    const int64_t wa = ((seg_start + p.R + 1) * We - 1) / U;
+    const int64_t wb = ((seg_start + len) * We - 1) / U;
     if (wa == wb) continue;
-    // the first worker's piece is its last one unless its share starts here
-    const int64_t sl0 = 2 * wa + ((U * wa) / We == seg_start ? 0 : 1);
+    // the first worker's piece is its first piece with blocks unless its
+    // share holds blocks of the segment before (units below seg_start)
+    const int64_t sl0 = 2 * wa + ((U * wa) / We >= seg_start ? 0 : 1);
     const int np = (int)(wb - wa + 1);
     auto slot_of = [&](int k) { return k == 0 ? sl0 : 2 * (wa + k); };
     float acc[PER];
@@ -350,6 +365,7 @@ StreamParams make_stream_params(const pkv::DecodeArgs& a, int grid, void* ws, si
   sp.ml = reinterpret_cast<float*>(w + off_ml);
   sp.part = reinterpret_cast<float*>(w + off_part);
   sp.W = grid * kSkWaves;
+  sp.R = pkv::kv_restart_units(a.kv_dtype);
   return sp;
 }
 

@@ -27,6 +27,22 @@ constexpr int kMaxPartition = 1 << 20;
 constexpr int kMaxStreamSeqs = 2048;        // sequences the balanced schedule handles per call
 constexpr int kDefaultStreamWorkgroups = 256;  // one wave per SIMD of a 256-CU MI355X
 
+// Units the balanced schedule charges for starting a piece of a segment, in
+// blocks: a start costs about two loaded HBM round trips (q rows and block
+// ids, then the first K/V tiles), ~2 us, against ~1.3 us per 16-bit block and
+// ~0.7 us per E4M3 block per wave at one wave per SIMD.  The 16-bit value is
+// the measured best on ragged batches (c2-shaped: 1 unit 5.68 TB/s, 2: 5.80,
+// 3: 5.92, 4: 5.96, 6: 5.94); E4M3 keeps the cost estimate.
+#ifndef PKV_RESTART_UNITS_16
+#define PKV_RESTART_UNITS_16 4
+#endif
+#ifndef PKV_RESTART_UNITS_FP8
+#define PKV_RESTART_UNITS_FP8 3
+#endif
+inline int kv_restart_units(int32_t kv_dtype) {
+  return kv_dtype == PKV_FP8_E4M3 ? PKV_RESTART_UNITS_FP8 : PKV_RESTART_UNITS_16;
+}
+
 struct DecodeArgs {
   void* out;
   const void* q;
