@@ -3,8 +3,10 @@
 
 A step is one pass of the whole decode hot path over one batch: the cache
 append of every sequence's new token (slot_mapping write) followed by paged
-decode attention over each sequence's context (partition kernel, plus the
-log-sum-exp reduction kernel when the context is split).  The block tables,
+decode attention over each sequence's context (the decode kernel, plus the
+merge or reduction kernel when contexts are split).  The timed region runs
+K steps back to back; a second pass of K steps records HIP events around
+the decode kernel for its own duration (the roofline figure).  The block tables,
 context lengths and slot mapping come from the native block pool, built
 before the timed region (its host cost per step is measured separately).
 
@@ -59,13 +61,14 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def kernel_source_hash():
-    """sha256 over the HIP/C++ sources of the library (what a counter profile
-    was taken of)."""
+    """sha256 over the sources that decide what the GPU runs (kernels, device
+    headers, the launch code): what a counter profile was taken of.  The host
+    block pool is left out; it never touches the device."""
     import hashlib
     csrc = os.path.join(ROOT, "paged_kv_cache_363_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        if name.endswith((".hip", ".h", ".cpp")) and name != "pkv_pool.cpp":
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -137,23 +140,28 @@ def setup(cfg, dev):
 
 
 def host_bookkeeping_us(cfg, st):
-    """Host time per decode step of the block bookkeeping: one append_slots
-    call per sequence on a copy of the tables (the real step's a1)."""
+    """Host time of one decode step's block bookkeeping (slots, new blocks,
+    copy-on-write) for the whole batch: one pkv_batch_append_slots call on the
+    decode layout, timed over successive steps from the workload's state."""
+    import numpy as np
     import paged_kv_cache_363_amd as pkv
     from synth import gen
-    nb = st["nb"]
-    pool = pkv.BlockPool(nb, cfg.block_size, gen.free_order(cfg, nb))
     from synth.scenario import build_state
+    nb = st["nb"]
     ctx = st["ctx"]
-    # rebuild to the pre-step state but stop before the step's own append
-    cfg_pre = cfg
-    state = build_state(cfg_pre, pool, ctx)
-    tables = [list(t) for t in state["tables"]]
+    pool = pkv.BlockPool(nb, cfg.block_size, gen.free_order(cfg, nb))
+    state = build_state(cfg, pool, ctx)
     reps = 20
+    mb = cfg.max_blocks_per_seq + -(-reps // cfg.block_size) + 1
+    rows = np.full((cfg.num_seqs, mb), -1, np.int32)
+    for s, t in enumerate(state["tables"]):
+        rows[s, :len(t)] = t
+    nblk = np.array([len(t) for t in state["tables"]], np.int32)
+    lens = np.asarray(ctx, np.int32).copy()
+    slots = np.empty(cfg.num_seqs, np.int64)
     t0 = time.perf_counter()
     for _ in range(reps):
-        for s in range(cfg.num_seqs):
-            pool.seq_append_slots(tables[s], int(ctx[s]) - 1, 1, cfg.max_blocks_per_seq)
+        pool.batch_append_slots(rows, nblk, lens, slot_mapping=slots)
     return (time.perf_counter() - t0) / reps * 1e6
 
 
@@ -193,26 +201,35 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
     torch.cuda.synchronize()
     log(f"warmup done ({R} replicas)")
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for trio in evs:       # create the underlying HIP events before handing them over
-        for e in trio:
-            e.record(stream)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    # Timed region: K whole steps back to back, nothing recorded between the
+    # kernels (an event record on the stream costs ~3 us of GPU time).
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(K):
-        step(i, evs[i])
+        step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
+    step_ms = total_ms / K
+    # Kernel pass: the same K steps again, with HIP events recorded by the
+    # library on the launch stream right before and after the decode kernel
+    # and after the merge/reduction kernel: the decode kernel's own duration.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for trio in evs:       # create the underlying HIP events before handing them over
+        for e in trio:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     part_ms = [a.elapsed_time(b) for a, b, _ in evs]
     red_ms = [b.elapsed_time(c) for _, b, c in evs]
     part_avg = sum(part_ms) / K
     red_avg = sum(red_ms) / K
-    step_ms = total_ms / K
     achieved = kv_bytes / (part_avg * 1e-3) / 1e9
     res = dict(
         config=cfg.name, kv_bytes=kv_bytes, replicas=R, cache_bytes_per_replica=cache_bytes,

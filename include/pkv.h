@@ -274,6 +274,33 @@ pkv_status pkv_seq_fork(pkv_pool* pool, const int32_t* table, int32_t nblocks);
 pkv_status pkv_seq_append_slots(pkv_pool* pool, int32_t* table, int32_t* nblocks, int32_t cap,
                                 int32_t cur_len, int32_t n_new, int64_t* slots_out,
                                 int32_t* cow_pairs, int32_t cow_cap, int32_t* n_cow);
+/* One decode step's bookkeeping for a whole batch in one call ("vLLM推理引擎
+ * 深度解析", section 2.2: a new block each time 16 more tokens are produced;
+ * "大语言模型推理引擎深度剖析", section 2.3: a shared block is copied before it
+ * is written).  The same as pkv_seq_append_slots applied to sequences
+ * 0 .. num_seqs-1 in that order, on the decode layout directly:
+ *   block_tables : host int32[num_seqs][max_blocks_per_seq], row s is sequence
+ *                  s's table; entries past nblocks[s] are free to overwrite.
+ *   nblocks      : host int32[num_seqs], blocks in each row (in/out).
+ *   context_lens : host int32[num_seqs], tokens already held (in); on return
+ *                  each has grown by its n_new, as the decode call expects.
+ *   n_new        : host int32[num_seqs] positions to add per sequence, or NULL
+ *                  for one each (a decode step).
+ *   slot_mapping : host int64[sum of n_new], slots of the new positions,
+ *                  sequence by sequence, as pkv_paged_cache_append takes them.
+ *   cow_pairs    : host int32[2*cow_cap]: (src, dst) for pkv_copy_blocks, in
+ *                  the order the copies are made; *n_cow receives their count
+ *                  and *n_slots (may be NULL) the length of slot_mapping.
+ * A shared block written by several sequences of the batch is copied by all
+ * but the last of its holders when every holder writes it.  All-or-nothing:
+ * any error (PKV_ERR_OUT_OF_BLOCKS, or PKV_ERR_INVALID_ARG for a gap, a full
+ * row, a bad block, cow_cap too small) leaves the pool, the tables, nblocks
+ * and context_lens unchanged. */
+pkv_status pkv_batch_append_slots(pkv_pool* pool, int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, int32_t* nblocks,
+                                  int32_t* context_lens, const int32_t* n_new, int32_t num_seqs,
+                                  int64_t* slot_mapping, int32_t* cow_pairs, int32_t cow_cap,
+                                  int32_t* n_cow, int32_t* n_slots);
 /* Release a sequence: decref its blocks from the last to the first. */
 pkv_status pkv_seq_free(pkv_pool* pool, const int32_t* table, int32_t nblocks);
 

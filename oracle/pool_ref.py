@@ -23,8 +23,12 @@ Readings where the pages leave a choice:
   - a sequence is freed from its last block to its first;
   - a write into an existing block whose count is above one copies it first
     (copy-on-write), whether or not the block is full;
-  - an append that cannot get every block it needs fails and changes nothing.
+  - an append that cannot get every block it needs fails and changes nothing;
+  - a batch append (one decode step's bookkeeping for many sequences) is the
+    single-sequence append applied to each sequence in batch order, and it
+    too either succeeds for every sequence or changes nothing.
 """
+import copy
 from collections import deque
 
 
@@ -143,6 +147,29 @@ class RefPool:
             else:
                 table.append(self.alloc())
         slots = [table[p // bs] * bs + p % bs for p in range(cur_len, cur_len + n_new)]
+        return slots, cows
+
+    def batch_append_slots(self, tables, lens, n_new, cap=None):
+        """One step's bookkeeping for a batch: sequence s, whose table is
+        tables[s] and whose length is lens[s], gets n_new[s] positions, in
+        order s = 0, 1, ...  tables and lens are updated in place.  Returns
+        (slots, cow_pairs): the slots of every new position, sequence by
+        sequence, and the copies in the order they were made.  On any error
+        the pool, the tables and the lengths are as before."""
+        saved = (copy.deepcopy(tables), list(lens), deque(self.free), list(self.ref))
+        slots, cows = [], []
+        try:
+            for s in range(len(tables)):
+                sl, cw = self.seq_append_slots(tables[s], lens[s], n_new[s], cap)
+                slots += sl
+                cows += cw
+                lens[s] += n_new[s]
+        except PoolError:
+            for s in range(len(tables)):
+                tables[s][:] = saved[0][s]
+            lens[:] = saved[1]
+            self.free, self.ref = saved[2], saved[3]
+            raise
         return slots, cows
 
     def seq_free(self, table):

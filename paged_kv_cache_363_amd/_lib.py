@@ -49,6 +49,7 @@ SIGNATURES = {
     "pkv_seq_create": (I32, [P, I32, P, I32, P]),
     "pkv_seq_fork": (I32, [P, P, I32]),
     "pkv_seq_append_slots": (I32, [P, P, P, I32, I32, I32, P, P, I32, P]),
+    "pkv_batch_append_slots": (I32, [P, P, I32, P, P, P, I32, P, P, I32, P, P]),
     "pkv_seq_free": (I32, [P, P, I32]),
 }
 

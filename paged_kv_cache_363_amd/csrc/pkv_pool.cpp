@@ -10,6 +10,7 @@
 // release (push tail) are O(1).  Every operation that can fail checks first
 // and mutates only when it is sure to succeed.
 #include <cstdint>
+#include <climits>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -24,6 +25,10 @@ struct pkv_pool {
   std::vector<int32_t> ring;  // free queue storage, capacity num_blocks
   int32_t head = 0;           // index of the queue head in ring
   int32_t count = 0;          // queue length
+  // batch bookkeeping: per-block writer counts (all zero between calls) and
+  // the ids with a nonzero count
+  std::vector<int32_t> touch;
+  std::vector<int32_t> touched;
 
   int32_t pop() {
     int32_t b = ring[head];
@@ -41,6 +46,66 @@ struct pkv_pool {
   bool valid(int32_t b) const { return b >= 0 && b < num_blocks; }
 };
 
+namespace {
+
+// Validation half of an append of n_new positions at cur_len to the table
+// table[0..nb): no gap after the table, room in the table, every block it
+// writes into is in use.  Adds the blocks past the table to *need_new and
+// calls on_shared(b) for each existing block b with a count above one that
+// the append writes into.  Changes nothing.
+template <class F>
+pkv_status check_append(const pkv_pool* pool, const int32_t* table, int32_t nb, int32_t cap,
+                        int32_t cur_len, int32_t n_new, int64_t* need_new, F&& on_shared,
+                        const char* who) {
+  const int32_t bs = pool->block_size;
+  const int64_t first = cur_len / bs, last = ((int64_t)cur_len + n_new - 1) / bs;
+  if (first > nb) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: gap after the table", who);
+  if (last + 1 > cap) return pkv::fail(PKV_ERR_INVALID_ARG, "%s: table capacity", who);
+  for (int64_t bi = first; bi <= last; ++bi) {
+    if (bi >= nb) {
+      ++*need_new;
+    } else {
+      const int32_t b = table[bi];
+      if (!pool->valid(b) || pool->ref[b] < 1)
+        return pkv::fail(PKV_ERR_INVALID_ARG, "%s: table holds a bad block", who);
+      if (pool->ref[b] > 1) on_shared(b);
+    }
+  }
+  return PKV_OK;
+}
+
+// Mutation half, run only once the free queue is known to hold enough blocks:
+// copy-on-write for shared blocks written into, new blocks past the table,
+// then the slot of each new position.
+void apply_append(pkv_pool* pool, int32_t* table, int32_t* nblocks, int32_t cur_len,
+                  int32_t n_new, int64_t* slots_out, int32_t* cow_pairs, int32_t* ncow) {
+  const int32_t bs = pool->block_size;
+  const int64_t first = cur_len / bs, last = ((int64_t)cur_len + n_new - 1) / bs;
+  const int32_t nb = *nblocks;
+  for (int64_t bi = first; bi <= last; ++bi) {
+    if (bi < nb) {
+      const int32_t old = table[bi];
+      if (pool->ref[old] > 1) {
+        const int32_t fresh = pool->pop();
+        cow_pairs[2 * *ncow] = old;
+        cow_pairs[2 * *ncow + 1] = fresh;
+        ++*ncow;
+        --pool->ref[old];  // stays >= 1: it was above 1
+        table[bi] = fresh;
+      }
+    } else {
+      table[bi] = pool->pop();
+    }
+  }
+  if (last + 1 > nb) *nblocks = (int32_t)(last + 1);
+  for (int32_t i = 0; i < n_new; ++i) {
+    const int64_t pos = (int64_t)cur_len + i;
+    slots_out[i] = (int64_t)table[pos / bs] * bs + pos % bs;
+  }
+}
+
+}  // namespace
+
 extern "C" {
 
 pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
@@ -54,6 +119,7 @@ pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t
   p->num_blocks = num_blocks;
   p->block_size = block_size;
   p->ref.assign(num_blocks, 0);
+  p->touch.assign(num_blocks, 0);
   p->ring.resize(num_blocks);
   if (free_order) {
     std::vector<char> seen(num_blocks, 0);
@@ -131,49 +197,87 @@ pkv_status pkv_seq_append_slots(pkv_pool* pool, int32_t* table, int32_t* nblocks
   if (n_new == 0) return PKV_OK;
   if (!table || !slots_out)
     return pkv::fail(PKV_ERR_INVALID_ARG, "seq_append_slots: NULL table/slots");
-  const int32_t bs = pool->block_size;
-  const int64_t last_pos = (int64_t)cur_len + n_new - 1;
-  const int64_t first = cur_len / bs, last = last_pos / bs;
-  const int32_t nb = *nblocks;
-  if (first > nb) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_append_slots: gap after the table");
-  if (last + 1 > cap) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_append_slots: table capacity");
   int64_t need_new = 0, need_cow = 0;
-  for (int64_t bi = first; bi <= last; ++bi) {
-    if (bi >= nb) {
-      ++need_new;
-    } else {
-      int32_t b = table[bi];
-      if (!pool->valid(b) || pool->ref[b] < 1)
-        return pkv::fail(PKV_ERR_INVALID_ARG, "seq_append_slots: table holds a bad block");
-      if (pool->ref[b] > 1) ++need_cow;
-    }
-  }
+  pkv_status st = check_append(pool, table, *nblocks, cap, cur_len, n_new, &need_new,
+                               [&](int32_t) { ++need_cow; }, "seq_append_slots");
+  if (st != PKV_OK) return st;
   if (need_cow > 0 && (!cow_pairs || need_cow > cow_cap))
     return pkv::fail(PKV_ERR_INVALID_ARG, "seq_append_slots: cow_pairs too small");
   if (need_new + need_cow > pool->count)
     return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "seq_append_slots: not enough free blocks");
   int32_t ncow = 0;
-  for (int64_t bi = first; bi <= last; ++bi) {
-    if (bi < nb) {
-      int32_t old = table[bi];
-      if (pool->ref[old] > 1) {
-        int32_t fresh = pool->pop();
-        cow_pairs[2 * ncow] = old;
-        cow_pairs[2 * ncow + 1] = fresh;
-        ++ncow;
-        --pool->ref[old];  // stays >= 1: it was above 1
-        table[bi] = fresh;
-      }
-    } else {
-      table[bi] = pool->pop();
+  apply_append(pool, table, nblocks, cur_len, n_new, slots_out, cow_pairs, &ncow);
+  if (n_cow) *n_cow = ncow;
+  return PKV_OK;
+}
+
+pkv_status pkv_batch_append_slots(pkv_pool* pool, int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, int32_t* nblocks,
+                                  int32_t* context_lens, const int32_t* n_new, int32_t num_seqs,
+                                  int64_t* slot_mapping, int32_t* cow_pairs, int32_t cow_cap,
+                                  int32_t* n_cow, int32_t* n_slots) {
+  if (n_cow) *n_cow = 0;
+  if (n_slots) *n_slots = 0;
+  if (!pool || num_seqs < 0 || max_blocks_per_seq < 0 || cow_cap < 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "batch_append_slots: bad argument");
+  if (num_seqs == 0) return PKV_OK;
+  if (!block_tables || !nblocks || !context_lens)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "batch_append_slots: NULL table/nblocks/lens");
+  const int64_t mb = max_blocks_per_seq;
+  // Pass 1: validate every sequence and count the blocks the batch takes.  A
+  // shared block (count r > 1) that t sequences of the batch write into is
+  // copied by the first min(t, r - 1) of them in batch order; the last writer
+  // of a block that every holder writes keeps it.  No block is released in a
+  // batch, so new blocks + copies is exactly what the free queue must hold.
+  std::vector<int32_t>& touch = pool->touch;
+  std::vector<int32_t>& touched = pool->touched;
+  touched.clear();
+  int64_t need_new = 0, total = 0;
+  pkv_status st = PKV_OK;
+  for (int32_t s = 0; s < num_seqs && st == PKV_OK; ++s) {
+    const int32_t k = n_new ? n_new[s] : 1;
+    if (context_lens[s] < 0 || k < 0 || nblocks[s] < 0 || nblocks[s] > max_blocks_per_seq) {
+      st = pkv::fail(PKV_ERR_INVALID_ARG, "batch_append_slots: bad length or block count");
+      break;
     }
+    total += k;
+    if (k == 0) continue;
+    st = check_append(pool, block_tables + s * mb, nblocks[s], max_blocks_per_seq,
+                      context_lens[s], k, &need_new,
+                      [&](int32_t b) {
+                        if (touch[b]++ == 0) touched.push_back(b);
+                      },
+                      "batch_append_slots");
   }
-  if (last + 1 > nb) *nblocks = (int32_t)(last + 1);
-  for (int32_t i = 0; i < n_new; ++i) {
-    int64_t pos = (int64_t)cur_len + i;
-    slots_out[i] = (int64_t)table[pos / bs] * bs + pos % bs;
+  int64_t need_cow = 0;
+  for (int32_t b : touched) {
+    const int64_t r = pool->ref[b];
+    need_cow += touch[b] < r - 1 ? touch[b] : r - 1;
+    touch[b] = 0;
+  }
+  touched.clear();
+  if (st != PKV_OK) return st;
+  if (total > 0 && !slot_mapping)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "batch_append_slots: slot_mapping is NULL");
+  if (total > INT32_MAX)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "batch_append_slots: too many new positions");
+  if (need_cow > 0 && (!cow_pairs || need_cow > cow_cap))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "batch_append_slots: cow_pairs too small");
+  if (need_new + need_cow > pool->count)
+    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "batch_append_slots: not enough free blocks");
+  // Pass 2: cannot fail.
+  int32_t ncow = 0;
+  int64_t t = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t k = n_new ? n_new[s] : 1;
+    if (k == 0) continue;
+    apply_append(pool, block_tables + s * mb, nblocks + s, context_lens[s], k, slot_mapping + t,
+                 cow_pairs, &ncow);
+    context_lens[s] += k;
+    t += k;
   }
   if (n_cow) *n_cow = ncow;
+  if (n_slots) *n_slots = (int32_t)t;
   return PKV_OK;
 }
 

@@ -1,7 +1,9 @@
 """Python handle on the native host block pool (pkv_pool_* / pkv_seq_*).
 
-Block tables are Python lists of ints on this side; each call marshals them
-into host int32 arrays for the C library and back.
+The per-sequence calls take block tables as Python lists of ints and marshal
+them into host int32 arrays for the C library and back.  batch_append_slots
+works in place on the decode layout (an int32 [num_seqs][max_blocks] array)
+with one call into the library for the whole batch.
 """
 import ctypes
 
@@ -11,7 +13,9 @@ from ._lib import check, lib
 
 
 def _ptr(a):
-    return a.ctypes.data_as(ctypes.c_void_p)
+    # the address as a plain int (ctypes takes it for a void* argument);
+    # ndarray.ctypes.data_as costs several microseconds per call
+    return a.ctypes.data
 
 
 class BlockPool:
@@ -27,6 +31,7 @@ class BlockPool:
         self._h = h
         self.num_blocks = num_blocks
         self.block_size = block_size
+        self._ncow, self._nslots = ctypes.c_int32(), ctypes.c_int32()
 
     def close(self):
         if self._h:
@@ -93,6 +98,42 @@ class BlockPool:
         table[:] = arr[:nb.value].tolist()
         pairs = [(int(cows[2 * i]), int(cows[2 * i + 1])) for i in range(ncow.value)]
         return slots[:n_new].tolist(), pairs
+
+    def batch_append_slots(self, block_tables, nblocks, context_lens, n_new=None,
+                           slot_mapping=None):
+        """One step's bookkeeping for a batch (pkv_batch_append_slots).
+
+        block_tables (int32 [S][MB]), nblocks (int32 [S]) and context_lens
+        (int32 [S]) are C-contiguous numpy arrays, updated in place; n_new is
+        None (one position per sequence) or int32 [S].  slot_mapping, if given,
+        is an int64 array with room for every new position.  Returns
+        (slot_mapping[:T], cow_pairs int32 [n][2])."""
+        for a in (block_tables, nblocks, context_lens):
+            if a.dtype != np.int32 or not a.flags.c_contiguous or not a.flags.writeable:
+                raise ValueError("block_tables, nblocks, context_lens: writable C-contiguous int32")
+        S = nblocks.shape[0]
+        if block_tables.ndim != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+            raise ValueError("block_tables must be [S][MB] with nblocks, context_lens [S]")
+        if n_new is not None:
+            n_new = np.ascontiguousarray(n_new, dtype=np.int32)
+            if n_new.shape != (S,):
+                raise ValueError("n_new must be [S]")
+            T = int(n_new.sum(dtype=np.int64))
+        else:
+            T = S
+        if slot_mapping is None:
+            slot_mapping = np.empty(max(T, 1), np.int64)
+        elif slot_mapping.dtype != np.int64 or not slot_mapping.flags.c_contiguous \
+                or slot_mapping.shape[0] < T:
+            raise ValueError("slot_mapping: C-contiguous int64 with room for every position")
+        cow_cap = self.num_blocks  # each copy takes a free block
+        cows = np.empty(2 * max(cow_cap, 1), np.int32)
+        ncow, nslots = self._ncow, self._nslots
+        check(lib().pkv_batch_append_slots(
+            self._h, _ptr(block_tables), block_tables.shape[1], _ptr(nblocks), _ptr(context_lens),
+            _ptr(n_new) if n_new is not None else None, S, _ptr(slot_mapping), _ptr(cows),
+            cow_cap, ctypes.byref(ncow), ctypes.byref(nslots)))
+        return slot_mapping[:nslots.value], cows[:2 * ncow.value].reshape(-1, 2)
 
     def seq_free(self, table):
         arr = np.ascontiguousarray(table, dtype=np.int32)
