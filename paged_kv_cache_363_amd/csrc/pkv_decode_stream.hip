@@ -34,6 +34,9 @@
 #ifndef PKV_PIPE_DEPTH_FP8
 #define PKV_PIPE_DEPTH_FP8 2   // same for E4M3 caches
 #endif
+#ifndef PKV_NT_FP8
+#define PKV_NT_FP8 0           // non-temporal K/V loads for E4M3 caches
+#endif
 
 namespace {
 
@@ -56,6 +59,16 @@ struct StreamParams {
   int R;                       // restart units counted at the start of every segment
 };
 
+// floor(n / c) for 0 <= n < 2^53 and c >= 1.  n and c are exact in double,
+// and a correctly rounded quotient cannot reach an integer that the exact
+// quotient lies below (that would take n >= 2^53), so truncation gives the
+// floor.  Far cheaper on the GPU than 64-bit integer division, which expands
+// into a long VALU sequence.  Every share boundary goes through here, in the
+// decode and the merge kernel alike.
+__device__ __forceinline__ int64_t floor_div53(int64_t n, int64_t c) {
+  return (int64_t)((double)n / (double)c);
+}
+
 // Unit prefix sums in LDS, computed by one workgroup of 4 waves.  A segment
 // of a sequence with nbk blocks spans nbk + R units: R units that stand for
 // the cost of starting a piece (the q rows and block ids must arrive before
@@ -64,7 +77,8 @@ struct StreamParams {
 // pref[s] = units of one segment of each sequence before s (0 for a
 // sequence without context).
 __device__ __forceinline__ void block_prefix(const StreamParams& p, int* sm_pref, int* sm_ctx) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int S = p.S;
   const int cap = p.mb * pkv::kBlockSize;
   for (int i = threadIdx.x; i < S; i += 64 * kSkWaves) {
@@ -101,7 +115,8 @@ void decode_stream_kernel(StreamParams p) {
   __shared__ int sm_pref[pkv::kMaxStreamSeqs + 1];   // segment units before sequence s
   __shared__ int sm_ctx[pkv::kMaxStreamSeqs];        // clamped context lengths
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int c = lane & 15, G = lane >> 4;
   const int S = p.S;
   block_prefix(p, sm_pref, sm_ctx);
@@ -118,24 +133,29 @@ void decode_stream_kernel(StreamParams p) {
 
   const int64_t We = U < W ? U : W;   // workers with a non-empty share
   if (wk >= We) return;
-  auto share = [&](int64_t k) { return (U * k) / We; };
-  const int64_t u_lo = share(wk), u_hi = share(wk + 1);
+  const int64_t u_lo = floor_div53(U * wk, We), u_hi = floor_div53(U * (wk + 1), We);
 
   // unit u -> (sequence s, segment y, position j in the segment's units): s
   // is the last sequence whose first unit is <= u (sequences without blocks
-  // own no unit)
+  // own no unit).  The prefix sums are non-decreasing, so the lanes that pass
+  // the test form a prefix of the wave: a 64-way search, two rounds of LDS
+  // reads for up to 4096 sequences.
   auto locate = [&](int64_t u, int& s, int& y, int& j) {
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (Y * sm_pref[mid] <= u) lo = mid;
-      else hi = mid - 1;
+    int lo = 0, span = S;   // Y * pref[lo] <= u
+    while (span > 1) {
+      const int step = (span + 63) >> 6;
+      const int i = lo + lane * step;
+      const bool ok = lane * step < span && Y * sm_pref[i] <= u;
+      const int cnt = __popcll(__ballot(ok));
+      lo += (cnt - 1) * step;
+      span = min(step, span - (cnt - 1) * step);
     }
     s = lo;
-    const int len = sm_pref[s + 1] - sm_pref[s];
-    const int64_t r = u - Y * sm_pref[s];
+    // U < 2^31 (checked by the host), so 32-bit division suffices
+    const uint32_t len = (uint32_t)(sm_pref[s + 1] - sm_pref[s]);
+    const uint32_t r = (uint32_t)(u - Y * sm_pref[s]);
     y = (int)(r / len);
-    j = (int)(r - (int64_t)y * len);
+    j = (int)(r - (uint32_t)y * len);
   };
 
   const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
@@ -207,7 +227,7 @@ void decode_stream_kernel(StreamParams p) {
       if (p.nb > 0) {
         const int64_t off = (int64_t)hk * T::TILE;
         mfma_piece<QT, KVT, D, KVT == PKV_FP8_E4M3 ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
-                   KVT != PKV_FP8_E4M3>(p.kc + off, p.vc + off, blk_stride,
+                   KVT != PKV_FP8_E4M3 || PKV_NT_FP8>(p.kc + off, p.vc + off, blk_stride,
                                         p.bt + (int64_t)s * p.mb, b, b1, last, ctx - 16 * last,
                                         p.nb, qr, p.sl2, m_run, l_run, o, lane);
       }
@@ -237,7 +257,8 @@ __global__ __launch_bounds__(64 * kSkWaves) void decode_split_merge_kernel(Strea
   __shared__ int sm_pref[pkv::kMaxStreamSeqs + 1];
   __shared__ int sm_ctx[pkv::kMaxStreamSeqs];
   block_prefix(p, sm_pref, sm_ctx);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int64_t Y = p.Y;
   const int64_t U = Y * sm_pref[p.S];
   const int64_t We = U < p.W ? U : p.W;
@@ -257,57 +278,81 @@ __global__ __launch_bounds__(64 * kSkWaves) void decode_split_merge_kernel(Strea
     if (len == 0) continue;
     // the segment's blocks are its units [seg_start + R, seg_start + len)
     const int64_t seg_start = Y * sm_pref[s] + (int64_t)y * len;
-    const int64_t wa = ((seg_start + p.R + 1) * We - 1) / U;
-    const int64_t wb = ((seg_start + len) * We - 1) / U;
+    const int64_t wa = floor_div53((seg_start + p.R + 1) * We - 1, U);
+    const int64_t wb = floor_div53((seg_start + len) * We - 1, U);
     if (wa == wb) continue;
     // the first worker's piece is its first piece with blocks unless its
     // share holds blocks of the segment before (units below seg_start)
-    const int64_t sl0 = 2 * wa + ((U * wa) / We >= seg_start ? 0 : 1);
+    const int64_t sl0 = 2 * wa + (floor_div53(U * wa, We) >= seg_start ? 0 : 1);
     const int np = (int)(wb - wa + 1);
     auto slot_of = [&](int k) { return k == 0 ? sl0 : 2 * (wa + k); };
+    auto ml_of = [&](int k) {
+      return *reinterpret_cast<const float2*>(p.ml + (slot_of(k) * HS + h) * 2);
+    };
+    // Accumulator rows of pieces base+j0 .. base+j0+7 (the last valid piece
+    // repeated past cnt; its weight is zero there).
+    auto load_rows = [&](float (&x)[8][PER], int base, int j0, int cnt) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t sl = slot_of(base + min(j0 + u, cnt - 1));
+#pragma unroll
+        for (int k2 = 0; k2 < PER; ++k2) {
+          const int d = lane + 64 * k2;
+          x[u][k2] = d < D ? p.part[(sl * HS + h) * D + d] : 0.f;
+        }
+      }
+    };
     float acc[PER];
 #pragma unroll
     for (int k2 = 0; k2 < PER; ++k2) acc[k2] = 0.f;
-    float L = 0.f;
-    // pass 1: the maximum over every piece
-    float M = kNegInf;
-    for (int k = lane; k < np; k += 64) {
-      const int64_t sl = slot_of(k);
-      const float lk = p.ml[(sl * HS + h) * 2 + 1];
-      const float mk = p.ml[(sl * HS + h) * 2];
-      if (lk > 0.f) M = fmaxf(M, mk);
+    auto add_rows = [&](const float (&x)[8][PER], float wgt, int j0, int cnt) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wj = __int_as_float(
+            __builtin_amdgcn_readlane(__float_as_int(wgt), min(j0 + u, 63)));
+        const float wu = (j0 + u < cnt) ? wj : 0.f;
+#pragma unroll
+        for (int k2 = 0; k2 < PER; ++k2) acc[k2] = fmaf(wu, x[u][k2], acc[k2]);
+      }
+    };
+    // Lane k holds piece k's (m, l).  Those and the first eight accumulator
+    // rows go out together: none depends on another, so the merge of a
+    // segment split over at most eight workers waits on memory once.
+    const int cnt0 = min(64, np);
+    float x0[8][PER];
+    load_rows(x0, 0, 0, cnt0);
+    float m0 = kNegInf, l0 = 0.f;
+    if (lane < np) {
+      const float2 v = ml_of(lane);
+      m0 = v.x;
+      l0 = v.y;
+    }
+    float M = l0 > 0.f ? m0 : kNegInf;
+    for (int k = lane + 64; k < np; k += 64) {
+      const float2 v = ml_of(k);
+      if (v.y > 0.f) M = fmaxf(M, v.x);
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float L = 0.f;
     if (M != kNegInf) {
       for (int base = 0; base < np; base += 64) {
         float wgt = 0.f;
         if (base + lane < np) {
-          const int64_t sl = slot_of(base + lane);
-          const float lk = p.ml[(sl * HS + h) * 2 + 1];
-          wgt = lk > 0.f ? __builtin_amdgcn_exp2f(p.ml[(sl * HS + h) * 2] - M) : 0.f;
-          L += wgt * lk;
+          const float2 v = base == 0 ? make_float2(m0, l0) : ml_of(base + lane);
+          wgt = v.y > 0.f ? __builtin_amdgcn_exp2f(v.x - M) : 0.f;
+          L += wgt * v.y;
         }
         const int cnt = min(64, np - base);
-        for (int j0 = 0; j0 < cnt; j0 += 8) {
+        int j0 = 0;
+        if (base == 0) {
+          add_rows(x0, wgt, 0, cnt);
+          j0 = 8;
+        }
+        for (; j0 < cnt; j0 += 8) {
           float x[8][PER];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const int64_t sl = slot_of(base + min(j0 + u, cnt - 1));
-#pragma unroll
-            for (int k2 = 0; k2 < PER; ++k2) {
-              const int d = lane + 64 * k2;
-              x[u][k2] = d < D ? p.part[(sl * HS + h) * D + d] : 0.f;
-            }
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const float wj = __int_as_float(
-                __builtin_amdgcn_readlane(__float_as_int(wgt), min(j0 + u, 63)));
-            const float wu = (j0 + u < cnt) ? wj : 0.f;
-#pragma unroll
-            for (int k2 = 0; k2 < PER; ++k2) acc[k2] = fmaf(wu, x[u][k2], acc[k2]);
-          }
+          load_rows(x, base, j0, cnt);
+          add_rows(x, wgt, j0, cnt);
         }
       }
     }
