@@ -183,6 +183,11 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
         kcs.append(st["k_cache"].clone())
         vcs.append(st["v_cache"].clone())
     ps = partition
+    if ps == 0 and args.algo == "auto":
+        # the schedule a serving loop would pick from its host-side lengths
+        ps = pkv.decode_partition_size(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads,
+                                       cfg.head_dim, cfg.max_blocks_per_seq,
+                                       DT_CODE[cfg.kv_dtype], 0, context_lens=st["ctx"])
     ws = pkv.alloc_workspace(st["q"], st["k_cache"], st["block_tables"], ps)
     out = torch.empty_like(st["q"])
     stream = torch.cuda.current_stream()

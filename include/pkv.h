@@ -127,6 +127,23 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t
                                   int32_t head_dim, int32_t max_blocks_per_seq, int32_t kv_dtype,
                                   int32_t partition_size);
 
+/* The partition_size to pass for a batch whose context lengths the caller
+ * holds on the host (a serving loop has them after its block bookkeeping).
+ * Where AUTO would run the balanced schedule, this weighs it against one
+ * fixed partition of max_blocks_per_seq * 16 tokens per (sequence, kv-head
+ * chunk), run single-pass: no partials and no merge kernel, but only as even
+ * as the lengths are.  Returns 0 (balanced) or max_blocks_per_seq * 16; in
+ * every other case the same as pkv_decode_partition_size(..., 0).  Both
+ * choices compute the same attention.
+ *   context_lens : host int32[num_seqs], the lengths the decode call will see
+ *                  (clamped to [0, max_blocks_per_seq * 16] as it does).
+ * Pure host function, O(num_seqs * kv-head chunks * log 256).  Returns -1 on
+ * bad arguments. */
+int32_t pkv_decode_partition_size_for_lengths(const int32_t* context_lens, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t max_blocks_per_seq,
+                                              int32_t kv_dtype);
+
 /* Bytes of device workspace a decode call with these arguments needs (0 for a
  * single-pass fixed partition).  Fixed partitions: float m[S][H_q][P],
  * float l[S][H_q][P], float acc[S][H_q][P][head_dim] (each part 256-byte

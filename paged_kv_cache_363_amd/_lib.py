@@ -26,6 +26,7 @@ SIGNATURES = {
     "pkv_kv_bytes_per_token": (U64, [I32, I32, I32, I32]),
     "pkv_paged_cache_append": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F32, F32, P]),
     "pkv_decode_partition_size": (I32, [I32, I32, I32, I32, I32, I32, I32]),
+    "pkv_decode_partition_size_for_lengths": (I32, [P, I32, I32, I32, I32, I32, I32]),
     "pkv_decode_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32]),
     "pkv_decode_algo_for": (I32, [I32, I32, I32, I32, I32]),
     "pkv_paged_decode_attention": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, F32,

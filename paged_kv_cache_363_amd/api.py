@@ -62,7 +62,19 @@ def paged_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping, k_scale=1.0
 
 
 def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                          kv_dtype=_lib.PKV_BF16, partition_size=0):
+                          kv_dtype=_lib.PKV_BF16, partition_size=0, context_lens=None):
+    """partition_size for a decode call (pkv_decode_partition_size).  With the
+    batch's context lengths on the host (context_lens: int sequence or numpy
+    array) and partition_size 0, the choice weighs them
+    (pkv_decode_partition_size_for_lengths)."""
+    if context_lens is not None and partition_size == 0:
+        import numpy as np
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        if cl.shape != (num_seqs,):
+            raise ValueError("context_lens must hold num_seqs lengths")
+        return int(lib().pkv_decode_partition_size_for_lengths(
+            cl.ctypes.data, num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+            kv_dtype))
     return int(lib().pkv_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                max_blocks_per_seq, kv_dtype, partition_size))
 

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <functional>
+#include <queue>
+#include <vector>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -213,6 +216,56 @@ int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t
     return -1;
   // AUTO runs the balanced schedule for a q-head group g > 1 (see resolve_algo)
   return plan.stream_ok && num_q_heads / num_kv_heads > 1 ? 0 : plan.partition;
+}
+
+int32_t pkv_decode_partition_size_for_lengths(const int32_t* context_lens, int32_t num_seqs,
+                                              int32_t num_q_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t max_blocks_per_seq,
+                                              int32_t kv_dtype) {
+  const int32_t auto_ps = pkv_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                    max_blocks_per_seq, kv_dtype, 0);
+  if (auto_ps != 0) return auto_ps;   // no balanced schedule to weigh (or bad arguments)
+  if (num_seqs > 0 && !context_lens) return -1;
+  const int64_t max_ctx = (int64_t)max_blocks_per_seq * kBlockSize;
+  if (max_ctx == 0 || max_ctx > kMaxPartition) return 0;
+  const int32_t g = num_q_heads / num_kv_heads;
+  const int32_t chunk = g < 16 ? g : 16;
+  const int64_t Y = (int64_t)num_kv_heads * ((g + chunk - 1) / chunk);
+  const int64_t R = kv_restart_units(kv_dtype);
+  // Costs in block loads of one wave (both schedules stream at the same
+  // per-wave rate; only the split differs).
+  //  balanced: the grid's waves share all units equally, then the merge
+  //            kernel runs (worth about kMergeUnits block loads);
+  //  one fixed partition per (sequence, kv-head chunk): a workgroup's four
+  //            waves take a quarter of the sequence each (plus one restart)
+  //            and the workgroups start, in grid order, on whichever CU frees
+  //            up first.
+  constexpr int64_t kMergeUnits = 4;
+  constexpr int kPlanCUs = 256;   // compute units of an MI355X
+  int64_t units = 0;
+  std::vector<int64_t> work(num_seqs);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t len = context_lens[s] < 0 ? 0 : (context_lens[s] > max_ctx ? max_ctx : context_lens[s]);
+    const int64_t nbk = (len + kBlockSize - 1) / kBlockSize;
+    units += nbk > 0 ? nbk + R : 0;
+    work[s] = nbk > 0 ? (nbk + kWaves - 1) / kWaves + R : 0;
+  }
+  if (units == 0) return 0;
+  const int64_t W = (int64_t)g_stream_workgroups.load() * 4;
+  const int64_t t_bal = (Y * units + W - 1) / W + kMergeUnits;
+  // list scheduling of the fixed grid (kv-head chunk fastest, then sequence)
+  std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+  for (int i = 0; i < kPlanCUs; ++i) free_at.push(0);
+  int64_t t_fix = 0;
+  for (int32_t s = 0; s < num_seqs && t_fix <= t_bal; ++s) {
+    for (int64_t y = 0; y < Y; ++y) {
+      const int64_t t = free_at.top() + work[s];
+      free_at.pop();
+      free_at.push(t);
+      if (t > t_fix) t_fix = t;
+    }
+  }
+  return t_fix <= t_bal ? (int32_t)max_ctx : 0;
 }
 
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
