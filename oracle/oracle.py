@@ -44,6 +44,8 @@ def _load():
     I64 = ctypes.c_int64
     lib.orc_paged_decode.argtypes = [P, P, I, P, P, I, P, P, I, I, I, I, I, I, D, D, D]
     lib.orc_paged_decode.restype = I
+    lib.orc_paged_multiquery.argtypes = [P, P, I, P, P, I, P, P, P, I, I, I, I, I, I, I, D, D, D]
+    lib.orc_paged_multiquery.restype = I
     lib.orc_softmax_weights.argtypes = [P, I, I, P, I, P, I, P, P, I, I, I, I, I, I, D, D]
     lib.orc_softmax_weights.restype = I
     lib.orc_partition_stats.argtypes = [P, P, P, I, I, I, I, P, I, P, P, I, P, P,
@@ -136,6 +138,31 @@ def paged_decode(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_l
                                   S, hq, hkv, d, bs, bt.shape[1], scale, k_scale, v_scale)
     if rc != 0:
         raise ValueError(f"oracle paged_decode failed ({rc})")
+    return out
+
+
+def paged_multiquery(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
+                     query_start, scale, k_scale=1.0, v_scale=1.0):
+    """fp64 out[rows][H_q][d]: the rows query_start[s]..query_start[s+1]-1 of
+    sequence s are its last positions and attend causally through the block
+    table (row i of n sits at position ctx - n + i)."""
+    q = _check_bits(q, q_dtype)
+    k_cache = _check_bits(k_cache, kv_dtype)
+    v_cache = _check_bits(v_cache, kv_dtype)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    rows, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    S = cl.shape[0]
+    assert d == d2 and bt.shape[0] == S and qs.shape[0] == S + 1
+    out = np.empty((rows, hq, d), dtype=np.float64)
+    rc = _load().orc_paged_multiquery(_ptr(out), _ptr(q), DTYPES[q_dtype], _ptr(k_cache),
+                                      _ptr(v_cache), DTYPES[kv_dtype], _ptr(bt), _ptr(cl),
+                                      _ptr(qs), S, rows, hq, hkv, d, bs, bt.shape[1], scale,
+                                      k_scale, v_scale)
+    if rc != 0:
+        raise ValueError(f"oracle paged_multiquery failed ({rc})")
     return out
 
 

@@ -26,6 +26,16 @@
  *    E4M3FN, per-tensor scale, real value = decode(code) * scale.
  *  - Cache append: only the new token's K and V are written ("Transformer 推理
  *    优化", section 2.2), at slot = physical_block*bs + offset.
+ *  - Several queries per sequence in one pass: a chunk of a long prompt
+ *    ("vLLM推理引擎深度解析" section 3.3; "推理加速三板斧" section 4.5, chunks
+ *    of about 512 tokens scheduled alongside decode requests) or the draft
+ *    tokens a target model checks in one parallel pass
+ *    ("大语言模型推理引擎深度剖析" section 4.1, typically 3-8 of them).  The
+ *    chunk's K/V are in the cache first; query i of a chunk of n at the end
+ *    of a context of ctx tokens sits at position ctx - n + i and attends to
+ *    positions 0 .. that position (each token sees its prefix, as in the
+ *    prefix-plus-current form of section 1.2 of "KV Cache 与
+ *    PageAttention深度实战").
  *
  * Everything is evaluated in double precision with plain loops.  Compile
  * without -ffast-math and with -ffp-contract=off.
@@ -267,6 +277,67 @@ int orc_paged_decode(double* out, const void* q, int q_dtype, const void* k_cach
     }
   }
   free(w);
+  return 0;
+}
+
+/* Multi-query attention through the block table.  Sequence s owns the
+ * query rows query_start[s] .. query_start[s+1]-1 of q and out ([rows][H_q]
+ * [d]); with n = that count and ctx = context_lens[s], row query_start[s]+i
+ * is position p = ctx - n + i and attends to tokens 0..p.  A row with p < 0
+ * (n > ctx) and every row no sequence owns yields zeros.  With n = 1 a row is
+ * the decode output of its sequence. */
+int orc_paged_multiquery(double* out, const void* q, int q_dtype, const void* k_cache,
+                         const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                         const int32_t* context_lens, const int32_t* query_start,
+                         int num_seqs, int num_rows, int num_q_heads, int num_kv_heads,
+                         int head_dim, int block_size, int max_blocks_per_seq, double scale,
+                         double k_scale, double v_scale) {
+  if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
+  const int g = num_q_heads / num_kv_heads;
+  const int max_ctx = max_blocks_per_seq * block_size;
+  const double ks = kv_dtype == ORC_FP8_E4M3 ? k_scale : 1.0;
+  const double vs = kv_dtype == ORC_FP8_E4M3 ? v_scale : 1.0;
+  /* the kv-side lookups of cache_elem only need the cache fields */
+  orc_args a = {q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
+                num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                max_blocks_per_seq, scale, ks, vs};
+  for (int64_t i = 0; i < (int64_t)num_rows * num_q_heads * head_dim; ++i) out[i] = 0.0;
+  double* z = (double*)malloc(sizeof(double) * (max_ctx > 0 ? max_ctx : 1));
+  if (!z) return -3;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int ctx = context_lens[s];
+    const int r0 = query_start[s], n = query_start[s + 1] - r0;
+    if (ctx > max_ctx || n < 0 || r0 < 0 || r0 + n > num_rows) { free(z); return -2; }
+    for (int i = 0; i < n; ++i) {
+      const int p = ctx - n + i;   /* position of this query */
+      if (p < 0) continue;
+      const int64_t row = r0 + i;
+      for (int hq = 0; hq < num_q_heads; ++hq) {
+        const int hk = hq / g;
+        double m = -INFINITY;
+        for (int t = 0; t <= p; ++t) {
+          double dot = 0.0;
+          for (int e = 0; e < head_dim; ++e) {
+            const double qe = load_elem(q, (row * num_q_heads + hq) * head_dim + e, q_dtype);
+            dot += qe * cache_elem(&a, k_cache, ks, s, hk, t, e);
+          }
+          z[t] = scale * dot;
+          if (z[t] > m) m = z[t];
+        }
+        double l = 0.0;
+        for (int t = 0; t <= p; ++t) {
+          z[t] = exp(z[t] - m);
+          l += z[t];
+        }
+        double* o = out + (row * num_q_heads + hq) * head_dim;
+        for (int t = 0; t <= p; ++t) {
+          const double wt = z[t] / l;
+          for (int e = 0; e < head_dim; ++e) o[e] += wt * cache_elem(&a, v_cache, vs, s, hk, t, e);
+        }
+      }
+    }
+  }
+  free(z);
   return 0;
 }
 

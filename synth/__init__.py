@@ -5,4 +5,4 @@ and rounds them to their storage type.  It holds none of the attention,
 append or bookkeeping arithmetic; both the oracle side and the HIP side of
 every test and of the benchmark take their inputs from here.
 """
-from .configs import CONFIGS, Config  # noqa: F401
+from .configs import CONFIGS, MQ_CONFIGS, Config, MQConfig  # noqa: F401

@@ -71,3 +71,41 @@ CONFIGS = {
         seed=1005, max_blocks_per_seq=2048, shared_prefix=2048, partition_size=512,
         description="32K-context bf16, 2048-token prefix shared by 16 tables, 512-token partitions"),
 }
+
+
+@dataclass(frozen=True)
+class MQConfig:
+    """A multi-query step on a decode workload's cache: each sequence's last
+    qlen positions (a chunk of a prompt, or draft tokens under verification)
+    attend causally in one pass.  The cache state, lengths and tables are the
+    base workload's; only the query rows are new."""
+    name: str
+    base: str                # key of CONFIGS
+    qlen_kind: str           # 'fixed' | 'uniform'
+    qlen_params: tuple
+    seed: int
+    description: str = ""
+
+
+MQ_CONFIGS = {
+    "mq_c2_verify4": MQConfig(
+        name="mq_c2_verify4", base="c2_qwen3_8b_bf16", qlen_kind="fixed", qlen_params=(4,),
+        seed=2002, description="speculative verify, 4 rows per sequence (3 drafts + 1), "
+                               "Qwen3-8B-shaped bf16 cache, batch 64"),
+    "mq_c2_mixed": MQConfig(
+        name="mq_c2_mixed", base="c2_qwen3_8b_bf16", qlen_kind="uniform", qlen_params=(0, 16),
+        seed=2012, description="mixed batch, 0..16 rows per sequence (decode rows, drafts, "
+                               "small chunks), Qwen3-8B-shaped bf16 cache"),
+    "mq_c3_chunk64": MQConfig(
+        name="mq_c3_chunk64", base="c3_llama2_7b_f16", qlen_kind="fixed", qlen_params=(64,),
+        seed=2003, description="64-token prompt chunks (at most the context) on the "
+                               "Llama-2-7B-shaped fp16 MHA cache, batch 256"),
+    "mq_c4_verify8": MQConfig(
+        name="mq_c4_verify8", base="c4_llama3_70b_fp8", qlen_kind="fixed", qlen_params=(8,),
+        seed=2004, description="speculative verify, 8 rows per sequence, Llama-3-70B-shaped "
+                               "E4M3 cache, batch 32"),
+    "mq_c5_chunk512": MQConfig(
+        name="mq_c5_chunk512", base="c5_long_shared_bf16", qlen_kind="fixed", qlen_params=(512,),
+        seed=2005, description="512-token prompt chunk at the end of each 32K context, bf16, "
+                               "batch 16"),
+}

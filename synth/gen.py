@@ -15,6 +15,7 @@ from .configs import Config
 _STREAM_CTX, _STREAM_ORDER, _STREAM_Q, _STREAM_K, _STREAM_V = 0, 1, 2, 3, 4
 _STREAM_PREFIX_K, _STREAM_PREFIX_V, _STREAM_MISC = 5, 6, 7
 _STREAM_STEP_K, _STREAM_STEP_V = 8, 9
+_STREAM_QLEN, _STREAM_MQ_Q = 10, 11
 
 TORCH_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -141,3 +142,31 @@ def misc_normal(cfg, key, shape, dtype):
     """Extra N(0,1) tensors for edge-case tests (stream keyed by `key`)."""
     x = rng(cfg, _STREAM_MISC, key).standard_normal(shape, dtype=np.float32)
     return round_to(x, dtype)
+
+
+def query_lens(mq, ctx):
+    """Rows per sequence of a multi-query step, int32[S]: the workload's count,
+    at most the sequence's context."""
+    S = len(ctx)
+    if mq.qlen_kind == "fixed":
+        n = np.full(S, mq.qlen_params[0], dtype=np.int64)
+    elif mq.qlen_kind == "uniform":
+        lo, hi = mq.qlen_params
+        n = rng(mq.seed, _STREAM_QLEN).integers(lo, hi + 1, size=S)
+    else:
+        raise ValueError(mq.qlen_kind)
+    return np.minimum(n, np.asarray(ctx, dtype=np.int64)).astype(np.int32)
+
+
+def query_start(qlens):
+    """Row offsets int32[S+1] of the sequences' rows, in sequence order."""
+    qs = np.zeros(len(qlens) + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(qlens)
+    return qs
+
+
+def mq_queries(mq, cfg, rows):
+    """Query rows [rows][H_q][d] of a multi-query step, in the q dtype."""
+    x = rng(mq.seed, _STREAM_MQ_Q).standard_normal(
+        (rows, cfg.num_q_heads, cfg.head_dim), dtype=np.float32)
+    return round_to(x, cfg.q_dtype)
