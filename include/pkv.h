@@ -226,6 +226,70 @@ pkv_status pkv_paged_decode_attention_profiled(
     size_t workspace_bytes, int32_t algo, void* stream, void* ev_begin, void* ev_mid,
     void* ev_end);
 
+/* ------------------------------------------- multi-query attention -- */
+
+/* Several query rows per sequence in one pass: a chunk of a long prompt
+ * ("vLLM推理引擎深度解析", section 3.3; "推理加速三板斧", section 4.5: prompts
+ * cut into chunks of about 512 tokens and scheduled with decode requests) or
+ * the draft tokens a target model verifies at once ("大语言模型推理引擎深度剖析",
+ * section 4.1).  Sequence s owns rows query_start[s] .. query_start[s+1]-1 of
+ * q and out; they are its last n positions, appended to the cache before the
+ * call (pkv_paged_cache_append), so row i sits at position
+ * context_lens[s] - n + i and attends to positions 0 .. that position
+ * through the block table (each token sees its prefix,
+ * "KV Cache 与 PageAttention深度实战", section 1.2).  One row per sequence is
+ * exactly pkv_paged_decode_attention.
+ *   q, out       : device [num_rows][num_q_heads][head_dim], q dtype (F16 or
+ *                  BF16); rows no sequence owns are not written.
+ *   query_start  : device int32[num_seqs + 1], non-decreasing; rows are
+ *                  clamped to [0, num_rows).  A sequence's rows past
+ *                  max_query_len are not computed (with partitions their
+ *                  output is unspecified): pass the largest row count.
+ *   caches       : the q dtype or FP8_E4M3, as for decode; block_tables,
+ *                  context_lens, block_size, num_blocks, scale, k_scale,
+ *                  v_scale as for decode.  Rows with n > context_lens[s]
+ *                  whose position is negative get zeros.
+ *   partition_size: 0 = pkv_multiquery_partition_size's choice, else a
+ *                  multiple of 16; with more than one partition the call
+ *                  needs a 256-byte-aligned workspace of
+ *                  pkv_multiquery_workspace_size bytes and runs a reduction.
+ * Runs on the matrix cores: 16 MFMA columns are 16 / min(g, 16) rows times
+ * min(g, 16) q-heads of one kv-head.  Errors as for decode; PKV_ERR_UNSUPPORTED
+ * for f32 q, head_dim not in {64, 128}, or a grid beyond 65535 sequences,
+ * 65535 kv-heads x row tiles or 2^31 rows x q-heads. */
+pkv_status pkv_paged_multiquery_attention(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+    int32_t num_seqs, int32_t num_rows, int32_t max_query_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, float scale, int32_t q_dtype, int32_t kv_dtype, float k_scale,
+    float v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    void* stream);
+/* The same, recording ev_begin before the attention kernel, ev_mid after it
+ * and ev_end after the reduction (any may be NULL). */
+pkv_status pkv_paged_multiquery_attention_profiled(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+    int32_t num_seqs, int32_t num_rows, int32_t max_query_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, float scale, int32_t q_dtype, int32_t kv_dtype, float k_scale,
+    float v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    void* stream, void* ev_begin, void* ev_mid, void* ev_end);
+/* Partition (tokens) a multi-query call with partition_size 0 uses: one pass
+ * over max_blocks_per_seq * 16 tokens when the sequences x kv-heads x row
+ * tiles reach 2048 workgroups, else 512 to 128 tokens.  partition_size > 0 is
+ * returned as is.  -1 on bad arguments. */
+int32_t pkv_multiquery_partition_size(int32_t num_seqs, int32_t max_query_len,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t max_blocks_per_seq, int32_t partition_size);
+/* Workspace bytes of a multi-query call (0 for one partition): float
+ * m[rows][H_q][P], l[rows][H_q][P], acc[rows][H_q][P][head_dim], each part
+ * 256-byte aligned.  SIZE_MAX on bad arguments. */
+size_t pkv_multiquery_workspace_size(int32_t num_rows, int32_t num_seqs, int32_t max_query_len,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t max_blocks_per_seq,
+                                     int32_t partition_size);
+
 /* ---------------------------------------------------- copy-on-write copy -- */
 
 /* Copy whole physical blocks, K and V: for i < num_pairs, block

@@ -36,6 +36,14 @@ SIGNATURES = {
     "pkv_paged_decode_attention_profiled": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                                   I32, F32, I32, I32, F32, F32, I32, P, SZ, I32, P,
                                                   P, P, P]),
+    "pkv_multiquery_partition_size": (I32, [I32, I32, I32, I32, I32, I32]),
+    "pkv_multiquery_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32, I32]),
+    "pkv_paged_multiquery_attention": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                             I32, I32, I32, F32, I32, I32, F32, F32, I32, P, SZ,
+                                             P]),
+    "pkv_paged_multiquery_attention_profiled": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32,
+                                                      I32, I32, I32, I32, F32, I32, I32, F32, F32,
+                                                      I32, P, SZ, P, P, P, P]),
     "pkv_copy_blocks": (I32, [P, P, P, I32, I32, I64, P]),
     "pkv_pool_create": (I32, [I32, I32, P, ctypes.POINTER(P)]),
     "pkv_pool_destroy": (None, [P]),

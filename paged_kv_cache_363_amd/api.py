@@ -132,6 +132,62 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
     return out
 
 
+def multiquery_partition_size(num_seqs, max_query_len, num_q_heads, num_kv_heads,
+                              max_blocks_per_seq, partition_size=0):
+    return int(lib().pkv_multiquery_partition_size(num_seqs, max_query_len, num_q_heads,
+                                                   num_kv_heads, max_blocks_per_seq,
+                                                   partition_size))
+
+
+def multiquery_workspace_size(num_rows, num_seqs, max_query_len, num_q_heads, num_kv_heads,
+                              head_dim, max_blocks_per_seq, partition_size=0):
+    n = lib().pkv_multiquery_workspace_size(num_rows, num_seqs, max_query_len, num_q_heads,
+                                            num_kv_heads, head_dim, max_blocks_per_seq,
+                                            partition_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise _lib.InvalidArg(_lib.PKV_ERR_INVALID_ARG, "bad multi-query workspace arguments")
+    return int(n)
+
+
+def paged_multiquery_attention(q, k_cache, v_cache, block_tables, context_lens, query_start,
+                               max_query_len, scale, k_scale=1.0, v_scale=1.0, partition_size=0,
+                               out=None, workspace=None, stream=None, events=None):
+    """out[rows][H_q][d] (q dtype): rows query_start[s] .. query_start[s+1]-1
+    of q (int32 device tensor [S+1]) are the last positions of sequence s and
+    attend causally through block_tables [S][MB]; row i of n sits at position
+    context_lens[s] - n + i.  max_query_len bounds the rows per sequence.
+    events: optional (begin, mid, end) torch.cuda.Event triple recorded around
+    the attention kernel and the partition reduction."""
+    rows, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    S = context_lens.shape[0]
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"),
+                    (query_start, "query_start")):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if block_tables.shape[0] != S or query_start.shape[0] != S + 1:
+        raise ValueError("block_tables [S][MB], context_lens [S], query_start [S+1]")
+    mb = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        n = multiquery_workspace_size(rows, S, max_query_len, hq, hkv, d, mb, partition_size)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    evs = [None, None, None]
+    if events is not None:
+        evs = [ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events]
+    check(lib().pkv_paged_multiquery_attention_profiled(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"),
+        _dev(query_start, "query_start"), S, rows, int(max_query_len), hq, hkv, d, bs, nb, mb,
+        float(scale), dtype_code(q), dtype_code(k_cache), float(k_scale), float(v_scale),
+        int(partition_size), _dev(workspace, "workspace"), workspace.numel(), _stream(q, stream),
+        *evs))
+    return out
+
+
 def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
     """Copy physical block pairs[i][0] into pairs[i][1] in both caches
     (src_dst_pairs: int32 device tensor [n][2])."""

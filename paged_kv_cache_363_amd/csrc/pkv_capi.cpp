@@ -131,6 +131,45 @@ static bool make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
   return true;
 }
 
+// Multi-query calls
+
+struct MQPlan {
+  int32_t partition, num_parts;
+  size_t off_l, off_acc, ws_bytes;
+};
+
+// Partition and workspace of a multi-query call; false on bad arguments.
+bool mq_plan(int32_t num_rows, int32_t num_seqs, int32_t max_query_len, int32_t num_q_heads,
+             int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+             int32_t partition_size, MQPlan* plan) {
+  if (num_rows < 0 || num_seqs < 0 || max_query_len < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || head_dim <= 0 || max_blocks_per_seq < 0 || partition_size < 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return false;
+  if (partition_size > 0 && (partition_size % kBlockSize != 0 || partition_size > kMaxPartition))
+    return false;
+  const int32_t max_ctx = max_blocks_per_seq * kBlockSize;
+  const MQTiles t = mq_tiles(num_q_heads / num_kv_heads, max_query_len > 0 ? max_query_len : 1);
+  // workgroups per sequence and partition: kv-heads x head chunks x row tiles
+  const int64_t per_seq = (int64_t)num_kv_heads * t.hchunks * t.qtiles;
+  const int32_t ps = partition_size > 0
+                         ? partition_size
+                         : choose_partition(num_seqs, per_seq > INT32_MAX ? INT32_MAX
+                                                                          : (int32_t)per_seq,
+                                            max_ctx);
+  plan->partition = ps;
+  plan->num_parts = max_ctx <= ps ? 1 : (max_ctx + ps - 1) / ps;
+  plan->off_l = plan->off_acc = plan->ws_bytes = 0;
+  if (plan->num_parts > 1) {
+    const size_t rows = (size_t)num_rows * num_q_heads * plan->num_parts;
+    const size_t bm = align256(rows * sizeof(float));
+    plan->off_l = bm;
+    plan->off_acc = 2 * bm;
+    plan->ws_bytes = 2 * bm + align256(rows * head_dim * sizeof(float));
+  }
+  return true;
+}
+
 }  // namespace pkv
 
 using namespace pkv;
@@ -434,6 +473,142 @@ pkv_status pkv_paged_decode_attention(void* out, const void* q, const void* k_ca
       out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
       head_dim, block_size, num_blocks, max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale,
       v_scale, partition_size, workspace, workspace_bytes, PKV_ALGO_AUTO, stream);
+}
+
+/* ---------------------------------------------------- multi-query -- */
+
+int32_t pkv_multiquery_partition_size(int32_t num_seqs, int32_t max_query_len,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t max_blocks_per_seq, int32_t partition_size) {
+  MQPlan plan;
+  if (!mq_plan(0, num_seqs, max_query_len, num_q_heads, num_kv_heads, 128, max_blocks_per_seq,
+               partition_size, &plan))
+    return -1;
+  return plan.partition;
+}
+
+size_t pkv_multiquery_workspace_size(int32_t num_rows, int32_t num_seqs, int32_t max_query_len,
+                                     int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t max_blocks_per_seq,
+                                     int32_t partition_size) {
+  MQPlan plan;
+  if (!mq_plan(num_rows, num_seqs, max_query_len, num_q_heads, num_kv_heads, head_dim,
+               max_blocks_per_seq, partition_size, &plan))
+    return SIZE_MAX;
+  return plan.ws_bytes;
+}
+
+pkv_status pkv_paged_multiquery_attention_profiled(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+    int32_t num_seqs, int32_t num_rows, int32_t max_query_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, float scale, int32_t q_dtype, int32_t kv_dtype, float k_scale,
+    float v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    void* stream, void* ev_begin, void* ev_mid, void* ev_end) {
+  clear_error();
+  if (num_seqs < 0 || num_rows < 0 || max_query_len < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+    return fail(PKV_ERR_INVALID_ARG, "multiquery: bad sizes");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "multiquery: num_q_heads %% num_kv_heads != 0");
+  if (block_size != kBlockSize)
+    return fail(PKV_ERR_UNSUPPORTED, "multiquery: block_size must be 16 (got %d)", block_size);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "multiquery: head_dim must be 64 or 128 (got %d)",
+                head_dim);
+  if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype))
+    return fail(PKV_ERR_INVALID_ARG, "multiquery: bad dtype");
+  if (!((q_dtype == PKV_F16 || q_dtype == PKV_BF16) &&
+        (kv_dtype == q_dtype || kv_dtype == PKV_FP8_E4M3)))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "multiquery: needs 16-bit q and a cache of the same dtype or E4M3 (%d, %d)",
+                q_dtype, kv_dtype);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "multiquery: scale must be finite");
+  if (kv_dtype == PKV_FP8_E4M3 && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
+    return fail(PKV_ERR_INVALID_ARG, "multiquery: FP8 scales must be finite");
+  MQPlan plan;
+  if (!mq_plan(num_rows, num_seqs, max_query_len, num_q_heads, num_kv_heads, head_dim,
+               max_blocks_per_seq, partition_size, &plan))
+    return fail(PKV_ERR_INVALID_ARG,
+                "multiquery: partition_size must be 0 or a multiple of 16 <= %d", kMaxPartition);
+  const MQTiles t = mq_tiles(num_q_heads / num_kv_heads, max_query_len > 0 ? max_query_len : 1);
+  if (num_seqs > 65535 || (int64_t)num_kv_heads * t.hchunks * t.qtiles > 65535 ||
+      (int64_t)num_rows * num_q_heads > INT32_MAX || plan.num_parts > 65535)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "multiquery: grid too large (sequences, kv-heads x row tiles, rows x q-heads)");
+  if (num_seqs == 0 || num_rows == 0 || max_query_len == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return fail(PKV_ERR_INVALID_ARG, "multiquery: NULL pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "multiquery: out, q and the caches must be 16-byte aligned");
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes)
+      return fail(PKV_ERR_WORKSPACE, "multiquery: workspace needs %zu bytes, got %zu",
+                  plan.ws_bytes, workspace ? workspace_bytes : (size_t)0);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(PKV_ERR_INVALID_ARG, "multiquery: workspace must be 256-byte aligned");
+  }
+  MQArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.num_seqs = num_seqs;
+  a.num_rows = num_rows;
+  a.max_query_len = max_query_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.q_dtype = q_dtype;
+  a.kv_dtype = kv_dtype;
+  a.scale = scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.partition = plan.partition;
+  a.num_parts = plan.num_parts;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_m = plan.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  a.ws_l = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
+  a.ws_acc = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_acc) : nullptr;
+  a.stream = stream;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), hs) != hipSuccess)
+    return fail(PKV_ERR_HIP, "multiquery: hipEventRecord failed");
+  int rc = launch_multiquery(a);
+  if (rc != 0)
+    return fail(PKV_ERR_HIP, "multiquery: launch failed: %s", hipGetErrorString((hipError_t)rc));
+  if (ev_mid && hipEventRecord(static_cast<hipEvent_t>(ev_mid), hs) != hipSuccess)
+    return fail(PKV_ERR_HIP, "multiquery: hipEventRecord failed");
+  if (plan.num_parts > 1) {
+    rc = launch_multiquery_reduce(a);
+    if (rc != 0)
+      return fail(PKV_ERR_HIP, "multiquery: reduce launch failed: %s",
+                  hipGetErrorString((hipError_t)rc));
+  }
+  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), hs) != hipSuccess)
+    return fail(PKV_ERR_HIP, "multiquery: hipEventRecord failed");
+  return PKV_OK;
+}
+
+pkv_status pkv_paged_multiquery_attention(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+    int32_t num_seqs, int32_t num_rows, int32_t max_query_len, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+    int32_t max_blocks_per_seq, float scale, int32_t q_dtype, int32_t kv_dtype, float k_scale,
+    float v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  return pkv_paged_multiquery_attention_profiled(
+      out, q, k_cache, v_cache, block_tables, context_lens, query_start, num_seqs, num_rows,
+      max_query_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+      max_blocks_per_seq, scale, q_dtype, kv_dtype, k_scale, v_scale, partition_size, workspace,
+      workspace_bytes, stream, nullptr, nullptr, nullptr);
 }
 
 pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,

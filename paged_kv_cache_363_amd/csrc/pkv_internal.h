@@ -61,7 +61,46 @@ struct DecodeArgs {
   void* stream;
 };
 
+// Multi-query call: rows query_start[s] .. query_start[s+1]-1 belong to
+// sequence s (at most max_query_len of them are computed).
+struct MQArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;
+  int32_t num_seqs, num_rows, max_query_len;
+  int32_t num_q_heads, num_kv_heads, head_dim, num_blocks, max_blocks_per_seq;
+  int32_t q_dtype, kv_dtype;
+  float scale, k_scale, v_scale;
+  int32_t partition;   // tokens per partition
+  int32_t num_parts;   // partitions in the grid (1 = single pass)
+  float* ws_m;         // [rows][Hq][P]
+  float* ws_l;         // [rows][Hq][P]
+  float* ws_acc;       // [rows][Hq][P][D]
+  void* stream;
+};
+
+// Column layout of a multi-query MFMA tile: 16 columns = qpt query rows x
+// chunk q-heads of one kv-head; hchunks head groups per kv-head; qtiles row
+// tiles for max_query_len rows.
+struct MQTiles {
+  int chunk, hchunks, qpt, qtiles;
+};
+inline MQTiles mq_tiles(int g, int max_query_len) {
+  MQTiles t;
+  t.chunk = g < 16 ? g : 16;
+  t.hchunks = (g + t.chunk - 1) / t.chunk;
+  t.qpt = 16 / t.chunk;
+  t.qtiles = (max_query_len + t.qpt - 1) / t.qpt;
+  return t;
+}
+
 // Kernel launchers (return hipError_t as int).
+int launch_multiquery(const MQArgs& a);
+int launch_multiquery_reduce(const MQArgs& a);
 int launch_decode_vector(const DecodeArgs& a);
 int launch_decode_mfma(const DecodeArgs& a);
 int launch_decode_reduce(const DecodeArgs& a);

@@ -188,9 +188,12 @@ struct MfmaTile {
   // Online-softmax update of (m_run, l_run, o) with one tile holding `valid`
   // live tokens (0 = none: the state does not change, and the tile's
   // registers are still read, so the caller need not branch around it).
-  // qr: raw q operand (zeros for padding heads).
-  __device__ static void consume(Raw& r, int valid, const uint4* qr, float sl2, float& m_run,
-                                 float& l_run, f32x4* o, int c, int G) {
+  // vis <= valid: tokens of the tile this lane's column may attend to (its
+  // causal limit; valid for a single query).  V rows past `valid` are zeroed,
+  // rows in [vis, valid) are finite and get weight zero.
+  // qr: raw q operand (zeros for padding columns).
+  __device__ static void consume(Raw& r, int valid, int vis, const uint4* qr, float sl2,
+                                 float& m_run, float& l_run, f32x4* o, int c, int G) {
     V8 kop[KSTEPS];
     if constexpr (FP8) {
 #pragma unroll
@@ -222,7 +225,7 @@ struct MfmaTile {
 
     float z[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) z[i] = (4 * G + i < valid) ? sacc[i] * sl2 : kNegInf;
+    for (int i = 0; i < 4; ++i) z[i] = (4 * G + i < vis) ? sacc[i] * sl2 : kNegInf;
     float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     bm = wave_max4(bm);
     const float m_new = fmaxf(m_run, bm);
@@ -285,12 +288,14 @@ struct MfmaTile {
 // Every load is issued unconditionally (ids past the chunk repeat its last
 // block, invalid ids read block 0 and carry no weight), so the load counter
 // can be waited on per block instead of drained.  nb must be > 0.
-template <int QT, int KVT, int D, int DEPTH, bool NT>
+// CAUSAL: the lane's column attends to positions <= pos only (several
+// queries of one sequence in one tile); otherwise pos is ignored.
+template <int QT, int KVT, int D, int DEPTH, bool NT, bool CAUSAL = false>
 __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
                                            int64_t blk_stride, const int32_t* row, int b0,
                                            int b1, int last, int tail, int nb, const uint4* qr,
                                            float sl2, float& m_run, float& l_run, f32x4* o,
-                                           int lane) {
+                                           int lane, int pos = 0) {
   using T = MfmaTile<QT, KVT, D>;
   using Raw = typename T::Raw;
   const int c = lane & 15, G = lane >> 4;
@@ -315,7 +320,8 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
         const int idn = id_at(ii + DEPTH);
         const int valid = (ii < n && (unsigned)idc[d] < (unsigned)nb)
                               ? (c0 + ii == last ? tail : 16) : 0;
-        T::consume(buf[d], valid, qr, sl2, m_run, l_run, o, c, G);
+        const int vis = CAUSAL ? min(valid, pos - 16 * (c0 + ii) + 1) : valid;
+        T::consume(buf[d], valid, vis, qr, sl2, m_run, l_run, o, c, G);
         const int64_t a = addr(idn);
         T::template issue<NT>(buf[d], kc + a, vc + a, koff, voff);
         idc[d] = idn;

@@ -115,3 +115,59 @@ def test_stream_workgroups_setting_changes_workspace():
 def test_copy_blocks_rejects():
     assert lib().pkv_copy_blocks(NULL, NULL, NULL, 1, 4, 24, NULL) == _lib.PKV_ERR_INVALID_ARG
     assert lib().pkv_copy_blocks(NULL, NULL, NULL, 0, 4, 32, NULL) == _lib.PKV_OK
+
+
+def multiquery(**kw):
+    a = dict(out=NULL, q=NULL, k=NULL, v=NULL, bt=NULL, cl=NULL, qs=NULL, S=4, rows=16, maxq=4,
+             hq=8, hkv=2, d=128, bs=16, nb=10, mb=4, scale=0.1, qd=_lib.PKV_BF16,
+             kvd=_lib.PKV_BF16, ks=1.0, vs=1.0, ps=0, ws=NULL, wsb=0, stream=NULL)
+    a.update(kw)
+    return lib().pkv_paged_multiquery_attention(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["S"], a["rows"], a["maxq"],
+        a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mb"], a["scale"], a["qd"], a["kvd"],
+        a["ks"], a["vs"], a["ps"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bs=32), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(d=96), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(hq=6, hkv=4), _lib.PKV_ERR_INVALID_ARG),
+    (dict(qd=_lib.PKV_F32, kvd=_lib.PKV_F32), _lib.PKV_ERR_UNSUPPORTED),   # MFMA only
+    (dict(qd=_lib.PKV_BF16, kvd=_lib.PKV_F16), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(qd=9), _lib.PKV_ERR_INVALID_ARG),
+    (dict(ps=24), _lib.PKV_ERR_INVALID_ARG),
+    (dict(rows=-1), _lib.PKV_ERR_INVALID_ARG),
+    (dict(maxq=-1), _lib.PKV_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.PKV_ERR_INVALID_ARG),
+    (dict(kvd=_lib.PKV_FP8_E4M3, ks=float("inf")), _lib.PKV_ERR_INVALID_ARG),
+    (dict(hq=8, hkv=8, maxq=70000 * 16), _lib.PKV_ERR_UNSUPPORTED),      # row tiles beyond the grid
+    (dict(S=70000), _lib.PKV_ERR_UNSUPPORTED),
+    (dict(), _lib.PKV_ERR_INVALID_ARG),                                # NULL pointers
+])
+def test_multiquery_rejects(kw, status):
+    assert multiquery(**kw) == status
+    assert lib().pkv_last_error() != b""
+
+
+def test_multiquery_empty_calls_and_workspace_check():
+    assert multiquery(S=0) == _lib.PKV_OK
+    assert multiquery(rows=0) == _lib.PKV_OK
+    assert multiquery(maxq=0) == _lib.PKV_OK
+    fake = ctypes.c_void_p(1 << 20)
+    # 4 sequences x 2 kv-heads x 1 row tile: too few workgroups for one pass
+    st = multiquery(out=fake, q=fake, k=fake, v=fake, bt=fake, cl=fake, qs=fake, mb=256, ps=512)
+    assert st == _lib.PKV_ERR_WORKSPACE
+
+
+def test_multiquery_partition_and_workspace_helpers():
+    l = lib()
+    # 64 sequences x 8 kv-heads x 1 row tile = 512 workgroups: partitions of 512
+    assert l.pkv_multiquery_partition_size(64, 4, 32, 8, 256, 0) == 512
+    # 16 x 8 x 128 row tiles (512 rows, 4 per tile): one pass over the context
+    assert l.pkv_multiquery_partition_size(16, 512, 32, 8, 2048, 0) == 2048 * 16
+    assert l.pkv_multiquery_partition_size(16, 512, 32, 8, 2048, 64) == 64
+    assert l.pkv_multiquery_partition_size(16, 512, 32, 8, 2048, 24) == -1
+    assert l.pkv_multiquery_workspace_size(8192, 16, 512, 32, 8, 128, 2048, 0) == 0
+    n = l.pkv_multiquery_workspace_size(256, 64, 4, 32, 8, 128, 256, 512)
+    assert n >= 256 * 32 * 8 * (128 + 2) * 4
+    assert l.pkv_multiquery_workspace_size(-1, 64, 4, 32, 8, 128, 256, 512) == ctypes.c_size_t(-1).value
