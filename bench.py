@@ -42,6 +42,10 @@ def parse():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--all-configs", action="store_true",
                     help="also time the other workloads and add them under 'other_configs'")
+    ap.add_argument("--multiquery", action="store_true",
+                    help="also time the multi-query workloads (prompt chunks, draft "
+                         "verification) and add them under 'multiquery' (implied by "
+                         "--all-configs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (10 times): the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -254,6 +258,99 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
     return res
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/f16 MFMA, published peak
+
+
+def time_multiquery(mq, args, dev):
+    """One multi-query call (several rows per sequence attending causally) on
+    a decode workload's cache: K calls back to back, then a pass with events
+    around the attention kernel.  Algorithmic bytes: every context token's K
+    and V once; flops: 4 d per (row, q-head, visible token)."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_363_amd as pkv
+    from synth import CONFIGS, gen
+    cfg = CONFIGS[mq.base]
+    log(f"setup {mq.name}")
+    st = setup(cfg, dev)
+    pkv.paged_cache_append(st["k_cache"], st["v_cache"], st["k_new"], st["v_new"], st["slots"],
+                           st["k_scale"], st["v_scale"])
+    ctx = st["ctx"].astype(np.int64)
+    ql = gen.query_lens(mq, st["ctx"])
+    qs = gen.query_start(ql)
+    rows = int(qs[-1])
+    q = gen.mq_queries(mq, cfg, rows).to(dev)
+    qs_dev = torch.from_numpy(qs).to(dev)
+    max_q = int(ql.max(initial=0))
+    eb = kv_elem_bytes(cfg.kv_dtype)
+    kv_bytes = int(ctx.sum()) * 2 * cfg.num_kv_heads * cfg.head_dim * eb
+    visible = sum(int(ctx[s]) * int(ql[s]) - int(ql[s]) * (int(ql[s]) - 1) // 2
+                  for s in range(cfg.num_seqs))      # sum over rows of (position + 1)
+    flops = 4 * cfg.head_dim * cfg.num_q_heads * visible
+    R = max(1, min(8, math.ceil(4 * MALL_BYTES / max(kv_bytes, 1))))
+    kcs, vcs = [st["k_cache"]], [st["v_cache"]]
+    for _ in range(R - 1):
+        kcs.append(st["k_cache"].clone())
+        vcs.append(st["v_cache"].clone())
+    ps = pkv.multiquery_partition_size(cfg.num_seqs, max_q, cfg.num_q_heads, cfg.num_kv_heads,
+                                       cfg.max_blocks_per_seq, 0)
+    n = pkv.multiquery_workspace_size(rows, cfg.num_seqs, max_q, cfg.num_q_heads,
+                                      cfg.num_kv_heads, cfg.head_dim, cfg.max_blocks_per_seq, ps)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def call(i, evs=None):
+        r = i % R
+        pkv.paged_multiquery_attention(q, kcs[r], vcs[r], st["block_tables"], st["context_lens"],
+                                       qs_dev, max_q, cfg.scale, st["k_scale"], st["v_scale"],
+                                       partition_size=ps, out=out, workspace=ws, events=evs)
+
+    for i in range(max(2, args.warmup // 4)):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    call(0)
+    torch.cuda.synchronize()
+    K = max(3, min(args.steps, int(2.0 / max(time.perf_counter() - t0, 1e-6))))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(K):
+        call(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    call_ms = a.elapsed_time(b) / K
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for trio in evs:
+        for e in trio:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(K):
+        call(i, evs[i])
+    torch.cuda.synchronize()
+    kern_ms = sum(x.elapsed_time(y) for x, y, _ in evs) / K
+    red_ms = sum(y.elapsed_time(z) for _, y, z in evs) / K
+    gbs = kv_bytes / (kern_ms * 1e-3) / 1e9
+    tflops = flops / (kern_ms * 1e-3) / 1e12
+    mfma_bound = flops / kv_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    roof = ({"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+            if mfma_bound else
+            {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    log(f"{mq.name}: {K} calls, {call_ms:.4f} ms/call, attention kernel {kern_ms:.4f} ms")
+    res = {"description": mq.description, "rows": rows, "max_rows_per_seq": max_q,
+           "partition": ps, "ms_per_call": round(call_ms, 5), "kernel_ms": round(kern_ms, 5),
+           "reduce_ms": round(red_ms, 5), "rows_per_s": round(rows / (call_ms * 1e-3), 1),
+           "kv_gbs_call": round(kv_bytes / (call_ms * 1e-3) / 1e9, 2),
+           "kv_gbs_kernel": round(gbs, 2), "tflops_kernel": round(tflops, 2),
+           "flop_per_byte": round(flops / kv_bytes, 2), "kv_bytes": kv_bytes, "flops": flops,
+           "calls": K, "replicas": R, "roofline": roof}
+    del kcs, vcs, st
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg, st, budget_s, gpu_out):
     """The fp64 oracle, single-threaded, on a bounded sample of the same
     workload's sequences (longest context first, until the time budget is
@@ -373,6 +470,9 @@ def main():
             del r
             torch.cuda.empty_cache()
         line["other_configs"] = others
+    if args.all_configs or args.multiquery:
+        from synth import MQ_CONFIGS
+        line["multiquery"] = {name: time_multiquery(m, args, dev) for name, m in MQ_CONFIGS.items()}
     print(json.dumps(line), flush=True)
 
 
