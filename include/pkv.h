@@ -15,13 +15,17 @@
  *   - "KV Cache 与 PageAttention深度实战": 1.2 (Attention(Q,K,V) =
  *     softmax(QK^T/sqrt(d_k))V; the decode output attends over
  *     [K_prefix, K_t], [V_prefix, V_t]), 3.2 (attention gathers K/V through
- *     the block table).
+ *     the block table), 4.1 (blocks swapped out to CPU memory when space is
+ *     short).
  *   - "大语言模型推理引擎深度剖析": 2.2 (O(1) block allocation and release),
  *     2.3 (shared prefix blocks, reference counts, copy before write),
- *     4.2 (FP8 E4M3 with range +-448), 4.3 (FP8 KV cache, dequantised for
- *     compute).
+ *     3.3 (preemption by swapping blocks to host DRAM), 4.1 (draft tokens
+ *     verified in one parallel pass), 4.2 (FP8 E4M3 with range +-448), 4.3
+ *     (FP8 KV cache, dequantised for compute).
  *   - "vLLM推理引擎深度解析": 2.2 (block pool, block tables, free-block queue,
- *     a new block every 16 generated tokens).
+ *     a new block every 16 generated tokens), 3.3 (chunked prefill).
+ *   - "推理加速三板斧": 4.5 (prompts cut into chunks of about 512 tokens and
+ *     scheduled with decode requests).
  *
  * Conventions shared by every entry point:
  *   - Every call returns a pkv_status; nothing throws across the ABI.  On an
@@ -290,6 +294,29 @@ size_t pkv_multiquery_workspace_size(int32_t num_rows, int32_t num_seqs, int32_t
                                      int32_t head_dim, int32_t max_blocks_per_seq,
                                      int32_t partition_size);
 
+/* ------------------------------------------------------------ swapping -- */
+
+/* Copy whole blocks between two caches of the same layout ([blocks][H_kv]
+ * [16][d], block_bytes per block of one cache), K and V: for i < num_pairs,
+ * block src_dst_pairs[2i] of (src_k, src_v) goes to block src_dst_pairs[2i+1]
+ * of (dst_k, dst_v).  Either side may be pinned host memory
+ * (hipHostMalloc), which the kernel reads or writes through its mapping:
+ * swapping a preempted request's blocks to host DRAM and back
+ * ("大语言模型推理引擎深度剖析", section 3.3, bounded by the host link).
+ *   src_dst_pairs : int32[num_pairs][2] readable by the device; a pair with
+ *                   an id outside [0, src_num_blocks) or [0, dst_num_blocks)
+ *                   is skipped.  When src and dst are the same cache, no
+ *                   destination may also be a source of the call.
+ *   block_bytes   : a multiple of 16; caches 16-byte aligned.
+ * Every buffer must be device memory or pinned host memory: the call looks
+ * each one up (hipPointerGetAttributes) and returns PKV_ERR_INVALID_ARG for
+ * memory a kernel cannot reach, such as pageable host memory.
+ * Asynchronous on stream. */
+pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks, const void* src_k,
+                           const void* src_v, int32_t src_num_blocks,
+                           const int32_t* src_dst_pairs, int32_t num_pairs, int64_t block_bytes,
+                           void* stream);
+
 /* ---------------------------------------------------- copy-on-write copy -- */
 
 /* Copy whole physical blocks, K and V: for i < num_pairs, block
@@ -382,6 +409,20 @@ pkv_status pkv_batch_append_slots(pkv_pool* pool, int32_t* block_tables,
                                   int32_t* context_lens, const int32_t* n_new, int32_t num_seqs,
                                   int64_t* slot_mapping, int32_t* cow_pairs, int32_t cow_cap,
                                   int32_t* n_cow, int32_t* n_slots);
+/* Swap a sequence to another pool: the pools stand for device blocks and
+ * host-memory blocks ("大语言模型推理引擎深度剖析", section 3.3: under memory
+ * pressure a request's blocks move from HBM to host DRAM and come back
+ * without recomputation; "KV Cache 与 PageAttention深度实战", section 4.1).
+ * Takes nblocks blocks of `to` in free-queue order into table_out, writes
+ * (table[i], table_out[i]) to pairs_out[2i], pairs_out[2i+1] for
+ * pkv_swap_blocks, then releases `table` in `from` as pkv_seq_free does
+ * (blocks shared with other sequences stay).  from == to is allowed (every
+ * new block is taken before any is released).  table_out: host int32[nblocks];
+ * pairs_out: host int32[2*nblocks].  All-or-nothing: PKV_ERR_OUT_OF_BLOCKS,
+ * PKV_ERR_REFCOUNT or PKV_ERR_INVALID_ARG (bad id, block sizes differ) change
+ * neither pool. */
+pkv_status pkv_seq_swap(pkv_pool* from, pkv_pool* to, const int32_t* table, int32_t nblocks,
+                        int32_t* table_out, int32_t* pairs_out);
 /* Release a sequence: decref its blocks from the last to the first. */
 pkv_status pkv_seq_free(pkv_pool* pool, const int32_t* table, int32_t nblocks);
 

@@ -26,7 +26,12 @@ Readings where the pages leave a choice:
   - an append that cannot get every block it needs fails and changes nothing;
   - a batch append (one decode step's bookkeeping for many sequences) is the
     single-sequence append applied to each sequence in batch order, and it
-    too either succeeds for every sequence or changes nothing.
+    too either succeeds for every sequence or changes nothing;
+  - swapping a sequence to another pool (device blocks to host memory and
+    back, "大语言模型推理引擎深度剖析" section 3.3) takes one block of the
+    target pool per block of the table, in table order, then releases the
+    table in the source pool as a free does; it needs every target block or
+    changes nothing.
 """
 import copy
 from collections import deque
@@ -171,6 +176,22 @@ class RefPool:
             self.free, self.ref = saved[2], saved[3]
             raise
         return slots, cows
+
+    def seq_swap(self, target, table):
+        """Move a sequence's blocks to `target` (another pool, e.g. host
+        memory): returns (new table, [(old block, new block), ...]) for the
+        caller to copy, and releases the table here."""
+        for b in table:
+            self._check(b)
+            if self.ref[b] < 1:
+                raise RefcountError(f"swap of free block {b}")
+        if target.block_size != self.block_size:
+            raise InvalidArg("block sizes differ")
+        if len(target.free) < len(table):
+            raise OutOfBlocks(f"need {len(table)} blocks, {len(target.free)} free")
+        new = [target.alloc() for _ in table]
+        self.seq_free(table)
+        return new, list(zip(table, new))
 
     def seq_free(self, table):
         for b in table:

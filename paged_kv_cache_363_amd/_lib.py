@@ -45,6 +45,8 @@ SIGNATURES = {
                                                       I32, I32, I32, I32, F32, I32, I32, F32, F32,
                                                       I32, P, SZ, P, P, P, P]),
     "pkv_copy_blocks": (I32, [P, P, P, I32, I32, I64, P]),
+    "pkv_swap_blocks": (I32, [P, P, I32, P, P, I32, P, I32, I64, P]),
+    "pkv_seq_swap": (I32, [P, P, P, I32, P, P]),
     "pkv_pool_create": (I32, [I32, I32, P, ctypes.POINTER(P)]),
     "pkv_pool_destroy": (None, [P]),
     "pkv_pool_alloc": (I32, [P, P]),

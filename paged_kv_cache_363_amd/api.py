@@ -188,6 +188,28 @@ def paged_multiquery_attention(q, k_cache, v_cache, block_tables, context_lens, 
     return out
 
 
+def swap_blocks(dst_k, dst_v, src_k, src_v, src_dst_pairs, stream=None):
+    """Copy block pairs[i][0] of (src_k, src_v) into block pairs[i][1] of
+    (dst_k, dst_v); either side may be a pinned host tensor (swap out / in).
+    src_dst_pairs: int32 tensor [n][2] on the device or in pinned memory."""
+    if tuple(dst_k.shape[1:]) != tuple(src_k.shape[1:]) or dst_k.dtype != src_k.dtype:
+        raise ValueError("the two caches must have the same block layout and dtype")
+    for t, name in ((dst_k, "dst_k"), (dst_v, "dst_v"), (src_k, "src_k"), (src_v, "src_v"),
+                    (src_dst_pairs, "src_dst_pairs")):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError(f"{name} must be a device tensor or pinned host memory")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if src_dst_pairs.dtype != torch.int32:
+        raise TypeError("src_dst_pairs must be int32")
+    dev = dst_k if dst_k.is_cuda else src_k
+    block_bytes = dst_k[0].numel() * dst_k.element_size()
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    check(lib().pkv_swap_blocks(ptr(dst_k), ptr(dst_v), dst_k.shape[0], ptr(src_k), ptr(src_v),
+                                src_k.shape[0], ptr(src_dst_pairs), src_dst_pairs.shape[0],
+                                block_bytes, _stream(dev, stream)))
+
+
 def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
     """Copy physical block pairs[i][0] into pairs[i][1] in both caches
     (src_dst_pairs: int32 device tensor [n][2])."""

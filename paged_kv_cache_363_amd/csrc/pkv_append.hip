@@ -81,6 +81,22 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ 
   for (int64_t i = threadIdx.x; i < n; i += 256) d[i] = s[i];
 }
 
+// One workgroup copies one block of K (blockIdx.y == 0) or V between two
+// caches of the same block layout; either may be pinned host memory mapped
+// into the device's address space (swapping blocks out and back in).
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    uint8_t* __restrict__ dk, uint8_t* __restrict__ dv, int dst_blocks,
+    const uint8_t* __restrict__ sk, const uint8_t* __restrict__ sv, int src_blocks,
+    const int32_t* __restrict__ pairs, int64_t block_bytes) {
+  const int src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const uint4* s =
+      reinterpret_cast<const uint4*>((blockIdx.y ? sv : sk) + (int64_t)src * block_bytes);
+  uint4* d = reinterpret_cast<uint4*>((blockIdx.y ? dv : dk) + (int64_t)dst * block_bytes);
+  const int64_t n = block_bytes / 16;
+  for (int64_t i = threadIdx.x; i < n; i += 256) d[i] = s[i];
+}
+
 template <int NEW_DT, int KV_DT>
 int launch_append_t(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                     const int64_t* slots, int32_t T, int32_t H, int32_t D, int32_t nb,
@@ -127,6 +143,16 @@ int launch_cache_append(void* k_cache, void* v_cache, const void* k_new, const v
     }
   }
   return (int)hipErrorInvalidValue;
+}
+
+int launch_swap_blocks(void* dst_k, void* dst_v, int32_t dst_blocks, const void* src_k,
+                       const void* src_v, int32_t src_blocks, const int32_t* pairs,
+                       int32_t num_pairs, int64_t block_bytes, void* stream) {
+  if (num_pairs <= 0) return 0;
+  swap_blocks_kernel<<<dim3(num_pairs, 2), dim3(256), 0, (hipStream_t)stream>>>(
+      (uint8_t*)dst_k, (uint8_t*)dst_v, dst_blocks, (const uint8_t*)src_k,
+      (const uint8_t*)src_v, src_blocks, pairs, block_bytes);
+  return (int)hipGetLastError();
 }
 
 int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,

@@ -629,4 +629,48 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_
   return PKV_OK;
 }
 
+// Address through which a kernel reaches p: device memory as is, pinned host
+// memory through its device mapping; nullptr for memory no kernel can touch
+// (pageable host memory), so that such a call fails instead of faulting.
+static const void* kernel_view(const void* p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();   // clear the sticky "not registered" error
+    return nullptr;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) return p;
+  if (at.type == hipMemoryTypeHost) return at.devicePointer;
+  return nullptr;
+}
+
+pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks, const void* src_k,
+                           const void* src_v, int32_t src_num_blocks,
+                           const int32_t* src_dst_pairs, int32_t num_pairs, int64_t block_bytes,
+                           void* stream) {
+  clear_error();
+  if (num_pairs < 0 || dst_num_blocks < 0 || src_num_blocks < 0 || block_bytes <= 0 ||
+      block_bytes % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "swap_blocks: bad sizes");
+  if (num_pairs == 0) return PKV_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !src_dst_pairs)
+    return fail(PKV_ERR_INVALID_ARG, "swap_blocks: NULL pointer");
+  if (!aligned16(dst_k) || !aligned16(dst_v) || !aligned16(src_k) || !aligned16(src_v))
+    return fail(PKV_ERR_INVALID_ARG, "swap_blocks: caches must be 16-byte aligned");
+  void* dk = const_cast<void*>(kernel_view(dst_k));
+  void* dv = const_cast<void*>(kernel_view(dst_v));
+  const void* sk = kernel_view(src_k);
+  const void* sv = kernel_view(src_v);
+  const int32_t* pp = static_cast<const int32_t*>(kernel_view(src_dst_pairs));
+  if (!dk || !dv || !sk || !sv || !pp)
+    return fail(PKV_ERR_INVALID_ARG,
+                "swap_blocks: every buffer must be device memory or pinned host memory");
+  if (!aligned16(dk) || !aligned16(dv) || !aligned16(sk) || !aligned16(sv))
+    return fail(PKV_ERR_INVALID_ARG, "swap_blocks: caches must be 16-byte aligned");
+  int rc = launch_swap_blocks(dk, dv, dst_num_blocks, sk, sv, src_num_blocks, pp, num_pairs,
+                              block_bytes, stream);
+  if (rc != 0)
+    return fail(PKV_ERR_HIP, "swap_blocks: launch failed: %s", hipGetErrorString((hipError_t)rc));
+  return PKV_OK;
+}
+
 }  // extern "C"

@@ -111,6 +111,9 @@ int launch_cache_append(void* k_cache, void* v_cache, const void* k_new, const v
                         const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
                         int32_t head_dim, int32_t num_blocks, int32_t new_dtype, int32_t kv_dtype,
                         float k_inv_scale, float v_inv_scale, void* stream);
+int launch_swap_blocks(void* dst_k, void* dst_v, int32_t dst_blocks, const void* src_k,
+                       const void* src_v, int32_t src_blocks, const int32_t* pairs,
+                       int32_t num_pairs, int64_t block_bytes, void* stream);
 int launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
                        int32_t num_blocks, int64_t block_bytes, void* stream);
 

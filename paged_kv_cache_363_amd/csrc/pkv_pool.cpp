@@ -306,6 +306,33 @@ pkv_status pkv_seq_fork(pkv_pool* pool, const int32_t* table, int32_t nblocks) {
   return PKV_OK;
 }
 
+pkv_status pkv_seq_swap(pkv_pool* from, pkv_pool* to, const int32_t* table, int32_t nblocks,
+                        int32_t* table_out, int32_t* pairs_out) {
+  if (!from || !to || nblocks < 0 || (nblocks > 0 && (!table || !table_out || !pairs_out)))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "seq_swap: bad argument");
+  if (from->block_size != to->block_size)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "seq_swap: block sizes differ");
+  for (int32_t i = 0; i < nblocks; ++i) {
+    const int32_t b = table[i];
+    if (!from->valid(b)) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_swap: bad block id");
+    if (from->ref[b] < 1) return pkv::fail(PKV_ERR_REFCOUNT, "seq_swap: block is free");
+  }
+  if (to->count < nblocks)
+    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "seq_swap: target pool has too few free blocks");
+  // take every target block first (so a swap within one pool never hands out
+  // a block of the table), then release the table as pkv_seq_free does
+  for (int32_t i = 0; i < nblocks; ++i) {
+    table_out[i] = to->pop();
+    pairs_out[2 * i] = table[i];
+    pairs_out[2 * i + 1] = table_out[i];
+  }
+  for (int32_t i = nblocks - 1; i >= 0; --i) {
+    const int32_t b = table[i];
+    if (--from->ref[b] == 0) from->push(b);
+  }
+  return PKV_OK;
+}
+
 pkv_status pkv_seq_free(pkv_pool* pool, const int32_t* table, int32_t nblocks) {
   if (!pool || nblocks < 0 || (nblocks > 0 && !table))
     return pkv::fail(PKV_ERR_INVALID_ARG, "seq_free: bad argument");

@@ -135,6 +135,16 @@ class BlockPool:
             cow_cap, ctypes.byref(ncow), ctypes.byref(nslots)))
         return slot_mapping[:nslots.value], cows[:2 * ncow.value].reshape(-1, 2)
 
+    def seq_swap(self, target, table):
+        """Move a sequence's blocks to pool `target` (pkv_seq_swap): returns
+        (new table, [(old, new), ...]) and releases `table` here."""
+        arr = np.ascontiguousarray(table, dtype=np.int32)
+        n = len(table)
+        out = np.empty(max(n, 1), np.int32)
+        pairs = np.empty(2 * max(n, 1), np.int32)
+        check(lib().pkv_seq_swap(self._h, target._h, _ptr(arr), n, _ptr(out), _ptr(pairs)))
+        return out[:n].tolist(), [(int(pairs[2 * i]), int(pairs[2 * i + 1])) for i in range(n)]
+
     def seq_free(self, table):
         arr = np.ascontiguousarray(table, dtype=np.int32)
         check(lib().pkv_seq_free(self._h, _ptr(arr), len(table)))

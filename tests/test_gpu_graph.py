@@ -1,0 +1,101 @@
+"""A whole decode step captured into one HIP graph ("大语言模型推理引擎深度剖析",
+section 6: capturing the step cuts kernel-launch overhead): the library's
+calls launch kernels only (no allocation, no memset), so the append, the
+decode kernel and its merge or reduction record as graph nodes.  Each graph
+is replayed several times with eager work and synchronisations between the
+replays, and every replay must equal the eager step bit for bit (the kernels
+are deterministic for a fixed grid)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_harness import gpu_setup
+from synth import CONFIGS, MQ_CONFIGS, gen
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_step(st, cfg, ps, out, ws):
+    import paged_kv_cache_363_amd as pkv
+    pkv.paged_cache_append(st["k_cache"], st["v_cache"], st["step"]["k"], st["step"]["v"],
+                           st["step"]["slots"], st["k_scale"], st["v_scale"])
+    pkv.paged_decode_attention(st["q"], st["k_cache"], st["v_cache"], st["block_tables"],
+                               st["context_lens"], cfg.scale, st["k_scale"], st["v_scale"],
+                               partition_size=ps, out=out, workspace=ws)
+
+
+@pytest.mark.parametrize("name,ps", [("c2_qwen3_8b_bf16", 0), ("c4_llama3_70b_fp8", 2560),
+                                     ("c5_long_shared_bf16", 512), ("c3_llama2_7b_f16", 0)])
+def test_captured_decode_step_replays_equal_eager(name, ps):
+    import paged_kv_cache_363_amd as pkv
+    print(f"[case] graph decode {name} partition={ps}", flush=True)
+    cfg = CONFIGS[name]
+    st = gpu_setup(cfg)
+    ws = pkv.alloc_workspace(st["q"], st["k_cache"], st["block_tables"], ps)
+    eager = torch.empty_like(st["q"])
+    _decode_step(st, cfg, ps, eager, ws)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(st["q"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):      # warm the capture stream, as torch asks
+        _decode_step(st, cfg, ps, out, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _decode_step(st, cfg, ps, out, ws)
+    for rep in range(4):
+        out.zero_()
+        # eager work between the replays: a decode into another buffer
+        other = torch.empty_like(st["q"])
+        _decode_step(st, cfg, ps, other, ws)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(other.view(torch.int16), eager.view(torch.int16))
+
+
+def test_captured_multiquery_call_replays_equal_eager():
+    import paged_kv_cache_363_amd as pkv
+    print("[case] graph multiquery mq_c2_verify4", flush=True)
+    mq = MQ_CONFIGS["mq_c2_verify4"]
+    cfg = CONFIGS[mq.base]
+    st = gpu_setup(cfg)
+    ql = gen.query_lens(mq, st["ctx"])
+    qs = torch.from_numpy(gen.query_start(ql)).to("cuda")
+    q = gen.mq_queries(mq, cfg, int(qs[-1])).to("cuda")
+    max_q = int(ql.max())
+    ps = pkv.multiquery_partition_size(cfg.num_seqs, max_q, cfg.num_q_heads, cfg.num_kv_heads,
+                                       cfg.max_blocks_per_seq, 0)
+    n = pkv.multiquery_workspace_size(q.shape[0], cfg.num_seqs, max_q, cfg.num_q_heads,
+                                      cfg.num_kv_heads, cfg.head_dim, cfg.max_blocks_per_seq, ps)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+
+    def call(o):
+        pkv.paged_multiquery_attention(q, st["k_cache"], st["v_cache"], st["block_tables"],
+                                       st["context_lens"], qs, max_q, cfg.scale,
+                                       partition_size=ps, out=o, workspace=ws)
+
+    eager = torch.empty_like(q)
+    call(eager)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out)
+    for rep in range(4):
+        out.zero_()
+        scratch = torch.empty_like(q)
+        call(scratch)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"

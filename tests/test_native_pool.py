@@ -264,3 +264,88 @@ def test_batch_step_equals_per_sequence_calls(name):
         assert slots.tolist() == want
     assert [rows[s, :nbk[s]].tolist() for s in range(cfg.num_seqs)] == st1["tables"]
     assert p1.free_list() == p2.free_list()
+
+
+# -- swapping a sequence to another pool (pkv_seq_swap) ----------------------
+
+def test_swap_out_and_back_in():
+    dev = pkv.BlockPool(8, 16, [3, 1, 4, 0, 5, 2, 6, 7])
+    host = pkv.BlockPool(4, 16, [2, 0, 3, 1])
+    t = dev.seq_create(40)                       # blocks [3, 1, 4]
+    other = dev.seq_fork(t)                      # shared: counts 2
+    ht, pairs = dev.seq_swap(host, t)
+    assert ht == [2, 0, 3] and pairs == [(3, 2), (1, 0), (4, 3)]
+    # the fork still holds the device blocks; nothing went back to the queue
+    assert [dev.refcount(b) for b in t] == [1, 1, 1] and dev.num_free() == 5
+    assert host.free_list() == [1]
+    dt, back = host.seq_swap(dev, ht)
+    assert dt == [0, 5, 2] and back == [(2, 0), (0, 5), (3, 2)]
+    assert host.free_list() == [1, 3, 0, 2]      # released last to first
+    dev.seq_free(other)
+    assert sorted(dev.free_list() + dt) == list(range(8))
+
+
+def test_swap_needs_every_target_block_or_changes_nothing():
+    a = pkv.BlockPool(8, 16)
+    b = pkv.BlockPool(2, 16)
+    t = a.seq_create(40)
+    before = (a.free_list(), b.free_list())
+    with pytest.raises(pkv.OutOfBlocks):
+        a.seq_swap(b, t)
+    with pytest.raises(pkv.InvalidArg):
+        a.seq_swap(pkv.BlockPool(8, 32), t)
+    with pytest.raises(pkv.RefcountError):
+        a.seq_swap(b, [7])
+    assert (a.free_list(), b.free_list()) == before
+    assert [a.refcount(x) for x in t] == [1, 1, 1]
+
+
+def test_swap_within_one_pool_never_reuses_the_table():
+    p = pkv.BlockPool(6, 16)
+    t = p.seq_create(48)                         # [0, 1, 2]
+    nt, pairs = p.seq_swap(p, t)
+    assert nt == [3, 4, 5] and not set(nt) & set(t)
+    assert p.free_list() == [2, 1, 0]
+
+
+def test_swap_random_operations_match_reference():
+    rs = np.random.default_rng(91)
+    od, oh = rs.permutation(40), rs.permutation(24)
+    nd, nh = pkv.BlockPool(40, 16, od), pkv.BlockPool(24, 16, oh)
+    rd, rh = RefPool(40, 16, od), RefPool(24, 16, oh)
+    seqs = []          # [native table, ref table, on device?]
+    for _ in range(1500):
+        op = int(rs.integers(0, 4))
+        if op == 0 or not seqs:
+            k = int(rs.integers(1, 60))
+            try:
+                tr = rd.seq_create(k)
+            except RefOOB:
+                continue
+            seqs.append([nd.seq_create(k), tr, True])
+        elif op == 1:
+            i = int(rs.integers(len(seqs)))
+            tn, tr, on_dev = seqs[i]
+            src_n, dst_n = (nd, nh) if on_dev else (nh, nd)
+            src_r, dst_r = (rd, rh) if on_dev else (rh, rd)
+            try:
+                new_r, pairs_r = src_r.seq_swap(dst_r, tr)
+            except RefOOB:
+                with pytest.raises(pkv.OutOfBlocks):
+                    src_n.seq_swap(dst_n, tn)
+                continue
+            new_n, pairs_n = src_n.seq_swap(dst_n, tn)
+            assert new_n == new_r and pairs_n == pairs_r
+            seqs[i] = [new_n, new_r, not on_dev]
+        elif op == 2:
+            i = int(rs.integers(len(seqs)))
+            tn, tr, on_dev = seqs[i]
+            if on_dev:
+                seqs.append([nd.seq_fork(tn), rd.seq_fork(tr), True])
+        else:
+            i = int(rs.integers(len(seqs)))
+            tn, tr, on_dev = seqs.pop(i)
+            (nd if on_dev else nh).seq_free(tn)
+            (rd if on_dev else rh).seq_free(tr)
+        same(nd, rd)
+        same(nh, rh)
