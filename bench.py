@@ -46,6 +46,9 @@ def parse():
                     help="also time the multi-query workloads (prompt chunks, draft "
                          "verification) and add them under 'multiquery' (implied by "
                          "--all-configs)")
+    ap.add_argument("--swap", action="store_true",
+                    help="also time swapping half the sequences to pinned host memory and "
+                         "back (implied by --all-configs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (10 times): the reference for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -239,6 +242,33 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
     red_ms = [b.elapsed_time(c) for _, b, c in evs]
     part_avg = sum(part_ms) / K
     red_avg = sum(red_ms) / K
+    # The same step captured once into a HIP graph and replayed K times (the
+    # launch path a serving loop can use; every kernel here is capturable).
+    g_step_ms = None
+    try:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(r)
+            graphs.append(g)
+        graphs[0].replay()
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(K):
+            graphs[i % R].replay()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        g_step_ms = t_start.elapsed_time(t_end) / K
+        del graphs
+    except RuntimeError as e:   # reported, never silently replaced
+        log(f"graph capture failed: {e}")
     achieved = kv_bytes / (part_avg * 1e-3) / 1e9
     res = dict(
         config=cfg.name, kv_bytes=kv_bytes, replicas=R, cache_bytes_per_replica=cache_bytes,
@@ -248,6 +278,7 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
         ms_per_step=step_ms, wall_ms_per_step=wall / K * 1e3,
         decode_kernel_ms=part_avg, reduce_kernel_ms=red_avg,
         step_gbs=kv_bytes / (step_ms * 1e-3) / 1e9,
+        graph_ms_per_step=g_step_ms,
         decode_kernel_gbs=achieved, tokens_per_s=cfg.num_seqs / (step_ms * 1e-3),
         t_pool_build_s=st["t_pool_build"])
     log(f"timed {K} steps: {step_ms:.4f} ms/step, decode kernel {part_avg:.4f} ms")
@@ -347,6 +378,58 @@ def time_multiquery(mq, args, dev):
            "flop_per_byte": round(flops / kv_bytes, 2), "kv_bytes": kv_bytes, "flops": flops,
            "calls": K, "replicas": R, "roofline": roof}
     del kcs, vcs, st
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_swap(cfg, args, dev):
+    """Swap half of the workload's sequences to pinned host memory and back
+    (pkv_seq_swap bookkeeping, pkv_swap_blocks copies): GB/s each way over the
+    K and V bytes moved, each direction timed over several repetitions."""
+    import torch
+    import paged_kv_cache_363_amd as pkv
+    log(f"setup swap {cfg.name}")
+    st = setup(cfg, dev)
+    pool, tables = st["pool"], st["state"]["tables"]
+    moved = list(range(0, cfg.num_seqs, 2))
+    n = sum(len(tables[s]) for s in moved)
+    host = pkv.BlockPool(n, cfg.block_size)
+    shape = (n,) + tuple(st["k_cache"].shape[1:])
+    hk = torch.empty(shape, dtype=st["k_cache"].dtype, pin_memory=True)
+    hv = torch.empty(shape, dtype=st["k_cache"].dtype, pin_memory=True)
+    t0 = time.perf_counter()
+    out_pairs, host_tables = [], {}
+    for s in moved:
+        host_tables[s], pr = pool.seq_swap(host, tables[s])
+        out_pairs += pr
+    t_book = time.perf_counter() - t0
+    p_out = torch.tensor(out_pairs, dtype=torch.int32, device=dev)
+    p_in = torch.tensor([(b, a) for a, b in out_pairs], dtype=torch.int32, device=dev)
+    block_bytes = st["k_cache"][0].numel() * st["k_cache"].element_size()
+    moved_bytes = 2 * n * block_bytes
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    reps = 5
+    pkv.swap_blocks(hk, hv, st["k_cache"], st["v_cache"], p_out)
+    pkv.swap_blocks(st["k_cache"], st["v_cache"], hk, hv, p_in)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        pkv.swap_blocks(hk, hv, st["k_cache"], st["v_cache"], p_out)
+    ev[1].record()
+    for _ in range(reps):
+        pkv.swap_blocks(st["k_cache"], st["v_cache"], hk, hv, p_in)
+    ev[2].record()
+    torch.cuda.synchronize()
+    out_ms = ev[0].elapsed_time(ev[1]) / reps
+    in_ms = ev[1].elapsed_time(ev[2]) / reps
+    res = {"workload": cfg.name, "sequences": len(moved), "blocks": n,
+           "bytes_each_way": moved_bytes,
+           "out_ms": round(out_ms, 4), "in_ms": round(in_ms, 4),
+           "out_gbs": round(moved_bytes / (out_ms * 1e-3) / 1e9, 2),
+           "in_gbs": round(moved_bytes / (in_ms * 1e-3) / 1e9, 2),
+           "host_bookkeeping_ms": round(t_book * 1e3, 3)}
+    log(f"swap: {res['out_gbs']} GB/s out, {res['in_gbs']} GB/s in")
+    del hk, hv, st
     torch.cuda.empty_cache()
     return res
 
@@ -451,6 +534,9 @@ def main():
                      "kernel_ms": round(res["decode_kernel_ms"], 5),
                      "algorithmic_bytes_per_launch": res["kv_bytes"]},
         "merge_or_reduce_ms": round(res["reduce_kernel_ms"], 5),
+        "graph": ({"ms_per_step": round(res["graph_ms_per_step"], 5),
+                   "step_gbs": round(res["kv_bytes"] / (res["graph_ms_per_step"] * 1e-3) / 1e9, 2)}
+                  if res["graph_ms_per_step"] else None),
         "host_bookkeeping_us_per_step": round(res["host_bookkeeping_us_per_step"], 1),
         "cpu_baseline": res.get("cpu_baseline"),
     }
@@ -466,10 +552,14 @@ def main():
                             "ms_per_step": round(r["ms_per_step"], 5),
                             "decode_kernel_ms": round(r["decode_kernel_ms"], 5),
                             "tokens_per_s": round(r["tokens_per_s"], 1), "algo": r["algo"],
+                            "graph_ms_per_step": (round(r["graph_ms_per_step"], 5)
+                                                  if r["graph_ms_per_step"] else None),
                             "kernel": r["kernel"], "partition": r["partition"]}
             del r
             torch.cuda.empty_cache()
         line["other_configs"] = others
+    if args.all_configs or args.swap:
+        line["swap"] = time_swap(cfg, args, dev)
     if args.all_configs or args.multiquery:
         from synth import MQ_CONFIGS
         line["multiquery"] = {name: time_multiquery(m, args, dev) for name, m in MQ_CONFIGS.items()}
