@@ -409,6 +409,39 @@ pkv_status pkv_batch_append_slots(pkv_pool* pool, int32_t* block_tables,
                                   int32_t* context_lens, const int32_t* n_new, int32_t num_seqs,
                                   int64_t* slot_mapping, int32_t* cow_pairs, int32_t cow_cap,
                                   int32_t* n_cow, int32_t* n_slots);
+/* Prefix caching ("vLLM推理引擎深度解析", section 4.1: computed KV blocks of
+ * shared prompts are cached and reused; "KV Cache 与 PageAttention深度实战",
+ * section 4.2: an LRU cache of computed prefix blocks that a request with the
+ * same prefix reuses directly).  A full block is known by the exact key
+ * (parent block, the parent's allocation generation, its block_size token
+ * ids), the first block's parent being -1.  Registered blocks stay findable
+ * while in use and after release, at the tail of the free queue, until
+ * allocation reaches them at the head (least recently freed first) and
+ * evicts them; a block's generation advances at every hand-out, so a chain
+ * whose parent was reused never matches.  Blocks never registered behave as
+ * before; a pool that is never asked to register behaves exactly as without
+ * caching.
+ *
+ * A table for a prompt of token ids: its longest run of cached full blocks
+ * from the start is reused (one more reference each; a free one leaves the
+ * queue), the rest are new blocks.  table: host int32[cap]; *nblocks receives
+ * ceil(prompt_len / block_size), *cached_tokens the tokens whose K/V are
+ * already in the reused blocks (a multiple of block_size).  All-or-nothing:
+ * PKV_ERR_OUT_OF_BLOCKS or PKV_ERR_INVALID_ARG (cap too small) change
+ * nothing. */
+pkv_status pkv_seq_create_cached(pkv_pool* pool, const int32_t* tokens, int32_t prompt_len,
+                                int32_t* table, int32_t cap, int32_t* nblocks,
+                                int32_t* cached_tokens);
+/* Declare the full blocks among the first num_tokens tokens of a sequence
+ * (table[0..nblocks), tokens[0..num_tokens)) computed: each becomes findable
+ * under its key, unless another block already holds that key (it then stays
+ * unregistered).  Call it once the K/V of those tokens are in the cache.
+ * PKV_ERR_INVALID_ARG if a block is registered under another key,
+ * PKV_ERR_REFCOUNT for a free block; nothing changes on an error. */
+pkv_status pkv_pool_register_blocks(pkv_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                                    const int32_t* table, int32_t nblocks);
+/* Blocks currently findable in the prefix cache (-1 for NULL). */
+int32_t pkv_pool_cached_blocks(const pkv_pool* pool);
 /* Swap a sequence to another pool: the pools stand for device blocks and
  * host-memory blocks ("大语言模型推理引擎深度剖析", section 3.3: under memory
  * pressure a request's blocks move from HBM to host DRAM and come back

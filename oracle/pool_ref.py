@@ -27,6 +27,18 @@ Readings where the pages leave a choice:
   - a batch append (one decode step's bookkeeping for many sequences) is the
     single-sequence append applied to each sequence in batch order, and it
     too either succeeds for every sequence or changes nothing;
+  - prefix caching ("vLLM推理引擎深度解析" sections 2.2 and 4.1; "KV Cache 与
+    PageAttention深度实战" section 4.2: computed prefix blocks are kept in an
+    LRU cache and a request with the same prefix reuses them).  Reading: a
+    full block is known by the exact key (parent block, the parent's
+    allocation generation, its own token ids), the root's parent being -1;
+    a block's generation grows each time it is handed out, so a chain whose
+    parent was reused never matches.  The caller registers blocks once their
+    K/V are computed.  A freed block keeps its key and joins the tail of the
+    free queue; allocation takes the head, which drops the key (eviction of
+    the least recently freed block).  A lookup matches full blocks from the
+    start and stops at the first miss; a hit on a free block takes it out of
+    the queue;
   - swapping a sequence to another pool (device blocks to host memory and
     back, "大语言模型推理引擎深度剖析" section 3.3) takes one block of the
     target pool per block of the table, in table order, then releases the
@@ -64,6 +76,9 @@ class RefPool:
         self.block_size = block_size
         self.free = deque(order)
         self.ref = [0] * num_blocks
+        self.gen = [0] * num_blocks      # times each block was handed out
+        self.key = [None] * num_blocks   # prefix-cache key of a registered block
+        self.cache = {}                  # key -> block
 
     # -- single blocks -------------------------------------------------------
     def _check(self, b):
@@ -74,6 +89,10 @@ class RefPool:
         if not self.free:
             raise OutOfBlocks("no free block")
         b = self.free.popleft()
+        if self.key[b] is not None:      # evict the least recently freed
+            del self.cache[self.key[b]]
+            self.key[b] = None
+        self.gen[b] += 1
         self.ref[b] = 1
         return b
 
@@ -176,6 +195,69 @@ class RefPool:
             self.free, self.ref = saved[2], saved[3]
             raise
         return slots, cows
+
+    # -- prefix caching --------------------------------------------------------
+    def _block_keys(self, tokens, n_full):
+        """Walk the cache along the prompt: the blocks hit, stopping at the
+        first full block not cached."""
+        bs = self.block_size
+        hits, parent = [], (-1, 0)
+        for i in range(n_full):
+            b = self.cache.get(parent + (tuple(tokens[i * bs:(i + 1) * bs]),))
+            if b is None:
+                break
+            hits.append(b)
+            parent = (b, self.gen[b])
+        return hits
+
+    def seq_create_cached(self, tokens, prompt_len, cap=None):
+        """A table for a prompt of token ids: its longest cached run of full
+        blocks is reused (one more reference each), the rest is new.
+        Returns (table, cached_tokens)."""
+        bs = self.block_size
+        if prompt_len < 0 or len(tokens) < prompt_len:
+            raise InvalidArg("prompt_len")
+        need = -(-prompt_len // bs)
+        if cap is not None and need > cap:
+            raise InvalidArg("table capacity exceeded")
+        hits = self._block_keys(tokens, prompt_len // bs)
+        revived = sum(1 for b in hits if self.ref[b] == 0)
+        if need - len(hits) > len(self.free) - revived:
+            raise OutOfBlocks("not enough free blocks")
+        for b in hits:
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+        table = hits + [self.alloc() for _ in range(need - len(hits))]
+        return table, len(hits) * bs
+
+    def register_blocks(self, tokens, num_tokens, table):
+        """Declare the full blocks among the first num_tokens of a sequence
+        computed: each becomes findable by its key unless another block
+        already holds that key."""
+        bs = self.block_size
+        n_full = num_tokens // bs
+        if n_full > len(table) or len(tokens) < num_tokens:
+            raise InvalidArg("table or tokens too short")
+        for b in table[:n_full]:
+            self._check(b)
+            if self.ref[b] < 1:
+                raise RefcountError(f"register of free block {b}")
+        keys, parent = [], (-1, 0)
+        for i in range(n_full):
+            b = table[i]
+            k = parent + (tuple(tokens[i * bs:(i + 1) * bs]),)
+            if self.key[b] is not None and self.key[b] != k:
+                raise InvalidArg(f"block {b} holds another prefix")
+            keys.append(k)
+            parent = (b, self.gen[b])
+        for b, k in zip(table[:n_full], keys):
+            if self.key[b] is None and k not in self.cache:
+                self.cache[k] = b
+                self.key[b] = k
+
+    def cached_blocks(self):
+        return len(self.cache)
 
     def seq_swap(self, target, table):
         """Move a sequence's blocks to `target` (another pool, e.g. host

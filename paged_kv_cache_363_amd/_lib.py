@@ -47,6 +47,9 @@ SIGNATURES = {
     "pkv_copy_blocks": (I32, [P, P, P, I32, I32, I64, P]),
     "pkv_swap_blocks": (I32, [P, P, I32, P, P, I32, P, I32, I64, P]),
     "pkv_seq_swap": (I32, [P, P, P, I32, P, P]),
+    "pkv_seq_create_cached": (I32, [P, P, I32, P, I32, P, P]),
+    "pkv_pool_register_blocks": (I32, [P, P, I32, P, I32]),
+    "pkv_pool_cached_blocks": (I32, [P]),
     "pkv_pool_create": (I32, [I32, I32, P, ctypes.POINTER(P)]),
     "pkv_pool_destroy": (None, [P]),
     "pkv_pool_alloc": (I32, [P, P]),

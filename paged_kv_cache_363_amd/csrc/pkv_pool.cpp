@@ -1,18 +1,31 @@
 // Host block pool: physical block ids, reference counts and a FIFO free queue.
 //
 // Follows "vLLM推理引擎深度解析" section 2.2 (a pool of physical blocks, a table
-// per request, a queue of free blocks, a new block every 16 generated tokens)
-// and "大语言模型推理引擎深度剖析" sections 2.2-2.3 (O(1) allocation and
-// release; tables may share blocks; counts are kept and a block goes back to
-// the free pool at zero; a shared block is copied before it is written).
+// per request, a queue of free blocks ordered by LRU, a new block every 16
+// generated tokens) and "大语言模型推理引擎深度剖析" sections 2.2-2.3 (O(1)
+// allocation and release; tables may share blocks; counts are kept and a
+// block goes back to the free pool at zero; a shared block is copied before
+// it is written).
 //
-// The free queue is a ring buffer over the block ids, so alloc (pop head) and
-// release (push tail) are O(1).  Every operation that can fail checks first
-// and mutates only when it is sure to succeed.
+// The free queue is an intrusive doubly linked list over the block ids:
+// alloc (pop head), release (push tail) and taking a cached block back out of
+// the queue are all O(1).  Every operation that can fail checks first and
+// mutates only when it is sure to succeed.
+//
+// Prefix caching ("vLLM推理引擎深度解析" section 4.1; "KV Cache 与
+// PageAttention深度实战" section 4.2): a full block whose K/V are computed can
+// be registered under the exact key (parent block, the parent's allocation
+// generation, its token ids).  A freed block keeps its key at the tail of the
+// free queue until allocation reaches it at the head (least recently freed
+// first) and evicts it; each hand-out advances the block's generation, so a
+// chain whose parent was reused never matches.  The index is a multimap from
+// a 64-bit FNV-1a hash of the key to blocks; every candidate is compared
+// against the full stored key, so a hash collision cannot produce a hit.
 #include <cstdint>
 #include <climits>
 #include <cstring>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "pkv.h"
@@ -21,32 +34,95 @@
 struct pkv_pool {
   int32_t num_blocks;
   int32_t block_size;
-  std::vector<int32_t> ref;   // 0 = free
-  std::vector<int32_t> ring;  // free queue storage, capacity num_blocks
-  int32_t head = 0;           // index of the queue head in ring
-  int32_t count = 0;          // queue length
+  std::vector<int32_t> ref;    // 0 = free
+  std::vector<int32_t> prev;   // free queue links (-1 = none)
+  std::vector<int32_t> next;
+  std::vector<uint8_t> queued;  // 1 while the block is in the free queue
+  int32_t head = -1, tail = -1;
+  int32_t count = 0;            // queue length
   // batch bookkeeping: per-block writer counts (all zero between calls) and
   // the ids with a nonzero count
   std::vector<int32_t> touch;
   std::vector<int32_t> touched;
+  // prefix cache
+  std::vector<uint32_t> gen;          // times each block was handed out
+  std::vector<uint8_t> keyed;         // 1 = registered under key_*
+  std::vector<int32_t> key_parent;
+  std::vector<uint32_t> key_gen;
+  std::vector<uint64_t> key_hash;
+  std::vector<int32_t> key_tokens;    // [num_blocks][block_size], allocated on first use
+  std::unordered_multimap<uint64_t, int32_t> index;
 
-  int32_t pop() {
-    int32_t b = ring[head];
-    head = (head + 1 == num_blocks) ? 0 : head + 1;
+  void unlink(int32_t b) {
+    const int32_t p = prev[b], n = next[b];
+    if (p >= 0) next[p] = n; else head = n;
+    if (n >= 0) prev[n] = p; else tail = p;
+    prev[b] = next[b] = -1;
+    queued[b] = 0;
     --count;
-    ref[b] = 1;
-    return b;
   }
   void push(int32_t b) {
-    int32_t tail = head + count;
-    if (tail >= num_blocks) tail -= num_blocks;
-    ring[tail] = b;
+    prev[b] = tail;
+    next[b] = -1;
+    if (tail >= 0) next[tail] = b; else head = b;
+    tail = b;
+    queued[b] = 1;
     ++count;
+  }
+  void evict(int32_t b) {
+    if (!keyed[b]) return;
+    auto range = index.equal_range(key_hash[b]);
+    for (auto it = range.first; it != range.second; ++it)
+      if (it->second == b) {
+        index.erase(it);
+        break;
+      }
+    keyed[b] = 0;
+  }
+  int32_t pop() {
+    const int32_t b = head;
+    unlink(b);
+    evict(b);
+    ++gen[b];
+    ref[b] = 1;
+    return b;
   }
   bool valid(int32_t b) const { return b >= 0 && b < num_blocks; }
 };
 
 namespace {
+
+// FNV-1a, 64-bit (Fowler, Noll, Vo): xor each byte in, multiply by the prime.
+uint64_t fnv1a(uint64_t h, const void* data, size_t n) {
+  const uint8_t* p = static_cast<const uint8_t*>(data);
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= 1099511628211ull;
+  }
+  return h;
+}
+
+uint64_t key_hash(int32_t parent, uint32_t pgen, const int32_t* tokens, int32_t bs) {
+  uint64_t h = 14695981039346656037ull;
+  h = fnv1a(h, &parent, sizeof parent);
+  h = fnv1a(h, &pgen, sizeof pgen);
+  return fnv1a(h, tokens, sizeof(int32_t) * (size_t)bs);
+}
+
+// The block registered under (parent, pgen, tokens), or -1.
+int32_t find_cached(const pkv_pool* p, int32_t parent, uint32_t pgen, const int32_t* tokens,
+                    uint64_t h) {
+  if (p->key_tokens.empty()) return -1;
+  const int32_t bs = p->block_size;
+  auto range = p->index.equal_range(h);
+  for (auto it = range.first; it != range.second; ++it) {
+    const int32_t b = it->second;
+    if (p->key_parent[b] == parent && p->key_gen[b] == pgen &&
+        std::memcmp(&p->key_tokens[(size_t)b * bs], tokens, sizeof(int32_t) * (size_t)bs) == 0)
+      return b;
+  }
+  return -1;
+}
 
 // Validation half of an append of n_new positions at cur_len to the table
 // table[0..nb): no gap after the table, room in the table, every block it
@@ -120,7 +196,14 @@ pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t
   p->block_size = block_size;
   p->ref.assign(num_blocks, 0);
   p->touch.assign(num_blocks, 0);
-  p->ring.resize(num_blocks);
+  p->prev.assign(num_blocks, -1);
+  p->next.assign(num_blocks, -1);
+  p->queued.assign(num_blocks, 0);
+  p->gen.assign(num_blocks, 0);
+  p->keyed.assign(num_blocks, 0);
+  p->key_parent.assign(num_blocks, -1);
+  p->key_gen.assign(num_blocks, 0);
+  p->key_hash.assign(num_blocks, 0);
   if (free_order) {
     std::vector<char> seen(num_blocks, 0);
     for (int32_t i = 0; i < num_blocks; ++i) {
@@ -130,12 +213,11 @@ pkv_status pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t
         return pkv::fail(PKV_ERR_INVALID_ARG, "pool_create: free_order is not a permutation");
       }
       seen[b] = 1;
-      p->ring[i] = b;
     }
+    for (int32_t i = 0; i < num_blocks; ++i) p->push(free_order[i]);
   } else {
-    for (int32_t i = 0; i < num_blocks; ++i) p->ring[i] = i;
+    for (int32_t i = 0; i < num_blocks; ++i) p->push(i);
   }
-  p->count = num_blocks;
   *out = p;
   return PKV_OK;
 }
@@ -179,11 +261,8 @@ pkv_status pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, i
   *n = pool->count;
   if (cap < pool->count || (pool->count > 0 && !out))
     return pkv::fail(PKV_ERR_INVALID_ARG, "pool_free_list: cap too small");
-  for (int32_t i = 0; i < pool->count; ++i) {
-    int32_t j = pool->head + i;
-    if (j >= pool->num_blocks) j -= pool->num_blocks;
-    out[i] = pool->ring[j];
-  }
+  int32_t i = 0;
+  for (int32_t b = pool->head; b >= 0; b = pool->next[b]) out[i++] = b;
   return PKV_OK;
 }
 
@@ -304,6 +383,100 @@ pkv_status pkv_seq_fork(pkv_pool* pool, const int32_t* table, int32_t nblocks) {
   }
   for (int32_t i = 0; i < nblocks; ++i) ++pool->ref[table[i]];
   return PKV_OK;
+}
+
+pkv_status pkv_seq_create_cached(pkv_pool* pool, const int32_t* tokens, int32_t prompt_len,
+                                int32_t* table, int32_t cap, int32_t* nblocks,
+                                int32_t* cached_tokens) {
+  if (!pool || !nblocks || !cached_tokens || prompt_len < 0 || cap < 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "seq_create_cached: bad argument");
+  *nblocks = 0;
+  *cached_tokens = 0;
+  if (prompt_len == 0) return PKV_OK;
+  if (!tokens || !table) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_create_cached: NULL");
+  const int32_t bs = pool->block_size;
+  const int32_t need = (int32_t)(((int64_t)prompt_len + bs - 1) / bs);
+  if (need > cap) return pkv::fail(PKV_ERR_INVALID_ARG, "seq_create_cached: table capacity");
+  // walk the cache along the prompt's full blocks; stop at the first miss
+  std::vector<int32_t> hits;
+  int32_t parent = -1;
+  uint32_t pgen = 0;
+  for (int32_t i = 0; i < prompt_len / bs; ++i) {
+    const int32_t* tk = tokens + (int64_t)i * bs;
+    const int32_t b = find_cached(pool, parent, pgen, tk, key_hash(parent, pgen, tk, bs));
+    if (b < 0) break;
+    hits.push_back(b);
+    parent = b;
+    pgen = pool->gen[b];
+  }
+  int64_t revived = 0;
+  for (int32_t b : hits) revived += pool->ref[b] == 0;
+  if ((int64_t)need - (int64_t)hits.size() > (int64_t)pool->count - revived)
+    return pkv::fail(PKV_ERR_OUT_OF_BLOCKS, "seq_create_cached: not enough free blocks");
+  int32_t i = 0;
+  for (int32_t b : hits) {
+    if (pool->ref[b] == 0) pool->unlink(b);
+    ++pool->ref[b];
+    table[i++] = b;
+  }
+  for (; i < need; ++i) table[i] = pool->pop();
+  *nblocks = need;
+  *cached_tokens = (int32_t)hits.size() * bs;
+  return PKV_OK;
+}
+
+pkv_status pkv_pool_register_blocks(pkv_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                                    const int32_t* table, int32_t nblocks) {
+  if (!pool || num_tokens < 0 || nblocks < 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "register_blocks: bad argument");
+  const int32_t bs = pool->block_size;
+  const int32_t n_full = num_tokens / bs;
+  if (n_full == 0) return PKV_OK;
+  if (!tokens || !table || n_full > nblocks)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "register_blocks: table or tokens too short");
+  for (int32_t i = 0; i < n_full; ++i) {
+    if (!pool->valid(table[i])) return pkv::fail(PKV_ERR_INVALID_ARG, "register_blocks: bad id");
+    if (pool->ref[table[i]] < 1)
+      return pkv::fail(PKV_ERR_REFCOUNT, "register_blocks: block is free");
+  }
+  // pass 1: every block either unregistered or already under this very key
+  std::vector<uint64_t> hs(n_full);
+  int32_t parent = -1;
+  uint32_t pgen = 0;
+  for (int32_t i = 0; i < n_full; ++i) {
+    const int32_t b = table[i];
+    const int32_t* tk = tokens + (int64_t)i * bs;
+    hs[i] = key_hash(parent, pgen, tk, bs);
+    if (pool->keyed[b] &&
+        (pool->key_parent[b] != parent || pool->key_gen[b] != pgen ||
+         std::memcmp(&pool->key_tokens[(size_t)b * bs], tk, sizeof(int32_t) * (size_t)bs) != 0))
+      return pkv::fail(PKV_ERR_INVALID_ARG, "register_blocks: block %d holds another prefix", b);
+    parent = b;
+    pgen = pool->gen[b];
+  }
+  if (pool->key_tokens.empty()) pool->key_tokens.assign((size_t)pool->num_blocks * bs, 0);
+  // pass 2: register the new ones whose key no other block holds
+  parent = -1;
+  pgen = 0;
+  for (int32_t i = 0; i < n_full; ++i) {
+    const int32_t b = table[i];
+    const int32_t* tk = tokens + (int64_t)i * bs;
+    if (!pool->keyed[b] && find_cached(pool, parent, pgen, tk, hs[i]) < 0) {
+      pool->keyed[b] = 1;
+      pool->key_parent[b] = parent;
+      pool->key_gen[b] = pgen;
+      pool->key_hash[b] = hs[i];
+      std::memcpy(&pool->key_tokens[(size_t)b * bs], tk, sizeof(int32_t) * (size_t)bs);
+      pool->index.emplace(hs[i], b);
+    }
+    parent = b;
+    pgen = pool->gen[b];
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_pool_cached_blocks(const pkv_pool* pool) {
+  return pool ? (int32_t)pool->index.size() : -1;
 }
 
 pkv_status pkv_seq_swap(pkv_pool* from, pkv_pool* to, const int32_t* table, int32_t nblocks,

@@ -135,6 +135,30 @@ class BlockPool:
             cow_cap, ctypes.byref(ncow), ctypes.byref(nslots)))
         return slot_mapping[:nslots.value], cows[:2 * ncow.value].reshape(-1, 2)
 
+    # -- prefix caching --------------------------------------------------------
+    def seq_create_cached(self, tokens, prompt_len, cap=None):
+        """(table, cached_tokens) for a prompt of token ids, reusing its
+        longest run of cached full blocks (pkv_seq_create_cached)."""
+        tk = np.ascontiguousarray(tokens, dtype=np.int32)
+        if tk.shape[0] < prompt_len:
+            raise ValueError("fewer tokens than prompt_len")
+        cap = cap if cap is not None else -(-prompt_len // self.block_size)
+        arr = np.empty(max(cap, 1), np.int32)
+        n, cached = ctypes.c_int32(), ctypes.c_int32()
+        check(lib().pkv_seq_create_cached(self._h, _ptr(tk), prompt_len, _ptr(arr), cap,
+                                          ctypes.byref(n), ctypes.byref(cached)))
+        return arr[:n.value].tolist(), cached.value
+
+    def register_blocks(self, tokens, num_tokens, table):
+        tk = np.ascontiguousarray(tokens, dtype=np.int32)
+        if tk.shape[0] < num_tokens:
+            raise ValueError("fewer tokens than num_tokens")
+        arr = np.ascontiguousarray(table, dtype=np.int32)
+        check(lib().pkv_pool_register_blocks(self._h, _ptr(tk), num_tokens, _ptr(arr), len(table)))
+
+    def cached_blocks(self):
+        return int(lib().pkv_pool_cached_blocks(self._h))
+
     def seq_swap(self, target, table):
         """Move a sequence's blocks to pool `target` (pkv_seq_swap): returns
         (new table, [(old, new), ...]) and releases `table` here."""

@@ -349,3 +349,86 @@ def test_swap_random_operations_match_reference():
             (rd if on_dev else rh).seq_free(tr)
         same(nd, rd)
         same(nh, rh)
+
+
+# -- prefix caching (pkv_seq_create_cached / pkv_pool_register_blocks) -------
+
+def _same_cache(n, r):
+    same(n, r)
+    assert n.cached_blocks() == r.cached_blocks()
+
+
+def test_prefix_cache_random_operations_match_reference():
+    rs = np.random.default_rng(5)
+    system = [[int(x) for x in rs.integers(0, 50, k)] for k in (16, 40, 64, 33)]
+    order = rs.permutation(48)
+    n, r = pkv.BlockPool(48, 16, order), RefPool(48, 16, order)
+    live = []          # [native table, ref table, tokens, length]
+    hits = 0
+    for step in range(3000):
+        op = int(rs.integers(0, 6))
+        if op <= 1 or not live:
+            base = system[int(rs.integers(len(system)))]
+            tail = [int(x) for x in rs.integers(0, 50, int(rs.integers(0, 40)))]
+            toks = base + tail
+            L = len(toks)
+            try:
+                tr, cr = r.seq_create_cached(toks, L)
+            except RefOOB:
+                with pytest.raises(pkv.OutOfBlocks):
+                    n.seq_create_cached(toks, L)
+                _same_cache(n, r)
+                continue
+            tn, cn = n.seq_create_cached(toks, L)
+            assert (tn, cn) == (tr, cr)
+            hits += cn > 0
+            live.append([tn, list(tr), toks, L])
+        elif op == 2:                       # the prompt's K/V are computed: register
+            i = int(rs.integers(len(live)))
+            tn, tr, toks, L = live[i]
+            n.register_blocks(toks, L, tn)
+            r.register_blocks(toks, L, tr)
+        elif op == 3:                       # a decode step
+            i = int(rs.integers(len(live)))
+            tn, tr, toks, L = live[i]
+            try:
+                out_r = r.seq_append_slots(tr, L, 1)
+            except RefOOB:
+                with pytest.raises(pkv.OutOfBlocks):
+                    n.seq_append_slots(tn, L, 1)
+                _same_cache(n, r)
+                continue
+            assert n.seq_append_slots(tn, L, 1) == (out_r[0], out_r[1])
+            toks.append(int(rs.integers(0, 50)))
+            live[i][3] = L + 1
+        elif op == 4 and live:
+            i = int(rs.integers(len(live)))
+            tn, tr, toks, L = live[i]
+            live.append([n.seq_fork(tn), r.seq_fork(tr), list(toks), L])
+        else:
+            i = int(rs.integers(len(live)))
+            tn, tr, _, _ = live.pop(i)
+            n.seq_free(tn)
+            r.seq_free(tr)
+        _same_cache(n, r)
+    assert hits > 50
+
+
+def test_prefix_cache_pins_on_the_native_pool():
+    rs = np.random.default_rng(3)
+    p = pkv.BlockPool(4, 16)
+    t = [int(x) for x in rs.integers(0, 1000, 32)]
+    a, _ = p.seq_create_cached(t, 32)
+    p.register_blocks(t, 32, a)
+    p.decref(a[0])                          # the parent alone goes back
+    fresh = [p.alloc(), p.alloc()]
+    y = p.alloc()                           # a[0]: evicted, generation moves on
+    assert y == a[0] and p.cached_blocks() == 1
+    other = [int(x) for x in rs.integers(0, 1000, 16)]
+    p.register_blocks(other, 16, [y])
+    for x in fresh:
+        p.decref(x)
+    table, cached = p.seq_create_cached(other + t[16:32], 32)
+    assert cached == 16 and table[0] == y and table[1] != a[1]
+    with pytest.raises(pkv.InvalidArg):
+        p.register_blocks(t, 32, table)     # y holds another prefix now

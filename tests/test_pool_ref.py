@@ -154,3 +154,88 @@ def test_random_operations_keep_invariants():
         except OutOfBlocks:
             pass
         check_invariants(pool, [s[0] for s in seqs])
+
+
+# -- prefix caching ----------------------------------------------------------
+
+def _prompt(rs, n, vocab=1000):
+    return [int(x) for x in rs.integers(0, vocab, n)]
+
+
+def test_same_prefix_reuses_computed_blocks():
+    # a request that shares the first 40 tokens of another reuses its two full
+    # blocks ("KV Cache 与 PageAttention深度实战" 4.2); the partial block is new
+    rs = np.random.default_rng(1)
+    p = RefPool(16, 16)
+    a_tok = _prompt(rs, 50)
+    a, cached = p.seq_create_cached(a_tok, 50)
+    assert cached == 0 and len(a) == 4
+    p.register_blocks(a_tok, 50, a)            # 3 full blocks become findable
+    assert p.cached_blocks() == 3
+    b_tok = a_tok[:40] + _prompt(rs, 5)
+    b, cached = p.seq_create_cached(b_tok, 45)
+    assert cached == 32 and b[:2] == a[:2] and b[2] not in a
+    assert [p.refcount(x) for x in a[:2]] == [2, 2] and p.refcount(a[2]) == 1
+
+
+def test_freed_blocks_stay_cached_until_evicted_lru():
+    rs = np.random.default_rng(2)
+    p = RefPool(8, 16)
+    t1 = _prompt(rs, 32)
+    t2 = _prompt(rs, 32)
+    a, _ = p.seq_create_cached(t1, 32)          # [0, 1]
+    p.register_blocks(t1, 32, a)
+    b, _ = p.seq_create_cached(t2, 32)          # [2, 3]
+    p.register_blocks(t2, 32, b)
+    p.seq_free(a)                               # freed last block first
+    p.seq_free(b)
+    assert p.cached_blocks() == 4
+    assert p.free_list() == [4, 5, 6, 7, 1, 0, 3, 2]
+    # a hit on a free block takes it out of the queue (count 1 again)
+    c, cached = p.seq_create_cached(t2, 32)
+    assert cached == 32 and c == b and p.num_free() == 6
+    p.seq_free(c)
+    # handing out 6 blocks evicts a's blocks (least recently freed) and keeps b's
+    fresh = [p.alloc() for _ in range(6)]
+    assert fresh == [4, 5, 6, 7, 1, 0] and p.cached_blocks() == 2
+    for x in fresh:
+        p.decref(x)                             # queue: [3, 2, 4, 5, 6, 7, 1, 0]
+    _, cached = p.seq_create_cached(t2, 32)     # b's blocks are still cached
+    assert cached == 32
+    _, cached = p.seq_create_cached(t1, 32)     # a's were evicted
+    assert cached == 0
+
+
+def test_a_reused_parent_never_matches_its_old_children():
+    rs = np.random.default_rng(3)
+    p = RefPool(4, 16)
+    t = _prompt(rs, 32)
+    a, _ = p.seq_create_cached(t, 32)           # [0, 1]
+    p.register_blocks(t, 32, a)
+    p.decref(a[0])                              # the parent alone goes back
+    fresh = [p.alloc(), p.alloc()]              # 2, 3
+    y = p.alloc()                               # 0: evicted and handed out again
+    assert y == a[0] and p.cached_blocks() == 1  # the child's key is still there
+    other = _prompt(rs, 16)
+    p.register_blocks(other, 16, [y])
+    for x in fresh:
+        p.decref(x)
+    # other + t's second block: the child was registered under y's old
+    # generation, so only the first block matches
+    table, cached = p.seq_create_cached(other + t[16:32], 32)
+    assert cached == 16 and table[0] == y and table[1] != a[1]
+
+
+def test_partial_blocks_are_never_cached_and_errors_change_nothing():
+    rs = np.random.default_rng(4)
+    p = RefPool(4, 16)
+    t = _prompt(rs, 40)
+    a, _ = p.seq_create_cached(t, 40)
+    p.register_blocks(t, 40, a)
+    assert p.cached_blocks() == 2              # the 8-token block is not
+    before = (p.free_list(), list(p.ref), dict(p.cache))
+    with pytest.raises(OutOfBlocks):
+        p.seq_create_cached(t[:32] + _prompt(rs, 40), 72)
+    with pytest.raises(InvalidArg):
+        p.register_blocks(_prompt(rs, 32), 32, a)   # a holds another prefix
+    assert (p.free_list(), list(p.ref), dict(p.cache)) == before
