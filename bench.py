@@ -434,6 +434,46 @@ def time_swap(cfg, args, dev):
     return res
 
 
+def time_prefix_cache(cfg):
+    """Host cost of prefix-cached table creation on a shared-prefix workload:
+    the first request's prompt blocks are registered, then every request
+    (prefix + its own tail) is created through the cache and released, over
+    several rounds.  Reports the tokens served from the cache and the host
+    microseconds per request."""
+    import numpy as np
+    import paged_kv_cache_363_amd as pkv
+    from synth import gen
+    ctx = gen.context_lens(cfg)
+    P = cfg.shared_prefix
+    rs = np.random.default_rng(cfg.seed)
+    prefix = [int(x) for x in rs.integers(0, 32000, P)]
+    prompts = [prefix + [int(x) for x in rs.integers(0, 32000, int(ctx[s]) - 1 - P)]
+               for s in range(cfg.num_seqs)]
+    nb = gen.num_blocks(cfg, ctx)
+    pool = pkv.BlockPool(nb, cfg.block_size, gen.free_order(cfg, nb))
+    toks = [np.asarray(t, np.int32) for t in prompts]
+    first, _ = pool.seq_create_cached(toks[0], len(prompts[0]), cfg.max_blocks_per_seq)
+    pool.register_blocks(toks[0], len(prompts[0]), first)
+    pool.seq_free(first)
+    rounds, hit_tokens, total_tokens = 5, 0, 0
+    t0 = time.perf_counter()
+    for _ in range(rounds):
+        tables = []
+        for t in toks:
+            tab, c = pool.seq_create_cached(t, len(t), cfg.max_blocks_per_seq)
+            hit_tokens += c
+            total_tokens += len(t)
+            tables.append(tab)
+        for tab in tables:
+            pool.seq_free(tab)
+    dt = time.perf_counter() - t0
+    n = rounds * len(toks)
+    return {"workload": cfg.name, "requests": n, "shared_prefix_tokens": P,
+            "cached_token_fraction": round(hit_tokens / total_tokens, 4),
+            "host_us_per_request": round(dt / n * 1e6, 2),
+            "cached_blocks": pool.cached_blocks()}
+
+
 def cpu_baseline(cfg, st, budget_s, gpu_out):
     """The fp64 oracle, single-threaded, on a bounded sample of the same
     workload's sequences (longest context first, until the time budget is
@@ -560,6 +600,8 @@ def main():
         line["other_configs"] = others
     if args.all_configs or args.swap:
         line["swap"] = time_swap(cfg, args, dev)
+    if args.all_configs:
+        line["prefix_cache"] = time_prefix_cache(CONFIGS["c5_long_shared_bf16"])
     if args.all_configs or args.multiquery:
         from synth import MQ_CONFIGS
         line["multiquery"] = {name: time_multiquery(m, args, dev) for name, m in MQ_CONFIGS.items()}
