@@ -60,10 +60,10 @@ def log(msg):
 
 
 def kv_elem_bytes(kv):
-    return {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[kv]
+    return {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}[kv]
 
 
-DT_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
+DT_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3, "int8": 4}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -124,7 +124,7 @@ def setup(cfg, dev):
     t0 = time.perf_counter()
     st = build_state(cfg, pool, ctx)
     t_pool = time.perf_counter() - t0
-    kv_t = torch.uint8 if cfg.kv_dtype == "fp8" else gen.TORCH_DTYPE[cfg.kv_dtype]
+    kv_t = {"fp8": torch.uint8, "int8": torch.int8}.get(cfg.kv_dtype) or gen.TORCH_DTYPE[cfg.kv_dtype]
     shape = (nb, cfg.num_kv_heads, cfg.block_size, cfg.head_dim)
     kc = torch.zeros(shape, dtype=kv_t, device=dev)
     vc = torch.zeros(shape, dtype=kv_t, device=dev)

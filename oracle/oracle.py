@@ -5,7 +5,8 @@ CPU-baseline leg of bench.py, never by the product package.  It shares no
 code with the HIP path.
 
 Arrays are numpy arrays holding raw element bits:
-  'f32' -> float32, 'f16' / 'bf16' -> uint16, 'fp8' -> uint8 (OCP E4M3FN).
+  'f32' -> float32, 'f16' / 'bf16' -> uint16, 'fp8' -> uint8 (OCP E4M3FN),
+  'int8' -> int8 (symmetric codes, value = code * scale).
 Cache arrays use the layout [num_blocks][num_kv_heads][block_size][head_dim].
 """
 import ctypes
@@ -18,9 +19,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pkv_oracle.c")
 _SO = os.path.join(_HERE, "liboracle.so")
 
-DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3}
-BITS_NP = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3, "int8": 4}
+BITS_NP = {"f32": np.float32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8,
+           "int8": np.int8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1, "int8": 1}
 
 _lib = None
 
@@ -57,6 +59,8 @@ def _load():
     lib.orc_cache_append.restype = I
     lib.orc_e4m3_encode_array.argtypes = [P, I64, P]
     lib.orc_e4m3_encode_array.restype = None
+    lib.orc_int8_encode_array.argtypes = [P, I64, P]
+    lib.orc_int8_encode_array.restype = None
     lib.orc_bits_to_f64.argtypes = [P, I, I64, P]
     lib.orc_bits_to_f64.restype = None
     lib.orc_kv_bytes_per_token.argtypes = [I, I, I, I]
@@ -90,6 +94,15 @@ def e4m3_encode(x):
     out = np.empty(x.shape, dtype=np.uint8)
     _load().orc_e4m3_encode_array(_ptr(x), x.size, _ptr(out))
     return out
+
+
+def int8_encode(x):
+    """INT8 codes (as int8) of float32 values: nearest integer, ties to even,
+    saturated to +-127, NaN -> 0."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _load().orc_int8_encode_array(_ptr(x), x.size, _ptr(out))
+    return out.view(np.int8)
 
 
 def kv_bytes_per_token(layers, kv_heads, head_dim, dtype):

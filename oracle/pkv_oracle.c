@@ -24,6 +24,11 @@
  *    the pages name GQA for Qwen3-8B and Llama-3-70B without the mapping).
  *  - FP8 E4M3 KV (range +-448, "大语言模型推理引擎深度剖析", section 4.2): OCP
  *    E4M3FN, per-tensor scale, real value = decode(code) * scale.
+ *  - INT8 KV ("推理加速三板斧", section 2.3, which lists INT8 KV caches
+ *    next to FP8 without the encoding; reading: symmetric, one scale per
+ *    tensor like FP8): code = the integer nearest to the binary32 product
+ *    x * (1/scale), ties to even, saturated to +-127, NaN -> 0; real value =
+ *    code * scale.
  *  - Cache append: only the new token's K and V are written ("Transformer 推理
  *    优化", section 2.2), at slot = physical_block*bs + offset.
  *  - Several queries per sequence in one pass: a chunk of a long prompt
@@ -45,7 +50,10 @@
 #include <string.h>
 #include <stdlib.h>
 
-enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_FP8_E4M3 = 3 };
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2, ORC_FP8_E4M3 = 3, ORC_INT8 = 4 };
+
+/* Caches whose codes carry a per-tensor scale. */
+static int scaled_dtype(int dt) { return dt == ORC_FP8_E4M3 || dt == ORC_INT8; }
 
 /* ---------------------------------------------------------------- decoders */
 
@@ -112,12 +120,23 @@ uint8_t orc_e4m3_encode(float x) {
   return (uint8_t)(best | (neg ? 0x80 : 0));
 }
 
+/* INT8 code of a binary32 value: nearest integer, ties to even (the default
+ * rounding of nearbyint), saturated to +-127; NaN -> 0. */
+uint8_t orc_int8_encode(float x) {
+  if (isnan(x)) return 0;
+  double r = nearbyint((double)x);
+  if (r > 127.0) r = 127.0;
+  if (r < -127.0) r = -127.0;
+  return (uint8_t)(int8_t)r;
+}
+
 static double load_elem(const void* base, int64_t idx, int dtype) {
   switch (dtype) {
     case ORC_F32: return orc_f32_bits_to_f64(((const uint32_t*)base)[idx]);
     case ORC_F16: return orc_f16_to_f64(((const uint16_t*)base)[idx]);
     case ORC_BF16: return orc_bf16_to_f64(((const uint16_t*)base)[idx]);
     case ORC_FP8_E4M3: return orc_e4m3_to_f64(((const uint8_t*)base)[idx]);
+    case ORC_INT8: return (double)((const int8_t*)base)[idx];
   }
   return NAN;
 }
@@ -135,6 +154,10 @@ void orc_e4m3_encode_array(const float* x, int64_t n, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(x[i]);
 }
 
+void orc_int8_encode_array(const float* x, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_int8_encode(x[i]);
+}
+
 /* --------------------------------------------------------------- KV bytes */
 
 /* Per-token KV bytes over the whole model: 2 (K and V) x layers x kv_heads x
@@ -148,7 +171,7 @@ uint64_t orc_kv_bytes_per_token(int layers, int kv_heads, int head_dim,
 /* ------------------------------------------------------------ cache append */
 
 static int elem_bytes(int dtype) {
-  return dtype == ORC_F32 ? 4 : (dtype == ORC_FP8_E4M3 ? 1 : 2);
+  return dtype == ORC_F32 ? 4 : (dtype == ORC_FP8_E4M3 || dtype == ORC_INT8 ? 1 : 2);
 }
 
 /* Write the new tokens' K and V rows into the paged caches.
@@ -174,11 +197,12 @@ int orc_cache_append(void* k_cache, void* v_cache, const void* k_new,
         for (int which = 0; which < 2; ++which) {
           const void* nb = which ? v_new : k_new;
           void* cb = which ? v_cache : k_cache;
-          if (kv_dtype == ORC_FP8_E4M3) {
+          if (scaled_dtype(kv_dtype)) {
             float scale = which ? v_scale : k_scale;
             float inv = 1.0f / scale;
             float y = load_as_f32(nb, src, new_dtype) * inv;
-            ((uint8_t*)cb)[dst] = orc_e4m3_encode(y);
+            ((uint8_t*)cb)[dst] =
+                kv_dtype == ORC_FP8_E4M3 ? orc_e4m3_encode(y) : orc_int8_encode(y);
           } else {
             if (eb_new != eb_kv) return -2;
             memcpy((char*)cb + dst * eb_kv, (const char*)nb + src * eb_new, eb_kv);
@@ -254,8 +278,8 @@ int orc_paged_decode(double* out, const void* q, int q_dtype, const void* k_cach
   orc_args a = {q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
                 context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                 block_size, max_blocks_per_seq, scale,
-                kv_dtype == ORC_FP8_E4M3 ? k_scale : 1.0,
-                kv_dtype == ORC_FP8_E4M3 ? v_scale : 1.0};
+                scaled_dtype(kv_dtype) ? k_scale : 1.0,
+                scaled_dtype(kv_dtype) ? v_scale : 1.0};
   int g = num_q_heads / num_kv_heads;
   int max_ctx = max_blocks_per_seq * block_size;
   double* w = (double*)malloc(sizeof(double) * (max_ctx > 0 ? max_ctx : 1));
@@ -295,8 +319,8 @@ int orc_paged_multiquery(double* out, const void* q, int q_dtype, const void* k_
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
   const int g = num_q_heads / num_kv_heads;
   const int max_ctx = max_blocks_per_seq * block_size;
-  const double ks = kv_dtype == ORC_FP8_E4M3 ? k_scale : 1.0;
-  const double vs = kv_dtype == ORC_FP8_E4M3 ? v_scale : 1.0;
+  const double ks = scaled_dtype(kv_dtype) ? k_scale : 1.0;
+  const double vs = scaled_dtype(kv_dtype) ? v_scale : 1.0;
   /* the kv-side lookups of cache_elem only need the cache fields */
   orc_args a = {q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
                 num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -351,7 +375,7 @@ int orc_softmax_weights(double* w, int s, int hq, const void* q, int q_dtype,
   orc_args a = {q, q_dtype, k_cache, NULL, kv_dtype, block_tables,
                 context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                 block_size, max_blocks_per_seq, scale,
-                kv_dtype == ORC_FP8_E4M3 ? k_scale : 1.0, 1.0};
+                scaled_dtype(kv_dtype) ? k_scale : 1.0, 1.0};
   int n = context_lens[s];
   if (n <= 0) return 0;
   double m, l;
@@ -374,8 +398,8 @@ int orc_partition_stats(double* m_out, double* l_out, double* acc, int s, int hq
   orc_args a = {q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
                 context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                 block_size, max_blocks_per_seq, scale,
-                kv_dtype == ORC_FP8_E4M3 ? k_scale : 1.0,
-                kv_dtype == ORC_FP8_E4M3 ? v_scale : 1.0};
+                scaled_dtype(kv_dtype) ? k_scale : 1.0,
+                scaled_dtype(kv_dtype) ? v_scale : 1.0};
   int g = num_q_heads / num_kv_heads;
   for (int i = 0; i < head_dim; ++i) acc[i] = 0.0;
   if (t1 <= t0) { *m_out = -INFINITY; *l_out = 0.0; return 0; }

@@ -1,4 +1,4 @@
-"""The five decode workloads: shapes, dtypes, context-length mixes and seeds.
+"""The decode workloads: shapes, dtypes, context-length mixes and seeds.
 
 Shapes follow the models the pages use as examples (Qwen3-8B: 32 q-heads /
 8 KV heads / head_dim 128; Llama-2-7B: 32 / 32 / 128; Llama-3-70B: 64 / 8 /
@@ -18,7 +18,7 @@ class Config:
     num_kv_heads: int
     head_dim: int
     q_dtype: str            # 'f32' | 'f16' | 'bf16' (also the output dtype)
-    kv_dtype: str           # 'f32' | 'f16' | 'bf16' | 'fp8'
+    kv_dtype: str           # 'f32' | 'f16' | 'bf16' | 'fp8' | 'int8'
     ctx_kind: str           # 'list' | 'uniform' | 'lognormal' | 'fixed'
     ctx_params: tuple
     seed: int
@@ -36,8 +36,9 @@ class Config:
 
     @property
     def new_dtype(self):
-        """dtype of the K/V rows handed to cache-append (q dtype for FP8 caches)."""
-        return self.q_dtype if self.kv_dtype == "fp8" else self.kv_dtype
+        """dtype of the K/V rows handed to cache-append (q dtype for FP8 and
+        INT8 caches)."""
+        return self.q_dtype if self.kv_dtype in ("fp8", "int8") else self.kv_dtype
 
     @property
     def group(self):
@@ -65,6 +66,12 @@ CONFIGS = {
         q_dtype="bf16", kv_dtype="fp8", ctx_kind="fixed", ctx_params=(2560,),
         seed=1004, max_blocks_per_seq=160,
         description="Llama-3-70B-shaped layer, E4M3 KV (per-tensor scale), bf16 q/out, ctx 2560"),
+    "c6_llama3_70b_int8": Config(
+        name="c6_llama3_70b_int8", num_seqs=32, num_q_heads=64, num_kv_heads=8, head_dim=128,
+        q_dtype="bf16", kv_dtype="int8", ctx_kind="fixed", ctx_params=(2560,),
+        seed=1006, max_blocks_per_seq=160,
+        description="Llama-3-70B-shaped layer, INT8 KV (symmetric, per-tensor scale), bf16 q/out, "
+                    "ctx 2560"),
     "c5_long_shared_bf16": Config(
         name="c5_long_shared_bf16", num_seqs=16, num_q_heads=32, num_kv_heads=8, head_dim=128,
         q_dtype="bf16", kv_dtype="bf16", ctx_kind="fixed", ctx_params=(32768,),

@@ -120,13 +120,16 @@ def step_kv(cfg):
 
 
 E4M3_MAX = 448.0  # largest finite E4M3 magnitude
+INT8_MAX = 127.0  # largest symmetric INT8 code
 
 
 def kv_scales(cfg, ctx):
-    """Per-tensor scales for an FP8 cache: amax over all K (resp. V) values of
-    all sequences (prefill and step rows), divided by the largest E4M3 magnitude, as float32."""
-    if cfg.kv_dtype != "fp8":
+    """Per-tensor scales for an FP8 or INT8 cache: amax over all K (resp. V)
+    values of all sequences (prefill and step rows), divided by the largest
+    code magnitude (448 for E4M3, 127 for INT8), as float32."""
+    if cfg.kv_dtype not in ("fp8", "int8"):
         return 1.0, 1.0
+    top = E4M3_MAX if cfg.kv_dtype == "fp8" else INT8_MAX
     k, v = step_kv(cfg)
     ak, av = float(k.float().abs().max()), float(v.float().abs().max())
     for s in range(cfg.num_seqs):
@@ -135,7 +138,7 @@ def kv_scales(cfg, ctx):
         k, v = seq_kv(cfg, s, int(ctx[s]) - 1)
         ak = max(ak, float(k.float().abs().max()))
         av = max(av, float(v.float().abs().max()))
-    return float(np.float32(ak / E4M3_MAX)), float(np.float32(av / E4M3_MAX))
+    return float(np.float32(ak / top)), float(np.float32(av / top))
 
 
 def misc_normal(cfg, key, shape, dtype):

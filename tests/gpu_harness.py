@@ -11,13 +11,16 @@ from harness import oracle_setup
 from synth.scenario import build_state, table_array
 
 POISON = {"f32": float("nan"), "f16": float("nan"), "bf16": float("nan")}
-TORCH_KV = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.uint8}
+TORCH_KV = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.uint8,
+            "int8": torch.int8}
 
 
 def new_cache(nb, hkv, d, kv_dtype, dev):
     shape = (nb, hkv, 16, d)
     if kv_dtype == "fp8":
         return torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
+    if kv_dtype == "int8":   # no NaN code: the largest one stands in for garbage
+        return torch.full(shape, 127, dtype=torch.int8, device=dev)
     return torch.full(shape, float("nan"), dtype=TORCH_KV[kv_dtype], device=dev)
 
 
@@ -69,6 +72,7 @@ def sample_seqs(cfg):
     if S <= 8:
         return list(range(S))
     n = {"c2_qwen3_8b_bf16": 6, "c3_llama2_7b_f16": 10, "c4_llama3_70b_fp8": 3,
+         "c6_llama3_70b_int8": 3,
          "c5_long_shared_bf16": 2}.get(cfg.name, 4)
     picks = {int(np.argmin(ctx)), int(np.argmax(ctx)), 0, S - 1}
     rs = np.random.default_rng(cfg.seed + 77)

@@ -13,7 +13,7 @@ from synth.scenario import build_state, table_array  # noqa: F401
 def poison_bits(dtype):
     """NaN bit pattern used to fill never-written cache slots."""
     return {"f32": np.float32(np.nan), "f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0),
-            "fp8": np.uint8(0x7F)}[dtype]
+            "fp8": np.uint8(0x7F), "int8": np.int8(127)}[dtype]   # int8 has no NaN
 
 
 def oracle_setup(cfg, seqs=None):

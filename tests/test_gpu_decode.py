@@ -59,6 +59,8 @@ SCHEDULES = {
                           ("mfma", 2560), ("auto", "plan")],
     "c5_long_shared_bf16": [("auto", None), ("mfma", 0), ("mfma", 512), ("vector", 1024),
                             ("auto", "plan")],
+    "c6_llama3_70b_int8": [("auto", None), ("mfma", 0), ("mfma", 256), ("vector", 512),
+                           ("mfma", 2560), ("auto", "plan")],
 }
 CASES = [(n, a, ps) for n in CONFIGS for a, ps in SCHEDULES[n]]
 

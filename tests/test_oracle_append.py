@@ -74,3 +74,31 @@ def test_fp8_append_matches_torch_cast(new_dtype):
     written = np.zeros((nb, bs), bool)
     written[slots // bs, slots % bs] = True
     assert np.all(kc.transpose(0, 2, 1, 3)[~written] == CANARY["fp8"])
+
+
+@pytest.mark.parametrize("new_dtype", ["bf16", "f16", "f32"])
+def test_int8_append_is_numpy_rint_of_the_scaled_value(new_dtype):
+    rs = np.random.default_rng(32)
+    nb, hkv, bs, d = 4, 2, 16, 64
+    kc = np.full((nb, hkv, bs, d), 99, np.int8)
+    vc = kc.copy()
+    T = 20
+    kn = _rand_bits(rs, (T, hkv, d), new_dtype)
+    vn = _rand_bits(rs, (T, hkv, d), new_dtype)
+    slots = rs.permutation(nb * bs)[:T].astype(np.int64)
+    k_scale, v_scale = float(np.float32(0.021)), float(np.float32(0.5))
+    orc.cache_append(kc, vc, kn, vn, slots, new_dtype, "int8", k_scale, v_scale)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[new_dtype]
+    for new, cache, sc in ((kn, kc, k_scale), (vn, vc, v_scale)):
+        x = torch.from_numpy(new.view(np.int16) if new_dtype != "f32" else new)
+        x = x.view(tdt).float() if new_dtype != "f32" else x
+        inv = np.float32(1.0) / np.float32(sc)
+        y = x.numpy().astype(np.float32) * inv
+        ref = np.clip(np.rint(y), -127, 127).astype(np.int8)
+        if sc == k_scale:
+            assert np.any(np.abs(y) > 127)      # K: 1/0.021 ~ 47.6 saturates the tails
+        for t, sl in enumerate(slots):
+            assert np.array_equal(cache[sl // bs, :, sl % bs, :], ref[t])
+    written = np.zeros((nb, bs), bool)
+    written[slots // bs, slots % bs] = True
+    assert np.all(kc.transpose(0, 2, 1, 3)[~written] == 99)

@@ -27,7 +27,7 @@ def _bits(t):
 
 
 NAN_BITS = {"f32": np.float32(np.nan), "f16": np.uint16(0x7E00), "bf16": np.uint16(0x7FC0),
-            "fp8": np.uint8(0x7F)}
+            "fp8": np.uint8(0x7F), "int8": np.int8(127)}   # int8 has no NaN: a large code
 TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
@@ -253,6 +253,29 @@ def test_fp8_cache_with_scales_matches_library():
     ref = sdpa_ref(c["q"], [dec(a) * ksc for a in kcodes], [dec(a) * vsc for a in vcodes],
                    1 / math.sqrt(d))
     assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_int8_cache_with_scales_matches_library():
+    """INT8 codes times the per-tensor scales (different for K and V) against
+    torch's dequantisation (int8 -> float64 times scale) feeding SDPA."""
+    rs = np.random.default_rng(19)
+    hq, hkv, d = 16, 2, 128
+    ctxs = [30, 64, 1]
+    c = random_case(rs, ctxs, hq, hkv, d, "bf16")
+    kcodes = [rs.integers(-127, 128, (n, hkv, d)).astype(np.int8) for n in ctxs]
+    vcodes = [rs.integers(-127, 128, (n, hkv, d)).astype(np.int8) for n in ctxs]
+    ksc, vsc = 0.0123, 0.037
+    kc = place(c["tables"], kcodes, c["nb"], hkv, 16, d, "int8")
+    vc = place(c["tables"], vcodes, c["nb"], hkv, 16, d, "int8")
+    got = orc.paged_decode(_bits(c["q"]), "bf16", kc, vc, "int8", c["bt"], c["ctx"],
+                           1 / math.sqrt(d), ksc, vsc)
+    dec = lambda a: torch.from_numpy(a).double()
+    ref = sdpa_ref(c["q"], [dec(a) * ksc for a in kcodes], [dec(a) * vsc for a in vcodes],
+                   1 / math.sqrt(d))
+    assert np.max(np.abs(got - ref)) < 1e-12
+    # one token: the output is its value row exactly (code * v_scale)
+    assert np.array_equal(got[2], (vcodes[2][0].astype(np.float64) * vsc)[
+        np.arange(hq) // (hq // hkv)])
 
 
 def test_block_size_is_a_parameter():

@@ -104,3 +104,23 @@ def test_16bit_decode_all_patterns_match_torch(dtype, tdt):
 def test_f32_decode_is_identity():
     x = np.random.default_rng(3).standard_normal(1000).astype(np.float32)
     assert np.array_equal(orc.to_f64(x, "f32"), x.astype(np.float64))
+
+
+# -- INT8 codes (symmetric, one scale per tensor) -----------------------------
+
+def test_int8_encode_matches_numpy_rint_and_clip():
+    """Nearest integer with ties to even (numpy's rint), saturated to +-127,
+    on a dense grid, every half-integer tie in range and beyond the range."""
+    grid = np.linspace(-140.0, 140.0, 280001, dtype=np.float32)
+    ties = np.arange(-130, 130, dtype=np.float32) + np.float32(0.5)
+    x = np.concatenate([grid, ties, np.float32([3e38, -3e38, 127.49, 127.5, -127.5, 0.0, -0.0])])
+    got = orc.int8_encode(x)
+    ref = np.clip(np.rint(x), -127, 127).astype(np.int8)
+    assert np.array_equal(got, ref)
+
+
+def test_int8_encode_specials():
+    got = orc.int8_encode(np.float32([np.nan, np.inf, -np.inf, 0.5, 1.5, 2.5, -0.5, -1.5]))
+    assert got.tolist() == [0, 127, -127, 0, 2, 2, 0, -2]
+    # -128 is never produced
+    assert orc.int8_encode(np.float32([-128.0, -1e9])).tolist() == [-127, -127]
