@@ -43,6 +43,10 @@
  *   - q-head h attends with kv-head h / (num_q_heads / num_kv_heads).
  *   - FP8 caches hold OCP E4M3FN codes with one scale per tensor (k_scale for
  *     K, v_scale for V): real value = decode(code) * scale.
+ *   - INT8 caches ("推理加速三板斧", section 2.3 lists INT8 KV beside FP8) hold
+ *     symmetric signed codes in [-127, 127] with one scale per tensor: real
+ *     value = code * scale.  Everything said of FP8 caches below (16-bit q,
+ *     scales, the kernels that serve them) holds for INT8 caches as well.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -64,7 +68,7 @@ typedef enum {
   PKV_ERR_WORKSPACE = 6      /* workspace missing or smaller than pkv_decode_workspace_size */
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 } pkv_dtype;
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3, PKV_INT8 = 4 } pkv_dtype;
 
 /* Which decode kernel family runs.  AUTO picks per shape (see
  * pkv_decode_algo_for): MFMA when the q-head group g > 1 and the dtypes
@@ -107,8 +111,10 @@ uint64_t pkv_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_d
  *                  with new_dtype in {F32, F16, BF16}: each element becomes the
  *                  E4M3 code nearest to the binary32 product x * (1/scale),
  *                  ties to even, saturating at +-448, NaN -> 0x7F; 1/scale is
- *                  rounded to binary32 first.  k_scale/v_scale must be > 0 and
- *                  finite for FP8 and are ignored otherwise.
+ *                  rounded to binary32 first.  kv_dtype == INT8: the integer
+ *                  nearest to the same product, ties to even, saturating at
+ *                  +-127, NaN -> 0.  k_scale/v_scale must be > 0 and finite
+ *                  for FP8 and INT8 and are ignored otherwise.
  *   block_size must be 16; head_dim a multiple of 8 in [8, 256]. */
 pkv_status pkv_paged_cache_append(void* k_cache, void* v_cache, const void* k_new,
                                   const void* v_new, const int64_t* slot_mapping,

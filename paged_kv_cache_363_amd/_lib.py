@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_OUT_OF_BLOCKS = 0, 1, 2, 3
 PKV_ERR_REFCOUNT, PKV_ERR_HIP, PKV_ERR_WORKSPACE = 4, 5, 6
-PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_INT8 = 0, 1, 2, 3, 4
 PKV_ALGO_AUTO, PKV_ALGO_VECTOR, PKV_ALGO_MFMA = 0, 1, 2
 
 P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float

@@ -2,7 +2,8 @@
 
 Tensors supply device memory and the current HIP stream; every step of the
 decode path runs in the library's kernels.  FP8 caches are uint8 (or
-torch.float8_e4m3fn) tensors holding OCP E4M3FN codes.
+torch.float8_e4m3fn) tensors holding OCP E4M3FN codes; INT8 caches are int8
+tensors of symmetric codes.
 """
 import ctypes
 
@@ -13,7 +14,7 @@ from ._lib import check, lib
 
 _DT = {torch.float32: _lib.PKV_F32, torch.float16: _lib.PKV_F16,
        torch.bfloat16: _lib.PKV_BF16, torch.uint8: _lib.PKV_FP8_E4M3,
-       torch.float8_e4m3fn: _lib.PKV_FP8_E4M3}
+       torch.float8_e4m3fn: _lib.PKV_FP8_E4M3, torch.int8: _lib.PKV_INT8}
 _ALGO = {"auto": _lib.PKV_ALGO_AUTO, "vector": _lib.PKV_ALGO_VECTOR, "mfma": _lib.PKV_ALGO_MFMA}
 BLOCK_SIZE = 16
 

@@ -47,7 +47,8 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
       for (int i = 0; i < nb_in; i += 16)
         *reinterpret_cast<uint4*>(outp + i) = *reinterpret_cast<const uint4*>(in + i);
     } else {
-      static_assert(KV_DT == PKV_FP8_E4M3, "only E4M3 caches convert");
+      static_assert(KV_DT == PKV_FP8_E4M3 || KV_DT == PKV_INT8,
+                    "only E4M3 and INT8 caches convert");
       const float inv = which ? v_inv : k_inv;
       float f[kElemsPerThread];
       if constexpr (NEW_DT == PKV_F32) {
@@ -59,8 +60,13 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        lo |= f32_to_e4m3(f[i] * inv) << (8 * i);
-        hi |= f32_to_e4m3(f[4 + i] * inv) << (8 * i);
+        if constexpr (KV_DT == PKV_FP8_E4M3) {
+          lo |= f32_to_e4m3(f[i] * inv) << (8 * i);
+          hi |= f32_to_e4m3(f[4 + i] * inv) << (8 * i);
+        } else {
+          lo |= f32_to_i8(f[i] * inv) << (8 * i);
+          hi |= f32_to_i8(f[4 + i] * inv) << (8 * i);
+        }
       }
       *reinterpret_cast<uint2*>(outp) = make_uint2(lo, hi);
     }
@@ -140,6 +146,18 @@ int launch_cache_append(void* k_cache, void* v_cache, const void* k_new, const v
       case PKV_BF16:
         return launch_append_t<PKV_BF16, PKV_FP8_E4M3>(k_cache, v_cache, k_new, v_new, slots, T,
                                                        H, D, nb, k_inv, v_inv, st);
+    }
+  } else if (kv_dt == PKV_INT8) {
+    switch (new_dt) {
+      case PKV_F32:
+        return launch_append_t<PKV_F32, PKV_INT8>(k_cache, v_cache, k_new, v_new, slots, T, H, D,
+                                                  nb, k_inv, v_inv, st);
+      case PKV_F16:
+        return launch_append_t<PKV_F16, PKV_INT8>(k_cache, v_cache, k_new, v_new, slots, T, H, D,
+                                                  nb, k_inv, v_inv, st);
+      case PKV_BF16:
+        return launch_append_t<PKV_BF16, PKV_INT8>(k_cache, v_cache, k_new, v_new, slots, T, H,
+                                                   D, nb, k_inv, v_inv, st);
     }
   }
   return (int)hipErrorInvalidValue;

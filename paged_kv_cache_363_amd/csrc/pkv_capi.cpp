@@ -34,13 +34,13 @@ void clear_error() { g_last_error.clear(); }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-static bool valid_dtype(int32_t dt) { return dt >= PKV_F32 && dt <= PKV_FP8_E4M3; }
+static bool valid_dtype(int32_t dt) { return dt >= PKV_F32 && dt <= PKV_INT8; }
 
 // (q, kv) dtype pairs the decode kernels implement.
 static bool decode_pair_ok(int32_t q, int32_t kv) {
   if (q == PKV_F32) return kv == PKV_F32;
-  if (q == PKV_F16) return kv == PKV_F16 || kv == PKV_FP8_E4M3;
-  if (q == PKV_BF16) return kv == PKV_BF16 || kv == PKV_FP8_E4M3;
+  if (q == PKV_F16) return kv == PKV_F16 || byte_codes(kv);
+  if (q == PKV_BF16) return kv == PKV_BF16 || byte_codes(kv);
   return false;
 }
 
@@ -63,7 +63,7 @@ static int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t 
 // contractions (g > 1) and the dtypes allow it; for g = 1 an MFMA tile would
 // use one of its 16 columns, so the vector kernel serves.
 static int32_t resolve_algo(int32_t g, int32_t q, int32_t kv) {
-  const bool mfma_ok = (q == PKV_F16 || q == PKV_BF16) && (kv == q || kv == PKV_FP8_E4M3);
+  const bool mfma_ok = (q == PKV_F16 || q == PKV_BF16) && (kv == q || byte_codes(kv));
   return mfma_ok && g > 1 ? PKV_ALGO_MFMA : PKV_ALGO_VECTOR;
 }
 
@@ -84,7 +84,7 @@ struct Plan {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static bool stream_capable_kv(int32_t kv_dtype) {
-  return kv_dtype == PKV_F16 || kv_dtype == PKV_BF16 || kv_dtype == PKV_FP8_E4M3;
+  return kv_dtype == PKV_F16 || kv_dtype == PKV_BF16 || byte_codes(kv_dtype);
 }
 
 static bool make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -221,15 +221,16 @@ pkv_status pkv_paged_cache_append(void* k_cache, void* v_cache, const void* k_ne
     return fail(PKV_ERR_UNSUPPORTED, "cache_append: head_dim must be a multiple of 8 in [8,256]");
   if (!valid_dtype(new_dtype) || !valid_dtype(kv_dtype))
     return fail(PKV_ERR_INVALID_ARG, "cache_append: bad dtype");
-  if (new_dtype == PKV_FP8_E4M3)
+  if (byte_codes(new_dtype))
     return fail(PKV_ERR_UNSUPPORTED, "cache_append: new rows must be f32, f16 or bf16");
-  if (kv_dtype != new_dtype && kv_dtype != PKV_FP8_E4M3)
-    return fail(PKV_ERR_UNSUPPORTED, "cache_append: kv dtype must equal the new rows' dtype or be FP8");
+  if (kv_dtype != new_dtype && !byte_codes(kv_dtype))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "cache_append: kv dtype must equal the new rows' dtype or be FP8/INT8");
   float k_inv = 1.0f, v_inv = 1.0f;
-  if (kv_dtype == PKV_FP8_E4M3) {
+  if (byte_codes(kv_dtype)) {
     if (!(k_scale > 0.0f) || !std::isfinite(k_scale) || !(v_scale > 0.0f) ||
         !std::isfinite(v_scale))
-      return fail(PKV_ERR_INVALID_ARG, "cache_append: FP8 scales must be finite and > 0");
+      return fail(PKV_ERR_INVALID_ARG, "cache_append: FP8/INT8 scales must be finite and > 0");
     k_inv = 1.0f / k_scale;
     v_inv = 1.0f / v_scale;
   }
@@ -351,8 +352,8 @@ pkv_status pkv_paged_decode_attention_profiled(
     return fail(PKV_ERR_UNSUPPORTED, "decode: unsupported (q, kv) dtype pair (%d, %d)", q_dtype,
                 kv_dtype);
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "decode: scale must be finite");
-  if (kv_dtype == PKV_FP8_E4M3 && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
-    return fail(PKV_ERR_INVALID_ARG, "decode: FP8 scales must be finite");
+  if (byte_codes(kv_dtype) && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
+    return fail(PKV_ERR_INVALID_ARG, "decode: FP8/INT8 scales must be finite");
   if (partition_size < 0 || (partition_size > 0 && (partition_size % kBlockSize != 0 ||
                                                      partition_size > kMaxPartition)))
     return fail(PKV_ERR_INVALID_ARG, "decode: partition_size must be 0 or a multiple of 16 <= %d",
@@ -361,7 +362,7 @@ pkv_status pkv_paged_decode_attention_profiled(
     return fail(PKV_ERR_INVALID_ARG, "decode: bad algo %d", algo);
   const int32_t g = num_q_heads / num_kv_heads;
   const bool mfma_ok =
-      (q_dtype == PKV_F16 || q_dtype == PKV_BF16) && (kv_dtype == q_dtype || kv_dtype == PKV_FP8_E4M3);
+      (q_dtype == PKV_F16 || q_dtype == PKV_BF16) && (kv_dtype == q_dtype || byte_codes(kv_dtype));
   if (algo == PKV_ALGO_MFMA && !mfma_ok)
     return fail(PKV_ERR_UNSUPPORTED, "decode: the MFMA path needs 16-bit q and a 16-bit/FP8 cache");
   if (algo == PKV_ALGO_AUTO) algo = resolve_algo(g, q_dtype, kv_dtype);
@@ -520,13 +521,13 @@ pkv_status pkv_paged_multiquery_attention_profiled(
   if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype))
     return fail(PKV_ERR_INVALID_ARG, "multiquery: bad dtype");
   if (!((q_dtype == PKV_F16 || q_dtype == PKV_BF16) &&
-        (kv_dtype == q_dtype || kv_dtype == PKV_FP8_E4M3)))
+        (kv_dtype == q_dtype || byte_codes(kv_dtype))))
     return fail(PKV_ERR_UNSUPPORTED,
                 "multiquery: needs 16-bit q and a cache of the same dtype or E4M3 (%d, %d)",
                 q_dtype, kv_dtype);
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "multiquery: scale must be finite");
-  if (kv_dtype == PKV_FP8_E4M3 && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
-    return fail(PKV_ERR_INVALID_ARG, "multiquery: FP8 scales must be finite");
+  if (byte_codes(kv_dtype) && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
+    return fail(PKV_ERR_INVALID_ARG, "multiquery: FP8/INT8 scales must be finite");
   MQPlan plan;
   if (!mq_plan(num_rows, num_seqs, max_query_len, num_q_heads, num_kv_heads, head_dim,
                max_blocks_per_seq, partition_size, &plan))

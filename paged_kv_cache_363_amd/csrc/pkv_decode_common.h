@@ -104,7 +104,7 @@ inline DecodeParams make_params(const pkv::DecodeArgs& a, int chunk_heads) {
   p.num_parts = a.num_parts;
   p.chunk_heads = p.g < chunk_heads ? p.g : chunk_heads;
   p.hchunks = (p.g + p.chunk_heads - 1) / p.chunk_heads;
-  const bool fp8 = a.kv_dtype == PKV_FP8_E4M3;
+  const bool fp8 = pkv::byte_codes(a.kv_dtype);   // scaled one-byte codes
   p.sl2 = a.scale * kLog2e * (fp8 ? a.k_scale : 1.0f);
   p.vsc = fp8 ? a.v_scale : 1.0f;
   p.ws_m = a.ws_m;

@@ -67,7 +67,7 @@ void decode_mfma_kernel(DecodeParams p) {
   if (p.nb > 0 && w1 > w0) {
     const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
     const int64_t head_off = (int64_t)hk * T::TILE;
-    mfma_piece<QT, KVT, D, KVT == PKV_FP8_E4M3 ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH, PKV_MFMA_NT>(p.kc + head_off, p.vc + head_off, blk_stride,
+    mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH, PKV_MFMA_NT>(p.kc + head_off, p.vc + head_off, blk_stride,
                                            p.bt + (int64_t)s * p.mb, w0, w1, nblk - 1,
                                            ctx - 16 * (nblk - 1), p.nb, qr, p.sl2, m_run, l_run,
                                            o, lane);
@@ -122,6 +122,10 @@ int launch_decode_mfma(const DecodeArgs& a) {
   PKV_MFMA_CASE(PKV_BF16, PKV_FP8_E4M3, 64)
   PKV_MFMA_CASE(PKV_F16, PKV_FP8_E4M3, 128)
   PKV_MFMA_CASE(PKV_F16, PKV_FP8_E4M3, 64)
+  PKV_MFMA_CASE(PKV_BF16, PKV_INT8, 128)
+  PKV_MFMA_CASE(PKV_BF16, PKV_INT8, 64)
+  PKV_MFMA_CASE(PKV_F16, PKV_INT8, 128)
+  PKV_MFMA_CASE(PKV_F16, PKV_INT8, 64)
 #undef PKV_MFMA_CASE
   return (int)hipErrorInvalidValue;
 }

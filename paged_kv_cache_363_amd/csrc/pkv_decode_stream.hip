@@ -226,8 +226,8 @@ void decode_stream_kernel(StreamParams p) {
       const int last = ((ctx + 15) >> 4) - 1;
       if (p.nb > 0) {
         const int64_t off = (int64_t)hk * T::TILE;
-        mfma_piece<QT, KVT, D, KVT == PKV_FP8_E4M3 ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
-                   KVT != PKV_FP8_E4M3 || PKV_NT_FP8>(p.kc + off, p.vc + off, blk_stride,
+        mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
+                   !pkv::byte_codes(KVT) || PKV_NT_FP8>(p.kc + off, p.vc + off, blk_stride,
                                         p.bt + (int64_t)s * p.mb, b, b1, last, ctx - 16 * last,
                                         p.nb, qr, p.sl2, m_run, l_run, o, lane);
       }
@@ -432,6 +432,10 @@ int launch_decode_stream(const DecodeArgs& a, int grid, void* ws, size_t off_ml,
   PKV_STREAM_CASE(PKV_BF16, PKV_FP8_E4M3, 64)
   PKV_STREAM_CASE(PKV_F16, PKV_FP8_E4M3, 128)
   PKV_STREAM_CASE(PKV_F16, PKV_FP8_E4M3, 64)
+  PKV_STREAM_CASE(PKV_BF16, PKV_INT8, 128)
+  PKV_STREAM_CASE(PKV_BF16, PKV_INT8, 64)
+  PKV_STREAM_CASE(PKV_F16, PKV_INT8, 128)
+  PKV_STREAM_CASE(PKV_F16, PKV_INT8, 64)
 #undef PKV_STREAM_CASE
   return (int)hipErrorInvalidValue;
 }

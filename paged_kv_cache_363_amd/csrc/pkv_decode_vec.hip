@@ -313,6 +313,10 @@ int launch_decode_vector(const DecodeArgs& a) {
   PKV_VEC_CASE(PKV_BF16, PKV_FP8_E4M3, 128)
   PKV_VEC_CASE(PKV_F16, PKV_FP8_E4M3, 64)
   PKV_VEC_CASE(PKV_F16, PKV_FP8_E4M3, 128)
+  PKV_VEC_CASE(PKV_BF16, PKV_INT8, 64)
+  PKV_VEC_CASE(PKV_BF16, PKV_INT8, 128)
+  PKV_VEC_CASE(PKV_F16, PKV_INT8, 64)
+  PKV_VEC_CASE(PKV_F16, PKV_INT8, 128)
 #undef PKV_VEC_CASE
   return (int)hipErrorInvalidValue;
 }

@@ -76,6 +76,10 @@ template <>
 struct DType<PKV_FP8_E4M3> {
   static constexpr int bytes = 1;
 };
+template <>
+struct DType<PKV_INT8> {
+  static constexpr int bytes = 1;
+};
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -140,6 +144,24 @@ __device__ __forceinline__ void chunk_to_f32<PKV_FP8_E4M3>(const uint4& r, float
     f[4 * i + 2] = b[0];
     f[4 * i + 3] = b[1];
   }
+}
+
+// Signed INT8 codes -> f32 (exact).
+template <>
+__device__ __forceinline__ void chunk_to_f32<PKV_INT8>(const uint4& r, float* f) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) f[4 * i + b] = (float)(int32_t)(int8_t)(w[i] >> (8 * b));
+}
+
+// Binary32 -> INT8 code: nearest integer, ties to even (rintf in the default
+// rounding mode), saturated to +-127, NaN -> 0.  Returned as the code's byte.
+__device__ __forceinline__ uint32_t f32_to_i8(float x) {
+  if (x != x) return 0u;
+  const float r = fminf(fmaxf(__builtin_rintf(x), -127.0f), 127.0f);
+  return (uint32_t)(int32_t)r & 0xFFu;
 }
 
 // Binary32 -> E4M3FN code: nearest, ties to even, |x| >= 448 (and +-inf)

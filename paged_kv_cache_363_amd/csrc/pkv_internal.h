@@ -17,9 +17,14 @@ inline int elem_bytes(int32_t dt) {
     case PKV_F16: return 2;
     case PKV_BF16: return 2;
     case PKV_FP8_E4M3: return 1;
+    case PKV_INT8: return 1;
   }
   return 0;
 }
+
+// Caches of one-byte codes with a per-tensor scale (E4M3 or INT8): the
+// kernels widen the codes in registers and fold the scales in.
+inline constexpr bool byte_codes(int32_t dt) { return dt == PKV_FP8_E4M3 || dt == PKV_INT8; }
 
 constexpr int kBlockSize = 16;   // tokens per physical block
 constexpr int kWaves = 4;        // waves per decode workgroup
@@ -31,8 +36,9 @@ constexpr int kDefaultStreamWorkgroups = 256;  // one wave per SIMD of a 256-CU 
 // blocks: a start costs about two loaded HBM round trips (q rows and block
 // ids, then the first K/V tiles), ~2 us, against ~1.3 us per 16-bit block and
 // ~0.7 us per E4M3 block per wave at one wave per SIMD.  The 16-bit value is
-// the measured best on ragged batches (c2-shaped: 1 unit 5.68 TB/s, 2: 5.80,
-// 3: 5.92, 4: 5.96, 6: 5.94); E4M3 keeps the cost estimate.
+// the measured best on a ragged batch (Qwen3-8B-shaped, 64 sequences of
+// 256..4096 tokens: 1 unit 5.68 TB/s, 2: 5.80, 3: 5.92, 4: 5.96, 6: 5.94);
+// one-byte codes keep the cost estimate.
 #ifndef PKV_RESTART_UNITS_16
 #define PKV_RESTART_UNITS_16 4
 #endif
@@ -40,7 +46,7 @@ constexpr int kDefaultStreamWorkgroups = 256;  // one wave per SIMD of a 256-CU 
 #define PKV_RESTART_UNITS_FP8 3
 #endif
 inline int kv_restart_units(int32_t kv_dtype) {
-  return kv_dtype == PKV_FP8_E4M3 ? PKV_RESTART_UNITS_FP8 : PKV_RESTART_UNITS_16;
+  return byte_codes(kv_dtype) ? PKV_RESTART_UNITS_FP8 : PKV_RESTART_UNITS_16;
 }
 
 struct DecodeArgs {

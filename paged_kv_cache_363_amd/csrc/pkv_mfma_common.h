@@ -60,6 +60,11 @@ struct Mfma<PKV_BF16> {
     return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
   }
+  // two INT8 codes (bytes 2*hi and 2*hi+1 of w) -> two bf16 (exact: |code| <= 127)
+  __device__ static uint32_t i8x2(uint32_t w, bool hi) {
+    const uint32_t h = hi ? w >> 16 : w;
+    return pack2((float)(int32_t)(int8_t)h, (float)(int32_t)(int8_t)(h >> 8));
+  }
   __device__ static float rounded(float a) { return (float)(__bf16)a; }
 };
 
@@ -81,6 +86,10 @@ struct Mfma<PKV_F16> {
   __device__ static uint32_t pack2(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+  }
+  __device__ static uint32_t i8x2(uint32_t w, bool hi) {
+    const uint32_t h = hi ? w >> 16 : w;
+    return pack2((float)(int32_t)(int8_t)h, (float)(int32_t)(int8_t)(h >> 8));
   }
   __device__ static float rounded(float a) { return (float)(_Float16)a; }
 };
@@ -136,11 +145,18 @@ struct MfmaTile {
   using V4 = typename M::v4;
   static constexpr int DPL = D / 16;        // dims per lane in a V row = PV m-tiles
   static constexpr int KSTEPS = D / 32;     // QK k-steps of 32
-  static constexpr bool FP8 = (KVT == PKV_FP8_E4M3);
-  static constexpr int KVB = FP8 ? 1 : 2;
+  // one-byte codes (E4M3 or INT8) widened to the q dtype in registers
+  static constexpr bool BYTE = (KVT == PKV_FP8_E4M3 || KVT == PKV_INT8);
+  static constexpr int KVB = BYTE ? 1 : 2;
   static constexpr int64_t TILE = 16 * D * KVB;   // bytes of one (block, kv-head) tile
   static constexpr int ROWB = DPL * KVB;          // bytes of a lane's slice of one V row
-  static constexpr int KL = FP8 ? D / 64 : KSTEPS;  // 16-byte K loads per lane
+  static constexpr int KL = BYTE ? D / 64 : KSTEPS;  // 16-byte K loads per lane
+
+  // two one-byte codes (half-word `hi` of w) -> two q-dtype values, exact
+  __device__ static uint32_t cvt2(uint32_t w, bool hi) {
+    if constexpr (KVT == PKV_INT8) return M::i8x2(w, hi);
+    else return M::fp8x2(w, hi);
+  }
 
   struct Raw {
     uint4 k[KL];
@@ -149,7 +165,7 @@ struct MfmaTile {
 
   // dim of element i of k-slot G in QK step kk (the same map for q and K)
   __device__ static int qk_dim0(int kk, int G) {
-    return FP8 ? (64 * (kk / 2) + 16 * G + 8 * (kk % 2)) : (32 * kk + 8 * G);
+    return BYTE ? (64 * (kk / 2) + 16 * G + 8 * (kk % 2)) : (32 * kk + 8 * G);
   }
 
   // raw q row slice of q-head `row` (or zeros when !live) for every QK step
@@ -167,7 +183,7 @@ struct MfmaTile {
   // that a load is a wave-uniform base plus one lane offset (the SGPR-base
   // form of global_load) with no per-lane 64-bit address arithmetic.
   __device__ static uint32_t k_lane_off(int c, int G) {
-    return FP8 ? (uint32_t)(c * D + 16 * G) : (uint32_t)((c * D + 8 * G) * 2);
+    return BYTE ? (uint32_t)(c * D + 16 * G) : (uint32_t)((c * D + 8 * G) * 2);
   }
   __device__ static uint32_t v_lane_off(int c, int G) {
     return (uint32_t)((4 * G * D + DPL * c) * KVB);
@@ -195,14 +211,14 @@ struct MfmaTile {
   __device__ static void consume(Raw& r, int valid, int vis, const uint4* qr, float sl2,
                                  float& m_run, float& l_run, f32x4* o, int c, int G) {
     V8 kop[KSTEPS];
-    if constexpr (FP8) {
+    if constexpr (BYTE) {
 #pragma unroll
       for (int mm = 0; mm < KL; ++mm) {
         const uint4 x = r.k[mm];
-        kop[2 * mm] = as_v8<V8>(make_uint4(M::fp8x2(x.x, false), M::fp8x2(x.x, true),
-                                           M::fp8x2(x.y, false), M::fp8x2(x.y, true)));
-        kop[2 * mm + 1] = as_v8<V8>(make_uint4(M::fp8x2(x.z, false), M::fp8x2(x.z, true),
-                                               M::fp8x2(x.w, false), M::fp8x2(x.w, true)));
+        kop[2 * mm] = as_v8<V8>(make_uint4(cvt2(x.x, false), cvt2(x.x, true),
+                                           cvt2(x.y, false), cvt2(x.y, true)));
+        kop[2 * mm + 1] = as_v8<V8>(make_uint4(cvt2(x.z, false), cvt2(x.z, true),
+                                               cvt2(x.w, false), cvt2(x.w, true)));
       }
     } else {
 #pragma unroll
@@ -251,15 +267,15 @@ struct MfmaTile {
     const V4 pl = as_v4<V4>(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]));
 
     // A operand of PV for m-tile e: dim DPL*c + e of tokens 4G..4G+3.
-    if constexpr (FP8) {
+    if constexpr (BYTE) {
 #pragma unroll
       for (int e = 0; e < DPL; e += 2) {
         const int wi = e / 4, k = e % 4;
         const uint32_t sel = (uint32_t)k | ((4u + k) << 8) | ((k + 1u) << 16) | ((5u + k) << 24);
         const uint32_t x01 = __builtin_amdgcn_perm(r.v[1].w[wi], r.v[0].w[wi], sel);
         const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
-        const V4 a0 = as_v4<V4>(M::fp8x2(x01, false), M::fp8x2(x23, false));
-        const V4 a1 = as_v4<V4>(M::fp8x2(x01, true), M::fp8x2(x23, true));
+        const V4 a0 = as_v4<V4>(cvt2(x01, false), cvt2(x23, false));
+        const V4 a1 = as_v4<V4>(cvt2(x01, true), cvt2(x23, true));
         o[e] = M::pv(a0, pl, M::pv(a0, pb, o[e]));
         o[e + 1] = M::pv(a1, pl, M::pv(a1, pb, o[e + 1]));
       }

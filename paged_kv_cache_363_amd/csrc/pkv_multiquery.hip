@@ -119,7 +119,7 @@ void multiquery_mfma_kernel(MQParams p) {
     const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
     const int64_t head_off = (int64_t)hk * T::TILE;
     const int last = ((ctx + 15) >> 4) - 1;
-    mfma_piece<QT, KVT, D, KVT == PKV_FP8_E4M3 ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH, false,
+    mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH, false,
                true>(p.kc + head_off, p.vc + head_off, blk_stride, p.bt + (int64_t)s * p.mb,
                      w0, w1, last, ctx - 16 * last, p.nb, qr, p.sl2, m_run, l_run, o, lane,
                      pos);
@@ -261,7 +261,7 @@ MQParams make_mq_params(const pkv::MQArgs& a) {
   p.qtiles = t.qtiles;
   p.part_blocks = a.partition / pkv::kBlockSize;
   p.num_parts = a.num_parts;
-  const bool fp8 = a.kv_dtype == PKV_FP8_E4M3;
+  const bool fp8 = pkv::byte_codes(a.kv_dtype);   // scaled one-byte codes
   p.sl2 = a.scale * kLog2e * (fp8 ? a.k_scale : 1.0f);
   p.vsc = fp8 ? a.v_scale : 1.0f;
   p.ws_m = a.ws_m;
@@ -303,6 +303,10 @@ int launch_multiquery(const MQArgs& a) {
   PKV_MQ_CASE(PKV_BF16, PKV_FP8_E4M3, 128)
   PKV_MQ_CASE(PKV_F16, PKV_FP8_E4M3, 64)
   PKV_MQ_CASE(PKV_F16, PKV_FP8_E4M3, 128)
+  PKV_MQ_CASE(PKV_BF16, PKV_INT8, 64)
+  PKV_MQ_CASE(PKV_BF16, PKV_INT8, 128)
+  PKV_MQ_CASE(PKV_F16, PKV_INT8, 64)
+  PKV_MQ_CASE(PKV_F16, PKV_INT8, 128)
 #undef PKV_MQ_CASE
   return (int)hipErrorInvalidValue;
 }

@@ -111,6 +111,10 @@ MQ_CONFIGS = {
         name="mq_c4_verify8", base="c4_llama3_70b_fp8", qlen_kind="fixed", qlen_params=(8,),
         seed=2004, description="speculative verify, 8 rows per sequence, Llama-3-70B-shaped "
                                "E4M3 cache, batch 32"),
+    "mq_c6_verify8": MQConfig(
+        name="mq_c6_verify8", base="c6_llama3_70b_int8", qlen_kind="fixed", qlen_params=(8,),
+        seed=2006, description="speculative verify, 8 rows per sequence, Llama-3-70B-shaped "
+                               "INT8 cache, batch 32"),
     "mq_c5_chunk512": MQConfig(
         name="mq_c5_chunk512", base="c5_long_shared_bf16", qlen_kind="fixed", qlen_params=(512,),
         seed=2005, description="512-token prompt chunk at the end of each 32K context, bf16, "

@@ -1,7 +1,7 @@
 """Decode edge cases on the GPU against the oracle: empty and one-token
 contexts, exact block boundaries, bad table entries, clamped lengths, every
-GQA group size, head_dim 64, f16 with an FP8 cache, the E4M3 decode of every
-code, and the pages' invariants (physical-block permutation, shared prefix)
+GQA group size, head_dim 64, f16 with an FP8 cache, INT8 caches, the E4M3 and
+INT8 decode of every code, and the pages' invariants (physical-block permutation, shared prefix)
 checked bit for bit on the GPU itself."""
 import dataclasses
 
@@ -57,7 +57,8 @@ GROUPS = [(4, 4), (8, 4), (6, 2), (10, 2), (16, 2), (32, 2), (64, 2), (3, 1)]
 @pytest.mark.parametrize("hq,hkv", GROUPS)
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("q,kv", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "fp8"),
-                                  ("f16", "fp8"), ("f32", "f32")])
+                                  ("f16", "fp8"), ("f32", "f32"), ("bf16", "int8"),
+                                  ("f16", "int8")])
 def test_group_sizes_dtypes_and_head_dims(hq, hkv, d, q, kv):
     ctxs = [1, 15, 16, 17, 33, 100, 257]
     cfg = small_cfg(f"g{hq}_{hkv}_{d}_{q}_{kv}", hq, hkv, d, q, kv, ctxs, seed=hq * 100 + d)
@@ -105,6 +106,29 @@ def test_e4m3_decode_of_every_code(algo):
     out = pkv.paged_decode_attention(q, kc, vc, bt, cl, 0.1, 1.0, 1.0, algo=algo)
     torch.cuda.synchronize()
     ref = orc.to_f64(vrows, "fp8")
+    for h in range(4):
+        assert np.array_equal(out[:, h].float().cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("algo", ["vector", "mfma"])
+def test_int8_decode_of_every_code(algo):
+    """One-token contexts whose V rows enumerate all 255 symmetric INT8 codes:
+    the output is code * v_scale, exact in bf16 for a power-of-two scale."""
+    import paged_kv_cache_363_amd as pkv
+    print(f"[case] int8 codes {algo}", flush=True)
+    codes = np.arange(-127, 128, dtype=np.int8)
+    D, S, H = 128, 2, 1
+    vrows = np.zeros((S, D), np.int8)
+    vrows.ravel()[:codes.size] = codes
+    kc = torch.zeros((S, H, 16, D), dtype=torch.int8, device="cuda")
+    vc = torch.zeros((S, H, 16, D), dtype=torch.int8, device="cuda")
+    vc[:, 0, 0, :] = torch.from_numpy(vrows).cuda()
+    q = torch.randn(S, 4, D).to(torch.bfloat16).cuda()
+    bt = torch.arange(S, dtype=torch.int32, device="cuda").view(S, 1)
+    cl = torch.ones(S, dtype=torch.int32, device="cuda")
+    out = pkv.paged_decode_attention(q, kc, vc, bt, cl, 0.1, 1.0, 0.25, algo=algo)
+    torch.cuda.synchronize()
+    ref = vrows.astype(np.float64) * 0.25
     for h in range(4):
         assert np.array_equal(out[:, h].float().cpu().numpy().astype(np.float64), ref)
 

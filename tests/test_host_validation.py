@@ -171,3 +171,20 @@ def test_multiquery_partition_and_workspace_helpers():
     n = l.pkv_multiquery_workspace_size(256, 64, 4, 32, 8, 128, 256, 512)
     assert n >= 256 * 32 * 8 * (128 + 2) * 4
     assert l.pkv_multiquery_workspace_size(-1, 64, 4, 32, 8, 128, 256, 512) == ctypes.c_size_t(-1).value
+
+
+
+def test_int8_cache_is_a_scaled_byte_cache():
+    l = lib()
+    assert l.pkv_decode_algo_for(64, 8, 128, _lib.PKV_BF16, _lib.PKV_INT8) == _lib.PKV_ALGO_MFMA
+    assert l.pkv_decode_algo_for(32, 32, 128, _lib.PKV_F16, _lib.PKV_INT8) == _lib.PKV_ALGO_VECTOR
+    assert l.pkv_decode_partition_size(32, 64, 8, 128, 160, _lib.PKV_INT8, 0) == 0   # balanced
+    assert l.pkv_kv_bytes_per_token(80, 8, 128, _lib.PKV_INT8) == 2 * 80 * 8 * 128
+    # f32 q with an INT8 cache is not implemented; INT8 rows cannot be appended
+    assert decode(qd=_lib.PKV_F32, kvd=_lib.PKV_INT8) == _lib.PKV_ERR_UNSUPPORTED
+    st = lib().pkv_paged_cache_append(NULL, NULL, NULL, NULL, NULL, 3, 2, 64, 16, 4,
+                                      _lib.PKV_INT8, _lib.PKV_INT8, 1.0, 1.0, NULL)
+    assert st == _lib.PKV_ERR_UNSUPPORTED
+    st = lib().pkv_paged_cache_append(NULL, NULL, NULL, NULL, NULL, 3, 2, 64, 16, 4,
+                                      _lib.PKV_BF16, _lib.PKV_INT8, 0.0, 1.0, NULL)
+    assert st == _lib.PKV_ERR_INVALID_ARG                  # INT8 needs scales > 0
