@@ -48,6 +48,10 @@ def _load():
     lib.orc_paged_decode.restype = I
     lib.orc_paged_multiquery.argtypes = [P, P, I, P, P, I, P, P, P, I, I, I, I, I, I, I, D, D, D]
     lib.orc_paged_multiquery.restype = I
+    lib.orc_cache_append_channel.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, P]
+    lib.orc_cache_append_channel.restype = I
+    lib.orc_paged_decode_channel.argtypes = [P, P, I, P, P, I, P, P, I, I, I, I, I, I, D, P, P]
+    lib.orc_paged_decode_channel.restype = I
     lib.orc_softmax_weights.argtypes = [P, I, I, P, I, P, I, P, P, I, I, I, I, I, I, D, D]
     lib.orc_softmax_weights.restype = I
     lib.orc_partition_stats.argtypes = [P, P, P, I, I, I, I, P, I, P, P, I, P, P,
@@ -176,6 +180,45 @@ def paged_multiquery(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, conte
                                       k_scale, v_scale)
     if rc != 0:
         raise ValueError(f"oracle paged_multiquery failed ({rc})")
+    return out
+
+
+def cache_append_channel(k_cache, v_cache, k_new, v_new, slot_mapping, new_dtype, kv_dtype,
+                         k_scales, v_scales):
+    """Append into a one-byte-code cache with one float32 scale per (kv-head,
+    dim) channel: k_scales, v_scales [H_kv][d]."""
+    k_cache = _check_bits(k_cache, kv_dtype)
+    v_cache = _check_bits(v_cache, kv_dtype)
+    k_new = _check_bits(k_new, new_dtype)
+    v_new = _check_bits(v_new, new_dtype)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    ks = np.ascontiguousarray(k_scales, dtype=np.float32)
+    vs = np.ascontiguousarray(v_scales, dtype=np.float32)
+    nb, hkv, bs, d = k_cache.shape
+    assert ks.shape == (hkv, d) and vs.shape == (hkv, d)
+    rc = _load().orc_cache_append_channel(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new),
+                                          _ptr(sm), sm.shape[0], hkv, d, bs, nb,
+                                          DTYPES[new_dtype], DTYPES[kv_dtype], _ptr(ks), _ptr(vs))
+    if rc != 0:
+        raise ValueError(f"oracle cache_append_channel failed ({rc})")
+
+
+def paged_decode_channel(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
+                         scale, k_scales, v_scales):
+    """fp64 decode over a cache with per-channel scales [H_kv][d] (as float64)."""
+    q, k_cache, bt, cl, S, hq, hkv, d, bs = _common(q, q_dtype, k_cache, kv_dtype,
+                                                    block_tables, context_lens)
+    v_cache = _check_bits(v_cache, kv_dtype)
+    ks = np.ascontiguousarray(k_scales, dtype=np.float64)
+    vs = np.ascontiguousarray(v_scales, dtype=np.float64)
+    assert ks.shape == (hkv, d) and vs.shape == (hkv, d)
+    out = np.empty((S, hq, d), dtype=np.float64)
+    rc = _load().orc_paged_decode_channel(_ptr(out), _ptr(q), DTYPES[q_dtype], _ptr(k_cache),
+                                          _ptr(v_cache), DTYPES[kv_dtype], _ptr(bt), _ptr(cl),
+                                          S, hq, hkv, d, bs, bt.shape[1], scale, _ptr(ks),
+                                          _ptr(vs))
+    if rc != 0:
+        raise ValueError(f"oracle paged_decode_channel failed ({rc})")
     return out
 
 

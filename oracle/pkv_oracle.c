@@ -24,6 +24,11 @@
  *    the pages name GQA for Qwen3-8B and Llama-3-70B without the mapping).
  *  - FP8 E4M3 KV (range +-448, "大语言模型推理引擎深度剖析", section 4.2): OCP
  *    E4M3FN, per-tensor scale, real value = decode(code) * scale.
+ *  - Per-channel scales ("大语言模型推理引擎深度剖析", section 4.3: each head
+ *    dimension of the K and V tensors is quantised on its own, stored as FP8
+ *    and dequantised for compute): one scale per (kv-head, dim) channel, for
+ *    K and V separately, for E4M3 and INT8 codes alike; real value = code *
+ *    scale[kv_head][dim].
  *  - INT8 KV ("推理加速三板斧", section 2.3, which lists INT8 KV caches
  *    next to FP8 without the encoding; reading: symmetric, one scale per
  *    tensor like FP8): code = the integer nearest to the binary32 product
@@ -211,6 +216,91 @@ int orc_cache_append(void* k_cache, void* v_cache, const void* k_new,
       }
     }
   }
+  return 0;
+}
+
+/* The same append with one scale per (kv-head, dim) channel: element i of
+ * kv-head h is encoded from the binary32 product x * fp32(1/scale[h*d+i]).
+ * Caches must hold one-byte codes (E4M3 or INT8). */
+int orc_cache_append_channel(void* k_cache, void* v_cache, const void* k_new,
+                             const void* v_new, const int64_t* slot_mapping,
+                             int num_tokens, int num_kv_heads, int head_dim,
+                             int block_size, int num_blocks, int new_dtype,
+                             int kv_dtype, const float* k_scales, const float* v_scales) {
+  if (!scaled_dtype(kv_dtype)) return -2;
+  for (int t = 0; t < num_tokens; ++t) {
+    int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    if (slot >= (int64_t)num_blocks * block_size) return -1;
+    int64_t blk = slot / block_size, off = slot % block_size;
+    for (int h = 0; h < num_kv_heads; ++h) {
+      for (int i = 0; i < head_dim; ++i) {
+        int64_t src = ((int64_t)t * num_kv_heads + h) * head_dim + i;
+        int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * head_dim + i;
+        for (int which = 0; which < 2; ++which) {
+          float scale = (which ? v_scales : k_scales)[h * head_dim + i];
+          float inv = 1.0f / scale;
+          float y = load_as_f32(which ? v_new : k_new, src, new_dtype) * inv;
+          ((uint8_t*)(which ? v_cache : k_cache))[dst] =
+              kv_dtype == ORC_FP8_E4M3 ? orc_e4m3_encode(y) : orc_int8_encode(y);
+        }
+      }
+    }
+  }
+  return 0;
+}
+
+/* Decode attention over a cache with per-channel scales: the K element of
+ * (token t, kv-head h, dim i) is code * k_scales[h*d+i], likewise V.  Plain
+ * loops over the block table; out[S][H_q][d]. */
+int orc_paged_decode_channel(double* out, const void* q, int q_dtype, const void* k_cache,
+                             const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                             const int32_t* context_lens, int num_seqs, int num_q_heads,
+                             int num_kv_heads, int head_dim, int block_size,
+                             int max_blocks_per_seq, double scale, const double* k_scales,
+                             const double* v_scales) {
+  if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || !scaled_dtype(kv_dtype))
+    return -1;
+  const int g = num_q_heads / num_kv_heads;
+  const int max_ctx = max_blocks_per_seq * block_size;
+  double* z = (double*)malloc(sizeof(double) * (max_ctx > 0 ? max_ctx : 1));
+  if (!z) return -3;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int n = context_lens[s];
+    if (n > max_ctx) { free(z); return -2; }
+    for (int hq = 0; hq < num_q_heads; ++hq) {
+      const int hk = hq / g;
+      double* o = out + ((int64_t)s * num_q_heads + hq) * head_dim;
+      for (int i = 0; i < head_dim; ++i) o[i] = 0.0;
+      if (n <= 0) continue;
+      double m = -INFINITY;
+      for (int t = 0; t < n; ++t) {
+        const int32_t phys = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
+        const int64_t base = (((int64_t)phys * num_kv_heads + hk) * block_size +
+                              t % block_size) * head_dim;
+        double dot = 0.0;
+        for (int i = 0; i < head_dim; ++i)
+          dot += load_elem(q, ((int64_t)s * num_q_heads + hq) * head_dim + i, q_dtype) *
+                 (load_elem(k_cache, base + i, kv_dtype) * k_scales[hk * head_dim + i]);
+        z[t] = scale * dot;
+        if (z[t] > m) m = z[t];
+      }
+      double l = 0.0;
+      for (int t = 0; t < n; ++t) {
+        z[t] = exp(z[t] - m);
+        l += z[t];
+      }
+      for (int t = 0; t < n; ++t) {
+        const int32_t phys = block_tables[(int64_t)s * max_blocks_per_seq + t / block_size];
+        const int64_t base = (((int64_t)phys * num_kv_heads + hk) * block_size +
+                              t % block_size) * head_dim;
+        const double wt = z[t] / l;
+        for (int i = 0; i < head_dim; ++i)
+          o[i] += wt * (load_elem(v_cache, base + i, kv_dtype) * v_scales[hk * head_dim + i]);
+      }
+    }
+  }
+  free(z);
   return 0;
 }
 
