@@ -122,6 +122,23 @@ pkv_status pkv_paged_cache_append(void* k_cache, void* v_cache, const void* k_ne
                                   int32_t block_size, int32_t num_blocks, int32_t new_dtype,
                                   int32_t kv_dtype, float k_scale, float v_scale, void* stream);
 
+/* The same append into an FP8 or INT8 cache with per-channel scales
+ * ("大语言模型推理引擎深度剖析", section 4.3: each head dimension of the K and V
+ * tensors quantised on its own): element i of kv-head h is encoded from the
+ * binary32 product x * (1/k_scales[h*head_dim + i]) (likewise V), the
+ * reciprocal rounded to binary32.
+ *   k_scales, v_scales : device float[num_kv_heads][head_dim]; every scale
+ *                        must be finite and > 0 (read on the device, not
+ *                        checked).
+ * PKV_ERR_UNSUPPORTED for a 16-bit or f32 cache. */
+pkv_status pkv_paged_cache_append_per_channel(void* k_cache, void* v_cache, const void* k_new,
+                                              const void* v_new, const int64_t* slot_mapping,
+                                              int32_t num_tokens, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t block_size,
+                                              int32_t num_blocks, int32_t new_dtype,
+                                              int32_t kv_dtype, const float* k_scales,
+                                              const float* v_scales, void* stream);
+
 /* ------------------------------------------------------ decode attention -- */
 
 /* Effective partition size (tokens) an AUTO decode call with these arguments
@@ -235,6 +252,23 @@ pkv_status pkv_paged_decode_attention_profiled(
     int32_t kv_dtype, float k_scale, float v_scale, int32_t partition_size, void* workspace,
     size_t workspace_bytes, int32_t algo, void* stream, void* ev_begin, void* ev_mid,
     void* ev_end);
+
+/* Decode over an FP8 or INT8 cache with per-channel scales (see
+ * pkv_paged_cache_append_per_channel): the K element of (token, kv-head h,
+ * dim i) is code * k_scales[h*head_dim + i], likewise V.  The K scales are
+ * folded into q (q_i * k_scales_i in binary32, entering the matrix cores as a
+ * 16-bit head plus remainder, about 16 mantissa bits); the V scales multiply
+ * each output dim.  Arguments, schedules, workspace, algo and events as for
+ * pkv_paged_decode_attention_profiled.  PKV_ERR_UNSUPPORTED for a 16-bit or
+ * f32 cache; multi-query calls take per-tensor scales only. */
+pkv_status pkv_paged_decode_attention_per_channel(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, float scale, int32_t q_dtype,
+    int32_t kv_dtype, const float* k_scales, const float* v_scales, int32_t partition_size,
+    void* workspace, size_t workspace_bytes, int32_t algo, void* stream, void* ev_begin,
+    void* ev_mid, void* ev_end);
 
 /* ------------------------------------------- multi-query attention -- */
 

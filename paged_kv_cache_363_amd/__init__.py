@@ -8,5 +8,6 @@ from ._lib import (HipError, InvalidArg, OutOfBlocks, PkvError, RefcountError,  
 from .api import (BLOCK_SIZE, alloc_workspace, copy_blocks, decode_algo_for,  # noqa: F401
                   decode_partition_size, decode_workspace_size, kv_bytes_per_token,
                   multiquery_partition_size, multiquery_workspace_size, paged_cache_append,
+                  paged_cache_append_per_channel, paged_decode_attention_per_channel,
                   paged_decode_attention, paged_multiquery_attention, swap_blocks)
 from .pool import BlockPool  # noqa: F401

@@ -44,6 +44,11 @@ SIGNATURES = {
     "pkv_paged_multiquery_attention_profiled": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32,
                                                       I32, I32, I32, I32, F32, I32, I32, F32, F32,
                                                       I32, P, SZ, P, P, P, P]),
+    "pkv_paged_cache_append_per_channel": (I32, [P, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                                 I32, P, P, P]),
+    "pkv_paged_decode_attention_per_channel": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, I32,
+                                                     I32, I32, F32, I32, I32, P, P, I32, P, SZ,
+                                                     I32, P, P, P, P]),
     "pkv_copy_blocks": (I32, [P, P, P, I32, I32, I64, P]),
     "pkv_swap_blocks": (I32, [P, P, I32, P, P, I32, P, I32, I64, P]),
     "pkv_seq_swap": (I32, [P, P, P, I32, P, P]),

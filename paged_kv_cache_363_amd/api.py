@@ -62,6 +62,26 @@ def paged_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping, k_scale=1.0
         _stream(k_cache, stream)))
 
 
+def paged_cache_append_per_channel(k_cache, v_cache, k_new, v_new, slot_mapping, k_scales,
+                                   v_scales, stream=None):
+    """Append into an FP8/INT8 cache with per-channel scales: k_scales,
+    v_scales are float32 device tensors [H_kv][d]."""
+    nb, hkv, bs, d = k_cache.shape
+    T = slot_mapping.shape[0]
+    if tuple(k_new.shape) != (T, hkv, d) or tuple(v_new.shape) != (T, hkv, d):
+        raise ValueError(f"k_new/v_new must be [{T}, {hkv}, {d}]")
+    for t, name in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (hkv, d):
+            raise ValueError(f"{name} must be float32 [{hkv}, {d}]")
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    check(lib().pkv_paged_cache_append_per_channel(
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_new, "k_new"),
+        _dev(v_new, "v_new"), _dev(slot_mapping, "slot_mapping"), T, hkv, d, bs, nb,
+        dtype_code(k_new), dtype_code(k_cache), _dev(k_scales, "k_scales"),
+        _dev(v_scales, "v_scales"), _stream(k_cache, stream)))
+
+
 def decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                           kv_dtype=_lib.PKV_BF16, partition_size=0, context_lens=None):
     """partition_size for a decode call (pkv_decode_partition_size).  With the
@@ -209,6 +229,37 @@ def swap_blocks(dst_k, dst_v, src_k, src_v, src_dst_pairs, stream=None):
     check(lib().pkv_swap_blocks(ptr(dst_k), ptr(dst_v), dst_k.shape[0], ptr(src_k), ptr(src_v),
                                 src_k.shape[0], ptr(src_dst_pairs), src_dst_pairs.shape[0],
                                 block_bytes, _stream(dev, stream)))
+
+
+def paged_decode_attention_per_channel(q, k_cache, v_cache, block_tables, context_lens, scale,
+                                       k_scales, v_scales, partition_size=0, out=None,
+                                       workspace=None, algo="auto", stream=None, events=None):
+    """Decode over an FP8/INT8 cache with per-channel scales [H_kv][d]
+    (float32 device tensors); otherwise as paged_decode_attention."""
+    S, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    for t, name in ((k_scales, "k_scales"), (v_scales, "v_scales")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (hkv, d):
+            raise ValueError(f"{name} must be float32 [{hkv}, {d}]")
+    mb = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(q, k_cache, block_tables, partition_size)
+    evs = [None, None, None]
+    if events is not None:
+        evs = [ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events]
+    check(lib().pkv_paged_decode_attention_per_channel(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, hq, hkv, d,
+        bs, nb, mb, float(scale), dtype_code(q), dtype_code(k_cache),
+        _dev(k_scales, "k_scales"), _dev(v_scales, "v_scales"), int(partition_size),
+        _dev(workspace, "workspace"), workspace.numel(), _ALGO[algo], _stream(q, stream), *evs))
+    return out
 
 
 def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):

@@ -23,7 +23,8 @@ template <int NEW_DT, int KV_DT>
 __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
     uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, const uint8_t* __restrict__ kn,
     const uint8_t* __restrict__ vn, const int64_t* __restrict__ slots, int num_tokens, int H,
-    int D, int num_blocks, float k_inv, float v_inv) {
+    int D, int num_blocks, float k_inv, float v_inv, const float* __restrict__ k_sc,
+    const float* __restrict__ v_sc) {
   const int chunks = D / kElemsPerThread;
   const int64_t gid = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x;
   const int64_t total = (int64_t)num_tokens * H * chunks;
@@ -50,6 +51,13 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
       static_assert(KV_DT == PKV_FP8_E4M3 || KV_DT == PKV_INT8,
                     "only E4M3 and INT8 caches convert");
       const float inv = which ? v_inv : k_inv;
+      // per-channel scales (a scale per (kv-head, dim)): the element's own
+      // reciprocal, rounded to binary32 like the per-tensor one
+      const float* sc = which ? v_sc : k_sc;
+      float invs[kElemsPerThread];
+#pragma unroll
+      for (int i = 0; i < kElemsPerThread; ++i)
+        invs[i] = sc ? __fdiv_rn(1.0f, sc[(int64_t)h * D + c * kElemsPerThread + i]) : inv;
       float f[kElemsPerThread];
       if constexpr (NEW_DT == PKV_F32) {
         chunk_to_f32<PKV_F32>(*reinterpret_cast<const uint4*>(in), f);
@@ -61,11 +69,11 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (KV_DT == PKV_FP8_E4M3) {
-          lo |= f32_to_e4m3(f[i] * inv) << (8 * i);
-          hi |= f32_to_e4m3(f[4 + i] * inv) << (8 * i);
+          lo |= f32_to_e4m3(f[i] * invs[i]) << (8 * i);
+          hi |= f32_to_e4m3(f[4 + i] * invs[4 + i]) << (8 * i);
         } else {
-          lo |= f32_to_i8(f[i] * inv) << (8 * i);
-          hi |= f32_to_i8(f[4 + i] * inv) << (8 * i);
+          lo |= f32_to_i8(f[i] * invs[i]) << (8 * i);
+          hi |= f32_to_i8(f[4 + i] * invs[4 + i]) << (8 * i);
         }
       }
       *reinterpret_cast<uint2*>(outp) = make_uint2(lo, hi);
@@ -106,12 +114,13 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(
 template <int NEW_DT, int KV_DT>
 int launch_append_t(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                     const int64_t* slots, int32_t T, int32_t H, int32_t D, int32_t nb,
-                    float k_inv, float v_inv, hipStream_t stream) {
+                    float k_inv, float v_inv, hipStream_t stream, const float* k_sc,
+                    const float* v_sc) {
   const int64_t total = (int64_t)T * H * (D / kElemsPerThread);
   const int64_t grid = (total + kAppendThreads - 1) / kAppendThreads;
   cache_append_kernel<NEW_DT, KV_DT><<<dim3((unsigned)grid), dim3(kAppendThreads), 0, stream>>>(
       (uint8_t*)k_cache, (uint8_t*)v_cache, (const uint8_t*)k_new, (const uint8_t*)v_new, slots,
-      T, H, D, nb, k_inv, v_inv);
+      T, H, D, nb, k_inv, v_inv, k_sc, v_sc);
   return (int)hipGetLastError();
 }
 
@@ -121,43 +130,44 @@ namespace pkv {
 
 int launch_cache_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                         const int64_t* slots, int32_t T, int32_t H, int32_t D, int32_t nb,
-                        int32_t new_dt, int32_t kv_dt, float k_inv, float v_inv, void* stream) {
+                        int32_t new_dt, int32_t kv_dt, float k_inv, float v_inv, void* stream,
+                        const float* k_sc, const float* v_sc) {
   hipStream_t st = (hipStream_t)stream;
   if (kv_dt == new_dt) {
     switch (kv_dt) {
       case PKV_F32:
         return launch_append_t<PKV_F32, PKV_F32>(k_cache, v_cache, k_new, v_new, slots, T, H, D,
-                                                 nb, k_inv, v_inv, st);
+                                                 nb, k_inv, v_inv, st, k_sc, v_sc);
       case PKV_F16:
         return launch_append_t<PKV_F16, PKV_F16>(k_cache, v_cache, k_new, v_new, slots, T, H, D,
-                                                 nb, k_inv, v_inv, st);
+                                                 nb, k_inv, v_inv, st, k_sc, v_sc);
       case PKV_BF16:
         return launch_append_t<PKV_BF16, PKV_BF16>(k_cache, v_cache, k_new, v_new, slots, T, H,
-                                                   D, nb, k_inv, v_inv, st);
+                                                   D, nb, k_inv, v_inv, st, k_sc, v_sc);
     }
   } else if (kv_dt == PKV_FP8_E4M3) {
     switch (new_dt) {
       case PKV_F32:
         return launch_append_t<PKV_F32, PKV_FP8_E4M3>(k_cache, v_cache, k_new, v_new, slots, T,
-                                                      H, D, nb, k_inv, v_inv, st);
+                                                      H, D, nb, k_inv, v_inv, st, k_sc, v_sc);
       case PKV_F16:
         return launch_append_t<PKV_F16, PKV_FP8_E4M3>(k_cache, v_cache, k_new, v_new, slots, T,
-                                                      H, D, nb, k_inv, v_inv, st);
+                                                      H, D, nb, k_inv, v_inv, st, k_sc, v_sc);
       case PKV_BF16:
         return launch_append_t<PKV_BF16, PKV_FP8_E4M3>(k_cache, v_cache, k_new, v_new, slots, T,
-                                                       H, D, nb, k_inv, v_inv, st);
+                                                       H, D, nb, k_inv, v_inv, st, k_sc, v_sc);
     }
   } else if (kv_dt == PKV_INT8) {
     switch (new_dt) {
       case PKV_F32:
         return launch_append_t<PKV_F32, PKV_INT8>(k_cache, v_cache, k_new, v_new, slots, T, H, D,
-                                                  nb, k_inv, v_inv, st);
+                                                  nb, k_inv, v_inv, st, k_sc, v_sc);
       case PKV_F16:
         return launch_append_t<PKV_F16, PKV_INT8>(k_cache, v_cache, k_new, v_new, slots, T, H, D,
-                                                  nb, k_inv, v_inv, st);
+                                                  nb, k_inv, v_inv, st, k_sc, v_sc);
       case PKV_BF16:
         return launch_append_t<PKV_BF16, PKV_INT8>(k_cache, v_cache, k_new, v_new, slots, T, H,
-                                                   D, nb, k_inv, v_inv, st);
+                                                   D, nb, k_inv, v_inv, st, k_sc, v_sc);
     }
   }
   return (int)hipErrorInvalidValue;

@@ -174,6 +174,49 @@ bool mq_plan(int32_t num_rows, int32_t num_seqs, int32_t max_query_len, int32_t 
 
 using namespace pkv;
 
+// Body of both append entry points; k_scales / v_scales: per-channel scales
+// (device [H_kv][d]) of a one-byte-code cache, or nullptr for k_scale/v_scale.
+static pkv_status append_impl(void* k_cache, void* v_cache, const void* k_new,
+                              const void* v_new, const int64_t* slot_mapping,
+                              int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, int32_t new_dtype,
+                              int32_t kv_dtype, float k_scale, float v_scale,
+                              const float* k_scales, const float* v_scales, void* stream) {
+  clear_error();
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
+    return fail(PKV_ERR_INVALID_ARG, "cache_append: bad sizes");
+  if (block_size != kBlockSize)
+    return fail(PKV_ERR_UNSUPPORTED, "cache_append: block_size must be 16 (got %d)", block_size);
+  if (head_dim < 8 || head_dim > 256 || head_dim % 8 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "cache_append: head_dim must be a multiple of 8 in [8,256]");
+  if (!valid_dtype(new_dtype) || !valid_dtype(kv_dtype))
+    return fail(PKV_ERR_INVALID_ARG, "cache_append: bad dtype");
+  if (byte_codes(new_dtype))
+    return fail(PKV_ERR_UNSUPPORTED, "cache_append: new rows must be f32, f16 or bf16");
+  if (kv_dtype != new_dtype && !byte_codes(kv_dtype))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "cache_append: kv dtype must equal the new rows' dtype or be FP8/INT8");
+  float k_inv = 1.0f, v_inv = 1.0f;
+  if (byte_codes(kv_dtype)) {
+    if (!(k_scale > 0.0f) || !std::isfinite(k_scale) || !(v_scale > 0.0f) ||
+        !std::isfinite(v_scale))
+      return fail(PKV_ERR_INVALID_ARG, "cache_append: FP8/INT8 scales must be finite and > 0");
+    k_inv = 1.0f / k_scale;
+    v_inv = 1.0f / v_scale;
+  }
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "cache_append: NULL pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_ERR_INVALID_ARG, "cache_append: caches and new rows must be 16-byte aligned");
+  int rc = launch_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens,
+                               num_kv_heads, head_dim, num_blocks, new_dtype, kv_dtype, k_inv,
+                               v_inv, stream, k_scales, v_scales);
+  if (rc != 0) return fail(PKV_ERR_HIP, "cache_append: launch failed: %s",
+                           hipGetErrorString((hipError_t)rc));
+  return PKV_OK;
+}
+
 extern "C" {
 
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
@@ -212,39 +255,28 @@ pkv_status pkv_paged_cache_append(void* k_cache, void* v_cache, const void* k_ne
                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
                                   int32_t block_size, int32_t num_blocks, int32_t new_dtype,
                                   int32_t kv_dtype, float k_scale, float v_scale, void* stream) {
+  return append_impl(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens, num_kv_heads,
+                     head_dim, block_size, num_blocks, new_dtype, kv_dtype, k_scale, v_scale,
+                     nullptr, nullptr, stream);
+}
+
+pkv_status pkv_paged_cache_append_per_channel(void* k_cache, void* v_cache, const void* k_new,
+                                              const void* v_new, const int64_t* slot_mapping,
+                                              int32_t num_tokens, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t block_size,
+                                              int32_t num_blocks, int32_t new_dtype,
+                                              int32_t kv_dtype, const float* k_scales,
+                                              const float* v_scales, void* stream) {
   clear_error();
-  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
-    return fail(PKV_ERR_INVALID_ARG, "cache_append: bad sizes");
-  if (block_size != kBlockSize)
-    return fail(PKV_ERR_UNSUPPORTED, "cache_append: block_size must be 16 (got %d)", block_size);
-  if (head_dim < 8 || head_dim > 256 || head_dim % 8 != 0)
-    return fail(PKV_ERR_UNSUPPORTED, "cache_append: head_dim must be a multiple of 8 in [8,256]");
-  if (!valid_dtype(new_dtype) || !valid_dtype(kv_dtype))
-    return fail(PKV_ERR_INVALID_ARG, "cache_append: bad dtype");
-  if (byte_codes(new_dtype))
-    return fail(PKV_ERR_UNSUPPORTED, "cache_append: new rows must be f32, f16 or bf16");
-  if (kv_dtype != new_dtype && !byte_codes(kv_dtype))
-    return fail(PKV_ERR_UNSUPPORTED,
-                "cache_append: kv dtype must equal the new rows' dtype or be FP8/INT8");
-  float k_inv = 1.0f, v_inv = 1.0f;
-  if (byte_codes(kv_dtype)) {
-    if (!(k_scale > 0.0f) || !std::isfinite(k_scale) || !(v_scale > 0.0f) ||
-        !std::isfinite(v_scale))
-      return fail(PKV_ERR_INVALID_ARG, "cache_append: FP8/INT8 scales must be finite and > 0");
-    k_inv = 1.0f / k_scale;
-    v_inv = 1.0f / v_scale;
-  }
-  if (num_tokens == 0) return PKV_OK;
-  if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
-    return fail(PKV_ERR_INVALID_ARG, "cache_append: NULL pointer");
-  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
-    return fail(PKV_ERR_INVALID_ARG, "cache_append: caches and new rows must be 16-byte aligned");
-  int rc = launch_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens,
-                               num_kv_heads, head_dim, num_blocks, new_dtype, kv_dtype, k_inv,
-                               v_inv, stream);
-  if (rc != 0) return fail(PKV_ERR_HIP, "cache_append: launch failed: %s",
-                           hipGetErrorString((hipError_t)rc));
-  return PKV_OK;
+  if (!byte_codes(kv_dtype))
+    return fail(PKV_ERR_UNSUPPORTED, "cache_append_per_channel: the cache must hold FP8 or INT8 codes");
+  if (num_tokens > 0 && (!k_scales || !v_scales))
+    return fail(PKV_ERR_INVALID_ARG, "cache_append_per_channel: NULL scale array");
+  // the per-tensor scale checks see 1.0; each channel's scale is the caller's
+  // contract (finite, > 0), read on the device
+  return append_impl(k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens, num_kv_heads,
+                     head_dim, block_size, num_blocks, new_dtype, kv_dtype, 1.0f, 1.0f, k_scales,
+                     v_scales, stream);
 }
 
 int32_t pkv_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -326,14 +358,18 @@ int32_t pkv_decode_algo_for(int32_t num_q_heads, int32_t num_kv_heads, int32_t h
   return resolve_algo(num_q_heads / num_kv_heads, q_dtype, kv_dtype);
 }
 
-pkv_status pkv_paged_decode_attention_profiled(
+}  // extern "C"
+
+// Body of every decode entry point; k_scales / v_scales (device [H_kv][d]) are
+// per-channel scales of a one-byte-code cache, or nullptr.
+static pkv_status decode_impl(
     void* out, const void* q, const void* k_cache, const void* v_cache,
     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
     int32_t num_blocks, int32_t max_blocks_per_seq, float scale, int32_t q_dtype,
-    int32_t kv_dtype, float k_scale, float v_scale, int32_t partition_size, void* workspace,
-    size_t workspace_bytes, int32_t algo, void* stream, void* ev_begin, void* ev_mid,
-    void* ev_end) {
+    int32_t kv_dtype, float k_scale, float v_scale, const float* k_scales,
+    const float* v_scales, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    int32_t algo, void* stream, void* ev_begin, void* ev_mid, void* ev_end) {
   clear_error();
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 ||
       max_blocks_per_seq < 0)
@@ -402,6 +438,8 @@ pkv_status pkv_paged_decode_attention_profiled(
   a.scale = scale;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
   a.partition = plan.partition;
   a.num_parts = plan.num_parts;
   char* ws = static_cast<char*>(workspace);
@@ -442,6 +480,41 @@ pkv_status pkv_paged_decode_attention_profiled(
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), hs) != hipSuccess)
     return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
   return PKV_OK;
+}
+
+extern "C" {
+
+pkv_status pkv_paged_decode_attention_profiled(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, float scale, int32_t q_dtype,
+    int32_t kv_dtype, float k_scale, float v_scale, int32_t partition_size, void* workspace,
+    size_t workspace_bytes, int32_t algo, void* stream, void* ev_begin, void* ev_mid,
+    void* ev_end) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, scale,
+                     q_dtype, kv_dtype, k_scale, v_scale, nullptr, nullptr, partition_size,
+                     workspace, workspace_bytes, algo, stream, ev_begin, ev_mid, ev_end);
+}
+
+pkv_status pkv_paged_decode_attention_per_channel(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, float scale, int32_t q_dtype,
+    int32_t kv_dtype, const float* k_scales, const float* v_scales, int32_t partition_size,
+    void* workspace, size_t workspace_bytes, int32_t algo, void* stream, void* ev_begin,
+    void* ev_mid, void* ev_end) {
+  clear_error();
+  if (!byte_codes(kv_dtype))
+    return fail(PKV_ERR_UNSUPPORTED, "decode_per_channel: the cache must hold FP8 or INT8 codes");
+  if (num_seqs > 0 && (!k_scales || !v_scales))
+    return fail(PKV_ERR_INVALID_ARG, "decode_per_channel: NULL scale array");
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, scale,
+                     q_dtype, kv_dtype, 1.0f, 1.0f, k_scales, v_scales, partition_size,
+                     workspace, workspace_bytes, algo, stream, ev_begin, ev_mid, ev_end);
 }
 
 pkv_status pkv_paged_decode_attention_algo(void* out, const void* q, const void* k_cache,

@@ -35,6 +35,8 @@ struct DecodeParams {
   float* ws_m;
   float* ws_l;
   float* ws_acc;
+  const float* ks;   // per-channel K scales [Hkv][D] (nullptr: per tensor)
+  const float* vs;   // per-channel V scales [Hkv][D] (nullptr: vsc)
 };
 
 // Output store in the q dtype.
@@ -72,11 +74,12 @@ __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, con
       }
     }
     const int64_t row = (int64_t)s * p.Hq + h_first + h;
+    const float vsc = p.vs ? p.vs[(int64_t)((h_first + h) / p.g) * D + d] : p.vsc;
     if (p.num_parts == 1) {
-      store_out<QT>(p.out, row * D + d, L > 0.f ? acc * p.vsc / L : 0.f);
+      store_out<QT>(p.out, row * D + d, L > 0.f ? acc * vsc / L : 0.f);
     } else {
       const int64_t pr = row * p.num_parts + part;
-      p.ws_acc[pr * D + d] = acc * p.vsc;
+      p.ws_acc[pr * D + d] = acc * vsc;
       if (d == 0) {
         p.ws_m[pr] = M;
         p.ws_l[pr] = L;
@@ -110,6 +113,9 @@ inline DecodeParams make_params(const pkv::DecodeArgs& a, int chunk_heads) {
   p.ws_m = a.ws_m;
   p.ws_l = a.ws_l;
   p.ws_acc = a.ws_acc;
+  p.ks = a.k_scales;
+  p.vs = a.v_scales;
+  if (p.ks) p.sl2 = a.scale * kLog2e;   // the K scales go into q instead
   return p;
 }
 

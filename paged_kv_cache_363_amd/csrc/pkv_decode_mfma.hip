@@ -28,7 +28,8 @@ namespace {
 
 using namespace pkvd;
 
-template <int QT, int KVT, int D, int HS>
+// PC: a one-byte-code cache with per-channel scales (p.ks, p.vs).
+template <int QT, int KVT, int D, int HS, bool PC>
 __global__ __launch_bounds__(64 * pkv::kWaves) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WPE, 8)))
 void decode_mfma_kernel(DecodeParams p) {
   using T = MfmaTile<QT, KVT, D>;
@@ -52,7 +53,12 @@ void decode_mfma_kernel(DecodeParams p) {
   const int b_end = min(b_begin + p.part_blocks, nblk);
 
   uint4 qr[T::KSTEPS];
-  T::load_q(qr, p.q, (int64_t)s * p.Hq + h_first + c, c < nh, G);
+  uint4 qlo[PC ? T::KSTEPS : 1];
+  if constexpr (PC)
+    T::load_q_scaled(qr, qlo, p.q, (int64_t)s * p.Hq + h_first + c, c < nh, G,
+                     p.ks + (int64_t)hk * D);
+  else
+    T::load_q(qr, p.q, (int64_t)s * p.Hq + h_first + c, c < nh, G);
 
   f32x4 o[DPL];
 #pragma unroll
@@ -67,10 +73,11 @@ void decode_mfma_kernel(DecodeParams p) {
   if (p.nb > 0 && w1 > w0) {
     const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
     const int64_t head_off = (int64_t)hk * T::TILE;
-    mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH, PKV_MFMA_NT>(p.kc + head_off, p.vc + head_off, blk_stride,
+    mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH, PKV_MFMA_NT,
+               false, PC>(p.kc + head_off, p.vc + head_off, blk_stride,
                                            p.bt + (int64_t)s * p.mb, w0, w1, nblk - 1,
                                            ctx - 16 * (nblk - 1), p.nb, qr, p.sl2, m_run, l_run,
-                                           o, lane);
+                                           o, lane, 0, qlo);
   }
 
   // lane (G, c) holds O[head c][dim DPL*(4G+i) + e]; l needs the 4 G lanes
@@ -93,7 +100,14 @@ void decode_mfma_kernel(DecodeParams p) {
 template <int QT, int KVT, int D, int HS>
 int launch_t(const pkv::DecodeArgs& a, const DecodeParams& kp) {
   dim3 grid(kp.num_parts, a.num_kv_heads * kp.hchunks, a.num_seqs);
-  decode_mfma_kernel<QT, KVT, D, HS>
+  if constexpr (pkv::byte_codes(KVT)) {
+    if (kp.ks) {
+      decode_mfma_kernel<QT, KVT, D, HS, true>
+          <<<grid, dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(kp);
+      return (int)hipGetLastError();
+    }
+  }
+  decode_mfma_kernel<QT, KVT, D, HS, false>
       <<<grid, dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(kp);
   return (int)hipGetLastError();
 }

@@ -57,6 +57,8 @@ struct StreamParams {
   float* ml;                   // [2 W][chunk_heads][2]
   int W;                       // waves of the decode grid
   int R;                       // restart units counted at the start of every segment
+  const float* ks;             // per-channel K scales [Hkv][D] (nullptr: per tensor)
+  const float* vs;             // per-channel V scales [Hkv][D]
 };
 
 // floor(n / c) for 0 <= n < 2^53 and c >= 1.  n and c are exact in double,
@@ -105,7 +107,8 @@ __device__ __forceinline__ void block_prefix(const StreamParams& p, int* sm_pref
   __syncthreads();
 }
 
-template <int QT, int KVT, int D>
+// PC: a one-byte-code cache with per-channel scales (p.ks, p.vs).
+template <int QT, int KVT, int D, bool PC>
 __global__ __launch_bounds__(64 * kSkWaves) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void decode_stream_kernel(StreamParams p) {
   using T = MfmaTile<QT, KVT, D>;
@@ -160,6 +163,7 @@ void decode_stream_kernel(StreamParams p) {
 
   const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
   uint4 qr[KS];
+  uint4 qlo[PC ? KS : 1];
   f32x4 o[DPL];
   float m_run = kNegInf, l_run = 0.f;
   auto reset = [&]() {
@@ -179,22 +183,33 @@ void decode_stream_kernel(StreamParams p) {
     const float l_tot = wave_sum4(l_run);
     if (b0 == 0 && b_last == nbk - 1) {
       if (c < nh) {
-        const float inv = l_tot > 0.f ? p.vsc / l_tot : 0.f;
         const int64_t row = ((int64_t)s * p.Hq + h_first + c) * D + DPL * 4 * G;
+        if constexpr (PC) {
+          const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+          const float* vs = p.vs + (int64_t)(y / p.hchunks) * D + DPL * 4 * G;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) store_out<QT>(p.out, row + DPL * i + e, o[e][i] * inv);
+            for (int e = 0; e < DPL; ++e)
+              store_out<QT>(p.out, row + DPL * i + e, o[e][i] * vs[DPL * i + e] * inv);
+        } else {
+          const float inv = l_tot > 0.f ? p.vsc / l_tot : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) store_out<QT>(p.out, row + DPL * i + e, o[e][i] * inv);
+        }
       }
       return;
     }
     const int64_t slot = 2 * (int64_t)wk + (first_piece ? 0 : 1);
     if (c < nh) {
       float* dst = p.part + (slot * HS + c) * D + DPL * 4 * G;
+      const float* vs = PC ? p.vs + (int64_t)(y / p.hchunks) * D + DPL * 4 * G : nullptr;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) dst[DPL * i + e] = o[e][i] * p.vsc;
+        for (int e = 0; e < DPL; ++e) dst[DPL * i + e] = o[e][i] * (PC ? vs[DPL * i + e] : p.vsc);
       if (G == 0) {
         p.ml[(slot * HS + c) * 2] = m_run;
         p.ml[(slot * HS + c) * 2 + 1] = l_tot;
@@ -220,16 +235,20 @@ void decode_stream_kernel(StreamParams p) {
       const int hc = y % p.hchunks;
       const int hk = y / p.hchunks;
       const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
-      T::load_q(qr, p.q, (int64_t)s * p.Hq + hk * p.g + hc * p.chunk_heads + c, c < nh, G);
+      if constexpr (PC)
+        T::load_q_scaled(qr, qlo, p.q, (int64_t)s * p.Hq + hk * p.g + hc * p.chunk_heads + c,
+                         c < nh, G, p.ks + (int64_t)hk * D);
+      else
+        T::load_q(qr, p.q, (int64_t)s * p.Hq + hk * p.g + hc * p.chunk_heads + c, c < nh, G);
       reset();
       const int ctx = sm_ctx[s];
       const int last = ((ctx + 15) >> 4) - 1;
       if (p.nb > 0) {
         const int64_t off = (int64_t)hk * T::TILE;
         mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
-                   !pkv::byte_codes(KVT) || PKV_NT_FP8>(p.kc + off, p.vc + off, blk_stride,
-                                        p.bt + (int64_t)s * p.mb, b, b1, last, ctx - 16 * last,
-                                        p.nb, qr, p.sl2, m_run, l_run, o, lane);
+                   !pkv::byte_codes(KVT) || PKV_NT_FP8, false, PC>(
+            p.kc + off, p.vc + off, blk_stride, p.bt + (int64_t)s * p.mb, b, b1, last,
+            ctx - 16 * last, p.nb, qr, p.sl2, m_run, l_run, o, lane, 0, qlo);
       }
       finish(s, y, b, b1 - 1, first_piece);
       first_piece = false;
@@ -370,7 +389,14 @@ __global__ __launch_bounds__(64 * kSkWaves) void decode_split_merge_kernel(Strea
 
 template <int QT, int KVT, int D>
 int launch_t(const pkv::DecodeArgs& a, const StreamParams& sp, int grid) {
-  decode_stream_kernel<QT, KVT, D>
+  if constexpr (pkv::byte_codes(KVT)) {
+    if (sp.ks) {
+      decode_stream_kernel<QT, KVT, D, true>
+          <<<dim3(grid), dim3(64 * kSkWaves), 0, (hipStream_t)a.stream>>>(sp);
+      return (int)hipGetLastError();
+    }
+  }
+  decode_stream_kernel<QT, KVT, D, false>
       <<<dim3(grid), dim3(64 * kSkWaves), 0, (hipStream_t)a.stream>>>(sp);
   return (int)hipGetLastError();
 }
@@ -411,6 +437,8 @@ StreamParams make_stream_params(const pkv::DecodeArgs& a, int grid, void* ws, si
   sp.part = reinterpret_cast<float*>(w + off_part);
   sp.W = grid * kSkWaves;
   sp.R = pkv::kv_restart_units(a.kv_dtype);
+  sp.ks = kp.ks;
+  sp.vs = kp.vs;
   return sp;
 }
 

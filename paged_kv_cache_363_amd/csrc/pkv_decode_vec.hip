@@ -69,6 +69,14 @@ __global__ __launch_bounds__(64 * pkv::kWaves) void decode_vec_kernel(DecodePara
       for (int e = 0; e < EPC; ++e) qf[h][e] = 0.f;
     }
   }
+  if (p.ks) {   // per-channel K scales: q_i * ks_i, so the codes enter as they are
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      const float ke = p.ks[(int64_t)hk * D + dim0 + e];
+#pragma unroll
+      for (int h = 0; h < GMAX; ++h) qf[h][e] *= ke;
+    }
+  }
 
   float acc[GMAX][EPC];
   float m_run[GMAX], l_run[GMAX];

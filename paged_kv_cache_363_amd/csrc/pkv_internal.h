@@ -65,6 +65,10 @@ struct DecodeArgs {
   float* ws_l;         // [S][Hq][P]
   float* ws_acc;       // [S][Hq][P][D]
   void* stream;
+  // per-channel scales of a one-byte-code cache, device float[H_kv][D] each;
+  // nullptr: k_scale / v_scale apply to the whole tensor
+  const float* k_scales = nullptr;
+  const float* v_scales = nullptr;
 };
 
 // Multi-query call: rows query_start[s] .. query_start[s+1]-1 belong to
@@ -116,7 +120,8 @@ int launch_decode_split_merge(const DecodeArgs& a, int grid, void* ws, size_t of
 int launch_cache_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
                         const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
                         int32_t head_dim, int32_t num_blocks, int32_t new_dtype, int32_t kv_dtype,
-                        float k_inv_scale, float v_inv_scale, void* stream);
+                        float k_inv_scale, float v_inv_scale, void* stream,
+                        const float* k_scales = nullptr, const float* v_scales = nullptr);
 int launch_swap_blocks(void* dst_k, void* dst_v, int32_t dst_blocks, const void* src_k,
                        const void* src_v, int32_t src_blocks, const int32_t* pairs,
                        int32_t num_pairs, int64_t block_bytes, void* stream);

@@ -178,6 +178,34 @@ struct MfmaTile {
     }
   }
 
+  // The same for a cache with per-channel K scales: q_i * ks_i in fp32, as a
+  // q-dtype head (qhi) plus its remainder (qlo), so that two MFMAs keep about
+  // 16 mantissa bits of each product.  ks: the kv-head's row of scales.
+  __device__ static void load_q_scaled(uint4* qhi, uint4* qlo, const void* q, int64_t row,
+                                       bool live, int G, const float* ks) {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(q) + row * D;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      qhi[kk] = make_uint4(0, 0, 0, 0);
+      qlo[kk] = make_uint4(0, 0, 0, 0);
+      if (live) {
+        const int d0 = qk_dim0(kk, G);
+        const uint4 raw = *reinterpret_cast<const uint4*>(qrow + d0);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = (QT == PKV_F16 ? f16_lo(w[i]) : bf16_lo(w[i])) * ks[d0 + 2 * i];
+          const float b = (QT == PKV_F16 ? f16_hi(w[i]) : bf16_hi(w[i])) * ks[d0 + 2 * i + 1];
+          hi[i] = M::pack2(a, b);
+          lo[i] = M::pack2(a - M::rounded(a), b - M::rounded(b));
+        }
+        qhi[kk] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        qlo[kk] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      }
+    }
+  }
+
   // Byte offsets of a lane's first K and V element inside a tile; the other
   // loads of the lane sit at fixed distances from them.  Unsigned 32-bit, so
   // that a load is a wave-uniform base plus one lane offset (the SGPR-base
@@ -207,9 +235,12 @@ struct MfmaTile {
   // vis <= valid: tokens of the tile this lane's column may attend to (its
   // causal limit; valid for a single query).  V rows past `valid` are zeroed,
   // rows in [vis, valid) are finite and get weight zero.
-  // qr: raw q operand (zeros for padding columns).
+  // qr: raw q operand (zeros for padding columns); PC: qlo holds the
+  // remainder of per-channel-scaled q (load_q_scaled), a second QK pass.
+  template <bool PC = false>
   __device__ static void consume(Raw& r, int valid, int vis, const uint4* qr, float sl2,
-                                 float& m_run, float& l_run, f32x4* o, int c, int G) {
+                                 float& m_run, float& l_run, f32x4* o, int c, int G,
+                                 const uint4* qlo = nullptr) {
     V8 kop[KSTEPS];
     if constexpr (BYTE) {
 #pragma unroll
@@ -238,6 +269,10 @@ struct MfmaTile {
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) sacc = M::qk(kop[kk], as_v8<V8>(qr[kk]), sacc);
+    if constexpr (PC) {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) sacc = M::qk(kop[kk], as_v8<V8>(qlo[kk]), sacc);
+    }
 
     float z[4];
 #pragma unroll
@@ -306,12 +341,13 @@ struct MfmaTile {
 // can be waited on per block instead of drained.  nb must be > 0.
 // CAUSAL: the lane's column attends to positions <= pos only (several
 // queries of one sequence in one tile); otherwise pos is ignored.
-template <int QT, int KVT, int D, int DEPTH, bool NT, bool CAUSAL = false>
+// PC: per-channel K scales, qlo the remainder of the scaled q (load_q_scaled).
+template <int QT, int KVT, int D, int DEPTH, bool NT, bool CAUSAL = false, bool PC = false>
 __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
                                            int64_t blk_stride, const int32_t* row, int b0,
                                            int b1, int last, int tail, int nb, const uint4* qr,
                                            float sl2, float& m_run, float& l_run, f32x4* o,
-                                           int lane, int pos = 0) {
+                                           int lane, int pos = 0, const uint4* qlo = nullptr) {
   using T = MfmaTile<QT, KVT, D>;
   using Raw = typename T::Raw;
   const int c = lane & 15, G = lane >> 4;
@@ -337,7 +373,7 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
         const int valid = (ii < n && (unsigned)idc[d] < (unsigned)nb)
                               ? (c0 + ii == last ? tail : 16) : 0;
         const int vis = CAUSAL ? min(valid, pos - 16 * (c0 + ii) + 1) : valid;
-        T::consume(buf[d], valid, vis, qr, sl2, m_run, l_run, o, c, G);
+        T::template consume<PC>(buf[d], valid, vis, qr, sl2, m_run, l_run, o, c, G, qlo);
         const int64_t a = addr(idn);
         T::template issue<NT>(buf[d], kc + a, vc + a, koff, voff);
         idc[d] = idn;
