@@ -9,17 +9,25 @@
 // product (lane l holds rows 4(l/16)+i, column l%16) is the B-operand layout
 // of the second one (PV computed as O^T = V^T P^T), so the softmax weights
 // stay in registers, and O^T keeps one head per lane column, which makes the
-// online-softmax rescale a per-lane multiply.  The weights enter PV as a
-// 16-bit head plus a 16-bit remainder (two MFMAs), keeping about 16 bits of
-// each weight.
+// online-softmax rescale a per-lane multiply.
 //
-// E4M3 caches are widened to the q type in registers (every E4M3 value is
-// exact in bf16 and f16); k_scale is folded into the logit scale and v_scale
-// into the final normalisation.
+// Precision of the weights in PV: with an f16 cache, or a cache of one-byte
+// codes (E4M3, INT8; f16 holds every such value exactly), PV runs in f16 and
+// each weight is rounded once to f16 (11 significant bits, relative error at
+// most 2^-11).  bf16 holds only 8 bits, so with a bf16 cache a weight enters
+// PV as a bf16 head plus a bf16 remainder (two MFMAs, about 16 bits).
+//
+// One-byte K codes are widened to the q type in registers (every E4M3 value
+// and every INT8 code is exact in bf16 and f16); k_scale is folded into the
+// logit scale and v_scale into the final normalisation.
 #pragma once
 #include <hip/hip_runtime.h>
 
 #include "pkv_decode_common.h"
+
+#ifndef PKV_ID_VGPRS
+#define PKV_ID_VGPRS 2   // block-id windows of 64 * PKV_ID_VGPRS blocks
+#endif
 
 namespace pkvd {
 
@@ -92,6 +100,15 @@ struct Mfma<PKV_F16> {
     return pack2((float)(int32_t)(int8_t)h, (float)(int32_t)(int8_t)(h >> 8));
   }
   __device__ static float rounded(float a) { return (float)(_Float16)a; }
+  // two INT8 codes (bytes 2*hi and 2*hi+1 of w) -> two f16, exact: the byte
+  // c ^ 0x80 = c + 128 becomes the low mantissa bits of f16 1024 (0x6400),
+  // and subtracting 1152 in f16 leaves c
+  __device__ static uint32_t i8x2_magic(uint32_t w, bool hi) {
+    const uint32_t x = w ^ 0x80808080u;
+    const uint32_t m = __builtin_amdgcn_perm(0x64646464u, x, hi ? 0x04030402u : 0x04010400u);
+    const f16x2 r = __builtin_bit_cast(f16x2, m) - f16x2{(_Float16)1152.0f, (_Float16)1152.0f};
+    return __builtin_bit_cast(uint32_t, r);
+  }
 };
 
 template <typename V>
@@ -151,11 +168,21 @@ struct MfmaTile {
   static constexpr int64_t TILE = 16 * D * KVB;   // bytes of one (block, kv-head) tile
   static constexpr int ROWB = DPL * KVB;          // bytes of a lane's slice of one V row
   static constexpr int KL = BYTE ? D / 64 : KSTEPS;  // 16-byte K loads per lane
+  // PV in f16 with one f16 weight (f16 and one-byte caches), else in the
+  // q type with a head + remainder pair of weights
+  static constexpr bool PVH = BYTE || KVT == PKV_F16;
+  using PM = Mfma<PVH ? PKV_F16 : QT>;
+  using P4 = typename PM::v4;
 
   // two one-byte codes (half-word `hi` of w) -> two q-dtype values, exact
   __device__ static uint32_t cvt2(uint32_t w, bool hi) {
     if constexpr (KVT == PKV_INT8) return M::i8x2(w, hi);
     else return M::fp8x2(w, hi);
+  }
+  // the same, to f16 (the PV operand)
+  __device__ static uint32_t cvt2_f16(uint32_t w, bool hi) {
+    if constexpr (KVT == PKV_INT8) return PM::i8x2_magic(w, hi);
+    else return PM::fp8x2(w, hi);
   }
 
   struct Raw {
@@ -293,13 +320,8 @@ struct MfmaTile {
 #pragma unroll
       for (int e = 0; e < DPL; ++e) o[e] *= alpha;
     }
-    // B operand of PV: k-slot (G, i) = token 4G+i, column c = head c, as a
-    // 16-bit head plus a 16-bit remainder.
-    const V4 pb = as_v4<V4>(M::pack2(pr[0], pr[1]), M::pack2(pr[2], pr[3]));
-    float lo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo[i] = pr[i] - M::rounded(pr[i]);
-    const V4 pl = as_v4<V4>(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]));
+    // B operand of PV: k-slot (G, i) = token 4G+i, column c = head c.
+    const P4 pb = as_v4<P4>(PM::pack2(pr[0], pr[1]), PM::pack2(pr[2], pr[3]));
 
     // A operand of PV for m-tile e: dim DPL*c + e of tokens 4G..4G+3.
     if constexpr (BYTE) {
@@ -309,12 +331,26 @@ struct MfmaTile {
         const uint32_t sel = (uint32_t)k | ((4u + k) << 8) | ((k + 1u) << 16) | ((5u + k) << 24);
         const uint32_t x01 = __builtin_amdgcn_perm(r.v[1].w[wi], r.v[0].w[wi], sel);
         const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
-        const V4 a0 = as_v4<V4>(cvt2(x01, false), cvt2(x23, false));
-        const V4 a1 = as_v4<V4>(cvt2(x01, true), cvt2(x23, true));
-        o[e] = M::pv(a0, pl, M::pv(a0, pb, o[e]));
-        o[e + 1] = M::pv(a1, pl, M::pv(a1, pb, o[e + 1]));
+        const P4 a0 = as_v4<P4>(cvt2_f16(x01, false), cvt2_f16(x23, false));
+        const P4 a1 = as_v4<P4>(cvt2_f16(x01, true), cvt2_f16(x23, true));
+        o[e] = PM::pv(a0, pb, o[e]);
+        o[e + 1] = PM::pv(a1, pb, o[e + 1]);
+      }
+    } else if constexpr (PVH) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const int wi = e / 2;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint32_t x01 = __builtin_amdgcn_perm(r.v[1].w[wi], r.v[0].w[wi], sel);
+        const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
+        o[e] = PM::pv(as_v4<P4>(x01, x23), pb, o[e]);
       }
     } else {
+      // bf16: the weight as a bf16 head plus its bf16 remainder
+      float lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo[i] = pr[i] - M::rounded(pr[i]);
+      const V4 pl = as_v4<V4>(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]));
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
         const int wi = e / 2;
@@ -334,8 +370,11 @@ struct MfmaTile {
 //   kc, vc   : the caches, already offset to the segment's kv-head tile
 //   row      : the sequence's block-table row
 //   last     : index of the sequence's last block, tail its token count
-// Block ids come 64 at a time, one per lane of a VGPR, and are read back with
-// readlane.  K/V loads run DEPTH blocks ahead of the block being consumed.
+// Block ids come 64 * PKV_ID_VGPRS at a time, one per lane of each of
+// PKV_ID_VGPRS VGPRs, and are read back with readlane: a window boundary
+// stalls the loads (the next window's ids must arrive first), so windows are
+// wider than most pieces.  K/V loads run DEPTH blocks ahead of the block being
+// consumed.
 // Every load is issued unconditionally (ids past the chunk repeat its last
 // block, invalid ids read block 0 and carry no weight), so the load counter
 // can be waited on per block instead of drained.  nb must be > 0.
@@ -352,10 +391,22 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
   using Raw = typename T::Raw;
   const int c = lane & 15, G = lane >> 4;
   const uint32_t koff = T::k_lane_off(c, G), voff = T::v_lane_off(c, G);
-  for (int c0 = b0; c0 < b1; c0 += 64) {
-    const int n = min(64, b1 - c0);
-    const int ids = lane < n ? row[c0 + lane] : 0;
-    auto id_at = [&](int i) { return __builtin_amdgcn_readlane(ids, i < n ? i : n - 1); };
+  constexpr int NW = PKV_ID_VGPRS;
+  for (int c0 = b0; c0 < b1; c0 += 64 * NW) {
+    const int n = min(64 * NW, b1 - c0);
+    int ids[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) ids[w] = row[c0 + min(64 * w + lane, n - 1)];   // in bounds
+    auto id_at = [&](int i) {
+      const int k = i < n ? i : n - 1;
+      int v = __builtin_amdgcn_readlane(ids[0], k & 63);
+#pragma unroll
+      for (int w = 1; w < NW; ++w) {
+        const int vw = __builtin_amdgcn_readlane(ids[w], k & 63);
+        v = (k >> 6) == w ? vw : v;
+      }
+      return v;
+    };
     auto addr = [&](int id) { return (int64_t)((unsigned)id < (unsigned)nb ? id : 0) * blk_stride; };
     Raw buf[DEPTH];
     int idc[DEPTH];
