@@ -83,10 +83,10 @@ const char* pkv_status_string(int32_t status);
 /* Library version: major*10000 + minor*100 + patch. */
 int32_t pkv_version(void);
 
-/* Workgroups (of 4 waves) the balanced decode schedule launches; 0 restores
- * the default (256: one wave on every SIMD of a 256-CU MI355X).
- * Process-wide; it changes what pkv_decode_workspace_size returns, so set it
- * before sizing workspaces. */
+/* Workgroups (of 4 waves) the balanced decode and multi-query schedules
+ * launch; 0 restores the default (256: one wave on every SIMD of a 256-CU
+ * MI355X).  Process-wide; it changes what pkv_decode_workspace_size and
+ * pkv_multiquery_workspace_size return, so set it before sizing workspaces. */
 pkv_status pkv_set_stream_workgroups(int32_t n);
 
 /* --------------------------------------------------------------- sizes -- */
@@ -294,11 +294,20 @@ pkv_status pkv_paged_decode_attention_per_channel(
  *                  v_scale as for decode.  Rows with n > context_lens[s]
  *                  whose position is negative get zeros.
  *   partition_size: 0 = pkv_multiquery_partition_size's choice, else a
- *                  multiple of 16; with more than one partition the call
- *                  needs a 256-byte-aligned workspace of
- *                  pkv_multiquery_workspace_size bytes and runs a reduction.
+ *                  multiple of 16 (fixed partitions).  With more than one
+ *                  partition, or with the balanced schedule, the call needs
+ *                  a 256-byte-aligned workspace of
+ *                  pkv_multiquery_workspace_size bytes and runs a second,
+ *                  merging kernel.
  * Runs on the matrix cores: 16 MFMA columns are 16 / min(g, 16) rows times
- * min(g, 16) q-heads of one kv-head.  Errors as for decode; PKV_ERR_UNSUPPORTED
+ * min(g, 16) q-heads of one kv-head.  The balanced schedule splits the
+ * blocks that every (sequence, row tile, kv-head) must read into equal
+ * shares of a persistent grid, as the balanced decode schedule does, so
+ * ragged contexts leave no CU idle.  partition_size 0 takes it when one
+ * workgroup per (sequence, kv-head chunk, row tile) would give fewer than
+ * 2048 workgroups, num_seqs <= 2048 and num_seqs x ceil(max_query_len /
+ * rows per tile) <= 4096 (draft verification of a few rows); otherwise the
+ * fixed grid runs.  Errors as for decode; PKV_ERR_UNSUPPORTED
  * for f32 q, head_dim not in {64, 128}, or a grid beyond 65535 sequences,
  * 65535 kv-heads x row tiles or 2^31 rows x q-heads. */
 pkv_status pkv_paged_multiquery_attention(
@@ -319,16 +328,20 @@ pkv_status pkv_paged_multiquery_attention_profiled(
     int32_t max_blocks_per_seq, float scale, int32_t q_dtype, int32_t kv_dtype, float k_scale,
     float v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
     void* stream, void* ev_begin, void* ev_mid, void* ev_end);
-/* Partition (tokens) a multi-query call with partition_size 0 uses: one pass
- * over max_blocks_per_seq * 16 tokens when the sequences x kv-heads x row
- * tiles reach 2048 workgroups, else 512 to 128 tokens.  partition_size > 0 is
- * returned as is.  -1 on bad arguments. */
+/* Partition (tokens) a multi-query call with partition_size 0 uses: 0 for
+ * the balanced schedule (see pkv_paged_multiquery_attention); otherwise one
+ * pass over max_blocks_per_seq * 16 tokens when the sequences x kv-heads x
+ * row tiles reach 2048 workgroups, else 512 to 128 tokens.  partition_size
+ * > 0 is returned as is.  -1 on bad arguments. */
 int32_t pkv_multiquery_partition_size(int32_t num_seqs, int32_t max_query_len,
                                       int32_t num_q_heads, int32_t num_kv_heads,
                                       int32_t max_blocks_per_seq, int32_t partition_size);
-/* Workspace bytes of a multi-query call (0 for one partition): float
- * m[rows][H_q][P], l[rows][H_q][P], acc[rows][H_q][P][head_dim], each part
- * 256-byte aligned.  SIZE_MAX on bad arguments. */
+/* Workspace bytes of a multi-query call.  Balanced schedule: float
+ * (m, l)[2 W][16][2] and acc[2 W][16][head_dim] for the W = 4 x
+ * pkv_set_stream_workgroups waves of its grid (two partial slots per wave),
+ * each part 256-byte aligned.  Fixed partitions: 0 for one partition, else
+ * float m[rows][H_q][P], l[rows][H_q][P], acc[rows][H_q][P][head_dim], each
+ * part 256-byte aligned.  SIZE_MAX on bad arguments. */
 size_t pkv_multiquery_workspace_size(int32_t num_rows, int32_t num_seqs, int32_t max_query_len,
                                      int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t max_blocks_per_seq,

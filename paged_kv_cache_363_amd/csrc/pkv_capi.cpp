@@ -134,8 +134,11 @@ static bool make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
 // Multi-query calls
 
 struct MQPlan {
-  int32_t partition, num_parts;
+  int32_t partition, num_parts;   // partition 0: the balanced schedule
   size_t off_l, off_acc, ws_bytes;
+  bool stream;                     // balanced schedule (partition_size 0)
+  int32_t stream_grid;
+  size_t st_off_part;              // the (m, l) slots start the workspace
 };
 
 // Partition and workspace of a multi-query call; false on bad arguments.
@@ -150,6 +153,33 @@ bool mq_plan(int32_t num_rows, int32_t num_seqs, int32_t max_query_len, int32_t 
     return false;
   const int32_t max_ctx = max_blocks_per_seq * kBlockSize;
   const MQTiles t = mq_tiles(num_q_heads / num_kv_heads, max_query_len > 0 ? max_query_len : 1);
+  // Balanced schedule: partition_size 0 and a fixed grid of one workgroup
+  // per (sequence, kv-head chunk, row tile) too small to fill the chip (the
+  // same 2048 as choose_partition: below it the fixed path would cut the
+  // contexts into partitions), while the sequences and their row tiles fit
+  // the in-LDS prefix sums and the unit count stays below 2^31 (at the
+  // largest restart count).  Measured: draft verification of 4 and 8 rows
+  // gains; long prompt chunks, whose fixed grid is large and whose tiles are
+  // compute-bound, run faster on the fixed grid with its higher occupancy.
+  const int64_t Y = (int64_t)num_kv_heads * t.hchunks;
+  const int64_t tiles = (int64_t)num_seqs * t.qtiles;
+  const int64_t r_max = kv_restart_units(PKV_BF16) > kv_restart_units(PKV_FP8_E4M3)
+                            ? kv_restart_units(PKV_BF16)
+                            : kv_restart_units(PKV_FP8_E4M3);
+  plan->stream = partition_size == 0 && tiles * Y < 2048 && num_seqs <= kMaxStreamSeqs &&
+                 tiles <= kMaxStreamTiles &&
+                 tiles * (max_blocks_per_seq + r_max) * Y < ((int64_t)1 << 31);
+  plan->stream_grid = g_stream_workgroups.load();
+  plan->st_off_part = 0;
+  if (plan->stream) {
+    const size_t workers = (size_t)plan->stream_grid * kWaves;
+    plan->partition = 0;
+    plan->num_parts = 1;
+    plan->off_l = plan->off_acc = 0;
+    plan->st_off_part = align256(2 * workers * 16 * 2 * sizeof(float));
+    plan->ws_bytes = plan->st_off_part + align256(2 * workers * 16 * head_dim * sizeof(float));
+    return true;
+  }
   // workgroups per sequence and partition: kv-heads x head chunks x row tiles
   const int64_t per_seq = (int64_t)num_kv_heads * t.hchunks * t.qtiles;
   const int32_t ps = partition_size > 0
@@ -607,8 +637,11 @@ pkv_status pkv_paged_multiquery_attention_profiled(
     return fail(PKV_ERR_INVALID_ARG,
                 "multiquery: partition_size must be 0 or a multiple of 16 <= %d", kMaxPartition);
   const MQTiles t = mq_tiles(num_q_heads / num_kv_heads, max_query_len > 0 ? max_query_len : 1);
-  if (num_seqs > 65535 || (int64_t)num_kv_heads * t.hchunks * t.qtiles > 65535 ||
-      (int64_t)num_rows * num_q_heads > INT32_MAX || plan.num_parts > 65535)
+  if (!plan.stream && (num_seqs > 65535 || (int64_t)num_kv_heads * t.hchunks * t.qtiles > 65535 ||
+                      plan.num_parts > 65535))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "multiquery: grid too large (sequences, kv-heads x row tiles, rows x q-heads)");
+  if ((int64_t)num_rows * num_q_heads > INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED,
                 "multiquery: grid too large (sequences, kv-heads x row tiles, rows x q-heads)");
   if (num_seqs == 0 || num_rows == 0 || max_query_len == 0) return PKV_OK;
@@ -650,10 +683,27 @@ pkv_status pkv_paged_multiquery_attention_profiled(
   a.ws_m = plan.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_l = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
   a.ws_acc = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_acc) : nullptr;
+  a.stream_grid = plan.stream_grid;
+  a.st_ml = plan.stream ? reinterpret_cast<float*>(ws) : nullptr;
+  a.st_part = plan.stream ? reinterpret_cast<float*>(ws + plan.st_off_part) : nullptr;
   a.stream = stream;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), hs) != hipSuccess)
     return fail(PKV_ERR_HIP, "multiquery: hipEventRecord failed");
+  if (plan.stream) {
+    int rc = launch_multiquery_stream(a);
+    if (rc != 0)
+      return fail(PKV_ERR_HIP, "multiquery: launch failed: %s", hipGetErrorString((hipError_t)rc));
+    if (ev_mid && hipEventRecord(static_cast<hipEvent_t>(ev_mid), hs) != hipSuccess)
+      return fail(PKV_ERR_HIP, "multiquery: hipEventRecord failed");
+    rc = launch_multiquery_split_merge(a);
+    if (rc != 0)
+      return fail(PKV_ERR_HIP, "multiquery: merge launch failed: %s",
+                  hipGetErrorString((hipError_t)rc));
+    if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), hs) != hipSuccess)
+      return fail(PKV_ERR_HIP, "multiquery: hipEventRecord failed");
+    return PKV_OK;
+  }
   int rc = launch_multiquery(a);
   if (rc != 0)
     return fail(PKV_ERR_HIP, "multiquery: launch failed: %s", hipGetErrorString((hipError_t)rc));

@@ -40,7 +40,8 @@ void decode_mfma_kernel(DecodeParams p) {
   __shared__ float sm_l[pkv::kWaves * HS];
   __shared__ float sm_o[pkv::kWaves * HS * LD];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int c = lane & 15, G = lane >> 4;
   const int part = blockIdx.x, s = blockIdx.z;
   const int hk = blockIdx.y / p.hchunks, hc = blockIdx.y % p.hchunks;

@@ -26,7 +26,7 @@
 // ("KV Cache 与 PageAttention深度实战", sections 1.2 and 3.2).
 #include <hip/hip_runtime.h>
 
-#include "pkv_mfma_common.h"
+#include "pkv_stream_common.h"
 
 #ifndef PKV_PIPE_DEPTH
 #define PKV_PIPE_DEPTH 2       // K/V blocks in flight per wave, 16-bit caches
@@ -60,16 +60,6 @@ struct StreamParams {
   const float* ks;             // per-channel K scales [Hkv][D] (nullptr: per tensor)
   const float* vs;             // per-channel V scales [Hkv][D]
 };
-
-// floor(n / c) for 0 <= n < 2^53 and c >= 1.  n and c are exact in double,
-// and a correctly rounded quotient cannot reach an integer that the exact
-// quotient lies below (that would take n >= 2^53), so truncation gives the
-// floor.  Far cheaper on the GPU than 64-bit integer division, which expands
-// into a long VALU sequence.  Every share boundary goes through here, in the
-// decode and the merge kernel alike.
-__device__ __forceinline__ int64_t floor_div53(int64_t n, int64_t c) {
-  return (int64_t)((double)n / (double)c);
-}
 
 // Unit prefix sums in LDS, computed by one workgroup of 4 waves.  A segment
 // of a sequence with nbk blocks spans nbk + R units: R units that stand for
@@ -269,21 +259,18 @@ void decode_stream_kernel(StreamParams p) {
 // waves.  One wave per (segment, q-head of the segment); segments kept whole
 // by one wave were already stored by it.  The shares are recomputed exactly
 // as the decode kernel computed them: worker k owns units
-// [U k / We, U (k+1) / We).  Lane j holds piece j's (m, l) and weight; the
-// accumulator rows of all pieces are then read with independent loads.
+// [U k / We, U (k+1) / We).
 template <int QT, int D>
 __global__ __launch_bounds__(64 * kSkWaves) void decode_split_merge_kernel(StreamParams p) {
   __shared__ int sm_pref[pkv::kMaxStreamSeqs + 1];
   __shared__ int sm_ctx[pkv::kMaxStreamSeqs];
   block_prefix(p, sm_pref, sm_ctx);
-  const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int64_t Y = p.Y;
   const int64_t U = Y * sm_pref[p.S];
   const int64_t We = U < p.W ? U : p.W;
   if (We == 0) return;
   const int HS = p.chunk_heads;
-  constexpr int PER = (D + 63) / 64;
   const int64_t nitems = (int64_t)p.S * Y * HS;
   for (int64_t it = (int64_t)blockIdx.x * kSkWaves + w; it < nitems;
        it += (int64_t)gridDim.x * kSkWaves) {
@@ -303,87 +290,9 @@ __global__ __launch_bounds__(64 * kSkWaves) void decode_split_merge_kernel(Strea
     // the first worker's piece is its first piece with blocks unless its
     // share holds blocks of the segment before (units below seg_start)
     const int64_t sl0 = 2 * wa + (floor_div53(U * wa, We) >= seg_start ? 0 : 1);
-    const int np = (int)(wb - wa + 1);
-    auto slot_of = [&](int k) { return k == 0 ? sl0 : 2 * (wa + k); };
-    auto ml_of = [&](int k) {
-      return *reinterpret_cast<const float2*>(p.ml + (slot_of(k) * HS + h) * 2);
-    };
-    // Accumulator rows of pieces base+j0 .. base+j0+7 (the last valid piece
-    // repeated past cnt; its weight is zero there).
-    auto load_rows = [&](float (&x)[8][PER], int base, int j0, int cnt) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t sl = slot_of(base + min(j0 + u, cnt - 1));
-#pragma unroll
-        for (int k2 = 0; k2 < PER; ++k2) {
-          const int d = lane + 64 * k2;
-          x[u][k2] = d < D ? p.part[(sl * HS + h) * D + d] : 0.f;
-        }
-      }
-    };
-    float acc[PER];
-#pragma unroll
-    for (int k2 = 0; k2 < PER; ++k2) acc[k2] = 0.f;
-    auto add_rows = [&](const float (&x)[8][PER], float wgt, int j0, int cnt) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wj = __int_as_float(
-            __builtin_amdgcn_readlane(__float_as_int(wgt), min(j0 + u, 63)));
-        const float wu = (j0 + u < cnt) ? wj : 0.f;
-#pragma unroll
-        for (int k2 = 0; k2 < PER; ++k2) acc[k2] = fmaf(wu, x[u][k2], acc[k2]);
-      }
-    };
-    // Lane k holds piece k's (m, l).  Those and the first eight accumulator
-    // rows go out together: none depends on another, so the merge of a
-    // segment split over at most eight workers waits on memory once.
-    const int cnt0 = min(64, np);
-    float x0[8][PER];
-    load_rows(x0, 0, 0, cnt0);
-    float m0 = kNegInf, l0 = 0.f;
-    if (lane < np) {
-      const float2 v = ml_of(lane);
-      m0 = v.x;
-      l0 = v.y;
-    }
-    float M = l0 > 0.f ? m0 : kNegInf;
-    for (int k = lane + 64; k < np; k += 64) {
-      const float2 v = ml_of(k);
-      if (v.y > 0.f) M = fmaxf(M, v.x);
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float L = 0.f;
-    if (M != kNegInf) {
-      for (int base = 0; base < np; base += 64) {
-        float wgt = 0.f;
-        if (base + lane < np) {
-          const float2 v = base == 0 ? make_float2(m0, l0) : ml_of(base + lane);
-          wgt = v.y > 0.f ? __builtin_amdgcn_exp2f(v.x - M) : 0.f;
-          L += wgt * v.y;
-        }
-        const int cnt = min(64, np - base);
-        int j0 = 0;
-        if (base == 0) {
-          add_rows(x0, wgt, 0, cnt);
-          j0 = 8;
-        }
-        for (; j0 < cnt; j0 += 8) {
-          float x[8][PER];
-          load_rows(x, base, j0, cnt);
-          add_rows(x, wgt, j0, cnt);
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off);
     const int h_first = (y / p.hchunks) * p.g + hc * p.chunk_heads;
     const int64_t row = (int64_t)s * p.Hq + h_first + h;
-#pragma unroll
-    for (int k2 = 0; k2 < PER; ++k2) {
-      const int d = lane + 64 * k2;
-      if (d < D) store_out<QT>(p.out, row * D + d, L > 0.f ? acc[k2] / L : 0.f);
-    }
+    merge_split_column<QT, D>(p.part, p.ml, HS, h, wa, wb, sl0, p.out, row * D);
   }
 }
 

@@ -31,6 +31,7 @@ constexpr int kWaves = 4;        // waves per decode workgroup
 constexpr int kMaxPartition = 1 << 20;
 constexpr int kMaxStreamSeqs = 2048;        // sequences the balanced schedule handles per call
 constexpr int kDefaultStreamWorkgroups = 256;  // one wave per SIMD of a 256-CU MI355X
+constexpr int kMaxStreamTiles = 4096;        // (sequence, row tile) pairs of a balanced multi-query call
 
 // Units the balanced schedule charges for starting a piece of a segment, in
 // blocks: a start costs about two loaded HBM round trips (q rows and block
@@ -90,6 +91,10 @@ struct MQArgs {
   float* ws_m;         // [rows][Hq][P]
   float* ws_l;         // [rows][Hq][P]
   float* ws_acc;       // [rows][Hq][P][D]
+  // balanced schedule (launch_multiquery_stream): workers and partial slots
+  int32_t stream_grid;  // workgroups of 4 waves
+  float* st_ml;         // [2 W][16][2]
+  float* st_part;       // [2 W][16][D]
   void* stream;
 };
 
@@ -111,6 +116,8 @@ inline MQTiles mq_tiles(int g, int max_query_len) {
 // Kernel launchers (return hipError_t as int).
 int launch_multiquery(const MQArgs& a);
 int launch_multiquery_reduce(const MQArgs& a);
+int launch_multiquery_stream(const MQArgs& a);
+int launch_multiquery_split_merge(const MQArgs& a);
 int launch_decode_vector(const DecodeArgs& a);
 int launch_decode_mfma(const DecodeArgs& a);
 int launch_decode_reduce(const DecodeArgs& a);

@@ -18,9 +18,13 @@
 // quarters of them and merge in LDS.  With several partitions each workgroup
 // writes (m, l, acc) partials, an empty partition writing m = -inf, l = 0, and
 // multiquery_reduce_kernel merges every row's partitions by log-sum-exp.
+//
+// With partition_size 0 the work-balanced schedule runs instead
+// (multiquery_stream_kernel, then multiquery_split_merge_kernel): ragged
+// contexts leave no CU idle at the end of the call.
 #include <hip/hip_runtime.h>
 
-#include "pkv_mfma_common.h"
+#include "pkv_stream_common.h"
 
 #ifndef PKV_PIPE_DEPTH
 #define PKV_PIPE_DEPTH 2       // K/V blocks in flight per wave, 16-bit caches
@@ -237,6 +241,346 @@ __global__ __launch_bounds__(64) void multiquery_reduce_kernel(MQParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Work-balanced schedule.  As in the balanced decode kernel, the call's work
+// is flattened into units and a persistent grid of waves takes equal
+// contiguous shares of them.  A tile is one row tile (qpt rows) of one
+// sequence; it has Y = kv-heads x head chunks segments, each of nbk + R
+// units: R restart units (the cost of starting a piece) and one unit per
+// 16-token block its last row can see.  Tiles follow each other in
+// (sequence, row tile) order; the prefix sums of their units sit in LDS, and
+// both kernels derive every share from them.
+
+struct MQStreamParams {
+  MQParams b;
+  int Y;         // segments per tile: kv-heads x head chunks
+  int W;         // waves of the grid
+  int R;         // restart units at the start of every segment
+  float* ml;     // [2 W][16][2]
+  float* part;   // [2 W][16][D]
+};
+
+struct MQStreamSmem {
+  int pref[pkv::kMaxStreamTiles + 1];      // units of one segment of each tile before tile t
+  int tb[pkv::kMaxStreamSeqs + 1];         // first tile of sequence s
+  int ctx[pkv::kMaxStreamSeqs];            // clamped context lengths
+  int r0[pkv::kMaxStreamSeqs];             // first row of sequence s
+  int n[pkv::kMaxStreamSeqs];              // rows of sequence s (clamped, <= max_q)
+  uint16_t tseq[pkv::kMaxStreamTiles];     // sequence of tile t
+};
+
+// 16-token blocks the last row of row tile qt of a sequence (ctx tokens, n
+// rows) can see; 0 when every row of the tile sits before position 0.
+__device__ __forceinline__ int mq_tile_blocks(const MQParams& p, int ctx, int n, int qt) {
+  const int p_last = ctx - n + min(qt * p.qpt + p.qpt, n) - 1;
+  return p_last >= 0 ? (p_last >> 4) + 1 : 0;
+}
+
+// Inclusive scan of x over the lanes of one wave.
+__device__ __forceinline__ int wave_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Sequence data, tile bases and the unit prefix sums in LDS, computed by the
+// whole workgroup.  The host bounds the sequences by kMaxStreamSeqs and the
+// tiles (sequences x row tiles of max_query_len rows) by kMaxStreamTiles.
+__device__ void mq_tile_prefix(const MQStreamParams& sp, MQStreamSmem& sm) {
+  const MQParams& p = sp.b;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int S = p.S;
+  const int cap = p.mb * pkv::kBlockSize;
+  for (int i = threadIdx.x; i < S; i += 64 * pkv::kWaves) {
+    const int c = p.cl[i];
+    sm.ctx[i] = c < 0 ? 0 : (c > cap ? cap : c);
+    int r0, n;
+    seq_rows(p, i, r0, n);
+    sm.r0[i] = r0;
+    sm.n[i] = n;
+  }
+  __syncthreads();
+  if (w == 0) {
+    int carry = 0;
+    for (int base = 0; base < S; base += 64) {
+      const int i = base + lane;
+      const int x = wave_scan(i < S ? (sm.n[i] + p.qpt - 1) / p.qpt : 0, lane);
+      if (i < S) sm.tb[i + 1] = carry + x;
+      carry += __shfl(x, 63);
+    }
+    if (lane == 0) sm.tb[0] = 0;
+  }
+  __syncthreads();
+  // each tile's units, stored one place up for the in-place scan below
+  if (p.qtiles > 16) {
+    // long prompt chunks: a wave per sequence, its lanes over the row tiles
+    for (int i = w; i < S; i += pkv::kWaves) {
+      const int t0 = sm.tb[i], nt = sm.tb[i + 1] - t0;
+      for (int qt = lane; qt < nt; qt += 64) {
+        const int nbk = mq_tile_blocks(p, sm.ctx[i], sm.n[i], qt);
+        sm.tseq[t0 + qt] = (uint16_t)i;
+        sm.pref[t0 + qt + 1] = nbk > 0 ? nbk + sp.R : 0;
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < S; i += 64 * pkv::kWaves) {
+      const int t0 = sm.tb[i], nt = sm.tb[i + 1] - t0;
+      for (int qt = 0; qt < nt; ++qt) {
+        const int nbk = mq_tile_blocks(p, sm.ctx[i], sm.n[i], qt);
+        sm.tseq[t0 + qt] = (uint16_t)i;
+        sm.pref[t0 + qt + 1] = nbk > 0 ? nbk + sp.R : 0;
+      }
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int T = sm.tb[S];
+    int carry = 0;
+    for (int base = 0; base < T; base += 64) {
+      const int t = base + lane;
+      const int x = wave_scan(t < T ? sm.pref[t + 1] : 0, lane);
+      if (t < T) sm.pref[t + 1] = carry + x;
+      carry += __shfl(x, 63);
+    }
+    if (lane == 0) sm.pref[0] = 0;
+  }
+  __syncthreads();
+}
+
+// One wave per worker.  A share covers the tail of one segment, whole
+// segments and the head of another; a whole segment is normalised and stored
+// by its wave, a piece of a split segment goes to the wave's partial slot
+// (its first piece in slot 2 wk, its last in slot 2 wk + 1).
+template <int QT, int KVT, int D>
+__global__ __launch_bounds__(64 * pkv::kWaves) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void multiquery_stream_kernel(MQStreamParams sp) {
+  using T = MfmaTile<QT, KVT, D>;
+  constexpr int DPL = T::DPL;
+  __shared__ MQStreamSmem sm;
+  const MQParams& p = sp.b;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+  const int c = lane & 15, G = lane >> 4;
+  mq_tile_prefix(sp, sm);
+  const int Tn = sm.tb[p.S];
+  const int64_t Y = sp.Y;
+  const int64_t U = Y * sm.pref[Tn];
+  const int W = sp.W;
+  const int wk = blockIdx.x * pkv::kWaves + w;
+
+  // the rows of a tile that sees no block attend to nothing: zeros
+  for (int t = wk; t < Tn; t += W) {
+    if (sm.pref[t + 1] != sm.pref[t]) continue;
+    const int s = sm.tseq[t];
+    const int i0 = (t - sm.tb[s]) * p.qpt, i1 = min(i0 + p.qpt, sm.n[s]);
+    const int64_t base = (int64_t)(sm.r0[s] + i0) * p.Hq * D;
+    const int64_t cnt = (int64_t)(i1 - i0) * p.Hq * D;
+    for (int64_t i = lane; i < cnt; i += 64) store_out<QT>(p.out, base + i, 0.f);
+  }
+
+  const int64_t We = U < W ? U : W;   // workers with a non-empty share
+  if (wk >= We) return;
+  const int64_t u_lo = floor_div53(U * wk, We), u_hi = floor_div53(U * (wk + 1), We);
+
+  // unit u -> (tile t, segment y, position j in the segment's units): t is
+  // the last tile whose first unit is <= u (tiles without blocks own no
+  // unit); a 64-way search over the non-decreasing prefix sums.
+  auto locate = [&](int64_t u, int& t, int& y, int& j) {
+    int lo = 0, span = Tn;   // Y * pref[lo] <= u
+    while (span > 1) {
+      const int step = (span + 63) >> 6;
+      const int i = lo + lane * step;
+      const bool ok = lane * step < span && Y * sm.pref[i] <= u;
+      const int cnt = __popcll(__ballot(ok));
+      lo += (cnt - 1) * step;
+      span = min(step, span - (cnt - 1) * step);
+    }
+    t = lo;
+    // U < 2^31 (checked by the host), so 32-bit division suffices
+    const uint32_t len = (uint32_t)(sm.pref[t + 1] - sm.pref[t]);
+    const uint32_t r = (uint32_t)(u - Y * sm.pref[t]);
+    y = (int)(r / len);
+    j = (int)(r - (uint32_t)y * len);
+  };
+
+  const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
+  uint4 qr[T::KSTEPS];
+  f32x4 o[DPL];
+  float m_run, l_run;
+
+  int64_t u = u_lo;
+  int t, y, j;
+  locate(u, t, y, j);
+  int s = sm.tseq[t];
+  bool first_piece = true;
+  while (true) {
+    const int len = sm.pref[t + 1] - sm.pref[t];
+    const int64_t seg_start = Y * sm.pref[t] + (int64_t)y * len;
+    const int64_t pe = seg_start + len < u_hi ? seg_start + len : u_hi;
+    const int b = max(j - sp.R, 0);
+    const int b1 = max((int)(pe - seg_start) - sp.R, 0);
+    if (b1 > b) {
+      const int hc = y % p.hchunks, hk = y / p.hchunks;
+      const int n = sm.n[s], ctx = sm.ctx[s], r0 = sm.r0[s];
+      // this lane's column: row iq of the sequence, q-head h of the kv-head
+      const int iq = (t - sm.tb[s]) * p.qpt + c / p.chunk;
+      const int h = hc * p.chunk + c % p.chunk;
+      const bool live = c < p.qpt * p.chunk && iq < n && h < p.g;
+      const int pos = live ? ctx - n + iq : -1;   // < 0: the column attends to nothing
+      T::load_q(qr, p.q, (int64_t)(r0 + iq) * p.Hq + hk * p.g + h, live, G);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run = kNegInf;
+      l_run = 0.f;
+      const int last = ((ctx + 15) >> 4) - 1;
+      if (p.nb > 0) {
+        const int64_t off = (int64_t)hk * T::TILE;
+        mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
+                   !pkv::byte_codes(KVT), true>(
+            p.kc + off, p.vc + off, blk_stride, p.bt + (int64_t)s * p.mb, b, b1, last,
+            ctx - 16 * last, p.nb, qr, p.sl2, m_run, l_run, o, lane, pos);
+      }
+      // close the piece: store the rows, or leave (m, l, acc) for the merge
+      const float l_tot = wave_sum4(l_run);
+      if (b == 0 && b1 == len - sp.R) {
+        if (live) {
+          const int64_t row = ((int64_t)(r0 + iq) * p.Hq + hk * p.g + h) * D + DPL * 4 * G;
+          const float inv = l_tot > 0.f ? p.vsc / l_tot : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) store_out<QT>(p.out, row + DPL * i + e, o[e][i] * inv);
+        }
+      } else if (live) {
+        const int64_t slot = 2 * (int64_t)wk + (first_piece ? 0 : 1);
+        float* dst = sp.part + (slot * kCols + c) * D + DPL * 4 * G;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) dst[DPL * i + e] = o[e][i] * p.vsc;
+        if (G == 0) {
+          sp.ml[(slot * kCols + c) * 2] = m_run;
+          sp.ml[(slot * kCols + c) * 2 + 1] = l_tot;
+        }
+      }
+      first_piece = false;
+    }
+    u = pe;
+    if (u >= u_hi) break;
+    j = 0;
+    if (++y == Y) {
+      y = 0;
+      do {
+        ++t;
+      } while (sm.pref[t + 1] == sm.pref[t]);
+      s = sm.tseq[t];
+    }
+  }
+}
+
+// Merge the pieces of every segment the grid above split between waves, the
+// shares recomputed exactly as there.  One wave per split segment: lane l
+// takes column l / 4 of the tile and a quarter of its dims, and folds the
+// pieces in order with the running log-sum-exp rescale, the loads of piece
+// k + 1 in flight while piece k is added.
+template <int QT, int D>
+__global__ __launch_bounds__(64 * pkv::kWaves) void multiquery_split_merge_kernel(
+    MQStreamParams sp) {
+  constexpr int DQ = D / 4;    // dims per lane
+  constexpr int NV = DQ / 4;   // float4 loads per lane and piece
+  __shared__ MQStreamSmem sm;
+  mq_tile_prefix(sp, sm);
+  const MQParams& p = sp.b;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+  const int cc = lane >> 2, d0 = (lane & 3) * DQ;
+  const int Tn = sm.tb[p.S];
+  const int64_t Y = sp.Y;
+  const int64_t U = Y * sm.pref[Tn];
+  const int64_t We = U < sp.W ? U : sp.W;
+  if (We == 0) return;
+  const int64_t nsegs = (int64_t)Tn * Y;
+  for (int64_t seg = (int64_t)blockIdx.x * pkv::kWaves + w; seg < nsegs;
+       seg += (int64_t)gridDim.x * pkv::kWaves) {
+    const int t = (int)(seg / Y), y = (int)(seg % Y);
+    const int len = sm.pref[t + 1] - sm.pref[t];
+    if (len == 0) continue;
+    // the segment's blocks are its units [seg_start + R, seg_start + len)
+    const int64_t seg_start = Y * sm.pref[t] + (int64_t)y * len;
+    const int64_t wa = floor_div53((seg_start + sp.R + 1) * We - 1, U);
+    const int64_t wb = floor_div53((seg_start + len) * We - 1, U);
+    if (wa == wb) continue;
+    // the first worker's piece is its first piece with blocks unless its
+    // share holds blocks of the segment before (units below seg_start)
+    const int64_t sl0 = 2 * wa + (floor_div53(U * wa, We) >= seg_start ? 0 : 1);
+    const int np = (int)(wb - wa + 1);
+    const int s = sm.tseq[t];
+    const int hc = y % p.hchunks, hk = y / p.hchunks;
+    const int iq = (t - sm.tb[s]) * p.qpt + cc / p.chunk;
+    const int h = hc * p.chunk + cc % p.chunk;
+    const bool live = cc < p.qpt * p.chunk && iq < sm.n[s] && h < p.g;
+    auto slot_of = [&](int k) { return k == 0 ? sl0 : 2 * (wa + k); };
+    // (m, l) and this lane's accumulator dims of piece k (zeros for a dead
+    // column, which never reads)
+    auto load_piece = [&](int k, float2& v, float4 (&x)[NV]) {
+      const int64_t sl = slot_of(k) * kCols + cc;
+      v = make_float2(kNegInf, 0.f);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (live) {
+        v = *reinterpret_cast<const float2*>(sp.ml + sl * 2);
+        const float4* src = reinterpret_cast<const float4*>(sp.part + sl * D + d0);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) x[i] = src[i];
+      }
+    };
+    float M = kNegInf, L = 0.f;
+    float4 acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    float2 v_cur;
+    float4 x_cur[NV];
+    load_piece(0, v_cur, x_cur);
+    for (int k = 0; k < np; ++k) {
+      float2 v_nxt;
+      float4 x_nxt[NV];
+      load_piece(k + 1 < np ? k + 1 : k, v_nxt, x_nxt);
+      if (v_cur.y > 0.f) {
+        const float Mn = fmaxf(M, v_cur.x);
+        const float a = __builtin_amdgcn_exp2f(M - Mn);   // 0 while M = -inf
+        const float b = __builtin_amdgcn_exp2f(v_cur.x - Mn);
+        L = L * a + v_cur.y * b;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          acc[i].x = acc[i].x * a + x_cur[i].x * b;
+          acc[i].y = acc[i].y * a + x_cur[i].y * b;
+          acc[i].z = acc[i].z * a + x_cur[i].z * b;
+          acc[i].w = acc[i].w * a + x_cur[i].w * b;
+        }
+        M = Mn;
+      }
+      v_cur = v_nxt;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) x_cur[i] = x_nxt[i];
+    }
+    if (live) {
+      const int64_t row = ((int64_t)(sm.r0[s] + iq) * p.Hq + hk * p.g + h) * D + d0;
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        store_out<QT>(p.out, row + 4 * i, acc[i].x * inv);
+        store_out<QT>(p.out, row + 4 * i + 1, acc[i].y * inv);
+        store_out<QT>(p.out, row + 4 * i + 2, acc[i].z * inv);
+        store_out<QT>(p.out, row + 4 * i + 3, acc[i].w * inv);
+      }
+    }
+  }
+}
+
 MQParams make_mq_params(const pkv::MQArgs& a) {
   MQParams p;
   p.out = a.out;
@@ -287,9 +631,70 @@ int launch_mq_reduce_t(const pkv::MQArgs& a) {
   return (int)hipGetLastError();
 }
 
+MQStreamParams make_mq_stream_params(const pkv::MQArgs& a) {
+  MQStreamParams sp;
+  sp.b = make_mq_params(a);
+  sp.Y = sp.b.Hkv * sp.b.hchunks;
+  sp.W = a.stream_grid * pkv::kWaves;
+  sp.R = pkv::kv_restart_units(a.kv_dtype);
+  sp.ml = a.st_ml;
+  sp.part = a.st_part;
+  return sp;
+}
+
+template <int QT, int KVT, int D>
+int launch_mq_stream_t(const pkv::MQArgs& a) {
+  const MQStreamParams sp = make_mq_stream_params(a);
+  multiquery_stream_kernel<QT, KVT, D>
+      <<<dim3(a.stream_grid), dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(sp);
+  return (int)hipGetLastError();
+}
+
+template <int QT, int D>
+int launch_mq_split_merge_t(const pkv::MQArgs& a) {
+  const MQStreamParams sp = make_mq_stream_params(a);
+  // one wave per segment: tiles x segments, bounded by sequences x row tiles
+  const int64_t nsegs = (int64_t)sp.b.S * sp.b.qtiles * sp.Y;
+  int64_t grid = (nsegs + pkv::kWaves - 1) / pkv::kWaves;
+  if (grid > 4096) grid = 4096;
+  if (grid < 1) grid = 1;
+  multiquery_split_merge_kernel<QT, D>
+      <<<dim3((unsigned)grid), dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(sp);
+  return (int)hipGetLastError();
+}
+
 }  // namespace
 
 namespace pkv {
+
+int launch_multiquery_stream(const MQArgs& a) {
+  const int q = a.q_dtype, kv = a.kv_dtype, D = a.head_dim;
+#define PKV_MQ_CASE(QT, KVT, DD) \
+  if (q == QT && kv == KVT && D == DD) return launch_mq_stream_t<QT, KVT, DD>(a);
+  PKV_MQ_CASE(PKV_BF16, PKV_BF16, 64)
+  PKV_MQ_CASE(PKV_BF16, PKV_BF16, 128)
+  PKV_MQ_CASE(PKV_F16, PKV_F16, 64)
+  PKV_MQ_CASE(PKV_F16, PKV_F16, 128)
+  PKV_MQ_CASE(PKV_BF16, PKV_FP8_E4M3, 64)
+  PKV_MQ_CASE(PKV_BF16, PKV_FP8_E4M3, 128)
+  PKV_MQ_CASE(PKV_F16, PKV_FP8_E4M3, 64)
+  PKV_MQ_CASE(PKV_F16, PKV_FP8_E4M3, 128)
+  PKV_MQ_CASE(PKV_BF16, PKV_INT8, 64)
+  PKV_MQ_CASE(PKV_BF16, PKV_INT8, 128)
+  PKV_MQ_CASE(PKV_F16, PKV_INT8, 64)
+  PKV_MQ_CASE(PKV_F16, PKV_INT8, 128)
+#undef PKV_MQ_CASE
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_multiquery_split_merge(const MQArgs& a) {
+  const int q = a.q_dtype, D = a.head_dim;
+  if (q == PKV_BF16 && D == 128) return launch_mq_split_merge_t<PKV_BF16, 128>(a);
+  if (q == PKV_BF16 && D == 64) return launch_mq_split_merge_t<PKV_BF16, 64>(a);
+  if (q == PKV_F16 && D == 128) return launch_mq_split_merge_t<PKV_F16, 128>(a);
+  if (q == PKV_F16 && D == 64) return launch_mq_split_merge_t<PKV_F16, 64>(a);
+  return (int)hipErrorInvalidValue;
+}
 
 int launch_multiquery(const MQArgs& a) {
   const int q = a.q_dtype, kv = a.kv_dtype, D = a.head_dim;

@@ -161,17 +161,30 @@ def test_multiquery_empty_calls_and_workspace_check():
 
 def test_multiquery_partition_and_workspace_helpers():
     l = lib()
-    # 64 sequences x 8 kv-heads x 1 row tile = 512 workgroups: partitions of 512
-    assert l.pkv_multiquery_partition_size(64, 4, 32, 8, 256, 0) == 512
-    # 16 x 8 x 128 row tiles (512 rows, 4 per tile): one pass over the context
+    # partition_size 0: the balanced schedule when one workgroup per
+    # (sequence, kv-head, row tile) would not fill the chip: 64 x 8 x 1
+    assert l.pkv_multiquery_partition_size(64, 4, 32, 8, 256, 0) == 0
+    assert l.pkv_multiquery_partition_size(32, 8, 64, 8, 160, 0) == 0       # 32 x 8 x 4
+    # 16 x 8 x 128 row tiles (512 rows, 4 per tile) fill it: one pass over the
+    # context on the fixed grid
     assert l.pkv_multiquery_partition_size(16, 512, 32, 8, 2048, 0) == 2048 * 16
+    # too many sequences for the balanced schedule's prefix sums: fixed
+    assert l.pkv_multiquery_partition_size(4096, 1, 32, 8, 16, 0) > 0
+    assert l.pkv_multiquery_partition_size(3000, 1, 4, 4, 16, 0) > 0
     assert l.pkv_multiquery_partition_size(16, 512, 32, 8, 2048, 64) == 64
     assert l.pkv_multiquery_partition_size(16, 512, 32, 8, 2048, 24) == -1
+    # balanced: (m, l) and accumulator slots, two per wave of the grid, of
+    # the 16 tile columns; the same for any row count
+    W = 256 * 4
+    want = 2 * W * 16 * 2 * 4 + 2 * W * 16 * 128 * 4
+    assert l.pkv_multiquery_workspace_size(256, 64, 4, 32, 8, 128, 256, 0) == want
+    assert l.pkv_multiquery_workspace_size(64, 64, 4, 32, 8, 128, 256, 0) == want
+    # one fixed pass: no workspace
     assert l.pkv_multiquery_workspace_size(8192, 16, 512, 32, 8, 128, 2048, 0) == 0
+    # fixed partitions of 512 over 4096 tokens: partials per row, head, partition
     n = l.pkv_multiquery_workspace_size(256, 64, 4, 32, 8, 128, 256, 512)
     assert n >= 256 * 32 * 8 * (128 + 2) * 4
     assert l.pkv_multiquery_workspace_size(-1, 64, 4, 32, 8, 128, 256, 512) == ctypes.c_size_t(-1).value
-
 
 
 def test_int8_cache_is_a_scaled_byte_cache():
