@@ -135,6 +135,7 @@ static bool make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
 
 struct MQPlan {
   int32_t partition, num_parts;   // partition 0: the balanced schedule
+  int32_t max_ntl;                 // column tiles per wave at most
   size_t off_l, off_acc, ws_bytes;
   bool stream;                     // balanced schedule (partition_size 0)
   int32_t stream_grid;
@@ -152,34 +153,50 @@ bool mq_plan(int32_t num_rows, int32_t num_seqs, int32_t max_query_len, int32_t 
   if (partition_size > 0 && (partition_size % kBlockSize != 0 || partition_size > kMaxPartition))
     return false;
   const int32_t max_ctx = max_blocks_per_seq * kBlockSize;
-  const MQTiles t = mq_tiles(num_q_heads / num_kv_heads, max_query_len > 0 ? max_query_len : 1);
-  // Balanced schedule: partition_size 0 and a fixed grid of one workgroup
-  // per (sequence, kv-head chunk, row tile) too small to fill the chip (the
-  // same 2048 as choose_partition: below it the fixed path would cut the
-  // contexts into partitions), while the sequences and their row tiles fit
-  // the in-LDS prefix sums and the unit count stays below 2^31 (at the
-  // largest restart count).  Measured: draft verification of 4 and 8 rows
-  // gains; long prompt chunks, whose fixed grid is large and whose tiles are
-  // compute-bound, run faster on the fixed grid with its higher occupancy.
-  const int64_t Y = (int64_t)num_kv_heads * t.hchunks;
-  const int64_t tiles = (int64_t)num_seqs * t.qtiles;
-  const int64_t r_max = kv_restart_units(PKV_BF16) > kv_restart_units(PKV_FP8_E4M3)
-                            ? kv_restart_units(PKV_BF16)
-                            : kv_restart_units(PKV_FP8_E4M3);
-  plan->stream = partition_size == 0 && tiles * Y < 2048 && num_seqs <= kMaxStreamSeqs &&
-                 tiles <= kMaxStreamTiles &&
-                 tiles * (max_blocks_per_seq + r_max) * Y < ((int64_t)1 << 31);
-  plan->stream_grid = g_stream_workgroups.load();
-  plan->st_off_part = 0;
-  if (plan->stream) {
-    const size_t workers = (size_t)plan->stream_grid * kWaves;
-    plan->partition = 0;
-    plan->num_parts = 1;
-    plan->off_l = plan->off_acc = 0;
-    plan->st_off_part = align256(2 * workers * 16 * 2 * sizeof(float));
-    plan->ws_bytes = plan->st_off_part + align256(2 * workers * 16 * head_dim * sizeof(float));
-    return true;
+  const int32_t g = num_q_heads / num_kv_heads;
+  const int32_t mq = max_query_len > 0 ? max_query_len : 1;
+  // Balanced schedule, with up to four column tiles per wave: partition_size
+  // 0 and a fixed grid of one workgroup per (sequence, kv-head chunk, row
+  // tile) too small to fill the chip (the same 2048 as choose_partition:
+  // below it the fixed path would cut the contexts into partitions), while
+  // the sequences and their row tiles fit the in-LDS prefix sums and the
+  // unit count stays below 2^31 (at the largest restart count).  Measured:
+  // draft verification and mixed batches of a few rows gain; long prompt
+  // chunks, whose fixed grid is large and whose tiles are compute-bound, run
+  // faster on the fixed grid.
+  {
+    const MQTiles t = mq_tiles(g, mq, 4);
+    const int64_t Y = (int64_t)num_kv_heads * t.hchunks;
+    const int64_t tiles = (int64_t)num_seqs * t.qtiles;
+    const int64_t r_max = kv_restart_units(PKV_BF16) > kv_restart_units(PKV_FP8_E4M3)
+                              ? kv_restart_units(PKV_BF16)
+                              : kv_restart_units(PKV_FP8_E4M3);
+    plan->stream = partition_size == 0 && tiles * Y < 2048 && num_seqs <= kMaxStreamSeqs &&
+                   tiles <= kMaxStreamTiles &&
+                   tiles * (max_blocks_per_seq + r_max) * Y < ((int64_t)1 << 31);
+    plan->stream_grid = g_stream_workgroups.load();
+    plan->st_off_part = 0;
+    if (plan->stream) {
+      const size_t workers = (size_t)plan->stream_grid * kWaves;
+      const size_t cols = (size_t)16 * t.ntl;   // columns of a row tile
+      plan->max_ntl = 4;
+      plan->partition = 0;
+      plan->num_parts = 1;
+      plan->off_l = plan->off_acc = 0;
+      plan->st_off_part = align256(2 * workers * cols * 2 * sizeof(float));
+      plan->ws_bytes = plan->st_off_part + align256(2 * workers * cols * head_dim * sizeof(float));
+      return true;
+    }
   }
+  // Fixed grid.  Several column tiles per wave read a (sequence, kv-head)'s
+  // K/V once instead of once per row tile; that pays when the re-reads would
+  // not stay in the L2, for tables of 8192 tokens or more (2-4 MB of K/V per
+  // kv-head at head_dim 128).  Shorter contexts keep one column tile, whose
+  // smaller register file lets two waves share a SIMD.  Measured: 512-row
+  // chunks at 32K tokens 18.1 -> 12.8 ms with four tiles; 64-row chunks of
+  // contexts up to 2048 tokens 0.72 -> 0.81 ms, so those keep one.
+  plan->max_ntl = max_ctx >= 8192 ? 4 : 1;
+  const MQTiles t = mq_tiles(g, mq, plan->max_ntl);
   // workgroups per sequence and partition: kv-heads x head chunks x row tiles
   const int64_t per_seq = (int64_t)num_kv_heads * t.hchunks * t.qtiles;
   const int32_t ps = partition_size > 0
@@ -636,7 +653,8 @@ pkv_status pkv_paged_multiquery_attention_profiled(
                max_blocks_per_seq, partition_size, &plan))
     return fail(PKV_ERR_INVALID_ARG,
                 "multiquery: partition_size must be 0 or a multiple of 16 <= %d", kMaxPartition);
-  const MQTiles t = mq_tiles(num_q_heads / num_kv_heads, max_query_len > 0 ? max_query_len : 1);
+  const MQTiles t = mq_tiles(num_q_heads / num_kv_heads, max_query_len > 0 ? max_query_len : 1,
+                            plan.max_ntl);
   if (!plan.stream && (num_seqs > 65535 || (int64_t)num_kv_heads * t.hchunks * t.qtiles > 65535 ||
                       plan.num_parts > 65535))
     return fail(PKV_ERR_UNSUPPORTED,
@@ -683,6 +701,7 @@ pkv_status pkv_paged_multiquery_attention_profiled(
   a.ws_m = plan.ws_bytes ? reinterpret_cast<float*>(ws) : nullptr;
   a.ws_l = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
   a.ws_acc = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_acc) : nullptr;
+  a.max_ntl = plan.max_ntl;
   a.stream_grid = plan.stream_grid;
   a.st_ml = plan.stream ? reinterpret_cast<float*>(ws) : nullptr;
   a.st_part = plan.stream ? reinterpret_cast<float*>(ws + plan.st_off_part) : nullptr;

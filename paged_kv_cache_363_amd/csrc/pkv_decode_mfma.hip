@@ -77,8 +77,8 @@ void decode_mfma_kernel(DecodeParams p) {
     mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH, PKV_MFMA_NT,
                false, PC>(p.kc + head_off, p.vc + head_off, blk_stride,
                                            p.bt + (int64_t)s * p.mb, w0, w1, nblk - 1,
-                                           ctx - 16 * (nblk - 1), p.nb, qr, p.sl2, m_run, l_run,
-                                           o, lane, 0, qlo);
+                                           ctx - 16 * (nblk - 1), p.nb, qr, p.sl2, &m_run, &l_run,
+                                           o, lane, nullptr, qlo);
   }
 
   // lane (G, c) holds O[head c][dim DPL*(4G+i) + e]; l needs the 4 G lanes

@@ -238,7 +238,7 @@ void decode_stream_kernel(StreamParams p) {
         mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
                    !pkv::byte_codes(KVT) || PKV_NT_FP8, false, PC>(
             p.kc + off, p.vc + off, blk_stride, p.bt + (int64_t)s * p.mb, b, b1, last,
-            ctx - 16 * last, p.nb, qr, p.sl2, m_run, l_run, o, lane, 0, qlo);
+            ctx - 16 * last, p.nb, qr, p.sl2, &m_run, &l_run, o, lane, nullptr, qlo);
       }
       finish(s, y, b, b1 - 1, first_piece);
       first_piece = false;

@@ -91,6 +91,7 @@ struct MQArgs {
   float* ws_m;         // [rows][Hq][P]
   float* ws_l;         // [rows][Hq][P]
   float* ws_acc;       // [rows][Hq][P][D]
+  int32_t max_ntl;      // column tiles per wave at most (the plan's choice)
   // balanced schedule (launch_multiquery_stream): workers and partial slots
   int32_t stream_grid;  // workgroups of 4 waves
   float* st_ml;         // [2 W][16][2]
@@ -99,17 +100,22 @@ struct MQArgs {
 };
 
 // Column layout of a multi-query MFMA tile: 16 columns = qpt query rows x
-// chunk q-heads of one kv-head; hchunks head groups per kv-head; qtiles row
-// tiles for max_query_len rows.
+// chunk q-heads of one kv-head; hchunks head groups per kv-head.  One wave
+// carries ntl such column tiles (ntl * qpt consecutive rows, a row tile)
+// against each K/V load, at most max_ntl (1, 2 or 4) and no more than the
+// rows need; qtiles row tiles cover max_query_len rows.
 struct MQTiles {
-  int chunk, hchunks, qpt, qtiles;
+  int chunk, hchunks, qpt, ntl, qtiles;
 };
-inline MQTiles mq_tiles(int g, int max_query_len) {
+inline MQTiles mq_tiles(int g, int max_query_len, int max_ntl) {
   MQTiles t;
   t.chunk = g < 16 ? g : 16;
   t.hchunks = (g + t.chunk - 1) / t.chunk;
   t.qpt = 16 / t.chunk;
-  t.qtiles = (max_query_len + t.qpt - 1) / t.qpt;
+  const int col_tiles = (max_query_len + t.qpt - 1) / t.qpt;
+  t.ntl = col_tiles >= 4 ? 4 : (col_tiles >= 2 ? 2 : 1);
+  if (t.ntl > max_ntl) t.ntl = max_ntl;
+  t.qtiles = (max_query_len + t.qpt * t.ntl - 1) / (t.qpt * t.ntl);
   return t;
 }
 

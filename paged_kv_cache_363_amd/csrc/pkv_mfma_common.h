@@ -256,18 +256,21 @@ struct MfmaTile {
     for (int rr = 0; rr < 4; ++rr) r.v[rr] = load_row<ROWB, NT>(vp + rr * D * KVB);
   }
 
-  // Online-softmax update of (m_run, l_run, o) with one tile holding `valid`
-  // live tokens (0 = none: the state does not change, and the tile's
+  // Online-softmax update of NTL column tiles with one K/V tile holding
+  // `valid` live tokens (0 = none: the state does not change, and the tile's
   // registers are still read, so the caller need not branch around it).
-  // vis <= valid: tokens of the tile this lane's column may attend to (its
-  // causal limit; valid for a single query).  V rows past `valid` are zeroed,
-  // rows in [vis, valid) are finite and get weight zero.
-  // qr: raw q operand (zeros for padding columns); PC: qlo holds the
-  // remainder of per-channel-scaled q (load_q_scaled), a second QK pass.
-  template <bool PC = false>
-  __device__ static void consume(Raw& r, int valid, int vis, const uint4* qr, float sl2,
-                                 float& m_run, float& l_run, f32x4* o, int c, int G,
+  // Column tile j has its own q operand qr[j][KSTEPS], state m_run[j],
+  // l_run[j], o[j][DPL] and causal limit vis[j] <= valid: tokens of the tile
+  // this lane's column may attend to (valid for a single query).  K and V are
+  // widened once and serve every column tile.  V rows past `valid` are
+  // zeroed; rows in [vis, valid) are finite and get weight zero.
+  // PC (one column tile only): qlo holds the remainder of per-channel-scaled
+  // q (load_q_scaled), a second QK pass.
+  template <int NTL = 1, bool PC = false>
+  __device__ static void consume(Raw& r, int valid, const int* vis, const uint4* qr, float sl2,
+                                 float* m_run, float* l_run, f32x4* o, int c, int G,
                                  const uint4* qlo = nullptr) {
+    static_assert(!PC || NTL == 1, "per-channel scales take one column tile");
     V8 kop[KSTEPS];
     if constexpr (BYTE) {
 #pragma unroll
@@ -292,38 +295,52 @@ struct MfmaTile {
           for (int i = 0; i < ROWB / 4; ++i) r.v[rr].w[i] = 0u;
     }
 
-    // S = K Q^T: lane (G, c) gets tokens 4G+i, head c.
-    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    P4 pb[NTL];            // PV weights of each column tile
+    [[maybe_unused]] V4 pl[NTL];   // their bf16 remainders (bf16 caches)
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) sacc = M::qk(kop[kk], as_v8<V8>(qr[kk]), sacc);
-    if constexpr (PC) {
+    for (int j = 0; j < NTL; ++j) {
+      // S = K Q^T: lane (G, c) gets tokens 4G+i, column c.
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) sacc = M::qk(kop[kk], as_v8<V8>(qlo[kk]), sacc);
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        sacc = M::qk(kop[kk], as_v8<V8>(qr[j * KSTEPS + kk]), sacc);
+      if constexpr (PC) {
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) sacc = M::qk(kop[kk], as_v8<V8>(qlo[kk]), sacc);
+      }
+
+      float z[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = (4 * G + i < vis[j]) ? sacc[i] * sl2 : kNegInf;
+      float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      bm = wave_max4(bm);
+      const float m_new = fmaxf(m_run[j], bm);
+      // A tile with no valid token so far (m_new still -inf) shifts by 0, so
+      // that it leaves the state at zero instead of producing NaN.
+      const float m_ref = m_new == kNegInf ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_ref);
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_ref);
+      l_run[j] = l_run[j] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      m_run[j] = m_new;
+      if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[j * DPL + e] *= alpha;
+      }
+      // B operand of PV: k-slot (G, i) = token 4G+i, column c.
+      pb[j] = as_v4<P4>(PM::pack2(pr[0], pr[1]), PM::pack2(pr[2], pr[3]));
+      if constexpr (!PVH) {
+        // bf16: the weight as a bf16 head plus its bf16 remainder
+        float lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo[i] = pr[i] - M::rounded(pr[i]);
+        pl[j] = as_v4<V4>(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]));
+      }
     }
 
-    float z[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) z[i] = (4 * G + i < vis) ? sacc[i] * sl2 : kNegInf;
-    float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-    bm = wave_max4(bm);
-    const float m_new = fmaxf(m_run, bm);
-    // A tile with no valid token so far (m_new still -inf) shifts by 0, so
-    // that it leaves the state at zero instead of producing NaN.
-    const float m_ref = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_ref);
-    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m_run = m_new;
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] *= alpha;
-    }
-    // B operand of PV: k-slot (G, i) = token 4G+i, column c = head c.
-    const P4 pb = as_v4<P4>(PM::pack2(pr[0], pr[1]), PM::pack2(pr[2], pr[3]));
-
-    // A operand of PV for m-tile e: dim DPL*c + e of tokens 4G..4G+3.
+    // A operand of PV for m-tile e: dim DPL*c + e of tokens 4G..4G+3, built
+    // once for every column tile.
     if constexpr (BYTE) {
 #pragma unroll
       for (int e = 0; e < DPL; e += 2) {
@@ -333,32 +350,27 @@ struct MfmaTile {
         const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
         const P4 a0 = as_v4<P4>(cvt2_f16(x01, false), cvt2_f16(x23, false));
         const P4 a1 = as_v4<P4>(cvt2_f16(x01, true), cvt2_f16(x23, true));
-        o[e] = PM::pv(a0, pb, o[e]);
-        o[e + 1] = PM::pv(a1, pb, o[e + 1]);
-      }
-    } else if constexpr (PVH) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        const int wi = e / 2;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint32_t x01 = __builtin_amdgcn_perm(r.v[1].w[wi], r.v[0].w[wi], sel);
-        const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
-        o[e] = PM::pv(as_v4<P4>(x01, x23), pb, o[e]);
+        for (int j = 0; j < NTL; ++j) {
+          o[j * DPL + e] = PM::pv(a0, pb[j], o[j * DPL + e]);
+          o[j * DPL + e + 1] = PM::pv(a1, pb[j], o[j * DPL + e + 1]);
+        }
       }
     } else {
-      // bf16: the weight as a bf16 head plus its bf16 remainder
-      float lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lo[i] = pr[i] - M::rounded(pr[i]);
-      const V4 pl = as_v4<V4>(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]));
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
         const int wi = e / 2;
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
         const uint32_t x01 = __builtin_amdgcn_perm(r.v[1].w[wi], r.v[0].w[wi], sel);
         const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
-        const V4 a0 = as_v4<V4>(x01, x23);
-        o[e] = M::pv(a0, pl, M::pv(a0, pb, o[e]));
+        const P4 a0 = as_v4<P4>(x01, x23);
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) {
+          if constexpr (PVH)
+            o[j * DPL + e] = PM::pv(a0, pb[j], o[j * DPL + e]);
+          else
+            o[j * DPL + e] = M::pv(a0, pl[j], M::pv(a0, pb[j], o[j * DPL + e]));
+        }
       }
     }
   }
@@ -366,7 +378,8 @@ struct MfmaTile {
 
 
 // Online-softmax pass of one wave over the blocks [b0, b1) of one
-// (sequence, kv-head) segment, continuing the running (m_run, l_run, o).
+// (sequence, kv-head) segment, continuing the running state of NTL column
+// tiles (m_run[j], l_run[j], o[j][DPL], q operand qr[j][KSTEPS]).
 //   kc, vc   : the caches, already offset to the segment's kv-head tile
 //   row      : the sequence's block-table row
 //   last     : index of the sequence's last block, tail its token count
@@ -378,15 +391,17 @@ struct MfmaTile {
 // Every load is issued unconditionally (ids past the chunk repeat its last
 // block, invalid ids read block 0 and carry no weight), so the load counter
 // can be waited on per block instead of drained.  nb must be > 0.
-// CAUSAL: the lane's column attends to positions <= pos only (several
-// queries of one sequence in one tile); otherwise pos is ignored.
+// CAUSAL: column tile j of the lane attends to positions <= pos[j] only
+// (several queries of one sequence in one pass); otherwise pos is ignored.
 // PC: per-channel K scales, qlo the remainder of the scaled q (load_q_scaled).
-template <int QT, int KVT, int D, int DEPTH, bool NT, bool CAUSAL = false, bool PC = false>
+template <int QT, int KVT, int D, int DEPTH, bool NT, bool CAUSAL = false, bool PC = false,
+          int NTL = 1>
 __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
                                            int64_t blk_stride, const int32_t* row, int b0,
                                            int b1, int last, int tail, int nb, const uint4* qr,
-                                           float sl2, float& m_run, float& l_run, f32x4* o,
-                                           int lane, int pos = 0, const uint4* qlo = nullptr) {
+                                           float sl2, float* m_run, float* l_run, f32x4* o,
+                                           int lane, const int* pos = nullptr,
+                                           const uint4* qlo = nullptr) {
   using T = MfmaTile<QT, KVT, D>;
   using Raw = typename T::Raw;
   const int c = lane & 15, G = lane >> 4;
@@ -423,8 +438,11 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
         const int idn = id_at(ii + DEPTH);
         const int valid = (ii < n && (unsigned)idc[d] < (unsigned)nb)
                               ? (c0 + ii == last ? tail : 16) : 0;
-        const int vis = CAUSAL ? min(valid, pos - 16 * (c0 + ii) + 1) : valid;
-        T::template consume<PC>(buf[d], valid, vis, qr, sl2, m_run, l_run, o, c, G, qlo);
+        int vis[NTL];
+#pragma unroll
+        for (int j = 0; j < NTL; ++j)
+          vis[j] = CAUSAL ? min(valid, pos[j] - 16 * (c0 + ii) + 1) : valid;
+        T::template consume<NTL, PC>(buf[d], valid, vis, qr, sl2, m_run, l_run, o, c, G, qlo);
         const int64_t a = addr(idn);
         T::template issue<NT>(buf[d], kc + a, vc + a, koff, voff);
         idc[d] = idn;

@@ -9,9 +9,10 @@
 //
 // The MFMA tile of the decode kernels has 16 columns.  Here a column is a
 // (query row, q-head) pair of one kv-head: chunk = min(g, 16) q-heads times
-// 16 / chunk rows (4 rows x 4 heads at g = 4, 16 rows x 1 head for MHA), so
-// one K/V tile load serves every row of the tile.  Each lane masks its
-// column's logits at that row's position.
+// qpt = 16 / chunk rows (4 rows x 4 heads at g = 4, 16 rows x 1 head for
+// MHA).  A wave carries ntl <= 4 such column tiles (a row tile of ntl x qpt
+// rows), so one K/V load, widened once, serves up to 64 (row, q-head)
+// columns.  Each lane masks its column's logits at that row's position.
 //
 // Grid (partition, kv-head x head chunk x row tile, sequence).  A workgroup
 // walks the blocks its last row can see; its four waves take contiguous
@@ -51,7 +52,9 @@ struct MQParams {
   int Hq, Hkv, g, nb, mb;
   int chunk;         // q-heads per column group
   int hchunks;       // column groups per kv-head
-  int qpt;           // query rows per tile (16 / chunk)
+  int qpt;           // query rows per column tile (16 / chunk)
+  int ntl;           // column tiles per wave (its template argument)
+  int rpt;           // rows per row tile: qpt * ntl
   int qtiles;        // row tiles per (sequence, kv-head, head chunk) in the grid
   int part_blocks;   // 16-token blocks per partition
   int num_parts;     // partitions in the grid (1 = single pass)
@@ -72,12 +75,15 @@ __device__ __forceinline__ void seq_rows(const MQParams& p, int s, int& r0, int&
   n = min(b - a, p.max_q);
 }
 
-template <int QT, int KVT, int D>
-__global__ __launch_bounds__(64 * pkv::kWaves) __attribute__((amdgpu_waves_per_eu(2, 8)))
+// NTL column tiles per wave: the rows of a row tile share every K/V load.
+template <int QT, int KVT, int D, int NTL>
+__global__ __launch_bounds__(64 * pkv::kWaves)
+__attribute__((amdgpu_waves_per_eu(NTL > 1 ? 1 : 2, 8)))
 void multiquery_mfma_kernel(MQParams p) {
   using T = MfmaTile<QT, KVT, D>;
   constexpr int LD = D + 4;
   constexpr int DPL = T::DPL;
+  constexpr int KS = T::KSTEPS;
 
   __shared__ float sm_m[pkv::kWaves * kCols];
   __shared__ float sm_l[pkv::kWaves * kCols];
@@ -93,29 +99,39 @@ void multiquery_mfma_kernel(MQParams p) {
   const int hc = yy % p.hchunks, hk = yy / p.hchunks;
   int r0, n;
   seq_rows(p, s, r0, n);
-  const int i0 = qt * p.qpt;
+  const int i0 = qt * p.rpt;
   if (i0 >= n) return;   // no row of this sequence in the tile
   const int cap = p.mb * pkv::kBlockSize;
   const int ctx = min(max(p.cl[s], 0), cap);
 
-  // this lane's column: row i0 + c / chunk, q-head hk*g + hc*chunk + c % chunk
-  const int iq = i0 + c / p.chunk;
+  // this lane's column in column tile j: row i0 + j qpt + c / chunk, q-head
+  // hk*g + hc*chunk + c % chunk
   const int h = hc * p.chunk + c % p.chunk;
-  const bool live = c < p.qpt * p.chunk && iq < n && h < p.g;
-  const int pos = live ? ctx - n + iq : -1;   // < 0: the row attends to nothing
+  auto row_of = [&](int j) { return i0 + j * p.qpt + c / p.chunk; };
+  auto live_of = [&](int j) { return c < p.qpt * p.chunk && row_of(j) < n && h < p.g; };
+  int pos[NTL];
+  uint4 qr[NTL * KS];
+#pragma unroll
+  for (int j = 0; j < NTL; ++j) {
+    pos[j] = live_of(j) ? ctx - n + row_of(j) : -1;   // < 0: the column attends to nothing
+    T::load_q(qr + j * KS, p.q, (int64_t)(r0 + row_of(j)) * p.Hq + hk * p.g + h, live_of(j), G);
+  }
   // blocks any row of the tile can see: up to its last row's position
-  const int p_last = ctx - n + min(i0 + p.qpt, n) - 1;
+  const int p_last = ctx - n + min(i0 + p.rpt, n) - 1;
   const int nblk = p_last >= 0 ? (p_last >> 4) + 1 : 0;
   const int b_begin = part * p.part_blocks;
   const int b_end = min(b_begin + p.part_blocks, nblk);
   const int nblk_p = max(b_end - b_begin, 0);
 
-  uint4 qr[T::KSTEPS];
-  T::load_q(qr, p.q, (int64_t)(r0 + iq) * p.Hq + hk * p.g + h, live, G);
-  f32x4 o[DPL];
+  f32x4 o[NTL * DPL];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
+  for (int e = 0; e < NTL * DPL; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NTL], l_run[NTL];
+#pragma unroll
+  for (int j = 0; j < NTL; ++j) {
+    m_run[j] = kNegInf;
+    l_run[j] = 0.f;
+  }
 
   const int w0 = b_begin + (nblk_p * w) / pkv::kWaves;
   const int w1 = b_begin + (nblk_p * (w + 1)) / pkv::kWaves;
@@ -124,52 +140,57 @@ void multiquery_mfma_kernel(MQParams p) {
     const int64_t head_off = (int64_t)hk * T::TILE;
     const int last = ((ctx + 15) >> 4) - 1;
     mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH, false,
-               true>(p.kc + head_off, p.vc + head_off, blk_stride, p.bt + (int64_t)s * p.mb,
-                     w0, w1, last, ctx - 16 * last, p.nb, qr, p.sl2, m_run, l_run, o, lane,
-                     pos);
+               true, false, NTL>(p.kc + head_off, p.vc + head_off, blk_stride,
+                                 p.bt + (int64_t)s * p.mb, w0, w1, last, ctx - 16 * last, p.nb,
+                                 qr, p.sl2, m_run, l_run, o, lane, pos);
   }
 
-  // lane (G, c) holds O[column c][dim DPL*(4G+i) + e]; l needs the 4 G lanes
-  l_run = wave_sum4(l_run);
-  if (G == 0) {
-    sm_m[w * kCols + c] = m_run;
-    sm_l[w * kCols + c] = l_run;
-  }
-  {
-    float* dst = sm_o + (w * kCols + c) * LD + DPL * 4 * G;
+  // One column tile at a time through LDS: lane (G, c) holds O[column c][dim
+  // DPL*(4G+i) + e]; l needs the 4 G lanes.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) dst[DPL * i + e] = o[e][i];
-  }
-  __syncthreads();
-
-  for (int idx = threadIdx.x; idx < kCols * D; idx += 64 * pkv::kWaves) {
-    const int cc = idx / D, d = idx % D;
-    const int ic = i0 + cc / p.chunk, hh = hc * p.chunk + cc % p.chunk;
-    if (cc >= p.qpt * p.chunk || ic >= n || hh >= p.g) continue;
-    float M = kNegInf;
-#pragma unroll
-    for (int v = 0; v < pkv::kWaves; ++v) M = fmaxf(M, sm_m[v * kCols + cc]);
-    float L = 0.f, acc = 0.f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int v = 0; v < pkv::kWaves; ++v) {
-        const float mv = sm_m[v * kCols + cc];
-        const float f = (mv == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-        L += f * sm_l[v * kCols + cc];
-        acc += f * sm_o[(v * kCols + cc) * LD + d];
-      }
+  for (int j = 0; j < NTL; ++j) {
+    const float lj = wave_sum4(l_run[j]);
+    if (j > 0) __syncthreads();   // the previous tile's reads are done
+    if (G == 0) {
+      sm_m[w * kCols + c] = m_run[j];
+      sm_l[w * kCols + c] = lj;
     }
-    const int64_t row = (int64_t)(r0 + ic) * p.Hq + hk * p.g + hh;
-    if (p.num_parts == 1) {
-      store_out<QT>(p.out, row * D + d, L > 0.f ? acc * p.vsc / L : 0.f);
-    } else {
-      const int64_t pr = row * p.num_parts + part;
-      p.ws_acc[pr * D + d] = acc * p.vsc;
-      if (d == 0) {
-        p.ws_m[pr] = M;
-        p.ws_l[pr] = L;
+    {
+      float* dst = sm_o + (w * kCols + c) * LD + DPL * 4 * G;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) dst[DPL * i + e] = o[j * DPL + e][i];
+    }
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < kCols * D; idx += 64 * pkv::kWaves) {
+      const int cc = idx / D, d = idx % D;
+      const int ic = i0 + j * p.qpt + cc / p.chunk, hh = hc * p.chunk + cc % p.chunk;
+      if (cc >= p.qpt * p.chunk || ic >= n || hh >= p.g) continue;
+      float M = kNegInf;
+#pragma unroll
+      for (int v = 0; v < pkv::kWaves; ++v) M = fmaxf(M, sm_m[v * kCols + cc]);
+      float L = 0.f, acc = 0.f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int v = 0; v < pkv::kWaves; ++v) {
+          const float mv = sm_m[v * kCols + cc];
+          const float f = (mv == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+          L += f * sm_l[v * kCols + cc];
+          acc += f * sm_o[(v * kCols + cc) * LD + d];
+        }
+      }
+      const int64_t row = (int64_t)(r0 + ic) * p.Hq + hk * p.g + hh;
+      if (p.num_parts == 1) {
+        store_out<QT>(p.out, row * D + d, L > 0.f ? acc * p.vsc / L : 0.f);
+      } else {
+        const int64_t pr = row * p.num_parts + part;
+        p.ws_acc[pr * D + d] = acc * p.vsc;
+        if (d == 0) {
+          p.ws_m[pr] = M;
+          p.ws_l[pr] = L;
+        }
       }
     }
   }
@@ -244,10 +265,10 @@ __global__ __launch_bounds__(64) void multiquery_reduce_kernel(MQParams p) {
 // ---------------------------------------------------------------------------
 // Work-balanced schedule.  As in the balanced decode kernel, the call's work
 // is flattened into units and a persistent grid of waves takes equal
-// contiguous shares of them.  A tile is one row tile (qpt rows) of one
-// sequence; it has Y = kv-heads x head chunks segments, each of nbk + R
-// units: R restart units (the cost of starting a piece) and one unit per
-// 16-token block its last row can see.  Tiles follow each other in
+// contiguous shares of them.  A tile is one row tile (rpt = ntl x qpt rows,
+// ntl column tiles of 16 columns) of one sequence; it has Y = kv-heads x head
+// chunks segments, each of nbk + R units: R restart units (the cost of
+// starting a piece) and one unit per 16-token block its last row can see.  Tiles follow each other in
 // (sequence, row tile) order; the prefix sums of their units sit in LDS, and
 // both kernels derive every share from them.
 
@@ -256,8 +277,8 @@ struct MQStreamParams {
   int Y;         // segments per tile: kv-heads x head chunks
   int W;         // waves of the grid
   int R;         // restart units at the start of every segment
-  float* ml;     // [2 W][16][2]
-  float* part;   // [2 W][16][D]
+  float* ml;     // [2 W][16 ntl][2]
+  float* part;   // [2 W][16 ntl][D]
 };
 
 struct MQStreamSmem {
@@ -272,7 +293,7 @@ struct MQStreamSmem {
 // 16-token blocks the last row of row tile qt of a sequence (ctx tokens, n
 // rows) can see; 0 when every row of the tile sits before position 0.
 __device__ __forceinline__ int mq_tile_blocks(const MQParams& p, int ctx, int n, int qt) {
-  const int p_last = ctx - n + min(qt * p.qpt + p.qpt, n) - 1;
+  const int p_last = ctx - n + min(qt * p.rpt + p.rpt, n) - 1;
   return p_last >= 0 ? (p_last >> 4) + 1 : 0;
 }
 
@@ -308,7 +329,7 @@ __device__ void mq_tile_prefix(const MQStreamParams& sp, MQStreamSmem& sm) {
     int carry = 0;
     for (int base = 0; base < S; base += 64) {
       const int i = base + lane;
-      const int x = wave_scan(i < S ? (sm.n[i] + p.qpt - 1) / p.qpt : 0, lane);
+      const int x = wave_scan(i < S ? (sm.n[i] + p.rpt - 1) / p.rpt : 0, lane);
       if (i < S) sm.tb[i + 1] = carry + x;
       carry += __shfl(x, 63);
     }
@@ -354,12 +375,15 @@ __device__ void mq_tile_prefix(const MQStreamParams& sp, MQStreamSmem& sm) {
 // One wave per worker.  A share covers the tail of one segment, whole
 // segments and the head of another; a whole segment is normalised and stored
 // by its wave, a piece of a split segment goes to the wave's partial slot
-// (its first piece in slot 2 wk, its last in slot 2 wk + 1).
-template <int QT, int KVT, int D>
+// (its first piece in slot 2 wk, its last in slot 2 wk + 1).  NTL column
+// tiles per wave, as in the fixed kernel.
+template <int QT, int KVT, int D, int NTL>
 __global__ __launch_bounds__(64 * pkv::kWaves) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void multiquery_stream_kernel(MQStreamParams sp) {
   using T = MfmaTile<QT, KVT, D>;
   constexpr int DPL = T::DPL;
+  constexpr int KS = T::KSTEPS;
+  constexpr int NC = kCols * NTL;   // columns of a row tile
   __shared__ MQStreamSmem sm;
   const MQParams& p = sp.b;
   const int lane = threadIdx.x & 63;
@@ -376,7 +400,7 @@ void multiquery_stream_kernel(MQStreamParams sp) {
   for (int t = wk; t < Tn; t += W) {
     if (sm.pref[t + 1] != sm.pref[t]) continue;
     const int s = sm.tseq[t];
-    const int i0 = (t - sm.tb[s]) * p.qpt, i1 = min(i0 + p.qpt, sm.n[s]);
+    const int i0 = (t - sm.tb[s]) * p.rpt, i1 = min(i0 + p.rpt, sm.n[s]);
     const int64_t base = (int64_t)(sm.r0[s] + i0) * p.Hq * D;
     const int64_t cnt = (int64_t)(i1 - i0) * p.Hq * D;
     for (int64_t i = lane; i < cnt; i += 64) store_out<QT>(p.out, base + i, 0.f);
@@ -408,9 +432,10 @@ void multiquery_stream_kernel(MQStreamParams sp) {
   };
 
   const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
-  uint4 qr[T::KSTEPS];
-  f32x4 o[DPL];
-  float m_run, l_run;
+  uint4 qr[NTL * KS];
+  f32x4 o[NTL * DPL];
+  float m_run[NTL], l_run[NTL];
+  int pos[NTL];
 
   int64_t u = u_lo;
   int t, y, j;
@@ -426,45 +451,55 @@ void multiquery_stream_kernel(MQStreamParams sp) {
     if (b1 > b) {
       const int hc = y % p.hchunks, hk = y / p.hchunks;
       const int n = sm.n[s], ctx = sm.ctx[s], r0 = sm.r0[s];
-      // this lane's column: row iq of the sequence, q-head h of the kv-head
-      const int iq = (t - sm.tb[s]) * p.qpt + c / p.chunk;
+      // this lane's column in column tile k: row iq(k) of the sequence,
+      // q-head h of the kv-head
       const int h = hc * p.chunk + c % p.chunk;
-      const bool live = c < p.qpt * p.chunk && iq < n && h < p.g;
-      const int pos = live ? ctx - n + iq : -1;   // < 0: the column attends to nothing
-      T::load_q(qr, p.q, (int64_t)(r0 + iq) * p.Hq + hk * p.g + h, live, G);
+      const int i0 = (t - sm.tb[s]) * p.rpt + c / p.chunk;
+      auto iq = [&](int k) { return i0 + k * p.qpt; };
+      auto live = [&](int k) { return c < p.qpt * p.chunk && iq(k) < n && h < p.g; };
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-      m_run = kNegInf;
-      l_run = 0.f;
+      for (int k = 0; k < NTL; ++k) {
+        pos[k] = live(k) ? ctx - n + iq(k) : -1;   // < 0: the column attends to nothing
+        T::load_q(qr + k * KS, p.q, (int64_t)(r0 + iq(k)) * p.Hq + hk * p.g + h, live(k), G);
+        m_run[k] = kNegInf;
+        l_run[k] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < NTL * DPL; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int last = ((ctx + 15) >> 4) - 1;
       if (p.nb > 0) {
         const int64_t off = (int64_t)hk * T::TILE;
         mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
-                   !pkv::byte_codes(KVT), true>(
+                   !pkv::byte_codes(KVT), true, false, NTL>(
             p.kc + off, p.vc + off, blk_stride, p.bt + (int64_t)s * p.mb, b, b1, last,
             ctx - 16 * last, p.nb, qr, p.sl2, m_run, l_run, o, lane, pos);
       }
       // close the piece: store the rows, or leave (m, l, acc) for the merge
-      const float l_tot = wave_sum4(l_run);
-      if (b == 0 && b1 == len - sp.R) {
-        if (live) {
-          const int64_t row = ((int64_t)(r0 + iq) * p.Hq + hk * p.g + h) * D + DPL * 4 * G;
+      const bool whole = b == 0 && b1 == len - sp.R;
+      const int64_t slot = 2 * (int64_t)wk + (first_piece ? 0 : 1);
+#pragma unroll
+      for (int k = 0; k < NTL; ++k) {
+        const float l_tot = wave_sum4(l_run[k]);
+        if (!live(k)) continue;
+        if (whole) {
+          const int64_t row = ((int64_t)(r0 + iq(k)) * p.Hq + hk * p.g + h) * D + DPL * 4 * G;
           const float inv = l_tot > 0.f ? p.vsc / l_tot : 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) store_out<QT>(p.out, row + DPL * i + e, o[e][i] * inv);
-        }
-      } else if (live) {
-        const int64_t slot = 2 * (int64_t)wk + (first_piece ? 0 : 1);
-        float* dst = sp.part + (slot * kCols + c) * D + DPL * 4 * G;
+            for (int e = 0; e < DPL; ++e)
+              store_out<QT>(p.out, row + DPL * i + e, o[k * DPL + e][i] * inv);
+        } else {
+          const int64_t col = slot * NC + k * kCols + c;
+          float* dst = sp.part + col * D + DPL * 4 * G;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) dst[DPL * i + e] = o[e][i] * p.vsc;
-        if (G == 0) {
-          sp.ml[(slot * kCols + c) * 2] = m_run;
-          sp.ml[(slot * kCols + c) * 2 + 1] = l_tot;
+            for (int e = 0; e < DPL; ++e) dst[DPL * i + e] = o[k * DPL + e][i] * p.vsc;
+          if (G == 0) {
+            sp.ml[col * 2] = m_run[k];
+            sp.ml[col * 2 + 1] = l_tot;
+          }
         }
       }
       first_piece = false;
@@ -483,10 +518,10 @@ void multiquery_stream_kernel(MQStreamParams sp) {
 }
 
 // Merge the pieces of every segment the grid above split between waves, the
-// shares recomputed exactly as there.  One wave per split segment: lane l
-// takes column l / 4 of the tile and a quarter of its dims, and folds the
-// pieces in order with the running log-sum-exp rescale, the loads of piece
-// k + 1 in flight while piece k is added.
+// shares recomputed exactly as there.  One wave per (split segment, column
+// tile): lane l takes column l / 4 of the column tile and a quarter of its
+// dims, and folds the pieces in order with the running log-sum-exp rescale,
+// the loads of piece k + 1 in flight while piece k is added.
 template <int QT, int D>
 __global__ __launch_bounds__(64 * pkv::kWaves) void multiquery_split_merge_kernel(
     MQStreamParams sp) {
@@ -503,9 +538,11 @@ __global__ __launch_bounds__(64 * pkv::kWaves) void multiquery_split_merge_kerne
   const int64_t U = Y * sm.pref[Tn];
   const int64_t We = U < sp.W ? U : sp.W;
   if (We == 0) return;
-  const int64_t nsegs = (int64_t)Tn * Y;
-  for (int64_t seg = (int64_t)blockIdx.x * pkv::kWaves + w; seg < nsegs;
-       seg += (int64_t)gridDim.x * pkv::kWaves) {
+  const int64_t nitems = (int64_t)Tn * Y * p.ntl;
+  for (int64_t it = (int64_t)blockIdx.x * pkv::kWaves + w; it < nitems;
+       it += (int64_t)gridDim.x * pkv::kWaves) {
+    const int ct = (int)(it % p.ntl);
+    const int64_t seg = it / p.ntl;
     const int t = (int)(seg / Y), y = (int)(seg % Y);
     const int len = sm.pref[t + 1] - sm.pref[t];
     if (len == 0) continue;
@@ -520,62 +557,65 @@ __global__ __launch_bounds__(64 * pkv::kWaves) void multiquery_split_merge_kerne
     const int np = (int)(wb - wa + 1);
     const int s = sm.tseq[t];
     const int hc = y % p.hchunks, hk = y / p.hchunks;
-    const int iq = (t - sm.tb[s]) * p.qpt + cc / p.chunk;
     const int h = hc * p.chunk + cc % p.chunk;
-    const bool live = cc < p.qpt * p.chunk && iq < sm.n[s] && h < p.g;
-    auto slot_of = [&](int k) { return k == 0 ? sl0 : 2 * (wa + k); };
-    // (m, l) and this lane's accumulator dims of piece k (zeros for a dead
-    // column, which never reads)
-    auto load_piece = [&](int k, float2& v, float4 (&x)[NV]) {
-      const int64_t sl = slot_of(k) * kCols + cc;
-      v = make_float2(kNegInf, 0.f);
+    const int nc = kCols * p.ntl;   // columns of a slot
+    {
+      const int iq = (t - sm.tb[s]) * p.rpt + ct * p.qpt + cc / p.chunk;
+      const bool live = cc < p.qpt * p.chunk && iq < sm.n[s] && h < p.g;
+      auto slot_of = [&](int k) { return k == 0 ? sl0 : 2 * (wa + k); };
+      // (m, l) and this lane's accumulator dims of piece k (zeros for a dead
+      // column, which never reads)
+      auto load_piece = [&](int k, float2& v, float4 (&x)[NV]) {
+        const int64_t sl = slot_of(k) * nc + ct * kCols + cc;
+        v = make_float2(kNegInf, 0.f);
 #pragma unroll
-      for (int i = 0; i < NV; ++i) x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (live) {
-        v = *reinterpret_cast<const float2*>(sp.ml + sl * 2);
-        const float4* src = reinterpret_cast<const float4*>(sp.part + sl * D + d0);
+        for (int i = 0; i < NV; ++i) x[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (live) {
+          v = *reinterpret_cast<const float2*>(sp.ml + sl * 2);
+          const float4* src = reinterpret_cast<const float4*>(sp.part + sl * D + d0);
 #pragma unroll
-        for (int i = 0; i < NV; ++i) x[i] = src[i];
+          for (int i = 0; i < NV; ++i) x[i] = src[i];
+        }
+      };
+      float M = kNegInf, L = 0.f;
+      float4 acc[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      float2 v_cur;
+      float4 x_cur[NV];
+      load_piece(0, v_cur, x_cur);
+      for (int k = 0; k < np; ++k) {
+        float2 v_nxt;
+        float4 x_nxt[NV];
+        load_piece(k + 1 < np ? k + 1 : k, v_nxt, x_nxt);
+        if (v_cur.y > 0.f) {
+          const float Mn = fmaxf(M, v_cur.x);
+          const float a = __builtin_amdgcn_exp2f(M - Mn);   // 0 while M = -inf
+          const float b = __builtin_amdgcn_exp2f(v_cur.x - Mn);
+          L = L * a + v_cur.y * b;
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            acc[i].x = acc[i].x * a + x_cur[i].x * b;
+            acc[i].y = acc[i].y * a + x_cur[i].y * b;
+            acc[i].z = acc[i].z * a + x_cur[i].z * b;
+            acc[i].w = acc[i].w * a + x_cur[i].w * b;
+          }
+          M = Mn;
+        }
+        v_cur = v_nxt;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) x_cur[i] = x_nxt[i];
       }
-    };
-    float M = kNegInf, L = 0.f;
-    float4 acc[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    float2 v_cur;
-    float4 x_cur[NV];
-    load_piece(0, v_cur, x_cur);
-    for (int k = 0; k < np; ++k) {
-      float2 v_nxt;
-      float4 x_nxt[NV];
-      load_piece(k + 1 < np ? k + 1 : k, v_nxt, x_nxt);
-      if (v_cur.y > 0.f) {
-        const float Mn = fmaxf(M, v_cur.x);
-        const float a = __builtin_amdgcn_exp2f(M - Mn);   // 0 while M = -inf
-        const float b = __builtin_amdgcn_exp2f(v_cur.x - Mn);
-        L = L * a + v_cur.y * b;
+      if (live) {
+        const int64_t row = ((int64_t)(sm.r0[s] + iq) * p.Hq + hk * p.g + h) * D + d0;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-          acc[i].x = acc[i].x * a + x_cur[i].x * b;
-          acc[i].y = acc[i].y * a + x_cur[i].y * b;
-          acc[i].z = acc[i].z * a + x_cur[i].z * b;
-          acc[i].w = acc[i].w * a + x_cur[i].w * b;
+          store_out<QT>(p.out, row + 4 * i, acc[i].x * inv);
+          store_out<QT>(p.out, row + 4 * i + 1, acc[i].y * inv);
+          store_out<QT>(p.out, row + 4 * i + 2, acc[i].z * inv);
+          store_out<QT>(p.out, row + 4 * i + 3, acc[i].w * inv);
         }
-        M = Mn;
-      }
-      v_cur = v_nxt;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) x_cur[i] = x_nxt[i];
-    }
-    if (live) {
-      const int64_t row = ((int64_t)(sm.r0[s] + iq) * p.Hq + hk * p.g + h) * D + d0;
-      const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        store_out<QT>(p.out, row + 4 * i, acc[i].x * inv);
-        store_out<QT>(p.out, row + 4 * i + 1, acc[i].y * inv);
-        store_out<QT>(p.out, row + 4 * i + 2, acc[i].z * inv);
-        store_out<QT>(p.out, row + 4 * i + 3, acc[i].w * inv);
       }
     }
   }
@@ -598,10 +638,12 @@ MQParams make_mq_params(const pkv::MQArgs& a) {
   p.g = a.num_q_heads / a.num_kv_heads;
   p.nb = a.num_blocks;
   p.mb = a.max_blocks_per_seq;
-  const pkv::MQTiles t = pkv::mq_tiles(p.g, a.max_query_len);
+  const pkv::MQTiles t = pkv::mq_tiles(p.g, a.max_query_len, a.max_ntl);
   p.chunk = t.chunk;
   p.hchunks = t.hchunks;
   p.qpt = t.qpt;
+  p.ntl = t.ntl;
+  p.rpt = t.qpt * t.ntl;
   p.qtiles = t.qtiles;
   p.part_blocks = a.partition / pkv::kBlockSize;
   p.num_parts = a.num_parts;
@@ -618,8 +660,11 @@ template <int QT, int KVT, int D>
 int launch_mq_t(const pkv::MQArgs& a) {
   const MQParams p = make_mq_params(a);
   dim3 grid(p.num_parts, p.Hkv * p.hchunks * p.qtiles, p.S);
-  multiquery_mfma_kernel<QT, KVT, D>
-      <<<grid, dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(p);
+  const dim3 block(64 * pkv::kWaves);
+  hipStream_t st = (hipStream_t)a.stream;
+  if (p.ntl == 4) multiquery_mfma_kernel<QT, KVT, D, 4><<<grid, block, 0, st>>>(p);
+  else if (p.ntl == 2) multiquery_mfma_kernel<QT, KVT, D, 2><<<grid, block, 0, st>>>(p);
+  else multiquery_mfma_kernel<QT, KVT, D, 1><<<grid, block, 0, st>>>(p);
   return (int)hipGetLastError();
 }
 
@@ -645,17 +690,20 @@ MQStreamParams make_mq_stream_params(const pkv::MQArgs& a) {
 template <int QT, int KVT, int D>
 int launch_mq_stream_t(const pkv::MQArgs& a) {
   const MQStreamParams sp = make_mq_stream_params(a);
-  multiquery_stream_kernel<QT, KVT, D>
-      <<<dim3(a.stream_grid), dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(sp);
+  const dim3 grid(a.stream_grid), block(64 * pkv::kWaves);
+  hipStream_t st = (hipStream_t)a.stream;
+  if (sp.b.ntl == 4) multiquery_stream_kernel<QT, KVT, D, 4><<<grid, block, 0, st>>>(sp);
+  else if (sp.b.ntl == 2) multiquery_stream_kernel<QT, KVT, D, 2><<<grid, block, 0, st>>>(sp);
+  else multiquery_stream_kernel<QT, KVT, D, 1><<<grid, block, 0, st>>>(sp);
   return (int)hipGetLastError();
 }
 
 template <int QT, int D>
 int launch_mq_split_merge_t(const pkv::MQArgs& a) {
   const MQStreamParams sp = make_mq_stream_params(a);
-  // one wave per segment: tiles x segments, bounded by sequences x row tiles
-  const int64_t nsegs = (int64_t)sp.b.S * sp.b.qtiles * sp.Y;
-  int64_t grid = (nsegs + pkv::kWaves - 1) / pkv::kWaves;
+  // one wave per (segment, column tile), bounded by sequences x row tiles
+  const int64_t nitems = (int64_t)sp.b.S * sp.b.qtiles * sp.Y * sp.b.ntl;
+  int64_t grid = (nitems + pkv::kWaves - 1) / pkv::kWaves;
   if (grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;
   multiquery_split_merge_kernel<QT, D>
