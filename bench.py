@@ -67,17 +67,39 @@ DT_CODE = {"f32": 0, "f16": 1, "bf16": 2, "fp8": 3, "int8": 4}
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash():
-    """sha256 over the sources that decide what the GPU runs (kernels, device
-    headers, the launch code): what a counter profile was taken of.  The host
-    block pool is left out; it never touches the device."""
+# the source file that defines each decode kernel
+KERNEL_FILES = {"decode_stream_kernel": "pkv_decode_stream.hip",
+                "decode_mfma_kernel": "pkv_decode_mfma.hip",
+                "decode_vec_kernel": "pkv_decode_vec.hip"}
+
+
+def kernel_source_hash(kernel):
+    """sha256 over the file that defines `kernel` (with its launch code) and
+    every header it includes, followed through csrc/ and include/: what a
+    counter profile of that kernel was taken of.  Changes elsewhere in the
+    library (other kernels, the host pool, argument checks) leave it alone."""
     import hashlib
+    import re
     csrc = os.path.join(ROOT, "paged_kv_cache_363_amd", "csrc")
+    inc = os.path.join(ROOT, "include")
+    seen, todo = [], [KERNEL_FILES[kernel]]
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        path = next((os.path.join(d, name) for d in (csrc, inc)
+                     if os.path.exists(os.path.join(d, name))), None)
+        if path is None:
+            continue   # a system header
+        seen.append(name)
+        with open(path, "rb") as f:
+            todo += re.findall(rb'#include "([^"]+)"', f.read())
+        todo = [t.decode() if isinstance(t, bytes) else t for t in todo]
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")) and name != "pkv_pool.cpp":
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(seen):
+        path = next(os.path.join(d, name) for d in (csrc, inc) if os.path.exists(os.path.join(d, name)))
+        with open(path, "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -100,13 +122,13 @@ def decode_path(cfg, algo, partition):
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` on `workload` from a committed counter
     summary (profiles/<kernel>_<workload>_traffic.json), or None when there is
-    none or the library's sources changed since it was taken."""
+    none or the kernel's sources (kernel_source_hash) changed since it was taken."""
     path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256") != kernel_source_hash():
+    if rec.get("source_sha256") != kernel_source_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -594,7 +616,8 @@ def main():
                             "tokens_per_s": round(r["tokens_per_s"], 1), "algo": r["algo"],
                             "graph_ms_per_step": (round(r["graph_ms_per_step"], 5)
                                                   if r["graph_ms_per_step"] else None),
-                            "kernel": r["kernel"], "partition": r["partition"]}
+                            "kernel": r["kernel"], "partition": r["partition"],
+                            "traffic": measured_traffic(name, r["kernel"])}
             del r
             torch.cuda.empty_cache()
         line["other_configs"] = others
