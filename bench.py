@@ -194,6 +194,43 @@ def host_bookkeeping_us(cfg, st):
     return (time.perf_counter() - t0) / reps * 1e6
 
 
+PROBE_TILE = 4096   # bytes per tile of the streaming-read probe
+
+
+def time_stream_probe(kv_bytes, R, K, dev):
+    """The library's streaming-read probe over the workload's byte count: the
+    read rate this GPU achieves for paged decode's access pattern (4 KiB tiles
+    in a shuffled order, contiguous shares per wave, four tiles in flight).
+    R disjoint regions of kv_bytes (rounded to whole tiles), each read in its
+    own shuffled order and rotated like the cache replicas; the mean of K
+    launches, each between two events as the decode kernel is timed.
+    Returns (ms per launch, GB/s)."""
+    import torch
+    import paged_kv_cache_363_amd as pkv
+    nt = max(1, kv_bytes // PROBE_TILE)
+    buf = torch.empty(R * nt * PROBE_TILE, dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4099)
+    ids = [(torch.randperm(nt, device=dev, generator=gen) + r * nt).to(torch.int32)
+           for r in range(R)]
+    sink = torch.empty(256 * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(4):
+        pkv.stream_read_probe(buf, ids[i % R], sink)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        pkv.stream_read_probe(buf, ids[i % R], sink)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs) / K
+    del buf, ids, sink
+    torch.cuda.empty_cache()
+    return ms, nt * PROBE_TILE / (ms * 1e-3) / 1e9
+
+
 def time_config(cfg, args, dev, partition, with_cpu=True):
     import numpy as np
     import torch
@@ -292,6 +329,8 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
     except RuntimeError as e:   # reported, never silently replaced
         log(f"graph capture failed: {e}")
     achieved = kv_bytes / (part_avg * 1e-3) / 1e9
+    probe_ms, probe_gbs = time_stream_probe(kv_bytes, R, K, dev)
+    log(f"streaming-read probe: {probe_ms:.4f} ms, {probe_gbs:.1f} GB/s")
     res = dict(
         config=cfg.name, kv_bytes=kv_bytes, replicas=R, cache_bytes_per_replica=cache_bytes,
         kernel=decode_path(cfg, args.algo, ps)[0],
@@ -302,6 +341,7 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
         step_gbs=kv_bytes / (step_ms * 1e-3) / 1e9,
         graph_ms_per_step=g_step_ms,
         decode_kernel_gbs=achieved, tokens_per_s=cfg.num_seqs / (step_ms * 1e-3),
+        probe_ms=probe_ms, probe_gbs=probe_gbs,
         t_pool_build_s=st["t_pool_build"])
     log(f"timed {K} steps: {step_ms:.4f} ms/step, decode kernel {part_avg:.4f} ms")
     res["host_bookkeeping_us_per_step"] = host_bookkeeping_us(cfg, st)
@@ -595,6 +635,12 @@ def main():
                      "kernel": res["kernel"],
                      "kernel_ms": round(res["decode_kernel_ms"], 5),
                      "algorithmic_bytes_per_launch": res["kv_bytes"]},
+        "achievable_read": {
+            "gbs": round(res["probe_gbs"], 2), "ms": round(res["probe_ms"], 5),
+            "kernel_frac": round(res["decode_kernel_gbs"] / res["probe_gbs"], 4),
+            "probe": "pkv_stream_read_probe over the same bytes: shuffled 4 KiB tiles, "
+                     "contiguous shares per wave, 4 tiles in flight, 256 x 4 waves, "
+                     "timed between events like the decode kernel"},
         "merge_or_reduce_ms": round(res["reduce_kernel_ms"], 5),
         "graph": ({"ms_per_step": round(res["graph_ms_per_step"], 5),
                    "step_gbs": round(res["kv_bytes"] / (res["graph_ms_per_step"] * 1e-3) / 1e9, 2)}
@@ -616,6 +662,8 @@ def main():
                             "tokens_per_s": round(r["tokens_per_s"], 1), "algo": r["algo"],
                             "graph_ms_per_step": (round(r["graph_ms_per_step"], 5)
                                                   if r["graph_ms_per_step"] else None),
+                            "achievable_read_gbs": round(r["probe_gbs"], 2),
+                            "kernel_frac_of_achievable": round(r["decode_kernel_gbs"] / r["probe_gbs"], 4),
                             "kernel": r["kernel"], "partition": r["partition"],
                             "traffic": measured_traffic(name, r["kernel"])}
             del r

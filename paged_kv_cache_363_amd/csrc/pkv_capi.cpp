@@ -15,6 +15,7 @@
 
 #include "pkv.h"
 #include "pkv_internal.h"
+#include "pkv_probe.h"
 
 namespace pkv {
 
@@ -385,6 +386,33 @@ int32_t pkv_decode_partition_size_for_lengths(const int32_t* context_lens, int32
     }
   }
   return t_fix <= t_bal ? (int32_t)max_ctx : 0;
+}
+
+}  // extern "C"
+
+namespace pkv {
+int launch_stream_read_probe(const void* buf, int64_t buf_bytes, const int32_t* tile_ids,
+                             int32_t num_tiles, uint32_t* sink, int32_t workgroups, void* stream);
+}
+
+extern "C" {
+
+pkv_status pkv_stream_read_probe(const void* buf, int64_t buf_bytes, const int32_t* tile_ids,
+                                 int32_t num_tiles, uint32_t* sink, int32_t workgroups,
+                                 void* stream) {
+  clear_error();
+  if (buf_bytes < 0 || num_tiles < 0 || workgroups < 1 || workgroups > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "stream_read_probe: bad sizes");
+  if (!buf || !tile_ids || !sink)
+    return fail(PKV_ERR_INVALID_ARG, "stream_read_probe: NULL pointer");
+  if (!aligned16(buf))
+    return fail(PKV_ERR_INVALID_ARG, "stream_read_probe: buf must be 16-byte aligned");
+  const int rc = launch_stream_read_probe(buf, buf_bytes, tile_ids, num_tiles, sink, workgroups,
+                                          stream);
+  if (rc != 0)
+    return fail(PKV_ERR_HIP, "stream_read_probe: launch failed: %s",
+                hipGetErrorString((hipError_t)rc));
+  return PKV_OK;
 }
 
 size_t pkv_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
