@@ -203,7 +203,8 @@ def time_stream_probe(kv_bytes, R, K, dev):
     in a shuffled order, contiguous shares per wave, four tiles in flight).
     R disjoint regions of kv_bytes (rounded to whole tiles), each read in its
     own shuffled order and rotated like the cache replicas; the mean of K
-    launches, each between two events as the decode kernel is timed.
+    launches, each between two events its dispatch stamps, as the decode
+    kernel is timed.
     Returns (ms per launch, GB/s)."""
     import torch
     import paged_kv_cache_363_amd as pkv
@@ -219,11 +220,12 @@ def time_stream_probe(kv_bytes, R, K, dev):
         pkv.stream_read_probe(buf, ids[i % R], sink)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
+    for pair in evs:       # create the underlying HIP events before handing them over
+        for e in pair:
+            e.record(stream)
     torch.cuda.synchronize()
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        pkv.stream_read_probe(buf, ids[i % R], sink)
-        b.record(stream)
+    for i, pair in enumerate(evs):
+        pkv.stream_read_probe(buf, ids[i % R], sink, events=pair)
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in evs) / K
     del buf, ids, sink
@@ -640,7 +642,7 @@ def main():
             "kernel_frac": round(res["decode_kernel_gbs"] / res["probe_gbs"], 4),
             "probe": "pkv_stream_read_probe over the same bytes: shuffled 4 KiB tiles, "
                      "contiguous shares per wave, 4 tiles in flight, 256 x 4 waves, "
-                     "timed between events like the decode kernel"},
+                     "timed by dispatch-stamped events like the decode kernel"},
         "merge_or_reduce_ms": round(res["reduce_kernel_ms"], 5),
         "graph": ({"ms_per_step": round(res["graph_ms_per_step"], 5),
                    "step_gbs": round(res["kv_bytes"] / (res["graph_ms_per_step"] * 1e-3) / 1e9, 2)}

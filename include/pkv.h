@@ -239,11 +239,13 @@ pkv_status pkv_paged_decode_attention_algo(void* out, const void* q, const void*
                                            void* workspace, size_t workspace_bytes,
                                            int32_t algo, void* stream);
 
-/* Same as pkv_paged_decode_attention_algo, and records caller-created HIP
- * events (hipEvent_t passed as void*, NULL = skip) on `stream`: ev_begin
- * before the partition kernel, ev_mid after it, ev_end after the reduction
- * kernel (right after the partition kernel when the call is single-pass).
- * For timing the kernels from outside the library. */
+/* Same as pkv_paged_decode_attention_algo, and stamps caller-created HIP
+ * events (hipEvent_t passed as void*, NULL = skip) for timing the kernels
+ * from outside the library.  ev_begin and ev_mid are stamped by the decode
+ * kernel's own dispatch (hipExtLaunchKernel) at its start and end, so they
+ * bracket that kernel alone; ev_end by the end of the merge or reduction
+ * kernel, or recorded on `stream` right after the decode kernel when the
+ * call runs a single pass. */
 pkv_status pkv_paged_decode_attention_profiled(
     void* out, const void* q, const void* k_cache, const void* v_cache,
     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
@@ -318,8 +320,10 @@ pkv_status pkv_paged_multiquery_attention(
     int32_t max_blocks_per_seq, float scale, int32_t q_dtype, int32_t kv_dtype, float k_scale,
     float v_scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
     void* stream);
-/* The same, recording ev_begin before the attention kernel, ev_mid after it
- * and ev_end after the reduction (any may be NULL). */
+/* The same, with events as for pkv_paged_decode_attention_profiled:
+ * ev_begin and ev_mid stamped by the attention kernel's own dispatch,
+ * ev_end by the end of the merging kernel (or recorded after a single pass);
+ * any may be NULL. */
 pkv_status pkv_paged_multiquery_attention_profiled(
     void* out, const void* q, const void* k_cache, const void* v_cache,
     const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,

@@ -26,11 +26,14 @@ extern "C" {
  *   tile_ids  : device int32[num_tiles].
  *   sink      : device uint32[workgroups * 256], overwritten.
  *   workgroups: 1 .. 65535.
+ *   ev_start, ev_stop: caller-created HIP events (hipEvent_t as void*, NULL =
+ *               skip) stamped by the probe kernel's own dispatch at its
+ *               start and end, as the decode entry points stamp theirs.
  * Asynchronous on stream.  PKV_ERR_INVALID_ARG on NULL pointers, negative
  * sizes or a bad workgroup count. */
 pkv_status pkv_stream_read_probe(const void* buf, int64_t buf_bytes, const int32_t* tile_ids,
                                  int32_t num_tiles, uint32_t* sink, int32_t workgroups,
-                                 void* stream);
+                                 void* stream, void* ev_start, void* ev_stop);
 
 #ifdef __cplusplus
 }

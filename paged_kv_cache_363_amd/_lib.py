@@ -51,7 +51,7 @@ SIGNATURES = {
                                                      I32, P, P, P, P]),
     "pkv_copy_blocks": (I32, [P, P, P, I32, I32, I64, P]),
     "pkv_swap_blocks": (I32, [P, P, I32, P, P, I32, P, I32, I64, P]),
-    "pkv_stream_read_probe": (I32, [P, I64, P, I32, P, I32, P]),
+    "pkv_stream_read_probe": (I32, [P, I64, P, I32, P, I32, P, P, P]),
     "pkv_seq_swap": (I32, [P, P, P, I32, P, P]),
     "pkv_seq_create_cached": (I32, [P, P, I32, P, I32, P, P]),
     "pkv_pool_register_blocks": (I32, [P, P, I32, P, I32]),

@@ -275,16 +275,21 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None):
                                 _stream(k_cache, stream)))
 
 
-def stream_read_probe(buf, tile_ids, sink, workgroups=256, stream=None):
+def stream_read_probe(buf, tile_ids, sink, workgroups=256, stream=None, events=None):
     """Read the 4 KiB tiles of `buf` (a contiguous device tensor) listed in
     tile_ids (int32 device tensor) with the streaming-read probe: the
     achievable HBM read rate of paged decode's access pattern, for measuring
     the decode kernels against.  sink: uint32-sized device tensor of
-    workgroups * 256 elements, overwritten."""
+    workgroups * 256 elements, overwritten.  events: optional (start, stop)
+    torch.cuda.Event pair stamped by the probe kernel's dispatch."""
     if tile_ids.dtype != torch.int32:
         raise TypeError("tile_ids must be int32")
     if sink.numel() * sink.element_size() < workgroups * 256 * 4:
         raise ValueError("sink holds fewer than workgroups * 256 uint32")
+    evs = [None, None]
+    if events is not None:
+        evs = [ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events]
     check(lib().pkv_stream_read_probe(_dev(buf, "buf"), buf.numel() * buf.element_size(),
                                       _dev(tile_ids, "tile_ids"), tile_ids.numel(),
-                                      _dev(sink, "sink"), int(workgroups), _stream(buf, stream)))
+                                      _dev(sink, "sink"), int(workgroups), _stream(buf, stream),
+                                      *evs))

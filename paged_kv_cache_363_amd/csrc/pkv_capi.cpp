@@ -392,14 +392,15 @@ int32_t pkv_decode_partition_size_for_lengths(const int32_t* context_lens, int32
 
 namespace pkv {
 int launch_stream_read_probe(const void* buf, int64_t buf_bytes, const int32_t* tile_ids,
-                             int32_t num_tiles, uint32_t* sink, int32_t workgroups, void* stream);
+                             int32_t num_tiles, uint32_t* sink, int32_t workgroups, void* stream,
+                             void* ev_start, void* ev_stop);
 }
 
 extern "C" {
 
 pkv_status pkv_stream_read_probe(const void* buf, int64_t buf_bytes, const int32_t* tile_ids,
                                  int32_t num_tiles, uint32_t* sink, int32_t workgroups,
-                                 void* stream) {
+                                 void* stream, void* ev_start, void* ev_stop) {
   clear_error();
   if (buf_bytes < 0 || num_tiles < 0 || workgroups < 1 || workgroups > 65535)
     return fail(PKV_ERR_INVALID_ARG, "stream_read_probe: bad sizes");
@@ -408,7 +409,7 @@ pkv_status pkv_stream_read_probe(const void* buf, int64_t buf_bytes, const int32
   if (!aligned16(buf))
     return fail(PKV_ERR_INVALID_ARG, "stream_read_probe: buf must be 16-byte aligned");
   const int rc = launch_stream_read_probe(buf, buf_bytes, tile_ids, num_tiles, sink, workgroups,
-                                          stream);
+                                          stream, ev_start, ev_stop);
   if (rc != 0)
     return fail(PKV_ERR_HIP, "stream_read_probe: launch failed: %s",
                 hipGetErrorString((hipError_t)rc));
@@ -522,38 +523,39 @@ static pkv_status decode_impl(
   a.ws_l = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
   a.ws_acc = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.off_acc) : nullptr;
   a.stream = stream;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), hs) != hipSuccess)
-    return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
+  // ev_begin / ev_mid: stamped by the decode kernel's own dispatch (its start
+  // and end); ev_end: by the merge or reduction kernel's end, else recorded
+  // right after the decode kernel
+  a.ev_start = ev_begin;
+  a.ev_stop = ev_mid;
   if (use_stream) {
     int rc = launch_decode_stream(a, plan.stream_grid, workspace, plan.stream_off_ml,
                                   plan.stream_off_part);
     if (rc != 0)
       return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString((hipError_t)rc));
-    if (ev_mid && hipEventRecord(static_cast<hipEvent_t>(ev_mid), hs) != hipSuccess)
-      return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
+    a.ev_start = nullptr;
+    a.ev_stop = ev_end;
     rc = launch_decode_split_merge(a, plan.stream_grid, workspace, plan.stream_off_ml,
                                    plan.stream_off_part);
     if (rc != 0)
       return fail(PKV_ERR_HIP, "decode: merge launch failed: %s",
                   hipGetErrorString((hipError_t)rc));
-    if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), hs) != hipSuccess)
-      return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
     return PKV_OK;
   }
   int rc = (algo == PKV_ALGO_MFMA) ? launch_decode_mfma(a) : launch_decode_vector(a);
   if (rc != 0)
     return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString((hipError_t)rc));
-  if (ev_mid && hipEventRecord(static_cast<hipEvent_t>(ev_mid), hs) != hipSuccess)
-    return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
   if (plan.num_parts > 1) {
+    a.ev_start = nullptr;
+    a.ev_stop = ev_end;
     rc = launch_decode_reduce(a);
     if (rc != 0)
       return fail(PKV_ERR_HIP, "decode: reduce launch failed: %s",
                   hipGetErrorString((hipError_t)rc));
-  }
-  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), hs) != hipSuccess)
+  } else if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end),
+                                      static_cast<hipStream_t>(stream)) != hipSuccess) {
     return fail(PKV_ERR_HIP, "decode: hipEventRecord failed");
+  }
   return PKV_OK;
 }
 
@@ -734,36 +736,36 @@ pkv_status pkv_paged_multiquery_attention_profiled(
   a.st_ml = plan.stream ? reinterpret_cast<float*>(ws) : nullptr;
   a.st_part = plan.stream ? reinterpret_cast<float*>(ws + plan.st_off_part) : nullptr;
   a.stream = stream;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), hs) != hipSuccess)
-    return fail(PKV_ERR_HIP, "multiquery: hipEventRecord failed");
+  // events as for decode: stamped by the attention kernel's dispatch, ev_end
+  // by the merging kernel's end or recorded after a single pass
+  a.ev_start = ev_begin;
+  a.ev_stop = ev_mid;
   if (plan.stream) {
     int rc = launch_multiquery_stream(a);
     if (rc != 0)
       return fail(PKV_ERR_HIP, "multiquery: launch failed: %s", hipGetErrorString((hipError_t)rc));
-    if (ev_mid && hipEventRecord(static_cast<hipEvent_t>(ev_mid), hs) != hipSuccess)
-      return fail(PKV_ERR_HIP, "multiquery: hipEventRecord failed");
+    a.ev_start = nullptr;
+    a.ev_stop = ev_end;
     rc = launch_multiquery_split_merge(a);
     if (rc != 0)
       return fail(PKV_ERR_HIP, "multiquery: merge launch failed: %s",
                   hipGetErrorString((hipError_t)rc));
-    if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), hs) != hipSuccess)
-      return fail(PKV_ERR_HIP, "multiquery: hipEventRecord failed");
     return PKV_OK;
   }
   int rc = launch_multiquery(a);
   if (rc != 0)
     return fail(PKV_ERR_HIP, "multiquery: launch failed: %s", hipGetErrorString((hipError_t)rc));
-  if (ev_mid && hipEventRecord(static_cast<hipEvent_t>(ev_mid), hs) != hipSuccess)
-    return fail(PKV_ERR_HIP, "multiquery: hipEventRecord failed");
   if (plan.num_parts > 1) {
+    a.ev_start = nullptr;
+    a.ev_stop = ev_end;
     rc = launch_multiquery_reduce(a);
     if (rc != 0)
       return fail(PKV_ERR_HIP, "multiquery: reduce launch failed: %s",
                   hipGetErrorString((hipError_t)rc));
-  }
-  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), hs) != hipSuccess)
+  } else if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end),
+                                      static_cast<hipStream_t>(stream)) != hipSuccess) {
     return fail(PKV_ERR_HIP, "multiquery: hipEventRecord failed");
+  }
   return PKV_OK;
 }
 

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include "pkv_mfma_common.h"
+#include "pkv_launch.h"
 
 #ifndef PKV_PIPE_DEPTH
 #define PKV_PIPE_DEPTH 2       // K/V blocks in flight per wave, 16-bit caches
@@ -101,16 +102,14 @@ void decode_mfma_kernel(DecodeParams p) {
 template <int QT, int KVT, int D, int HS>
 int launch_t(const pkv::DecodeArgs& a, const DecodeParams& kp) {
   dim3 grid(kp.num_parts, a.num_kv_heads * kp.hchunks, a.num_seqs);
+  const dim3 block(64 * pkv::kWaves);
   if constexpr (pkv::byte_codes(KVT)) {
-    if (kp.ks) {
-      decode_mfma_kernel<QT, KVT, D, HS, true>
-          <<<grid, dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(kp);
-      return (int)hipGetLastError();
-    }
+    if (kp.ks)
+      return pkv::launch_kernel(decode_mfma_kernel<QT, KVT, D, HS, true>, grid, block, a.stream,
+                                kp, a.ev_start, a.ev_stop);
   }
-  decode_mfma_kernel<QT, KVT, D, HS, false>
-      <<<grid, dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(kp);
-  return (int)hipGetLastError();
+  return pkv::launch_kernel(decode_mfma_kernel<QT, KVT, D, HS, false>, grid, block, a.stream, kp,
+                            a.ev_start, a.ev_stop);
 }
 
 template <int QT, int KVT, int D>

@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include "pkv_stream_common.h"
+#include "pkv_launch.h"
 
 #ifndef PKV_PIPE_DEPTH
 #define PKV_PIPE_DEPTH 2       // K/V blocks in flight per wave, 16-bit caches
@@ -298,16 +299,14 @@ __global__ __launch_bounds__(64 * kSkWaves) void decode_split_merge_kernel(Strea
 
 template <int QT, int KVT, int D>
 int launch_t(const pkv::DecodeArgs& a, const StreamParams& sp, int grid) {
+  const dim3 block(64 * kSkWaves);
   if constexpr (pkv::byte_codes(KVT)) {
-    if (sp.ks) {
-      decode_stream_kernel<QT, KVT, D, true>
-          <<<dim3(grid), dim3(64 * kSkWaves), 0, (hipStream_t)a.stream>>>(sp);
-      return (int)hipGetLastError();
-    }
+    if (sp.ks)
+      return pkv::launch_kernel(decode_stream_kernel<QT, KVT, D, true>, dim3(grid), block,
+                                a.stream, sp, a.ev_start, a.ev_stop);
   }
-  decode_stream_kernel<QT, KVT, D, false>
-      <<<dim3(grid), dim3(64 * kSkWaves), 0, (hipStream_t)a.stream>>>(sp);
-  return (int)hipGetLastError();
+  return pkv::launch_kernel(decode_stream_kernel<QT, KVT, D, false>, dim3(grid), block, a.stream,
+                            sp, a.ev_start, a.ev_stop);
 }
 
 template <int QT, int D>
@@ -315,9 +314,8 @@ int launch_merge_t(const pkv::DecodeArgs& a, const StreamParams& sp) {
   const int64_t nitems = (int64_t)sp.S * sp.Y * sp.chunk_heads;
   int64_t grid = (nitems + kSkWaves - 1) / kSkWaves;
   if (grid > 4096) grid = 4096;
-  decode_split_merge_kernel<QT, D>
-      <<<dim3((unsigned)grid), dim3(64 * kSkWaves), 0, (hipStream_t)a.stream>>>(sp);
-  return (int)hipGetLastError();
+  return pkv::launch_kernel(decode_split_merge_kernel<QT, D>, dim3((unsigned)grid),
+                            dim3(64 * kSkWaves), a.stream, sp, a.ev_start, a.ev_stop);
 }
 
 StreamParams make_stream_params(const pkv::DecodeArgs& a, int grid, void* ws, size_t off_ml,

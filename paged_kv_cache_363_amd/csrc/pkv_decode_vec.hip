@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include "pkv_decode_common.h"
+#include "pkv_launch.h"
 
 namespace {
 
@@ -281,9 +282,8 @@ template <int QT, int KVT, int D, int GMAX>
 int launch_vec_t(const pkv::DecodeArgs& a) {
   const DecodeParams kp = make_params(a, GMAX);
   dim3 grid(kp.num_parts, a.num_kv_heads * kp.hchunks, a.num_seqs);
-  decode_vec_kernel<QT, KVT, D, GMAX>
-      <<<grid, dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(kp);
-  return (int)hipGetLastError();
+  return pkv::launch_kernel(decode_vec_kernel<QT, KVT, D, GMAX>, grid, dim3(64 * pkv::kWaves),
+                            a.stream, kp, a.ev_start, a.ev_stop);
 }
 
 template <int QT, int KVT, int D>
@@ -298,9 +298,8 @@ int launch_vec_g(const pkv::DecodeArgs& a) {
 template <int QT, int D>
 int launch_reduce_t(const pkv::DecodeArgs& a) {
   const DecodeParams kp = make_params(a, 16);
-  decode_reduce_kernel<QT, D><<<dim3(a.num_seqs * a.num_q_heads), dim3(64), 0,
-                                (hipStream_t)a.stream>>>(kp);
-  return (int)hipGetLastError();
+  return pkv::launch_kernel(decode_reduce_kernel<QT, D>, dim3(a.num_seqs * a.num_q_heads),
+                            dim3(64), a.stream, kp, a.ev_start, a.ev_stop);
 }
 
 }  // namespace

@@ -66,6 +66,9 @@ struct DecodeArgs {
   float* ws_l;         // [S][Hq][P]
   float* ws_acc;       // [S][Hq][P][D]
   void* stream;
+  // events the next launch's dispatch timestamps itself (launch_kernel)
+  void* ev_start = nullptr;
+  void* ev_stop = nullptr;
   // per-channel scales of a one-byte-code cache, device float[H_kv][D] each;
   // nullptr: k_scale / v_scale apply to the whole tensor
   const float* k_scales = nullptr;
@@ -97,6 +100,9 @@ struct MQArgs {
   float* st_ml;         // [2 W][16][2]
   float* st_part;       // [2 W][16][D]
   void* stream;
+  // events the next launch's dispatch timestamps itself (launch_kernel)
+  void* ev_start = nullptr;
+  void* ev_stop = nullptr;
 };
 
 // Column layout of a multi-query MFMA tile: 16 columns = qpt query rows x

@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 
 #include "pkv_stream_common.h"
+#include "pkv_launch.h"
 
 #ifndef PKV_PIPE_DEPTH
 #define PKV_PIPE_DEPTH 2       // K/V blocks in flight per wave, 16-bit caches
@@ -661,19 +662,18 @@ int launch_mq_t(const pkv::MQArgs& a) {
   const MQParams p = make_mq_params(a);
   dim3 grid(p.num_parts, p.Hkv * p.hchunks * p.qtiles, p.S);
   const dim3 block(64 * pkv::kWaves);
-  hipStream_t st = (hipStream_t)a.stream;
-  if (p.ntl == 4) multiquery_mfma_kernel<QT, KVT, D, 4><<<grid, block, 0, st>>>(p);
-  else if (p.ntl == 2) multiquery_mfma_kernel<QT, KVT, D, 2><<<grid, block, 0, st>>>(p);
-  else multiquery_mfma_kernel<QT, KVT, D, 1><<<grid, block, 0, st>>>(p);
-  return (int)hipGetLastError();
+  auto k = p.ntl == 4   ? multiquery_mfma_kernel<QT, KVT, D, 4>
+           : p.ntl == 2 ? multiquery_mfma_kernel<QT, KVT, D, 2>
+                        : multiquery_mfma_kernel<QT, KVT, D, 1>;
+  return pkv::launch_kernel(k, grid, block, a.stream, p, a.ev_start, a.ev_stop);
 }
 
 template <int QT, int D>
 int launch_mq_reduce_t(const pkv::MQArgs& a) {
   const MQParams p = make_mq_params(a);
-  multiquery_reduce_kernel<QT, D>
-      <<<dim3((unsigned)((int64_t)p.rows * p.Hq)), dim3(64), 0, (hipStream_t)a.stream>>>(p);
-  return (int)hipGetLastError();
+  return pkv::launch_kernel(multiquery_reduce_kernel<QT, D>,
+                            dim3((unsigned)((int64_t)p.rows * p.Hq)), dim3(64), a.stream, p,
+                            a.ev_start, a.ev_stop);
 }
 
 MQStreamParams make_mq_stream_params(const pkv::MQArgs& a) {
@@ -691,11 +691,10 @@ template <int QT, int KVT, int D>
 int launch_mq_stream_t(const pkv::MQArgs& a) {
   const MQStreamParams sp = make_mq_stream_params(a);
   const dim3 grid(a.stream_grid), block(64 * pkv::kWaves);
-  hipStream_t st = (hipStream_t)a.stream;
-  if (sp.b.ntl == 4) multiquery_stream_kernel<QT, KVT, D, 4><<<grid, block, 0, st>>>(sp);
-  else if (sp.b.ntl == 2) multiquery_stream_kernel<QT, KVT, D, 2><<<grid, block, 0, st>>>(sp);
-  else multiquery_stream_kernel<QT, KVT, D, 1><<<grid, block, 0, st>>>(sp);
-  return (int)hipGetLastError();
+  auto k = sp.b.ntl == 4   ? multiquery_stream_kernel<QT, KVT, D, 4>
+           : sp.b.ntl == 2 ? multiquery_stream_kernel<QT, KVT, D, 2>
+                           : multiquery_stream_kernel<QT, KVT, D, 1>;
+  return pkv::launch_kernel(k, grid, block, a.stream, sp, a.ev_start, a.ev_stop);
 }
 
 template <int QT, int D>
@@ -706,9 +705,8 @@ int launch_mq_split_merge_t(const pkv::MQArgs& a) {
   int64_t grid = (nitems + pkv::kWaves - 1) / pkv::kWaves;
   if (grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;
-  multiquery_split_merge_kernel<QT, D>
-      <<<dim3((unsigned)grid), dim3(64 * pkv::kWaves), 0, (hipStream_t)a.stream>>>(sp);
-  return (int)hipGetLastError();
+  return pkv::launch_kernel(multiquery_split_merge_kernel<QT, D>, dim3((unsigned)grid),
+                            dim3(64 * pkv::kWaves), a.stream, sp, a.ev_start, a.ev_stop);
 }
 
 }  // namespace

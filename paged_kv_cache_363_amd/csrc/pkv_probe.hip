@@ -13,6 +13,8 @@
 
 #include <cstdint>
 
+#include "pkv_launch.h"
+
 
 namespace {
 
@@ -26,11 +28,19 @@ __device__ __forceinline__ u32x4 ld_nt(const u32x4* p) { return __builtin_nontem
 constexpr int kTileBytes = 4096;
 constexpr int kDepth = 4;   // tiles in flight per wave
 
-__global__ __launch_bounds__(256) void stream_read_probe_kernel(const u32x4* __restrict__ buf,
-                                                                int64_t buf_tiles,
-                                                                const int32_t* __restrict__ ids,
-                                                                int32_t ntiles,
-                                                                uint32_t* __restrict__ sink) {
+struct ProbeParams {
+  const u32x4* buf;
+  int64_t buf_tiles;
+  const int32_t* ids;
+  int32_t ntiles;
+  uint32_t* sink;
+};
+
+__global__ __launch_bounds__(256) void stream_read_probe_kernel(ProbeParams pp) {
+  const u32x4* __restrict__ buf = pp.buf;
+  const int32_t* __restrict__ ids = pp.ids;
+  const int64_t buf_tiles = pp.buf_tiles;
+  const int32_t ntiles = pp.ntiles;
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = gridDim.x * 4;
@@ -71,7 +81,7 @@ __global__ __launch_bounds__(256) void stream_read_probe_kernel(const u32x4* __r
       }
     }
   }
-  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
+  pp.sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
 }  // namespace
@@ -80,10 +90,15 @@ namespace pkv {
 
 int launch_stream_read_probe(const void* buf, int64_t buf_bytes, const int32_t* tile_ids,
                              int32_t num_tiles, uint32_t* sink, int32_t workgroups,
-                             void* stream) {
-  stream_read_probe_kernel<<<dim3(workgroups), dim3(256), 0, (hipStream_t)stream>>>(
-      static_cast<const u32x4*>(buf), buf_bytes / kTileBytes, tile_ids, num_tiles, sink);
-  return (int)hipGetLastError();
+                             void* stream, void* ev_start, void* ev_stop) {
+  ProbeParams pp;
+  pp.buf = static_cast<const u32x4*>(buf);
+  pp.buf_tiles = buf_bytes / kTileBytes;
+  pp.ids = tile_ids;
+  pp.ntiles = num_tiles;
+  pp.sink = sink;
+  return launch_kernel(stream_read_probe_kernel, dim3(workgroups), dim3(256), stream, pp,
+                       ev_start, ev_stop);
 }
 
 }  // namespace pkv

@@ -206,12 +206,12 @@ def test_int8_cache_is_a_scaled_byte_cache():
 def test_stream_read_probe_rejects_bad_arguments():
     l = lib()
     fake = ctypes.c_void_p(1 << 20)
-    assert l.pkv_stream_read_probe(fake, 4096, fake, 1, fake, 0, NULL) == _lib.PKV_ERR_INVALID_ARG
-    assert l.pkv_stream_read_probe(fake, 4096, fake, 1, fake, 65536, NULL) == _lib.PKV_ERR_INVALID_ARG
-    assert l.pkv_stream_read_probe(fake, -1, fake, 1, fake, 4, NULL) == _lib.PKV_ERR_INVALID_ARG
-    assert l.pkv_stream_read_probe(fake, 4096, fake, -1, fake, 4, NULL) == _lib.PKV_ERR_INVALID_ARG
-    assert l.pkv_stream_read_probe(NULL, 4096, fake, 1, fake, 4, NULL) == _lib.PKV_ERR_INVALID_ARG
+    assert l.pkv_stream_read_probe(fake, 4096, fake, 1, fake, 0, NULL, NULL, NULL) == _lib.PKV_ERR_INVALID_ARG
+    assert l.pkv_stream_read_probe(fake, 4096, fake, 1, fake, 65536, NULL, NULL, NULL) == _lib.PKV_ERR_INVALID_ARG
+    assert l.pkv_stream_read_probe(fake, -1, fake, 1, fake, 4, NULL, NULL, NULL) == _lib.PKV_ERR_INVALID_ARG
+    assert l.pkv_stream_read_probe(fake, 4096, fake, -1, fake, 4, NULL, NULL, NULL) == _lib.PKV_ERR_INVALID_ARG
+    assert l.pkv_stream_read_probe(NULL, 4096, fake, 1, fake, 4, NULL, NULL, NULL) == _lib.PKV_ERR_INVALID_ARG
     assert l.pkv_stream_read_probe(ctypes.c_void_p((1 << 20) + 4), 4096, fake, 1, fake, 4,
-                                   NULL) == _lib.PKV_ERR_INVALID_ARG
+                                   NULL, NULL, NULL) == _lib.PKV_ERR_INVALID_ARG
     assert b"stream_read_probe" in l.pkv_last_error()
 
