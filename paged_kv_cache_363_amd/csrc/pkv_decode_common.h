@@ -51,22 +51,22 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
   }
 }
 
-// Merge the kWaves waves' (m, l, acc) held in LDS and write the result.
-//   sm_m, sm_l : [kWaves][HP]      sm_o : [kWaves][HP][D + 4]
-template <int QT, int D, int HP>
+// Merge the NWV waves' (m, l, acc) held in LDS and write the result.
+//   sm_m, sm_l : [NWV][HP]      sm_o : [NWV][HP][D + 4]
+template <int QT, int D, int HP, int NWV = pkv::kWaves>
 __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, const float* sm_m,
                                                       const float* sm_l, const float* sm_o,
                                                       int nh, int s, int h_first, int part) {
   constexpr int LD = D + 4;
-  for (int idx = threadIdx.x; idx < nh * D; idx += 64 * pkv::kWaves) {
+  for (int idx = threadIdx.x; idx < nh * D; idx += 64 * NWV) {
     const int h = idx / D, d = idx % D;
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < pkv::kWaves; ++w) M = fmaxf(M, sm_m[w * HP + h]);
+    for (int w = 0; w < NWV; ++w) M = fmaxf(M, sm_m[w * HP + h]);
     float L = 0.f, acc = 0.f;
     if (M != kNegInf) {
 #pragma unroll
-      for (int w = 0; w < pkv::kWaves; ++w) {
+      for (int w = 0; w < NWV; ++w) {
         const float mw = sm_m[w * HP + h];
         const float f = (mw == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
         L += f * sm_l[w * HP + h];
