@@ -39,7 +39,8 @@ namespace {
 
 using namespace pkvd;
 
-constexpr int kCols = 16;   // MFMA tile columns
+constexpr int kCols = 16;       // MFMA tile columns
+constexpr int kPlanCUs = 256;   // compute units of an MI355X
 
 struct MQParams {
   void* out;
@@ -520,30 +521,36 @@ void multiquery_stream_kernel(MQStreamParams sp) {
 
 // Merge the pieces of every segment the grid above split between waves, the
 // shares recomputed exactly as there.  One wave per (split segment, column
-// tile): lane l takes column l / 4 of the column tile and a quarter of its
-// dims, and folds the pieces in order with the running log-sum-exp rescale,
-// the loads of piece k + 1 in flight while piece k is added.
+// tile, quarter of the head dim): lane l takes column l / 4 of the column
+// tile and a sixteenth of its dims, and folds the pieces in order with the
+// running log-sum-exp rescale, the loads of four pieces at a time in flight
+// together.  (The partials of 16 columns make this merge four times the
+// decode merge's traffic per segment; the split gives it enough waves to
+// keep that many loads in flight.)
 template <int QT, int D>
 __global__ __launch_bounds__(64 * pkv::kWaves) void multiquery_split_merge_kernel(
     MQStreamParams sp) {
-  constexpr int DQ = D / 4;    // dims per lane
-  constexpr int NV = DQ / 4;   // float4 loads per lane and piece
+  constexpr int kDimSplit = 4;          // waves per (segment, column tile)
+  constexpr int DQ = D / (4 * kDimSplit);   // dims per lane
+  constexpr int NV = DQ / 4;            // float4 loads per lane and piece
   __shared__ MQStreamSmem sm;
   mq_tile_prefix(sp, sm);
   const MQParams& p = sp.b;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
-  const int cc = lane >> 2, d0 = (lane & 3) * DQ;
+  const int cc = lane >> 2;
   const int Tn = sm.tb[p.S];
   const int64_t Y = sp.Y;
   const int64_t U = Y * sm.pref[Tn];
   const int64_t We = U < sp.W ? U : sp.W;
   if (We == 0) return;
-  const int64_t nitems = (int64_t)Tn * Y * p.ntl;
+  const int64_t nitems = (int64_t)Tn * Y * p.ntl * kDimSplit;
   for (int64_t it = (int64_t)blockIdx.x * pkv::kWaves + w; it < nitems;
        it += (int64_t)gridDim.x * pkv::kWaves) {
-    const int ct = (int)(it % p.ntl);
-    const int64_t seg = it / p.ntl;
+    const int dq = (int)(it % kDimSplit);
+    const int d0 = dq * (D / kDimSplit) + (lane & 3) * DQ;
+    const int ct = (int)(it / kDimSplit % p.ntl);
+    const int64_t seg = it / kDimSplit / p.ntl;
     const int t = (int)(seg / Y), y = (int)(seg % Y);
     const int len = sm.pref[t + 1] - sm.pref[t];
     if (len == 0) continue;
@@ -582,30 +589,31 @@ __global__ __launch_bounds__(64 * pkv::kWaves) void multiquery_split_merge_kerne
       float4 acc[NV];
 #pragma unroll
       for (int i = 0; i < NV; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      float2 v_cur;
-      float4 x_cur[NV];
-      load_piece(0, v_cur, x_cur);
-      for (int k = 0; k < np; ++k) {
-        float2 v_nxt;
-        float4 x_nxt[NV];
-        load_piece(k + 1 < np ? k + 1 : k, v_nxt, x_nxt);
-        if (v_cur.y > 0.f) {
-          const float Mn = fmaxf(M, v_cur.x);
-          const float a = __builtin_amdgcn_exp2f(M - Mn);   // 0 while M = -inf
-          const float b = __builtin_amdgcn_exp2f(v_cur.x - Mn);
-          L = L * a + v_cur.y * b;
+      // kBatch pieces' loads go out together, then fold in order (pieces
+      // past np repeat the last one and are not folded)
+      constexpr int kBatch = 4;
+      for (int base = 0; base < np; base += kBatch) {
+        float2 v[kBatch];
+        float4 x[kBatch][NV];
 #pragma unroll
-          for (int i = 0; i < NV; ++i) {
-            acc[i].x = acc[i].x * a + x_cur[i].x * b;
-            acc[i].y = acc[i].y * a + x_cur[i].y * b;
-            acc[i].z = acc[i].z * a + x_cur[i].z * b;
-            acc[i].w = acc[i].w * a + x_cur[i].w * b;
+        for (int u = 0; u < kBatch; ++u) load_piece(min(base + u, np - 1), v[u], x[u]);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (base + u < np && v[u].y > 0.f) {
+            const float Mn = fmaxf(M, v[u].x);
+            const float a = __builtin_amdgcn_exp2f(M - Mn);   // 0 while M = -inf
+            const float b = __builtin_amdgcn_exp2f(v[u].x - Mn);
+            L = L * a + v[u].y * b;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+              acc[i].x = acc[i].x * a + x[u][i].x * b;
+              acc[i].y = acc[i].y * a + x[u][i].y * b;
+              acc[i].z = acc[i].z * a + x[u][i].z * b;
+              acc[i].w = acc[i].w * a + x[u][i].w * b;
+            }
+            M = Mn;
           }
-          M = Mn;
         }
-        v_cur = v_nxt;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) x_cur[i] = x_nxt[i];
       }
       if (live) {
         const int64_t row = ((int64_t)(sm.r0[s] + iq) * p.Hq + hk * p.g + h) * D + d0;
@@ -700,10 +708,14 @@ int launch_mq_stream_t(const pkv::MQArgs& a) {
 template <int QT, int D>
 int launch_mq_split_merge_t(const pkv::MQArgs& a) {
   const MQStreamParams sp = make_mq_stream_params(a);
-  // one wave per (segment, column tile), bounded by sequences x row tiles
-  const int64_t nitems = (int64_t)sp.b.S * sp.b.qtiles * sp.Y * sp.b.ntl;
+  // one wave per (segment, column tile, quarter of the head dim), bounded
+  // by sequences x row tiles.  At most two workgroups per CU: each one
+  // rebuilds the tile prefix sums in LDS first (57 KB, so two fit on a CU),
+  // and one round of that is cheaper than several, the waves looping over
+  // the items instead.
+  const int64_t nitems = (int64_t)sp.b.S * sp.b.qtiles * sp.Y * sp.b.ntl * 4;
   int64_t grid = (nitems + pkv::kWaves - 1) / pkv::kWaves;
-  if (grid > 4096) grid = 4096;
+  if (grid > 2 * kPlanCUs) grid = 2 * kPlanCUs;
   if (grid < 1) grid = 1;
   return pkv::launch_kernel(multiquery_split_merge_kernel<QT, D>, dim3((unsigned)grid),
                             dim3(64 * pkv::kWaves), a.stream, sp, a.ev_start, a.ev_stop);
