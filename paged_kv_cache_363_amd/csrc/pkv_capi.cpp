@@ -361,7 +361,6 @@ int32_t pkv_decode_partition_size_for_lengths(const int32_t* context_lens, int32
   //            and the workgroups start, in grid order, on whichever CU frees
   //            up first.
   constexpr int64_t kMergeUnits = 4;
-  constexpr int kPlanCUs = 256;   // compute units of an MI355X
   int64_t units = 0;
   std::vector<int64_t> work(num_seqs);
   for (int32_t s = 0; s < num_seqs; ++s) {
@@ -375,7 +374,7 @@ int32_t pkv_decode_partition_size_for_lengths(const int32_t* context_lens, int32
   const int64_t t_bal = (Y * units + W - 1) / W + kMergeUnits;
   // list scheduling of the fixed grid (kv-head chunk fastest, then sequence)
   std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
-  for (int i = 0; i < kPlanCUs; ++i) free_at.push(0);
+  for (int i = 0; i < kCUs; ++i) free_at.push(0);
   int64_t t_fix = 0;
   for (int32_t s = 0; s < num_seqs && t_fix <= t_bal; ++s) {
     for (int64_t y = 0; y < Y; ++y) {

@@ -30,7 +30,8 @@ constexpr int kBlockSize = 16;   // tokens per physical block
 constexpr int kWaves = 4;        // waves per decode workgroup
 constexpr int kMaxPartition = 1 << 20;
 constexpr int kMaxStreamSeqs = 2048;        // sequences the balanced schedule handles per call
-constexpr int kDefaultStreamWorkgroups = 256;  // one wave per SIMD of a 256-CU MI355X
+constexpr int kCUs = 256;                   // compute units of an MI355X
+constexpr int kDefaultStreamWorkgroups = kCUs;  // one wave per SIMD
 constexpr int kMaxStreamTiles = 4096;        // (sequence, row tile) pairs of a balanced multi-query call
 
 // Units the balanced schedule charges for starting a piece of a segment, in

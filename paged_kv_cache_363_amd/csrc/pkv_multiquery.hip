@@ -39,8 +39,7 @@ namespace {
 
 using namespace pkvd;
 
-constexpr int kCols = 16;       // MFMA tile columns
-constexpr int kPlanCUs = 256;   // compute units of an MI355X
+constexpr int kCols = 16;   // MFMA tile columns
 
 struct MQParams {
   void* out;
@@ -715,7 +714,7 @@ int launch_mq_split_merge_t(const pkv::MQArgs& a) {
   // the items instead.
   const int64_t nitems = (int64_t)sp.b.S * sp.b.qtiles * sp.Y * sp.b.ntl * 4;
   int64_t grid = (nitems + pkv::kWaves - 1) / pkv::kWaves;
-  if (grid > 2 * kPlanCUs) grid = 2 * kPlanCUs;
+  if (grid > 2 * pkv::kCUs) grid = 2 * pkv::kCUs;
   if (grid < 1) grid = 1;
   return pkv::launch_kernel(multiquery_split_merge_kernel<QT, D>, dim3((unsigned)grid),
                             dim3(64 * pkv::kWaves), a.stream, sp, a.ev_start, a.ev_stop);
