@@ -217,42 +217,50 @@ __global__ __launch_bounds__(64 * kVecWaves) void decode_vec_kernel(DecodeParams
   merge_waves_and_store<QT, D, GMAX, kVecWaves>(p, sm_m, sm_l, sm_o, nh, s, h_first, part);
 }
 
-// Split-K reduction: one wave per (sequence, q-head) merges the partitions
-// that cover the sequence's context,
+// Split-K reduction: one workgroup of NW waves per (sequence, q-head)
+// merges the partitions that cover the sequence's context,
 //   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  out = sum_p acc_p 2^(m_p - M) / L.
-// Lane p computes partition p's weight; the accumulation then reads every
-// partition's row with independent loads.
-template <int QT, int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
+// Wave w merges a contiguous 1/NW of the partitions the same way (lane p
+// holds partition p's weight, and the accumulator rows are read with
+// independent loads, eight at a time); the waves' (M_w, L_w, acc_w) are then
+// combined in LDS by the same rule.  With many partitions one wave per row
+// keeps too few loads in flight (64 partitions take eight dependent rounds);
+// with few, the combine costs more than it saves.
+template <int QT, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_reduce_kernel(DecodeParams p) {
+  constexpr int PER = (D + 63) / 64;
+  __shared__ float sm_m[NW], sm_l[NW];
+  __shared__ float sm_acc[NW][D];
   const int row = blockIdx.x;            // s * Hq + h
   const int s = row / p.Hq;
   const int ctx = clamped_ctx(p, s);
   const int part_tokens = p.part_blocks * pkv::kBlockSize;
   int np = (ctx + part_tokens - 1) / part_tokens;
   np = np < 1 ? 1 : (np > p.num_parts ? p.num_parts : np);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p0 = np * w / NW, p1 = np * (w + 1) / NW;   // this wave's partitions
   const float* m = p.ws_m + (int64_t)row * p.num_parts;
   const float* l = p.ws_l + (int64_t)row * p.num_parts;
   const float* a = p.ws_acc + (int64_t)row * p.num_parts * D;
-  const int lane = threadIdx.x;
   float M = kNegInf;
-  for (int i = lane; i < np; i += 64) M = fmaxf(M, l[i] > 0.f ? m[i] : kNegInf);
+  for (int i = p0 + lane; i < p1; i += 64) M = fmaxf(M, l[i] > 0.f ? m[i] : kNegInf);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-  constexpr int PER = (D + 63) / 64;
   float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
   float L = 0.f;
   if (M != kNegInf) {
-    for (int base = 0; base < np; base += 64) {
+    for (int base = p0; base < p1; base += 64) {
       const int i = base + lane;
       float wgt = 0.f;
-      if (i < np) {
+      if (i < p1) {
         const float li = l[i];
         wgt = li > 0.f ? __builtin_amdgcn_exp2f(m[i] - M) : 0.f;
         L += wgt * li;
       }
-      const int cnt = min(64, np - base);
+      const int cnt = min(64, p1 - base);
       const float* ab = a + (int64_t)base * D;
       // 8 partitions per round, loads issued together (rows past cnt are
       // not read: their weight is zero and the load is predicated off)
@@ -278,10 +286,39 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off);
+  if constexpr (NW == 1) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int d = lane + 64 * k;
+      if (d < D) store_out<QT>(p.out, (int64_t)row * D + d, L > 0.f ? acc[k] / L : 0.f);
+    }
+    return;
+  }
+  // combine the waves' partial merges
+  if (lane == 0) {
+    sm_m[w] = M;
+    sm_l[w] = L;
+  }
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int d = lane + 64 * k;
-    if (d < D) store_out<QT>(p.out, (int64_t)row * D + d, L > 0.f ? acc[k] / L : 0.f);
+    if (d < D) sm_acc[w][d] = acc[k];
+  }
+  __syncthreads();
+  float Mt = kNegInf;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) Mt = fmaxf(Mt, sm_l[v] > 0.f ? sm_m[v] : kNegInf);
+  float f[NW], Lt = 0.f;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    f[v] = (Mt != kNegInf && sm_l[v] > 0.f) ? __builtin_amdgcn_exp2f(sm_m[v] - Mt) : 0.f;
+    Lt += f[v] * sm_l[v];
+  }
+  for (int d = threadIdx.x; d < D; d += 64 * NW) {
+    float o = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) o = fmaf(f[v], sm_acc[v][d], o);
+    store_out<QT>(p.out, (int64_t)row * D + d, Lt > 0.f ? o / Lt : 0.f);
   }
 }
 
@@ -305,8 +342,13 @@ int launch_vec_g(const pkv::DecodeArgs& a) {
 template <int QT, int D>
 int launch_reduce_t(const pkv::DecodeArgs& a) {
   const DecodeParams kp = make_params(a, 16);
-  return pkv::launch_kernel(decode_reduce_kernel<QT, D>, dim3(a.num_seqs * a.num_q_heads),
-                            dim3(64), a.stream, kp, a.ev_start, a.ev_stop);
+  // four waves per row only when rows can have many partitions
+  const dim3 grid(a.num_seqs * a.num_q_heads);
+  if (kp.num_parts > 16)
+    return pkv::launch_kernel(decode_reduce_kernel<QT, D, 4>, grid, dim3(256), a.stream, kp,
+                              a.ev_start, a.ev_stop);
+  return pkv::launch_kernel(decode_reduce_kernel<QT, D, 1>, grid, dim3(64), a.stream, kp,
+                            a.ev_start, a.ev_stop);
 }
 
 }  // namespace
