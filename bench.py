@@ -116,6 +116,9 @@ def decode_path(cfg, algo, partition):
     # balanced schedule, so the helper reports the fixed choice)
     ps = pkv.decode_partition_size(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
                                    cfg.max_blocks_per_seq, DT_CODE["f32"], partition)
+    if a == "mfma" and ps < cfg.max_blocks_per_seq * 16 and cfg.num_seqs <= 2048:
+        # several fixed partitions: the persistent grid in partition mode
+        return "decode_stream_kernel", a, ps
     return ("decode_mfma_kernel" if a == "mfma" else "decode_vec_kernel"), a, ps
 
 

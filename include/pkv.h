@@ -212,7 +212,11 @@ int32_t pkv_decode_algo_for(int32_t num_q_heads, int32_t num_kv_heads, int32_t h
  *                  waves, when the algo resolves to MFMA and the cache is
  *                  16-bit or FP8; else fixed partitions of its choice), else
  *                  a multiple of 16 in [16, 2^20] (fixed partitions plus the
- *                  reduction kernel when a context spans several).
+ *                  reduction kernel when a context spans several).  On the
+ *                  matrix cores, with several partitions, a persistent grid
+ *                  computes the partitions (each one whole in one wave, the
+ *                  waves' shares cut at partition boundaries); the result
+ *                  does not depend on the grid size.
  *   workspace    : device memory of at least pkv_decode_workspace_size(...)
  *                  bytes (may be NULL when that is 0).  Its contents on entry
  *                  do not matter; calls sharing one workspace must not

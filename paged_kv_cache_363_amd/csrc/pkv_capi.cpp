@@ -70,6 +70,14 @@ static int32_t resolve_algo(int32_t g, int32_t q, int32_t kv) {
 
 static std::atomic<int32_t> g_stream_workgroups{kDefaultStreamWorkgroups};
 
+#ifndef PKV_PARTS_ON_STREAM_GRID
+#define PKV_PARTS_ON_STREAM_GRID 1
+#endif
+// MFMA calls with fixed partitions run on the persistent grid (one pipelined
+// pass per wave through whole partitions) rather than one workgroup per
+// partition.
+constexpr bool kPartsOnStreamGrid = PKV_PARTS_ON_STREAM_GRID != 0;
+
 struct Plan {
   // fixed partitions (the partition kernels plus the reduction kernel)
   int32_t partition;
@@ -78,6 +86,9 @@ struct Plan {
   size_t off_l, off_acc;
   // balanced schedule (partition_size == 0, MFMA-capable caches)
   bool stream_ok;
+  // the fixed partitions on the balanced schedule's persistent grid
+  // (partition_size > 0 with more than one partition, MFMA-capable caches)
+  bool parts_stream_ok;
   int32_t stream_grid;
   size_t stream_off_ml, stream_off_part, stream_bytes;
 };
@@ -115,10 +126,11 @@ static bool make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
   const int32_t g = num_q_heads / num_kv_heads;
   const int32_t chunk = g < 16 ? g : 16;
   const int64_t Y = (int64_t)num_kv_heads * ((g + chunk - 1) / chunk);
-  plan->stream_ok = partition_size == 0 && stream_capable_kv(kv_dtype) &&
-                    num_seqs <= kMaxStreamSeqs &&
-                    (int64_t)num_seqs * (max_blocks_per_seq + kv_restart_units(kv_dtype)) * Y <
-                        ((int64_t)1 << 31);
+  const bool grid_ok = stream_capable_kv(kv_dtype) && num_seqs <= kMaxStreamSeqs &&
+                       (int64_t)num_seqs * (max_blocks_per_seq + kv_restart_units(kv_dtype)) * Y <
+                           ((int64_t)1 << 31);
+  plan->stream_ok = partition_size == 0 && grid_ok;
+  plan->parts_stream_ok = kPartsOnStreamGrid && partition_size > 0 && plan->num_parts > 1 && grid_ok;
   plan->stream_grid = g_stream_workgroups.load();
   plan->stream_off_ml = plan->stream_off_part = plan->stream_bytes = 0;
   if (plan->stream_ok) {
@@ -541,7 +553,10 @@ static pkv_status decode_impl(
                   hipGetErrorString((hipError_t)rc));
     return PKV_OK;
   }
-  int rc = (algo == PKV_ALGO_MFMA) ? launch_decode_mfma(a) : launch_decode_vector(a);
+  int rc = (algo == PKV_ALGO_MFMA)
+               ? (plan.parts_stream_ok ? launch_decode_stream_parts(a, plan.stream_grid)
+                                       : launch_decode_mfma(a))
+               : launch_decode_vector(a);
   if (rc != 0)
     return fail(PKV_ERR_HIP, "decode: launch failed: %s", hipGetErrorString((hipError_t)rc));
   if (plan.num_parts > 1) {

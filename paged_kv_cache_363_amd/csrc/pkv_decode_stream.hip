@@ -22,6 +22,20 @@
 // Both kernels derive the shares from the same prefix sums of the block
 // counts, so the workspace carries nothing but the partial slots.
 //
+// Fixed partitions (partition mode): when the caller fixes the split-K
+// partition size, the same persistent grid computes one (m, l, acc) per
+// partition of P blocks into the fixed-partition workspace, and the
+// split-K reduction kernel merges them.  The shares' boundaries are moved up
+// to the next partition boundary, so every partition belongs to one wave,
+// and a wave closes each of its partitions when it has consumed the
+// partition's last block, with the loads of the next blocks in flight: the
+// load pipeline runs through a wave's whole share instead of restarting for
+// every partition, as one workgroup per partition would.  A closed partition
+// goes to a stash in LDS, not to memory: a store issued between two loads in
+// flight holds up the wait for the older load until the store is
+// acknowledged (vector loads and stores share one counter on CDNA), so the
+// stash is written out only when it is full and at the end of the piece.
+//
 // Math: softmax(q K^T * scale) V over the block-table-gathered context
 // ("KV Cache 与 PageAttention深度实战", sections 1.2 and 3.2).
 #include <hip/hip_runtime.h>
@@ -38,12 +52,18 @@
 #ifndef PKV_NT_FP8
 #define PKV_NT_FP8 0           // non-temporal K/V loads for E4M3 caches
 #endif
+#ifndef PKV_NT_16
+#define PKV_NT_16 1            // non-temporal K/V loads for 16-bit caches
+#endif
 
 namespace {
 
 using namespace pkvd;
 
 constexpr int kSkWaves = 4;   // waves per workgroup; each wave is its own worker
+// partition mode: LDS stash of closed partitions, per wave
+constexpr int kStashFloats = 8192;   // accumulators (32 KiB)
+constexpr int kStashSlots = 16;      // at most this many partitions
 
 struct StreamParams {
   void* out;
@@ -60,6 +80,12 @@ struct StreamParams {
   int R;                       // restart units counted at the start of every segment
   const float* ks;             // per-channel K scales [Hkv][D] (nullptr: per tensor)
   const float* vs;             // per-channel V scales [Hkv][D]
+  // partition mode: P blocks per partition, the reduction's workspace
+  // (m, l: [S][Hq][num_parts], acc: [S][Hq][num_parts][D])
+  int P, num_parts;
+  float* ws_m;
+  float* ws_l;
+  float* ws_acc;
 };
 
 // Unit prefix sums in LDS, computed by one workgroup of 4 waves.  A segment
@@ -99,7 +125,8 @@ __device__ __forceinline__ void block_prefix(const StreamParams& p, int* sm_pref
 }
 
 // PC: a one-byte-code cache with per-channel scales (p.ks, p.vs).
-template <int QT, int KVT, int D, bool PC>
+// PM: partition mode (p.P blocks per partition).
+template <int QT, int KVT, int D, bool PC, bool PM>
 __global__ __launch_bounds__(64 * kSkWaves) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void decode_stream_kernel(StreamParams p) {
   using T = MfmaTile<QT, KVT, D>;
@@ -108,6 +135,10 @@ void decode_stream_kernel(StreamParams p) {
 
   __shared__ int sm_pref[pkv::kMaxStreamSeqs + 1];   // segment units before sequence s
   __shared__ int sm_ctx[pkv::kMaxStreamSeqs];        // clamped context lengths
+  // partition mode: closed partitions of each wave, [slot][head][D] and
+  // [slot][head][2] (m, l)
+  __shared__ float sm_stash[PM ? kSkWaves * kStashFloats : 1];
+  __shared__ float sm_stml[PM ? kSkWaves * kStashSlots * 16 * 2 : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -120,10 +151,20 @@ void decode_stream_kernel(StreamParams p) {
   const int W = p.W;
   const int wk = blockIdx.x * kSkWaves + w;
 
-  // sequences without context get zero rows
-  for (int s = wk; s < S; s += W)
-    if (sm_ctx[s] == 0)
+  // sequences without context get zero rows (in partition mode: an empty
+  // first partition, which the reduction turns into zeros)
+  for (int s = wk; s < S; s += W) {
+    if (sm_ctx[s] != 0) continue;
+    if constexpr (PM) {
+      for (int h = lane; h < p.Hq; h += 64) {
+        const int64_t prow = ((int64_t)s * p.Hq + h) * p.num_parts;
+        p.ws_m[prow] = kNegInf;
+        p.ws_l[prow] = 0.f;
+      }
+    } else {
       for (int i = lane; i < p.Hq * D; i += 64) store_out<QT>(p.out, (int64_t)s * p.Hq * D + i, 0.f);
+    }
+  }
 
   const int64_t We = U < W ? U : W;   // workers with a non-empty share
   if (wk >= We) return;
@@ -220,8 +261,15 @@ void decode_stream_kernel(StreamParams p) {
     const int len = sm_pref[s + 1] - sm_pref[s];
     const int64_t seg_start = Y * sm_pref[s] + (int64_t)y * len;
     const int64_t pe = seg_start + len < u_hi ? seg_start + len : u_hi;
-    const int b = max(j - p.R, 0);
-    const int b1 = max((int)(pe - seg_start) - p.R, 0);
+    int b = max(j - p.R, 0);
+    int b1 = max((int)(pe - seg_start) - p.R, 0);
+    if constexpr (PM) {
+      // both ends up to the next partition boundary (or the segment's end);
+      // the neighbouring share moves the same boundary the same way
+      const int nbk = len - p.R;
+      b = min((b + p.P - 1) / p.P * p.P, nbk);
+      b1 = min((b1 + p.P - 1) / p.P * p.P, nbk);
+    }
     if (b1 > b) {
       const int hc = y % p.hchunks;
       const int hk = y / p.hchunks;
@@ -234,14 +282,71 @@ void decode_stream_kernel(StreamParams p) {
       reset();
       const int ctx = sm_ctx[s];
       const int last = ((ctx + 15) >> 4) - 1;
-      if (p.nb > 0) {
-        const int64_t off = (int64_t)hk * T::TILE;
-        mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
-                   !pkv::byte_codes(KVT) || PKV_NT_FP8, false, PC>(
-            p.kc + off, p.vc + off, blk_stride, p.bt + (int64_t)s * p.mb, b, b1, last,
-            ctx - 16 * last, p.nb, qr, p.sl2, &m_run, &l_run, o, lane, nullptr, qlo);
+      constexpr int DEPTH = pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH;
+      constexpr bool NT = pkv::byte_codes(KVT) ? PKV_NT_FP8 : PKV_NT_16;
+      const int64_t off = (int64_t)hk * T::TILE;
+      if constexpr (PM) {
+        // Close partition kp0 + n_st into stash slot n_st and start the next
+        // partition; write the stash out when it is full and at the end.
+        // Lane (G, c) stashes and later stores its own 4 * DPL accumulators,
+        // so no other lane reads what it wrote.
+        const int h_first = hk * p.g + hc * p.chunk_heads;
+        const int HS = p.chunk_heads;
+        const int slots = min(kStashSlots, kStashFloats / (HS * D));
+        float* st = sm_stash + w * kStashFloats + c * D + DPL * 4 * G;
+        float* stml = sm_stml + w * kStashSlots * 32 + 2 * c;
+        int kp0 = b / p.P, n_st = 0;
+        auto write_out = [&]() {
+          if (c < nh) {
+            const int64_t row = (int64_t)s * p.Hq + h_first + c;
+            for (int k = 0; k < n_st; ++k) {
+              const int64_t prow = row * p.num_parts + kp0 + k;
+              const float* src = st + k * HS * D;
+              float* dst = p.ws_acc + prow * D + DPL * 4 * G;
+#pragma unroll
+              for (int i = 0; i < 4 * DPL; ++i) dst[i] = src[i];
+              if (G == 0) {
+                p.ws_m[prow] = stml[k * 32];
+                p.ws_l[prow] = stml[k * 32 + 1];
+              }
+            }
+          }
+          kp0 += n_st;
+          n_st = 0;
+        };
+        auto close = [&]() {
+          const float l_tot = wave_sum4(l_run);
+          if (c < nh) {
+            float* dst = st + n_st * HS * D;
+            const float* vs = PC ? p.vs + (int64_t)hk * D + DPL * 4 * G : nullptr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int e = 0; e < DPL; ++e)
+                dst[DPL * i + e] = o[e][i] * (PC ? vs[DPL * i + e] : p.vsc);
+            if (G == 0) {
+              stml[n_st * 32] = m_run;
+              stml[n_st * 32 + 1] = l_tot;
+            }
+          }
+          if (++n_st == slots) write_out();
+          reset();
+        };
+        const PeriodHook<decltype(close)> hook{p.P, close};
+        if (p.nb > 0)
+          mfma_piece<QT, KVT, D, DEPTH, NT, false, PC, 1, PeriodHook<decltype(close)>>(
+              p.kc + off, p.vc + off, blk_stride, p.bt + (int64_t)s * p.mb, b, b1, last,
+              ctx - 16 * last, p.nb, qr, p.sl2, &m_run, &l_run, o, lane, nullptr, qlo, hook);
+        else   // no block can be valid: every partition is empty
+          for (int k = b / p.P; k < (b1 + p.P - 1) / p.P; ++k) close();
+        write_out();
+      } else {
+        if (p.nb > 0)
+          mfma_piece<QT, KVT, D, DEPTH, NT, false, PC>(
+              p.kc + off, p.vc + off, blk_stride, p.bt + (int64_t)s * p.mb, b, b1, last,
+              ctx - 16 * last, p.nb, qr, p.sl2, &m_run, &l_run, o, lane, nullptr, qlo);
+        finish(s, y, b, b1 - 1, first_piece);
       }
-      finish(s, y, b, b1 - 1, first_piece);
       first_piece = false;
     }
     u = pe;
@@ -297,16 +402,22 @@ __global__ __launch_bounds__(64 * kSkWaves) void decode_split_merge_kernel(Strea
   }
 }
 
-template <int QT, int KVT, int D>
-int launch_t(const pkv::DecodeArgs& a, const StreamParams& sp, int grid) {
+template <int QT, int KVT, int D, bool PM>
+int launch_pm(const pkv::DecodeArgs& a, const StreamParams& sp, int grid) {
   const dim3 block(64 * kSkWaves);
   if constexpr (pkv::byte_codes(KVT)) {
     if (sp.ks)
-      return pkv::launch_kernel(decode_stream_kernel<QT, KVT, D, true>, dim3(grid), block,
+      return pkv::launch_kernel(decode_stream_kernel<QT, KVT, D, true, PM>, dim3(grid), block,
                                 a.stream, sp, a.ev_start, a.ev_stop);
   }
-  return pkv::launch_kernel(decode_stream_kernel<QT, KVT, D, false>, dim3(grid), block, a.stream,
-                            sp, a.ev_start, a.ev_stop);
+  return pkv::launch_kernel(decode_stream_kernel<QT, KVT, D, false, PM>, dim3(grid), block,
+                            a.stream, sp, a.ev_start, a.ev_stop);
+}
+
+template <int QT, int KVT, int D>
+int launch_t(const pkv::DecodeArgs& a, const StreamParams& sp, int grid) {
+  if (sp.P > 0) return launch_pm<QT, KVT, D, true>(a, sp, grid);
+  return launch_pm<QT, KVT, D, false>(a, sp, grid);
 }
 
 template <int QT, int D>
@@ -346,6 +457,9 @@ StreamParams make_stream_params(const pkv::DecodeArgs& a, int grid, void* ws, si
   sp.R = pkv::kv_restart_units(a.kv_dtype);
   sp.ks = kp.ks;
   sp.vs = kp.vs;
+  sp.P = 0;
+  sp.num_parts = 0;
+  sp.ws_m = sp.ws_l = sp.ws_acc = nullptr;
   return sp;
 }
 
@@ -356,6 +470,33 @@ namespace pkv {
 int launch_decode_stream(const DecodeArgs& a, int grid, void* ws, size_t off_ml,
                          size_t off_part) {
   const StreamParams sp = make_stream_params(a, grid, ws, off_ml, off_part);
+  const int q = a.q_dtype, kv = a.kv_dtype, D = a.head_dim;
+#define PKV_STREAM_CASE(QT, KVT, DD) \
+  if (q == QT && kv == KVT && D == DD) return launch_t<QT, KVT, DD>(a, sp, grid);
+  PKV_STREAM_CASE(PKV_BF16, PKV_BF16, 128)
+  PKV_STREAM_CASE(PKV_BF16, PKV_BF16, 64)
+  PKV_STREAM_CASE(PKV_F16, PKV_F16, 128)
+  PKV_STREAM_CASE(PKV_F16, PKV_F16, 64)
+  PKV_STREAM_CASE(PKV_BF16, PKV_FP8_E4M3, 128)
+  PKV_STREAM_CASE(PKV_BF16, PKV_FP8_E4M3, 64)
+  PKV_STREAM_CASE(PKV_F16, PKV_FP8_E4M3, 128)
+  PKV_STREAM_CASE(PKV_F16, PKV_FP8_E4M3, 64)
+  PKV_STREAM_CASE(PKV_BF16, PKV_INT8, 128)
+  PKV_STREAM_CASE(PKV_BF16, PKV_INT8, 64)
+  PKV_STREAM_CASE(PKV_F16, PKV_INT8, 128)
+  PKV_STREAM_CASE(PKV_F16, PKV_INT8, 64)
+#undef PKV_STREAM_CASE
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_decode_stream_parts(const DecodeArgs& a, int grid) {
+  StreamParams sp = make_stream_params(a, grid, nullptr, 0, 0);
+  sp.ml = sp.part = nullptr;
+  sp.P = a.partition / kBlockSize;
+  sp.num_parts = a.num_parts;
+  sp.ws_m = a.ws_m;
+  sp.ws_l = a.ws_l;
+  sp.ws_acc = a.ws_acc;
   const int q = a.q_dtype, kv = a.kv_dtype, D = a.head_dim;
 #define PKV_STREAM_CASE(QT, KVT, DD) \
   if (q == QT && kv == KVT && D == DD) return launch_t<QT, KVT, DD>(a, sp, grid);

@@ -135,6 +135,8 @@ int launch_decode_vector(const DecodeArgs& a);
 int launch_decode_mfma(const DecodeArgs& a);
 int launch_decode_reduce(const DecodeArgs& a);
 int launch_decode_stream(const DecodeArgs& a, int grid, void* ws, size_t off_ml, size_t off_part);
+// fixed partitions on the persistent grid: partials into a.ws_m / ws_l / ws_acc
+int launch_decode_stream_parts(const DecodeArgs& a, int grid);
 int launch_decode_split_merge(const DecodeArgs& a, int grid, void* ws, size_t off_ml,
                               size_t off_part);
 int launch_cache_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,

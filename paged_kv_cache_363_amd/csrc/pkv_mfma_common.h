@@ -394,19 +394,40 @@ struct MfmaTile {
 // CAUSAL: column tile j of the lane attends to positions <= pos[j] only
 // (several queries of one sequence in one pass); otherwise pos is ignored.
 // PC: per-channel K scales, qlo the remainder of the scaled q (load_q_scaled).
+// Hook: with Hook::active, hook() runs after the last block of every run of
+// hook.period blocks (runs aligned to multiples of the period) and after the
+// piece's last block; it may read and reset the running state.  The loads of
+// the next blocks stay in flight across it.
+struct NoHook {
+  static constexpr bool active = false;
+  int period = 0;
+  __device__ void operator()() const {}
+};
+
+// A hook that calls f every `period` blocks.
+template <typename F>
+struct PeriodHook {
+  static constexpr bool active = true;
+  int period;
+  F f;
+  __device__ void operator()() const { f(); }
+};
+
 template <int QT, int KVT, int D, int DEPTH, bool NT, bool CAUSAL = false, bool PC = false,
-          int NTL = 1>
+          int NTL = 1, typename Hook = NoHook>
 __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
                                            int64_t blk_stride, const int32_t* row, int b0,
                                            int b1, int last, int tail, int nb, const uint4* qr,
                                            float sl2, float* m_run, float* l_run, f32x4* o,
                                            int lane, const int* pos = nullptr,
-                                           const uint4* qlo = nullptr) {
+                                           const uint4* qlo = nullptr,
+                                           const Hook& hook = Hook{}) {
   using T = MfmaTile<QT, KVT, D>;
   using Raw = typename T::Raw;
   const int c = lane & 15, G = lane >> 4;
   const uint32_t koff = T::k_lane_off(c, G), voff = T::v_lane_off(c, G);
   constexpr int NW = PKV_ID_VGPRS;
+  [[maybe_unused]] int rem = Hook::active ? hook.period - b0 % hook.period : 0;
   for (int c0 = b0; c0 < b1; c0 += 64 * NW) {
     const int n = min(64 * NW, b1 - c0);
     int ids[NW];
@@ -443,6 +464,12 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
         for (int j = 0; j < NTL; ++j)
           vis[j] = CAUSAL ? min(valid, pos[j] - 16 * (c0 + ii) + 1) : valid;
         T::template consume<NTL, PC>(buf[d], valid, vis, qr, sl2, m_run, l_run, o, c, G, qlo);
+        if constexpr (Hook::active) {
+          if (ii < n && (--rem == 0 || c0 + ii == b1 - 1)) {
+            hook();
+            rem = hook.period;
+          }
+        }
         const int64_t a = addr(idn);
         T::template issue<NT>(buf[d], kc + a, vc + a, koff, voff);
         idc[d] = idn;

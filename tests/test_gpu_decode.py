@@ -92,6 +92,31 @@ def test_balanced_schedule_any_grid(name, wgs):
     check_parity(name, out, seqs, ref)
 
 
+@pytest.mark.parametrize("wgs", [1, 3, 37, 512, 2048])
+@pytest.mark.parametrize("name,ps", [("c2_qwen3_8b_bf16", 512), ("c2_qwen3_8b_bf16", 16),
+                                     ("c4_llama3_70b_fp8", 256)])
+def test_fixed_partitions_on_any_grid(name, ps, wgs):
+    """Fixed partitions on the MFMA path run on the persistent grid: share
+    boundaries move up to partition boundaries, each wave closes whole
+    partitions into an LDS stash and writes it out when full (16-token
+    partitions fill it many times per share), and the split-K reduction merges
+    them.  Every grid size must give the oracle's answer, and the same bits as
+    the default grid."""
+    import paged_kv_cache_363_amd as pkv
+    print(f"[case] fixed partitions {name} partition={ps} workgroups={wgs}", flush=True)
+    st = gpu_state(name)
+    seqs, ref, _ = oracle_ref(name)
+    base = run_decode(st, "mfma", ps)
+    pkv.lib().pkv_set_stream_workgroups(wgs)
+    try:
+        out = run_decode(st, "mfma", ps)
+    finally:
+        pkv.lib().pkv_set_stream_workgroups(0)
+    check_parity(name, out, seqs, ref)
+    # a partition's (m, l, acc) does not depend on which wave computed it
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+
+
 def test_balanced_schedule_ignores_stale_workspace():
     """The workspace only carries partials written and read within one call:
     a workspace full of garbage or left by earlier calls gives the same
