@@ -18,8 +18,11 @@
 #ifndef PKV_PIPE_DEPTH_FP8
 #define PKV_PIPE_DEPTH_FP8 2   // same for E4M3 caches
 #endif
-#ifndef PKV_MFMA_NT
-#define PKV_MFMA_NT false      // non-temporal K/V loads
+#ifndef PKV_MFMA_NT16
+#define PKV_MFMA_NT16 false    // non-temporal K/V loads, 16-bit caches
+#endif
+#ifndef PKV_MFMA_NT8
+#define PKV_MFMA_NT8 true      // non-temporal K/V loads, one-byte codes
 #endif
 #ifndef PKV_MFMA_WPE
 #define PKV_MFMA_WPE 2     // minimum waves per SIMD the register budget must allow
@@ -75,7 +78,8 @@ void decode_mfma_kernel(DecodeParams p) {
   if (p.nb > 0 && w1 > w0) {
     const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
     const int64_t head_off = (int64_t)hk * T::TILE;
-    mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH, PKV_MFMA_NT,
+    mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
+               pkv::byte_codes(KVT) ? PKV_MFMA_NT8 : PKV_MFMA_NT16,
                false, PC>(p.kc + head_off, p.vc + head_off, blk_stride,
                                            p.bt + (int64_t)s * p.mb, w0, w1, nblk - 1,
                                            ctx - 16 * (nblk - 1), p.nb, qr, p.sl2, &m_run, &l_run,

@@ -50,7 +50,7 @@
 #define PKV_PIPE_DEPTH_FP8 2   // same for E4M3 caches
 #endif
 #ifndef PKV_NT_FP8
-#define PKV_NT_FP8 0           // non-temporal K/V loads for E4M3 caches
+#define PKV_NT_FP8 1           // non-temporal K/V loads for one-byte codes
 #endif
 #ifndef PKV_NT_16
 #define PKV_NT_16 1            // non-temporal K/V loads for 16-bit caches

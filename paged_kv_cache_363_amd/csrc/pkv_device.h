@@ -55,6 +55,21 @@ __device__ __forceinline__ uint32_t ld_tile4(const void* p) {
   }
 }
 
+// The same loads kept in the loaded vector type.  A loop that carries the
+// result of a non-temporal load across its back edge after converting it to
+// a struct type (uint4, uint2) can get register copies there, and a copy of
+// a register still being loaded waits for every load in flight.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_vec16(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ u32x2 ld_vec8(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  else return *reinterpret_cast<const u32x2*>(p);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
 

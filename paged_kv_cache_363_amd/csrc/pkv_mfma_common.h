@@ -116,11 +116,16 @@ __device__ __forceinline__ V as_v8(uint4 r) {
   return __builtin_bit_cast(V, r);
 }
 template <typename V>
+__device__ __forceinline__ V as_v8(u32x4 r) {
+  return __builtin_bit_cast(V, r);
+}
+template <typename V>
 __device__ __forceinline__ V as_v4(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(V, make_uint2(a, b));
 }
 
-// Row of V for one token as seen by one lane: DPL elements of the kv type.
+// Row of V for one token as seen by one lane: DPL elements of the kv type,
+// held in the loaded vector type (see ld_vec16).
 template <int BYTES>
 struct Row;
 template <>
@@ -129,22 +134,20 @@ struct Row<4> {
 };
 template <>
 struct Row<8> {
-  uint32_t w[2];
+  u32x2 w;
 };
 template <>
 struct Row<16> {
-  uint32_t w[4];
+  u32x4 w;
 };
 
 template <int BYTES, bool NT>
 __device__ __forceinline__ Row<BYTES> load_row(const uint8_t* ptr) {
   Row<BYTES> r;
   if constexpr (BYTES == 16) {
-    uint4 v = ld_tile16<NT>(ptr);
-    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    r.w = ld_vec16<NT>(ptr);
   } else if constexpr (BYTES == 8) {
-    uint2 v = ld_tile8<NT>(ptr);
-    r.w[0] = v.x; r.w[1] = v.y;
+    r.w = ld_vec8<NT>(ptr);
   } else {
     r.w[0] = ld_tile4<NT>(ptr);
   }
@@ -186,7 +189,7 @@ struct MfmaTile {
   }
 
   struct Raw {
-    uint4 k[KL];
+    u32x4 k[KL];
     Row<ROWB> v[4];
   };
 
@@ -251,7 +254,7 @@ struct MfmaTile {
     const uint8_t* kp = kt + koff;
     const uint8_t* vp = vt + voff;
 #pragma unroll
-    for (int kk = 0; kk < KL; ++kk) r.k[kk] = ld_tile16<NT>(kp + 64 * kk);
+    for (int kk = 0; kk < KL; ++kk) r.k[kk] = ld_vec16<NT>(kp + 64 * kk);
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) r.v[rr] = load_row<ROWB, NT>(vp + rr * D * KVB);
   }
@@ -275,7 +278,7 @@ struct MfmaTile {
     if constexpr (BYTE) {
 #pragma unroll
       for (int mm = 0; mm < KL; ++mm) {
-        const uint4 x = r.k[mm];
+        const u32x4 x = r.k[mm];
         kop[2 * mm] = as_v8<V8>(make_uint4(cvt2(x.x, false), cvt2(x.x, true),
                                            cvt2(x.y, false), cvt2(x.y, true)));
         kop[2 * mm + 1] = as_v8<V8>(make_uint4(cvt2(x.z, false), cvt2(x.z, true),
