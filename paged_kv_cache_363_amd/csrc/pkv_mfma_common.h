@@ -64,9 +64,10 @@ struct Mfma<PKV_BF16> {
                               hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
                                  : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
   }
+  // both halves rounded to nearest even in one v_cvt_pk_bf16_f32 (two
+  // scalar conversions cost two of them plus a shift and an or)
   __device__ static uint32_t pack2(float a, float b) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
   }
   // two INT8 codes (bytes 2*hi and 2*hi+1 of w) -> two bf16 (exact: |code| <= 127)
   __device__ static uint32_t i8x2(uint32_t w, bool hi) {
