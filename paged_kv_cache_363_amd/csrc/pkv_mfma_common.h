@@ -25,6 +25,9 @@
 
 #include "pkv_decode_common.h"
 
+#ifndef PKV_LAZY_RESCALE
+#define PKV_LAZY_RESCALE 8.0f   // see MfmaTile::consume
+#endif
 #ifndef PKV_ID_VGPRS
 #define PKV_ID_VGPRS 2   // block-id windows of 64 * PKV_ID_VGPRS blocks
 #endif
@@ -318,16 +321,23 @@ struct MfmaTile {
       for (int i = 0; i < 4; ++i) z[i] = (4 * G + i < vis[j]) ? sacc[i] * sl2 : kNegInf;
       float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
       bm = wave_max4(bm);
+      // The reference the weights are taken against moves only when the
+      // tile's maximum exceeds it by more than PKV_LAZY_RESCALE (base-2
+      // units): weights up to 2^PKV_LAZY_RESCALE, no rescale of l and acc
+      // for small rises.  l and acc keep one common reference, so the final
+      // acc / l (and the log-sum-exp merges) are the same in real arithmetic.
       const float m_new = fmaxf(m_run[j], bm);
-      // A tile with no valid token so far (m_new still -inf) shifts by 0, so
+      const float m_keep =
+          (m_run[j] != kNegInf && m_new <= m_run[j] + PKV_LAZY_RESCALE) ? m_run[j] : m_new;
+      // A tile with no valid token so far (m_keep still -inf) shifts by 0, so
       // that it leaves the state at zero instead of producing NaN.
-      const float m_ref = m_new == kNegInf ? 0.f : m_new;
+      const float m_ref = m_keep == kNegInf ? 0.f : m_keep;
       const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_ref);
       float pr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_ref);
       l_run[j] = l_run[j] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-      m_run[j] = m_new;
+      m_run[j] = m_keep;
       if (__any(alpha != 1.0f)) {
 #pragma unroll
         for (int e = 0; e < DPL; ++e) o[j * DPL + e] *= alpha;
