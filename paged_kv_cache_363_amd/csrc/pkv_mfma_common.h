@@ -304,21 +304,26 @@ struct MfmaTile {
 
     P4 pb[NTL];            // PV weights of each column tile
     [[maybe_unused]] V4 pl[NTL];   // their bf16 remainders (bf16 caches)
+    float alpha[NTL];      // rescale factor of each column tile's acc
+    // S = K Q^T of every column tile first (independent MFMA chains, one
+    // basic block): lane (G, c) gets tokens 4G+i, column c.
+    f32x4 sacc[NTL];
 #pragma unroll
     for (int j = 0; j < NTL; ++j) {
-      // S = K Q^T: lane (G, c) gets tokens 4G+i, column c.
-      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+      sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk)
-        sacc = M::qk(kop[kk], as_v8<V8>(qr[j * KSTEPS + kk]), sacc);
+        sacc[j] = M::qk(kop[kk], as_v8<V8>(qr[j * KSTEPS + kk]), sacc[j]);
       if constexpr (PC) {
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) sacc = M::qk(kop[kk], as_v8<V8>(qlo[kk]), sacc);
+        for (int kk = 0; kk < KSTEPS; ++kk) sacc[j] = M::qk(kop[kk], as_v8<V8>(qlo[kk]), sacc[j]);
       }
-
+    }
+#pragma unroll
+    for (int j = 0; j < NTL; ++j) {
       float z[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = (4 * G + i < vis[j]) ? sacc[i] * sl2 : kNegInf;
+      for (int i = 0; i < 4; ++i) z[i] = (4 * G + i < vis[j]) ? sacc[j][i] * sl2 : kNegInf;
       float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
       bm = wave_max4(bm);
       // The reference the weights are taken against moves only when the
@@ -332,16 +337,12 @@ struct MfmaTile {
       // A tile with no valid token so far (m_keep still -inf) shifts by 0, so
       // that it leaves the state at zero instead of producing NaN.
       const float m_ref = m_keep == kNegInf ? 0.f : m_keep;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_ref);
+      alpha[j] = __builtin_amdgcn_exp2f(m_run[j] - m_ref);
       float pr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_ref);
-      l_run[j] = l_run[j] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      l_run[j] = l_run[j] * alpha[j] + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
       m_run[j] = m_keep;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) o[j * DPL + e] *= alpha;
-      }
       // B operand of PV: k-slot (G, i) = token 4G+i, column c.
       pb[j] = as_v4<P4>(PM::pack2(pr[0], pr[1]), PM::pack2(pr[2], pr[3]));
       if constexpr (!PVH) {
@@ -351,6 +352,18 @@ struct MfmaTile {
         for (int i = 0; i < 4; ++i) lo[i] = pr[i] - M::rounded(pr[i]);
         pl[j] = as_v4<V4>(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]));
       }
+    }
+    // One branch for every column tile's rescale (a tile whose factor is 1
+    // is multiplied by 1, which changes nothing), so that the tiles' MFMA
+    // chains above are not cut into separate basic blocks.
+    bool resc = false;
+#pragma unroll
+    for (int j = 0; j < NTL; ++j) resc = resc || alpha[j] != 1.0f;
+    if (__any(resc)) {
+#pragma unroll
+      for (int j = 0; j < NTL; ++j)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[j * DPL + e] *= alpha[j];
     }
 
     // A operand of PV for m-tile e: dim DPL*c + e of tokens 4G..4G+3, built
