@@ -111,8 +111,11 @@ uint8_t orc_e4m3_encode(float x) {
   uint32_t u;
   memcpy(&u, &x, 4);
   int neg = (u >> 31) & 1;
-  if (isinf(x)) return (uint8_t)(neg ? 0xFE : 0x7E);
   double ax = fabs((double)x);
+  /* Beyond the largest code every magnitude saturates (infinities
+   * included).  The search below could not show it for huge values: there
+   * ax - code rounds to ax in double for every code and the distances tie. */
+  if (ax >= 448.0) return (uint8_t)(neg ? 0xFE : 0x7E);
   int best = 0;
   double best_d = INFINITY;
   for (int c = 0; c <= 126; ++c) {

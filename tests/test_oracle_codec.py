@@ -91,6 +91,27 @@ def test_e4m3_encode_saturates_and_nan():
     assert orc.e4m3_encode(x).tolist() == [0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7F, 0x7E]
 
 
+def test_e4m3_encode_saturates_every_large_magnitude():
+    # every bf16 magnitude from 448 to the largest finite float (the whole
+    # exponent range beyond the codes), both signs
+    pat = np.arange(0x43E0, 0x7F80, dtype=np.uint32) << np.uint32(16)
+    x = pat.view(np.float32)
+    x = np.concatenate([x, np.nextafter(x, np.float32(np.inf)), np.float32(3.4028235e38)[None]])
+    x = x[np.isfinite(x)]
+    assert np.all(orc.e4m3_encode(x) == 0x7E)
+    assert np.all(orc.e4m3_encode(-x) == 0xFE)
+
+
+def test_e4m3_encode_is_monotone_over_every_bf16_pattern():
+    # nearest-code rounding never decreases as the input grows
+    x = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16).view(np.uint16)
+    f = (x.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    f = np.sort(f[np.isfinite(f)])
+    dec = orc.to_f64(orc.e4m3_encode(f), "fp8")
+    assert np.all(np.diff(dec) >= 0)
+    assert dec[0] == -448.0 and dec[-1] == 448.0
+
+
 @pytest.mark.parametrize("dtype,tdt", [("f16", torch.float16), ("bf16", torch.bfloat16)])
 def test_16bit_decode_all_patterns_match_torch(dtype, tdt):
     pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
