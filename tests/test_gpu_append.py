@@ -149,3 +149,55 @@ def test_copy_blocks_bit_exact():
     ev[7], ev[8] = v0[1], v0[2]
     assert torch.equal(kc.view(torch.int16), ek.view(torch.int16))
     assert torch.equal(vc.view(torch.int16), ev.view(torch.int16))
+
+
+def _encode_on_gpu(x, codes, scale):
+    """Append the rows of x (a CPU tensor of any new dtype, length a multiple
+    of 128) as K and V with the given code type; return both caches' codes."""
+    import paged_kv_cache_363_amd as pkv
+    D = 128
+    T = x.numel() // D
+    rows = x.view(T, 1, D).cuda()
+    nb = (T + 15) // 16
+    kc = new_cache(nb, 1, D, codes, "cuda")
+    vc = new_cache(nb, 1, D, codes, "cuda")
+    slots = torch.arange(T, dtype=torch.int64, device="cuda")
+    pkv.paged_cache_append(kc, vc, rows, rows, slots, scale, scale)
+    torch.cuda.synchronize()
+    return (kc.cpu().numpy().reshape(-1, D)[:T].reshape(-1),
+            vc.cpu().numpy().reshape(-1, D)[:T].reshape(-1))
+
+
+@pytest.mark.parametrize("codes", ["fp8", "int8"])
+@pytest.mark.parametrize("new_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("scale", [1.0, 0.37, 3.1])
+def test_encode_every_16bit_input(codes, new_dtype, scale):
+    """Every one of the 65,536 bf16 (or f16) bit patterns, NaNs and infinities
+    included, encoded by the append kernel: bit for bit the oracle's codec on
+    fp32(x) * fp32(1 / scale)."""
+    print(f"[case] {codes} every {new_dtype} pattern, scale {scale}", flush=True)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[new_dtype]
+    x = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16).view(tdt)
+    scale = float(np.float32(scale))
+    gk, gv = _encode_on_gpu(x, codes, scale)
+    inv = np.float32(1.0) / np.float32(scale)
+    with np.errstate(invalid="ignore", over="ignore"):   # NaN and infinite inputs
+        xs = (x.float().numpy() * inv).astype(np.float32)
+    ref = orc.e4m3_encode(xs) if codes == "fp8" else orc.int8_encode(xs)
+    assert np.array_equal(gk, ref) and np.array_equal(gv, ref)
+
+
+@pytest.mark.parametrize("codes", ["fp8", "int8"])
+def test_encode_f32_patterns_one_in_256(codes):
+    """2^24 fp32 inputs, one in every 256 consecutive bit patterns (a random
+    low byte), covering every sign, exponent and the top 15 mantissa bits,
+    NaN and infinity patterns included, at scale 1: bit for bit the oracle's
+    codec."""
+    print(f"[case] {codes} fp32 patterns 1/256", flush=True)
+    rs = np.random.default_rng(5)
+    bits = (np.arange(1 << 24, dtype=np.uint64) << np.uint64(8)) | rs.integers(
+        0, 256, 1 << 24, dtype=np.uint64)
+    xs = bits.astype(np.uint32).view(np.float32)
+    gk, gv = _encode_on_gpu(torch.from_numpy(xs.copy()), codes, 1.0)
+    ref = orc.e4m3_encode(xs) if codes == "fp8" else orc.int8_encode(xs)
+    assert np.array_equal(gk, ref) and np.array_equal(gv, ref)
