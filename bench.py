@@ -390,8 +390,11 @@ def time_multiquery(mq, args, dev):
     for _ in range(R - 1):
         kcs.append(st["k_cache"].clone())
         vcs.append(st["v_cache"].clone())
+    # the host planner weighs the balanced schedule against one fixed pass
+    # with the batch's lengths, as a serving loop holding them would
     ps = pkv.multiquery_partition_size(cfg.num_seqs, max_q, cfg.num_q_heads, cfg.num_kv_heads,
-                                       cfg.max_blocks_per_seq, 0)
+                                       cfg.max_blocks_per_seq, 0, context_lens=st["ctx"],
+                                       kv_dtype=DT_CODE[cfg.kv_dtype])
     n = pkv.multiquery_workspace_size(rows, cfg.num_seqs, max_q, cfg.num_q_heads,
                                       cfg.num_kv_heads, cfg.head_dim, cfg.max_blocks_per_seq, ps)
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)

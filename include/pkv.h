@@ -344,6 +344,19 @@ pkv_status pkv_paged_multiquery_attention_profiled(
 int32_t pkv_multiquery_partition_size(int32_t num_seqs, int32_t max_query_len,
                                       int32_t num_q_heads, int32_t num_kv_heads,
                                       int32_t max_blocks_per_seq, int32_t partition_size);
+/* The partition_size to pass for a multi-query batch whose context lengths
+ * the caller holds on the host (context_lens, host int32[num_seqs]).  Where
+ * pkv_multiquery_partition_size(..., 0) picks the balanced schedule, this
+ * weighs it against one fixed pass of max_blocks_per_seq * 16 tokens, which
+ * then runs four column tiles per wave: the single pass when its workgroups
+ * (at most two per CU) finish no later than the balanced shares plus their
+ * merge, as with uniform draft verification.  Returns 0 or
+ * max_blocks_per_seq * 16 then; otherwise what pkv_multiquery_partition_size
+ * returns.  -1 on bad arguments (context_lens NULL with num_seqs > 0). */
+int32_t pkv_multiquery_partition_size_for_lengths(const int32_t* context_lens, int32_t num_seqs,
+                                                  int32_t max_query_len, int32_t num_q_heads,
+                                                  int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                                                  int32_t kv_dtype);
 /* Workspace bytes of a multi-query call.  Balanced schedule: float
  * (m, l)[2 W][16][2] and acc[2 W][16][head_dim] for the W = 4 x
  * pkv_set_stream_workgroups waves of its grid (two partial slots per wave),

@@ -37,6 +37,7 @@ SIGNATURES = {
                                                   I32, F32, I32, I32, F32, F32, I32, P, SZ, I32, P,
                                                   P, P, P]),
     "pkv_multiquery_partition_size": (I32, [I32, I32, I32, I32, I32, I32]),
+    "pkv_multiquery_partition_size_for_lengths": (I32, [P, I32, I32, I32, I32, I32, I32]),
     "pkv_multiquery_workspace_size": (SZ, [I32, I32, I32, I32, I32, I32, I32, I32]),
     "pkv_paged_multiquery_attention": (I32, [P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                              I32, I32, I32, F32, I32, I32, F32, F32, I32, P, SZ,

@@ -154,7 +154,20 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
 
 
 def multiquery_partition_size(num_seqs, max_query_len, num_q_heads, num_kv_heads,
-                              max_blocks_per_seq, partition_size=0):
+                              max_blocks_per_seq, partition_size=0, context_lens=None,
+                              kv_dtype=_lib.PKV_BF16):
+    """partition_size for a multi-query call (pkv_multiquery_partition_size).
+    With the batch's context lengths on the host (context_lens) and
+    partition_size 0, the choice weighs them
+    (pkv_multiquery_partition_size_for_lengths)."""
+    if context_lens is not None and partition_size == 0:
+        import numpy as np
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        if cl.shape != (num_seqs,):
+            raise ValueError("context_lens must hold num_seqs lengths")
+        return int(lib().pkv_multiquery_partition_size_for_lengths(
+            cl.ctypes.data, num_seqs, max_query_len, num_q_heads, num_kv_heads,
+            max_blocks_per_seq, kv_dtype))
     return int(lib().pkv_multiquery_partition_size(num_seqs, max_query_len, num_q_heads,
                                                    num_kv_heads, max_blocks_per_seq,
                                                    partition_size))

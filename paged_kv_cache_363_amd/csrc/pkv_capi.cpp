@@ -155,6 +155,13 @@ struct MQPlan {
   size_t st_off_part;              // the (m, l) slots start the workspace
 };
 
+// The fixed grid with four column tiles per wave has at most two workgroups
+// per CU.
+static bool mq_small_grid(int32_t num_seqs, int32_t num_kv_heads, int32_t g, int32_t mq) {
+  const MQTiles t4 = mq_tiles(g, mq, 4);
+  return (int64_t)num_seqs * num_kv_heads * t4.hchunks * t4.qtiles <= 2 * kCUs;
+}
+
 // Partition and workspace of a multi-query call; false on bad arguments.
 bool mq_plan(int32_t num_rows, int32_t num_seqs, int32_t max_query_len, int32_t num_q_heads,
              int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
@@ -204,11 +211,18 @@ bool mq_plan(int32_t num_rows, int32_t num_seqs, int32_t max_query_len, int32_t 
   // Fixed grid.  Several column tiles per wave read a (sequence, kv-head)'s
   // K/V once instead of once per row tile; that pays when the re-reads would
   // not stay in the L2, for tables of 8192 tokens or more (2-4 MB of K/V per
-  // kv-head at head_dim 128).  Shorter contexts keep one column tile, whose
-  // smaller register file lets two waves share a SIMD.  Measured: 512-row
-  // chunks at 32K tokens 18.1 -> 12.8 ms with four tiles; 64-row chunks of
-  // contexts up to 2048 tokens 0.72 -> 0.81 ms, so those keep one.
-  plan->max_ntl = max_ctx >= 8192 ? 4 : 1;
+  // kv-head at head_dim 128), and for a single pass whose four-tile grid is
+  // at most two workgroups per CU (there the row tiles of one kv-head, dealt
+  // round robin to the XCDs, would each fetch the K/V from HBM).  Otherwise
+  // one column tile, whose smaller register file lets two waves share a
+  // SIMD.  Measured: 512-row chunks at 32K tokens 18.1 -> 12.8 ms with four
+  // tiles; 8-row verification on the 70B-shaped E4M3 cache, one pass, 98.3
+  // -> 65.6 us; 64-row chunks of contexts up to 2048 tokens (8192 four-tile
+  // workgroups) 0.72 -> 0.81 ms, so those keep one.
+  const bool one_pass = partition_size >= max_ctx && max_ctx > 0;
+  plan->max_ntl = (max_ctx >= 8192 || (one_pass && mq_small_grid(num_seqs, num_kv_heads, g, mq)))
+                      ? 4
+                      : 1;
   const MQTiles t = mq_tiles(g, mq, plan->max_ntl);
   // workgroups per sequence and partition: kv-heads x head chunks x row tiles
   const int64_t per_seq = (int64_t)num_kv_heads * t.hchunks * t.qtiles;
@@ -650,6 +664,55 @@ int32_t pkv_multiquery_partition_size(int32_t num_seqs, int32_t max_query_len,
                partition_size, &plan))
     return -1;
   return plan.partition;
+}
+
+int32_t pkv_multiquery_partition_size_for_lengths(const int32_t* context_lens, int32_t num_seqs,
+                                                  int32_t max_query_len, int32_t num_q_heads,
+                                                  int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                                                  int32_t kv_dtype) {
+  const int32_t auto_ps = pkv_multiquery_partition_size(num_seqs, max_query_len, num_q_heads,
+                                                        num_kv_heads, max_blocks_per_seq, 0);
+  if (auto_ps != 0) return auto_ps;   // no balanced schedule to weigh (or bad arguments)
+  if (num_seqs > 0 && !context_lens) return -1;
+  const int64_t max_ctx = (int64_t)max_blocks_per_seq * kBlockSize;
+  const int32_t g = num_q_heads / num_kv_heads;
+  const int32_t mq = max_query_len > 0 ? max_query_len : 1;
+  if (max_ctx == 0 || max_ctx > kMaxPartition || !mq_small_grid(num_seqs, num_kv_heads, g, mq))
+    return 0;
+  const MQTiles t = mq_tiles(g, mq, 4);
+  const int64_t Y = (int64_t)num_kv_heads * t.hchunks;
+  const int64_t R = kv_restart_units(kv_dtype);
+  // Costs in block loads of one wave, as for decode (both schedules run four
+  // column tiles per wave here):
+  //  balanced: the grid's waves share every row tile's units equally, then
+  //            the merge kernel runs (its 16-column partials weigh about
+  //            kMergeUnits block loads);
+  //  one pass: a workgroup's four waves take a quarter of the sequence each
+  //            (plus one restart), list-scheduled over the CUs.
+  constexpr int64_t kMergeUnits = 8;
+  int64_t units = 0;
+  std::vector<int64_t> work(num_seqs);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t len = context_lens[s] < 0 ? 0 : (context_lens[s] > max_ctx ? max_ctx : context_lens[s]);
+    const int64_t nbk = (len + kBlockSize - 1) / kBlockSize;
+    units += nbk > 0 ? nbk + R : 0;
+    work[s] = nbk > 0 ? (nbk + kWaves - 1) / kWaves + R : 0;
+  }
+  if (units == 0) return 0;
+  const int64_t W = (int64_t)g_stream_workgroups.load() * kWaves;
+  const int64_t t_bal = (Y * t.qtiles * units + W - 1) / W + kMergeUnits;
+  std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+  for (int i = 0; i < kCUs; ++i) free_at.push(0);
+  int64_t t_fix = 0;
+  for (int32_t s = 0; s < num_seqs && t_fix <= t_bal; ++s) {
+    for (int64_t y = 0; y < Y * t.qtiles; ++y) {
+      const int64_t tt = free_at.top() + work[s];
+      free_at.pop();
+      free_at.push(tt);
+      if (tt > t_fix) t_fix = tt;
+    }
+  }
+  return t_fix <= t_bal ? (int32_t)max_ctx : 0;
 }
 
 size_t pkv_multiquery_workspace_size(int32_t num_rows, int32_t num_seqs, int32_t max_query_len,

@@ -66,3 +66,26 @@ def test_empty_or_missing_lengths():
     got = _lib.lib().pkv_decode_partition_size_for_lengths(None, 4, 32, 8, 128, 16, BF16)
     assert got == -1
     assert _lib.lib().pkv_decode_partition_size_for_lengths(None, 4, 30, 8, 128, 16, BF16) == -1
+
+
+def mq_plan(lens, max_q, hq, hkv, mb, kv):
+    lens = np.asarray(lens, np.int32)
+    return pkv.multiquery_partition_size(len(lens), max_q, hq, hkv, mb, 0, context_lens=lens,
+                                         kv_dtype=kv)
+
+
+def test_multiquery_uniform_verification_runs_one_pass():
+    # 32 sequences x 8 kv-heads, 8 rows of 8 q-heads: 256 four-tile workgroups
+    assert mq_plan([2560] * 32, 8, 64, 8, 160, FP8) == 2560
+
+
+def test_multiquery_ragged_verification_stays_balanced():
+    rs = np.random.default_rng(1002)
+    assert mq_plan(rs.integers(256, 4097, 64), 4, 32, 8, 256, BF16) == 0
+
+
+def test_multiquery_large_fixed_grids_keep_the_library_choice():
+    # 256 sequences x 32 kv-heads of 64-row MHA chunks: no balanced schedule
+    lens = np.full(256, 2048, np.int32)
+    assert mq_plan(lens, 64, 32, 32, 128, F16) == pkv.multiquery_partition_size(256, 64, 32, 32, 128, 0)
+    assert mq_plan(lens, 64, 32, 32, 128, F16) != 0

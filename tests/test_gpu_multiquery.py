@@ -70,7 +70,8 @@ def check(got, ref, what):
 
 CASES = [("mq_c2_verify4", 0), ("mq_c2_mixed", 0), ("mq_c2_mixed", 16), ("mq_c2_mixed", 512),
          ("mq_c2_mixed", 4096), ("mq_c3_chunk64", 0), ("mq_c3_chunk64", 128),
-         ("mq_c4_verify8", 0), ("mq_c4_verify8", 2560), ("mq_c6_verify8", 0)]
+         ("mq_c4_verify8", 0), ("mq_c4_verify8", 2560), ("mq_c6_verify8", 0),
+         ("mq_c6_verify8", 2560)]
 
 
 @pytest.mark.parametrize("name,ps", CASES)
