@@ -29,7 +29,7 @@ _lib = None
 
 def build_oracle():
     """Compile pkv_oracle.c with gcc (no fast-math, no FP contraction)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
            "-ffp-contract=off", _SRC, "-o", _SO + ".tmp", "-lm"]
     subprocess.check_call(cmd)
     os.replace(_SO + ".tmp", _SO)
@@ -46,8 +46,13 @@ def _load():
     I64 = ctypes.c_int64
     lib.orc_paged_decode.argtypes = [P, P, I, P, P, I, P, P, I, I, I, I, I, I, D, D, D]
     lib.orc_paged_decode.restype = I
+    lib.orc_paged_decode_mt.argtypes = [P, P, I, P, P, I, P, P, I, I, I, I, I, I, D, D, D, I]
+    lib.orc_paged_decode_mt.restype = I
     lib.orc_paged_multiquery.argtypes = [P, P, I, P, P, I, P, P, P, I, I, I, I, I, I, I, D, D, D]
     lib.orc_paged_multiquery.restype = I
+    lib.orc_paged_multiquery_mt.argtypes = [P, P, I, P, P, I, P, P, P, I, I, I, I, I, I, I, D, D,
+                                            D, I]
+    lib.orc_paged_multiquery_mt.restype = I
     lib.orc_cache_append_channel.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, P, P]
     lib.orc_cache_append_channel.restype = I
     lib.orc_paged_decode_channel.argtypes = [P, P, I, P, P, I, P, P, I, I, I, I, I, I, D, P, P]
@@ -71,6 +76,14 @@ def _load():
     lib.orc_kv_bytes_per_token.restype = ctypes.c_uint64
     _lib = lib
     return lib
+
+
+def default_threads():
+    """Threads for the oracle's row-parallel entry points: OMP_NUM_THREADS if
+    set, else the host's CPU count, at most 16."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    n = int(env) if env.isdigit() and int(env) > 0 else (os.cpu_count() or 1)
+    return max(1, min(16, n))
 
 
 def _ptr(a):
@@ -144,25 +157,36 @@ def _common(q, q_dtype, k_cache, kv_dtype, block_tables, context_lens):
 
 
 def paged_decode(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
-                 scale, k_scale=1.0, v_scale=1.0):
-    """fp64 out[S][H_q][d] of single-query attention through the block table."""
+                 scale, k_scale=1.0, v_scale=1.0, threads=None):
+    """fp64 out[S][H_q][d] of single-query attention through the block table.
+    threads: rows (sequence, q-head) shared among this many threads (None:
+    default_threads(); 1: the serial loop).  The result is the same bit for
+    bit: each row is computed by one thread with the same loops."""
     q, k_cache, bt, cl, S, hq, hkv, d, bs = _common(q, q_dtype, k_cache, kv_dtype,
                                                     block_tables, context_lens)
     v_cache = _check_bits(v_cache, kv_dtype)
     out = np.empty((S, hq, d), dtype=np.float64)
-    rc = _load().orc_paged_decode(_ptr(out), _ptr(q), DTYPES[q_dtype], _ptr(k_cache),
-                                  _ptr(v_cache), DTYPES[kv_dtype], _ptr(bt), _ptr(cl),
-                                  S, hq, hkv, d, bs, bt.shape[1], scale, k_scale, v_scale)
+    nt = default_threads() if threads is None else int(threads)
+    if nt <= 1:
+        rc = _load().orc_paged_decode(_ptr(out), _ptr(q), DTYPES[q_dtype], _ptr(k_cache),
+                                      _ptr(v_cache), DTYPES[kv_dtype], _ptr(bt), _ptr(cl),
+                                      S, hq, hkv, d, bs, bt.shape[1], scale, k_scale, v_scale)
+    else:
+        rc = _load().orc_paged_decode_mt(_ptr(out), _ptr(q), DTYPES[q_dtype], _ptr(k_cache),
+                                         _ptr(v_cache), DTYPES[kv_dtype], _ptr(bt), _ptr(cl),
+                                         S, hq, hkv, d, bs, bt.shape[1], scale, k_scale,
+                                         v_scale, nt)
     if rc != 0:
         raise ValueError(f"oracle paged_decode failed ({rc})")
     return out
 
 
 def paged_multiquery(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
-                     query_start, scale, k_scale=1.0, v_scale=1.0):
+                     query_start, scale, k_scale=1.0, v_scale=1.0, threads=None):
     """fp64 out[rows][H_q][d]: the rows query_start[s]..query_start[s+1]-1 of
     sequence s are its last positions and attend causally through the block
-    table (row i of n sits at position ctx - n + i)."""
+    table (row i of n sits at position ctx - n + i).  threads as for
+    paged_decode."""
     q = _check_bits(q, q_dtype)
     k_cache = _check_bits(k_cache, kv_dtype)
     v_cache = _check_bits(v_cache, kv_dtype)
@@ -174,10 +198,12 @@ def paged_multiquery(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, conte
     S = cl.shape[0]
     assert d == d2 and bt.shape[0] == S and qs.shape[0] == S + 1
     out = np.empty((rows, hq, d), dtype=np.float64)
-    rc = _load().orc_paged_multiquery(_ptr(out), _ptr(q), DTYPES[q_dtype], _ptr(k_cache),
-                                      _ptr(v_cache), DTYPES[kv_dtype], _ptr(bt), _ptr(cl),
-                                      _ptr(qs), S, rows, hq, hkv, d, bs, bt.shape[1], scale,
-                                      k_scale, v_scale)
+    nt = default_threads() if threads is None else int(threads)
+    args = (_ptr(out), _ptr(q), DTYPES[q_dtype], _ptr(k_cache), _ptr(v_cache), DTYPES[kv_dtype],
+            _ptr(bt), _ptr(cl), _ptr(qs), S, rows, hq, hkv, d, bs, bt.shape[1], scale, k_scale,
+            v_scale)
+    rc = (_load().orc_paged_multiquery(*args) if nt <= 1
+          else _load().orc_paged_multiquery_mt(*args, nt))
     if rc != 0:
         raise ValueError(f"oracle paged_multiquery failed ({rc})")
     return out

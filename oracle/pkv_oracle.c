@@ -102,6 +102,13 @@ double orc_e4m3_to_f64(uint8_t c) {
   return s ? -v : v;
 }
 
+/* The values of the 127 non-negative finite codes, from the decoder above,
+ * filled once when the library is loaded. */
+static double e4m3_value[127];
+__attribute__((constructor)) static void fill_e4m3_values(void) {
+  for (int c = 0; c <= 126; ++c) e4m3_value[c] = orc_e4m3_to_f64((uint8_t)c);
+}
+
 /* Encode a binary32 value as E4M3FN: the nearest finite code, ties to the
  * code with an even mantissa, magnitudes beyond 448 (and infinities)
  * saturate to +-448, NaN gives 0x7F.  Written as a search over the 127
@@ -119,7 +126,7 @@ uint8_t orc_e4m3_encode(float x) {
   int best = 0;
   double best_d = INFINITY;
   for (int c = 0; c <= 126; ++c) {
-    double d = fabs(ax - orc_e4m3_to_f64((uint8_t)c));
+    double d = fabs(ax - e4m3_value[c]);
     if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
       best = c;
       best_d = d;
@@ -138,12 +145,22 @@ uint8_t orc_int8_encode(float x) {
   return (uint8_t)(int8_t)r;
 }
 
+/* Every f16 and E4M3 bit pattern's value, from the decoders above, filled
+ * once when the library is loaded (the decoders are the definition; the
+ * tables only save recomputing them per element). */
+static double f16_value[65536];
+static double e4m3_code_value[256];
+__attribute__((constructor)) static void fill_decode_tables(void) {
+  for (int b = 0; b < 65536; ++b) f16_value[b] = orc_f16_to_f64((uint16_t)b);
+  for (int c = 0; c < 256; ++c) e4m3_code_value[c] = orc_e4m3_to_f64((uint8_t)c);
+}
+
 static double load_elem(const void* base, int64_t idx, int dtype) {
   switch (dtype) {
     case ORC_F32: return orc_f32_bits_to_f64(((const uint32_t*)base)[idx]);
-    case ORC_F16: return orc_f16_to_f64(((const uint16_t*)base)[idx]);
+    case ORC_F16: return f16_value[((const uint16_t*)base)[idx]];
     case ORC_BF16: return orc_bf16_to_f64(((const uint16_t*)base)[idx]);
-    case ORC_FP8_E4M3: return orc_e4m3_to_f64(((const uint8_t*)base)[idx]);
+    case ORC_FP8_E4M3: return e4m3_code_value[((const uint8_t*)base)[idx]];
     case ORC_INT8: return (double)((const int8_t*)base)[idx];
   }
   return NAN;
@@ -198,6 +215,10 @@ int orc_cache_append(void* k_cache, void* v_cache, const void* k_new,
     if (slot < 0) continue;
     if (slot >= (int64_t)num_blocks * block_size) return -1;
     int64_t blk = slot / block_size, off = slot % block_size;
+    int bad = 0;
+    /* a token's elements are written once each: they may be shared among
+     * threads */
+#pragma omp parallel for collapse(2) schedule(static) if (num_kv_heads * head_dim >= 512)
     for (int h = 0; h < num_kv_heads; ++h) {
       for (int i = 0; i < head_dim; ++i) {
         int64_t src = ((int64_t)t * num_kv_heads + h) * head_dim + i;
@@ -211,13 +232,16 @@ int orc_cache_append(void* k_cache, void* v_cache, const void* k_new,
             float y = load_as_f32(nb, src, new_dtype) * inv;
             ((uint8_t*)cb)[dst] =
                 kv_dtype == ORC_FP8_E4M3 ? orc_e4m3_encode(y) : orc_int8_encode(y);
+          } else if (eb_new != eb_kv) {
+#pragma omp atomic write
+            bad = 1;
           } else {
-            if (eb_new != eb_kv) return -2;
             memcpy((char*)cb + dst * eb_kv, (const char*)nb + src * eb_new, eb_kv);
           }
         }
       }
     }
+    if (bad) return -2;
   }
   return 0;
 }
@@ -236,6 +260,7 @@ int orc_cache_append_channel(void* k_cache, void* v_cache, const void* k_new,
     if (slot < 0) continue;
     if (slot >= (int64_t)num_blocks * block_size) return -1;
     int64_t blk = slot / block_size, off = slot % block_size;
+#pragma omp parallel for collapse(2) schedule(static) if (num_kv_heads * head_dim >= 512)
     for (int h = 0; h < num_kv_heads; ++h) {
       for (int i = 0; i < head_dim; ++i) {
         int64_t src = ((int64_t)t * num_kv_heads + h) * head_dim + i;
@@ -360,6 +385,65 @@ static void weights(const orc_args* a, int s, int hq, int t0, int t1, double* z,
   *l_out = l;
 }
 
+/* One output row, out[s][hq][:], over the sequence's n = context_lens[s]
+ * tokens: the softmax weights of the row's logits, then the weighted sum of
+ * its V rows.  w holds at least n doubles of scratch.  n <= 0 gives zeros. */
+static void decode_row(const orc_args* a, int s, int hq, double* w, double* o) {
+  const int g = a->num_q_heads / a->num_kv_heads;
+  const int n = a->context_lens[s];
+  for (int i = 0; i < a->head_dim; ++i) o[i] = 0.0;
+  if (n <= 0) return;
+  double m, l;
+  weights(a, s, hq, 0, n, w, &m, &l);
+  for (int t = 0; t < n; ++t) {
+    double wt = w[t] / l;
+    for (int i = 0; i < a->head_dim; ++i)
+      o[i] += wt * cache_elem(a, a->v_cache, a->v_scale, s, hq / g, t, i);
+  }
+}
+
+/* Every (sequence, q-head) row is independent of the others, so the rows may
+ * be shared among threads: each row is still computed by one thread with the
+ * same loops in the same order, and the result does not depend on the thread
+ * count, bit for bit.  num_threads <= 1 runs serially. */
+static int decode_rows(const orc_args* a, double* out, int num_threads) {
+  const int max_ctx = a->max_blocks_per_seq * a->block_size;
+  for (int s = 0; s < a->num_seqs; ++s)
+    if (a->context_lens[s] > max_ctx) return -2;
+  const int64_t nrows = (int64_t)a->num_seqs * a->num_q_heads;
+  int failed = 0;
+#pragma omp parallel num_threads(num_threads > 1 ? num_threads : 1) if (num_threads > 1)
+  {
+    double* w = (double*)malloc(sizeof(double) * (max_ctx > 0 ? max_ctx : 1));
+    if (!w) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+      if (!w) continue;
+      const int s = (int)(r / a->num_q_heads), hq = (int)(r % a->num_q_heads);
+      decode_row(a, s, hq, w, out + r * a->head_dim);
+    }
+    free(w);
+  }
+  return failed ? -3 : 0;
+}
+
+static orc_args decode_args(const void* q, int q_dtype, const void* k_cache,
+                            const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                            const int32_t* context_lens, int num_seqs, int num_q_heads,
+                            int num_kv_heads, int head_dim, int block_size,
+                            int max_blocks_per_seq, double scale, double k_scale,
+                            double v_scale) {
+  orc_args a = {q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
+                context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                block_size, max_blocks_per_seq, scale,
+                scaled_dtype(kv_dtype) ? k_scale : 1.0,
+                scaled_dtype(kv_dtype) ? v_scale : 1.0};
+  return a;
+}
+
 /* out[S][H_q][d] (double).  A sequence with context length 0 yields zeros. */
 int orc_paged_decode(double* out, const void* q, int q_dtype, const void* k_cache,
                      const void* v_cache, int kv_dtype,
@@ -368,33 +452,104 @@ int orc_paged_decode(double* out, const void* q, int q_dtype, const void* k_cach
                      int head_dim, int block_size, int max_blocks_per_seq,
                      double scale, double k_scale, double v_scale) {
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
-  orc_args a = {q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
-                context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                block_size, max_blocks_per_seq, scale,
-                scaled_dtype(kv_dtype) ? k_scale : 1.0,
-                scaled_dtype(kv_dtype) ? v_scale : 1.0};
-  int g = num_q_heads / num_kv_heads;
-  int max_ctx = max_blocks_per_seq * block_size;
-  double* w = (double*)malloc(sizeof(double) * (max_ctx > 0 ? max_ctx : 1));
-  if (!w) return -3;
-  for (int s = 0; s < num_seqs; ++s) {
-    int n = context_lens[s];
-    if (n > max_ctx) { free(w); return -2; }
-    for (int hq = 0; hq < num_q_heads; ++hq) {
-      double* o = out + ((int64_t)s * num_q_heads + hq) * head_dim;
-      for (int i = 0; i < head_dim; ++i) o[i] = 0.0;
-      if (n <= 0) continue;
-      double m, l;
-      weights(&a, s, hq, 0, n, w, &m, &l);
-      for (int t = 0; t < n; ++t) {
-        double wt = w[t] / l;
-        for (int i = 0; i < head_dim; ++i)
-          o[i] += wt * cache_elem(&a, v_cache, a.v_scale, s, hq / g, t, i);
-      }
+  const orc_args a = decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
+                                 context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                 block_size, max_blocks_per_seq, scale, k_scale, v_scale);
+  return decode_rows(&a, out, 1);
+}
+
+/* The same result with the rows shared among num_threads threads. */
+int orc_paged_decode_mt(double* out, const void* q, int q_dtype, const void* k_cache,
+                        const void* v_cache, int kv_dtype,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        int num_seqs, int num_q_heads, int num_kv_heads,
+                        int head_dim, int block_size, int max_blocks_per_seq,
+                        double scale, double k_scale, double v_scale, int num_threads) {
+  if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
+  const orc_args a = decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
+                                 context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                 block_size, max_blocks_per_seq, scale, k_scale, v_scale);
+  return decode_rows(&a, out, num_threads);
+}
+
+/* One output row of a multi-query call: q row `row` of sequence s, q-head hq,
+ * sitting at position p, over tokens 0..p.  z holds at least p + 1 doubles. */
+static void mq_row(const orc_args* a, int s, int64_t row, int hq, int p, double* z,
+                   double* o) {
+  const int g = a->num_q_heads / a->num_kv_heads, hk = hq / g, d = a->head_dim;
+  double m = -INFINITY;
+  for (int t = 0; t <= p; ++t) {
+    double dot = 0.0;
+    for (int e = 0; e < d; ++e) {
+      const double qe = load_elem(a->q, (row * a->num_q_heads + hq) * d + e, a->q_dtype);
+      dot += qe * cache_elem(a, a->k_cache, a->k_scale, s, hk, t, e);
+    }
+    z[t] = a->scale * dot;
+    if (z[t] > m) m = z[t];
+  }
+  double l = 0.0;
+  for (int t = 0; t <= p; ++t) {
+    z[t] = exp(z[t] - m);
+    l += z[t];
+  }
+  for (int t = 0; t <= p; ++t) {
+    const double wt = z[t] / l;
+    for (int e = 0; e < d; ++e) o[e] += wt * cache_elem(a, a->v_cache, a->v_scale, s, hk, t, e);
+  }
+}
+
+/* Every (row, q-head) is independent; with num_threads > 1 they are shared
+ * among threads, each computed by one thread exactly as serially. */
+static int multiquery_rows(const orc_args* a, double* out, const int32_t* query_start,
+                           int num_rows, int num_threads) {
+  const int max_ctx = a->max_blocks_per_seq * a->block_size;
+  const int hq_n = a->num_q_heads, d = a->head_dim;
+  for (int64_t i = 0; i < (int64_t)num_rows * hq_n * d; ++i) out[i] = 0.0;
+  /* the placed rows: (sequence, row, position) of every row with p >= 0 */
+  int64_t placed = 0;
+  for (int s = 0; s < a->num_seqs; ++s) {
+    const int ctx = a->context_lens[s];
+    const int r0 = query_start[s], n = query_start[s + 1] - r0;
+    if (ctx > max_ctx || n < 0 || r0 < 0 || r0 + n > num_rows) return -2;
+    for (int i = 0; i < n; ++i)
+      if (ctx - n + i >= 0) ++placed;
+  }
+  int32_t* rs = (int32_t*)malloc(sizeof(int32_t) * (placed > 0 ? placed : 1) * 3);
+  if (!rs) return -3;
+  int64_t k = 0;
+  for (int s = 0; s < a->num_seqs; ++s) {
+    const int ctx = a->context_lens[s];
+    const int r0 = query_start[s], n = query_start[s + 1] - r0;
+    for (int i = 0; i < n; ++i) {
+      const int p = ctx - n + i;   /* position of this query */
+      if (p < 0) continue;
+      rs[3 * k] = s;
+      rs[3 * k + 1] = r0 + i;
+      rs[3 * k + 2] = p;
+      ++k;
     }
   }
-  free(w);
-  return 0;
+  int failed = 0;
+  const int64_t items = placed * hq_n;
+#pragma omp parallel num_threads(num_threads > 1 ? num_threads : 1) if (num_threads > 1)
+  {
+    double* z = (double*)malloc(sizeof(double) * (max_ctx > 0 ? max_ctx : 1));
+    if (!z) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t it = 0; it < items; ++it) {
+      if (!z) continue;
+      const int64_t j = it / hq_n;
+      const int hq = (int)(it % hq_n);
+      const int64_t row = rs[3 * j + 1];
+      mq_row(a, rs[3 * j], row, hq, rs[3 * j + 2], z, out + (row * hq_n + hq) * d);
+    }
+    free(z);
+  }
+  free(rs);
+  return failed ? -3 : 0;
 }
 
 /* Multi-query attention through the block table.  Sequence s owns the
@@ -410,52 +565,25 @@ int orc_paged_multiquery(double* out, const void* q, int q_dtype, const void* k_
                          int head_dim, int block_size, int max_blocks_per_seq, double scale,
                          double k_scale, double v_scale) {
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
-  const int g = num_q_heads / num_kv_heads;
-  const int max_ctx = max_blocks_per_seq * block_size;
-  const double ks = scaled_dtype(kv_dtype) ? k_scale : 1.0;
-  const double vs = scaled_dtype(kv_dtype) ? v_scale : 1.0;
-  /* the kv-side lookups of cache_elem only need the cache fields */
-  orc_args a = {q, q_dtype, k_cache, v_cache, kv_dtype, block_tables, context_lens,
-                num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                max_blocks_per_seq, scale, ks, vs};
-  for (int64_t i = 0; i < (int64_t)num_rows * num_q_heads * head_dim; ++i) out[i] = 0.0;
-  double* z = (double*)malloc(sizeof(double) * (max_ctx > 0 ? max_ctx : 1));
-  if (!z) return -3;
-  for (int s = 0; s < num_seqs; ++s) {
-    const int ctx = context_lens[s];
-    const int r0 = query_start[s], n = query_start[s + 1] - r0;
-    if (ctx > max_ctx || n < 0 || r0 < 0 || r0 + n > num_rows) { free(z); return -2; }
-    for (int i = 0; i < n; ++i) {
-      const int p = ctx - n + i;   /* position of this query */
-      if (p < 0) continue;
-      const int64_t row = r0 + i;
-      for (int hq = 0; hq < num_q_heads; ++hq) {
-        const int hk = hq / g;
-        double m = -INFINITY;
-        for (int t = 0; t <= p; ++t) {
-          double dot = 0.0;
-          for (int e = 0; e < head_dim; ++e) {
-            const double qe = load_elem(q, (row * num_q_heads + hq) * head_dim + e, q_dtype);
-            dot += qe * cache_elem(&a, k_cache, ks, s, hk, t, e);
-          }
-          z[t] = scale * dot;
-          if (z[t] > m) m = z[t];
-        }
-        double l = 0.0;
-        for (int t = 0; t <= p; ++t) {
-          z[t] = exp(z[t] - m);
-          l += z[t];
-        }
-        double* o = out + (row * num_q_heads + hq) * head_dim;
-        for (int t = 0; t <= p; ++t) {
-          const double wt = z[t] / l;
-          for (int e = 0; e < head_dim; ++e) o[e] += wt * cache_elem(&a, v_cache, vs, s, hk, t, e);
-        }
-      }
-    }
-  }
-  free(z);
-  return 0;
+  const orc_args a = decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
+                                 context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                 block_size, max_blocks_per_seq, scale, k_scale, v_scale);
+  return multiquery_rows(&a, out, query_start, num_rows, 1);
+}
+
+/* The same result with the (row, q-head) pairs shared among num_threads
+ * threads. */
+int orc_paged_multiquery_mt(double* out, const void* q, int q_dtype, const void* k_cache,
+                            const void* v_cache, int kv_dtype, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* query_start,
+                            int num_seqs, int num_rows, int num_q_heads, int num_kv_heads,
+                            int head_dim, int block_size, int max_blocks_per_seq, double scale,
+                            double k_scale, double v_scale, int num_threads) {
+  if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
+  const orc_args a = decode_args(q, q_dtype, k_cache, v_cache, kv_dtype, block_tables,
+                                 context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                 block_size, max_blocks_per_seq, scale, k_scale, v_scale);
+  return multiquery_rows(&a, out, query_start, num_rows, num_threads);
 }
 
 /* Normalised softmax weights of one (sequence, q-head): w[ctx]. */

@@ -5,8 +5,8 @@ Tolerances: f32 caches max|err| <= 1e-5; 16-bit and FP8 caches
 |gpu - ref| <= 2e-3 + 1e-2 |ref| per element (outputs are rounded to the q
 dtype, whose half-ulp is at most 2^-9 relative, and the MFMA path rounds the
 softmax weights to the q dtype, about 2^-9 relative per weight).
-At full size the oracle evaluates a sample of sequences (listed below,
-always including the shortest and the longest context)."""
+Every output row of every sequence is compared, at the workloads' full sizes
+and in every schedule, grid size and partition size below."""
 import numpy as np
 import pytest
 import torch

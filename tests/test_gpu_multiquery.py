@@ -3,11 +3,12 @@ fp64 oracle, element by element.
 
 Every workload reuses a decode workload's device cache (filled by the
 library's append, the step's token included) and adds seeded query rows.
-Sampled sequences are checked row by row against oracle.paged_multiquery.
-For the 512-row chunks at the end of 32K contexts the oracle would run for
-minutes, so sampled rows are checked against oracle.paged_decode over the
-row's own prefix (a pinned identity: row i of n is the decode step of a
-context of ctx - n + i + 1 tokens).  Tolerance as for decode:
+Every row of every sequence is checked against oracle.paged_multiquery.
+For the 512-row chunks at the end of 32K contexts the full oracle would run
+for hours, so six rows of each of the 16 sequences (the first, the last and
+four interior ones) are checked against oracle.paged_decode over the row's
+own prefix (a pinned identity: row i of n is the decode step of a context of
+ctx - n + i + 1 tokens).  Tolerance as for decode:
 |gpu - ref| <= 2e-3 + 1e-2 |ref| per element."""
 import numpy as np
 import pytest
@@ -46,11 +47,17 @@ def run_mq(m, partition_size=0, out=None):
     return out
 
 
+_MQ_REF = {}
+
+
 def oracle_rows(m, seqs):
-    """fp64 rows of the sampled sequences (oracle.paged_multiquery on the
-    oracle-side caches, which hold exactly those sequences' K/V)."""
+    """fp64 rows of the given sequences (oracle.paged_multiquery on the
+    oracle-side caches), computed once per workload and sequence set."""
     from oracle import oracle as orc
     cfg = m["cfg"]
+    key = (m["mq"].name, tuple(seqs))
+    if key in _MQ_REF:
+        return _MQ_REF[key]
     _, _, o = oracle_ref(cfg.name)
     qs, ql = m["qs"], m["ql"]
     sub_qs = np.zeros(len(seqs) + 1, np.int32)
@@ -60,6 +67,7 @@ def oracle_rows(m, seqs):
     ref = orc.paged_multiquery(qb, cfg.q_dtype, o["k_cache"], o["v_cache"], cfg.kv_dtype,
                                o["block_tables"][seqs], o["ctx"][seqs], sub_qs, cfg.scale,
                                o["k_scale"], o["v_scale"])
+    _MQ_REF[key] = (rows, ref)
     return rows, ref
 
 
@@ -86,24 +94,44 @@ def test_multiquery_matches_oracle(name, ps):
     check(got, ref, f"{name} ps={ps}")
 
 
+_CHUNK_REF = {}
+
+
+def chunk_rows_reference(m):
+    """Rows (first, two near the start, two interior, last) of every sequence
+    of the 512-row chunk workload, and their fp64 references: each row is
+    the decode of its own prefix, so all of them go to the oracle as one
+    decode batch whose 'sequences' are (sequence, row) pairs sharing the
+    sequence's block table."""
+    from oracle import oracle as orc
+    if "c5" in _CHUNK_REF:
+        return _CHUNK_REF["c5"]
+    cfg = m["cfg"]
+    seqs, _, o = oracle_ref(cfg.name)
+    qb = gen.bits(m["q"])
+    rows, tables, lens = [], [], []
+    for s in seqs:
+        n, ctx = int(m["ql"][s]), int(m["st"]["ctx"][s])
+        for i in sorted({0, 1, 128, 255, 400, n - 1}):
+            rows.append(int(m["qs"][s]) + i)
+            tables.append(o["block_tables"][s])
+            lens.append(ctx - n + i + 1)
+    rows = np.array(rows, np.int64)
+    ref = orc.paged_decode(qb[rows], cfg.q_dtype, o["k_cache"], o["v_cache"], cfg.kv_dtype,
+                           np.stack(tables), np.array(lens, np.int32), cfg.scale,
+                           o["k_scale"], o["v_scale"])
+    _CHUNK_REF["c5"] = (rows, ref)
+    return rows, ref
+
+
 @pytest.mark.parametrize("ps", [0, 4096])
 def test_long_context_chunk_rows_match_decode_over_their_prefix(ps):
     print(f"[case] multiquery mq_c5_chunk512 partition={ps}", flush=True)
-    from oracle import oracle as orc
     m = mq_state("mq_c5_chunk512")
-    cfg = m["cfg"]
-    seqs, _, o = oracle_ref(cfg.name)
+    rows, ref = chunk_rows_reference(m)
     out = run_mq(m, ps).float().cpu().numpy().astype(np.float64)
-    qb = gen.bits(m["q"])
-    for s in seqs:
-        n, ctx = int(m["ql"][s]), int(m["st"]["ctx"][s])
-        for i in (0, 1, 255, n - 1):
-            r = int(m["qs"][s]) + i
-            ref = orc.paged_decode(qb[r:r + 1], cfg.q_dtype, o["k_cache"], o["v_cache"],
-                                   cfg.kv_dtype, o["block_tables"][s:s + 1],
-                                   np.array([ctx - n + i + 1], np.int32), cfg.scale,
-                                   o["k_scale"], o["v_scale"])
-            check(out[r:r + 1], ref, f"chunk row {i} of sequence {s}")
+    assert len(rows) == 6 * m["cfg"].num_seqs
+    check(out[rows], ref, f"chunk rows partition={ps}")
 
 
 def test_rows_outside_the_sequences_untouched_and_unplaced_rows_zero():
