@@ -4,16 +4,26 @@
 A step is one pass of the whole decode hot path over one batch: the cache
 append of every sequence's new token (slot_mapping write) followed by paged
 decode attention over each sequence's context (the decode kernel, plus the
-merge or reduction kernel when contexts are split).  The timed region runs
-K steps back to back; a second pass of K steps records HIP events around
-the decode kernel for its own duration (the roofline figure).  The block tables,
+merge or reduction kernel when contexts are split).  The block tables,
 context lengths and slot mapping come from the native block pool, built
 before the timed region (its host cost per step is measured separately).
 
-Prints one JSON line.  Inputs are seeded synthetic data of the workload's
-shape.  To keep every timed step reading cold HBM rather than the 256 MB
-Infinity Cache, the caches are replicated and the steps rotate over the
-replicas.
+Per workload:
+  - timed region: K steps back to back (nothing recorded between kernels);
+    `value` = algorithmic KV bytes per step / mean step time;
+  - profiled pass: at least 50 steps whose decode and merge/reduction kernels
+    are bracketed by events their own dispatch stamps: the decode kernel
+    alone, t_attn = decode + merge/reduction (the roofline figure), and the
+    period between successive steps' decode starts, each as mean and
+    p10/p50/p90;
+  - the same step replayed from a HIP graph, and the streaming-read probe
+    over the same byte count (the achievable read rate).
+
+The headline is the 32K-token shared-prefix workload (the largest that fits
+one GPU); the other decode workloads follow under "configs".  Prints one
+JSON line.  Inputs are seeded synthetic data of the workloads' shapes.  To
+keep every timed step reading cold HBM rather than the 256 MB Infinity Cache,
+the caches are replicated and the steps rotate over the replicas.
 """
 import argparse
 import json
@@ -34,14 +44,20 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2_qwen3_8b_bf16")
+    ap.add_argument("--config", default="c5_long_shared_bf16",
+                    help="the headline workload (default: the 32K-token shared-prefix one, "
+                         "the largest single-GPU workload)")
+    ap.add_argument("--others", default="c2_qwen3_8b_bf16,c3_llama2_7b_f16,c4_llama3_70b_fp8,"
+                                        "c6_llama3_70b_int8",
+                    help="comma-separated workloads timed after the headline and reported "
+                         "under 'configs' ('' for none)")
     ap.add_argument("--algo", default="auto", choices=["auto", "vector", "mfma"])
     ap.add_argument("--partition", type=int, default=-1, help="-1: the workload's own setting")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 4x the MALL")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--all-configs", action="store_true",
-                    help="also time the other workloads and add them under 'other_configs'")
+                    help="also time the multi-query workloads, swapping and prefix caching")
     ap.add_argument("--multiquery", action="store_true",
                     help="also time the multi-query workloads (prompt chunks, draft "
                          "verification) and add them under 'multiquery' (implied by "
@@ -69,8 +85,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 # the source file that defines each decode kernel
 KERNEL_FILES = {"decode_stream_kernel": "pkv_decode_stream.hip",
+                "decode_split_merge_kernel": "pkv_decode_stream.hip",
                 "decode_mfma_kernel": "pkv_decode_mfma.hip",
-                "decode_vec_kernel": "pkv_decode_vec.hip"}
+                "decode_vec_kernel": "pkv_decode_vec.hip",
+                "decode_reduce_kernel": "pkv_decode_vec.hip",
+                "cache_append_kernel": "pkv_append.hip",
+                "multiquery_mfma_kernel": "pkv_multiquery.hip",
+                "multiquery_stream_kernel": "pkv_multiquery.hip",
+                "multiquery_reduce_kernel": "pkv_multiquery.hip",
+                "multiquery_split_merge_kernel": "pkv_multiquery.hip"}
 
 
 def kernel_source_hash(kernel):
@@ -236,6 +259,20 @@ def time_stream_probe(kv_bytes, R, K, dev):
     return ms, nt * PROBE_TILE / (ms * 1e-3) / 1e9
 
 
+def pct(xs, q):
+    """q-th percentile (0..100) of xs, linear interpolation."""
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
+def summary_ms(xs):
+    return {"mean": round(sum(xs) / len(xs), 5), "p10": round(pct(xs, 10), 5),
+            "p50": round(pct(xs, 50), 5), "p90": round(pct(xs, 90), 5), "n": len(xs)}
+
+
+PROFILE_STEPS = 50   # steps of the profiled pass (percentiles), at least
+
+
 def time_config(cfg, args, dev, partition, with_cpu=True):
     import numpy as np
     import torch
@@ -259,6 +296,8 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
         ps = pkv.decode_partition_size(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads,
                                        cfg.head_dim, cfg.max_blocks_per_seq,
                                        DT_CODE[cfg.kv_dtype], 0, context_lens=st["ctx"])
+    kernel, algo, part = decode_path(cfg, args.algo, ps)
+    has_reduce = kernel == "decode_stream_kernel" or part < cfg.max_blocks_per_seq * 16
     ws = pkv.alloc_workspace(st["q"], st["k_cache"], st["block_tables"], ps)
     out = torch.empty_like(st["q"])
     stream = torch.cuda.current_stream()
@@ -291,21 +330,26 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     step_ms = total_ms / K
-    # Kernel pass: the same K steps again, with HIP events recorded by the
-    # library on the launch stream right before and after the decode kernel
-    # and after the merge/reduction kernel: the decode kernel's own duration.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # Profiled pass: at least PROFILE_STEPS steps, each decode kernel launched
+    # with start/stop events its own dispatch stamps (no event records between
+    # the kernels), and the merge/reduction kernel's end stamped the same way.
+    # Per step: the decode kernel alone, t_attn = decode + merge/reduction, and
+    # the period from one step's decode start to the next one's (one append,
+    # decode and merge each): the step time distribution.
+    Kp = max(K, PROFILE_STEPS)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(Kp)]
     for trio in evs:       # create the underlying HIP events before handing them over
         for e in trio:
             e.record(stream)
     torch.cuda.synchronize()
-    for i in range(K):
-        step(i, evs[i])
+    for i in range(Kp):
+        a, b, c = evs[i]
+        step(i, (a, b, c if has_reduce else None))
     torch.cuda.synchronize()
-    part_ms = [a.elapsed_time(b) for a, b, _ in evs]
-    red_ms = [b.elapsed_time(c) for _, b, c in evs]
-    part_avg = sum(part_ms) / K
-    red_avg = sum(red_ms) / K
+    dec_ms = [a.elapsed_time(b) for a, b, _ in evs]
+    attn_ms = ([a.elapsed_time(c) for a, _, c in evs] if has_reduce else list(dec_ms))
+    red_ms = [x - y for x, y in zip(attn_ms, dec_ms)]
+    period_ms = [evs[i][0].elapsed_time(evs[i + 1][0]) for i in range(Kp - 1)]
     # The same step captured once into a HIP graph and replayed K times (the
     # launch path a serving loop can use; every kernel here is capturable).
     g_step_ms = None
@@ -333,27 +377,89 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
         del graphs
     except RuntimeError as e:   # reported, never silently replaced
         log(f"graph capture failed: {e}")
-    achieved = kv_bytes / (part_avg * 1e-3) / 1e9
+    dec_avg = sum(dec_ms) / Kp
+    attn_avg = sum(attn_ms) / Kp
     probe_ms, probe_gbs = time_stream_probe(kv_bytes, R, K, dev)
     log(f"streaming-read probe: {probe_ms:.4f} ms, {probe_gbs:.1f} GB/s")
     res = dict(
         config=cfg.name, kv_bytes=kv_bytes, replicas=R, cache_bytes_per_replica=cache_bytes,
-        kernel=decode_path(cfg, args.algo, ps)[0],
-        algo=decode_path(cfg, args.algo, ps)[1],
-        partition=decode_path(cfg, args.algo, ps)[2],
+        kernel=kernel, algo=algo, partition=part, has_reduce=has_reduce,
         ms_per_step=step_ms, wall_ms_per_step=wall / K * 1e3,
-        decode_kernel_ms=part_avg, reduce_kernel_ms=red_avg,
+        decode_kernel_ms=dec_avg, reduce_kernel_ms=attn_avg - dec_avg, t_attn_ms=attn_avg,
+        decode_ms_stats=summary_ms(dec_ms), t_attn_ms_stats=summary_ms(attn_ms),
+        reduce_ms_stats=summary_ms(red_ms), step_period_ms_stats=summary_ms(period_ms),
         step_gbs=kv_bytes / (step_ms * 1e-3) / 1e9,
         graph_ms_per_step=g_step_ms,
-        decode_kernel_gbs=achieved, tokens_per_s=cfg.num_seqs / (step_ms * 1e-3),
+        decode_kernel_gbs=kv_bytes / (dec_avg * 1e-3) / 1e9,
+        t_attn_gbs=kv_bytes / (attn_avg * 1e-3) / 1e9,
+        tokens_per_s=cfg.num_seqs / (step_ms * 1e-3),
         probe_ms=probe_ms, probe_gbs=probe_gbs,
         t_pool_build_s=st["t_pool_build"])
-    log(f"timed {K} steps: {step_ms:.4f} ms/step, decode kernel {part_avg:.4f} ms")
+    log(f"timed {K} steps: {step_ms:.4f} ms/step; {Kp} profiled: decode kernel "
+        f"{dec_avg:.4f} ms, decode + merge/reduction {attn_avg:.4f} ms")
     res["host_bookkeeping_us_per_step"] = host_bookkeeping_us(cfg, st)
     if with_cpu and args.cpu_budget > 0:
         res["cpu_baseline"] = cpu_baseline(cfg, st, args.cpu_budget, out)
         log("cpu baseline done")
+    del kcs, vcs, ws, out, st
+    torch.cuda.empty_cache()
     return res
+
+
+def roofline_obj(cfg, res):
+    """The roofline object of one workload: t_attn (decode kernel + merge or
+    reduction) against the HBM peak on the algorithmic KV bytes, with the
+    decode kernel's own fraction beside it and the counter traffic of the
+    decode kernel (and of the reduction, when one runs)."""
+    traffic = measured_traffic(cfg.name, res["kernel"])
+    red_kernel = reduce_kernel_of(res)
+    red_traffic = measured_traffic(cfg.name, red_kernel) if red_kernel else None
+    return {"bound": "hbm", "achieved": round(res["t_attn_gbs"], 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(res["t_attn_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": res["kernel"] + (f" + {red_kernel}" if red_kernel else ""),
+            "t_attn_ms": round(res["t_attn_ms"], 5),
+            "decode_kernel_ms": round(res["decode_kernel_ms"], 5),
+            "reduce_kernel_ms": round(res["reduce_kernel_ms"], 5),
+            "decode_only_frac": round(res["decode_kernel_gbs"] / HBM_PEAK_GBS, 4),
+            "decode_only_gbs": round(res["decode_kernel_gbs"], 2),
+            "reduce_traffic": red_traffic,
+            "algorithmic_bytes_per_launch": res["kv_bytes"],
+            "pct_of_peak": round(100 * res["t_attn_gbs"] / HBM_PEAK_GBS, 2),
+            "target_pct": 70.0 if cfg.name in LONG_CONTEXT else None}
+
+
+def reduce_kernel_of(res):
+    """The merge or reduction kernel a step runs after the decode kernel."""
+    if not res["has_reduce"]:
+        return None
+    if res["kernel"] == "decode_stream_kernel" and res["partition"] == 0:
+        return "decode_split_merge_kernel"
+    return "decode_reduce_kernel"
+
+
+# the workloads the 70%-of-peak bar applies to (long contexts)
+LONG_CONTEXT = ("c2_qwen3_8b_bf16", "c4_llama3_70b_fp8", "c5_long_shared_bf16")
+
+
+def config_obj(cfg, res):
+    """One workload's figures for the JSON line."""
+    return {"workload": cfg.name, "description": cfg.description, "algo": res["algo"],
+            "kernel": res["kernel"], "partition": res["partition"],
+            "kv_bytes_per_step": res["kv_bytes"],
+            "step_gbs": round(res["step_gbs"], 2),
+            "pct_hbm_peak_step": round(100 * res["step_gbs"] / HBM_PEAK_GBS, 2),
+            "ms_per_step": round(res["ms_per_step"], 5),
+            "decode_tokens_per_s": round(res["tokens_per_s"], 1),
+            "roofline": roofline_obj(cfg, res),
+            "decode_kernel_ms": res["decode_ms_stats"],
+            "t_attn_ms": res["t_attn_ms_stats"],
+            "step_period_ms": res["step_period_ms_stats"],
+            "graph_ms_per_step": (round(res["graph_ms_per_step"], 5)
+                                  if res["graph_ms_per_step"] else None),
+            "achievable_read_gbs": round(res["probe_gbs"], 2),
+            "t_attn_frac_of_achievable": round(res["t_attn_gbs"] / res["probe_gbs"], 4),
+            "replicas": res["replicas"]}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/f16 MFMA, published peak
@@ -545,10 +651,14 @@ def time_prefix_cache(cfg):
 
 
 def cpu_baseline(cfg, st, budget_s, gpu_out):
-    """The fp64 oracle, single-threaded, on a bounded sample of the same
-    workload's sequences (longest context first, until the time budget is
-    spent): oracle KV GB/s and decode tokens/s.  The sampled rows are also
-    compared with the GPU output of the timed steps."""
+    """The fp64 oracle on the host, two legs on the same workload's sequences
+    (longest context first):
+      - single-threaded, on a bounded sample (until budget_s is spent);
+      - each sequence's rows (one per q-head) shared among the host's
+        threads (oracle.default_threads: OMP_NUM_THREADS, else the CPU
+        count, at most 16), on as many sequences as fit the same budget.
+    Reported: oracle KV GB/s and decode tokens/s per leg.  The rows the
+    oracle computed are compared with the GPU output of the timed steps."""
     import numpy as np
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from harness import allclose_report, oracle_setup
@@ -559,25 +669,50 @@ def cpu_baseline(cfg, st, budget_s, gpu_out):
     o = oracle_setup(cfg, order)
     qb = gen.bits(o["q"])
     eb = kv_elem_bytes(cfg.kv_dtype)
-    done, t_used, nbytes, worst, ok_all = 0, 0.0, 0, 0.0, True
-    for s in order:
+    per_seq = [int(ctx[s]) * 2 * cfg.num_kv_heads * cfg.head_dim * eb for s in range(cfg.num_seqs)]
+    worst, ok_all = 0.0, True
+
+    def run(seqs, threads):
+        nonlocal worst, ok_all
         t0 = time.perf_counter()
-        ref = orc.paged_decode(qb[[s]], cfg.q_dtype, o["k_cache"], o["v_cache"], cfg.kv_dtype,
-                               o["block_tables"][[s]], o["ctx"][[s]], cfg.scale, o["k_scale"],
-                               o["v_scale"])
-        t_used += time.perf_counter() - t0
-        done += 1
-        nbytes += int(ctx[s]) * 2 * cfg.num_kv_heads * cfg.head_dim * eb
-        got = gpu_out[s:s + 1].float().cpu().numpy().astype(np.float64)
+        ref = orc.paged_decode(qb[seqs], cfg.q_dtype, o["k_cache"], o["v_cache"], cfg.kv_dtype,
+                               o["block_tables"][seqs], o["ctx"][seqs], cfg.scale, o["k_scale"],
+                               o["v_scale"], threads=threads)
+        dt = time.perf_counter() - t0
+        got = gpu_out[seqs].float().cpu().numpy().astype(np.float64)
         ok, _, err = allclose_report(got, ref, 2e-3, 1e-2)
         ok_all &= ok
         worst = max(worst, err)
-        if t_used >= budget_s:
+        return dt
+
+    # single thread: one sequence at a time until the budget is spent
+    done, t1 = 0, 0.0
+    for s in order:
+        t1 += run([s], 1)
+        done += 1
+        if t1 >= budget_s:
             break
-    return {"value": round(nbytes / t_used / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "tokens_per_s": round(done / t_used, 3),
-            "sample": f"{done} of {cfg.num_seqs} sequences of {cfg.name} (longest first), all "
-                      f"q-heads, {t_used:.1f} s of single-threaded fp64 oracle",
+    b1 = sum(per_seq[s] for s in order[:done])
+    # all threads: one sequence per call (its H_q rows shared among them),
+    # longest first, until the same budget is spent
+    nt = orc.default_threads()
+    doneN, tN = 0, 0.0
+    for s in order:
+        tN += run([s], nt)
+        doneN += 1
+        if tN >= budget_s:
+            break
+    bN = sum(per_seq[s] for s in order[:doneN])
+    return {"value": round(bN / tN / 1e9, 4), "unit": "GB/s", "cores": nt, "kind": "oracle",
+            "tokens_per_s": round(doneN / tN, 3),
+            "sample": f"{doneN} of {cfg.num_seqs} sequences of {cfg.name} (longest first), all "
+                      f"q-heads, {tN:.1f} s of fp64 oracle with its rows shared among {nt} "
+                      f"threads",
+            "single_thread": {
+                "value": round(b1 / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                "tokens_per_s": round(done / t1, 3),
+                "sample": f"{done} of {cfg.num_seqs} sequences of {cfg.name} (longest first), "
+                          f"all q-heads, {t1:.1f} s of single-threaded fp64 oracle"},
             "gpu_rows_match_oracle": ok_all, "max_abs_err": worst}
 
 
@@ -636,47 +771,29 @@ def main():
                    "replicas": res["replicas"]},
         "decode_tokens_per_s": round(res["tokens_per_s"], 1),
         "pct_hbm_peak_step": round(100 * res["step_gbs"] / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "achieved": round(res["decode_kernel_gbs"], 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(res["decode_kernel_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(cfg.name, res["kernel"]),
-                     "kernel": res["kernel"],
-                     "kernel_ms": round(res["decode_kernel_ms"], 5),
-                     "algorithmic_bytes_per_launch": res["kv_bytes"]},
+        "roofline": roofline_obj(cfg, res),
+        "step_period_ms": res["step_period_ms_stats"],
+        "t_attn_ms": res["t_attn_ms_stats"],
+        "decode_kernel_ms": res["decode_ms_stats"],
         "achievable_read": {
             "gbs": round(res["probe_gbs"], 2), "ms": round(res["probe_ms"], 5),
-            "kernel_frac": round(res["decode_kernel_gbs"] / res["probe_gbs"], 4),
+            "t_attn_frac": round(res["t_attn_gbs"] / res["probe_gbs"], 4),
             "probe": "pkv_stream_read_probe over the same bytes: shuffled 4 KiB tiles, "
                      "contiguous shares per wave, 4 tiles in flight, 256 x 4 waves, "
                      "timed by dispatch-stamped events like the decode kernel"},
-        "merge_or_reduce_ms": round(res["reduce_kernel_ms"], 5),
         "graph": ({"ms_per_step": round(res["graph_ms_per_step"], 5),
                    "step_gbs": round(res["kv_bytes"] / (res["graph_ms_per_step"] * 1e-3) / 1e9, 2)}
                   if res["graph_ms_per_step"] else None),
         "host_bookkeeping_us_per_step": round(res["host_bookkeeping_us_per_step"], 1),
         "cpu_baseline": res.get("cpu_baseline"),
     }
-    if args.all_configs:
-        others = {}
-        for name, c in CONFIGS.items():
-            if name == cfg.name:
-                continue
+    others = [n for n in args.others.split(",") if n and n != cfg.name]
+    if others:
+        line["configs"] = {}
+        for name in others:
+            c = CONFIGS[name]
             r = time_config(c, args, dev, c.partition_size, with_cpu=False)
-            others[name] = {"step_gbs": round(r["step_gbs"], 2),
-                            "decode_kernel_gbs": round(r["decode_kernel_gbs"], 2),
-                            "frac": round(r["decode_kernel_gbs"] / HBM_PEAK_GBS, 4),
-                            "ms_per_step": round(r["ms_per_step"], 5),
-                            "decode_kernel_ms": round(r["decode_kernel_ms"], 5),
-                            "tokens_per_s": round(r["tokens_per_s"], 1), "algo": r["algo"],
-                            "graph_ms_per_step": (round(r["graph_ms_per_step"], 5)
-                                                  if r["graph_ms_per_step"] else None),
-                            "achievable_read_gbs": round(r["probe_gbs"], 2),
-                            "kernel_frac_of_achievable": round(r["decode_kernel_gbs"] / r["probe_gbs"], 4),
-                            "kernel": r["kernel"], "partition": r["partition"],
-                            "traffic": measured_traffic(name, r["kernel"])}
-            del r
-            torch.cuda.empty_cache()
-        line["other_configs"] = others
+            line["configs"][name] = config_obj(c, r)
     if args.all_configs or args.swap:
         line["swap"] = time_swap(cfg, args, dev)
     if args.all_configs:

@@ -83,12 +83,6 @@ const char* pkv_status_string(int32_t status);
 /* Library version: major*10000 + minor*100 + patch. */
 int32_t pkv_version(void);
 
-/* Workgroups (of 4 waves) the balanced decode and multi-query schedules
- * launch; 0 restores the default (256: one wave on every SIMD of a 256-CU
- * MI355X).  Process-wide; it changes what pkv_decode_workspace_size and
- * pkv_multiquery_workspace_size return, so set it before sizing workspaces. */
-pkv_status pkv_set_stream_workgroups(int32_t n);
-
 /* --------------------------------------------------------------- sizes -- */
 
 /* KV-cache bytes per token of a whole model: 2 x layers x kv_heads x head_dim
@@ -99,7 +93,12 @@ uint64_t pkv_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_d
 
 /* --------------------------------------------------------- cache append -- */
 
-/* Write the K/V rows of num_tokens new tokens into the paged caches.
+/* Write the K/V rows of num_tokens new tokens into the paged caches: a
+ * decode step computes K and V for its new token only and adds them to the
+ * cache ("Transformer 推理优化：KV Cache、PagedAttention 与 vLLM", section
+ * 2.2), in the slot its sequence's block table gives it (same page, section
+ * 3.3: logical block t / 16 maps to a physical block, offset t % 16; a new
+ * block is taken every 16 tokens, "vLLM推理引擎深度解析", section 2.2).
  *   k_new, v_new : device, [num_tokens][num_kv_heads][head_dim] of new_dtype,
  *                  contiguous.
  *   slot_mapping : device int64[num_tokens]; slot = block * block_size + offset.
@@ -359,7 +358,8 @@ int32_t pkv_multiquery_partition_size_for_lengths(const int32_t* context_lens, i
                                                   int32_t kv_dtype);
 /* Workspace bytes of a multi-query call.  Balanced schedule: float
  * (m, l)[2 W][16][2] and acc[2 W][16][head_dim] for the W = 4 x
- * pkv_set_stream_workgroups waves of its grid (two partial slots per wave),
+ * (compute units of the current device) waves of its grid (two partial
+ * slots per wave),
  * each part 256-byte aligned.  Fixed partitions: 0 for one partition, else
  * float m[rows][H_q][P], l[rows][H_q][P], acc[rows][H_q][P][head_dim], each
  * part 256-byte aligned.  SIZE_MAX on bad arguments. */
@@ -401,7 +401,11 @@ pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks, con
  *                   distinct and no destination may be a source.
  *   block_bytes   : bytes of one physical block of one cache
  *                   (num_kv_heads * block_size * head_dim * element bytes),
- *                   a multiple of 16. */
+ *                   a multiple of 16.
+ * The caches and the pairs must be device memory or pinned host memory: the
+ * call looks each pointer up (hipPointerGetAttributes) and returns
+ * PKV_ERR_INVALID_ARG for memory no kernel can reach (pageable host memory)
+ * before launching anything. */
 pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
                            int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
                            void* stream);

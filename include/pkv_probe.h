@@ -1,6 +1,7 @@
-/* Measurement helper of libpkv: the streaming-read probe, kept apart from
- * pkv.h because it is not part of the attention path.  Same status codes
- * and error reporting as pkv.h (pkv_last_error). */
+/* Measurement and testing helpers of libpkv, kept apart from pkv.h because
+ * they are not part of the attention path: the streaming-read probe, and an
+ * override of the balanced schedules' grid size for tests and measurements.
+ * Same status codes and error reporting as pkv.h (pkv_last_error). */
 #ifndef PKV_PROBE_H
 #define PKV_PROBE_H
 
@@ -34,6 +35,16 @@ extern "C" {
 pkv_status pkv_stream_read_probe(const void* buf, int64_t buf_bytes, const int32_t* tile_ids,
                                  int32_t num_tiles, uint32_t* sink, int32_t workgroups,
                                  void* stream, void* ev_start, void* ev_stop);
+
+/* Workgroups (of 4 waves) the balanced decode and multi-query schedules
+ * launch for calls made later by the calling thread; n = 0 restores the
+ * default (the current device's compute-unit count: one wave on every
+ * SIMD).  Thread-local: other threads' calls keep their own setting.  It
+ * changes what pkv_decode_workspace_size and pkv_multiquery_workspace_size
+ * return on this thread, so set it before sizing workspaces.  For tests (any
+ * grid must give the same attention) and measurements.  PKV_ERR_INVALID_ARG
+ * for n < 0 or n > 65535. */
+pkv_status pkv_set_stream_workgroups(int32_t n);
 
 #ifdef __cplusplus
 }

@@ -68,7 +68,34 @@ static int32_t resolve_algo(int32_t g, int32_t q, int32_t kv) {
   return mfma_ok && g > 1 ? PKV_ALGO_MFMA : PKV_ALGO_VECTOR;
 }
 
-static std::atomic<int32_t> g_stream_workgroups{kDefaultStreamWorkgroups};
+int32_t device_cus() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int32_t> cached[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  if (dev < kMaxDevices) {
+    const int32_t v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0) {
+    (void)hipGetLastError();
+    n = kDefaultCUs;
+  }
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// 0: no override (the device's CU count)
+static thread_local int32_t t_stream_workgroups = 0;
+
+int32_t stream_workgroups() {
+  return t_stream_workgroups > 0 ? t_stream_workgroups : device_cus();
+}
 
 #ifndef PKV_PARTS_ON_STREAM_GRID
 #define PKV_PARTS_ON_STREAM_GRID 1
@@ -131,7 +158,7 @@ static bool make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
                            ((int64_t)1 << 31);
   plan->stream_ok = partition_size == 0 && grid_ok;
   plan->parts_stream_ok = kPartsOnStreamGrid && partition_size > 0 && plan->num_parts > 1 && grid_ok;
-  plan->stream_grid = g_stream_workgroups.load();
+  plan->stream_grid = stream_workgroups();
   plan->stream_off_ml = plan->stream_off_part = plan->stream_bytes = 0;
   if (plan->stream_ok) {
     const size_t workers = (size_t)plan->stream_grid * 4;
@@ -159,7 +186,7 @@ struct MQPlan {
 // per CU.
 static bool mq_small_grid(int32_t num_seqs, int32_t num_kv_heads, int32_t g, int32_t mq) {
   const MQTiles t4 = mq_tiles(g, mq, 4);
-  return (int64_t)num_seqs * num_kv_heads * t4.hchunks * t4.qtiles <= 2 * kCUs;
+  return (int64_t)num_seqs * num_kv_heads * t4.hchunks * t4.qtiles <= 2 * device_cus();
 }
 
 // Partition and workspace of a multi-query call; false on bad arguments.
@@ -194,7 +221,7 @@ bool mq_plan(int32_t num_rows, int32_t num_seqs, int32_t max_query_len, int32_t 
     plan->stream = partition_size == 0 && tiles * Y < 2048 && num_seqs <= kMaxStreamSeqs &&
                    tiles <= kMaxStreamTiles &&
                    tiles * (max_blocks_per_seq + r_max) * Y < ((int64_t)1 << 31);
-    plan->stream_grid = g_stream_workgroups.load();
+    plan->stream_grid = stream_workgroups();
     plan->st_off_part = 0;
     if (plan->stream) {
       const size_t workers = (size_t)plan->stream_grid * kWaves;
@@ -313,7 +340,7 @@ int32_t pkv_version(void) { return 100; }
 pkv_status pkv_set_stream_workgroups(int32_t n) {
   clear_error();
   if (n < 0 || n > 65535) return fail(PKV_ERR_INVALID_ARG, "set_stream_workgroups: bad count");
-  g_stream_workgroups.store(n == 0 ? kDefaultStreamWorkgroups : n);
+  t_stream_workgroups = n;
   return PKV_OK;
 }
 
@@ -396,11 +423,11 @@ int32_t pkv_decode_partition_size_for_lengths(const int32_t* context_lens, int32
     work[s] = nbk > 0 ? (nbk + kWaves - 1) / kWaves + R : 0;
   }
   if (units == 0) return 0;
-  const int64_t W = (int64_t)g_stream_workgroups.load() * 4;
+  const int64_t W = (int64_t)stream_workgroups() * kWaves;
   const int64_t t_bal = (Y * units + W - 1) / W + kMergeUnits;
   // list scheduling of the fixed grid (kv-head chunk fastest, then sequence)
   std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
-  for (int i = 0; i < kCUs; ++i) free_at.push(0);
+  for (int32_t i = 0, n = device_cus(); i < n; ++i) free_at.push(0);
   int64_t t_fix = 0;
   for (int32_t s = 0; s < num_seqs && t_fix <= t_bal; ++s) {
     for (int64_t y = 0; y < Y; ++y) {
@@ -699,10 +726,10 @@ int32_t pkv_multiquery_partition_size_for_lengths(const int32_t* context_lens, i
     work[s] = nbk > 0 ? (nbk + kWaves - 1) / kWaves + R : 0;
   }
   if (units == 0) return 0;
-  const int64_t W = (int64_t)g_stream_workgroups.load() * kWaves;
+  const int64_t W = (int64_t)stream_workgroups() * kWaves;
   const int64_t t_bal = (Y * t.qtiles * units + W - 1) / W + kMergeUnits;
   std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
-  for (int i = 0; i < kCUs; ++i) free_at.push(0);
+  for (int32_t i = 0, n = device_cus(); i < n; ++i) free_at.push(0);
   int64_t t_fix = 0;
   for (int32_t s = 0; s < num_seqs && t_fix <= t_bal; ++s) {
     for (int64_t y = 0; y < Y * t.qtiles; ++y) {
@@ -861,24 +888,6 @@ pkv_status pkv_paged_multiquery_attention(
       workspace_bytes, stream, nullptr, nullptr, nullptr);
 }
 
-pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
-                           int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
-                           void* stream) {
-  clear_error();
-  if (num_pairs < 0 || num_blocks < 0 || block_bytes <= 0 || block_bytes % 16 != 0)
-    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: bad sizes");
-  if (num_pairs == 0) return PKV_OK;
-  if (!k_cache || !v_cache || !src_dst_pairs)
-    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: NULL pointer");
-  if (!aligned16(k_cache) || !aligned16(v_cache))
-    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: caches must be 16-byte aligned");
-  int rc = launch_copy_blocks(k_cache, v_cache, src_dst_pairs, num_pairs, num_blocks,
-                              block_bytes, stream);
-  if (rc != 0)
-    return fail(PKV_ERR_HIP, "copy_blocks: launch failed: %s", hipGetErrorString((hipError_t)rc));
-  return PKV_OK;
-}
-
 // Address through which a kernel reaches p: device memory as is, pinned host
 // memory through its device mapping; nullptr for memory no kernel can touch
 // (pageable host memory), so that such a call fails instead of faulting.
@@ -891,6 +900,33 @@ static const void* kernel_view(const void* p) {
   if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) return p;
   if (at.type == hipMemoryTypeHost) return at.devicePointer;
   return nullptr;
+}
+
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
+                           int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
+                           void* stream) {
+  clear_error();
+  if (num_pairs < 0 || num_blocks < 0 || block_bytes <= 0 || block_bytes % 16 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: bad sizes");
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !src_dst_pairs)
+    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: NULL pointer");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: caches must be 16-byte aligned");
+  // every buffer is read or written by the kernel: memory it cannot reach
+  // (pageable host memory) is refused here instead of faulting the GPU
+  void* kc = const_cast<void*>(kernel_view(k_cache));
+  void* vc = const_cast<void*>(kernel_view(v_cache));
+  const int32_t* pp = static_cast<const int32_t*>(kernel_view(src_dst_pairs));
+  if (!kc || !vc || !pp)
+    return fail(PKV_ERR_INVALID_ARG,
+                "copy_blocks: the caches and the pairs must be device or pinned host memory");
+  if (!aligned16(kc) || !aligned16(vc))
+    return fail(PKV_ERR_INVALID_ARG, "copy_blocks: caches must be 16-byte aligned");
+  int rc = launch_copy_blocks(kc, vc, pp, num_pairs, num_blocks, block_bytes, stream);
+  if (rc != 0)
+    return fail(PKV_ERR_HIP, "copy_blocks: launch failed: %s", hipGetErrorString((hipError_t)rc));
+  return PKV_OK;
 }
 
 pkv_status pkv_swap_blocks(void* dst_k, void* dst_v, int32_t dst_num_blocks, const void* src_k,

@@ -30,8 +30,15 @@ constexpr int kBlockSize = 16;   // tokens per physical block
 constexpr int kWaves = 4;        // waves per decode workgroup
 constexpr int kMaxPartition = 1 << 20;
 constexpr int kMaxStreamSeqs = 2048;        // sequences the balanced schedule handles per call
-constexpr int kCUs = 256;                   // compute units of an MI355X
-constexpr int kDefaultStreamWorkgroups = kCUs;  // one wave per SIMD
+constexpr int kDefaultCUs = 256;            // an MI355X, when no device answers
+// Compute units of the calling thread's current HIP device, read once per
+// device; kDefaultCUs when no device is visible (the host planners still
+// answer on a machine without one).
+int32_t device_cus();
+// Workgroups of 4 waves the balanced schedules launch for calls made by the
+// calling thread: the device's CU count (one wave per SIMD) unless the
+// thread set an override (pkv_set_stream_workgroups).
+int32_t stream_workgroups();
 constexpr int kMaxStreamTiles = 4096;        // (sequence, row tile) pairs of a balanced multi-query call
 
 // Units the balanced schedule charges for starting a piece of a segment, in

@@ -714,7 +714,8 @@ int launch_mq_split_merge_t(const pkv::MQArgs& a) {
   // the items instead.
   const int64_t nitems = (int64_t)sp.b.S * sp.b.qtiles * sp.Y * sp.b.ntl * 4;
   int64_t grid = (nitems + pkv::kWaves - 1) / pkv::kWaves;
-  if (grid > 2 * pkv::kCUs) grid = 2 * pkv::kCUs;
+  const int64_t cap = 2 * (int64_t)pkv::device_cus();
+  if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   return pkv::launch_kernel(multiquery_split_merge_kernel<QT, D>, dim3((unsigned)grid),
                             dim3(64 * pkv::kWaves), a.stream, sp, a.ev_start, a.ev_stop);

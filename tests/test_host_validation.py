@@ -215,3 +215,37 @@ def test_stream_read_probe_rejects_bad_arguments():
                                    NULL, NULL, NULL) == _lib.PKV_ERR_INVALID_ARG
     assert b"stream_read_probe" in l.pkv_last_error()
 
+
+
+def test_copy_blocks_rejects_pageable_host_memory():
+    """Buffers no kernel can reach (pageable host memory) are refused before
+    any launch, for the caches and for the pairs alike."""
+    import numpy as np
+    host = np.zeros(4096, np.uint8)
+    pairs = np.array([0, 1], np.int32)
+    hp, pp = host.ctypes.data, pairs.ctypes.data
+    st = lib().pkv_copy_blocks(hp, hp, pp, 1, 2, 1024, NULL)
+    assert st == _lib.PKV_ERR_INVALID_ARG
+    assert b"device or pinned host memory" in lib().pkv_last_error()
+
+
+def test_stream_workgroups_override_is_per_thread():
+    """The grid override of one thread leaves other threads' workspace sizes
+    (and grids) alone."""
+    import threading
+    l = lib()
+    base = l.pkv_decode_workspace_size(64, 32, 8, 128, 256, _lib.PKV_BF16, 0)
+    seen = {}
+
+    def other():
+        seen["size"] = l.pkv_decode_workspace_size(64, 32, 8, 128, 256, _lib.PKV_BF16, 0)
+
+    assert l.pkv_set_stream_workgroups(1024) == _lib.PKV_OK
+    try:
+        th = threading.Thread(target=other)
+        th.start()
+        th.join()
+        assert l.pkv_decode_workspace_size(64, 32, 8, 128, 256, _lib.PKV_BF16, 0) > base
+    finally:
+        assert l.pkv_set_stream_workgroups(0) == _lib.PKV_OK
+    assert seen["size"] == base

@@ -432,3 +432,55 @@ def test_prefix_cache_pins_on_the_native_pool():
     assert cached == 16 and table[0] == y and table[1] != a[1]
     with pytest.raises(pkv.InvalidArg):
         p.register_blocks(t, 32, table)     # y holds another prefix now
+
+
+def test_batch_never_emits_a_slot_twice():
+    """Every slot a batch step hands out is distinct, lies in a block its
+    sequence alone holds (count 1, after any copy-on-write), and is never
+    handed out again while the sequences live: the append kernel's slots are
+    unique by construction, so no cache row is written twice.  Random pools
+    with forks (shared partial blocks) and 0..4 new tokens per sequence."""
+    rs = np.random.default_rng(11)
+    steps = 0
+    for trial in range(40):
+        nblk = int(rs.integers(40, 120))
+        pool = pkv.BlockPool(nblk, 16, rs.permutation(nblk).astype(np.int32))
+        tables, lens = [], []
+        for _ in range(int(rs.integers(2, 9))):
+            if tables and rs.random() < 0.5:
+                i = int(rs.integers(len(tables)))
+                tables.append(pool.seq_fork(tables[i]))
+                lens.append(lens[i])
+            else:
+                L = int(rs.integers(0, 70))
+                tables.append(pool.seq_create(L))
+                lens.append(L)
+        mb = 16
+        rows = as_rows(tables, mb)
+        nb = np.array([len(t) for t in tables], np.int32)
+        cl = np.array(lens, np.int32)
+        seen = set()
+        for _ in range(12):
+            k = rs.integers(0, 5, len(tables)).astype(np.int32)
+            if np.any(cl + k > mb * 16):
+                break
+            before = cl.copy()
+            try:
+                slots, _ = pool.batch_append_slots(rows, nb, cl, k)
+            except pkv.OutOfBlocks:
+                break
+            steps += 1
+            sl = slots.tolist()
+            assert len(sl) == int(k.sum()) and all(x >= 0 for x in sl)
+            assert len(set(sl)) == len(sl), "a slot handed out twice in one step"
+            assert not (seen & set(sl)), "a slot handed out again in a later step"
+            seen |= set(sl)
+            t = 0
+            for s in range(len(tables)):
+                for j in range(int(k[s])):
+                    pos = int(before[s]) + j
+                    blk = int(rows[s, pos // 16])
+                    assert sl[t] == blk * 16 + pos % 16
+                    assert pool.refcount(blk) == 1
+                    t += 1
+    assert steps > 200
