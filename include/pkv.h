@@ -275,6 +275,34 @@ pkv_status pkv_paged_decode_attention_per_channel(
     void* workspace, size_t workspace_bytes, int32_t algo, void* stream, void* ev_begin,
     void* ev_mid, void* ev_end);
 
+/* Bytes of the static device scratch array of pkv_paged_decode_attention_noalloc
+ * (one per GPU, held until the process ends): 32 MiB. */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* Decode for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * call as pkv_paged_decode_attention_algo (same arguments, schedules, kernels
+ * and results, bit for bit) without the workspace: the partial results of
+ * split contexts go to a static device array of the library, one per GPU, of
+ * PKV_NOALLOC_SCRATCH_BYTES.  The call allocates nothing: the first call on a
+ * device only looks the array's address up (hipGetSymbolAddress) and keeps it.
+ *   - A call whose schedule needs more than PKV_NOALLOC_SCRATCH_BYTES (compare
+ *     pkv_decode_workspace_size) returns PKV_ERR_WORKSPACE before anything is
+ *     launched; a larger partition_size needs less.
+ *   - Every call on one GPU shares that GPU's array.  Its contents on entry do
+ *     not matter (a call writes every partial it reads), but calls that
+ *     overlap in time on one GPU (other streams, other threads) race on it and
+ *     may corrupt each other's results: serialise them.
+ * Errors as for pkv_paged_decode_attention; PKV_ERR_HIP if the array's
+ * address cannot be looked up. */
+pkv_status pkv_paged_decode_attention_noalloc(
+    void* out, const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t num_blocks, int32_t max_blocks_per_seq, float scale, int32_t q_dtype,
+    int32_t kv_dtype, float k_scale, float v_scale, int32_t partition_size, int32_t algo,
+    void* stream);
+
 /* ------------------------------------------- multi-query attention -- */
 
 /* Several query rows per sequence in one pass: a chunk of a long prompt

@@ -153,6 +153,34 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
     return out
 
 
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def paged_decode_attention_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale,
+                                   k_scale=1.0, v_scale=1.0, partition_size=0, out=None,
+                                   algo="auto", stream=None):
+    """paged_decode_attention without a workspace: the library keeps split
+    contexts' partials in its static per-GPU scratch array
+    (pkv_paged_decode_attention_noalloc).  `out` must be given by a caller
+    that cannot allocate; calls overlapping in time on one GPU race."""
+    S, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables/context_lens must have one row per sequence")
+    if out is None:
+        out = torch.empty_like(q)
+    check(lib().pkv_paged_decode_attention_noalloc(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, hq, hkv, d,
+        bs, nb, block_tables.shape[1], float(scale), dtype_code(q), dtype_code(k_cache),
+        float(k_scale), float(v_scale), int(partition_size), _ALGO[algo], _stream(q, stream)))
+    return out
+
+
 def multiquery_partition_size(num_seqs, max_query_len, num_q_heads, num_kv_heads,
                               max_blocks_per_seq, partition_size=0, context_lens=None,
                               kv_dtype=_lib.PKV_BF16):

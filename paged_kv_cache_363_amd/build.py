@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 
 SOURCES = ["pkv_capi.cpp", "pkv_pool.cpp", "pkv_append.hip", "pkv_decode_vec.hip",
            "pkv_decode_mfma.hip", "pkv_decode_stream.hip", "pkv_multiquery.hip",
-           "pkv_probe.hip"]
+           "pkv_probe.hip", "pkv_noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -490,7 +490,7 @@ int32_t pkv_decode_algo_for(int32_t num_q_heads, int32_t num_kv_heads, int32_t h
 
 // Body of every decode entry point; k_scales / v_scales (device [H_kv][d]) are
 // per-channel scales of a one-byte-code cache, or nullptr.
-static pkv_status decode_impl(
+pkv_status pkv::decode_impl(
     void* out, const void* q, const void* k_cache, const void* v_cache,
     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

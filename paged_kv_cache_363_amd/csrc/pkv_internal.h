@@ -133,6 +133,18 @@ inline MQTiles mq_tiles(int g, int max_query_len, int max_ntl) {
   return t;
 }
 
+// Argument checks, schedule choice and launches of every decode entry point
+// (pkv_capi.cpp); k_scales / v_scales: per-channel scales or nullptr.
+pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                       int32_t max_blocks_per_seq, float scale, int32_t q_dtype,
+                       int32_t kv_dtype, float k_scale, float v_scale, const float* k_scales,
+                       const float* v_scales, int32_t partition_size, void* workspace,
+                       size_t workspace_bytes, int32_t algo, void* stream, void* ev_begin,
+                       void* ev_mid, void* ev_end);
+
 // Kernel launchers (return hipError_t as int).
 int launch_multiquery(const MQArgs& a);
 int launch_multiquery_reduce(const MQArgs& a);

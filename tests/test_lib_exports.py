@@ -39,3 +39,10 @@ def test_pure_helpers():
     assert _lib.lib().pkv_kv_bytes_per_token(1, 1, 1, 9) == 0
     assert _lib.lib().pkv_version() >= 100
     assert _lib.lib().pkv_status_string(3) == b"out of blocks"
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(os.path.join(INCLUDE, "pkv.h")).read()
+    m = re.search(r"#define PKV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m, "PKV_NOALLOC_SCRATCH_BYTES not found"
+    assert int(m.group(1)) << int(m.group(2)) == pkv.api.NOALLOC_SCRATCH_BYTES
