@@ -51,35 +51,99 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
   }
 }
 
+// Four consecutive outputs in the q dtype, at an element index that is a
+// multiple of 4 (out is 16-byte aligned): one 16- or 8-byte store.
+template <int QT>
+__device__ __forceinline__ void store_out4(void* out, int64_t idx, float a, float b, float c,
+                                           float d) {
+  if constexpr (QT == PKV_F32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + idx) = make_float4(a, b, c, d);
+  } else {
+    uint32_t lo, hi;
+    if constexpr (QT == PKV_F16) {
+      lo = (uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16);
+      hi = (uint32_t)f32_to_f16(c) | ((uint32_t)f32_to_f16(d) << 16);
+    } else {
+      lo = (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+      hi = (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16);
+    }
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + idx) = make_uint2(lo, hi);
+  }
+}
+
+// N consecutive outputs (N = 4 or 8) in the q dtype at an element index that
+// is a multiple of N: one store of 2N bytes for a 16-bit dtype.
+template <int QT, int N>
+__device__ __forceinline__ void store_out_n(void* out, int64_t idx, const float* v) {
+  static_assert(N == 4 || N == 8, "4 or 8 outputs");
+  if constexpr (QT == PKV_F32 || N == 4) {
+#pragma unroll
+    for (int k = 0; k < N; k += 4) store_out4<QT>(out, idx + k, v[k], v[k + 1], v[k + 2], v[k + 3]);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (QT == PKV_F16)
+        w[k] = (uint32_t)f32_to_f16(v[2 * k]) | ((uint32_t)f32_to_f16(v[2 * k + 1]) << 16);
+      else
+        w[k] = (uint32_t)f32_to_bf16(v[2 * k]) | ((uint32_t)f32_to_bf16(v[2 * k + 1]) << 16);
+    }
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + idx) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // Merge the NWV waves' (m, l, acc) held in LDS and write the result.
-//   sm_m, sm_l : [NWV][HP]      sm_o : [NWV][HP][D + 4]
+//   sm_m, sm_l : [NWV][HP]      sm_o : [NWV][HP][D + 4], 16-byte aligned
+// Each thread takes whole quads of 4 consecutive dims of one head, a number
+// of them known at compile time, and writes each with one store: a loop
+// with a store per element made every iteration wait for the previous
+// store (loads and stores share one counter) and the first one for the K/V
+// loads still in flight.
 template <int QT, int D, int HP, int NWV = pkv::kWaves>
 __device__ __forceinline__ void merge_waves_and_store(const DecodeParams& p, const float* sm_m,
                                                       const float* sm_l, const float* sm_o,
                                                       int nh, int s, int h_first, int part) {
   constexpr int LD = D + 4;
-  for (int idx = threadIdx.x; idx < nh * D; idx += 64 * NWV) {
-    const int h = idx / D, d = idx % D;
+  constexpr int QD = D / 4;                                   // quads per head row
+  constexpr int ITER = (HP * QD + 64 * NWV - 1) / (64 * NWV);
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int qi = threadIdx.x + it * 64 * NWV;
+    const int h = qi / QD, d = (qi % QD) * 4;
+    if (h >= nh) continue;
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < NWV; ++w) M = fmaxf(M, sm_m[w * HP + h]);
-    float L = 0.f, acc = 0.f;
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (M != kNegInf) {
 #pragma unroll
       for (int w = 0; w < NWV; ++w) {
         const float mw = sm_m[w * HP + h];
         const float f = (mw == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
         L += f * sm_l[w * HP + h];
-        acc += f * sm_o[(w * HP + h) * LD + d];
+        const float4 x = *reinterpret_cast<const float4*>(sm_o + (w * HP + h) * LD + d);
+        acc.x += f * x.x;
+        acc.y += f * x.y;
+        acc.z += f * x.z;
+        acc.w += f * x.w;
       }
     }
     const int64_t row = (int64_t)s * p.Hq + h_first + h;
-    const float vsc = p.vs ? p.vs[(int64_t)((h_first + h) / p.g) * D + d] : p.vsc;
+    float4 vsc = make_float4(p.vsc, p.vsc, p.vsc, p.vsc);
+    if (p.vs) {   // the caller's scale array: no alignment beyond 4 bytes
+      const float* v = p.vs + (int64_t)((h_first + h) / p.g) * D + d;
+      vsc = make_float4(v[0], v[1], v[2], v[3]);
+    }
     if (p.num_parts == 1) {
-      store_out<QT>(p.out, row * D + d, L > 0.f ? acc * vsc / L : 0.f);
+      store_out4<QT>(p.out, row * D + d, L > 0.f ? acc.x * vsc.x / L : 0.f,
+                     L > 0.f ? acc.y * vsc.y / L : 0.f, L > 0.f ? acc.z * vsc.z / L : 0.f,
+                     L > 0.f ? acc.w * vsc.w / L : 0.f);
     } else {
       const int64_t pr = row * p.num_parts + part;
-      p.ws_acc[pr * D + d] = acc * vsc;
+      *reinterpret_cast<float4*>(p.ws_acc + pr * D + d) =
+          make_float4(acc.x * vsc.x, acc.y * vsc.y, acc.z * vsc.z, acc.w * vsc.w);
       if (d == 0) {
         p.ws_m[pr] = M;
         p.ws_l[pr] = L;

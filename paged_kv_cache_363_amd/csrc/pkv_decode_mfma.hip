@@ -1,9 +1,10 @@
 // Paged decode attention on the CDNA4 matrix cores, fixed partitions.
 //
-// Each workgroup owns one (partition, kv-head, head chunk, sequence); its four
-// waves take four contiguous runs of the partition's 16-token blocks, each
-// with an online softmax (mfma_piece, pkv_mfma_common.h), and merge through
-// LDS at the end (see pkv_decode_common.h).
+// Each workgroup owns one (partition, kv-head, head chunk, sequence); its
+// waves take the partition's 16-token blocks in turn (wave w every NWG-th
+// block from the w-th), each with an online softmax (mfma_piece,
+// pkv_mfma_common.h), and merge through LDS at the end (see
+// pkv_decode_common.h).
 //
 // Math: softmax(q K^T * scale) V over the block-table-gathered context
 // ("KV Cache 与 PageAttention深度实战", sections 1.2 and 3.2).
@@ -27,22 +28,27 @@
 #ifndef PKV_MFMA_WPE
 #define PKV_MFMA_WPE 2     // minimum waves per SIMD the register budget must allow
 #endif
+#ifndef PKV_MFMA_WAVES
+#define PKV_MFMA_WAVES 4   // waves per workgroup (they split the partition's blocks)
+#endif
 
 namespace {
 
 using namespace pkvd;
 
+constexpr int NWG = PKV_MFMA_WAVES;
+
 // PC: a one-byte-code cache with per-channel scales (p.ks, p.vs).
 template <int QT, int KVT, int D, int HS, bool PC>
-__global__ __launch_bounds__(64 * pkv::kWaves) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WPE, 8)))
+__global__ __launch_bounds__(64 * NWG) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WPE, 8)))
 void decode_mfma_kernel(DecodeParams p) {
   using T = MfmaTile<QT, KVT, D>;
   constexpr int LD = D + 4;
   constexpr int DPL = T::DPL;
 
-  __shared__ float sm_m[pkv::kWaves * HS];
-  __shared__ float sm_l[pkv::kWaves * HS];
-  __shared__ float sm_o[pkv::kWaves * HS * LD];
+  __shared__ float sm_m[NWG * HS];
+  __shared__ float sm_l[NWG * HS];
+  __shared__ __align__(16) float sm_o[NWG * HS * LD];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -51,12 +57,21 @@ void decode_mfma_kernel(DecodeParams p) {
   const int hk = blockIdx.y / p.hchunks, hc = blockIdx.y % p.hchunks;
   const int h_first = hk * p.g + hc * p.chunk_heads;
   const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
-  const int ctx = clamped_ctx(p, s);
-  const int nblk = (ctx + 15) >> 4;
   const int b_begin = part * p.part_blocks;
-  if (part > 0 && b_begin >= nblk) return;
-  const int b_end = min(b_begin + p.part_blocks, nblk);
+  const int32_t* row = p.bt + (int64_t)s * p.mb;
 
+  // Wave w takes blocks b_begin + w, b_begin + w + NWG, ... of the partition.
+  // Which ids those are does not depend on the context length, so the first
+  // window of them (and q) is requested before the length arrives: the
+  // first K/V loads wait for one round trip less.  Indices past the table
+  // row are clamped to its last entry (never used: the piece stops at the
+  // context).
+  int ids0[PKV_ID_VGPRS];
+  if (p.mb > 0) {
+#pragma unroll
+    for (int k = 0; k < PKV_ID_VGPRS; ++k)
+      ids0[k] = row[min(b_begin + w + NWG * (64 * k + lane), p.mb - 1)];
+  }
   uint4 qr[T::KSTEPS];
   uint4 qlo[PC ? T::KSTEPS : 1];
   if constexpr (PC)
@@ -65,25 +80,29 @@ void decode_mfma_kernel(DecodeParams p) {
   else
     T::load_q(qr, p.q, (int64_t)s * p.Hq + h_first + c, c < nh, G);
 
+  const int ctx = clamped_ctx(p, s);
+  const int nblk = (ctx + 15) >> 4;
+  if (part > 0 && b_begin >= nblk) return;
+  const int b_end = min(b_begin + p.part_blocks, nblk);
+
   f32x4 o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  // wave w takes the w-th of four contiguous, near-equal runs of the
-  // partition's blocks
+  // this wave's steps, and the step holding the context's last block (if any)
   const int nblk_p = b_end - b_begin;
-  const int w0 = b_begin + (nblk_p * w) / pkv::kWaves;
-  const int w1 = b_begin + (nblk_p * (w + 1)) / pkv::kWaves;
-  if (p.nb > 0 && w1 > w0) {
+  const int steps = nblk_p > w ? (nblk_p - w + NWG - 1) / NWG : 0;
+  const int lb = nblk - 1 - b_begin - w;
+  const int last_step = (b_end == nblk && lb >= 0 && lb % NWG == 0) ? lb / NWG : -1;
+  if (p.nb > 0 && steps > 0) {
     const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
     const int64_t head_off = (int64_t)hk * T::TILE;
     mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
-               pkv::byte_codes(KVT) ? PKV_MFMA_NT8 : PKV_MFMA_NT16,
-               false, PC>(p.kc + head_off, p.vc + head_off, blk_stride,
-                                           p.bt + (int64_t)s * p.mb, w0, w1, nblk - 1,
-                                           ctx - 16 * (nblk - 1), p.nb, qr, p.sl2, &m_run, &l_run,
-                                           o, lane, nullptr, qlo);
+               pkv::byte_codes(KVT) ? PKV_MFMA_NT8 : PKV_MFMA_NT16, false, PC>(
+        p.kc + head_off, p.vc + head_off, blk_stride, row + b_begin + w, 0, steps, last_step,
+        ctx - 16 * (nblk - 1), p.nb, qr, p.sl2, &m_run, &l_run, o, lane, nullptr, qlo, NoHook{},
+        NWG, ids0);
   }
 
   // lane (G, c) holds O[head c][dim DPL*(4G+i) + e]; l needs the 4 G lanes
@@ -100,13 +119,13 @@ void decode_mfma_kernel(DecodeParams p) {
       for (int e = 0; e < DPL; ++e) dst[DPL * i + e] = o[e][i];
   }
   __syncthreads();
-  merge_waves_and_store<QT, D, HS>(p, sm_m, sm_l, sm_o, nh, s, h_first, part);
+  merge_waves_and_store<QT, D, HS, NWG>(p, sm_m, sm_l, sm_o, nh, s, h_first, part);
 }
 
 template <int QT, int KVT, int D, int HS>
 int launch_t(const pkv::DecodeArgs& a, const DecodeParams& kp) {
   dim3 grid(kp.num_parts, a.num_kv_heads * kp.hchunks, a.num_seqs);
-  const dim3 block(64 * pkv::kWaves);
+  const dim3 block(64 * NWG);
   if constexpr (pkv::byte_codes(KVT)) {
     if (kp.ks)
       return pkv::launch_kernel(decode_mfma_kernel<QT, KVT, D, HS, true>, grid, block, a.stream,

@@ -216,20 +216,27 @@ void decode_stream_kernel(StreamParams p) {
     if (b0 == 0 && b_last == nbk - 1) {
       if (c < nh) {
         const int64_t row = ((int64_t)s * p.Hq + h_first + c) * D + DPL * 4 * G;
+        // lane (G, c) holds dims DPL*(4G+i) + e, e < DPL: DPL consecutive
+        // outputs per i, written with one store each
         if constexpr (PC) {
           const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
           const float* vs = p.vs + (int64_t)(y / p.hchunks) * D + DPL * 4 * G;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            float v[DPL];
 #pragma unroll
-            for (int e = 0; e < DPL; ++e)
-              store_out<QT>(p.out, row + DPL * i + e, o[e][i] * vs[DPL * i + e] * inv);
+            for (int e = 0; e < DPL; ++e) v[e] = o[e][i] * vs[DPL * i + e] * inv;
+            store_out_n<QT, DPL>(p.out, row + DPL * i, v);
+          }
         } else {
           const float inv = l_tot > 0.f ? p.vsc / l_tot : 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            float v[DPL];
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) store_out<QT>(p.out, row + DPL * i + e, o[e][i] * inv);
+            for (int e = 0; e < DPL; ++e) v[e] = o[e][i] * inv;
+            store_out_n<QT, DPL>(p.out, row + DPL * i, v);
+          }
         }
       }
       return;
@@ -241,7 +248,12 @@ void decode_stream_kernel(StreamParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) dst[DPL * i + e] = o[e][i] * (PC ? vs[DPL * i + e] : p.vsc);
+        for (int e = 0; e < DPL; e += 4)
+          *reinterpret_cast<float4*>(dst + DPL * i + e) =
+              make_float4(o[e][i] * (PC ? vs[DPL * i + e] : p.vsc),
+                          o[e + 1][i] * (PC ? vs[DPL * i + e + 1] : p.vsc),
+                          o[e + 2][i] * (PC ? vs[DPL * i + e + 2] : p.vsc),
+                          o[e + 3][i] * (PC ? vs[DPL * i + e + 3] : p.vsc));
       if (G == 0) {
         p.ml[(slot * HS + c) * 2] = m_run;
         p.ml[(slot * HS + c) * 2 + 1] = l_tot;

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(64 * kVecWaves) void decode_vec_kernel(DecodeParams
 
   __shared__ float sm_m[kVecWaves * GMAX];
   __shared__ float sm_l[kVecWaves * GMAX];
-  __shared__ float sm_o[kVecWaves * GMAX * LD];
+  __shared__ __align__(16) float sm_o[kVecWaves * GMAX * LD];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int part = blockIdx.x, s = blockIdx.z;

@@ -292,14 +292,17 @@ struct MfmaTile {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) kop[kk] = as_v8<V8>(r.k[kk]);
     }
-    if (valid < 16) {
-      // tokens past the context hold stale data (possibly NaN): zero their V
-      // so that a zero weight cannot meet a NaN in the PV product
+    // Tokens past the context hold stale data (possibly NaN): zero their V
+    // so that a zero weight cannot meet a NaN in the PV product.  A select
+    // per word on every tile, not a branch on valid < 16: a branch joins
+    // two paths in the middle of the pipelined loop, and at the join the
+    // compiler's load-counter tracking falls back to waiting for nearly
+    // every load in flight (with four blocks in flight it waited for three).
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        if (4 * G + rr >= valid)
+    for (int rr = 0; rr < 4; ++rr) {
+      const bool live = 4 * G + rr < valid;
 #pragma unroll
-          for (int i = 0; i < ROWB / 4; ++i) r.v[rr].w[i] = 0u;
+      for (int i = 0; i < ROWB / 4; ++i) r.v[rr].w[i] = live ? r.v[rr].w[i] : 0u;
     }
 
     P4 pb[NTL];            // PV weights of each column tile
@@ -418,6 +421,12 @@ struct MfmaTile {
 // Every load is issued unconditionally (ids past the chunk repeat its last
 // block, invalid ids read block 0 and carry no weight), so the load counter
 // can be waited on per block instead of drained.  nb must be > 0.
+// stride: step i of the piece reads the block whose id is row[i * stride]
+// (1: consecutive blocks; a wave taking every stride-th block of a run gets
+// row offset to its first one).  Steps b0, b1, last and the hook's period
+// count steps.  ids_first: the first window's ids, already loaded by the
+// caller (lane l of ids_first[w] = row[(b0 + 64 w + l) * stride], any
+// in-bounds id past the piece's end); nullptr: loaded here.
 // CAUSAL: column tile j of the lane attends to positions <= pos[j] only
 // (several queries of one sequence in one pass); otherwise pos is ignored.
 // PC: per-channel K scales, qlo the remainder of the scaled q (load_q_scaled).
@@ -448,18 +457,30 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
                                            float sl2, float* m_run, float* l_run, f32x4* o,
                                            int lane, const int* pos = nullptr,
                                            const uint4* qlo = nullptr,
-                                           const Hook& hook = Hook{}) {
+                                           const Hook& hook = Hook{}, int stride = 1,
+                                           const int* ids_first = nullptr) {
   using T = MfmaTile<QT, KVT, D>;
   using Raw = typename T::Raw;
   const int c = lane & 15, G = lane >> 4;
   const uint32_t koff = T::k_lane_off(c, G), voff = T::v_lane_off(c, G);
   constexpr int NW = PKV_ID_VGPRS;
   [[maybe_unused]] int rem = Hook::active ? hook.period - b0 % hook.period : 0;
+  // ids of the window of steps starting at c0 (in bounds: the step index is
+  // clamped to the piece's last one)
+  auto load_ids = [&](int* ids, int c0) {
+    const int n = min(64 * NW, b1 - c0);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) ids[w] = row[(int64_t)(c0 + min(64 * w + lane, n - 1)) * stride];
+  };
+  int ids[NW];
+  if (ids_first) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) ids[w] = ids_first[w];
+  } else {
+    load_ids(ids, b0);
+  }
   for (int c0 = b0; c0 < b1; c0 += 64 * NW) {
     const int n = min(64 * NW, b1 - c0);
-    int ids[NW];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) ids[w] = row[c0 + min(64 * w + lane, n - 1)];   // in bounds
     auto id_at = [&](int i) {
       const int k = i < n ? i : n - 1;
       int v = __builtin_amdgcn_readlane(ids[0], k & 63);
@@ -478,6 +499,10 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
       idc[d] = id_at(d);
       const int64_t a = addr(idc[d]);
       T::template issue<NT>(buf[d], kc + a, vc + a, koff, voff);
+      // Keep the blocks' loads in consumption order: the scheduler would
+      // otherwise issue buf[0] last, and at the loop entry the load counter
+      // would then be waited down to the newest block only.
+      __builtin_amdgcn_sched_barrier(0);
     }
     for (int i = 0; i < n; i += DEPTH) {
 #pragma unroll
@@ -502,6 +527,7 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
         idc[d] = idn;
       }
     }
+    if (c0 + 64 * NW < b1) load_ids(ids, c0 + 64 * NW);
   }
 }
 
