@@ -62,6 +62,9 @@ def parse():
                     help="also time the multi-query workloads (prompt chunks, draft "
                          "verification) and add them under 'multiquery' (implied by "
                          "--all-configs)")
+    ap.add_argument("--mq-only", default="",
+                    help="time only this multi-query workload (a key of synth.MQ_CONFIGS) and "
+                         "print its figures: for profiling one multi-query kernel")
     ap.add_argument("--swap", action="store_true",
                     help="also time swapping half the sequences to pinned host memory and "
                          "back (implied by --all-configs)")
@@ -747,6 +750,11 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     dev = "cuda:0"
+    if args.mq_only:
+        from synth import MQ_CONFIGS
+        res = time_multiquery(MQ_CONFIGS[args.mq_only], args, dev)
+        print(json.dumps({"multiquery_workload": args.mq_only, **res}), flush=True)
+        return
     cfg = CONFIGS[args.config]
     ps = cfg.partition_size if args.partition < 0 else args.partition
     res = time_config(cfg, args, dev, ps)

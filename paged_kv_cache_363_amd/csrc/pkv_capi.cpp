@@ -90,6 +90,27 @@ int32_t device_cus() {
   return n;
 }
 
+int32_t device_xccs() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int32_t> cached[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return 8;
+  }
+  if (dev < kMaxDevices) {
+    const int32_t v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = 8;
+  }
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 // 0: no override (the device's CU count)
 static thread_local int32_t t_stream_workgroups = 0;
 
@@ -235,21 +256,18 @@ bool mq_plan(int32_t num_rows, int32_t num_seqs, int32_t max_query_len, int32_t 
       return true;
     }
   }
-  // Fixed grid.  Several column tiles per wave read a (sequence, kv-head)'s
-  // K/V once instead of once per row tile; that pays when the re-reads would
-  // not stay in the L2, for tables of 8192 tokens or more (2-4 MB of K/V per
-  // kv-head at head_dim 128), and for a single pass whose four-tile grid is
-  // at most two workgroups per CU (there the row tiles of one kv-head, dealt
-  // round robin to the XCDs, would each fetch the K/V from HBM).  Otherwise
-  // one column tile, whose smaller register file lets two waves share a
-  // SIMD.  Measured: 512-row chunks at 32K tokens 18.1 -> 12.8 ms with four
-  // tiles; 8-row verification on the 70B-shaped E4M3 cache, one pass, 98.3
-  // -> 65.6 us; 64-row chunks of contexts up to 2048 tokens (8192 four-tile
-  // workgroups) 0.72 -> 0.81 ms, so those keep one.
-  const bool one_pass = partition_size >= max_ctx && max_ctx > 0;
-  plan->max_ntl = (max_ctx >= 8192 || (one_pass && mq_small_grid(num_seqs, num_kv_heads, g, mq)))
-                      ? 4
-                      : 1;
+  // Fixed grid: two column tiles per wave.  Against one, each K/V load
+  // serves twice the columns; against four, the accumulators of two tiles
+  // fit the vector registers of two waves per SIMD, which overlap each
+  // other's softmax and matrix work.  Measured on the fixed grid (all with
+  // the accumulators in vector registers): 8-row verification on the
+  // 70B-shaped E4M3 cache 78.0 / 55.5 / 63.8 us with 1 / 2 / 4 tiles, 64-row
+  // MHA chunks 728 / 504 / 717 us, 512-row chunks at 32K tokens 18.1 / 10.0 /
+  // 10.6 ms.
+  plan->max_ntl = 2;
+#ifdef PKV_MQ_FORCE_NTL
+  plan->max_ntl = PKV_MQ_FORCE_NTL;
+#endif
   const MQTiles t = mq_tiles(g, mq, plan->max_ntl);
   // workgroups per sequence and partition: kv-heads x head chunks x row tiles
   const int64_t per_seq = (int64_t)num_kv_heads * t.hchunks * t.qtiles;

@@ -35,6 +35,9 @@ constexpr int kDefaultCUs = 256;            // an MI355X, when no device answers
 // device; kDefaultCUs when no device is visible (the host planners still
 // answer on a machine without one).
 int32_t device_cus();
+// XCDs (compute dies, each with its own L2) of the current device, read once
+// per device; 8 (an MI355X) when no device answers.
+int32_t device_xccs();
 // Workgroups of 4 waves the balanced schedules launch for calls made by the
 // calling thread: the device's CU count (one wave per SIMD) unless the
 // thread set an override (pkv_set_stream_workgroups).

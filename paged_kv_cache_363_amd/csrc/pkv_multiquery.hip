@@ -14,7 +14,8 @@
 // rows), so one K/V load, widened once, serves up to 64 (row, q-head)
 // columns.  Each lane masks its column's logits at that row's position.
 //
-// Grid (partition, kv-head x head chunk x row tile, sequence).  A workgroup
+// One workgroup per (partition, sequence, kv-head, head chunk, row tile),
+// ordered so that a group's row tiles share an XCD (see the kernel).  A workgroup
 // walks the blocks its last row can see; its four waves take contiguous
 // quarters of them and merge in LDS.  With several partitions each workgroup
 // writes (m, l, acc) partials, an empty partition writing m = -inf, l = 0, and
@@ -64,6 +65,8 @@ struct MQParams {
   float* ws_m;       // [rows][Hq][P]
   float* ws_l;       // [rows][Hq][P]
   float* ws_acc;     // [rows][Hq][P][D]
+  int nx;            // XCDs of the device (workgroup placement, see below)
+  int64_t groups;    // (partition, sequence, kv-head, head chunk) groups
 };
 
 // Rows [r0, r0 + n) of sequence s, clamped so that every row index lies in
@@ -93,10 +96,24 @@ void multiquery_mfma_kernel(MQParams p) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, G = lane >> 4;
-  const int part = blockIdx.x, s = blockIdx.z;
-  int yy = blockIdx.y;
-  const int qt = yy % p.qtiles;
-  yy /= p.qtiles;
+  // The row tiles of one (partition, sequence, kv-head, head chunk) group
+  // read the same K/V.  Workgroups are dealt to the XCDs round robin by
+  // index, each XCD with its own L2, so the grid is ordered to put all row
+  // tiles of a group on one XCD: runs of nx * qtiles workgroups hold nx
+  // groups, group x of a run taking the indices congruent to x mod nx.
+  // (Any order computes the same result; this one lets one XCD's L2 serve
+  // a group's repeated reads.)
+  const int64_t run = (int64_t)p.nx * p.qtiles;
+  const int64_t g0 = blockIdx.x / run;
+  const int rr = (int)(blockIdx.x - g0 * run);
+  const int qt = rr / p.nx;
+  const int64_t grp = g0 * p.nx + rr % p.nx;
+  if (grp >= p.groups) return;
+  const int part = (int)(grp % p.num_parts);
+  int64_t yy64 = grp / p.num_parts;
+  const int Yg = p.Hkv * p.hchunks;
+  const int s = (int)(yy64 / Yg);
+  const int yy = (int)(yy64 % Yg);
   const int hc = yy % p.hchunks, hk = yy / p.hchunks;
   int r0, n;
   seq_rows(p, s, r0, n);
@@ -661,13 +678,18 @@ MQParams make_mq_params(const pkv::MQArgs& a) {
   p.ws_m = a.ws_m;
   p.ws_l = a.ws_l;
   p.ws_acc = a.ws_acc;
+  p.nx = pkv::device_xccs();
+  p.groups = (int64_t)p.num_parts * p.S * p.Hkv * p.hchunks;
   return p;
 }
 
 template <int QT, int KVT, int D>
 int launch_mq_t(const pkv::MQArgs& a) {
   const MQParams p = make_mq_params(a);
-  dim3 grid(p.num_parts, p.Hkv * p.hchunks * p.qtiles, p.S);
+  const int64_t runs = (p.groups + p.nx - 1) / p.nx;
+  const int64_t nwg = runs * p.nx * p.qtiles;
+  if (nwg > INT32_MAX) return (int)hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)nwg);
   const dim3 block(64 * pkv::kWaves);
   auto k = p.ntl == 4   ? multiquery_mfma_kernel<QT, KVT, D, 4>
            : p.ntl == 2 ? multiquery_mfma_kernel<QT, KVT, D, 2>
