@@ -72,6 +72,7 @@ struct Mfma<PKV_BF16> {
   __device__ static uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
   }
+  __device__ static uint32_t pack2_one(float a, float b) { return pack2(a, b); }
   // two INT8 codes (bytes 2*hi and 2*hi+1 of w) -> two bf16 (exact: |code| <= 127)
   __device__ static uint32_t i8x2(uint32_t w, bool hi) {
     const uint32_t h = hi ? w >> 16 : w;
@@ -98,6 +99,13 @@ struct Mfma<PKV_F16> {
   __device__ static uint32_t pack2(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+  }
+  // The same rounding (nearest, ties to even) in one v_cvt_pk_f16_f32: fewer
+  // instructions for the multi-query kernels, which are bound by their
+  // per-tile instructions; decode on the 70B-shaped E4M3 cache measured
+  // 0.3 us slower with it, so decode keeps pack2.
+  __device__ static uint32_t pack2_one(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
   }
   __device__ static uint32_t i8x2(uint32_t w, bool hi) {
     const uint32_t h = hi ? w >> 16 : w;
@@ -273,7 +281,7 @@ struct MfmaTile {
   // zeroed; rows in [vis, valid) are finite and get weight zero.
   // PC (one column tile only): qlo holds the remainder of per-channel-scaled
   // q (load_q_scaled), a second QK pass.
-  template <int NTL = 1, bool PC = false>
+  template <int NTL = 1, bool PC = false, bool CAUSAL = false>
   __device__ static void consume(Raw& r, int valid, const int* vis, const uint4* qr, float sl2,
                                  float* m_run, float* l_run, f32x4* o, int c, int G,
                                  const uint4* qlo = nullptr) {
@@ -292,22 +300,36 @@ struct MfmaTile {
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) kop[kk] = as_v8<V8>(r.k[kk]);
     }
+    // Several column tiles or a causal limit: the multi-query kernels, whose
+    // time goes to the per-tile update; one tile without it: decode, bound
+    // by memory.  The two keep separate forms of the steps below, each the
+    // faster one measured for its kernels.
+    constexpr bool MQ = NTL > 1 || CAUSAL;
     // Tokens past the context hold stale data (possibly NaN): zero their V
-    // so that a zero weight cannot meet a NaN in the PV product.  A select
-    // per word on every tile, not a branch on valid < 16: a branch joins
-    // two paths in the middle of the pipelined loop, and at the join the
-    // compiler's load-counter tracking falls back to waiting for nearly
-    // every load in flight (with four blocks in flight it waited for three).
+    // so that a zero weight cannot meet a NaN in the PV product.  Only a
+    // context's last block has fewer than 16 valid tokens: the multi-query
+    // form skips the others with a branch (12 instructions per block saved;
+    // with two blocks in flight its join adds no wait), decode selects on
+    // every tile.
+    if constexpr (MQ) {
+      if (valid < 16) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const bool live = 4 * G + rr < valid;
+        for (int rr = 0; rr < 4; ++rr)
+          if (4 * G + rr >= valid)
 #pragma unroll
-      for (int i = 0; i < ROWB / 4; ++i) r.v[rr].w[i] = live ? r.v[rr].w[i] : 0u;
+            for (int i = 0; i < ROWB / 4; ++i) r.v[rr].w[i] = 0u;
+      }
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const bool live = 4 * G + rr < valid;
+#pragma unroll
+        for (int i = 0; i < ROWB / 4; ++i) r.v[rr].w[i] = live ? r.v[rr].w[i] : 0u;
+      }
     }
 
     P4 pb[NTL];            // PV weights of each column tile
     [[maybe_unused]] V4 pl[NTL];   // their bf16 remainders (bf16 caches)
-    float alpha[NTL];      // rescale factor of each column tile's acc
     // S = K Q^T of every column tile first (independent MFMA chains, one
     // basic block): lane (G, c) gets tokens 4G+i, column c.
     f32x4 sacc[NTL];
@@ -322,32 +344,13 @@ struct MfmaTile {
         for (int kk = 0; kk < KSTEPS; ++kk) sacc[j] = M::qk(kop[kk], as_v8<V8>(qlo[kk]), sacc[j]);
       }
     }
-#pragma unroll
-    for (int j = 0; j < NTL; ++j) {
-      float z[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = (4 * G + i < vis[j]) ? sacc[j][i] * sl2 : kNegInf;
-      float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      bm = wave_max4(bm);
-      // The reference the weights are taken against moves only when the
-      // tile's maximum exceeds it by more than PKV_LAZY_RESCALE (base-2
-      // units): weights up to 2^PKV_LAZY_RESCALE, no rescale of l and acc
-      // for small rises.  l and acc keep one common reference, so the final
-      // acc / l (and the log-sum-exp merges) are the same in real arithmetic.
-      const float m_new = fmaxf(m_run[j], bm);
-      const float m_keep =
-          (m_run[j] != kNegInf && m_new <= m_run[j] + PKV_LAZY_RESCALE) ? m_run[j] : m_new;
-      // A tile with no valid token so far (m_keep still -inf) shifts by 0, so
-      // that it leaves the state at zero instead of producing NaN.
-      const float m_ref = m_keep == kNegInf ? 0.f : m_keep;
-      alpha[j] = __builtin_amdgcn_exp2f(m_run[j] - m_ref);
-      float pr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_ref);
-      l_run[j] = l_run[j] * alpha[j] + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-      m_run[j] = m_keep;
-      // B operand of PV: k-slot (G, i) = token 4G+i, column c.
-      pb[j] = as_v4<P4>(PM::pack2(pr[0], pr[1]), PM::pack2(pr[2], pr[3]));
+    // the PV B operand of column tile j from its weights
+    auto weights = [&](int j, const float* pr) {
+      // k-slot (G, i) = token 4G+i, column c
+      if constexpr (MQ)
+        pb[j] = as_v4<P4>(PM::pack2_one(pr[0], pr[1]), PM::pack2_one(pr[2], pr[3]));
+      else
+        pb[j] = as_v4<P4>(PM::pack2(pr[0], pr[1]), PM::pack2(pr[2], pr[3]));
       if constexpr (!PVH) {
         // bf16: the weight as a bf16 head plus its bf16 remainder
         float lo[4];
@@ -355,18 +358,91 @@ struct MfmaTile {
         for (int i = 0; i < 4; ++i) lo[i] = pr[i] - M::rounded(pr[i]);
         pl[j] = as_v4<V4>(M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]));
       }
-    }
-    // One branch for every column tile's rescale (a tile whose factor is 1
-    // is multiplied by 1, which changes nothing), so that the tiles' MFMA
-    // chains above are not cut into separate basic blocks.
-    bool resc = false;
+    };
+    // The reference the weights are taken against moves only when the
+    // tile's maximum exceeds it by more than PKV_LAZY_RESCALE (base-2 units):
+    // weights up to 2^PKV_LAZY_RESCALE, no rescale of l and acc for small
+    // rises.  l and acc keep one common reference, so the final acc / l (and
+    // the log-sum-exp merges) are the same in real arithmetic.  A tile with
+    // no valid token so far (m_keep still -inf) shifts by 0, so that it
+    // leaves the state at zero instead of producing NaN.  acc is rescaled in
+    // one branch for every column tile (a tile whose factor is 1 is
+    // multiplied by 1, which changes nothing), so that the tiles' MFMA chains
+    // above stay in one basic block.
+    if constexpr (!MQ) {
+      float z[4];
 #pragma unroll
-    for (int j = 0; j < NTL; ++j) resc = resc || alpha[j] != 1.0f;
-    if (__any(resc)) {
+      for (int i = 0; i < 4; ++i) z[i] = (4 * G + i < vis[0]) ? sacc[0][i] * sl2 : kNegInf;
+      float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      bm = wave_max4(bm);
+      const float m_new = fmaxf(m_run[0], bm);
+      const float m_keep =
+          (m_run[0] != kNegInf && m_new <= m_run[0] + PKV_LAZY_RESCALE) ? m_run[0] : m_new;
+      const float m_ref = m_keep == kNegInf ? 0.f : m_keep;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[0] - m_ref);
+      float pr[4];
 #pragma unroll
-      for (int j = 0; j < NTL; ++j)
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_ref);
+      l_run[0] = l_run[0] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+      m_run[0] = m_keep;
+      weights(0, pr);
+      if (__any(alpha != 1.0f)) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) o[j * DPL + e] *= alpha[j];
+        for (int e = 0; e < DPL; ++e) o[e] *= alpha;
+      }
+    } else {
+      // Most tiles are seen whole by every column: then the per-token test
+      // of the causal limit is skipped (a wave-uniform branch with no load
+      // inside).  The rescale factors' exponentials and the multiplies run
+      // only when some reference moves.
+      float zz[NTL][4];
+      bool whole = true;
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) whole = whole && vis[j] >= 16;
+      if (__all(whole)) {
+#pragma unroll
+        for (int j = 0; j < NTL; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) zz[j][i] = sacc[j][i] * sl2;
+      } else {
+#pragma unroll
+        for (int j = 0; j < NTL; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            zz[j][i] = (4 * G + i < vis[j]) ? sacc[j][i] * sl2 : kNegInf;
+      }
+      float m_old[NTL], m_rf[NTL], psum[NTL];
+      bool resc = false;
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) {
+        const float* z = zz[j];
+        float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        bm = wave_max4(bm);
+        const float m_new = fmaxf(m_run[j], bm);
+        const bool keep = m_run[j] != kNegInf && m_new <= m_run[j] + PKV_LAZY_RESCALE;
+        const float m_keep = keep ? m_run[j] : m_new;
+        const float m_ref = m_keep == kNegInf ? 0.f : m_keep;
+        resc = resc || !keep;
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_ref);
+        psum[j] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        m_old[j] = m_run[j];
+        m_rf[j] = m_ref;
+        m_run[j] = m_keep;
+        weights(j, pr);
+      }
+      if (__any(resc)) {
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) {
+          const float alpha = __builtin_amdgcn_exp2f(m_old[j] - m_rf[j]);
+          l_run[j] *= alpha;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) o[j * DPL + e] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NTL; ++j) l_run[j] += psum[j];
     }
 
     // A operand of PV for m-tile e: dim DPL*c + e of tokens 4G..4G+3, built
@@ -515,7 +591,8 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
 #pragma unroll
         for (int j = 0; j < NTL; ++j)
           vis[j] = CAUSAL ? min(valid, pos[j] - 16 * (c0 + ii) + 1) : valid;
-        T::template consume<NTL, PC>(buf[d], valid, vis, qr, sl2, m_run, l_run, o, c, G, qlo);
+        T::template consume<NTL, PC, CAUSAL>(buf[d], valid, vis, qr, sl2, m_run, l_run, o, c, G,
+                                             qlo);
         if constexpr (Hook::active) {
           if (ii < n && (--rem == 0 || c0 + ii == b1 - 1)) {
             hook();
