@@ -175,7 +175,7 @@ static bool make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
   const int32_t chunk = g < 16 ? g : 16;
   const int64_t Y = (int64_t)num_kv_heads * ((g + chunk - 1) / chunk);
   const bool grid_ok = stream_capable_kv(kv_dtype) && num_seqs <= kMaxStreamSeqs &&
-                       (int64_t)num_seqs * (max_blocks_per_seq + kv_restart_units(kv_dtype)) * Y <
+                       (int64_t)num_seqs * (max_blocks_per_seq + stream_restart_units(kv_dtype)) * Y <
                            ((int64_t)1 << 31);
   plan->stream_ok = partition_size == 0 && grid_ok;
   plan->parts_stream_ok = kPartsOnStreamGrid && partition_size > 0 && plan->num_parts > 1 && grid_ok;
@@ -422,7 +422,8 @@ int32_t pkv_decode_partition_size_for_lengths(const int32_t* context_lens, int32
   const int32_t g = num_q_heads / num_kv_heads;
   const int32_t chunk = g < 16 ? g : 16;
   const int64_t Y = (int64_t)num_kv_heads * ((g + chunk - 1) / chunk);
-  const int64_t R = kv_restart_units(kv_dtype);
+  const int64_t R = stream_restart_units(kv_dtype);   // a piece of the balanced schedule
+  const int64_t Rf = kv_restart_units(kv_dtype);      // a wave's start in a fixed partition
   // Costs in block loads of one wave (both schedules stream at the same
   // per-wave rate; only the split differs).
   //  balanced: the grid's waves share all units equally, then the merge
@@ -438,7 +439,7 @@ int32_t pkv_decode_partition_size_for_lengths(const int32_t* context_lens, int32
     const int64_t len = context_lens[s] < 0 ? 0 : (context_lens[s] > max_ctx ? max_ctx : context_lens[s]);
     const int64_t nbk = (len + kBlockSize - 1) / kBlockSize;
     units += nbk > 0 ? nbk + R : 0;
-    work[s] = nbk > 0 ? (nbk + kWaves - 1) / kWaves + R : 0;
+    work[s] = nbk > 0 ? (nbk + kWaves - 1) / kWaves + Rf : 0;
   }
   if (units == 0) return 0;
   const int64_t W = (int64_t)stream_workgroups() * kWaves;
@@ -557,7 +558,10 @@ pkv_status pkv::decode_impl(
   if (!make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, kv_dtype,
                  partition_size, &plan))
     return fail(PKV_ERR_INVALID_ARG, "decode: bad partition arguments");
-  const bool use_stream = plan.stream_ok && algo == PKV_ALGO_MFMA;
+  // the balanced kernels address a block's tile of one kv-head by the 31-bit
+  // index id * num_kv_heads + head
+  const bool tiles_fit = (int64_t)num_blocks * num_kv_heads < ((int64_t)1 << 31);
+  const bool use_stream = plan.stream_ok && tiles_fit && algo == PKV_ALGO_MFMA;
   const size_t need = use_stream ? plan.stream_bytes : (plan.num_parts > 1 ? plan.ws_bytes : 0);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
@@ -613,7 +617,7 @@ pkv_status pkv::decode_impl(
     return PKV_OK;
   }
   int rc = (algo == PKV_ALGO_MFMA)
-               ? (plan.parts_stream_ok ? launch_decode_stream_parts(a, plan.stream_grid)
+               ? (plan.parts_stream_ok && tiles_fit ? launch_decode_stream_parts(a, plan.stream_grid)
                                        : launch_decode_mfma(a))
                : launch_decode_vector(a);
   if (rc != 0)

@@ -6,18 +6,30 @@
 // flattened into units -- one 16-token block of one segment, a segment being
 // the q-heads of one kv-head (at most 16 of them) of one sequence, segments
 // in sequence order -- and a fixed grid of waves splits the units into equal
-// contiguous shares.  Every wave walks its share one piece (the part of one
-// segment inside the share) at a time with mfma_piece, which keeps the K/V
-// loads of the next blocks in flight while it works on the current one.
+// contiguous shares.  A share covers the tail of one segment, whole segments
+// and the head of another: a wave's pieces (the part of one segment inside
+// the share).
 //
-// A share covers the tail of one segment, whole segments and the head of
-// another.  A whole segment is normalised and stored by its wave.  A piece of
-// a segment is stored as (m, l, acc) in the wave's partial slot (its first
-// piece in slot 0, its last in slot 1).  The waves never signal each other:
-// across the XCDs of an MI355X that would need the L2 written back and
-// invalidated at every signal.  Instead decode_split_merge_kernel runs next
-// on the stream and merges the pieces of every split segment with the
-// log-sum-exp rule
+// One load pipeline runs through a wave's whole share.  Before the first
+// block the wave turns its steps (blocks, in share order) into cache tile
+// indices in LDS (block id * kv-heads + kv-head, so one index addresses a
+// block of any segment) and stages the q rows of its first pieces in LDS.
+// Every step then consumes one block and issues the loads of the block
+// DEPTH steps ahead, whichever piece it belongs to; a new piece only closes
+// the running softmax state and takes its q rows from LDS, with the next
+// blocks' loads in flight.  (A pipeline per piece paid about one loaded
+// round trip at every piece.)
+//
+// A closed piece goes to an LDS stash, not to memory: a store issued between
+// loads in flight holds up the wait for the next block until the store is
+// acknowledged (vector loads and stores share one counter on CDNA).  The
+// stash is written out when full and after the share's last block.  A whole
+// segment is normalised and stored; a piece of a split segment is stored as
+// (m, l, acc) in the wave's partial slot (its first piece in slot 0, its last
+// in slot 1).  The waves never signal each other: across the XCDs of an
+// MI355X that would need the L2 written back and invalidated at every
+// signal.  Instead decode_split_merge_kernel runs next on the stream and
+// merges the pieces of every split segment with the log-sum-exp rule
 //   M = max_k m_k,  L = sum_k l_k 2^(m_k - M),  out = sum_k acc_k 2^(m_k - M) / L.
 // Both kernels derive the shares from the same prefix sums of the block
 // counts, so the workspace carries nothing but the partial slots.
@@ -27,14 +39,8 @@
 // partition of P blocks into the fixed-partition workspace, and the
 // split-K reduction kernel merges them.  The shares' boundaries are moved up
 // to the next partition boundary, so every partition belongs to one wave,
-// and a wave closes each of its partitions when it has consumed the
-// partition's last block, with the loads of the next blocks in flight: the
-// load pipeline runs through a wave's whole share instead of restarting for
-// every partition, as one workgroup per partition would.  A closed partition
-// goes to a stash in LDS, not to memory: a store issued between two loads in
-// flight holds up the wait for the older load until the store is
-// acknowledged (vector loads and stores share one counter on CDNA), so the
-// stash is written out only when it is full and at the end of the piece.
+// and a wave closes each of its partitions into the stash when it has
+// consumed the partition's last block.
 //
 // Math: softmax(q K^T * scale) V over the block-table-gathered context
 // ("KV Cache 与 PageAttention深度实战", sections 1.2 and 3.2).
@@ -61,9 +67,14 @@ namespace {
 using namespace pkvd;
 
 constexpr int kSkWaves = 4;   // waves per workgroup; each wave is its own worker
-// partition mode: LDS stash of closed partitions, per wave
-constexpr int kStashFloats = 8192;   // accumulators (32 KiB)
-constexpr int kStashSlots = 16;      // at most this many partitions
+// per wave in LDS: the stash of closed pieces (partitions), the tile list of
+// the share's next steps, the q rows of the share's first pieces
+constexpr int kStashFloats = 4096;   // accumulators (16 KiB)
+constexpr int kStashSlots = 16;      // at most this many closed pieces
+constexpr int kTileCap = 512;        // steps (2 KiB)
+constexpr int kQStage = 768;         // uint4 (12 KiB): 3 pieces at D = 128
+// s_waitcnt vmcnt(0) (lgkmcnt and expcnt left at their maxima)
+constexpr int kVmcnt0 = 0x0F70;
 
 struct StreamParams {
   void* out;
@@ -130,15 +141,28 @@ template <int QT, int KVT, int D, bool PC, bool PM>
 __global__ __launch_bounds__(64 * kSkWaves) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void decode_stream_kernel(StreamParams p) {
   using T = MfmaTile<QT, KVT, D>;
+  using Raw = typename T::Raw;
   constexpr int DPL = T::DPL;
   constexpr int KS = T::KSTEPS;
+  constexpr int NW = PKV_ID_VGPRS;
+  constexpr int WIN = 64 * NW;                 // steps per register window of tiles
+  constexpr int QU4 = KS * 64 * (PC ? 2 : 1);  // uint4 of one piece's staged q
+  constexpr int NQ = kQStage / QU4 < 4 ? kQStage / QU4 : 4;
+  static_assert(NQ >= 1, "q stage holds at least one piece");
+  static_assert(kTileCap % WIN == 0, "tile list holds whole windows");
+  constexpr int DEPTH = pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH;
+  constexpr bool NT = pkv::byte_codes(KVT) ? PKV_NT_FP8 : PKV_NT_16;
 
   __shared__ int sm_pref[pkv::kMaxStreamSeqs + 1];   // segment units before sequence s
   __shared__ int sm_ctx[pkv::kMaxStreamSeqs];        // clamped context lengths
-  // partition mode: closed partitions of each wave, [slot][head][D] and
-  // [slot][head][2] (m, l)
-  __shared__ float sm_stash[PM ? kSkWaves * kStashFloats : 1];
-  __shared__ float sm_stml[PM ? kSkWaves * kStashSlots * 16 * 2 : 1];
+  // per wave: closed pieces or partitions ([slot][head][D] accumulators,
+  // [slot][head][2] (m, l), [slot] destination), the tile list of the
+  // share's next steps, and the q rows of its first pieces
+  __shared__ float sm_stash[kSkWaves * kStashFloats];
+  __shared__ float sm_stml[kSkWaves * kStashSlots * 16 * 2];
+  __shared__ int4 sm_meta[kSkWaves * kStashSlots];
+  __shared__ int sm_tiles[kSkWaves * kTileCap];
+  __shared__ uint4 sm_q[kSkWaves * kQStage];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -193,9 +217,128 @@ void decode_stream_kernel(StreamParams p) {
     j = (int)(r - (uint32_t)y * len);
   };
 
-  const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
-  uint4 qr[KS];
-  uint4 qlo[PC ? KS : 1];
+  // The share piece by piece: a piece is the part of one segment's blocks
+  // that lies in [u_lo, u_hi).  Segments follow each other in (sequence, y)
+  // order; sequences without blocks own no segment.  A piece made of restart
+  // units only has no block and is skipped.  Three walkers go over the same
+  // pieces: one counts them, one feeds the tile list, one follows the
+  // consumed blocks.
+  struct Walk {
+    int64_t u;
+    int s, y, j;
+    bool more;
+  };
+  struct Piece {
+    int s, y, b, b1;
+  };
+  Walk w0;
+  w0.u = u_lo;
+  w0.more = true;
+  locate(u_lo, w0.s, w0.y, w0.j);
+  auto walk_next = [&](Walk& wv, Piece& pc) -> bool {
+    while (wv.more) {
+      const int p0 = __builtin_amdgcn_readfirstlane(sm_pref[wv.s]);
+      const int len = __builtin_amdgcn_readfirstlane(sm_pref[wv.s + 1]) - p0;
+      const int64_t seg_start = Y * p0 + (int64_t)wv.y * len;
+      const int64_t pe = seg_start + len < u_hi ? seg_start + len : u_hi;
+      int b = max(wv.j - p.R, 0);
+      int b1 = max((int)(pe - seg_start) - p.R, 0);
+      if constexpr (PM) {
+        // both ends up to the next partition boundary (or the segment's
+        // end); the neighbouring share moves the same boundary the same way
+        const int nbk = len - p.R;
+        b = min((b + p.P - 1) / p.P * p.P, nbk);
+        b1 = min((b1 + p.P - 1) / p.P * p.P, nbk);
+      }
+      const Piece found{wv.s, wv.y, b, b1};
+      wv.u = pe;
+      if (wv.u >= u_hi) {
+        wv.more = false;
+      } else {
+        wv.j = 0;
+        if (++wv.y == p.Y) {
+          wv.y = 0;
+          do {
+            ++wv.s;
+          } while (sm_pref[wv.s + 1] == sm_pref[wv.s]);
+        }
+      }
+      if (b1 > b) {
+        pc = found;
+        return true;
+      }
+    }
+    return false;
+  };
+
+  // ---- stash of closed pieces (partitions), written out at the end ----
+  // A closed piece goes to LDS, not to memory: a store issued between loads
+  // in flight holds up the wait for the next block until the store is
+  // acknowledged (vector loads and stores share one counter on CDNA).  The
+  // stash is written out when full and after the share's last block.
+  // Lane (G, c) stashes and later stores its own 4 * DPL accumulators, so no
+  // other lane reads what it wrote.
+  const int HS = p.chunk_heads;
+  const int slots = min(kStashSlots, kStashFloats / (HS * D));
+  float* st = sm_stash + w * kStashFloats + c * D + DPL * 4 * G;
+  float* stml = sm_stml + w * kStashSlots * 32 + 2 * c;
+  int4* meta = sm_meta + w * kStashSlots;
+  int n_st = 0;
+  enum { kOut = 0, kPart = 1, kWsPart = 2 };
+  auto flush = [&]() {
+    for (int k = 0; k < n_st; ++k) {
+      const int4 mt = meta[k];
+      const int kind = __builtin_amdgcn_readfirstlane(mt.x);
+      const int s = __builtin_amdgcn_readfirstlane(mt.y);
+      const int y = __builtin_amdgcn_readfirstlane(mt.z);
+      const int idx = __builtin_amdgcn_readfirstlane(mt.w);
+      const int hc = y % p.hchunks, hk = y / p.hchunks;
+      const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
+      const int h_first = hk * p.g + hc * p.chunk_heads;
+      if (c >= nh) continue;
+      const float* src = st + k * HS * D;
+      const float m = stml[k * 32], l = stml[k * 32 + 1];
+      const float* vs = PC ? p.vs + (int64_t)hk * D + DPL * 4 * G : nullptr;
+      if (!PM && kind == kOut) {
+        const int64_t row = ((int64_t)s * p.Hq + h_first + c) * D + DPL * 4 * G;
+        const float inv = l > 0.f ? (PC ? 1.f / l : p.vsc / l) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v[DPL];
+#pragma unroll
+          for (int e = 0; e < DPL; ++e)
+            v[e] = PC ? src[DPL * i + e] * vs[DPL * i + e] * inv : src[DPL * i + e] * inv;
+          store_out_n<QT, DPL>(p.out, row + DPL * i, v);
+        }
+      } else {
+        float* dst;
+        float* dm;
+        float* dl;
+        if (PM) {
+          const int64_t prow = ((int64_t)s * p.Hq + h_first + c) * p.num_parts + idx;
+          dst = p.ws_acc + prow * D + DPL * 4 * G;
+          dm = p.ws_m + prow;
+          dl = p.ws_l + prow;
+        } else {
+          dst = p.part + ((int64_t)idx * HS + c) * D + DPL * 4 * G;
+          dm = p.ml + ((int64_t)idx * HS + c) * 2;
+          dl = dm + 1;
+        }
+#pragma unroll
+        for (int i = 0; i < 4 * DPL; i += 4)
+          *reinterpret_cast<float4*>(dst + i) =
+              make_float4(src[i] * (PC ? vs[i] : p.vsc), src[i + 1] * (PC ? vs[i + 1] : p.vsc),
+                          src[i + 2] * (PC ? vs[i + 2] : p.vsc),
+                          src[i + 3] * (PC ? vs[i + 3] : p.vsc));
+        if (G == 0) {
+          *dm = m;
+          *dl = l;
+        }
+      }
+    }
+    n_st = 0;
+  };
+
   f32x4 o[DPL];
   float m_run = kNegInf, l_run = 0.f;
   auto reset = [&]() {
@@ -204,173 +347,286 @@ void decode_stream_kernel(StreamParams p) {
     m_run = kNegInf;
     l_run = 0.f;
   };
-
-  // Close the piece [b0, b_last] of segment (s, y): store or merge.
-  auto finish = [&](int s, int y, int b0, int b_last, bool first_piece) {
-    const int nbk = sm_pref[s + 1] - sm_pref[s] - p.R;
-    const int hc = y % p.hchunks;
-    const int h_first = (y / p.hchunks) * p.g + hc * p.chunk_heads;
-    const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
-    const int HS = p.chunk_heads;
+  // close the running state into the stash with its destination
+  auto close = [&](int kind, int s, int y, int idx) {
     const float l_tot = wave_sum4(l_run);
-    if (b0 == 0 && b_last == nbk - 1) {
-      if (c < nh) {
-        const int64_t row = ((int64_t)s * p.Hq + h_first + c) * D + DPL * 4 * G;
-        // lane (G, c) holds dims DPL*(4G+i) + e, e < DPL: DPL consecutive
-        // outputs per i, written with one store each
-        if constexpr (PC) {
-          const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-          const float* vs = p.vs + (int64_t)(y / p.hchunks) * D + DPL * 4 * G;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v[DPL];
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) v[e] = o[e][i] * vs[DPL * i + e] * inv;
-            store_out_n<QT, DPL>(p.out, row + DPL * i, v);
-          }
-        } else {
-          const float inv = l_tot > 0.f ? p.vsc / l_tot : 0.f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v[DPL];
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) v[e] = o[e][i] * inv;
-            store_out_n<QT, DPL>(p.out, row + DPL * i, v);
-          }
-        }
-      }
-      return;
-    }
-    const int64_t slot = 2 * (int64_t)wk + (first_piece ? 0 : 1);
-    if (c < nh) {
-      float* dst = p.part + (slot * HS + c) * D + DPL * 4 * G;
-      const float* vs = PC ? p.vs + (int64_t)(y / p.hchunks) * D + DPL * 4 * G : nullptr;
+    if (c < HS) {   // rows past the chunk would run into the next slot
+      float* dst = st + n_st * HS * D;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < DPL; e += 4)
-          *reinterpret_cast<float4*>(dst + DPL * i + e) =
-              make_float4(o[e][i] * (PC ? vs[DPL * i + e] : p.vsc),
-                          o[e + 1][i] * (PC ? vs[DPL * i + e + 1] : p.vsc),
-                          o[e + 2][i] * (PC ? vs[DPL * i + e + 2] : p.vsc),
-                          o[e + 3][i] * (PC ? vs[DPL * i + e + 3] : p.vsc));
-      if (G == 0) {
-        p.ml[(slot * HS + c) * 2] = m_run;
-        p.ml[(slot * HS + c) * 2 + 1] = l_tot;
-      }
+        for (int e = 0; e < DPL; ++e) dst[DPL * i + e] = o[e][i];
     }
+    if (G == 0) {
+      stml[n_st * 32] = m_run;
+      stml[n_st * 32 + 1] = l_tot;
+    }
+    if (lane == 0) meta[n_st] = make_int4(kind, s, y, idx);
+    if (++n_st == slots) flush();
+    reset();
   };
 
-  // Walk the share piece by piece: a piece is the part of one segment's
-  // blocks that lies in [u_lo, u_hi).  Segments follow each other in
-  // (sequence, y) order; sequences without blocks own no segment.  A piece
-  // made of restart units only has no block and is skipped.
-  int64_t u = u_lo;
-  int s, y, j;
-  locate(u, s, y, j);
-  bool first_piece = true;
-  while (true) {
-    const int len = sm_pref[s + 1] - sm_pref[s];
-    const int64_t seg_start = Y * sm_pref[s] + (int64_t)y * len;
-    const int64_t pe = seg_start + len < u_hi ? seg_start + len : u_hi;
-    int b = max(j - p.R, 0);
-    int b1 = max((int)(pe - seg_start) - p.R, 0);
-    if constexpr (PM) {
-      // both ends up to the next partition boundary (or the segment's end);
-      // the neighbouring share moves the same boundary the same way
-      const int nbk = len - p.R;
-      b = min((b + p.P - 1) / p.P * p.P, nbk);
-      b1 = min((b1 + p.P - 1) / p.P * p.P, nbk);
-    }
-    if (b1 > b) {
-      const int hc = y % p.hchunks;
-      const int hk = y / p.hchunks;
-      const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
-      if constexpr (PC)
-        T::load_q_scaled(qr, qlo, p.q, (int64_t)s * p.Hq + hk * p.g + hc * p.chunk_heads + c,
-                         c < nh, G, p.ks + (int64_t)hk * D);
-      else
-        T::load_q(qr, p.q, (int64_t)s * p.Hq + hk * p.g + hc * p.chunk_heads + c, c < nh, G);
-      reset();
-      const int ctx = sm_ctx[s];
-      const int last = ((ctx + 15) >> 4) - 1;
-      constexpr int DEPTH = pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH;
-      constexpr bool NT = pkv::byte_codes(KVT) ? PKV_NT_FP8 : PKV_NT_16;
-      const int64_t off = (int64_t)hk * T::TILE;
-      if constexpr (PM) {
-        // Close partition kp0 + n_st into stash slot n_st and start the next
-        // partition; write the stash out when it is full and at the end.
-        // Lane (G, c) stashes and later stores its own 4 * DPL accumulators,
-        // so no other lane reads what it wrote.
-        const int h_first = hk * p.g + hc * p.chunk_heads;
-        const int HS = p.chunk_heads;
-        const int slots = min(kStashSlots, kStashFloats / (HS * D));
-        float* st = sm_stash + w * kStashFloats + c * D + DPL * 4 * G;
-        float* stml = sm_stml + w * kStashSlots * 32 + 2 * c;
-        int kp0 = b / p.P, n_st = 0;
-        auto write_out = [&]() {
-          if (c < nh) {
-            const int64_t row = (int64_t)s * p.Hq + h_first + c;
-            for (int k = 0; k < n_st; ++k) {
-              const int64_t prow = row * p.num_parts + kp0 + k;
-              const float* src = st + k * HS * D;
-              float* dst = p.ws_acc + prow * D + DPL * 4 * G;
+  // ---- count the share's steps (blocks) and note its first pieces ----
+  int total = 0, npieces = 0;
+  Piece pq[NQ];
+  {
+    Walk tw = w0;
+    Piece pc;
+    while (walk_next(tw, pc)) {
 #pragma unroll
-              for (int i = 0; i < 4 * DPL; ++i) dst[i] = src[i];
-              if (G == 0) {
-                p.ws_m[prow] = stml[k * 32];
-                p.ws_l[prow] = stml[k * 32 + 1];
-              }
-            }
-          }
-          kp0 += n_st;
-          n_st = 0;
-        };
-        auto close = [&]() {
-          const float l_tot = wave_sum4(l_run);
-          if (c < nh) {
-            float* dst = st + n_st * HS * D;
-            const float* vs = PC ? p.vs + (int64_t)hk * D + DPL * 4 * G : nullptr;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-              for (int e = 0; e < DPL; ++e)
-                dst[DPL * i + e] = o[e][i] * (PC ? vs[DPL * i + e] : p.vsc);
-            if (G == 0) {
-              stml[n_st * 32] = m_run;
-              stml[n_st * 32 + 1] = l_tot;
-            }
-          }
-          if (++n_st == slots) write_out();
-          reset();
-        };
-        const PeriodHook<decltype(close)> hook{p.P, close};
-        if (p.nb > 0)
-          mfma_piece<QT, KVT, D, DEPTH, NT, false, PC, 1, PeriodHook<decltype(close)>>(
-              p.kc + off, p.vc + off, blk_stride, p.bt + (int64_t)s * p.mb, b, b1, last,
-              ctx - 16 * last, p.nb, qr, p.sl2, &m_run, &l_run, o, lane, nullptr, qlo, hook);
-        else   // no block can be valid: every partition is empty
-          for (int k = b / p.P; k < (b1 + p.P - 1) / p.P; ++k) close();
-        write_out();
-      } else {
-        if (p.nb > 0)
-          mfma_piece<QT, KVT, D, DEPTH, NT, false, PC>(
-              p.kc + off, p.vc + off, blk_stride, p.bt + (int64_t)s * p.mb, b, b1, last,
-              ctx - 16 * last, p.nb, qr, p.sl2, &m_run, &l_run, o, lane, nullptr, qlo);
-        finish(s, y, b, b1 - 1, first_piece);
-      }
-      first_piece = false;
-    }
-    u = pe;
-    if (u >= u_hi) break;
-    j = 0;
-    if (++y == p.Y) {
-      y = 0;
-      do {
-        ++s;
-      } while (sm_pref[s + 1] == sm_pref[s]);
+      for (int i = 0; i < NQ; ++i)
+        if (npieces == i) pq[i] = pc;
+      ++npieces;
+      total += pc.b1 - pc.b;
     }
   }
+  if (total == 0) return;
+  reset();
+
+  if (p.nb == 0) {
+    // no block id can be valid: every piece (partition) closes empty
+    Walk tw = w0;
+    Piece pc;
+    int pi = 0;
+    while (walk_next(tw, pc)) {
+      if constexpr (PM) {
+        for (int k = pc.b / p.P; k < (pc.b1 + p.P - 1) / p.P; ++k) close(kWsPart, pc.s, pc.y, k);
+      } else {
+        const int nbk = (sm_ctx[pc.s] + 15) >> 4;
+        if (pc.b == 0 && pc.b1 == nbk) close(kOut, pc.s, pc.y, 0);
+        else close(kPart, pc.s, pc.y, 2 * wk + (pi == 0 ? 0 : 1));
+      }
+      ++pi;
+    }
+    flush();
+    return;
+  }
+
+  // ---- q rows of the first pieces: loaded together, staged in LDS ----
+  const int nq = min(npieces, NQ);
+  auto q_row = [&](const Piece& pc) {
+    const int hc = pc.y % p.hchunks, hk = pc.y / p.hchunks;
+    return (int64_t)pc.s * p.Hq + hk * p.g + hc * p.chunk_heads + c;
+  };
+  auto q_live = [&](const Piece& pc) {
+    const int hc = pc.y % p.hchunks;
+    return c < min(p.chunk_heads, p.g - hc * p.chunk_heads);
+  };
+  auto load_q_of = [&](const Piece& pc, uint4* qh, uint4* ql) {
+    if constexpr (PC)
+      T::load_q_scaled(qh, ql, p.q, q_row(pc), q_live(pc), G,
+                       p.ks + (int64_t)(pc.y / p.hchunks) * D);
+    else
+      T::load_q(qh, p.q, q_row(pc), q_live(pc), G);
+  };
+  uint4 qr[KS];
+  uint4 qlo[PC ? KS : 1];
+  uint4 qt[NQ][KS];
+  uint4 qtl[NQ][PC ? KS : 1];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i)
+    if (i < nq) load_q_of(pq[i], qt[i], qtl[i]);
+
+  // ---- tile list: the share's steps as cache tile indices ----
+  // tile = id * Hkv + hk for a valid block id, -1 for an invalid one (its
+  // loads read tile 0 and it carries no weight).  Filled kTileCap steps at a
+  // time by all lanes (lane t of window v: step 64 v + t), steps past the
+  // share's end repeating its last one; read back a window of WIN steps at
+  // a time into registers.
+  int* tiles = sm_tiles + w * kTileCap;
+  Walk lw = w0;
+  Piece lp;
+  bool lp_ok = walk_next(lw, lp);
+  int lo_off = 0;
+  uint32_t last_roff = 0;
+  int last_hk = 0;
+  auto fill = [&]() {
+    constexpr int NV = kTileCap / 64;
+    uint32_t roff[NV];
+    int hkv[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      roff[v] = 0;
+      hkv[v] = 0;
+    }
+    int acc = 0;
+    while (lp_ok && acc < kTileCap) {
+      const int L = lp.b1 - lp.b - lo_off;
+      const int take = min(L, kTileCap - acc);
+      // step t of this fill (acc <= t < acc + take) is block lp.b + lo_off + t - acc
+      const uint32_t base = (uint32_t)lp.s * (uint32_t)p.mb + (uint32_t)(lp.b + lo_off) - (uint32_t)acc;
+      const int hkp = lp.y / p.hchunks;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int t = 64 * v + lane;
+        if (t >= acc && t < acc + take) {
+          roff[v] = base + (uint32_t)t;
+          hkv[v] = hkp;
+        }
+      }
+      last_roff = base + (uint32_t)(acc + take - 1);
+      last_hk = hkp;
+      acc += take;
+      lo_off += take;
+      if (lo_off == lp.b1 - lp.b) {
+        lo_off = 0;
+        lp_ok = walk_next(lw, lp);
+      }
+    }
+    int id[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int t = 64 * v + lane;
+      if (t >= acc) {
+        roff[v] = last_roff;
+        hkv[v] = last_hk;
+      }
+      id[v] = p.bt[roff[v]];
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      tiles[64 * v + lane] = (unsigned)id[v] < (unsigned)p.nb ? id[v] * p.Hkv + hkv[v] : -1;
+  };
+  int idw[NW];
+  int wk0 = 0, fill_base = 0;
+  auto read_window = [&]() {
+#pragma unroll
+    for (int v = 0; v < NW; ++v) idw[v] = tiles[wk0 - fill_base + 64 * v + lane];
+  };
+  fill();
+  int fe = kTileCap;
+  read_window();
+
+  // stage the q rows (the first piece's go straight to registers)
+#pragma unroll
+  for (int k = 0; k < KS; ++k) {
+    qr[k] = qt[0][k];
+    if constexpr (PC) qlo[k] = qtl[0][k];
+  }
+  uint4* qs = sm_q + w * kQStage;
+#pragma unroll
+  for (int i = 1; i < NQ; ++i)
+    if (i < nq) {
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        qs[(i * KS + k) * 64 + lane] = qt[i][k];
+        if constexpr (PC) qs[((NQ + i) * KS + k) * 64 + lane] = qtl[i][k];
+      }
+    }
+
+  // tile of the next step to issue (steps past the end repeat the last)
+  int kiss = 0;
+  auto next_tile = [&]() -> int {
+    const int k = min(kiss, total - 1);
+    ++kiss;
+    if (k >= wk0 + WIN) {
+      wk0 += WIN;
+      if (wk0 == fe) {
+        fill_base = fe;
+        fill();
+        fe += kTileCap;
+      }
+      read_window();
+    }
+    const int i = k - wk0;
+    int v = __builtin_amdgcn_readlane(idw[0], i & 63);
+#pragma unroll
+    for (int vv = 1; vv < NW; ++vv) {
+      const int x = __builtin_amdgcn_readlane(idw[vv], i & 63);
+      v = (i >> 6) == vv ? x : v;
+    }
+    return v;
+  };
+
+  // ---- the consumed piece ----
+  Walk cw = w0;
+  Piece cur;
+  walk_next(cw, cur);
+  int pi = 0;          // index of the current piece
+  int cb = cur.b;      // block of the segment consumed next
+  int c_last = ((sm_ctx[cur.s] + 15) >> 4) - 1;
+  int c_tail = sm_ctx[cur.s] - 16 * c_last;
+  int rem = PM ? p.P : 0;   // blocks left in the current partition
+
+  const uint32_t koff = T::k_lane_off(c, G), voff = T::v_lane_off(c, G);
+  auto issue = [&](Raw& r, int tile) {
+    const int64_t a = (int64_t)(tile < 0 ? 0 : tile) * T::TILE;
+    T::template issue<NT>(r, p.kc + a, p.vc + a, koff, voff);
+  };
+
+  Raw buf[DEPTH];
+  int idc[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    idc[d] = next_tile();
+    issue(buf[d], idc[d]);
+    // keep the blocks' loads in consumption order
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // step kc from slot d: consume, then close / switch pieces as due
+  int kc = 0;
+  auto consume_step = [&](int d) {
+    const bool live = kc < total;
+    const int valid = live && idc[d] >= 0 ? (cb == c_last ? c_tail : 16) : 0;
+    const int vis[1] = {valid};
+    T::template consume<1, PC, false>(buf[d], valid, vis, qr, p.sl2, &m_run, &l_run, o, c, G,
+                                      qlo);
+    if (live) {
+      ++cb;
+      if constexpr (PM) {
+        if (--rem == 0 || cb == cur.b1) {
+          close(kWsPart, cur.s, cur.y, (cb - 1) / p.P);
+          rem = p.P;
+        }
+      }
+      if (cb == cur.b1) {
+        if constexpr (!PM) {
+          if (cur.b == 0 && cur.b1 == c_last + 1) close(kOut, cur.s, cur.y, 0);
+          else close(kPart, cur.s, cur.y, 2 * wk + (pi == 0 ? 0 : 1));
+        }
+        if (++pi < npieces) {
+          walk_next(cw, cur);
+          cb = cur.b;
+          c_last = ((sm_ctx[cur.s] + 15) >> 4) - 1;
+          c_tail = sm_ctx[cur.s] - 16 * c_last;
+          if (pi < NQ) {
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+              qr[k] = qs[(pi * KS + k) * 64 + lane];
+              if constexpr (PC) qlo[k] = qs[((NQ + pi) * KS + k) * 64 + lane];
+            }
+          } else {
+            load_q_of(cur, qr, qlo);
+            // wait here: q registers left in flight on this rare path would
+            // make every later block wait for the newest loads
+            __builtin_amdgcn_s_waitcnt(kVmcnt0);
+          }
+        }
+      }
+    }
+    ++kc;
+  };
+
+  // Groups of DEPTH steps.  While the share has steps beyond the group's
+  // loads, every step issues the loads of the step DEPTH ahead (past the
+  // share's end they repeat its last tile), and a group runs to its end
+  // (a step past the end consumes nothing): a branch that skipped an issue
+  // would join the loop again and make the compiler wait for the newest
+  // loads at every block.  The last group issues nothing, so that nothing
+  // is left in flight when the stash is written out.
+  while (kc + DEPTH < total) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      consume_step(d);
+      const int tn = next_tile();
+      issue(buf[d], tn);
+      idc[d] = tn;
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) consume_step(d);
+  flush();
 }
 
 // Merge the pieces of every segment that the decode grid split between
@@ -466,7 +722,7 @@ StreamParams make_stream_params(const pkv::DecodeArgs& a, int grid, void* ws, si
   sp.ml = reinterpret_cast<float*>(w + off_ml);
   sp.part = reinterpret_cast<float*>(w + off_part);
   sp.W = grid * kSkWaves;
-  sp.R = pkv::kv_restart_units(a.kv_dtype);
+  sp.R = pkv::stream_restart_units(a.kv_dtype);
   sp.ks = kp.ks;
   sp.vs = kp.vs;
   sp.P = 0;

@@ -44,22 +44,29 @@ int32_t device_xccs();
 int32_t stream_workgroups();
 constexpr int kMaxStreamTiles = 4096;        // (sequence, row tile) pairs of a balanced multi-query call
 
-// Units the balanced schedule charges for starting a piece of a segment, in
-// blocks: a start costs about two loaded HBM round trips (q rows and block
-// ids, then the first K/V tiles), ~2 us, against ~1.3 us per 16-bit block and
-// ~0.7 us per E4M3 block per wave at one wave per SIMD.  The 16-bit value is
-// the measured best on a ragged batch (Qwen3-8B-shaped, 64 sequences of
-// 256..4096 tokens: 1 unit 5.68 TB/s, 2: 5.80, 3: 5.92, 4: 5.96, 6: 5.94);
-// one-byte codes keep the cost estimate.
+// Units a schedule charges for starting a piece of a segment, in blocks.
+// Where a piece starts with its own load pipeline (the one-workgroup-per-
+// partition kernels, the multi-query kernels) a start costs about two loaded
+// HBM round trips (q rows and block ids, then the first K/V tiles), ~2 us,
+// against ~1.3 us per 16-bit block and ~0.7 us per E4M3 block per wave at one
+// wave per SIMD: 4 and 3 units.  The balanced decode kernel keeps one load
+// pipeline through a wave's whole share, so a new piece costs only the close
+// of the previous one and the q rows staged in LDS; 2 units measured best on
+// a ragged batch (Qwen3-8B-shaped, 64 sequences of 256..4096 tokens: 88.8 us
+// at 1 unit, 88.5 at 2, 89.0 at 4) and on 32K contexts.
 #ifndef PKV_RESTART_UNITS_16
 #define PKV_RESTART_UNITS_16 4
 #endif
 #ifndef PKV_RESTART_UNITS_FP8
 #define PKV_RESTART_UNITS_FP8 3
 #endif
+#ifndef PKV_STREAM_RESTART_UNITS
+#define PKV_STREAM_RESTART_UNITS 2
+#endif
 inline int kv_restart_units(int32_t kv_dtype) {
   return byte_codes(kv_dtype) ? PKV_RESTART_UNITS_FP8 : PKV_RESTART_UNITS_16;
 }
+inline int stream_restart_units(int32_t) { return PKV_STREAM_RESTART_UNITS; }
 
 struct DecodeArgs {
   void* out;
