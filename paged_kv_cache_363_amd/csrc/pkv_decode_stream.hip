@@ -37,10 +37,10 @@
 // Fixed partitions (partition mode): when the caller fixes the split-K
 // partition size, the same persistent grid computes one (m, l, acc) per
 // partition of P blocks into the fixed-partition workspace, and the
-// split-K reduction kernel merges them.  The shares' boundaries are moved up
-// to the next partition boundary, so every partition belongs to one wave,
-// and a wave closes each of its partitions into the stash when it has
-// consumed the partition's last block.
+// split-K reduction kernel merges them.  There the units are whole
+// partitions, so every partition belongs to one wave, and a wave closes each
+// of its partitions into the stash when it has consumed the partition's last
+// block.
 //
 // Math: softmax(q K^T * scale) V over the block-table-gathered context
 // ("KV Cache 与 PageAttention深度实战", sections 1.2 and 3.2).
@@ -101,9 +101,11 @@ struct StreamParams {
 
 // Unit prefix sums in LDS, computed by one workgroup of 4 waves.  A segment
 // of a sequence with nbk blocks spans nbk + R units: R units that stand for
-// the cost of starting a piece (the q rows and block ids must arrive before
-// the first K/V loads can go out) followed by one unit per block.  Equal
-// shares of units are then equal in time, not just in blocks.
+// the cost of starting a piece (closing the previous one and taking the new
+// q rows) followed by one unit per block.  Equal shares of units are then
+// equal in time, not just in blocks.  In partition mode a unit is a whole
+// partition of the segment instead, so that no partition is split between
+// waves and no share needs rounding.
 // pref[s] = units of one segment of each sequence before s (0 for a
 // sequence without context).
 __device__ __forceinline__ void block_prefix(const StreamParams& p, int* sm_pref, int* sm_ctx) {
@@ -121,7 +123,8 @@ __device__ __forceinline__ void block_prefix(const StreamParams& p, int* sm_pref
     for (int base = 0; base < S; base += 64) {
       const int i = base + lane;
       const int nbk = i < S ? (sm_ctx[i] + 15) >> 4 : 0;
-      int x = nbk > 0 ? nbk + p.R : 0;
+      // partition mode: one unit per partition of the segment
+      int x = nbk > 0 ? (p.P > 0 ? (nbk + p.P - 1) / p.P : nbk + p.R) : 0;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(x, off);
@@ -241,14 +244,15 @@ void decode_stream_kernel(StreamParams p) {
       const int len = __builtin_amdgcn_readfirstlane(sm_pref[wv.s + 1]) - p0;
       const int64_t seg_start = Y * p0 + (int64_t)wv.y * len;
       const int64_t pe = seg_start + len < u_hi ? seg_start + len : u_hi;
-      int b = max(wv.j - p.R, 0);
-      int b1 = max((int)(pe - seg_start) - p.R, 0);
+      int b, b1;
       if constexpr (PM) {
-        // both ends up to the next partition boundary (or the segment's
-        // end); the neighbouring share moves the same boundary the same way
-        const int nbk = len - p.R;
-        b = min((b + p.P - 1) / p.P * p.P, nbk);
-        b1 = min((b1 + p.P - 1) / p.P * p.P, nbk);
+        // units are whole partitions: the piece is partitions [j, pe)
+        const int nbk = (sm_ctx[wv.s] + 15) >> 4;
+        b = wv.j * p.P;
+        b1 = min((int)(pe - seg_start) * p.P, nbk);
+      } else {
+        b = max(wv.j - p.R, 0);
+        b1 = max((int)(pe - seg_start) - p.R, 0);
       }
       const Piece found{wv.s, wv.y, b, b1};
       wv.u = pe;
@@ -272,12 +276,13 @@ void decode_stream_kernel(StreamParams p) {
   };
 
   // ---- stash of closed pieces (partitions), written out at the end ----
-  // A closed piece goes to LDS, not to memory: a store issued between loads
-  // in flight holds up the wait for the next block until the store is
-  // acknowledged (vector loads and stores share one counter on CDNA).  The
-  // stash is written out when full and after the share's last block.
-  // Lane (G, c) stashes and later stores its own 4 * DPL accumulators, so no
-  // other lane reads what it wrote.
+  // A closed piece goes to LDS, not to memory, and the stash is written out
+  // after the share's last block (or when full).  Writes mixed into the read
+  // stream cost far more than their bytes: flushing every partition as it
+  // closes made the 32K partitioned step 11% slower, and a fifth wave per
+  // workgroup that wrote the stash out while the other four streamed made
+  // it 12% slower, although no streaming wave then waited on a store.
+  // Lane (G, c) stashes its own 4 * DPL accumulators (row c of the slot).
   const int HS = p.chunk_heads;
   const int slots = min(kStashSlots, kStashFloats / (HS * D));
   float* st = sm_stash + w * kStashFloats + c * D + DPL * 4 * G;
@@ -285,6 +290,12 @@ void decode_stream_kernel(StreamParams p) {
   int4* meta = sm_meta + w * kStashSlots;
   int n_st = 0;
   enum { kOut = 0, kPart = 1, kWsPart = 2 };
+  // Written out row by row: a slot is HS rows of D floats in LDS, and every
+  // lane takes 4 consecutive floats of it, so each store instruction writes
+  // whole rows (the lanes' own 4 * DPL accumulators are scattered over 16
+  // rows and would leave most lanes idle and most lines partly written).
+  const float* stw = sm_stash + w * kStashFloats;
+  const float* stmw = sm_stml + w * kStashSlots * 32;
   auto flush = [&]() {
     for (int k = 0; k < n_st; ++k) {
       const int4 mt = meta[k];
@@ -294,45 +305,39 @@ void decode_stream_kernel(StreamParams p) {
       const int idx = __builtin_amdgcn_readfirstlane(mt.w);
       const int hc = y % p.hchunks, hk = y / p.hchunks;
       const int nh = min(p.chunk_heads, p.g - hc * p.chunk_heads);
-      const int h_first = hk * p.g + hc * p.chunk_heads;
-      if (c >= nh) continue;
-      const float* src = st + k * HS * D;
-      const float m = stml[k * 32], l = stml[k * 32 + 1];
-      const float* vs = PC ? p.vs + (int64_t)hk * D + DPL * 4 * G : nullptr;
-      if (!PM && kind == kOut) {
-        const int64_t row = ((int64_t)s * p.Hq + h_first + c) * D + DPL * 4 * G;
-        const float inv = l > 0.f ? (PC ? 1.f / l : p.vsc / l) : 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v[DPL];
-#pragma unroll
-          for (int e = 0; e < DPL; ++e)
-            v[e] = PC ? src[DPL * i + e] * vs[DPL * i + e] * inv : src[DPL * i + e] * inv;
-          store_out_n<QT, DPL>(p.out, row + DPL * i, v);
-        }
-      } else {
-        float* dst;
-        float* dm;
-        float* dl;
-        if (PM) {
-          const int64_t prow = ((int64_t)s * p.Hq + h_first + c) * p.num_parts + idx;
-          dst = p.ws_acc + prow * D + DPL * 4 * G;
-          dm = p.ws_m + prow;
-          dl = p.ws_l + prow;
+      const int64_t row0 = (int64_t)s * p.Hq + hk * p.g + hc * p.chunk_heads;   // first q-head
+      for (int e = 4 * lane; e < nh * D; e += 256) {
+        const int h = e / D, dim = e % D;
+        const float4 a = *reinterpret_cast<const float4*>(stw + k * HS * D + e);
+        const float m = stmw[k * 32 + 2 * h], l = stmw[k * 32 + 2 * h + 1];
+        float4 sc;
+        if constexpr (PC) {   // the caller's scale rows need only 4-byte alignment
+          const float* vr = p.vs + (int64_t)hk * D + dim;
+          sc = make_float4(vr[0], vr[1], vr[2], vr[3]);
         } else {
-          dst = p.part + ((int64_t)idx * HS + c) * D + DPL * 4 * G;
-          dm = p.ml + ((int64_t)idx * HS + c) * 2;
-          dl = dm + 1;
+          sc = make_float4(p.vsc, p.vsc, p.vsc, p.vsc);
         }
-#pragma unroll
-        for (int i = 0; i < 4 * DPL; i += 4)
-          *reinterpret_cast<float4*>(dst + i) =
-              make_float4(src[i] * (PC ? vs[i] : p.vsc), src[i + 1] * (PC ? vs[i + 1] : p.vsc),
-                          src[i + 2] * (PC ? vs[i + 2] : p.vsc),
-                          src[i + 3] * (PC ? vs[i + 3] : p.vsc));
-        if (G == 0) {
-          *dm = m;
-          *dl = l;
+        if (!PM && kind == kOut) {
+          const float inv = l > 0.f ? (PC ? 1.f / l : p.vsc / l) : 0.f;
+          if constexpr (PC)
+            store_out4<QT>(p.out, (row0 + h) * D + dim, a.x * sc.x * inv, a.y * sc.y * inv,
+                           a.z * sc.z * inv, a.w * sc.w * inv);
+          else
+            store_out4<QT>(p.out, (row0 + h) * D + dim, a.x * inv, a.y * inv, a.z * inv,
+                           a.w * inv);
+        } else if (PM) {
+          const int64_t prow = (row0 + h) * p.num_parts + idx;
+          *reinterpret_cast<float4*>(p.ws_acc + prow * D + dim) =
+              make_float4(a.x * sc.x, a.y * sc.y, a.z * sc.z, a.w * sc.w);
+          if (dim == 0) {
+            p.ws_m[prow] = m;
+            p.ws_l[prow] = l;
+          }
+        } else {
+          const int64_t prow = (int64_t)idx * HS + h;
+          *reinterpret_cast<float4*>(p.part + prow * D + dim) =
+              make_float4(a.x * sc.x, a.y * sc.y, a.z * sc.z, a.w * sc.w);
+          if (dim == 0) *reinterpret_cast<float2*>(p.ml + prow * 2) = make_float2(m, l);
         }
       }
     }
