@@ -23,11 +23,13 @@ typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 // Loads of cache tiles.  Every K/V byte of a decode step is read once, so
 // the streaming form carries the non-temporal hint and does not displace
 // other lines from the L2 and the Infinity Cache.  Measured on MI355X: random
-// 4 KiB tiles stream at 6.8 TB/s with the hint against 6.1 TB/s without, and
-// the balanced kernel on 16-bit caches gains 7-14%; the fixed-partition
-// kernel and E4M3 caches measure faster with ordinary loads (with the hint
-// the fixed-partition kernel fetches 12% more bytes from HBM), so NT is a
-// choice per call site.
+// 4 KiB tiles stream at 6.8 TB/s with the hint against 6.1 TB/s without; the
+// balanced kernel gains with it on every cache type, and so does the
+// fixed-partition kernel on one-byte caches (E4M3 and INT8, once the loads
+// stay in the loaded vector type, see below).  The fixed-partition kernel on
+// 16-bit caches is faster without it: there sequences that share a prefix
+// re-read its blocks, and the hint evicts them.  NT is a choice per call
+// site.
 template <bool NT>
 __device__ __forceinline__ uint4 ld_tile16(const void* p) {
   if constexpr (NT) {
