@@ -46,6 +46,8 @@
 // ("KV Cache 与 PageAttention深度实战", sections 1.2 and 3.2).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "pkv_stream_common.h"
 #include "pkv_launch.h"
 
@@ -371,21 +373,15 @@ void decode_stream_kernel(StreamParams p) {
     reset();
   };
 
-  // ---- count the share's steps (blocks) and note its first pieces ----
-  int total = 0, npieces = 0;
-  Piece pq[NQ];
+  // ---- setup ----
+  // The first K/V loads wait on the shares, the first piece and its block
+  // ids; everything else (counting the share's pieces and blocks, the q rows
+  // of later pieces) is done while those loads are in flight.
+  Piece first;
   {
     Walk tw = w0;
-    Piece pc;
-    while (walk_next(tw, pc)) {
-#pragma unroll
-      for (int i = 0; i < NQ; ++i)
-        if (npieces == i) pq[i] = pc;
-      ++npieces;
-      total += pc.b1 - pc.b;
-    }
+    if (!walk_next(tw, first)) return;   // a share of restart units only
   }
-  if (total == 0) return;
   reset();
 
   if (p.nb == 0) {
@@ -407,8 +403,6 @@ void decode_stream_kernel(StreamParams p) {
     return;
   }
 
-  // ---- q rows of the first pieces: loaded together, staged in LDS ----
-  const int nq = min(npieces, NQ);
   auto q_row = [&](const Piece& pc) {
     const int hc = pc.y % p.hchunks, hk = pc.y / p.hchunks;
     return (int64_t)pc.s * p.Hq + hk * p.g + hc * p.chunk_heads + c;
@@ -424,13 +418,12 @@ void decode_stream_kernel(StreamParams p) {
     else
       T::load_q(qh, p.q, q_row(pc), q_live(pc), G);
   };
+  // the first piece's q rows go out with its block ids (the scaled form for
+  // per-channel caches computes on them, so it waits until the first K/V
+  // loads are out)
   uint4 qr[KS];
   uint4 qlo[PC ? KS : 1];
-  uint4 qt[NQ][KS];
-  uint4 qtl[NQ][PC ? KS : 1];
-#pragma unroll
-  for (int i = 0; i < NQ; ++i)
-    if (i < nq) load_q_of(pq[i], qt[i], qtl[i]);
+  if constexpr (!PC) load_q_of(first, qr, qlo);
 
   // ---- tile list: the share's steps as cache tile indices ----
   // tile = id * Hkv + hk for a valid block id, -1 for an invalid one (its
@@ -445,8 +438,12 @@ void decode_stream_kernel(StreamParams p) {
   int lo_off = 0;
   uint32_t last_roff = 0;
   int last_hk = 0;
-  auto fill = [&]() {
-    constexpr int NV = kTileCap / 64;
+  // fills CAP steps (the first fill one window, so that the first loads go
+  // out sooner; later ones the whole list); returns how many of the share's
+  // steps it found
+  auto fill = [&](auto cap) -> int {
+    constexpr int CAP = decltype(cap)::value;
+    constexpr int NV = CAP / 64;
     uint32_t roff[NV];
     int hkv[NV];
 #pragma unroll
@@ -455,9 +452,9 @@ void decode_stream_kernel(StreamParams p) {
       hkv[v] = 0;
     }
     int acc = 0;
-    while (lp_ok && acc < kTileCap) {
+    while (lp_ok && acc < CAP) {
       const int L = lp.b1 - lp.b - lo_off;
-      const int take = min(L, kTileCap - acc);
+      const int take = min(L, CAP - acc);
       // step t of this fill (acc <= t < acc + take) is block lp.b + lo_off + t - acc
       const uint32_t base = (uint32_t)lp.s * (uint32_t)p.mb + (uint32_t)(lp.b + lo_off) - (uint32_t)acc;
       const int hkp = lp.y / p.hchunks;
@@ -491,6 +488,7 @@ void decode_stream_kernel(StreamParams p) {
 #pragma unroll
     for (int v = 0; v < NV; ++v)
       tiles[64 * v + lane] = (unsigned)id[v] < (unsigned)p.nb ? id[v] * p.Hkv + hkv[v] : -1;
+    return acc;
   };
   int idw[NW];
   int wk0 = 0, fill_base = 0;
@@ -498,26 +496,12 @@ void decode_stream_kernel(StreamParams p) {
 #pragma unroll
     for (int v = 0; v < NW; ++v) idw[v] = tiles[wk0 - fill_base + 64 * v + lane];
   };
-  fill();
-  int fe = kTileCap;
+  const int filled = fill(std::integral_constant<int, WIN>{});
+  int fe = WIN;
   read_window();
-
-  // stage the q rows (the first piece's go straight to registers)
-#pragma unroll
-  for (int k = 0; k < KS; ++k) {
-    qr[k] = qt[0][k];
-    if constexpr (PC) qlo[k] = qtl[0][k];
-  }
-  uint4* qs = sm_q + w * kQStage;
-#pragma unroll
-  for (int i = 1; i < NQ; ++i)
-    if (i < nq) {
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        qs[(i * KS + k) * 64 + lane] = qt[i][k];
-        if constexpr (PC) qs[((NQ + i) * KS + k) * 64 + lane] = qtl[i][k];
-      }
-    }
+  // The share's step count: known now when the first fill took all of it,
+  // else at least WIN (> DEPTH) and counted below.
+  int total = lp_ok ? INT32_MAX : filled;
 
   // tile of the next step to issue (steps past the end repeat the last)
   int kiss = 0;
@@ -528,7 +512,7 @@ void decode_stream_kernel(StreamParams p) {
       wk0 += WIN;
       if (wk0 == fe) {
         fill_base = fe;
-        fill();
+        fill(std::integral_constant<int, kTileCap>{});
         fe += kTileCap;
       }
       read_window();
@@ -542,16 +526,6 @@ void decode_stream_kernel(StreamParams p) {
     }
     return v;
   };
-
-  // ---- the consumed piece ----
-  Walk cw = w0;
-  Piece cur;
-  walk_next(cw, cur);
-  int pi = 0;          // index of the current piece
-  int cb = cur.b;      // block of the segment consumed next
-  int c_last = ((sm_ctx[cur.s] + 15) >> 4) - 1;
-  int c_tail = sm_ctx[cur.s] - 16 * c_last;
-  int rem = PM ? p.P : 0;   // blocks left in the current partition
 
   const uint32_t koff = T::k_lane_off(c, G), voff = T::v_lane_off(c, G);
   auto issue = [&](Raw& r, int tile) {
@@ -568,6 +542,50 @@ void decode_stream_kernel(StreamParams p) {
     // keep the blocks' loads in consumption order
     __builtin_amdgcn_sched_barrier(0);
   }
+
+  // ---- with the first loads in flight ----
+  if constexpr (PC) load_q_of(first, qr, qlo);
+  // the share's pieces and steps, and the q rows of its first pieces after
+  // the first, staged in LDS
+  int npieces = 0;
+  Piece pq[NQ];
+  {
+    Walk tw = w0;
+    Piece pc;
+    int t = 0;
+    while (walk_next(tw, pc)) {
+#pragma unroll
+      for (int i = 0; i < NQ; ++i)
+        if (npieces == i) pq[i] = pc;
+      ++npieces;
+      t += pc.b1 - pc.b;
+    }
+    total = t;
+  }
+  const int nq = min(npieces, NQ);
+  uint4* qs = sm_q + w * kQStage;
+#pragma unroll
+  for (int i = 1; i < NQ; ++i)
+    if (i < nq) {
+      uint4 qt[KS];
+      uint4 qtl[PC ? KS : 1];
+      load_q_of(pq[i], qt, qtl);
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        qs[(i * KS + k) * 64 + lane] = qt[k];
+        if constexpr (PC) qs[((NQ + i) * KS + k) * 64 + lane] = qtl[k];
+      }
+    }
+
+  // ---- the consumed piece ----
+  Walk cw = w0;
+  Piece cur;
+  walk_next(cw, cur);
+  int pi = 0;          // index of the current piece
+  int cb = cur.b;      // block of the segment consumed next
+  int c_last = ((sm_ctx[cur.s] + 15) >> 4) - 1;
+  int c_tail = sm_ctx[cur.s] - 16 * c_last;
+  int rem = PM ? p.P : 0;   // blocks left in the current partition
 
   // step kc from slot d: consume, then close / switch pieces as due
   int kc = 0;
