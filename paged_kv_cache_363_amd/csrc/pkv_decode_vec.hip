@@ -220,51 +220,80 @@ __global__ __launch_bounds__(64 * kVecWaves) void decode_vec_kernel(DecodeParams
 // Split-K reduction: one workgroup of NW waves per (sequence, q-head)
 // merges the partitions that cover the sequence's context,
 //   M = max_p m_p,  L = sum_p l_p 2^(m_p - M),  out = sum_p acc_p 2^(m_p - M) / L.
-// Wave w merges a contiguous 1/NW of the partitions the same way (lane p
-// holds partition p's weight, and the accumulator rows are read with
-// independent loads, eight at a time); the waves' (M_w, L_w, acc_w) are then
-// combined in LDS by the same rule.  With many partitions one wave per row
-// keeps too few loads in flight (64 partitions take eight dependent rounds);
-// with few, the combine costs more than it saves.
+// Wave w merges a contiguous 1/NW of the row's partitions the same way (lane
+// p holds partition p's weight, and the accumulator rows are read with
+// independent loads); the waves' (M_w, L_w, acc_w) are then combined in LDS
+// by the same rule.  With many partitions one wave per row keeps too few
+// loads in flight (64 partitions take eight dependent rounds); with few, the
+// combine costs more than it saves.
+// A wave's share is fixed by the partition count alone, not by the context,
+// so that its (m, l) values and its first kPrefetch accumulator rows go out
+// together with the context length: the merge of a share of up to kPrefetch
+// partitions waits on memory once.  Partitions past the context hold stale
+// data; they get no weight and their rows are skipped, never multiplied.
 template <int QT, int D, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_reduce_kernel(DecodeParams p) {
   constexpr int PER = (D + 63) / 64;
+  constexpr int kPrefetch = 16;
   __shared__ float sm_m[NW], sm_l[NW];
   __shared__ float sm_acc[NW][D];
   const int row = blockIdx.x;            // s * Hq + h
   const int s = row / p.Hq;
-  const int ctx = clamped_ctx(p, s);
-  const int part_tokens = p.part_blocks * pkv::kBlockSize;
-  int np = (ctx + part_tokens - 1) / part_tokens;
-  np = np < 1 ? 1 : (np > p.num_parts ? p.num_parts : np);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int p0 = np * w / NW, p1 = np * (w + 1) / NW;   // this wave's partitions
+  const int p0 = p.num_parts * w / NW, p1 = p.num_parts * (w + 1) / NW;   // this wave's share
   const float* m = p.ws_m + (int64_t)row * p.num_parts;
   const float* l = p.ws_l + (int64_t)row * p.num_parts;
   const float* a = p.ws_acc + (int64_t)row * p.num_parts * D;
-  float M = kNegInf;
-  for (int i = p0 + lane; i < p1; i += 64) M = fmaxf(M, l[i] > 0.f ? m[i] : kNegInf);
+  const int ctx = clamped_ctx(p, s);
+  float x0[kPrefetch][PER];
+#pragma unroll
+  for (int u = 0; u < kPrefetch; ++u)
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int d = lane + 64 * k;
+      x0[u][k] = (p0 + u < p1 && d < D) ? a[(int64_t)(p0 + u) * D + d] : 0.f;
+    }
+  const int i0 = p0 + lane;
+  const float m0 = i0 < p1 ? m[i0] : kNegInf, l0 = i0 < p1 ? l[i0] : 0.f;
+  const int part_tokens = p.part_blocks * pkv::kBlockSize;
+  int np = (ctx + part_tokens - 1) / part_tokens;
+  np = np < 1 ? 1 : (np > p.num_parts ? p.num_parts : np);
+  const int q1 = min(p1, np);            // this wave's partitions inside the context
+  float M = (i0 < q1 && l0 > 0.f) ? m0 : kNegInf;
+  for (int i = i0 + 64; i < q1; i += 64) M = fmaxf(M, l[i] > 0.f ? m[i] : kNegInf);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
   float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
   float L = 0.f;
+  auto add_row = [&](float wgt, int j, const float* x) {   // lane j of wgt weighs row x
+    const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), j));
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] = fmaf(wj, x[k], acc[k]);
+  };
   if (M != kNegInf) {
-    for (int base = p0; base < p1; base += 64) {
+    for (int base = p0; base < q1; base += 64) {
       const int i = base + lane;
       float wgt = 0.f;
-      if (i < p1) {
-        const float li = l[i];
-        wgt = li > 0.f ? __builtin_amdgcn_exp2f(m[i] - M) : 0.f;
+      if (i < q1) {
+        const float li = base == p0 ? l0 : l[i];
+        const float mi = base == p0 ? m0 : m[i];
+        wgt = li > 0.f ? __builtin_amdgcn_exp2f(mi - M) : 0.f;
         L += wgt * li;
       }
-      const int cnt = min(64, p1 - base);
+      const int cnt = min(64, q1 - base);
+      int j0 = 0;
+      if (base == p0) {
+#pragma unroll
+        for (int u = 0; u < kPrefetch; ++u)
+          if (u < cnt) add_row(wgt, u, x0[u]);
+        j0 = kPrefetch;
+      }
+      // 8 rows per round, loads issued together
       const float* ab = a + (int64_t)base * D;
-      // 8 partitions per round, loads issued together (rows past cnt are
-      // not read: their weight is zero and the load is predicated off)
-      for (int j0 = 0; j0 < cnt; j0 += 8) {
+      for (; j0 < cnt; j0 += 8) {
         float x[8][PER];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -274,13 +303,8 @@ __global__ __launch_bounds__(64 * NW) void decode_reduce_kernel(DecodeParams p) 
             x[u][k] = (j0 + u < cnt && d < D) ? ab[(int64_t)(j0 + u) * D + d] : 0.f;
           }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float wj = __int_as_float(
-              __builtin_amdgcn_readlane(__float_as_int(wgt), min(j0 + u, 63)));
-          const float wu = (j0 + u < cnt) ? wj : 0.f;
-#pragma unroll
-          for (int k = 0; k < PER; ++k) acc[k] = fmaf(wu, x[u][k], acc[k]);
-        }
+        for (int u = 0; u < 8; ++u)
+          if (j0 + u < cnt) add_row(wgt, j0 + u, x[u]);
       }
     }
   }
