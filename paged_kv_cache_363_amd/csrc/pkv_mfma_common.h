@@ -393,56 +393,68 @@ struct MfmaTile {
     } else {
       // Most tiles are seen whole by every column: then the per-token test
       // of the causal limit is skipped (a wave-uniform branch with no load
-      // inside).  The rescale factors' exponentials and the multiplies run
-      // only when some reference moves.
-      float zz[NTL][4];
+      // inside).  Logits are taken against the running references first, one
+      // fma each: while no logit of the wave exceeds its column's reference
+      // by more than PKV_LAZY_RESCALE (the common case once a piece has
+      // started), every reference stays, as the lazy rule above keeps it, and
+      // the wave needs no maximum across lanes, no rescale and no test of an
+      // empty state (a reference of -inf puts any live logit at +inf, and a
+      // column with none live so far gets weights exp2(-inf) = 0).  Otherwise
+      // the references are updated by the lazy rule, acc and l rescaled, and
+      // the logits retaken.
+      float t[NTL][4];
       bool whole = true;
 #pragma unroll
       for (int j = 0; j < NTL; ++j) whole = whole && vis[j] >= 16;
-      if (__all(whole)) {
+      const bool all_whole = __all(whole);
+      auto logits = [&](const float* mr) {
+        if (all_whole) {
 #pragma unroll
-        for (int j = 0; j < NTL; ++j)
+          for (int j = 0; j < NTL; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) zz[j][i] = sacc[j][i] * sl2;
-      } else {
+            for (int i = 0; i < 4; ++i) t[j][i] = __builtin_fmaf(sacc[j][i], sl2, -mr[j]);
+        } else {
 #pragma unroll
-        for (int j = 0; j < NTL; ++j)
+          for (int j = 0; j < NTL; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            zz[j][i] = (4 * G + i < vis[j]) ? sacc[j][i] * sl2 : kNegInf;
-      }
-      float m_old[NTL], m_rf[NTL], psum[NTL];
-      bool resc = false;
+            for (int i = 0; i < 4; ++i)
+              t[j][i] = (4 * G + i < vis[j]) ? __builtin_fmaf(sacc[j][i], sl2, -mr[j]) : kNegInf;
+        }
+      };
+      logits(m_run);
+      float tmax = kNegInf;
 #pragma unroll
-      for (int j = 0; j < NTL; ++j) {
-        const float* z = zz[j];
-        float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-        bm = wave_max4(bm);
-        const float m_new = fmaxf(m_run[j], bm);
-        const bool keep = m_run[j] != kNegInf && m_new <= m_run[j] + PKV_LAZY_RESCALE;
-        const float m_keep = keep ? m_run[j] : m_new;
-        const float m_ref = m_keep == kNegInf ? 0.f : m_keep;
-        resc = resc || !keep;
-        float pr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(z[i] - m_ref);
-        psum[j] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        m_old[j] = m_run[j];
-        m_rf[j] = m_ref;
-        m_run[j] = m_keep;
-        weights(j, pr);
-      }
-      if (__any(resc)) {
+      for (int j = 0; j < NTL; ++j)
+        tmax = fmaxf(tmax, fmaxf(fmaxf(t[j][0], t[j][1]), fmaxf(t[j][2], t[j][3])));
+      if (__any(tmax > PKV_LAZY_RESCALE)) {
+        float m_rf[NTL];
 #pragma unroll
         for (int j = 0; j < NTL; ++j) {
-          const float alpha = __builtin_amdgcn_exp2f(m_old[j] - m_rf[j]);
+          float bm = kNegInf;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (all_whole || 4 * G + i < vis[j]) bm = fmaxf(bm, sacc[j][i] * sl2);
+          bm = wave_max4(bm);
+          const float m_new = fmaxf(m_run[j], bm);
+          const bool keep = m_run[j] != kNegInf && m_new <= m_run[j] + PKV_LAZY_RESCALE;
+          const float m_keep = keep ? m_run[j] : m_new;
+          m_rf[j] = m_keep == kNegInf ? 0.f : m_keep;
+          const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_rf[j]);
           l_run[j] *= alpha;
 #pragma unroll
           for (int e = 0; e < DPL; ++e) o[j * DPL + e] *= alpha;
+          m_run[j] = m_keep;
         }
+        logits(m_rf);
       }
 #pragma unroll
-      for (int j = 0; j < NTL; ++j) l_run[j] += psum[j];
+      for (int j = 0; j < NTL; ++j) {
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(t[j][i]);
+        l_run[j] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        weights(j, pr);
+      }
     }
 
     // A operand of PV for m-tile e: dim DPL*c + e of tokens 4G..4G+3, built
@@ -557,8 +569,11 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
   }
   for (int c0 = b0; c0 < b1; c0 += 64 * NW) {
     const int n = min(64 * NW, b1 - c0);
+    // The step index, the id and the tile's address are wave-uniform: kept
+    // in scalar registers, the loads take the SGPR-base form and none of it
+    // costs vector instructions.
     auto id_at = [&](int i) {
-      const int k = i < n ? i : n - 1;
+      const int k = __builtin_amdgcn_readfirstlane(i < n ? i : n - 1);
       int v = __builtin_amdgcn_readlane(ids[0], k & 63);
 #pragma unroll
       for (int w = 1; w < NW; ++w) {

@@ -103,24 +103,30 @@ void multiquery_mfma_kernel(MQParams p) {
   // groups, group x of a run taking the indices congruent to x mod nx.
   // (Any order computes the same result; this one lets one XCD's L2 serve
   // a group's repeated reads.)
+  // (The integer divisions below expand to vector code; their uniform
+  // results are moved to scalar registers, so that the block loop's
+  // addresses are scalar arithmetic.)
   const int64_t run = (int64_t)p.nx * p.qtiles;
   const int64_t g0 = blockIdx.x / run;
   const int rr = (int)(blockIdx.x - g0 * run);
-  const int qt = rr / p.nx;
+  const int qt = __builtin_amdgcn_readfirstlane(rr / p.nx);
   const int64_t grp = g0 * p.nx + rr % p.nx;
   if (grp >= p.groups) return;
-  const int part = (int)(grp % p.num_parts);
+  const int part = __builtin_amdgcn_readfirstlane((int)(grp % p.num_parts));
   int64_t yy64 = grp / p.num_parts;
   const int Yg = p.Hkv * p.hchunks;
-  const int s = (int)(yy64 / Yg);
+  const int s = __builtin_amdgcn_readfirstlane((int)(yy64 / Yg));
   const int yy = (int)(yy64 % Yg);
-  const int hc = yy % p.hchunks, hk = yy / p.hchunks;
+  const int hc = __builtin_amdgcn_readfirstlane(yy % p.hchunks);
+  const int hk = __builtin_amdgcn_readfirstlane(yy / p.hchunks);
   int r0, n;
   seq_rows(p, s, r0, n);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  n = __builtin_amdgcn_readfirstlane(n);
   const int i0 = qt * p.rpt;
   if (i0 >= n) return;   // no row of this sequence in the tile
   const int cap = p.mb * pkv::kBlockSize;
-  const int ctx = min(max(p.cl[s], 0), cap);
+  const int ctx = __builtin_amdgcn_readfirstlane(min(max(p.cl[s], 0), cap));
 
   // this lane's column in column tile j: row i0 + j qpt + c / chunk, q-head
   // hk*g + hc*chunk + c % chunk
@@ -164,7 +170,12 @@ void multiquery_mfma_kernel(MQParams p) {
   }
 
   // One column tile at a time through LDS: lane (G, c) holds O[column c][dim
-  // DPL*(4G+i) + e]; l needs the 4 G lanes.
+  // DPL*(4G+i) + e]; l needs the 4 G lanes.  The merge gives each thread one
+  // column and DPT consecutive dims: the column's factors and 1 / L are taken
+  // once, and its outputs leave in one store.
+  constexpr int DPT = D / 16;
+  static_assert(kCols * 16 == 64 * pkv::kWaves, "one thread per (column, run of dims)");
+  const int mc = threadIdx.x >> 4, md0 = (threadIdx.x & 15) * DPT;
 #pragma unroll
   for (int j = 0; j < NTL; ++j) {
     const float lj = wave_sum4(l_run[j]);
@@ -182,30 +193,43 @@ void multiquery_mfma_kernel(MQParams p) {
     }
     __syncthreads();
 
-    for (int idx = threadIdx.x; idx < kCols * D; idx += 64 * pkv::kWaves) {
-      const int cc = idx / D, d = idx % D;
-      const int ic = i0 + j * p.qpt + cc / p.chunk, hh = hc * p.chunk + cc % p.chunk;
-      if (cc >= p.qpt * p.chunk || ic >= n || hh >= p.g) continue;
+    const int ic = i0 + j * p.qpt + mc / p.chunk, hh = hc * p.chunk + mc % p.chunk;
+    if (mc < p.qpt * p.chunk && ic < n && hh < p.g) {
       float M = kNegInf;
 #pragma unroll
-      for (int v = 0; v < pkv::kWaves; ++v) M = fmaxf(M, sm_m[v * kCols + cc]);
-      float L = 0.f, acc = 0.f;
-      if (M != kNegInf) {
+      for (int v = 0; v < pkv::kWaves; ++v) M = fmaxf(M, sm_m[v * kCols + mc]);
+      float L = 0.f, acc[DPT];
 #pragma unroll
-        for (int v = 0; v < pkv::kWaves; ++v) {
-          const float mv = sm_m[v * kCols + cc];
-          const float f = (mv == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-          L += f * sm_l[v * kCols + cc];
-          acc += f * sm_o[(v * kCols + cc) * LD + d];
+      for (int k = 0; k < DPT; ++k) acc[k] = 0.f;
+#pragma unroll
+      for (int v = 0; v < pkv::kWaves; ++v) {
+        const float mv = sm_m[v * kCols + mc];
+        const float f = (mv == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+        L += f * sm_l[v * kCols + mc];
+        const float4* src = reinterpret_cast<const float4*>(sm_o + (v * kCols + mc) * LD + md0);
+#pragma unroll
+        for (int k4 = 0; k4 < DPT / 4; ++k4) {
+          const float4 x = src[k4];
+          acc[4 * k4] += f * x.x;
+          acc[4 * k4 + 1] += f * x.y;
+          acc[4 * k4 + 2] += f * x.z;
+          acc[4 * k4 + 3] += f * x.w;
         }
       }
       const int64_t row = (int64_t)(r0 + ic) * p.Hq + hk * p.g + hh;
       if (p.num_parts == 1) {
-        store_out<QT>(p.out, row * D + d, L > 0.f ? acc * p.vsc / L : 0.f);
+        const float inv = L > 0.f ? p.vsc / L : 0.f;
+#pragma unroll
+        for (int k = 0; k < DPT; ++k) acc[k] *= inv;
+        store_out_n<QT, DPT>(p.out, row * D + md0, acc);
       } else {
         const int64_t pr = row * p.num_parts + part;
-        p.ws_acc[pr * D + d] = acc * p.vsc;
-        if (d == 0) {
+        float4* dst = reinterpret_cast<float4*>(p.ws_acc + pr * D + md0);
+#pragma unroll
+        for (int k4 = 0; k4 < DPT / 4; ++k4)
+          dst[k4] = make_float4(acc[4 * k4] * p.vsc, acc[4 * k4 + 1] * p.vsc,
+                                acc[4 * k4 + 2] * p.vsc, acc[4 * k4 + 3] * p.vsc);
+        if (md0 == 0) {
           p.ws_m[pr] = M;
           p.ws_l[pr] = L;
         }
@@ -214,8 +238,7 @@ void multiquery_mfma_kernel(MQParams p) {
   }
 }
 
-// One wave per (row, q-head) of the rows some sequence owns: the log-sum-exp
-// merge of the row's partitions, every one of which the kernel above wrote.
+
 template <int QT, int D>
 __global__ __launch_bounds__(64) void multiquery_reduce_kernel(MQParams p) {
   const int64_t rh = blockIdx.x;   // row * Hq + head
