@@ -256,15 +256,16 @@ bool mq_plan(int32_t num_rows, int32_t num_seqs, int32_t max_query_len, int32_t 
       return true;
     }
   }
-  // Fixed grid: two column tiles per wave.  Against one, each K/V load
-  // serves twice the columns; against four, the accumulators of two tiles
-  // fit the vector registers of two waves per SIMD, which overlap each
-  // other's softmax and matrix work.  Measured on the fixed grid (all with
-  // the accumulators in vector registers): 8-row verification on the
-  // 70B-shaped E4M3 cache 78.0 / 55.5 / 63.8 us with 1 / 2 / 4 tiles, 64-row
-  // MHA chunks 728 / 504 / 717 us, 512-row chunks at 32K tokens 18.1 / 10.0 /
-  // 10.6 ms.
-  plan->max_ntl = 2;
+  // Fixed grid: four column tiles per wave.  Each K/V load and its widening
+  // serve four times the columns of one tile, and a (sequence, kv-head) is
+  // read once instead of once per pair of tiles.  Four tiles' accumulators
+  // leave one wave per SIMD; since the tile update takes its logits against
+  // the running references (no cross-lane maximum per block), that wave
+  // keeps the matrix cores busier than two waves of two tiles.  Measured on
+  // the fixed grid with 2 / 4 tiles: 8-row verification on the 70B-shaped
+  // E4M3 cache 47.2 / 43.2 us, on its INT8 cache 48.4 / 46.4 us, 512-row
+  // chunks at 32K tokens 9.19 / 7.86 ms, 64-row MHA chunks 401 / 404 us.
+  plan->max_ntl = 4;
 #ifdef PKV_MQ_FORCE_NTL
   plan->max_ntl = PKV_MQ_FORCE_NTL;
 #endif

@@ -592,9 +592,8 @@ void decode_stream_kernel(StreamParams p) {
   auto consume_step = [&](int d) {
     const bool live = kc < total;
     const int valid = live && idc[d] >= 0 ? (cb == c_last ? c_tail : 16) : 0;
-    const int vis[1] = {valid};
-    T::template consume<1, PC, false>(buf[d], valid, vis, qr, p.sl2, &m_run, &l_run, o, c, G,
-                                      qlo);
+    T::template consume<1, PC, false>(buf[d], valid, valid == 16, nullptr, 0, qr, p.sl2, &m_run,
+                                      &l_run, o, c, G, qlo);
     if (live) {
       ++cb;
       if constexpr (PM) {

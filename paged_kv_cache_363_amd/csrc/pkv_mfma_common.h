@@ -41,6 +41,11 @@ __device__ __forceinline__ float wave_max4(float x) {
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) x = min(x, __shfl_xor(x, k));
+  return x;
+}
 __device__ __forceinline__ float wave_sum4(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
@@ -274,17 +279,21 @@ struct MfmaTile {
   // Online-softmax update of NTL column tiles with one K/V tile holding
   // `valid` live tokens (0 = none: the state does not change, and the tile's
   // registers are still read, so the caller need not branch around it).
-  // Column tile j has its own q operand qr[j][KSTEPS], state m_run[j],
-  // l_run[j], o[j][DPL] and causal limit vis[j] <= valid: tokens of the tile
-  // this lane's column may attend to (valid for a single query).  K and V are
-  // widened once and serve every column tile.  V rows past `valid` are
-  // zeroed; rows in [vis, valid) are finite and get weight zero.
+  // Column tile j has its own q operand qr[j][KSTEPS] and state m_run[j],
+  // l_run[j], o[j][DPL].  CAUSAL: the lane's column of tile j sits at
+  // position pos[j] and attends to min(valid, pos[j] - tok0 + 1) tokens of
+  // the tile, whose first token is at position tok0; otherwise to `valid`.
+  // whole (wave-uniform): every column of the wave attends to all 16 tokens,
+  // so the per-token limits need not be taken (the multi-query form).  K and
+  // V are widened once and serve every column tile.  V rows past `valid` are
+  // zeroed; rows below `valid` past a column's limit are finite and get
+  // weight zero.
   // PC (one column tile only): qlo holds the remainder of per-channel-scaled
   // q (load_q_scaled), a second QK pass.
   template <int NTL = 1, bool PC = false, bool CAUSAL = false>
-  __device__ static void consume(Raw& r, int valid, const int* vis, const uint4* qr, float sl2,
-                                 float* m_run, float* l_run, f32x4* o, int c, int G,
-                                 const uint4* qlo = nullptr) {
+  __device__ static void consume(Raw& r, int valid, bool whole, const int* pos, int tok0,
+                                 const uint4* qr, float sl2, float* m_run, float* l_run,
+                                 f32x4* o, int c, int G, const uint4* qlo = nullptr) {
     static_assert(!PC || NTL == 1, "per-channel scales take one column tile");
     V8 kop[KSTEPS];
     if constexpr (BYTE) {
@@ -330,6 +339,10 @@ struct MfmaTile {
 
     P4 pb[NTL];            // PV weights of each column tile
     [[maybe_unused]] V4 pl[NTL];   // their bf16 remainders (bf16 caches)
+    // Multi-query form on bf16 caches: head and remainder side by side, the
+    // B operand of one 16x16x32 MFMA (see the PV step below)
+    constexpr bool PV32 = MQ && !PVH;
+    [[maybe_unused]] uint4 phl[PV32 ? NTL : 1];
     // S = K Q^T of every column tile first (independent MFMA chains, one
     // basic block): lane (G, c) gets tokens 4G+i, column c.
     f32x4 sacc[NTL];
@@ -346,6 +359,14 @@ struct MfmaTile {
     }
     // the PV B operand of column tile j from its weights
     auto weights = [&](int j, const float* pr) {
+      if constexpr (PV32) {
+        float lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo[i] = pr[i] - M::rounded(pr[i]);
+        phl[j] = make_uint4(M::pack2(pr[0], pr[1]), M::pack2(pr[2], pr[3]),
+                            M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]));
+        return;
+      }
       // k-slot (G, i) = token 4G+i, column c
       if constexpr (MQ)
         pb[j] = as_v4<P4>(PM::pack2_one(pr[0], pr[1]), PM::pack2_one(pr[2], pr[3]));
@@ -372,7 +393,7 @@ struct MfmaTile {
     if constexpr (!MQ) {
       float z[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = (4 * G + i < vis[0]) ? sacc[0][i] * sl2 : kNegInf;
+      for (int i = 0; i < 4; ++i) z[i] = (4 * G + i < valid) ? sacc[0][i] * sl2 : kNegInf;
       float bm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
       bm = wave_max4(bm);
       const float m_new = fmaxf(m_run[0], bm);
@@ -403,22 +424,20 @@ struct MfmaTile {
       // the references are updated by the lazy rule, acc and l rescaled, and
       // the logits retaken.
       float t[NTL][4];
-      bool whole = true;
-#pragma unroll
-      for (int j = 0; j < NTL; ++j) whole = whole && vis[j] >= 16;
-      const bool all_whole = __all(whole);
+      auto lim = [&](int j) { return CAUSAL ? min(valid, pos[j] - tok0 + 1) : valid; };
       auto logits = [&](const float* mr) {
-        if (all_whole) {
 #pragma unroll
-          for (int j = 0; j < NTL; ++j)
+        for (int j = 0; j < NTL; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) t[j][i] = __builtin_fmaf(sacc[j][i], sl2, -mr[j]);
-        } else {
+          for (int i = 0; i < 4; ++i) t[j][i] = __builtin_fmaf(sacc[j][i], sl2, -mr[j]);
+        if (!whole) {
 #pragma unroll
-          for (int j = 0; j < NTL; ++j)
+          for (int j = 0; j < NTL; ++j) {
+            const int v = lim(j);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              t[j][i] = (4 * G + i < vis[j]) ? __builtin_fmaf(sacc[j][i], sl2, -mr[j]) : kNegInf;
+              if (4 * G + i >= v) t[j][i] = kNegInf;
+          }
         }
       };
       logits(m_run);
@@ -431,9 +450,10 @@ struct MfmaTile {
 #pragma unroll
         for (int j = 0; j < NTL; ++j) {
           float bm = kNegInf;
+          const int v = whole ? 16 : lim(j);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (all_whole || 4 * G + i < vis[j]) bm = fmaxf(bm, sacc[j][i] * sl2);
+            if (4 * G + i < v) bm = fmaxf(bm, sacc[j][i] * sl2);
           bm = wave_max4(bm);
           const float m_new = fmaxf(m_run[j], bm);
           const bool keep = m_run[j] != kNegInf && m_new <= m_run[j] + PKV_LAZY_RESCALE;
@@ -482,6 +502,17 @@ struct MfmaTile {
         const uint32_t x01 = __builtin_amdgcn_perm(r.v[1].w[wi], r.v[0].w[wi], sel);
         const uint32_t x23 = __builtin_amdgcn_perm(r.v[3].w[wi], r.v[2].w[wi], sel);
         const P4 a0 = as_v4<P4>(x01, x23);
+        if constexpr (PV32) {
+          // o += V (w_hi + w_lo) as one MFMA with k = 32: k-slots 8G..8G+3
+          // hold tokens 4G..4G+3 against the weights' heads, 8G+4..8G+7 the
+          // same tokens against their remainders; the A operand carries the
+          // V values twice.  One full-rate 16x16x32 instead of two half-rate
+          // 16x16x16.
+          const V8 a2 = as_v8<V8>(make_uint4(x01, x23, x01, x23));
+#pragma unroll
+          for (int j = 0; j < NTL; ++j) o[j * DPL + e] = M::qk(a2, as_v8<V8>(phl[j]), o[j * DPL + e]);
+          continue;
+        }
 #pragma unroll
         for (int j = 0; j < NTL; ++j) {
           if constexpr (PVH)
@@ -560,6 +591,15 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
 #pragma unroll
     for (int w = 0; w < NW; ++w) ids[w] = row[(int64_t)(c0 + min(64 * w + lane, n - 1)) * stride];
   };
+  // CAUSAL: steps before whole_end are seen whole by every column (block b
+  // is whole for a column at position q when 16 b + 15 <= q)
+  int whole_end = 0;
+  if constexpr (CAUSAL) {
+    int pm = pos[0];
+#pragma unroll
+    for (int j = 1; j < NTL; ++j) pm = min(pm, pos[j]);
+    whole_end = __builtin_amdgcn_readfirstlane((wave_min(pm) + 1) >> 4);
+  }
   int ids[NW];
   if (ids_first) {
 #pragma unroll
@@ -602,12 +642,9 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
         const int idn = id_at(ii + DEPTH);
         const int valid = (ii < n && (unsigned)idc[d] < (unsigned)nb)
                               ? (c0 + ii == last ? tail : 16) : 0;
-        int vis[NTL];
-#pragma unroll
-        for (int j = 0; j < NTL; ++j)
-          vis[j] = CAUSAL ? min(valid, pos[j] - 16 * (c0 + ii) + 1) : valid;
-        T::template consume<NTL, PC, CAUSAL>(buf[d], valid, vis, qr, sl2, m_run, l_run, o, c, G,
-                                             qlo);
+        const bool whole = valid == 16 && (!CAUSAL || c0 + ii < whole_end);
+        T::template consume<NTL, PC, CAUSAL>(buf[d], valid, whole, pos, 16 * (c0 + ii), qr, sl2,
+                                             m_run, l_run, o, c, G, qlo);
         if constexpr (Hook::active) {
           if (ii < n && (--rem == 0 || c0 + ii == b1 - 1)) {
             hook();

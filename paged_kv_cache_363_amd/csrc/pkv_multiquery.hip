@@ -41,6 +41,7 @@ namespace {
 using namespace pkvd;
 
 constexpr int kCols = 16;   // MFMA tile columns
+constexpr int kSeesAll = 1 << 30;   // causal position of a column that is not stored
 
 struct MQParams {
   void* out;
@@ -137,7 +138,10 @@ void multiquery_mfma_kernel(MQParams p) {
   uint4 qr[NTL * KS];
 #pragma unroll
   for (int j = 0; j < NTL; ++j) {
-    pos[j] = live_of(j) ? ctx - n + row_of(j) : -1;   // < 0: the column attends to nothing
+    // < 0: the column attends to nothing.  A column that is not stored
+    // (q zero) is taken to see every token, so that it never asks for the
+    // per-token causal limits.
+    pos[j] = live_of(j) ? ctx - n + row_of(j) : kSeesAll;
     T::load_q(qr + j * KS, p.q, (int64_t)(r0 + row_of(j)) * p.Hq + hk * p.g + h, live_of(j), G);
   }
   // blocks any row of the tile can see: up to its last row's position
@@ -500,7 +504,8 @@ void multiquery_stream_kernel(MQStreamParams sp) {
       auto live = [&](int k) { return c < p.qpt * p.chunk && iq(k) < n && h < p.g; };
 #pragma unroll
       for (int k = 0; k < NTL; ++k) {
-        pos[k] = live(k) ? ctx - n + iq(k) : -1;   // < 0: the column attends to nothing
+        // < 0: the column attends to nothing; one not stored sees every token
+        pos[k] = live(k) ? ctx - n + iq(k) : kSeesAll;
         T::load_q(qr + k * KS, p.q, (int64_t)(r0 + iq(k)) * p.Hq + hk * p.g + h, live(k), G);
         m_run[k] = kNegInf;
         l_run[k] = 0.f;
