@@ -280,7 +280,11 @@ struct MfmaTile {
   // `valid` live tokens (0 = none: the state does not change, and the tile's
   // registers are still read, so the caller need not branch around it).
   // Column tile j has its own q operand qr[j][KSTEPS] and state m_run[j],
-  // l_run[j], o[j][DPL].  CAUSAL: the lane's column of tile j sits at
+  // l_run[j], o[j][DPL].  In the multi-query form (NTL > 1 or CAUSAL) l_run
+  // holds one f32x4 per column tile (4 NTL floats, 16-byte aligned), which
+  // accumulates on the matrix cores: every element is the column's whole
+  // sum of weights.  Otherwise l_run[j] is this lane's share of it (tokens
+  // 4G..4G+3), summed over the lanes of a column by the caller.  CAUSAL: the lane's column of tile j sits at
   // position pos[j] and attends to min(valid, pos[j] - tok0 + 1) tokens of
   // the tile, whose first token is at position tok0; otherwise to `valid`.
   // whole (wave-uniform): every column of the wave attends to all 16 tokens,
@@ -460,7 +464,7 @@ struct MfmaTile {
           const float m_keep = keep ? m_run[j] : m_new;
           m_rf[j] = m_keep == kNegInf ? 0.f : m_keep;
           const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_rf[j]);
-          l_run[j] *= alpha;
+          reinterpret_cast<f32x4*>(l_run)[j] *= alpha;
 #pragma unroll
           for (int e = 0; e < DPL; ++e) o[j * DPL + e] *= alpha;
           m_run[j] = m_keep;
@@ -472,7 +476,6 @@ struct MfmaTile {
         float pr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(t[j][i]);
-        l_run[j] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         weights(j, pr);
       }
     }
@@ -520,6 +523,22 @@ struct MfmaTile {
           else
             o[j * DPL + e] = M::pv(a0, pl[j], M::pv(a0, pb[j], o[j * DPL + e]));
         }
+      }
+    }
+    // Multi-query form: l += the weights of the tile's 16 tokens, as one
+    // MFMA against an all-ones A operand (the same weights as PV, so l and
+    // acc sum identical terms; no VALU adds)
+    if constexpr (MQ) {
+      f32x4* la = reinterpret_cast<f32x4*>(l_run);
+      if constexpr (PV32) {
+        const V8 ones = as_v8<V8>(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) la[j] = M::qk(ones, as_v8<V8>(phl[j]), la[j]);
+      } else {
+        static_assert(PVH, "the multi-query form takes f16 weights or bf16 head/remainder pairs");
+        const P4 ones = as_v4<P4>(0x3C003C00u, 0x3C003C00u);   // f16 1.0
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) la[j] = PM::pv(ones, pb[j], la[j]);
       }
     }
   }

@@ -154,11 +154,13 @@ void multiquery_mfma_kernel(MQParams p) {
   f32x4 o[NTL * DPL];
 #pragma unroll
   for (int e = 0; e < NTL * DPL; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[NTL], l_run[NTL];
+  // l of column tile j: every element of l_acc[j] holds the column's sum
+  float m_run[NTL];
+  f32x4 l_acc[NTL];
 #pragma unroll
   for (int j = 0; j < NTL; ++j) {
     m_run[j] = kNegInf;
-    l_run[j] = 0.f;
+    l_acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   const int w0 = b_begin + (nblk_p * w) / pkv::kWaves;
@@ -170,7 +172,8 @@ void multiquery_mfma_kernel(MQParams p) {
     mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH, false,
                true, false, NTL>(p.kc + head_off, p.vc + head_off, blk_stride,
                                  p.bt + (int64_t)s * p.mb, w0, w1, last, ctx - 16 * last, p.nb,
-                                 qr, p.sl2, m_run, l_run, o, lane, pos);
+                                 qr, p.sl2, m_run, reinterpret_cast<float*>(l_acc), o, lane,
+                                 pos);
   }
 
   // One column tile at a time through LDS: lane (G, c) holds O[column c][dim
@@ -182,7 +185,7 @@ void multiquery_mfma_kernel(MQParams p) {
   const int mc = threadIdx.x >> 4, md0 = (threadIdx.x & 15) * DPT;
 #pragma unroll
   for (int j = 0; j < NTL; ++j) {
-    const float lj = wave_sum4(l_run[j]);
+    const float lj = l_acc[j][0];
     if (j > 0) __syncthreads();   // the previous tile's reads are done
     if (G == 0) {
       sm_m[w * kCols + c] = m_run[j];
@@ -479,7 +482,8 @@ void multiquery_stream_kernel(MQStreamParams sp) {
   const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
   uint4 qr[NTL * KS];
   f32x4 o[NTL * DPL];
-  float m_run[NTL], l_run[NTL];
+  float m_run[NTL];
+  f32x4 l_acc[NTL];   // every element: the column's sum of weights
   int pos[NTL];
 
   int64_t u = u_lo;
@@ -508,7 +512,7 @@ void multiquery_stream_kernel(MQStreamParams sp) {
         pos[k] = live(k) ? ctx - n + iq(k) : kSeesAll;
         T::load_q(qr + k * KS, p.q, (int64_t)(r0 + iq(k)) * p.Hq + hk * p.g + h, live(k), G);
         m_run[k] = kNegInf;
-        l_run[k] = 0.f;
+        l_acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int e = 0; e < NTL * DPL; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -518,14 +522,15 @@ void multiquery_stream_kernel(MQStreamParams sp) {
         mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
                    !pkv::byte_codes(KVT), true, false, NTL>(
             p.kc + off, p.vc + off, blk_stride, p.bt + (int64_t)s * p.mb, b, b1, last,
-            ctx - 16 * last, p.nb, qr, p.sl2, m_run, l_run, o, lane, pos);
+            ctx - 16 * last, p.nb, qr, p.sl2, m_run, reinterpret_cast<float*>(l_acc), o, lane,
+            pos);
       }
       // close the piece: store the rows, or leave (m, l, acc) for the merge
       const bool whole = b == 0 && b1 == len - sp.R;
       const int64_t slot = 2 * (int64_t)wk + (first_piece ? 0 : 1);
 #pragma unroll
       for (int k = 0; k < NTL; ++k) {
-        const float l_tot = wave_sum4(l_run[k]);
+        const float l_tot = l_acc[k][0];
         if (!live(k)) continue;
         if (whole) {
           const int64_t row = ((int64_t)(r0 + iq(k)) * p.Hq + hk * p.g + h) * D + DPL * 4 * G;
