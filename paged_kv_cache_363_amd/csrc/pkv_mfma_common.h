@@ -364,11 +364,13 @@ struct MfmaTile {
     // the PV B operand of column tile j from its weights
     auto weights = [&](int j, const float* pr) {
       if constexpr (PV32) {
-        float lo[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lo[i] = pr[i] - M::rounded(pr[i]);
-        phl[j] = make_uint4(M::pack2(pr[0], pr[1]), M::pack2(pr[2], pr[3]),
-                            M::pack2(lo[0], lo[1]), M::pack2(lo[2], lo[3]));
+        // the heads' values read back from their packed bf16 words
+        const uint32_t h01 = M::pack2(pr[0], pr[1]), h23 = M::pack2(pr[2], pr[3]);
+        const float lo0 = pr[0] - __uint_as_float(h01 << 16);
+        const float lo1 = pr[1] - __uint_as_float(h01 & 0xFFFF0000u);
+        const float lo2 = pr[2] - __uint_as_float(h23 << 16);
+        const float lo3 = pr[3] - __uint_as_float(h23 & 0xFFFF0000u);
+        phl[j] = make_uint4(h01, h23, M::pack2(lo0, lo1), M::pack2(lo2, lo3));
         return;
       }
       // k-slot (G, i) = token 4G+i, column c
