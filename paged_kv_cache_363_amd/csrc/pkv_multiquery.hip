@@ -532,21 +532,27 @@ void multiquery_stream_kernel(MQStreamParams sp) {
       for (int k = 0; k < NTL; ++k) {
         const float l_tot = l_acc[k][0];
         if (!live(k)) continue;
+        // each lane's DPL consecutive dims of a row leave in one store
         if (whole) {
           const int64_t row = ((int64_t)(r0 + iq(k)) * p.Hq + hk * p.g + h) * D + DPL * 4 * G;
           const float inv = l_tot > 0.f ? p.vsc / l_tot : 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            float vals[DPL];
 #pragma unroll
-            for (int e = 0; e < DPL; ++e)
-              store_out<QT>(p.out, row + DPL * i + e, o[k * DPL + e][i] * inv);
+            for (int e = 0; e < DPL; ++e) vals[e] = o[k * DPL + e][i] * inv;
+            store_out_n<QT, DPL>(p.out, row + DPL * i, vals);
+          }
         } else {
           const int64_t col = slot * NC + k * kCols + c;
-          float* dst = sp.part + col * D + DPL * 4 * G;
+          float4* dst = reinterpret_cast<float4*>(sp.part + col * D + DPL * 4 * G);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) dst[DPL * i + e] = o[k * DPL + e][i] * p.vsc;
+            for (int e = 0; e < DPL; e += 4)
+              dst[(DPL * i + e) / 4] =
+                  make_float4(o[k * DPL + e][i] * p.vsc, o[k * DPL + e + 1][i] * p.vsc,
+                              o[k * DPL + e + 2][i] * p.vsc, o[k * DPL + e + 3][i] * p.vsc);
           if (G == 0) {
             sp.ml[col * 2] = m_run[k];
             sp.ml[col * 2 + 1] = l_tot;
@@ -668,12 +674,9 @@ __global__ __launch_bounds__(64 * pkv::kWaves) void multiquery_split_merge_kerne
         const int64_t row = ((int64_t)(sm.r0[s] + iq) * p.Hq + hk * p.g + h) * D + d0;
         const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-          store_out<QT>(p.out, row + 4 * i, acc[i].x * inv);
-          store_out<QT>(p.out, row + 4 * i + 1, acc[i].y * inv);
-          store_out<QT>(p.out, row + 4 * i + 2, acc[i].z * inv);
-          store_out<QT>(p.out, row + 4 * i + 3, acc[i].w * inv);
-        }
+        for (int i = 0; i < NV; ++i)
+          store_out4<QT>(p.out, row + 4 * i, acc[i].x * inv, acc[i].y * inv, acc[i].z * inv,
+                         acc[i].w * inv);
       }
     }
   }
