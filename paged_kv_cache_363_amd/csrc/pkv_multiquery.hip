@@ -486,6 +486,57 @@ void multiquery_stream_kernel(MQStreamParams sp) {
   f32x4 l_acc[NTL];   // every element: the column's sum of weights
   int pos[NTL];
 
+  // The piece after the one ending at unit u0 in segment (t0, y0): the next
+  // segment of the share that holds blocks (a segment's first R units are
+  // restart units).  False if the share has none.
+  auto next_piece = [&](int t0, int y0, int64_t u0, int& t1, int& y1, int& b1n) -> bool {
+    int tt = t0, yy = y0;
+    int64_t uu = u0;
+    while (uu < u_hi) {
+      if (++yy == Y) {
+        yy = 0;
+        do {
+          ++tt;
+        } while (sm.pref[tt + 1] == sm.pref[tt]);
+      }
+      const int ln = sm.pref[tt + 1] - sm.pref[tt];
+      const int64_t st = Y * sm.pref[tt] + (int64_t)yy * ln;
+      const int64_t en = st + ln < u_hi ? st + ln : u_hi;
+      const int bb1 = max((int)(en - st) - sp.R, 0);
+      if (bb1 > 0) {
+        t1 = tt;
+        y1 = yy;
+        b1n = bb1;
+        return true;
+      }
+      uu = en;
+    }
+    return false;
+  };
+  // q rows of the piece's column tiles, and the first window of its block
+  // ids (steps b0.., as mfma_piece reads them), for segment (tt, yy)
+  constexpr int NW = PKV_ID_VGPRS;
+  auto piece_loads = [&](int tt, int yy, int b0, int b1p, uint4* qd, int* idd) {
+    const int ss = sm.tseq[tt];
+    const int hc = yy % p.hchunks, hk = yy / p.hchunks;
+    const int n = sm.n[ss], r0 = sm.r0[ss];
+    const int h = hc * p.chunk + c % p.chunk;
+    const int i0 = (tt - sm.tb[ss]) * p.rpt + c / p.chunk;
+#pragma unroll
+    for (int k = 0; k < NTL; ++k) {
+      const int iqk = i0 + k * p.qpt;
+      const bool lv = c < p.qpt * p.chunk && iqk < n && h < p.g;
+      T::load_q(qd + k * KS, p.q, (int64_t)(r0 + iqk) * p.Hq + hk * p.g + h, lv, G);
+    }
+    const int32_t* row = p.bt + (int64_t)ss * p.mb;
+    const int nn = min(64 * NW, b1p - b0);
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) idd[w2] = row[b0 + min(64 * w2 + lane, nn - 1)];
+  };
+  uint4 qn[NTL * KS];   // the next piece's, loaded while this one streams
+  int idc0[NW], idn[NW];
+  bool have_next = false;
+
   int64_t u = u_lo;
   int t, y, j;
   locate(u, t, y, j);
@@ -506,11 +557,24 @@ void multiquery_stream_kernel(MQStreamParams sp) {
       const int i0 = (t - sm.tb[s]) * p.rpt + c / p.chunk;
       auto iq = [&](int k) { return i0 + k * p.qpt; };
       auto live = [&](int k) { return c < p.qpt * p.chunk && iq(k) < n && h < p.g; };
+      // this piece's q and first ids: loaded ahead by the previous piece
+      // (which started at step 0 of this segment), else now
+      if (have_next) {
+#pragma unroll
+        for (int k = 0; k < NTL * KS; ++k) qr[k] = qn[k];
+#pragma unroll
+        for (int w2 = 0; w2 < NW; ++w2) idc0[w2] = idn[w2];
+      } else {
+        piece_loads(t, y, b, b1, qr, idc0);
+      }
+      // the next piece's loads go out before this piece's blocks
+      int tn = t, yn = y, b1n = 0;
+      have_next = p.nb > 0 && next_piece(t, y, pe, tn, yn, b1n);
+      if (have_next) piece_loads(tn, yn, 0, b1n, qn, idn);
 #pragma unroll
       for (int k = 0; k < NTL; ++k) {
         // < 0: the column attends to nothing; one not stored sees every token
         pos[k] = live(k) ? ctx - n + iq(k) : kSeesAll;
-        T::load_q(qr + k * KS, p.q, (int64_t)(r0 + iq(k)) * p.Hq + hk * p.g + h, live(k), G);
         m_run[k] = kNegInf;
         l_acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -523,7 +587,7 @@ void multiquery_stream_kernel(MQStreamParams sp) {
                    !pkv::byte_codes(KVT), true, false, NTL>(
             p.kc + off, p.vc + off, blk_stride, p.bt + (int64_t)s * p.mb, b, b1, last,
             ctx - 16 * last, p.nb, qr, p.sl2, m_run, reinterpret_cast<float*>(l_acc), o, lane,
-            pos);
+            pos, nullptr, NoHook{}, 1, idc0);
       }
       // close the piece: store the rows, or leave (m, l, acc) for the merge
       const bool whole = b == 0 && b1 == len - sp.R;
