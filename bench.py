@@ -4,7 +4,10 @@
 A step is one pass of the whole decode hot path over one batch: the cache
 append of every sequence's new token (slot_mapping write) followed by paged
 decode attention over each sequence's context (the decode kernel, plus the
-merge or reduction kernel when contexts are split).  The block tables,
+merge or reduction kernel when contexts are split), issued as one call
+(pkv_paged_decode_attention_appending: on the fixed-partition kernel the
+decode kernel writes the new rows itself; elsewhere the append kernel runs
+first).  The block tables,
 context lengths and slot mapping come from the native block pool, built
 before the timed region (its host cost per step is measured separately).
 
@@ -52,6 +55,11 @@ def parse():
                     help="comma-separated workloads timed after the headline and reported "
                          "under 'configs' ('' for none)")
     ap.add_argument("--algo", default="auto", choices=["auto", "vector", "mfma"])
+    ap.add_argument("--step", default="appending", choices=["appending", "two-calls"],
+                    help="appending: one call that appends the new rows and decodes "
+                         "(pkv_paged_decode_attention_appending; the fixed-partition kernel "
+                         "writes the rows itself, other paths launch the append first); "
+                         "two-calls: pkv_paged_cache_append, then the decode")
     ap.add_argument("--partition", type=int, default=-1, help="-1: the workload's own setting")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 4x the MALL")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -307,12 +315,18 @@ def time_config(cfg, args, dev, partition, with_cpu=True):
 
     def step(i, evs=None):
         r = i % R
-        pkv.paged_cache_append(kcs[r], vcs[r], st["k_new"], st["v_new"], st["slots"],
-                               st["k_scale"], st["v_scale"])
-        pkv.paged_decode_attention(st["q"], kcs[r], vcs[r], st["block_tables"],
-                                   st["context_lens"], cfg.scale, st["k_scale"], st["v_scale"],
-                                   partition_size=ps, out=out, workspace=ws, algo=args.algo,
-                                   events=evs)
+        if args.step == "two-calls":
+            pkv.paged_cache_append(kcs[r], vcs[r], st["k_new"], st["v_new"], st["slots"],
+                                   st["k_scale"], st["v_scale"])
+            pkv.paged_decode_attention(st["q"], kcs[r], vcs[r], st["block_tables"],
+                                       st["context_lens"], cfg.scale, st["k_scale"],
+                                       st["v_scale"], partition_size=ps, out=out, workspace=ws,
+                                       algo=args.algo, events=evs)
+        else:
+            pkv.paged_decode_attention_appending(
+                st["q"], st["k_new"], st["v_new"], st["slots"], kcs[r], vcs[r],
+                st["block_tables"], st["context_lens"], cfg.scale, st["k_scale"], st["v_scale"],
+                partition_size=ps, out=out, workspace=ws, algo=args.algo, events=evs)
 
     for i in range(args.warmup):
         step(i)
@@ -781,7 +795,7 @@ def main():
                    "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
                    "block_size": cfg.block_size, "partition": res["partition"],
                    "algo": res["algo"], "kv_bytes_per_step": res["kv_bytes"],
-                   "replicas": res["replicas"]},
+                   "replicas": res["replicas"], "step": args.step},
         "decode_tokens_per_s": round(res["tokens_per_s"], 1),
         "pct_hbm_peak_step": round(100 * res["step_gbs"] / HBM_PEAK_GBS, 2),
         "roofline": roofline_obj(cfg, res),

@@ -258,6 +258,42 @@ pkv_status pkv_paged_decode_attention_profiled(
     size_t workspace_bytes, int32_t algo, void* stream, void* ev_begin, void* ev_mid,
     void* ev_end);
 
+/* The decode step's append and its attention in one call: the result is that
+ * of pkv_paged_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping,
+ * num_tokens = num_seqs, ..., new_dtype = q_dtype, kv_dtype, k_scale,
+ * v_scale) followed by pkv_paged_decode_attention_profiled with the other
+ * arguments ("Transformer 推理优化：KV Cache、PagedAttention 与 vLLM",
+ * sections 2.2 and 3.3: a decode step stores the new token's K and V at its
+ * slot, then attends over the whole context).  On the fixed-partition MFMA
+ * path (the planner's single pass, or explicit partitions beyond the
+ * persistent grid) the decode kernel writes the rows itself, with no append
+ * launch before it: the wave that consumes the slot's block puts the encoded
+ * row into the loaded tile, so no read waits for the write.  On every other
+ * path the append kernel runs first.
+ *   k_new, v_new : device [num_seqs][num_kv_heads][head_dim] in q_dtype,
+ *                  16-byte aligned: sequence s's new row.
+ *   slot_mapping : device int64[num_seqs].  Negative: sequence s appends
+ *                  nothing.  Otherwise a slot in a block that no other
+ *                  sequence's context reads (a block being written is
+ *                  private: copy-on-write, same page, section 3.5), distinct
+ *                  across sequences; normally the slot of the context's last
+ *                  token, block_tables[s][(L-1)/16] * 16 + (L-1) % 16 with
+ *                  L = context_lens[s].  A slot in a block that another
+ *                  sequence reads is still written, but that sequence's
+ *                  output is then unspecified.
+ *   events       : as for pkv_paged_decode_attention_profiled (they stamp
+ *                  the decode kernel, not an append launched before it).
+ * FP8/INT8 scales must be finite and > 0 (the append's rule); other errors as
+ * for pkv_paged_decode_attention_profiled. */
+pkv_status pkv_paged_decode_attention_appending(
+    void* out, const void* q, const void* k_new, const void* v_new,
+    const int64_t* slot_mapping, void* k_cache, void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    float scale, int32_t q_dtype, int32_t kv_dtype, float k_scale, float v_scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t algo, void* stream,
+    void* ev_begin, void* ev_mid, void* ev_end);
+
 /* Decode over an FP8 or INT8 cache with per-channel scales (see
  * pkv_paged_cache_append_per_channel): the K element of (token, kv-head h,
  * dim i) is code * k_scales[h*head_dim + i], likewise V.  The K scales are

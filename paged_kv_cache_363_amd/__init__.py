@@ -9,7 +9,8 @@ from .api import (BLOCK_SIZE, alloc_workspace, copy_blocks, decode_algo_for,  # 
                   decode_partition_size, decode_workspace_size, kv_bytes_per_token,
                   multiquery_partition_size, multiquery_workspace_size, paged_cache_append,
                   paged_cache_append_per_channel, paged_decode_attention_per_channel,
-                  paged_decode_attention, paged_decode_attention_noalloc,
+                  paged_decode_attention, paged_decode_attention_appending,
+                  paged_decode_attention_noalloc,
                   paged_multiquery_attention,
                   stream_read_probe, swap_blocks)
 from .pool import BlockPool  # noqa: F401

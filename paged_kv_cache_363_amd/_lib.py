@@ -36,6 +36,9 @@ SIGNATURES = {
     "pkv_paged_decode_attention_profiled": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                                   I32, F32, I32, I32, F32, F32, I32, P, SZ, I32, P,
                                                   P, P, P]),
+    "pkv_paged_decode_attention_appending": (I32, [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32,
+                                                   I32, I32, I32, F32, I32, I32, F32, F32, I32, P,
+                                                   SZ, I32, P, P, P, P]),
     "pkv_paged_decode_attention_noalloc": (I32, [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                                  I32, F32, I32, I32, F32, F32, I32, I32, P]),
     "pkv_multiquery_partition_size": (I32, [I32, I32, I32, I32, I32, I32]),

@@ -153,6 +153,47 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, context_lens, scal
     return out
 
 
+def paged_decode_attention_appending(q, k_new, v_new, slot_mapping, k_cache, v_cache,
+                                     block_tables, context_lens, scale, k_scale=1.0, v_scale=1.0,
+                                     partition_size=0, out=None, workspace=None, algo="auto",
+                                     stream=None, events=None):
+    """The decode step's append and attention in one call: the same result
+    as paged_cache_append(k_cache, v_cache, k_new, v_new, slot_mapping, ...)
+    followed by paged_decode_attention(...).  k_new, v_new [S][H_kv][d] in
+    the q dtype; slot_mapping [S] int64, negative (no row) or the slot of the
+    context's last token (pkv_paged_decode_attention_appending)."""
+    S, hq, d = q.shape
+    nb, hkv, bs, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shapes do not match q")
+    if tuple(k_new.shape) != (S, hkv, d) or tuple(v_new.shape) != (S, hkv, d):
+        raise ValueError(f"k_new/v_new must be [{S}, {hkv}, {d}]")
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise TypeError("k_new and v_new must be in the q dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape[0] != S:
+        raise TypeError("slot_mapping must be int64 [S]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables/context_lens must have one row per sequence")
+    mb = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(q, k_cache, block_tables, partition_size)
+    evs = [None, None, None]
+    if events is not None:
+        evs = [ctypes.c_void_p(e.cuda_event) if e is not None else None for e in events]
+    check(lib().pkv_paged_decode_attention_appending(
+        _dev(out, "out"), _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+        _dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(context_lens, "context_lens"), S, hq, hkv, d,
+        bs, nb, mb, float(scale), dtype_code(q), dtype_code(k_cache), float(k_scale),
+        float(v_scale), int(partition_size), _dev(workspace, "workspace"), workspace.numel(),
+        _ALGO[algo], _stream(q, stream), *evs))
+    return out
+
+
 NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES
 
 

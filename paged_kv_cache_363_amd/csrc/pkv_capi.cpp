@@ -517,7 +517,8 @@ pkv_status pkv::decode_impl(
     int32_t num_blocks, int32_t max_blocks_per_seq, float scale, int32_t q_dtype,
     int32_t kv_dtype, float k_scale, float v_scale, const float* k_scales,
     const float* v_scales, int32_t partition_size, void* workspace, size_t workspace_bytes,
-    int32_t algo, void* stream, void* ev_begin, void* ev_mid, void* ev_end) {
+    int32_t algo, void* stream, void* ev_begin, void* ev_mid, void* ev_end, const void* k_new,
+    const void* v_new, const int64_t* slot_mapping, float k_inv, float v_inv) {
   clear_error();
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks < 0 ||
       max_blocks_per_seq < 0)
@@ -603,6 +604,27 @@ pkv_status pkv::decode_impl(
   // right after the decode kernel
   a.ev_start = ev_begin;
   a.ev_stop = ev_mid;
+  if (k_new) {
+    // the step's new rows: appended by the fixed-partition MFMA kernel
+    // itself, else by the append kernel first
+    const bool fused = !use_stream && algo == PKV_ALGO_MFMA &&
+                       !(plan.parts_stream_ok && tiles_fit) && !k_scales;
+    if (fused) {
+      a.k_new = k_new;
+      a.v_new = v_new;
+      a.slots = slot_mapping;
+      a.k_inv = k_inv;
+      a.v_inv = v_inv;
+    } else {
+      const int rc = launch_cache_append(const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                                         k_new, v_new, slot_mapping, num_seqs, num_kv_heads,
+                                         head_dim, num_blocks, q_dtype, kv_dtype, k_inv, v_inv,
+                                         stream, nullptr, nullptr);
+      if (rc != 0)
+        return fail(PKV_ERR_HIP, "decode: append launch failed: %s",
+                    hipGetErrorString((hipError_t)rc));
+    }
+  }
   if (use_stream) {
     int rc = launch_decode_stream(a, plan.stream_grid, workspace, plan.stream_off_ml,
                                   plan.stream_off_part);
@@ -651,6 +673,37 @@ pkv_status pkv_paged_decode_attention_profiled(
                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, scale,
                      q_dtype, kv_dtype, k_scale, v_scale, nullptr, nullptr, partition_size,
                      workspace, workspace_bytes, algo, stream, ev_begin, ev_mid, ev_end);
+}
+
+pkv_status pkv_paged_decode_attention_appending(
+    void* out, const void* q, const void* k_new, const void* v_new,
+    const int64_t* slot_mapping, void* k_cache, void* v_cache, const int32_t* block_tables,
+    const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+    int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+    float scale, int32_t q_dtype, int32_t kv_dtype, float k_scale, float v_scale,
+    int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t algo, void* stream,
+    void* ev_begin, void* ev_mid, void* ev_end) {
+  clear_error();
+  // the append's own checks (pkv_paged_cache_append with num_tokens = num_seqs)
+  float k_inv = 1.0f, v_inv = 1.0f;
+  if (byte_codes(kv_dtype)) {
+    if (!(k_scale > 0.0f) || !std::isfinite(k_scale) || !(v_scale > 0.0f) ||
+        !std::isfinite(v_scale))
+      return fail(PKV_ERR_INVALID_ARG, "decode_appending: FP8/INT8 scales must be finite and > 0");
+    k_inv = 1.0f / k_scale;
+    v_inv = 1.0f / v_scale;
+  }
+  if (num_seqs > 0) {
+    if (!k_new || !v_new || !slot_mapping)
+      return fail(PKV_ERR_INVALID_ARG, "decode_appending: NULL pointer");
+    if (!aligned16(k_new) || !aligned16(v_new))
+      return fail(PKV_ERR_INVALID_ARG, "decode_appending: new rows must be 16-byte aligned");
+  }
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, scale,
+                     q_dtype, kv_dtype, k_scale, v_scale, nullptr, nullptr, partition_size,
+                     workspace, workspace_bytes, algo, stream, ev_begin, ev_mid, ev_end,
+                     num_seqs > 0 ? k_new : nullptr, v_new, slot_mapping, k_inv, v_inv);
 }
 
 pkv_status pkv_paged_decode_attention_per_channel(

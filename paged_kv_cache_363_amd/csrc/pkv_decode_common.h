@@ -37,6 +37,13 @@ struct DecodeParams {
   float* ws_acc;
   const float* ks;   // per-channel K scales [Hkv][D] (nullptr: per tensor)
   const float* vs;   // per-channel V scales [Hkv][D] (nullptr: vsc)
+  // The step's new rows, appended by the decode kernel itself (nullptr: none):
+  // kn, vn [S][Hkv][D] in the q dtype, slot of sequence s in slots[s],
+  // encoded with k_inv / v_inv (1 / scale in binary32, as the cache append)
+  const uint8_t* kn;
+  const uint8_t* vn;
+  const int64_t* slots;
+  float k_inv, v_inv;
 };
 
 // Output store in the q dtype.
@@ -179,6 +186,11 @@ inline DecodeParams make_params(const pkv::DecodeArgs& a, int chunk_heads) {
   p.ws_acc = a.ws_acc;
   p.ks = a.k_scales;
   p.vs = a.v_scales;
+  p.kn = static_cast<const uint8_t*>(a.k_new);
+  p.vn = static_cast<const uint8_t*>(a.v_new);
+  p.slots = a.slots;
+  p.k_inv = a.k_inv;
+  p.v_inv = a.v_inv;
   if (p.ks) p.sl2 = a.scale * kLog2e;   // the K scales go into q instead
   return p;
 }

@@ -38,8 +38,84 @@ using namespace pkvd;
 
 constexpr int NWG = PKV_MFMA_WAVES;
 
+// The step's new K/V row of one (sequence, kv-head), appended inside the
+// decode: the row goes to its slot and attention reads the context with it
+// ("Transformer 推理优化", sections 2.2 and 3.3).  Lane l holds the raw
+// 16-bit elements EPL l .. EPL l + EPL - 1 of the K and V rows (kraw, vraw;
+// EPL = D / 64).  prepare() encodes them to the cache's type with the bytes
+// the cache append stores, stages the encoded rows in the wave's own LDS
+// area (K row, then V row), and in the writer wave stores them to the slot.
+// sub() runs before each loaded tile is consumed: when the tile's block
+// holds the slot, it reads the row back in the lane's share of the tile
+// layout and puts it at the slot's position.  Every wave of this sequence
+// that consumes that block therefore sees the new row, whether its loads
+// ran before or after the store, and no ordering is needed.
+template <int QT, int KVT, int D>
+struct AppendRow {
+  using T = MfmaTile<QT, KVT, D>;
+  static constexpr bool active = false;
+  static constexpr bool subst = true;
+  static constexpr int EPL = D / 64;
+  static constexpr int LB = EPL * T::KVB;   // encoded bytes per lane and row
+  uint32_t kraw, vraw;
+  float k_inv, v_inv;
+  int64_t slot;    // the row's slot (negative: no row)
+  bool writer;
+  uint8_t* lds;    // 2 D KVB bytes of the wave's LDS, 16-byte aligned
+  uint8_t* kc;
+  uint8_t* vc;
+  int nb, Hkv, hk, lane;
+  int period = 0;
+  __device__ void operator()() const {}
+
+  __device__ static void put(uint8_t* dst, uint32_t x) {
+    if constexpr (LB == 4) *reinterpret_cast<uint32_t*>(dst) = x;
+    else if constexpr (LB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)x;
+    else *dst = (uint8_t)x;
+  }
+
+  __device__ void prepare() const {
+    uint32_t ke, ve;
+    encode_new_chunk<QT, KVT, EPL>(make_uint4(kraw, 0u, 0u, 0u), k_inv, &ke);
+    encode_new_chunk<QT, KVT, EPL>(make_uint4(vraw, 0u, 0u, 0u), v_inv, &ve);
+    put(lds + LB * lane, ke);
+    put(lds + D * T::KVB + LB * lane, ve);
+    if (writer && slot >= 0 && slot < (int64_t)nb * pkv::kBlockSize) {
+      const int64_t row0 = (((slot >> 4) * Hkv + hk) * pkv::kBlockSize + (slot & 15)) * D;
+      put(kc + row0 * T::KVB + LB * lane, ke);
+      put(vc + row0 * T::KVB + LB * lane, ve);
+    }
+  }
+
+  // r: the tile of block `id` (wave-uniform)
+  __device__ void sub(typename T::Raw& r, int id) const {
+    if (slot < 0 || (int64_t)id != slot >> 4) return;
+    const int tn = (int)(slot & 15);   // the row's position in the tile
+    const int c = lane & 15, G = lane >> 4;
+    const bool kl = c == tn, vl = G == (tn >> 2);
+#pragma unroll
+    for (int kk = 0; kk < T::KL; ++kk) {
+      const int d0 = T::BYTE ? 64 * kk + 16 * G : 32 * kk + 8 * G;   // as MfmaTile::issue
+      const u32x4 e = *reinterpret_cast<const u32x4*>(lds + d0 * T::KVB);
+      r.k[kk] = kl ? e : r.k[kk];
+    }
+    const typename T::VRow e = *reinterpret_cast<const typename T::VRow*>(
+        lds + (D + T::DPL * c) * T::KVB);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const bool take = vl && rr == (tn & 3);
+      if constexpr (T::ROWB == 4)
+        r.v[rr].w[0] = take ? e.w[0] : r.v[rr].w[0];
+      else
+        r.v[rr].w = take ? e.w : r.v[rr].w;
+    }
+  }
+};
+
 // PC: a one-byte-code cache with per-channel scales (p.ks, p.vs).
-template <int QT, int KVT, int D, int HS, bool PC>
+// APP: the kernel appends the step's new K/V rows itself (p.kn, p.vn,
+// p.slots; AppendRow).
+template <int QT, int KVT, int D, int HS, bool PC, bool APP = false>
 __global__ __launch_bounds__(64 * NWG) __attribute__((amdgpu_waves_per_eu(PKV_MFMA_WPE, 8)))
 void decode_mfma_kernel(DecodeParams p) {
   using T = MfmaTile<QT, KVT, D>;
@@ -66,6 +142,10 @@ void decode_mfma_kernel(DecodeParams p) {
   // first K/V loads wait for one round trip less.  Indices past the table
   // row are clamped to its last entry (never used: the piece stops at the
   // context).
+  // APP: the new row's slot (AppendRow), read first: before any store of
+  // the kernel, so that it stays a scalar load
+  [[maybe_unused]] int64_t slot = -1;
+  if constexpr (APP) slot = p.slots[s];
   int ids0[PKV_ID_VGPRS];
   if (p.mb > 0) {
 #pragma unroll
@@ -80,9 +160,29 @@ void decode_mfma_kernel(DecodeParams p) {
   else
     T::load_q(qr, p.q, (int64_t)s * p.Hq + h_first + c, c < nh, G);
 
+  // APP: the raw new row of this (sequence, kv-head), lane l's elements
+  // (AppendRow), requested with q, before the context length, which it does
+  // not depend on.
+  [[maybe_unused]] uint32_t kraw = 0u, vraw = 0u;
+  if constexpr (APP) {
+    const int64_t e0 = ((int64_t)s * p.Hkv + hk) * D + (D / 64) * lane;
+    if constexpr (D == 128) {
+      kraw = reinterpret_cast<const uint32_t*>(p.kn)[e0 / 2];
+      vraw = reinterpret_cast<const uint32_t*>(p.vn)[e0 / 2];
+    } else {
+      kraw = reinterpret_cast<const uint16_t*>(p.kn)[e0];
+      vraw = reinterpret_cast<const uint16_t*>(p.vn)[e0];
+    }
+  }
   const int ctx = clamped_ctx(p, s);
   const int nblk = (ctx + 15) >> 4;
-  if (part > 0 && b_begin >= nblk) return;
+  if (part > 0 && b_begin >= nblk) {
+    // the new row is used on this path too, so the compiler keeps its loads
+    // above the branch (sunk below it, they would be issued after the
+    // length's round trip, and the first K/V loads would wait for them)
+    if constexpr (APP) asm volatile("" ::"v"(kraw), "v"(vraw), "s"(slot));
+    return;
+  }
   const int b_end = min(b_begin + p.part_blocks, nblk);
 
   f32x4 o[DPL];
@@ -95,14 +195,28 @@ void decode_mfma_kernel(DecodeParams p) {
   const int steps = nblk_p > w ? (nblk_p - w + NWG - 1) / NWG : 0;
   const int lb = nblk - 1 - b_begin - w;
   const int last_step = (b_end == nblk && lb >= 0 && lb % NWG == 0) ? lb / NWG : -1;
+  [[maybe_unused]] const AppendRow<QT, KVT, D> app{
+      kraw, vraw, p.k_inv, p.v_inv, slot, part == 0 && hc == 0 && w == 0,
+      reinterpret_cast<uint8_t*>(sm_o + w * HS * LD), const_cast<uint8_t*>(p.kc),
+      const_cast<uint8_t*>(p.vc), p.nb, p.Hkv, hk, lane};
   if (p.nb > 0 && steps > 0) {
     const int64_t blk_stride = (int64_t)p.Hkv * T::TILE;
     const int64_t head_off = (int64_t)hk * T::TILE;
-    mfma_piece<QT, KVT, D, pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH,
-               pkv::byte_codes(KVT) ? PKV_MFMA_NT8 : PKV_MFMA_NT16, false, PC>(
-        p.kc + head_off, p.vc + head_off, blk_stride, row + b_begin + w, 0, steps, last_step,
-        ctx - 16 * (nblk - 1), p.nb, qr, p.sl2, &m_run, &l_run, o, lane, nullptr, qlo, NoHook{},
-        NWG, ids0);
+    constexpr int DEPTH = pkv::byte_codes(KVT) ? PKV_PIPE_DEPTH_FP8 : PKV_PIPE_DEPTH;
+    constexpr bool NT = pkv::byte_codes(KVT) ? PKV_MFMA_NT8 : PKV_MFMA_NT16;
+    if constexpr (APP) {
+      mfma_piece<QT, KVT, D, DEPTH, NT, false, PC>(
+          p.kc + head_off, p.vc + head_off, blk_stride, row + b_begin + w, 0, steps, last_step,
+          ctx - 16 * (nblk - 1), p.nb, qr, p.sl2, &m_run, &l_run, o, lane, nullptr, qlo, app,
+          NWG, ids0);
+    } else {
+      mfma_piece<QT, KVT, D, DEPTH, NT, false, PC>(
+          p.kc + head_off, p.vc + head_off, blk_stride, row + b_begin + w, 0, steps, last_step,
+          ctx - 16 * (nblk - 1), p.nb, qr, p.sl2, &m_run, &l_run, o, lane, nullptr, qlo,
+          NoHook{}, NWG, ids0);
+    }
+  } else if constexpr (APP) {
+    if (app.writer) app.prepare();   // no blocks here: only the store remains
   }
 
   // lane (G, c) holds O[head c][dim DPL*(4G+i) + e]; l needs the 4 G lanes
@@ -131,6 +245,9 @@ int launch_t(const pkv::DecodeArgs& a, const DecodeParams& kp) {
       return pkv::launch_kernel(decode_mfma_kernel<QT, KVT, D, HS, true>, grid, block, a.stream,
                                 kp, a.ev_start, a.ev_stop);
   }
+  if (kp.kn)
+    return pkv::launch_kernel(decode_mfma_kernel<QT, KVT, D, HS, false, true>, grid, block,
+                              a.stream, kp, a.ev_start, a.ev_stop);
   return pkv::launch_kernel(decode_mfma_kernel<QT, KVT, D, HS, false>, grid, block, a.stream, kp,
                             a.ev_start, a.ev_stop);
 }

@@ -202,4 +202,46 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | (code > 0x7Eu ? 0x7Eu : code);
 }
 
+// N = 1, 2, 4 or 8 consecutive elements of a new K or V row in the 16-bit
+// dtype NEW_DT (raw: their bits, the first N * 2 bytes of the 16), in the
+// cache dtype KV_DT as the cache append stores them: the same bits for a
+// 16-bit cache (KV_DT == NEW_DT), else each element's code from x * inv in
+// binary32 (f32_to_e4m3 / f32_to_i8), byte i of the chunk at bits 8 (i % 4)
+// of word i / 4.  w receives the N * bytes(KV_DT) bytes in whole words (the
+// bytes past them zero).
+template <int NEW_DT, int KV_DT, int N>
+__device__ __forceinline__ void encode_new_chunk(uint4 raw, float inv, uint32_t* w) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "1, 2, 4 or 8 elements");
+  static_assert(NEW_DT == PKV_F16 || NEW_DT == PKV_BF16, "16-bit new rows");
+  if constexpr (N <= 4) {
+    raw.z = 0u;
+    raw.w = 0u;
+  }
+  if constexpr (N <= 2) raw.y = 0u;
+  if constexpr (N == 1) raw.x &= 0xFFFFu;
+  if constexpr (KV_DT == NEW_DT) {
+    w[0] = raw.x;
+    if constexpr (N >= 4) w[1] = raw.y;
+    if constexpr (N == 8) {
+      w[2] = raw.z;
+      w[3] = raw.w;
+    }
+  } else {
+    static_assert(KV_DT == PKV_FP8_E4M3 || KV_DT == PKV_INT8, "one-byte codes");
+    float f[8];
+    chunk_to_f32<NEW_DT>(raw, f);
+    constexpr int NW = N < 4 ? 1 : N / 4;
+    uint32_t word[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) word[k] = 0u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float x = f[i] * inv;
+      word[i / 4] |= (KV_DT == PKV_FP8_E4M3 ? f32_to_e4m3(x) : f32_to_i8(x)) << (8 * (i % 4));
+    }
+#pragma unroll
+    for (int k = 0; k < NW; ++k) w[k] = word[k];
+  }
+}
+
 }  // namespace pkvd

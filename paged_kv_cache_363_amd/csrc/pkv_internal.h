@@ -91,6 +91,12 @@ struct DecodeArgs {
   // nullptr: k_scale / v_scale apply to the whole tensor
   const float* k_scales = nullptr;
   const float* v_scales = nullptr;
+  // the step's new K/V rows [S][H_kv][D] (q dtype) and their slots, appended
+  // by the decode kernel (nullptr: the caches already hold them)
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  const int64_t* slots = nullptr;
+  float k_inv = 1.0f, v_inv = 1.0f;
 };
 
 // Multi-query call: rows query_start[s] .. query_start[s+1]-1 belong to
@@ -153,7 +159,9 @@ pkv_status decode_impl(void* out, const void* q, const void* k_cache, const void
                        int32_t kv_dtype, float k_scale, float v_scale, const float* k_scales,
                        const float* v_scales, int32_t partition_size, void* workspace,
                        size_t workspace_bytes, int32_t algo, void* stream, void* ev_begin,
-                       void* ev_mid, void* ev_end);
+                       void* ev_mid, void* ev_end, const void* k_new = nullptr,
+                       const void* v_new = nullptr, const int64_t* slot_mapping = nullptr,
+                       float k_inv = 1.0f, float v_inv = 1.0f);
 
 // Kernel launchers (return hipError_t as int).
 int launch_multiquery(const MQArgs& a);

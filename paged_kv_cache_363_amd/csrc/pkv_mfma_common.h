@@ -205,9 +205,10 @@ struct MfmaTile {
     else return PM::fp8x2(w, hi);
   }
 
+  using VRow = Row<ROWB>;
   struct Raw {
     u32x4 k[KL];
-    Row<ROWB> v[4];
+    VRow v[4];
   };
 
   // dim of element i of k-slot G in QK step kk (the same map for q and K)
@@ -573,9 +574,13 @@ struct MfmaTile {
 // Hook: with Hook::active, hook() runs after the last block of every run of
 // hook.period blocks (runs aligned to multiples of the period) and after the
 // piece's last block; it may read and reset the running state.  The loads of
-// the next blocks stay in flight across it.
+// the next blocks stay in flight across it.  With Hook::subst,
+// hook.prepare() runs once after the piece's first loads are issued, and
+// hook.sub(tile, id) before each tile of block `id` is consumed (it may
+// change the tile's registers).
 struct NoHook {
   static constexpr bool active = false;
+  static constexpr bool subst = false;
   int period = 0;
   __device__ void operator()() const {}
 };
@@ -584,6 +589,7 @@ struct NoHook {
 template <typename F>
 struct PeriodHook {
   static constexpr bool active = true;
+  static constexpr bool subst = false;
   int period;
   F f;
   __device__ void operator()() const { f(); }
@@ -656,6 +662,9 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
       // would then be waited down to the newest block only.
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (Hook::subst) {
+      if (c0 == b0) hook.prepare();
+    }
     for (int i = 0; i < n; i += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
@@ -664,6 +673,7 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
         const int valid = (ii < n && (unsigned)idc[d] < (unsigned)nb)
                               ? (c0 + ii == last ? tail : 16) : 0;
         const bool whole = valid == 16 && (!CAUSAL || c0 + ii < whole_end);
+        if constexpr (Hook::subst) hook.sub(buf[d], idc[d]);
         T::template consume<NTL, PC, CAUSAL>(buf[d], valid, whole, pos, 16 * (c0 + ii), qr, sl2,
                                              m_run, l_run, o, c, G, qlo);
         if constexpr (Hook::active) {
