@@ -5,8 +5,8 @@ A step is one pass of the whole decode hot path over one batch: the cache
 append of every sequence's new token (slot_mapping write) followed by paged
 decode attention over each sequence's context (the decode kernel, plus the
 merge or reduction kernel when contexts are split), issued as one call
-(pkv_paged_decode_attention_appending: on the fixed-partition kernel the
-decode kernel writes the new rows itself; elsewhere the append kernel runs
+(pkv_paged_decode_attention_appending: the MFMA decode kernels write the
+new rows themselves; before the vector kernel the append kernel runs
 first).  The block tables,
 context lengths and slot mapping come from the native block pool, built
 before the timed region (its host cost per step is measured separately).
@@ -57,8 +57,9 @@ def parse():
     ap.add_argument("--algo", default="auto", choices=["auto", "vector", "mfma"])
     ap.add_argument("--step", default="appending", choices=["appending", "two-calls"],
                     help="appending: one call that appends the new rows and decodes "
-                         "(pkv_paged_decode_attention_appending; the fixed-partition kernel "
-                         "writes the rows itself, other paths launch the append first); "
+                         "(pkv_paged_decode_attention_appending; the MFMA decode kernels "
+                         "write the rows themselves, the vector path launches the append "
+                         "first); "
                          "two-calls: pkv_paged_cache_append, then the decode")
     ap.add_argument("--partition", type=int, default=-1, help="-1: the workload's own setting")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed 4x the MALL")

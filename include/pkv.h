@@ -264,12 +264,12 @@ pkv_status pkv_paged_decode_attention_profiled(
  * v_scale) followed by pkv_paged_decode_attention_profiled with the other
  * arguments ("Transformer 推理优化：KV Cache、PagedAttention 与 vLLM",
  * sections 2.2 and 3.3: a decode step stores the new token's K and V at its
- * slot, then attends over the whole context).  On the fixed-partition MFMA
- * path (the planner's single pass, or explicit partitions beyond the
- * persistent grid) the decode kernel writes the rows itself, with no append
- * launch before it: the wave that consumes the slot's block puts the encoded
- * row into the loaded tile, so no read waits for the write.  On every other
- * path the append kernel runs first.
+ * slot, then attends over the whole context).  On the MFMA paths (fixed
+ * partitions, the balanced grid, partitions on the persistent grid) the
+ * decode kernel writes the rows itself, with no append launch before it:
+ * every wave that consumes the slot's block puts the encoded row into the
+ * loaded tile, so no read waits for the write.  The vector kernel
+ * (algo = vector, f32 caches, MHA under AUTO) runs the append kernel first.
  *   k_new, v_new : device [num_seqs][num_kv_heads][head_dim] in q_dtype,
  *                  16-byte aligned: sequence s's new row.
  *   slot_mapping : device int64[num_seqs].  Negative: sequence s appends

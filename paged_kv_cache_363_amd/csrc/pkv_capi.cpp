@@ -605,10 +605,9 @@ pkv_status pkv::decode_impl(
   a.ev_start = ev_begin;
   a.ev_stop = ev_mid;
   if (k_new) {
-    // the step's new rows: appended by the fixed-partition MFMA kernel
-    // itself, else by the append kernel first
-    const bool fused = !use_stream && algo == PKV_ALGO_MFMA &&
-                       !(plan.parts_stream_ok && tiles_fit) && !k_scales;
+    // the step's new rows: appended by the MFMA decode kernels themselves,
+    // else (vector kernel, per-channel scales) by the append kernel first
+    const bool fused = algo == PKV_ALGO_MFMA && !k_scales;
     if (fused) {
       a.k_new = k_new;
       a.v_new = v_new;

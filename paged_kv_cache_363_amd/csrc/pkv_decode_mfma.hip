@@ -38,77 +38,40 @@ using namespace pkvd;
 
 constexpr int NWG = PKV_MFMA_WAVES;
 
-// The step's new K/V row of one (sequence, kv-head), appended inside the
-// decode: the row goes to its slot and attention reads the context with it
-// ("Transformer 推理优化", sections 2.2 and 3.3).  Lane l holds the raw
-// 16-bit elements EPL l .. EPL l + EPL - 1 of the K and V rows (kraw, vraw;
-// EPL = D / 64).  prepare() encodes them to the cache's type with the bytes
-// the cache append stores, stages the encoded rows in the wave's own LDS
-// area (K row, then V row), and in the writer wave stores them to the slot.
-// sub() runs before each loaded tile is consumed: when the tile's block
-// holds the slot, it reads the row back in the lane's share of the tile
-// layout and puts it at the slot's position.  Every wave of this sequence
-// that consumes that block therefore sees the new row, whether its loads
-// ran before or after the store, and no ordering is needed.
+// The step's new K/V row of one (sequence, kv-head) (NewRow), appended by
+// the decode kernel itself.  prepare() encodes the lane's raw elements and
+// stages the encoded rows in the wave's own part of the LDS merge area (not
+// used until the wave's blocks are done); the writer wave also stores them
+// to the slot.  sub() runs before each loaded tile is consumed and puts the
+// row into the tile when its block holds the slot.
 template <int QT, int KVT, int D>
 struct AppendRow {
-  using T = MfmaTile<QT, KVT, D>;
+  using N = NewRow<QT, KVT, D>;
   static constexpr bool active = false;
   static constexpr bool subst = true;
-  static constexpr int EPL = D / 64;
-  static constexpr int LB = EPL * T::KVB;   // encoded bytes per lane and row
   uint32_t kraw, vraw;
   float k_inv, v_inv;
   int64_t slot;    // the row's slot (negative: no row)
   bool writer;
-  uint8_t* lds;    // 2 D KVB bytes of the wave's LDS, 16-byte aligned
+  uint8_t* lds;    // N::STAGE bytes of the wave's LDS, 16-byte aligned
   uint8_t* kc;
   uint8_t* vc;
   int nb, Hkv, hk, lane;
   int period = 0;
   __device__ void operator()() const {}
 
-  __device__ static void put(uint8_t* dst, uint32_t x) {
-    if constexpr (LB == 4) *reinterpret_cast<uint32_t*>(dst) = x;
-    else if constexpr (LB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)x;
-    else *dst = (uint8_t)x;
-  }
-
   __device__ void prepare() const {
     uint32_t ke, ve;
-    encode_new_chunk<QT, KVT, EPL>(make_uint4(kraw, 0u, 0u, 0u), k_inv, &ke);
-    encode_new_chunk<QT, KVT, EPL>(make_uint4(vraw, 0u, 0u, 0u), v_inv, &ve);
-    put(lds + LB * lane, ke);
-    put(lds + D * T::KVB + LB * lane, ve);
-    if (writer && slot >= 0 && slot < (int64_t)nb * pkv::kBlockSize) {
-      const int64_t row0 = (((slot >> 4) * Hkv + hk) * pkv::kBlockSize + (slot & 15)) * D;
-      put(kc + row0 * T::KVB + LB * lane, ke);
-      put(vc + row0 * T::KVB + LB * lane, ve);
-    }
+    N::encode(kraw, vraw, k_inv, v_inv, ke, ve);
+    N::stage(lds, lane, ke, ve);
+    if (writer && slot >= 0 && slot < (int64_t)nb * pkv::kBlockSize)
+      N::store(kc, vc, slot, Hkv, hk, lane, ke, ve);
   }
 
   // r: the tile of block `id` (wave-uniform)
-  __device__ void sub(typename T::Raw& r, int id) const {
+  __device__ void sub(typename N::T::Raw& r, int id) const {
     if (slot < 0 || (int64_t)id != slot >> 4) return;
-    const int tn = (int)(slot & 15);   // the row's position in the tile
-    const int c = lane & 15, G = lane >> 4;
-    const bool kl = c == tn, vl = G == (tn >> 2);
-#pragma unroll
-    for (int kk = 0; kk < T::KL; ++kk) {
-      const int d0 = T::BYTE ? 64 * kk + 16 * G : 32 * kk + 8 * G;   // as MfmaTile::issue
-      const u32x4 e = *reinterpret_cast<const u32x4*>(lds + d0 * T::KVB);
-      r.k[kk] = kl ? e : r.k[kk];
-    }
-    const typename T::VRow e = *reinterpret_cast<const typename T::VRow*>(
-        lds + (D + T::DPL * c) * T::KVB);
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const bool take = vl && rr == (tn & 3);
-      if constexpr (T::ROWB == 4)
-        r.v[rr].w[0] = take ? e.w[0] : r.v[rr].w[0];
-      else
-        r.v[rr].w = take ? e.w : r.v[rr].w;
-    }
+    N::sub(r, lds, (int)(slot & 15), lane);
   }
 };
 
@@ -164,16 +127,8 @@ void decode_mfma_kernel(DecodeParams p) {
   // (AppendRow), requested with q, before the context length, which it does
   // not depend on.
   [[maybe_unused]] uint32_t kraw = 0u, vraw = 0u;
-  if constexpr (APP) {
-    const int64_t e0 = ((int64_t)s * p.Hkv + hk) * D + (D / 64) * lane;
-    if constexpr (D == 128) {
-      kraw = reinterpret_cast<const uint32_t*>(p.kn)[e0 / 2];
-      vraw = reinterpret_cast<const uint32_t*>(p.vn)[e0 / 2];
-    } else {
-      kraw = reinterpret_cast<const uint16_t*>(p.kn)[e0];
-      vraw = reinterpret_cast<const uint16_t*>(p.vn)[e0];
-    }
-  }
+  if constexpr (APP)
+    NewRow<QT, KVT, D>::load(p.kn, p.vn, (int64_t)s * p.Hkv + hk, lane, kraw, vraw);
   const int ctx = clamped_ctx(p, s);
   const int nblk = (ctx + 15) >> 4;
   if (part > 0 && b_begin >= nblk) {

@@ -99,6 +99,12 @@ struct StreamParams {
   float* ws_m;
   float* ws_l;
   float* ws_acc;
+  // the step's new K/V rows ([S][Hkv][D] in the q dtype) and their slots,
+  // appended by the decode kernel itself (nullptr: none)
+  const uint8_t* kn;
+  const uint8_t* vn;
+  const int64_t* slots;
+  float k_inv, v_inv;
 };
 
 // Unit prefix sums in LDS, computed by one workgroup of 4 waves.  A segment
@@ -142,7 +148,12 @@ __device__ __forceinline__ void block_prefix(const StreamParams& p, int* sm_pref
 
 // PC: a one-byte-code cache with per-channel scales (p.ks, p.vs).
 // PM: partition mode (p.P blocks per partition).
-template <int QT, int KVT, int D, bool PC, bool PM>
+// APP: the kernel appends the step's new K/V rows itself (p.kn, p.vn,
+// p.slots; NewRow): a piece stages the new row of its (sequence, kv-head)
+// in LDS, puts it into the tile of the slot's block before consuming it,
+// and the piece holding the last block of its sequence's kv-head (head
+// chunk 0) stores it to the slot.
+template <int QT, int KVT, int D, bool PC, bool PM, bool APP = false>
 __global__ __launch_bounds__(64 * kSkWaves) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void decode_stream_kernel(StreamParams p) {
   using T = MfmaTile<QT, KVT, D>;
@@ -168,6 +179,11 @@ void decode_stream_kernel(StreamParams p) {
   __shared__ int4 sm_meta[kSkWaves * kStashSlots];
   __shared__ int sm_tiles[kSkWaves * kTileCap];
   __shared__ uint4 sm_q[kSkWaves * kQStage];
+  // APP: the new rows and slots of the pieces being staged (piece k in
+  // place k % NQ)
+  using NR = NewRow<QT, KVT, D>;
+  __shared__ __align__(16) uint8_t sm_new[APP ? kSkWaves * NQ * NR::STAGE : 16];
+  __shared__ int64_t sm_nslot[APP ? kSkWaves * NQ : 1];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -192,6 +208,18 @@ void decode_stream_kernel(StreamParams p) {
       }
     } else {
       for (int i = lane; i < p.Hq * D; i += 64) store_out<QT>(p.out, (int64_t)s * p.Hq * D + i, 0.f);
+    }
+    if constexpr (APP) {   // no piece reads the row, only the store remains
+      const int64_t sl = p.slots[s];
+      if (sl >= 0 && sl < (int64_t)p.nb * pkv::kBlockSize) {
+        for (int hk = 0; hk < p.Hkv; ++hk) {
+          uint32_t kr, vr, ke, ve;
+          NR::load(p.kn, p.vn, (int64_t)s * p.Hkv + hk, lane, kr, vr);
+          NR::encode(kr, vr, p.k_inv, p.v_inv, ke, ve);
+          NR::store(const_cast<uint8_t*>(p.kc), const_cast<uint8_t*>(p.vc), sl, p.Hkv, hk, lane,
+                    ke, ve);
+        }
+      }
     }
   }
 
@@ -563,6 +591,47 @@ void decode_stream_kernel(StreamParams p) {
     total = t;
   }
   const int nq = min(npieces, NQ);
+  // APP: the new rows of the first pieces: loaded here, ahead of the q rows
+  // of the staging below, unconditionally (places past the share's pieces
+  // repeat the first), so that no branch leaves the load counter's order
+  // unknown; encoded and staged in LDS after the q rows
+  // (the places live in LDS, addressed from the wave index, so that the
+  // block loop carries no more than one scalar for them: the slot's tile)
+  [[maybe_unused]] auto place_row = [&](int k) { return sm_new + (w * NQ + k) * NR::STAGE; };
+  [[maybe_unused]] auto place_slot = [&](int k) {
+    const int64_t v = sm_nslot[w * NQ + k];
+    return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)v));
+  };
+  [[maybe_unused]] uint32_t nkr[APP ? NQ : 1], nvr[APP ? NQ : 1];
+  [[maybe_unused]] int64_t nsl_r[APP ? NQ : 1];
+  [[maybe_unused]] Piece pcs[APP ? NQ : 1];
+  if constexpr (APP) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      if (i < nq) pcs[i] = pq[i];
+      else pcs[i] = pq[0];
+      nsl_r[i] = p.slots[pcs[i].s];
+      NR::load(p.kn, p.vn, (int64_t)pcs[i].s * p.Hkv + pcs[i].y / p.hchunks, lane, nkr[i],
+               nvr[i]);
+    }
+  }
+  // piece pc's new row (raw elements kr, vr; slot sl) into place k; the
+  // piece holding the last block of its sequence's kv-head (head chunk 0)
+  // also stores it to the slot
+  // (real = false: only the row is staged, into a place no piece reads)
+  [[maybe_unused]] auto stage_piece = [&](const Piece& pc, int k, uint32_t kr, uint32_t vr,
+                                          int64_t sl, bool real = true) {
+    uint32_t ke, ve;
+    NR::encode(kr, vr, p.k_inv, p.v_inv, ke, ve);
+    NR::stage(place_row(k), lane, ke, ve);
+    if (!real) return;
+    if (lane == 0) sm_nslot[w * NQ + k] = sl;
+    if (pc.y % p.hchunks == 0 && pc.b1 == (sm_ctx[pc.s] + 15) >> 4 && sl >= 0 &&
+        sl < (int64_t)p.nb * pkv::kBlockSize)
+      NR::store(const_cast<uint8_t*>(p.kc), const_cast<uint8_t*>(p.vc), sl, p.Hkv,
+                pc.y / p.hchunks, lane, ke, ve);
+  };
   uint4* qs = sm_q + w * kQStage;
 #pragma unroll
   for (int i = 1; i < NQ; ++i)
@@ -577,6 +646,15 @@ void decode_stream_kernel(StreamParams p) {
       }
     }
 
+  // APP: the new rows of the first pieces, staged in LDS (their loads went
+  // out before the q rows above).  Every place is written, so that every
+  // load is consumed here: a load left unconsumed on some paths would still
+  // count as in flight in the block loop, which would then wait for it.
+  if constexpr (APP) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) stage_piece(pcs[i], i, nkr[i], nvr[i], nsl_r[i], i < nq);
+  }
+
   // ---- the consumed piece ----
   Walk cw = w0;
   Piece cur;
@@ -586,12 +664,27 @@ void decode_stream_kernel(StreamParams p) {
   int c_last = ((sm_ctx[cur.s] + 15) >> 4) - 1;
   int c_tail = sm_ctx[cur.s] - 16 * c_last;
   int rem = PM ? p.P : 0;   // blocks left in the current partition
+  // APP: the tile index of the current piece's slot block (-2, which no
+  // tile has, when there is no row); its row and slot sit in place pi % NQ
+  [[maybe_unused]] int cur_tile = -2;
+  [[maybe_unused]] auto take_row = [&](int k) {
+    const int64_t sl = place_slot(k);
+    const bool ok = sl >= 0 && sl < (int64_t)p.nb * pkv::kBlockSize;
+    cur_tile = ok ? (int)(sl >> 4) * p.Hkv + cur.y / p.hchunks : -2;
+  };
+  if constexpr (APP) take_row(0);
 
   // step kc from slot d: consume, then close / switch pieces as due
   int kc = 0;
   auto consume_step = [&](int d) {
     const bool live = kc < total;
     const int valid = live && idc[d] >= 0 ? (cb == c_last ? c_tail : 16) : 0;
+    if constexpr (APP) {
+      if (idc[d] == cur_tile) {
+        const int k = pi % NQ;
+        NR::sub(buf[d], place_row(k), (int)(place_slot(k) & 15), lane);
+      }
+    }
     T::template consume<1, PC, false>(buf[d], valid, valid == 16, nullptr, 0, qr, p.sl2, &m_run,
                                       &l_run, o, c, G, qlo);
     if (live) {
@@ -620,10 +713,20 @@ void decode_stream_kernel(StreamParams p) {
             }
           } else {
             load_q_of(cur, qr, qlo);
+            [[maybe_unused]] uint32_t kr = 0u, vr = 0u;
+            [[maybe_unused]] int64_t sl = -1;
+            if constexpr (APP) {
+              sl = p.slots[cur.s];
+              NR::load(p.kn, p.vn, (int64_t)cur.s * p.Hkv + cur.y / p.hchunks, lane, kr,
+                       vr);
+            }
+
             // wait here: q registers left in flight on this rare path would
             // make every later block wait for the newest loads
             __builtin_amdgcn_s_waitcnt(kVmcnt0);
+            if constexpr (APP) stage_piece(cur, pi % NQ, kr, vr, sl);
           }
+          if constexpr (APP) take_row(pi % NQ);
         }
       }
     }
@@ -700,6 +803,9 @@ int launch_pm(const pkv::DecodeArgs& a, const StreamParams& sp, int grid) {
       return pkv::launch_kernel(decode_stream_kernel<QT, KVT, D, true, PM>, dim3(grid), block,
                                 a.stream, sp, a.ev_start, a.ev_stop);
   }
+  if (sp.kn)
+    return pkv::launch_kernel(decode_stream_kernel<QT, KVT, D, false, PM, true>, dim3(grid), block,
+                              a.stream, sp, a.ev_start, a.ev_stop);
   return pkv::launch_kernel(decode_stream_kernel<QT, KVT, D, false, PM>, dim3(grid), block,
                             a.stream, sp, a.ev_start, a.ev_stop);
 }
@@ -750,6 +856,11 @@ StreamParams make_stream_params(const pkv::DecodeArgs& a, int grid, void* ws, si
   sp.P = 0;
   sp.num_parts = 0;
   sp.ws_m = sp.ws_l = sp.ws_acc = nullptr;
+  sp.kn = kp.kn;
+  sp.vn = kp.vn;
+  sp.slots = kp.slots;
+  sp.k_inv = kp.k_inv;
+  sp.v_inv = kp.v_inv;
   return sp;
 }
 

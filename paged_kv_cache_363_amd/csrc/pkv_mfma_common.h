@@ -548,6 +548,93 @@ struct MfmaTile {
 };
 
 
+// The step's new K/V row of one (sequence, kv-head), appended inside a decode
+// kernel: the row goes to its slot and attention reads the context with it
+// ("Transformer 推理优化", sections 2.2 and 3.3).  Lane l of a wave takes the
+// row's elements EPL l .. EPL l + EPL - 1 (EPL = D / 64): it loads them raw
+// (16-bit, the q dtype), encodes them to the cache's type with the bytes the
+// cache append stores, and stages the encoded K row, then V row, in LDS
+// (STAGE bytes).  sub() puts the staged row into a loaded tile of the slot's
+// block, at the slot's position, in the tile's register layout: a wave that
+// does so before consuming the tile sees the new row whether its loads ran
+// before or after the row's store, so no read waits for the write.
+template <int QT, int KVT, int D>
+struct NewRow {
+  using T = MfmaTile<QT, KVT, D>;
+  static constexpr int EPL = D / 64;
+  static constexpr int LB = EPL * T::KVB;   // encoded bytes per lane and row
+  static constexpr int STAGE = 2 * D * T::KVB;
+
+  // row: (sequence * num_kv_heads + kv-head)
+  __device__ static void load(const uint8_t* kn, const uint8_t* vn, int64_t row, int lane,
+                              uint32_t& kraw, uint32_t& vraw) {
+    const int64_t e0 = row * D + EPL * lane;
+    if constexpr (EPL == 2) {
+      kraw = reinterpret_cast<const uint32_t*>(kn)[e0 / 2];
+      vraw = reinterpret_cast<const uint32_t*>(vn)[e0 / 2];
+    } else {
+      kraw = reinterpret_cast<const uint16_t*>(kn)[e0];
+      vraw = reinterpret_cast<const uint16_t*>(vn)[e0];
+    }
+  }
+  __device__ static void put(uint8_t* dst, uint32_t x) {
+    if constexpr (LB == 4) *reinterpret_cast<uint32_t*>(dst) = x;
+    else if constexpr (LB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)x;
+    else *dst = (uint8_t)x;
+  }
+  __device__ static void encode(uint32_t kraw, uint32_t vraw, float k_inv, float v_inv,
+                                uint32_t& ke, uint32_t& ve) {
+    encode_new_chunk<QT, KVT, EPL>(make_uint4(kraw, 0u, 0u, 0u), k_inv, &ke);
+    encode_new_chunk<QT, KVT, EPL>(make_uint4(vraw, 0u, 0u, 0u), v_inv, &ve);
+  }
+  // lds: STAGE bytes, 16-byte aligned
+  __device__ static void stage(uint8_t* lds, int lane, uint32_t ke, uint32_t ve) {
+    put(lds + LB * lane, ke);
+    put(lds + D * T::KVB + LB * lane, ve);
+  }
+  // the row's store at `slot` (0 <= slot < num_blocks * 16)
+  __device__ static void store(uint8_t* kc, uint8_t* vc, int64_t slot, int Hkv, int hk, int lane,
+                               uint32_t ke, uint32_t ve) {
+    const int64_t row0 = (((slot >> 4) * Hkv + hk) * pkv::kBlockSize + (slot & 15)) * D;
+    put(kc + row0 * T::KVB + LB * lane, ke);
+    put(vc + row0 * T::KVB + LB * lane, ve);
+  }
+  // r: a loaded tile of the slot's block; tn: the slot's position in it.
+  // Every lane reads the staged row (the empty asm takes the values in all
+  // lanes): otherwise the compiler turns the selects into exec-masked LDS
+  // reads straight into the tile's registers, whose branches leave the load
+  // counter's order unknown in the block loop, which then waits for every
+  // load in flight.
+  __device__ static void sub(typename T::Raw& r, const uint8_t* lds, int tn, int lane) {
+    const int c = lane & 15, G = lane >> 4;
+    const bool kl = c == tn, vl = G == (tn >> 2);
+    u32x4 ek[T::KL];
+#pragma unroll
+    for (int kk = 0; kk < T::KL; ++kk) {
+      const int d0 = T::BYTE ? 64 * kk + 16 * G : 32 * kk + 8 * G;   // as MfmaTile::issue
+      ek[kk] = *reinterpret_cast<const u32x4*>(lds + d0 * T::KVB);
+      asm volatile("" ::"v"(ek[kk]));
+    }
+#pragma unroll
+    for (int kk = 0; kk < T::KL; ++kk) r.k[kk] = kl ? ek[kk] : r.k[kk];
+    const typename T::VRow e =
+        *reinterpret_cast<const typename T::VRow*>(lds + (D + T::DPL * c) * T::KVB);
+    if constexpr (T::ROWB == 4)
+      asm volatile("" ::"v"(e.w[0]));
+    else
+      asm volatile("" ::"v"(e.w));
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const bool take = vl && rr == (tn & 3);
+      if constexpr (T::ROWB == 4)
+        r.v[rr].w[0] = take ? e.w[0] : r.v[rr].w[0];
+      else
+        r.v[rr].w = take ? e.w : r.v[rr].w;
+    }
+  }
+};
+
+
 // Online-softmax pass of one wave over the blocks [b0, b1) of one
 // (sequence, kv-head) segment, continuing the running state of NTL column
 // tiles (m_run[j], l_run[j], o[j][DPL], q operand qr[j][KSTEPS]).

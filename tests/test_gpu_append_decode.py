@@ -7,10 +7,12 @@ and the decode each already match the oracle: tests/test_gpu_append.py,
 tests/test_gpu_decode.py).
 
 Cases:
-  - the planner's single pass on the fixed-partition MFMA kernel, where the
-    decode kernel appends the rows itself (E4M3, INT8 and bf16 caches);
-  - the balanced schedule and the vector kernel, where the call runs the
-    append kernel first;
+  - the planner's schedule and the balanced one (E4M3, INT8, bf16, f16 and
+    f32 caches): on the MFMA kernels (fixed partitions, balanced grid,
+    partitions on the persistent grid) the decode kernel appends the rows
+    itself, on the vector kernel the call runs the append kernel first;
+  - 512-token partitions on the persistent grid, and the 32K shared-prefix
+    workload;
   - sequences without a new row (negative slot; their context stops before
     the step's token);
   - slots of earlier tokens of a sequence's own blocks (the row of token
@@ -109,8 +111,30 @@ def test_appending_decode_rewriting_an_earlier_token(name, back):
         pytest.skip(f"no workload {name}")
     print(f"[case] appending decode {name} rewriting token ctx-1-{back}", flush=True)
     st = state(name)
-    # one partition per context: the fixed-partition kernel, which appends itself
-    run_both(st, 16 * st["cfg"].max_blocks_per_seq, algo="mfma", back=back)
+    # one partition per context (the fixed-partition kernel), the balanced
+    # grid, and 512-token partitions on the persistent grid
+    for ps in (16 * st["cfg"].max_blocks_per_seq, 0, 512):
+        run_both(st, ps, algo="mfma", back=back)
+
+
+@pytest.mark.parametrize("name", ["c2_qwen3_8b_bf16", "c6_llama3_70b_int8"])
+def test_appending_decode_in_partition_mode(name):
+    if name not in CONFIGS:
+        pytest.skip(f"no workload {name}")
+    print(f"[case] appending decode {name}, 512-token partitions", flush=True)
+    st = state(name)
+    run_both(st, 512, algo="mfma")
+    run_both(st, 512, algo="mfma", skip_every=4)
+
+
+def test_appending_decode_long_shared_prefix():
+    name = "c5_long_shared_bf16"
+    if name not in CONFIGS:
+        pytest.skip(f"no workload {name}")
+    print(f"[case] appending decode {name} (its 512-token partitions, then balanced)", flush=True)
+    st = gpu_setup(CONFIGS[name], step_append=False)
+    run_both(st, CONFIGS[name].partition_size, algo="mfma")
+    run_both(st, 0, algo="mfma")
 
 
 def test_appending_decode_on_the_fixed_kernel_beyond_the_persistent_grid():
