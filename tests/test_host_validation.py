@@ -249,3 +249,42 @@ def test_stream_workgroups_override_is_per_thread():
     finally:
         assert l.pkv_set_stream_workgroups(0) == _lib.PKV_OK
     assert seen["size"] == base
+
+
+def appending(**kw):
+    fake = ctypes.c_void_p(1 << 20)   # 16-byte aligned, never dereferenced
+    a = dict(out=fake, q=fake, kn=fake, vn=fake, slots=fake, k=fake, v=fake, bt=fake, cl=fake, S=4,
+             hq=8, hkv=2, d=128, bs=16, nb=10, mb=4, scale=0.1, qd=_lib.PKV_BF16,
+             kvd=_lib.PKV_FP8_E4M3, ks=0.5, vs=0.5, ps=0, ws=NULL, wsb=0, algo=0)
+    a.update(kw)
+    return lib().pkv_paged_decode_attention_appending(
+        a["out"], a["q"], a["kn"], a["vn"], a["slots"], a["k"], a["v"], a["bt"], a["cl"], a["S"],
+        a["hq"], a["hkv"], a["d"], a["bs"], a["nb"], a["mb"], a["scale"], a["qd"], a["kvd"],
+        a["ks"], a["vs"], a["ps"], a["ws"], a["wsb"], a["algo"], NULL, NULL, NULL, NULL)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(kn=NULL), dict(vn=NULL), dict(slots=NULL),                     # the new rows
+    dict(kn=ctypes.c_void_p((1 << 20) + 8)),                            # misaligned new rows
+    dict(ks=0.0), dict(vs=float("nan")), dict(ks=float("inf")),         # one-byte scales
+    dict(bs=32), dict(d=96), dict(hq=6, hkv=4), dict(out=NULL),         # the decode's own checks
+    dict(mb=256, ps=512),                                               # workspace missing
+])
+def test_appending_decode_rejects_before_any_launch(kw):
+    """pkv_paged_decode_attention_appending reports the append's and the
+    decode's argument errors before it launches anything (the pointers here
+    are never dereferenced)."""
+    st = appending(**kw)
+    assert st != _lib.PKV_OK
+    assert lib().pkv_last_error() != b""
+
+
+def test_appending_decode_scales_matter_only_for_one_byte_caches():
+    # a bf16 cache ignores the scales: the call goes on to the decode's checks
+    # (here a block size the kernels do not take), not to the scale check
+    st = appending(kvd=_lib.PKV_BF16, ks=0.0, vs=0.0, bs=32)
+    assert st == _lib.PKV_ERR_UNSUPPORTED
+
+
+def test_appending_decode_of_zero_sequences_is_a_no_op():
+    assert appending(S=0, kn=NULL, vn=NULL, slots=NULL) == _lib.PKV_OK
