@@ -1,7 +1,8 @@
 """A whole decode step captured into one HIP graph ("大语言模型推理引擎深度剖析",
 section 6: capturing the step cuts kernel-launch overhead): the library's
 calls launch kernels only (no allocation, no memset), so the append, the
-decode kernel and its merge or reduction record as graph nodes.  Each graph
+decode kernel and its merge or reduction record as graph nodes; so does the
+one-call step, whose decode kernels write the new rows themselves.  Each graph
 is replayed several times with eager work and synchronisations between the
 replays, and every replay must equal the eager step bit for bit (the kernels
 are deterministic for a fixed grid)."""
@@ -15,8 +16,18 @@ from synth import CONFIGS, MQ_CONFIGS, gen
 pytestmark = pytest.mark.gpu
 
 
-def _decode_step(st, cfg, ps, out, ws):
+def _decode_step(st, cfg, ps, out, ws, one_call=False):
+    """The step as two calls (append, then decode), or as the one call that
+    appends inside the decode kernels (pkv_paged_decode_attention_appending).
+    Rewriting the same rows at the same slots leaves the cache unchanged, so
+    every replay computes the same step."""
     import paged_kv_cache_363_amd as pkv
+    if one_call:
+        pkv.paged_decode_attention_appending(
+            st["q"], st["step"]["k"], st["step"]["v"], st["step"]["slots"], st["k_cache"],
+            st["v_cache"], st["block_tables"], st["context_lens"], cfg.scale, st["k_scale"],
+            st["v_scale"], partition_size=ps, out=out, workspace=ws)
+        return
     pkv.paged_cache_append(st["k_cache"], st["v_cache"], st["step"]["k"], st["step"]["v"],
                            st["step"]["slots"], st["k_scale"], st["v_scale"])
     pkv.paged_decode_attention(st["q"], st["k_cache"], st["v_cache"], st["block_tables"],
@@ -24,32 +35,37 @@ def _decode_step(st, cfg, ps, out, ws):
                                partition_size=ps, out=out, workspace=ws)
 
 
+@pytest.mark.parametrize("one_call", [False, True])
 @pytest.mark.parametrize("name,ps", [("c2_qwen3_8b_bf16", 0), ("c4_llama3_70b_fp8", 2560),
                                      ("c5_long_shared_bf16", 512), ("c3_llama2_7b_f16", 0)])
-def test_captured_decode_step_replays_equal_eager(name, ps):
+def test_captured_decode_step_replays_equal_eager(name, ps, one_call):
     import paged_kv_cache_363_amd as pkv
-    print(f"[case] graph decode {name} partition={ps}", flush=True)
+    print(f"[case] graph decode {name} partition={ps} one_call={one_call}", flush=True)
     cfg = CONFIGS[name]
     st = gpu_setup(cfg)
     ws = pkv.alloc_workspace(st["q"], st["k_cache"], st["block_tables"], ps)
+    step = _decode_step
+    if one_call:
+        def step(st_, cfg_, ps_, out_, ws_):
+            _decode_step(st_, cfg_, ps_, out_, ws_, one_call=True)
     eager = torch.empty_like(st["q"])
-    _decode_step(st, cfg, ps, eager, ws)
+    step(st, cfg, ps, eager, ws)
     torch.cuda.synchronize()
     out = torch.zeros_like(st["q"])
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):      # warm the capture stream, as torch asks
-        _decode_step(st, cfg, ps, out, ws)
+        step(st, cfg, ps, out, ws)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        _decode_step(st, cfg, ps, out, ws)
+        step(st, cfg, ps, out, ws)
     for rep in range(4):
         out.zero_()
         # eager work between the replays: a decode into another buffer
         other = torch.empty_like(st["q"])
-        _decode_step(st, cfg, ps, other, ws)
+        step(st, cfg, ps, other, ws)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
