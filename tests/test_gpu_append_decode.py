@@ -147,3 +147,24 @@ def test_appending_decode_on_the_fixed_kernel_beyond_the_persistent_grid():
     st = gpu_setup(cfg, step_append=False)
     run_both(st, 16, algo="mfma")
     run_both(st, 16, algo="mfma", skip_every=5)
+
+
+@pytest.mark.parametrize("q_dtype,kv_dtype", [("bf16", "bf16"), ("f16", "f16"), ("bf16", "fp8"),
+                                              ("f16", "int8")])
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_appending_decode_every_dtype_and_head_dim_on_every_mfma_schedule(q_dtype, kv_dtype,
+                                                                          head_dim):
+    """One element of each new row per lane (head_dim 64) or two (128), for
+    16-bit copies and one-byte encodings, on the fixed-partition kernel (one
+    pass), the balanced grid and 64-token partitions on the persistent grid
+    (the fixed kernel's several partitions: the 2100-sequence test)."""
+    print(f"[case] appending decode {q_dtype}/{kv_dtype} d={head_dim}", flush=True)
+    rs = np.random.default_rng(head_dim + len(kv_dtype))
+    ctxs = tuple(int(x) for x in rs.integers(1, 300, 24))
+    cfg = Config(name="append_dtypes", num_seqs=len(ctxs), num_q_heads=8, num_kv_heads=2,
+                 head_dim=head_dim, q_dtype=q_dtype, kv_dtype=kv_dtype, ctx_kind="list",
+                 ctx_params=ctxs, seed=77 + head_dim, max_blocks_per_seq=19)
+    st = gpu_setup(cfg, step_append=False)
+    for ps in (16 * cfg.max_blocks_per_seq, 0, 64):
+        run_both(st, ps, algo="mfma")
+    run_both(st, 0, algo="mfma", skip_every=5, back=3)
