@@ -157,7 +157,8 @@ def test_appending_decode_every_dtype_and_head_dim_on_every_mfma_schedule(q_dtyp
     """One element of each new row per lane (head_dim 64) or two (128), for
     16-bit copies and one-byte encodings, on the fixed-partition kernel (one
     pass), the balanced grid and 64-token partitions on the persistent grid
-    (the fixed kernel's several partitions: the 2100-sequence test)."""
+    (the fixed kernel's several partitions: the 2100-sequence test), and the
+    vector kernel (append kernel first)."""
     print(f"[case] appending decode {q_dtype}/{kv_dtype} d={head_dim}", flush=True)
     rs = np.random.default_rng(head_dim + len(kv_dtype))
     ctxs = tuple(int(x) for x in rs.integers(1, 300, 24))
@@ -168,3 +169,7 @@ def test_appending_decode_every_dtype_and_head_dim_on_every_mfma_schedule(q_dtyp
     for ps in (16 * cfg.max_blocks_per_seq, 0, 64):
         run_both(st, ps, algo="mfma")
     run_both(st, 0, algo="mfma", skip_every=5, back=3)
+    # the vector kernel: one pass, and 64-token partitions with the reduction
+    for ps in (16 * cfg.max_blocks_per_seq, 64):
+        run_both(st, ps, algo="vector")
+    run_both(st, 64, algo="vector", skip_every=5, back=3)
