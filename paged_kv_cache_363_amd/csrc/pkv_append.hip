@@ -33,20 +33,37 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
   const int64_t th = gid / chunks;
   const int h = (int)(th % H);
   const int64_t t = th / H;
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= (int64_t)num_blocks * pkv::kBlockSize) return;
-  const int64_t blk = slot / pkv::kBlockSize, off = slot % pkv::kBlockSize;
   const int64_t src = (t * H + h) * D + (int64_t)c * kElemsPerThread;
-  const int64_t dst = ((blk * H + h) * pkv::kBlockSize + off) * D + (int64_t)c * kElemsPerThread;
   constexpr int nb_in = DType<NEW_DT>::bytes * kElemsPerThread;
+  constexpr int NI = nb_in / 16;
+  // The new rows do not depend on the slot: their loads go out with the
+  // slot's, so that the two round trips overlap.
+  uint4 raw[2][NI];
+#pragma unroll
+  for (int which = 0; which < 2; ++which)
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      raw[which][i] = reinterpret_cast<const uint4*>((which ? vn : kn) + src * DType<NEW_DT>::bytes)[i];
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= (int64_t)num_blocks * pkv::kBlockSize) {
+    // the rows are used on this path too, so the compiler keeps their loads
+    // above the branch
+#pragma unroll
+    for (int which = 0; which < 2; ++which)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        asm volatile("" ::"v"(raw[which][i].x), "v"(raw[which][i].y), "v"(raw[which][i].z),
+                     "v"(raw[which][i].w));
+    return;
+  }
+  const int64_t blk = slot / pkv::kBlockSize, off = slot % pkv::kBlockSize;
+  const int64_t dst = ((blk * H + h) * pkv::kBlockSize + off) * D + (int64_t)c * kElemsPerThread;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
-    const uint8_t* in = (which ? vn : kn) + src * DType<NEW_DT>::bytes;
     uint8_t* outp = (which ? vc : kc) + dst * DType<KV_DT>::bytes;
     if constexpr (KV_DT == NEW_DT) {
 #pragma unroll
-      for (int i = 0; i < nb_in; i += 16)
-        *reinterpret_cast<uint4*>(outp + i) = *reinterpret_cast<const uint4*>(in + i);
+      for (int i = 0; i < NI; ++i) reinterpret_cast<uint4*>(outp)[i] = raw[which][i];
     } else {
       static_assert(KV_DT == PKV_FP8_E4M3 || KV_DT == PKV_INT8,
                     "only E4M3 and INT8 caches convert");
@@ -60,10 +77,10 @@ __global__ __launch_bounds__(kAppendThreads) void cache_append_kernel(
         invs[i] = sc ? __fdiv_rn(1.0f, sc[(int64_t)h * D + c * kElemsPerThread + i]) : inv;
       float f[kElemsPerThread];
       if constexpr (NEW_DT == PKV_F32) {
-        chunk_to_f32<PKV_F32>(*reinterpret_cast<const uint4*>(in), f);
-        chunk_to_f32<PKV_F32>(*reinterpret_cast<const uint4*>(in + 16), f + 4);
+        chunk_to_f32<PKV_F32>(raw[which][0], f);
+        chunk_to_f32<PKV_F32>(raw[which][1], f + 4);
       } else {
-        chunk_to_f32<NEW_DT>(*reinterpret_cast<const uint4*>(in), f);
+        chunk_to_f32<NEW_DT>(raw[which][0], f);
       }
       uint32_t lo = 0, hi = 0;
 #pragma unroll
