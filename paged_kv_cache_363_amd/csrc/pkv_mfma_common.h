@@ -23,6 +23,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "pkv_decode_common.h"
 
 #ifndef PKV_LAZY_RESCALE
@@ -752,11 +754,12 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
     if constexpr (Hook::subst) {
       if (c0 == b0) hook.prepare();
     }
-    for (int i = 0; i < n; i += DEPTH) {
-#pragma unroll
-      for (int d = 0; d < DEPTH; ++d) {
-        const int ii = i + d;
-        const int idn = id_at(ii + DEPTH);
+    // Groups of DEPTH steps, each step issuing the step DEPTH ahead (past
+    // the window's end: its last block again).
+    if constexpr (NTL == 1) {
+      // step ii from slot d: consume it, then (ISSUE) issue the loads of
+      // step ii + DEPTH into the slot
+      auto step = [&](int d, int ii, auto issue_c) {
         const int valid = (ii < n && (unsigned)idc[d] < (unsigned)nb)
                               ? (c0 + ii == last ? tail : 16) : 0;
         const bool whole = valid == 16 && (!CAUSAL || c0 + ii < whole_end);
@@ -769,9 +772,52 @@ __device__ __forceinline__ void mfma_piece(const uint8_t* kc, const uint8_t* vc,
             rem = hook.period;
           }
         }
-        const int64_t a = addr(idn);
-        T::template issue<NT>(buf[d], kc + a, vc + a, koff, voff);
-        idc[d] = idn;
+        if constexpr (decltype(issue_c)::value) {
+          const int idn = id_at(ii + DEPTH);
+          const int64_t a = addr(idn);
+          T::template issue<NT>(buf[d], kc + a, vc + a, koff, voff);
+          idc[d] = idn;
+        }
+      };
+      // In the piece's last window the final group issues nothing, so that
+      // no unused load is left in flight when the piece ends (it would sit
+      // ahead of the next loads in the load counter, and hold up the wave's
+      // end).  The issuing and the final groups are separate code, so every
+      // load counter wait stays exact.
+      const bool last_win = c0 + 64 * NW >= b1;
+      int i = 0;
+      for (; last_win ? i + DEPTH < n : i < n; i += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) step(d, i + d, std::true_type{});
+      }
+      if (last_win) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) step(d, i + d, std::false_type{});
+      }
+    } else {
+      // Several column tiles: every group issues (a second copy of the
+      // group measured slower there: 64-row chunks 397 -> 418 us).
+      for (int i = 0; i < n; i += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+          const int ii = i + d;
+          const int idn = id_at(ii + DEPTH);
+          const int valid = (ii < n && (unsigned)idc[d] < (unsigned)nb)
+                                ? (c0 + ii == last ? tail : 16) : 0;
+          const bool whole = valid == 16 && (!CAUSAL || c0 + ii < whole_end);
+          if constexpr (Hook::subst) hook.sub(buf[d], idc[d]);
+          T::template consume<NTL, PC, CAUSAL>(buf[d], valid, whole, pos, 16 * (c0 + ii), qr,
+                                               sl2, m_run, l_run, o, c, G, qlo);
+          if constexpr (Hook::active) {
+            if (ii < n && (--rem == 0 || c0 + ii == b1 - 1)) {
+              hook();
+              rem = hook.period;
+            }
+          }
+          const int64_t a = addr(idn);
+          T::template issue<NT>(buf[d], kc + a, vc + a, koff, voff);
+          idc[d] = idn;
+        }
       }
     }
     if (c0 + 64 * NW < b1) load_ids(ids, c0 + 64 * NW);
